@@ -1,0 +1,179 @@
+"""Seeded synthetic workloads for the SSD layer core.
+
+This module only draws inputs. It holds none of the SSD arithmetic and is the
+one piece of code that both the GPU path's tests/bench and the CPU oracle
+consume. Every array it returns is float32 holding the *exact* value the
+device receives: on bf16 workloads each value has already been rounded to
+bf16 (round-to-nearest-even), so widening it to fp64 on the host loses
+nothing.
+
+Distributions (the selective-SSM parametrisation on the youngju.dev
+"Mamba / selective SSM" page, section on switching from LTI to selection:
+dt comes out of a softplus; Qiita "Mamba-2" article, section 4.2: A is a
+negative scalar per head, A = -exp(A_log)):
+
+    x      ~ N(0, 1)
+    dt     = clamp(softplus(N(0,1) - 4), 1e-3, 0.1)   (long-context workload:
+             dt = exp(U(ln 1e-4, ln 1e-1)), no clamp)
+    A_h    = -exp(U(0, ln 16))                       in [-16, -1]
+    B, C   ~ N(0, 1) / sqrt(N)
+    D_h    ~ N(0, 1)
+    init   = 0, or N(0, 0.1) (std 0.1) fp32 where the workload asks for it
+
+Draw order for a forward workload is x, dt, A, B, C, D, init; the generator is
+numpy's PCG64 ``default_rng(seed)``. Normal draws use numpy's float32
+ziggurat (``standard_normal(dtype=float32)``).
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional
+
+import numpy as np
+
+
+# --------------------------------------------------------------------------
+# bf16 carriers
+# --------------------------------------------------------------------------
+
+def round_to_bf16(a: np.ndarray) -> np.ndarray:
+    """Round float32 values to the nearest bf16 (ties to even), returned as
+    float32 carriers. NaN/Inf never occur in these workloads."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    u = a.view(np.uint32)
+    rounded = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) & np.uint32(0xFFFF0000)
+    return rounded.view(np.float32)
+
+
+def bf16_bits(a: np.ndarray) -> np.ndarray:
+    """The 16-bit patterns of float32 carriers that already hold bf16 values."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    return (a.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+# --------------------------------------------------------------------------
+# Workload descriptions
+# --------------------------------------------------------------------------
+
+@dataclasses.dataclass(frozen=True)
+class FwdWorkload:
+    name: str
+    batch: int
+    seqlen: int
+    nheads: int
+    headdim: int
+    dstate: int
+    ngroups: int
+    chunk_len: int
+    dtype: str                 # "f32" or "bf16": dtype of x, dt, B, C, y
+    dt_mode: str = "softplus"  # "softplus" (clamped) or "loguniform"
+    init: str = "zero"         # "zero" or "normal0.1"
+    seed: int = 0
+
+    @property
+    def tokens(self) -> int:
+        return self.batch * self.seqlen
+
+
+@dataclasses.dataclass(frozen=True)
+class DecodeWorkload:
+    name: str
+    batch: int
+    nheads: int
+    headdim: int
+    dstate: int
+    ngroups: int
+    steps: int
+    dtype: str = "bf16"
+    seed: int = 0
+
+
+# The five named workloads (shapes and distributions of the method's layer
+# sizes: a tiny fp32 case, a 130M-shaped layer, a 2.7B-shaped layer with a
+# nonzero initial state, a 128K-token long-context case, and a decode batch).
+TINY_F32 = FwdWorkload("tiny_f32_b1_T256_H2_P16_N16_Q64", 1, 256, 2, 16, 16, 1, 64,
+                       "f32", seed=4600)
+MAMBA2_130M = FwdWorkload("mamba2_130m_b8_T2048_H24_P64_N128_Q256", 8, 2048, 24, 64, 128, 1, 256,
+                          "bf16", seed=4601)
+MAMBA2_2P7B = FwdWorkload("mamba2_2p7b_b4_T4096_H80_P64_N128_Q256_init", 4, 4096, 80, 64, 128, 1, 256,
+                          "bf16", init="normal0.1", seed=4602)
+LONG_128K = FwdWorkload("long_b1_T131072_H24_P64_N256_Q256", 1, 131072, 24, 64, 256, 1, 256,
+                        "bf16", dt_mode="loguniform", seed=4603)
+DECODE_B256 = DecodeWorkload("decode_b256_H128_P64_N128_G8_64steps", 256, 128, 64, 128, 8, 64,
+                             "bf16", seed=4604)
+
+FWD_WORKLOADS = {w.name: w for w in (TINY_F32, MAMBA2_130M, MAMBA2_2P7B, LONG_128K)}
+
+
+def with_shape(w: FwdWorkload, **kw) -> FwdWorkload:
+    return dataclasses.replace(w, **kw)
+
+
+# --------------------------------------------------------------------------
+# Generators
+# --------------------------------------------------------------------------
+
+def _softplus(v: np.ndarray) -> np.ndarray:
+    v = v.astype(np.float64)
+    return np.where(v > 20.0, v, np.log1p(np.exp(np.minimum(v, 20.0))))
+
+
+def _store(a: np.ndarray, dtype: str) -> np.ndarray:
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    return round_to_bf16(a) if dtype == "bf16" else a
+
+
+def draw_dt(rng: np.random.Generator, shape, mode: str) -> np.ndarray:
+    if mode == "softplus":
+        v = rng.standard_normal(shape, dtype=np.float32).astype(np.float64) - 4.0
+        return np.clip(_softplus(v), 1e-3, 0.1).astype(np.float32)
+    if mode == "loguniform":
+        u = rng.uniform(math.log(1e-4), math.log(1e-1), size=shape)
+        return np.exp(u).astype(np.float32)
+    raise ValueError(mode)
+
+
+def draw_A(rng: np.random.Generator, nheads: int) -> np.ndarray:
+    return (-np.exp(rng.uniform(0.0, math.log(16.0), size=nheads))).astype(np.float32)
+
+
+def make_fwd_inputs(w: FwdWorkload, seed: Optional[int] = None) -> dict:
+    """Inputs of one forward call, all float32 carriers of the stored values.
+
+    x [b,T,H,P], dt [b,T,H], A [H], B/C [b,T,G,N], D [H], init [b,H,N,P] or None.
+    """
+    rng = np.random.default_rng(w.seed if seed is None else seed)
+    b, T, H, P, N, G = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups
+    x = _store(rng.standard_normal((b, T, H, P), dtype=np.float32), w.dtype)
+    dt = _store(draw_dt(rng, (b, T, H), w.dt_mode), w.dtype)
+    A = draw_A(rng, H)
+    s = np.float32(1.0 / math.sqrt(N))
+    B = _store(rng.standard_normal((b, T, G, N), dtype=np.float32) * s, w.dtype)
+    C = _store(rng.standard_normal((b, T, G, N), dtype=np.float32) * s, w.dtype)
+    D = rng.standard_normal(H, dtype=np.float32)
+    init = None
+    if w.init == "normal0.1":
+        init = (rng.standard_normal((b, H, N, P), dtype=np.float32) * np.float32(0.1))
+    elif w.init != "zero":
+        raise ValueError(w.init)
+    return dict(x=x, dt=dt, A=A, B=B, C=C, D=D, init=init)
+
+
+def make_decode_inputs(w: DecodeWorkload, seed: Optional[int] = None) -> dict:
+    """Inputs of ``w.steps`` chained decode steps.
+
+    state [b,H,N,P] f32 ~ N(0,1); per step: x [b,H,P], dt [b,H], B/C [b,G,N]
+    (stacked along a leading steps axis); A [H], D [H] fixed.
+    """
+    rng = np.random.default_rng(w.seed if seed is None else seed)
+    b, H, P, N, G, S = w.batch, w.nheads, w.headdim, w.dstate, w.ngroups, w.steps
+    A = draw_A(rng, H)
+    D = rng.standard_normal(H, dtype=np.float32)
+    state = rng.standard_normal((b, H, N, P), dtype=np.float32)
+    s = np.float32(1.0 / math.sqrt(N))
+    xs = _store(rng.standard_normal((S, b, H, P), dtype=np.float32), w.dtype)
+    dts = _store(draw_dt(rng, (S, b, H), "softplus"), w.dtype)
+    Bs = _store(rng.standard_normal((S, b, G, N), dtype=np.float32) * s, w.dtype)
+    Cs = _store(rng.standard_normal((S, b, G, N), dtype=np.float32) * s, w.dtype)
+    return dict(state=state, xs=xs, dts=dts, A=A, Bs=Bs, Cs=Cs, D=D)
