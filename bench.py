@@ -1,0 +1,349 @@
+#!/usr/bin/env python3
+"""Benchmark of the SSD layer core on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--no-cpu-baseline] [--no-extra]
+
+One step = one ssd_chunk_scan_fwd call (chunk_cumsum, chunk_state,
+state_passing, chunk_scan) over one batch of the workload, inputs resident in
+HBM. The headline workload is the Mamba-2-130M-shaped layer (batch 8,
+T 2048, H 24, P 64, N 128, 1 group, chunk 256, bf16 inputs, fp32
+accumulation and state). Prints ONE JSON line on stdout; progress goes to
+stderr.
+
+Kernel durations are measured live with hipEvents that the library records on
+its own stream between its four launches (ssd_chunk_scan_fwd_timed). The
+decode update (ssd_state_update) is measured on the batch-256 decode workload
+in the same run, and the fp64 CPU oracle is timed on the host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import platform
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import workloads  # noqa: E402
+
+METRIC = "SSD fwd tokens/s per layer + % of bf16 MFMA / HBM roofline on 1 MI355X"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = {
+    "chunk_cumsum": ["chunk_cumsum.hip"],
+    "chunk_state": ["chunk_state.hip", "chunk_state_mfma.hip"],
+    "state_passing": ["state_passing.hip"],
+    "chunk_scan": ["chunk_scan.hip", "chunk_scan_mfma.hip"],
+    "state_update": ["state_update.hip"],
+}
+STAGES = ["chunk_cumsum", "chunk_state", "state_passing", "chunk_scan"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# --------------------------------------------------------------------------
+# HIP events through the runtime's C API (the library records them itself)
+# --------------------------------------------------------------------------
+
+class Hip:
+    def __init__(self):
+        for name in ("libamdhip64.so", "/opt/rocm/lib/libamdhip64.so"):
+            try:
+                self.rt = ctypes.CDLL(name)
+                break
+            except OSError:
+                continue
+        else:
+            raise RuntimeError("libamdhip64.so not found")
+        self.rt.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.rt.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                ctypes.c_void_p]
+        self.rt.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.rt.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+
+    def event(self) -> int:
+        e = ctypes.c_void_p()
+        if self.rt.hipEventCreate(ctypes.byref(e)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        return e.value
+
+    def record(self, e, stream):
+        if self.rt.hipEventRecord(e, stream) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def ms(self, a, b) -> float:
+        out = ctypes.c_float()
+        if self.rt.hipEventElapsedTime(ctypes.byref(out), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(out.value)
+
+    def destroy(self, e):
+        self.rt.hipEventDestroy(e)
+
+
+# --------------------------------------------------------------------------
+# Algorithmic work per launch (each kernel's minimal I/O and useful flops)
+# --------------------------------------------------------------------------
+
+def fwd_work(w: workloads.FwdWorkload, with_init: bool) -> dict:
+    b, T, H, P, N, G, Q = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk_len
+    nc = -(-T // Q)
+    e = 2 if w.dtype == "bf16" else 4
+    x = b * T * H * P * e
+    dtb = b * T * H * e
+    bc = b * T * G * N * e
+    acs = 4 * b * H * nc * Q            # one fp32 row layout (Acs or dtq)
+    st = 4 * b * nc * H * N * P         # all chunk states, fp32
+    fst = 4 * b * H * N * P             # one [b,H,N,P] fp32 state
+    tri = Q * (Q + 1) // 2
+    return {
+        "chunk_cumsum": {"bytes": dtb + 2 * acs, "flops": b * T * H * 2},
+        "chunk_state": {"bytes": x + bc + 2 * acs + st, "flops": 2 * b * T * H * N * P},
+        "state_passing": {"bytes": 2 * st + 4 * b * H * nc + fst * (2 if with_init else 1),
+                          "flops": 2 * b * nc * H * N * P},
+        "chunk_scan": {"bytes": 2 * x + 2 * bc + 2 * acs + st,
+                       "flops": b * nc * (G * 2 * N * tri + H * (2 * P * tri + 2 * Q * N * P))},
+    }
+
+
+def decode_work(w: workloads.DecodeWorkload) -> dict:
+    b, H, P, N, G = w.batch, w.nheads, w.headdim, w.dstate, w.ngroups
+    e = 2 if w.dtype == "bf16" else 4
+    return {"bytes": 8 * b * H * N * P + 2 * b * H * P * e + b * H * e + 2 * b * G * N * e + 8 * H,
+            "flops": b * H * N * P * 5}
+
+
+# --------------------------------------------------------------------------
+# HBM traffic from committed rocprofv3 counter summaries
+# --------------------------------------------------------------------------
+
+def sources_digest(kernel: str) -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel] + ["ssd_internal.h"]:
+        p = os.path.join(ROOT, "selective_state_space_46_amd", "csrc", f)
+        if os.path.exists(p):
+            h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def counted_traffic(kernel: str, workload: str):
+    """Bytes per dispatch from profiles/traffic_<kernel>_<workload>.txt, or None
+    when no summary exists or the kernel's sources changed since it was taken."""
+    p = os.path.join(PROFILES, f"traffic_{kernel}_{workload}.txt")
+    if not os.path.exists(p):
+        return None
+    text = open(p).read()
+    m_src = re.search(r"^source_digest:\s*(\w+)", text, re.M)
+    m_b = re.search(r"^hbm_bytes_per_dispatch:\s*([0-9.eE+]+)", text, re.M)
+    if not m_src or not m_b or m_src.group(1) != sources_digest(kernel):
+        return None
+    return float(m_b.group(1))
+
+
+# --------------------------------------------------------------------------
+# GPU measurements
+# --------------------------------------------------------------------------
+
+def to_dev(a, dtype):
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(a, np.float32)).cuda()
+    return t.to(torch.bfloat16) if dtype == "bf16" else t
+
+
+def bench_fwd(hip, w, steps, warmup, cold=False):
+    import torch
+    import selective_state_space_46_amd as ssd
+
+    inp = workloads.make_fwd_inputs(w)
+    x, dt, B, C = (to_dev(inp[k], w.dtype) for k in ("x", "dt", "B", "C"))
+    A, D = to_dev(inp["A"], "f32"), to_dev(inp["D"], "f32")
+    init = to_dev(inp["init"], "f32") if inp["init"] is not None else None
+    y = torch.empty_like(x)
+    fin = torch.empty((w.batch, w.nheads, w.dstate, w.headdim), dtype=torch.float32, device="cuda")
+    code = ssd.SSD_BF16 if w.dtype == "bf16" else ssd.SSD_F32
+    nbytes = ssd.ssd_chunk_scan_fwd_workspace(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate,
+                                              w.ngroups, w.chunk_len, code)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    del inp
+
+    def call(ev=None):
+        ssd.ssd_chunk_scan_fwd_timed(x, dt, A, B, C, D, init, w.chunk_len, y=y, final_state=fin,
+                                     workspace=ws, stream=stream, stage_events=ev)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    evs = [[hip.event() for _ in range(5)] for _ in range(steps)]
+    t_start, t_end = hip.event(), hip.event()
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda") if cold else None
+
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    hip.record(t_start, stream)
+    for k in range(steps):
+        if flush is not None:
+            flush.fill_(k & 0xFF)     # evict the inputs from L2 / Infinity Cache
+        call(evs[k])
+    hip.record(t_end, stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+
+    stage_ms = {s: float(np.mean([hip.ms(ev[i], ev[i + 1]) for ev in evs])) for i, s in enumerate(STAGES)}
+    call_ms = float(np.mean([hip.ms(ev[0], ev[4]) for ev in evs]))
+    total_ms = hip.ms(t_start, t_end)
+    for e in [t_start, t_end] + [e for ev in evs for e in ev]:
+        hip.destroy(e)
+    ms_per_step = call_ms if cold else total_ms / steps
+    return dict(ms_per_step=ms_per_step, call_ms=call_ms, stage_ms=stage_ms, wall_s=wall,
+                tokens_per_s=w.tokens / (ms_per_step * 1e-3))
+
+
+def bench_decode(hip, w, warmup=4):
+    import torch
+    import selective_state_space_46_amd as ssd
+    inp = workloads.make_decode_inputs(w)
+    state = to_dev(inp["state"], "f32")
+    A, D = to_dev(inp["A"], "f32"), to_dev(inp["D"], "f32")
+    xs, dts, Bs, Cs = (to_dev(inp[k], w.dtype) for k in ("xs", "dts", "Bs", "Cs"))
+    ys = torch.empty_like(xs)
+    del inp
+    stream = torch.cuda.current_stream().cuda_stream
+    for s in range(warmup):
+        ssd.ssd_state_update(state, xs[s], dts[s], A, Bs[s], Cs[s], D, y=ys[s], stream=stream)
+    torch.cuda.synchronize()
+    evs = [hip.event() for _ in range(w.steps + 1)]
+    hip.record(evs[0], stream)
+    for s in range(w.steps):
+        ssd.ssd_state_update(state, xs[s], dts[s], A, Bs[s], Cs[s], D, y=ys[s], stream=stream)
+        hip.record(evs[s + 1], stream)
+    torch.cuda.synchronize()
+    per = [hip.ms(evs[i], evs[i + 1]) for i in range(w.steps)]
+    total = hip.ms(evs[0], evs[-1])
+    for e in evs:
+        hip.destroy(e)
+    work = decode_work(w)
+    avg = float(np.mean(per))
+    gbs = work["bytes"] / (avg * 1e-3) / 1e9
+    return {
+        "workload": w.name, "steps_chained": w.steps, "ms_per_update": avg,
+        "tokens_per_s": w.batch * w.steps / (total * 1e-3),
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": counted_traffic("state_update", "decode_b256")},
+    }
+
+
+def cpu_baseline(w, min_seconds=10.0):
+    import oracle
+    inp = workloads.make_fwd_inputs(w)
+    n = oracle.default_threads()
+    runs, t0 = 0, time.perf_counter()
+    while True:
+        oracle.ssd_fwd(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"], inp["init"],
+                       nthreads=n)
+        runs += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds:
+            break
+    cpu = platform.processor() or ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"value": round(w.tokens * runs / el, 1), "unit": "tokens/s", "cores": n, "kind": "oracle",
+            "sample": f"the whole {w.name} forward, {runs} run(s) in {el:.1f} s, fp64, {cpu}"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=workloads.MAMBA2_130M.name,
+                    choices=sorted(workloads.FWD_WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip decode / other workloads")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    hip = Hip()
+    w = workloads.FWD_WORKLOADS[args.workload]
+    log(f"[bench] {w.name}: warmup {args.warmup}, steps {args.steps}")
+    r = bench_fwd(hip, w, args.steps, args.warmup)
+    log(f"[bench] {r['ms_per_step']:.4f} ms/step, {r['tokens_per_s']:.4g} tok/s, stages {r['stage_ms']}")
+    cold = bench_fwd(hip, w, max(3, args.steps // 4), 1, cold=True)
+    log(f"[bench] cold (Infinity Cache flushed): {cold['ms_per_step']:.4f} ms/step")
+
+    work = fwd_work(w, w.init != "zero")
+    kernels = {}
+    for s in STAGES:
+        ms = r["stage_ms"][s]
+        kernels[s] = {"ms": round(ms, 5),
+                      "GB_per_s": round(work[s]["bytes"] / (ms * 1e-3) / 1e9, 1),
+                      "TFLOP_per_s": round(work[s]["flops"] / (ms * 1e-3) / 1e12, 2),
+                      "alg_bytes": work[s]["bytes"], "alg_flops": work[s]["flops"]}
+    dom = max(STAGES, key=lambda s: r["stage_ms"][s])
+    dms = r["stage_ms"][dom]
+    achieved = work[dom]["bytes"] / (dms * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": counted_traffic(dom, "mamba2_130m"),
+                "kernel": dom, "alg_bytes_per_launch": work[dom]["bytes"],
+                "mfma_frac_alg": round(work[dom]["flops"] / (dms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
+
+    out = {
+        "metric": METRIC, "value": round(r["tokens_per_s"], 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(r["ms_per_step"], 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32", "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "seq_len": w.seqlen, "nheads": w.nheads,
+                   "headdim": w.headdim, "dstate": w.dstate, "ngroups": w.ngroups,
+                   "chunk_len": w.chunk_len, "io_dtype": w.dtype, "state_dtype": "f32"},
+        "roofline": roofline,
+        "kernels": kernels,
+        "cold_cache_ms_per_step": round(cold["ms_per_step"], 5),
+    }
+    if not args.no_extra:
+        dw = workloads.DECODE_B256
+        log(f"[bench] decode {dw.name}")
+        out["decode"] = bench_decode(hip, dw)
+        log(f"[bench] decode {out['decode']['ms_per_update']:.4f} ms/update")
+        others = {}
+        for ow in (workloads.MAMBA2_2P7B, workloads.LONG_128K):
+            log(f"[bench] {ow.name}")
+            rr = bench_fwd(hip, ow, 5, 2)
+            others[ow.name] = {"tokens_per_s": round(rr["tokens_per_s"], 1),
+                               "ms_per_step": round(rr["ms_per_step"], 4),
+                               "stage_ms": {k: round(v, 4) for k, v in rr["stage_ms"].items()}}
+            log(f"[bench]   {rr['ms_per_step']:.4f} ms/step")
+        out["other_workloads"] = others
+    if not args.no_cpu_baseline:
+        log("[bench] timing the fp64 oracle on host cores")
+        out["cpu_baseline"] = cpu_baseline(w)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,169 @@
+/*
+ * ssd_api.h -- C ABI of the MI355X (gfx950) selective-state-space layer core.
+ *
+ * The layer is the multi-head selective SSM with one scalar decay per head
+ * (Qiita "Mamba-2" article, sections 4.1-4.2: A = -exp(A_log) is a scalar
+ * shared inside a head; B and C are shared by the heads of a group):
+ *
+ *     abar_t = exp(dt_t * A_h)                                   (discretised A)
+ *     h_t    = abar_t * h_{t-1} + (dt_t * B_t) x_t^T             (state, N x P)
+ *     y_t    = C_t^T h_t + D_h * x_t
+ *
+ * (youngju.dev "Mamba / selective SSM", section "LTIからSelectionへの切り替え":
+ * abar = exp(dt A), bbar = dt B, h_t = abar h_{t-1} + bbar x_t, y_t = C h_t.)
+ *
+ * ssd_chunk_scan_fwd evaluates it over a whole sequence chunk by chunk: inside
+ * a chunk the masked semiseparable product runs as matrix products, across
+ * chunks the state is passed by the recurrence (youngju.dev page, section
+ * "SSDアルゴリズムとチャンク分割"; Qiita article, section 4.2, step 3).
+ * ssd_state_update is the recurrent single-token mode used for inference
+ * (Qiita article, section 3.3; waylandz LLM book ch. 32, section 32.2.4).
+ *
+ * Conventions for every call:
+ *  - All tensor pointers are DEVICE pointers (HIP, gfx950). The caller owns
+ *    every buffer, including the forward workspace; the library allocates
+ *    nothing and keeps no state between calls.
+ *  - Layouts are dense, row-major, last index fastest; no strides:
+ *      x, y   [batch, seqlen, nheads, headdim]    (decode: [batch, nheads, headdim])
+ *      dt     [batch, seqlen, nheads]             (decode: [batch, nheads])
+ *      B, C   [batch, seqlen, ngroups, dstate]    (decode: [batch, ngroups, dstate])
+ *      state  [batch, nheads, dstate, headdim]    fp32 (init_state, final_state, state)
+ *      A, D   [nheads] fp32
+ *    Head h reads group g = h / (nheads / ngroups).
+ *  - `dtype` is the element type of x, dt, B, C and y (fp32 or bf16). A, D
+ *    and every state are fp32; accumulation is fp32.
+ *  - dt is used as given (already positive, e.g. after a softplus); A <= 0 is
+ *    the supported domain.
+ *  - Every pointer must be 16-byte aligned.
+ *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
+ *    stream) and never synchronise. All argument checks run on the host
+ *    before the first launch: on any error nothing is launched, nothing is
+ *    written and a status is returned. A launch failure returns SSD_ERR_HIP;
+ *    a device-side fault surfaces at the caller's next synchronisation.
+ *  - No C++ exception crosses this interface. Results are deterministic
+ *    (no atomics): the same inputs give bitwise-identical outputs.
+ */
+#ifndef SSD_API_H
+#define SSD_API_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__)
+#define SSD_API __attribute__((visibility("default")))
+#else
+#define SSD_API
+#endif
+
+typedef enum {
+    SSD_OK = 0,
+    SSD_ERR_NULL = 1,      /* a required pointer is NULL                          */
+    SSD_ERR_SHAPE = 2,     /* a dimension is < 1, nheads % ngroups != 0, or a
+                              headdim / dstate outside the supported range        */
+    SSD_ERR_DTYPE = 3,     /* dtype is not SSD_F32 or SSD_BF16                    */
+    SSD_ERR_CHUNK = 4,     /* chunk_len is not one of 16, 32, 64, 128, 256        */
+    SSD_ERR_WORKSPACE = 5, /* workspace NULL or smaller than the query's answer   */
+    SSD_ERR_HIP = 6,       /* a kernel launch failed                              */
+    SSD_ERR_ALIAS = 7,     /* an output overlaps an input it must not overlap     */
+    SSD_ERR_ALIGN = 8      /* a pointer is not 16-byte aligned                    */
+} ssd_status;
+
+typedef enum { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype;
+
+/* Supported ranges (checked; anything else is SSD_ERR_SHAPE / SSD_ERR_CHUNK):
+ *   1 <= headdim <= 256, 1 <= dstate <= 256, chunk_len in {16,32,64,128,256},
+ *   batch, seqlen, nheads, ngroups >= 1, nheads % ngroups == 0,
+ *   batch <= 65535, ceil(seqlen / chunk_len) <= 65535.                     */
+#define SSD_MAX_HEADDIM 256
+#define SSD_MAX_DSTATE 256
+
+/*
+ * Bytes of device workspace ssd_chunk_scan_fwd needs for these sizes; 0 when
+ * the sizes are invalid. The workspace holds the per-chunk cumulative decay
+ * (fp32 [batch, nheads, nchunks, chunk_len], nchunks = ceil(seqlen/chunk_len)),
+ * the step sizes widened to fp32 in the same layout, and the per-chunk states
+ * (fp32 [batch, nchunks, nheads, dstate, headdim]). It carries nothing from
+ * one call to the next.
+ */
+SSD_API size_t ssd_chunk_scan_fwd_workspace(int batch, int seqlen, int nheads, int headdim,
+                                    int dstate, int ngroups, int chunk_len, ssd_dtype dtype);
+
+/*
+ * Chunked forward over a whole sequence (the SSD algorithm: intra-chunk
+ * matrix products plus inter-chunk state passing; youngju.dev page, section
+ * "SSDアルゴリズムとチャンク分割"; Qiita article, section 4.2).
+ *
+ *   x [b,T,H,P], dt [b,T,H], B/C [b,T,G,N] : dtype        (read)
+ *   A [H], D [H] fp32                        (read; D may be NULL = no skip term)
+ *   init_state [b,H,N,P] fp32                (read; NULL = zero state). It is the
+ *                                            state before token 0, so token 0
+ *                                            decays it by exp(dt_0 A_h).
+ *   y [b,T,H,P] dtype                        (written; rounded to nearest even
+ *                                            when dtype is bf16)
+ *   final_state [b,H,N,P] fp32               (written; NULL = not produced). The
+ *                                            state after token T-1; feeding it as
+ *                                            init_state of the next call continues
+ *                                            the sequence (youngju.dev page,
+ *                                            "状態初期化とシーケンス境界").
+ *   workspace / workspace_bytes              (caller-owned scratch, see the query)
+ *
+ * seqlen need not be a multiple of chunk_len: the last chunk behaves as if
+ * padded with dt = 0 tokens, which leave the state unchanged (youngju.dev page,
+ * "デバッグチェックリスト": padding tokens get dt = 0). Results do not depend on
+ * chunk_len beyond rounding.
+ * Aliasing: y must not overlap any input or final_state; final_state may be
+ * the same buffer as init_state (in place), but must not partially overlap it.
+ */
+SSD_API ssd_status ssd_chunk_scan_fwd(const void *x, const void *dt, const float *A, const void *B,
+                              const void *C, const float *D, const float *init_state,
+                              void *y, float *final_state,
+                              int batch, int seqlen, int nheads, int headdim, int dstate,
+                              int ngroups, int chunk_len, ssd_dtype dtype,
+                              void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Measurement variant of ssd_chunk_scan_fwd: identical computation, and it
+ * records stage_events[0..4] (hipEvent_t handles created by the caller, e.g.
+ * with hipEventCreate) on `stream` before chunk_cumsum, before chunk_state,
+ * before state_passing, before chunk_scan and after chunk_scan, so that
+ * hipEventElapsedTime gives each kernel's duration on the stream it runs on.
+ * stage_events may be NULL (then it is ssd_chunk_scan_fwd). A failed event
+ * record returns SSD_ERR_HIP.
+ */
+SSD_API ssd_status ssd_chunk_scan_fwd_timed(const void *x, const void *dt, const float *A,
+                                            const void *B, const void *C, const float *D,
+                                            const float *init_state, void *y, float *final_state,
+                                            int batch, int seqlen, int nheads, int headdim,
+                                            int dstate, int ngroups, int chunk_len,
+                                            ssd_dtype dtype, void *workspace,
+                                            size_t workspace_bytes, void *stream,
+                                            void *const *stage_events);
+
+/*
+ * One recurrent step for every (batch row, head), in place on `state`
+ * (Qiita article, section 3.3: inference runs as a recurrence with constant
+ * memory; waylandz LLM book ch. 32, section 32.2.4, recurrent form):
+ *
+ *   state [b,H,N,P] fp32 : h <- exp(dt*A_h) h + (dt*B) x^T     (read, written)
+ *   x [b,H,P], dt [b,H], B/C [b,G,N] : dtype                   (read)
+ *   A [H], D [H] fp32 (D may be NULL)                           (read)
+ *   y [b,H,P] dtype : y = C^T h_new + D_h x                     (written)
+ *
+ * Aliasing: y must not overlap state or any input.
+ */
+SSD_API ssd_status ssd_state_update(float *state, const void *x, const void *dt, const float *A,
+                            const void *B, const void *C, const float *D, void *y,
+                            int batch, int nheads, int headdim, int dstate, int ngroups,
+                            ssd_dtype dtype, void *stream);
+
+/* Static, NUL-terminated description of a status code. */
+SSD_API const char *ssd_status_string(ssd_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSD_API_H */

@@ -1,0 +1,204 @@
+"""MI355X (gfx950) selective-state-space layer core: Python binding of libssd.so.
+
+This module only marshals arguments: it checks dtypes/devices, allocates
+outputs and the workspace with torch when the caller does not pass them, and
+calls the C ABI declared in ``include/ssd_api.h`` on torch's current stream.
+Every step of the computation runs in the HIP kernels of ``libssd.so``; there
+is no CPU or PyTorch fallback. If the library has not been built, importing
+the entry points raises.
+
+Entry points (same names as the C ABI):
+    ssd_chunk_scan_fwd_workspace(...) -> bytes
+    ssd_chunk_scan_fwd(x, dt, A, B, C, D, init_state, chunk_len) -> (y, final_state)
+    ssd_state_update(state, x, dt, A, B, C, D) -> y     (state updated in place)
+    ssd_status_string(code) -> str
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+__all__ = [
+    "SSD_F32", "SSD_BF16", "SSDError", "lib", "lib_path",
+    "ssd_chunk_scan_fwd_workspace", "ssd_chunk_scan_fwd", "ssd_chunk_scan_fwd_timed",
+    "ssd_state_update", "ssd_status_string",
+]
+
+SSD_F32 = 0
+SSD_BF16 = 1
+
+STATUS_NAMES = {
+    0: "SSD_OK", 1: "SSD_ERR_NULL", 2: "SSD_ERR_SHAPE", 3: "SSD_ERR_DTYPE", 4: "SSD_ERR_CHUNK",
+    5: "SSD_ERR_WORKSPACE", 6: "SSD_ERR_HIP", 7: "SSD_ERR_ALIAS", 8: "SSD_ERR_ALIGN",
+}
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libssd.so")
+_lib = None
+
+
+class SSDError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {STATUS_NAMES.get(code, code)} ({ssd_status_string(code)})")
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libssd.so with argument types set. Raises if it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(
+            f"{_LIB_PATH} is missing: build it with `python -m selective_state_space_46_amd.build` "
+            "(there is no fallback implementation)")
+    L = ctypes.CDLL(_LIB_PATH)
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    L.ssd_chunk_scan_fwd_workspace.argtypes = [i32] * 7 + [i32]
+    L.ssd_chunk_scan_fwd_workspace.restype = sz
+    L.ssd_chunk_scan_fwd.argtypes = [vp] * 9 + [i32] * 7 + [i32, vp, sz, vp]
+    L.ssd_chunk_scan_fwd.restype = i32
+    L.ssd_chunk_scan_fwd_timed.argtypes = [vp] * 9 + [i32] * 7 + [i32, vp, sz, vp, vp]
+    L.ssd_chunk_scan_fwd_timed.restype = i32
+    L.ssd_state_update.argtypes = [vp] * 8 + [i32] * 5 + [i32, vp]
+    L.ssd_state_update.restype = i32
+    L.ssd_status_string.argtypes = [i32]
+    L.ssd_status_string.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def ssd_status_string(code: int) -> str:
+    return lib().ssd_status_string(int(code)).decode()
+
+
+def ssd_chunk_scan_fwd_workspace(batch: int, seqlen: int, nheads: int, headdim: int, dstate: int,
+                                 ngroups: int, chunk_len: int, dtype: int) -> int:
+    return int(lib().ssd_chunk_scan_fwd_workspace(batch, seqlen, nheads, headdim, dstate, ngroups,
+                                                  chunk_len, dtype))
+
+
+# --------------------------------------------------------------------------
+# torch marshalling
+# --------------------------------------------------------------------------
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return SSD_F32
+    if t.dtype == torch.bfloat16:
+        return SSD_BF16
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _dev(t, dev, name):
+    if t is None:
+        return None
+    if not t.is_cuda or t.device != dev:
+        raise ValueError(f"{name} must be on {dev}")
+    return t.contiguous()
+
+
+def _same(t, dtype, name):
+    if t is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(dev, stream) -> int:
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream(dev).cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def ssd_chunk_scan_fwd(x, dt, A, B, C, D=None, init_state=None, chunk_len: int = 256, *,
+                       y=None, final_state=None, return_final_state: bool = True,
+                       workspace=None, stream=None) -> Tuple[object, object]:
+    """Chunked forward. x [b,T,H,P], dt [b,T,H], B/C [b,T,G,N] (fp32 or bf16,
+    all the same dtype), A/D [H] fp32, init_state [b,H,N,P] fp32 or None.
+    Returns (y [b,T,H,P] in x's dtype, final_state [b,H,N,P] fp32 or None)."""
+    return ssd_chunk_scan_fwd_timed(x, dt, A, B, C, D, init_state, chunk_len, y=y,
+                                    final_state=final_state, return_final_state=return_final_state,
+                                    workspace=workspace, stream=stream, stage_events=None)
+
+
+def ssd_chunk_scan_fwd_timed(x, dt, A, B, C, D=None, init_state=None, chunk_len: int = 256, *,
+                             y=None, final_state=None, return_final_state: bool = True,
+                             workspace=None, stream=None, stage_events=None):
+    """ssd_chunk_scan_fwd that also records 5 caller-created hipEvent_t handles
+    (ints) around its four kernels; stage_events=None skips them."""
+    import torch
+    dev = x.device
+    x = _dev(x, dev, "x")
+    dt, A, B, C = (_dev(v, dev, n) for v, n in ((dt, "dt"), (A, "A"), (B, "B"), (C, "C")))
+    D = _dev(D, dev, "D")
+    init_state = _dev(init_state, dev, "init_state")
+    code = _dtype_code(x)
+    for v, n in ((dt, "dt"), (B, "B"), (C, "C")):
+        _same(v, x.dtype, n)
+    for v, n in ((A, "A"), (D, "D"), (init_state, "init_state")):
+        _same(v, torch.float32, n)
+    b, T, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    if tuple(dt.shape) != (b, T, H) or tuple(B.shape) != (b, T, G, N) or tuple(C.shape) != (b, T, G, N):
+        raise ValueError("shape mismatch among x, dt, B, C")
+    if tuple(A.shape) != (H,) or (D is not None and tuple(D.shape) != (H,)):
+        raise ValueError("A and D must be [nheads]")
+    if init_state is not None and tuple(init_state.shape) != (b, H, N, P):
+        raise ValueError("init_state must be [b,H,N,P]")
+    if y is None:
+        y = torch.empty_like(x)
+    if final_state is None and return_final_state:
+        final_state = torch.empty((b, H, N, P), dtype=torch.float32, device=dev)
+    need = ssd_chunk_scan_fwd_workspace(b, T, H, P, N, G, chunk_len, code)
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    args = (_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(init_state), _ptr(y),
+            _ptr(final_state), b, T, H, P, N, G, chunk_len, code, _ptr(workspace),
+            workspace.numel() * workspace.element_size(), _stream(dev, stream))
+    if stage_events is None:
+        r = lib().ssd_chunk_scan_fwd(*args)
+    else:
+        if len(stage_events) != 5:
+            raise ValueError("stage_events needs 5 hipEvent_t handles")
+        ev = (ctypes.c_void_p * 5)(*[int(e) if e else None for e in stage_events])
+        r = lib().ssd_chunk_scan_fwd_timed(*args, ev)
+    if r != 0:
+        raise SSDError(r, "ssd_chunk_scan_fwd")
+    return y, final_state
+
+
+def ssd_state_update(state, x, dt, A, B, C, D=None, *, y=None, stream=None):
+    """One recurrent step, in place on state [b,H,N,P] fp32. x [b,H,P],
+    dt [b,H], B/C [b,G,N] (fp32 or bf16), A/D [H] fp32. Returns y [b,H,P]."""
+    import torch
+    dev = state.device
+    if not state.is_contiguous():
+        raise ValueError("state must be contiguous (it is updated in place)")
+    _same(state, torch.float32, "state")
+    x = _dev(x, dev, "x")
+    dt, A, B, C = (_dev(v, dev, n) for v, n in ((dt, "dt"), (A, "A"), (B, "B"), (C, "C")))
+    D = _dev(D, dev, "D")
+    code = _dtype_code(x)
+    for v, n in ((dt, "dt"), (B, "B"), (C, "C")):
+        _same(v, x.dtype, n)
+    b, H, P = x.shape
+    G, N = B.shape[1], B.shape[2]
+    if tuple(state.shape) != (b, H, N, P) or tuple(dt.shape) != (b, H) or tuple(C.shape) != (b, G, N):
+        raise ValueError("shape mismatch among state, x, dt, B, C")
+    if y is None:
+        y = torch.empty_like(x)
+    r = lib().ssd_state_update(_ptr(state), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                               _ptr(y), b, H, P, N, G, code, _stream(dev, stream))
+    if r != 0:
+        raise SSDError(r, "ssd_state_update")
+    return y

@@ -1,0 +1,184 @@
+// ssd_api.hip -- the C ABI: host-side argument checks, workspace layout and the
+// launch sequence. Every check runs before the first launch; on any error
+// nothing is launched or written.
+#include <stdint.h>
+
+#include "ssd_internal.h"
+
+using namespace ssd;
+
+namespace {
+
+bool is_chunk_ok(int q) { return q == 16 || q == 32 || q == 64 || q == 128 || q == 256; }
+
+bool misaligned(const void* p) { return p && (reinterpret_cast<uintptr_t>(p) & 15u); }
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+
+Range range_of(const void* p, size_t bytes) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  return Range{a, a + bytes};
+}
+
+bool overlaps(const void* a, size_t abytes, const void* b, size_t bbytes) {
+  if (!a || !b || !abytes || !bbytes) return false;
+  const Range ra = range_of(a, abytes), rb = range_of(b, bbytes);
+  return ra.lo < rb.hi && rb.lo < ra.hi;
+}
+
+size_t esize(ssd_dtype t) { return t == SSD_BF16 ? 2 : 4; }
+
+ssd_status check_dims(int batch, int seqlen, int H, int P, int N, int G) {
+  if (batch < 1 || seqlen < 1 || H < 1 || P < 1 || N < 1 || G < 1) return SSD_ERR_SHAPE;
+  if (H % G) return SSD_ERR_SHAPE;
+  if (P > SSD_MAX_HEADDIM || N > SSD_MAX_DSTATE) return SSD_ERR_SHAPE;
+  // grid limits: chunks and batch rows go to grid.y / grid.z
+  if (batch > 65535) return SSD_ERR_SHAPE;
+  return SSD_OK;
+}
+
+bool dtype_ok(ssd_dtype t) { return t == SSD_F32 || t == SSD_BF16; }
+
+FwdShape make_shape(int batch, int seqlen, int H, int P, int N, int G, int Q) {
+  FwdShape s;
+  s.b = batch; s.T = seqlen; s.H = H; s.P = P; s.N = N; s.G = G; s.Q = Q;
+  s.nc = (seqlen + Q - 1) / Q;
+  return s;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* ssd_status_string(ssd_status status) {
+  switch (status) {
+    case SSD_OK: return "ok";
+    case SSD_ERR_NULL: return "a required pointer is NULL";
+    case SSD_ERR_SHAPE: return "unsupported or inconsistent dimensions";
+    case SSD_ERR_DTYPE: return "unsupported dtype";
+    case SSD_ERR_CHUNK: return "chunk_len must be one of 16, 32, 64, 128, 256";
+    case SSD_ERR_WORKSPACE: return "workspace missing or too small";
+    case SSD_ERR_HIP: return "HIP kernel launch failed";
+    case SSD_ERR_ALIAS: return "an output overlaps an input";
+    case SSD_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+  }
+  return "unknown status";
+}
+
+size_t ssd_chunk_scan_fwd_workspace(int batch, int seqlen, int nheads, int headdim, int dstate,
+                                    int ngroups, int chunk_len, ssd_dtype dtype) {
+  if (!dtype_ok(dtype) || !is_chunk_ok(chunk_len)) return 0;
+  if (check_dims(batch, seqlen, nheads, headdim, dstate, ngroups) != SSD_OK) return 0;
+  const FwdShape s = make_shape(batch, seqlen, nheads, headdim, dstate, ngroups, chunk_len);
+  if (s.nc > 65535) return 0;
+  return ws_layout(s).total;
+}
+
+ssd_status ssd_chunk_scan_fwd_timed(const void* x, const void* dt, const float* A, const void* B,
+                                    const void* C, const float* D, const float* init_state,
+                                    void* y, float* final_state, int batch, int seqlen,
+                                    int nheads, int headdim, int dstate, int ngroups,
+                                    int chunk_len, ssd_dtype dtype, void* workspace,
+                                    size_t workspace_bytes, void* stream,
+                                    void* const* stage_events) {
+  if (!dtype_ok(dtype)) return SSD_ERR_DTYPE;
+  ssd_status st = check_dims(batch, seqlen, nheads, headdim, dstate, ngroups);
+  if (st != SSD_OK) return st;
+  if (!is_chunk_ok(chunk_len)) return SSD_ERR_CHUNK;
+  if (!x || !dt || !A || !B || !C || !y) return SSD_ERR_NULL;
+  if (!workspace) return SSD_ERR_WORKSPACE;
+  const void* ptrs[] = {x, dt, A, B, C, D, init_state, y, final_state, workspace};
+  for (const void* p : ptrs)
+    if (misaligned(p)) return SSD_ERR_ALIGN;
+
+  const FwdShape s = make_shape(batch, seqlen, nheads, headdim, dstate, ngroups, chunk_len);
+  if (s.nc > 65535) return SSD_ERR_SHAPE;
+  const WsLayout w = ws_layout(s);
+  if (workspace_bytes < w.total) return SSD_ERR_WORKSPACE;
+
+  const size_t e = esize(dtype);
+  const size_t tok = size_t(batch) * seqlen;
+  const size_t xb = tok * nheads * headdim * e, dtb = tok * nheads * e;
+  const size_t bcb = tok * ngroups * dstate * e, hb = size_t(nheads) * sizeof(float);
+  const size_t stb = size_t(batch) * nheads * dstate * headdim * sizeof(float);
+  struct In {
+    const void* p;
+    size_t n;
+  } ins[] = {{x, xb}, {dt, dtb}, {A, hb}, {B, bcb}, {C, bcb}, {D, hb}, {init_state, stb}};
+  for (const In& in : ins) {
+    if (overlaps(y, xb, in.p, in.n)) return SSD_ERR_ALIAS;
+    if (overlaps(workspace, w.total, in.p, in.n)) return SSD_ERR_ALIAS;
+    if (in.p != init_state && overlaps(final_state, stb, in.p, in.n)) return SSD_ERR_ALIAS;
+  }
+  if (overlaps(y, xb, final_state, stb) || overlaps(y, xb, workspace, w.total) ||
+      overlaps(final_state, stb, workspace, w.total))
+    return SSD_ERR_ALIAS;
+  if (final_state && init_state && final_state != static_cast<const void*>(init_state) &&
+      overlaps(final_state, stb, init_state, stb))
+    return SSD_ERR_ALIAS;
+
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  float* Acs = reinterpret_cast<float*>(ws + w.acs);
+  float* dtq = reinterpret_cast<float*>(ws + w.dtq);
+  float* S = reinterpret_cast<float*>(ws + w.st);
+
+  auto mark = [&](int i) {
+    if (!stage_events || !stage_events[i]) return true;
+    return hipEventRecord(static_cast<hipEvent_t>(stage_events[i]), hs) == hipSuccess;
+  };
+  if (!mark(0)) return SSD_ERR_HIP;
+  if (launch_chunk_cumsum(s, dtype, dt, A, Acs, dtq, hs) != hipSuccess) return SSD_ERR_HIP;
+  if (!mark(1)) return SSD_ERR_HIP;
+  if (launch_chunk_state(s, dtype, x, B, Acs, dtq, S, hs) != hipSuccess) return SSD_ERR_HIP;
+  if (!mark(2)) return SSD_ERR_HIP;
+  if (launch_state_passing(s, S, Acs, init_state, final_state, hs) != hipSuccess) return SSD_ERR_HIP;
+  if (!mark(3)) return SSD_ERR_HIP;
+  if (launch_chunk_scan(s, dtype, x, B, C, Acs, dtq, S, D, y, hs) != hipSuccess) return SSD_ERR_HIP;
+  if (!mark(4)) return SSD_ERR_HIP;
+  return SSD_OK;
+}
+
+ssd_status ssd_chunk_scan_fwd(const void* x, const void* dt, const float* A, const void* B,
+                              const void* C, const float* D, const float* init_state, void* y,
+                              float* final_state, int batch, int seqlen, int nheads, int headdim,
+                              int dstate, int ngroups, int chunk_len, ssd_dtype dtype,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  return ssd_chunk_scan_fwd_timed(x, dt, A, B, C, D, init_state, y, final_state, batch, seqlen,
+                                  nheads, headdim, dstate, ngroups, chunk_len, dtype, workspace,
+                                  workspace_bytes, stream, nullptr);
+}
+
+ssd_status ssd_state_update(float* state, const void* x, const void* dt, const float* A,
+                            const void* B, const void* C, const float* D, void* y, int batch,
+                            int nheads, int headdim, int dstate, int ngroups, ssd_dtype dtype,
+                            void* stream) {
+  if (!dtype_ok(dtype)) return SSD_ERR_DTYPE;
+  ssd_status st = check_dims(batch, 1, nheads, headdim, dstate, ngroups);
+  if (st != SSD_OK) return st;
+  if (!state || !x || !dt || !A || !B || !C || !y) return SSD_ERR_NULL;
+  const void* ptrs[] = {state, x, dt, A, B, C, D, y};
+  for (const void* p : ptrs)
+    if (misaligned(p)) return SSD_ERR_ALIGN;
+  const size_t e = esize(dtype);
+  const size_t xb = size_t(batch) * nheads * headdim * e, dtb = size_t(batch) * nheads * e;
+  const size_t bcb = size_t(batch) * ngroups * dstate * e, hb = size_t(nheads) * sizeof(float);
+  const size_t stb = size_t(batch) * nheads * dstate * headdim * sizeof(float);
+  struct In {
+    const void* p;
+    size_t n;
+  } ins[] = {{x, xb}, {dt, dtb}, {A, hb}, {B, bcb}, {C, bcb}, {D, hb}};
+  for (const In& in : ins) {
+    if (overlaps(y, xb, in.p, in.n)) return SSD_ERR_ALIAS;
+    if (overlaps(state, stb, in.p, in.n)) return SSD_ERR_ALIAS;
+  }
+  if (overlaps(y, xb, state, stb)) return SSD_ERR_ALIAS;
+  if (launch_state_update(dtype, state, x, dt, A, B, C, D, y, batch, nheads, headdim, dstate,
+                          ngroups, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return SSD_ERR_HIP;
+  return SSD_OK;
+}
+
+}  // extern "C"

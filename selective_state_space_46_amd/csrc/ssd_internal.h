@@ -1,0 +1,91 @@
+// ssd_internal.h -- private declarations shared by the HIP translation units of
+// libssd.so (device helpers, problem shape, workspace layout, launchers).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "ssd_api.h"
+
+namespace ssd {
+
+// Native clang vector types (usable with the nontemporal builtins, unlike the
+// HIP_vector_type structs).
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------------------
+// Element access. bf16 values travel as their raw 16-bit patterns (uint16_t);
+// the arithmetic is always fp32.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_to_f32(uint16_t v) { return __uint_as_float(uint32_t(v) << 16); }
+
+// fp32 -> bf16, round to nearest, ties to even (NaN stays NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return uint16_t((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return uint16_t(u >> 16);
+}
+
+__device__ __forceinline__ float to_f32(float v) { return v; }
+__device__ __forceinline__ float to_f32(uint16_t v) { return bf16_to_f32(v); }
+
+template <typename T> __device__ __forceinline__ T from_f32(float v);
+template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
+template <> __device__ __forceinline__ uint16_t from_f32<uint16_t>(float v) { return f32_to_bf16(v); }
+
+// exp(x) through the hardware base-2 exponential: exp(x) = 2^(x * log2(e)).
+__device__ __forceinline__ float exp_fast(float x) {
+  return __builtin_amdgcn_exp2f(x * 1.4426950408889634f);
+}
+
+// ---------------------------------------------------------------------------
+// Problem shape of one forward call.
+// ---------------------------------------------------------------------------
+struct FwdShape {
+  int b, T, H, P, N, G, Q, nc;  // batch, tokens, heads, headdim, dstate, groups, chunk, chunks
+};
+
+// Workspace layout (byte offsets, each 256-byte aligned):
+//   Acs [b, H, nc, Q] f32  cumulative dt*A inside each chunk (inclusive)
+//   dtq [b, H, nc, Q] f32  dt widened to fp32, 0 past the end of the sequence
+//   st  [b, nc, H, N, P] f32 chunk states; overwritten in place by the states
+//                           entering each chunk
+struct WsLayout {
+  size_t acs, dtq, st, total;
+};
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+inline WsLayout ws_layout(const FwdShape& s) {
+  WsLayout w;
+  const size_t row = size_t(s.b) * s.H * s.nc * s.Q * sizeof(float);
+  w.acs = 0;
+  w.dtq = align_up(w.acs + row, 256);
+  w.st = align_up(w.dtq + row, 256);
+  w.total = align_up(w.st + size_t(s.b) * s.nc * s.H * s.N * s.P * sizeof(float), 256);
+  return w;
+}
+
+// ---------------------------------------------------------------------------
+// Launchers (one translation unit each). All return the launch status.
+// ---------------------------------------------------------------------------
+hipError_t launch_chunk_cumsum(const FwdShape& s, ssd_dtype dt_type, const void* dt, const float* A,
+                               float* Acs, float* dtq, hipStream_t st);
+
+hipError_t launch_chunk_state(const FwdShape& s, ssd_dtype type, const void* x, const void* B,
+                              const float* Acs, const float* dtq, float* S, hipStream_t st);
+
+hipError_t launch_state_passing(const FwdShape& s, float* S, const float* Acs, const float* init,
+                                float* final_state, hipStream_t st);
+
+hipError_t launch_chunk_scan(const FwdShape& s, ssd_dtype type, const void* x, const void* B,
+                             const void* C, const float* Acs, const float* dtq, const float* Hst,
+                             const float* D, void* y, hipStream_t st);
+
+hipError_t launch_state_update(ssd_dtype type, float* state, const void* x, const void* dt,
+                               const float* A, const void* B, const void* C, const float* D, void* y,
+                               int batch, int H, int P, int N, int G, hipStream_t st);
+
+}  // namespace ssd

@@ -1,0 +1,60 @@
+"""Helpers shared by the GPU tests: move seeded inputs to the device, run the
+library through its binding, sample columns for full-size parity."""
+from __future__ import annotations
+
+import numpy as np
+
+import oracle
+import workloads
+
+
+def torch_dtype(name: str):
+    import torch
+    return {"f32": torch.float32, "bf16": torch.bfloat16}[name]
+
+
+def dev(a: np.ndarray, dtype: str = "f32"):
+    """float32 carrier -> device tensor of `dtype` (exact: carriers already hold
+    representable values)."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+    return t.to(torch_dtype(dtype)) if dtype != "f32" else t
+
+
+def host(t) -> np.ndarray:
+    import torch
+    return t.detach().to(torch.float64).cpu().numpy()
+
+
+def gpu_fwd(inp: dict, dtype: str, chunk_len: int, with_final: bool = True, init_in_place=False):
+    """Run ssd_chunk_scan_fwd; returns (y, final) as float64 numpy arrays."""
+    import torch
+    import selective_state_space_46_amd as ssd
+    x, dt, B, C = (dev(inp[k], dtype) for k in ("x", "dt", "B", "C"))
+    A, D = dev(inp["A"]), (dev(inp["D"]) if inp.get("D") is not None else None)
+    init = dev(inp["init"]) if inp.get("init") is not None else None
+    final = None
+    if init_in_place and init is not None:
+        final = init
+    y, fin = ssd.ssd_chunk_scan_fwd(x, dt, A, B, C, D, init, chunk_len, final_state=final,
+                                    return_final_state=with_final)
+    torch.cuda.synchronize()
+    return host(y), (host(fin) if fin is not None else None)
+
+
+def sample_columns(b, H, P, n, seed):
+    rng = np.random.default_rng(seed)
+    cols = {(0, 0, 0), (b - 1, H - 1, P - 1)}
+    while len(cols) < n:
+        cols.add((int(rng.integers(b)), int(rng.integers(H)), int(rng.integers(P))))
+    return sorted(cols)
+
+
+def columns_of(y, fin, cols):
+    """Gather (y[b,:,h,p], fin[b,h,:,p]) for the sampled columns."""
+    yc = np.stack([y[b, :, h, p] for b, h, p in cols])
+    fc = np.stack([fin[b, h, :, p] for b, h, p in cols]) if fin is not None else None
+    return yc, fc
+
+
+rel_l2 = oracle.rel_l2

@@ -1,0 +1,118 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every entry point include/ssd_api.h declares, and rejects bad arguments with
+the documented status codes before launching anything."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import selective_state_space_46_amd as ssd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 1 << 20          # a non-NULL, 16-byte aligned address that is never dereferenced
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(ssd.lib_path()):
+        from selective_state_space_46_amd import build
+        build.build()
+    return ssd.lib()
+
+
+def declared_symbols():
+    text = open(os.path.join(ROOT, "include", "ssd_api.h")).read()
+    return re.findall(r"SSD_API\s+[\w\s\*]*?\b(ssd_\w+)\s*\(", text)
+
+
+def test_header_declares_the_entry_points():
+    assert set(declared_symbols()) == {"ssd_chunk_scan_fwd_workspace", "ssd_chunk_scan_fwd",
+                                       "ssd_chunk_scan_fwd_timed", "ssd_state_update",
+                                       "ssd_status_string"}
+
+
+def test_library_exports_every_declared_symbol(L):
+    for name in declared_symbols():
+        assert hasattr(L, name), name
+
+
+def test_status_strings(L):
+    for code in range(9):
+        s = ssd.ssd_status_string(code)
+        assert s and s != "unknown status"
+    assert ssd.ssd_status_string(99) == "unknown status"
+
+
+def ws(b, T, H, P, N, G, Q, dt=ssd.SSD_BF16):
+    return ssd.ssd_chunk_scan_fwd_workspace(b, T, H, P, N, G, Q, dt)
+
+
+def test_workspace_query():
+    def expect(b, T, H, P, N, Q):
+        nc = -(-T // Q)
+        up = lambda v: -(-v // 256) * 256
+        row = up(b * H * nc * Q * 4)
+        return up(2 * row + b * nc * H * N * P * 4)
+    for args in [(8, 2048, 24, 64, 128, 1, 256), (1, 131072, 24, 64, 256, 1, 256), (1, 1, 1, 1, 1, 1, 16),
+                 (2, 100, 4, 3, 5, 2, 32)]:
+        b, T, H, P, N, G, Q = args
+        assert ws(*args) == expect(b, T, H, P, N, Q)
+    assert ws(1, 256, 3, 16, 16, 2, 64) == 0          # H % G != 0
+    assert ws(1, 256, 2, 16, 16, 1, 48) == 0          # chunk
+    assert ws(1, 0, 2, 16, 16, 1, 64) == 0            # T = 0
+    assert ws(1, 256, 2, 257, 16, 1, 64) == 0         # headdim too large
+    assert ws(1, 256, 2, 16, 16, 1, 64, dt=5) == 0    # dtype
+
+
+def fwd(L, **kw):
+    a = dict(x=FAKE, dt=FAKE + 0x100000, A=FAKE + 0x200000, B=FAKE + 0x300000, C=FAKE + 0x400000,
+             D=None, init=None, y=FAKE + 0x500000, fin=None, b=1, T=64, H=2, P=16, N=16, G=1, Q=64,
+             dtype=0, ws=FAKE + 0x600000, nbytes=1 << 30, stream=None)
+    a.update(kw)
+    return L.ssd_chunk_scan_fwd(a["x"], a["dt"], a["A"], a["B"], a["C"], a["D"], a["init"], a["y"],
+                                a["fin"], a["b"], a["T"], a["H"], a["P"], a["N"], a["G"], a["Q"],
+                                a["dtype"], a["ws"], a["nbytes"], a["stream"])
+
+
+def test_forward_argument_errors(L):
+    assert fwd(L, dtype=2) == 3
+    assert fwd(L, T=0) == 2
+    assert fwd(L, b=0) == 2
+    assert fwd(L, H=3, G=2) == 2
+    assert fwd(L, P=300) == 2
+    assert fwd(L, N=300) == 2
+    assert fwd(L, Q=100) == 4
+    assert fwd(L, Q=512) == 4
+    assert fwd(L, T=16 * 65536, Q=16) == 2          # more chunks than the grid allows
+    for k in ("x", "dt", "A", "B", "C", "y"):
+        assert fwd(L, **{k: None}) == 1, k
+    assert fwd(L, ws=None) == 5
+    assert fwd(L, nbytes=100) == 5
+    assert fwd(L, x=FAKE + 8) == 8
+    assert fwd(L, init=FAKE + 0x700004) == 8
+    assert fwd(L, y=FAKE) == 7                        # y over x
+    assert fwd(L, y=FAKE + 0x600000) == 7             # y over the workspace
+    assert fwd(L, fin=FAKE + 0x300000) == 7           # final over B
+    assert fwd(L, init=FAKE + 0x700000, fin=FAKE + 0x700010) == 7   # partial overlap
+    assert fwd(L, ws=FAKE + 0x100000) == 7            # workspace over dt
+
+
+def upd(L, **kw):
+    a = dict(state=FAKE, x=FAKE + 0x100000, dt=FAKE + 0x200000, A=FAKE + 0x300000, B=FAKE + 0x400000,
+             C=FAKE + 0x500000, D=None, y=FAKE + 0x600000, b=2, H=4, P=16, N=16, G=2, dtype=1,
+             stream=None)
+    a.update(kw)
+    return L.ssd_state_update(a["state"], a["x"], a["dt"], a["A"], a["B"], a["C"], a["D"], a["y"],
+                              a["b"], a["H"], a["P"], a["N"], a["G"], a["dtype"], a["stream"])
+
+
+def test_decode_argument_errors(L):
+    assert upd(L, dtype=7) == 3
+    assert upd(L, H=3) == 2
+    assert upd(L, N=0) == 2
+    for k in ("state", "x", "dt", "A", "B", "C", "y"):
+        assert upd(L, **{k: None}) == 1, k
+    assert upd(L, y=FAKE + 0x100000) == 7             # y over x
+    assert upd(L, state=FAKE + 0x600000) == 7         # state over y
+    assert upd(L, x=FAKE + 0x100002) == 8

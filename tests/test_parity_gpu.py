@@ -1,0 +1,242 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Bar: relative L2 error (||gpu - oracle||_2 / ||oracle||_2 over the whole
+tensor, or over the sampled columns at full size) <= 1e-5 on the fp32 path
+and <= 1e-2 on y and final_state on the bf16 path.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from ssd_testlib import columns_of, dev, gpu_fwd, host, rel_l2, sample_columns
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-5, "bf16": 1e-2}
+
+
+def _check_full(w, inp, chunk_len=None, init_in_place=False):
+    q = chunk_len or w.chunk_len
+    y, fin = gpu_fwd(inp, w.dtype, q, init_in_place=init_in_place)
+    y_ref, fin_ref = oracle.ssd_fwd(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"],
+                                    inp["init"])
+    ey, ef = rel_l2(y, y_ref), rel_l2(fin, fin_ref)
+    print(f"[{w.name} Q={q}] rel_l2 y={ey:.3e} final={ef:.3e}", flush=True)
+    assert ey <= TOL[w.dtype] and ef <= TOL[w.dtype], (ey, ef)
+    assert np.all(np.isfinite(y))
+    return y, fin
+
+
+# ---------------------------------------------------------------- small cases
+
+def test_tiny_f32_workload():
+    w = workloads.TINY_F32
+    _check_full(w, workloads.make_fwd_inputs(w))
+
+
+@pytest.mark.parametrize("q", [16, 32, 64, 128, 256])
+def test_tiny_f32_chunk_len_invariance(q):
+    w = workloads.TINY_F32
+    _check_full(w, workloads.make_fwd_inputs(w), chunk_len=q)
+
+
+@pytest.mark.parametrize("T", [1, 15, 63, 64, 65, 200, 257])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_ragged_lengths(T, dtype):
+    w = workloads.with_shape(workloads.TINY_F32, batch=2, seqlen=T, nheads=4, ngroups=2,
+                             dtype=dtype, init="normal0.1", seed=900 + T)
+    _check_full(w, workloads.make_fwd_inputs(w))
+
+
+@pytest.mark.parametrize("P,N,G,H", [(16, 16, 1, 2), (8, 24, 2, 4), (64, 128, 1, 3), (32, 64, 4, 8),
+                                     (3, 5, 1, 2), (128, 32, 1, 2), (64, 256, 1, 2)])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_shapes(P, N, G, H, dtype):
+    w = workloads.with_shape(workloads.TINY_F32, batch=2, seqlen=300, nheads=H, headdim=P,
+                             dstate=N, ngroups=G, chunk_len=64, dtype=dtype, init="normal0.1",
+                             seed=1000 + P + N)
+    _check_full(w, workloads.make_fwd_inputs(w))
+
+
+@pytest.mark.parametrize("q", [32, 64, 128, 256])
+def test_bf16_large_shape_small_batch(q):
+    """The 130M-layer shapes (H, P, N) on a short sequence that several chunks and
+    a ragged tail span, checked on every element."""
+    w = workloads.with_shape(workloads.MAMBA2_130M, batch=2, seqlen=3 * 256 + 77, init="normal0.1",
+                             chunk_len=q, seed=1200 + q)
+    _check_full(w, workloads.make_fwd_inputs(w))
+
+
+def test_long_context_shape_short_sequence():
+    w = workloads.with_shape(workloads.LONG_128K, seqlen=4 * 256 + 3, seed=1300)
+    _check_full(w, workloads.make_fwd_inputs(w))
+
+
+def test_init_state_in_place():
+    w = workloads.with_shape(workloads.TINY_F32, batch=2, seqlen=129, init="normal0.1", seed=1400)
+    _check_full(w, workloads.make_fwd_inputs(w), init_in_place=True)
+
+
+def test_no_D_no_final():
+    import selective_state_space_46_amd as ssd
+    import torch
+    w = workloads.with_shape(workloads.TINY_F32, seqlen=100, seed=1500)
+    inp = workloads.make_fwd_inputs(w)
+    y, fin = ssd.ssd_chunk_scan_fwd(dev(inp["x"]), dev(inp["dt"]), dev(inp["A"]), dev(inp["B"]),
+                                    dev(inp["C"]), None, None, 64, return_final_state=False)
+    torch.cuda.synchronize()
+    assert fin is None
+    y_ref, _ = oracle.ssd_fwd(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], None, None)
+    assert rel_l2(host(y), y_ref) <= 1e-5
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_split_and_resume(dtype):
+    """fwd(T1) then fwd(T2, init = final of the first) equals fwd(T1 + T2)."""
+    w = workloads.with_shape(workloads.MAMBA2_130M if dtype == "bf16" else workloads.TINY_F32,
+                             batch=2, seqlen=700, init="normal0.1", chunk_len=64, seed=1600)
+    inp = workloads.make_fwd_inputs(w)
+    y, fin = gpu_fwd(inp, dtype, 64)
+    T1 = 300
+    a = {k: (v[:, :T1] if k in ("x", "dt", "B", "C") else v) for k, v in inp.items()}
+    ya, fa = gpu_fwd(a, dtype, 64)
+    bb = {k: (v[:, T1:] if k in ("x", "dt", "B", "C") else v) for k, v in inp.items()}
+    bb["init"] = fa.astype(np.float32)
+    yb, fb = gpu_fwd(bb, dtype, 64)
+    assert rel_l2(np.concatenate([ya, yb], axis=1), y) <= TOL[dtype]
+    assert rel_l2(fb, fin) <= TOL[dtype]
+
+
+def test_deterministic():
+    w = workloads.with_shape(workloads.MAMBA2_130M, batch=2, seqlen=1000, seed=1700)
+    inp = workloads.make_fwd_inputs(w)
+    y1, f1 = gpu_fwd(inp, "bf16", 256)
+    y2, f2 = gpu_fwd(inp, "bf16", 256)
+    np.testing.assert_array_equal(y1, y2)
+    np.testing.assert_array_equal(f1, f2)
+
+
+# ---------------------------------------------------------------- decode
+
+def _gpu_decode(inp, dtype, steps=None):
+    import torch
+    import selective_state_space_46_amd as ssd
+    state = dev(inp["state"])
+    A, D = dev(inp["A"]), dev(inp["D"])
+    S = inp["xs"].shape[0] if steps is None else steps
+    ys = []
+    for s in range(S):
+        y = ssd.ssd_state_update(state, dev(inp["xs"][s], dtype), dev(inp["dts"][s], dtype), A,
+                                 dev(inp["Bs"][s], dtype), dev(inp["Cs"][s], dtype), D)
+        ys.append(y)
+    torch.cuda.synchronize()
+    return np.stack([host(y) for y in ys]), host(state)
+
+
+@pytest.mark.parametrize("dtype,P,N,G,H", [("f32", 64, 128, 2, 4), ("bf16", 64, 128, 8, 16),
+                                           ("f32", 6, 10, 1, 3), ("bf16", 16, 16, 1, 2)])
+def test_decode_small(dtype, P, N, G, H):
+    w = workloads.DecodeWorkload("dec", 3, H, P, N, G, 5, dtype, seed=1800 + P)
+    inp = workloads.make_decode_inputs(w)
+    ys, st = _gpu_decode(inp, dtype)
+    ys_ref, st_ref = oracle.ssd_decode(inp["state"], inp["xs"], inp["dts"], inp["A"], inp["Bs"],
+                                       inp["Cs"], inp["D"])
+    ey, es = rel_l2(ys, ys_ref), rel_l2(st, st_ref)
+    print(f"[decode {dtype} P{P} N{N}] y={ey:.3e} state={es:.3e}", flush=True)
+    assert ey <= TOL[dtype] and es <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_forward_equals_chained_decode(dtype):
+    """Parallel (chunked) form and recurrent form give the same result."""
+    w = workloads.with_shape(workloads.TINY_F32, batch=2, seqlen=70, nheads=4, headdim=16,
+                             dstate=32, ngroups=2, init="normal0.1", dtype=dtype, chunk_len=32,
+                             seed=1900)
+    inp = workloads.make_fwd_inputs(w)
+    y, fin = gpu_fwd(inp, dtype, 32)
+    dinp = dict(state=inp["init"], xs=inp["x"].transpose(1, 0, 2, 3), dts=inp["dt"].transpose(1, 0, 2),
+                A=inp["A"], Bs=inp["B"].transpose(1, 0, 2, 3), Cs=inp["C"].transpose(1, 0, 2, 3),
+                D=inp["D"])
+    ys, st = _gpu_decode(dinp, dtype)
+    assert rel_l2(ys.transpose(1, 0, 2, 3), y) <= TOL[dtype]
+    assert rel_l2(st, fin) <= TOL[dtype]
+
+
+# ---------------------------------------------------------------- full sizes
+
+@pytest.mark.slow
+def test_mamba2_130m_full():
+    w = workloads.MAMBA2_130M
+    _check_full(w, workloads.make_fwd_inputs(w))
+
+
+def _check_sampled(w, ncols=48):
+    inp = workloads.make_fwd_inputs(w)
+    y, fin = gpu_fwd(inp, w.dtype, w.chunk_len)
+    cols = sample_columns(w.batch, w.nheads, w.headdim, ncols, seed=w.seed)
+    yc_ref, fc_ref = oracle.ssd_fwd_columns(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"],
+                                            inp["D"], inp["init"], cols)
+    yc, fc = columns_of(y, fin, cols)
+    ey, ef = rel_l2(yc, yc_ref), rel_l2(fc, fc_ref)
+    print(f"[{w.name}] sampled {len(cols)} columns: y={ey:.3e} final={ef:.3e}", flush=True)
+    assert ey <= TOL[w.dtype] and ef <= TOL[w.dtype]
+    assert np.all(np.isfinite(y))
+
+
+@pytest.mark.slow
+def test_mamba2_2p7b_sampled():
+    _check_sampled(workloads.MAMBA2_2P7B)
+
+
+@pytest.mark.slow
+def test_long_context_sampled():
+    _check_sampled(workloads.LONG_128K, ncols=24)
+
+
+@pytest.mark.slow
+def test_decode_full_size_sampled_heads():
+    w = workloads.DECODE_B256
+    inp = workloads.make_decode_inputs(w)
+    ys, st = _gpu_decode(inp, w.dtype)
+    rng = np.random.default_rng(5)
+    heads = sorted({(0, 0), (w.batch - 1, w.nheads - 1)} |
+                   {(int(rng.integers(w.batch)), int(rng.integers(w.nheads))) for _ in range(40)})
+    ys_ref, st_ref = oracle.ssd_decode(inp["state"], inp["xs"], inp["dts"], inp["A"], inp["Bs"],
+                                       inp["Cs"], inp["D"], heads=heads)
+    yg = np.stack([ys[:, b, h] for b, h in heads])
+    sg = np.stack([st[b, h] for b, h in heads])
+    ey, es = rel_l2(yg, ys_ref), rel_l2(sg, st_ref)
+    print(f"[{w.name}] {len(heads)} heads: y={ey:.3e} state={es:.3e}", flush=True)
+    assert ey <= 1e-2 and es <= 1e-2
+
+
+# ---------------------------------------------------------------- errors on device tensors
+
+def test_errors_leave_outputs_untouched():
+    import torch
+    import selective_state_space_46_amd as ssd
+    L = ssd.lib()
+    x = torch.zeros(1, 64, 2, 16, device="cuda")
+    y = torch.full_like(x, 7.0)
+    dt = torch.zeros(1, 64, 2, device="cuda")
+    A = torch.zeros(2, device="cuda")
+    B = torch.zeros(1, 64, 1, 16, device="cuda")
+    ws = torch.empty(1 << 20, dtype=torch.uint8, device="cuda")
+    s = torch.cuda.current_stream().cuda_stream
+    args = lambda **k: dict(dict(x=x.data_ptr(), y=y.data_ptr(), q=64, ws=ws.data_ptr(), nbytes=ws.numel()), **k)
+
+    def call(a):
+        return L.ssd_chunk_scan_fwd(a["x"], dt.data_ptr(), A.data_ptr(), B.data_ptr(), B.data_ptr(),
+                                    None, None, a["y"], None, 1, 64, 2, 16, 16, 1, a["q"], 0,
+                                    a["ws"], a["nbytes"], s)
+
+    assert call(args(q=48)) == 4
+    assert call(args(nbytes=16)) == 5
+    assert call(args(y=x.data_ptr())) == 7             # y aliases x
+    assert call(args(x=x.data_ptr() + 4)) == 8         # misaligned
+    torch.cuda.synchronize()
+    assert torch.all(y == 7.0)                        # failed calls wrote nothing
+    assert call(args()) == 0
+    torch.cuda.synchronize()
+    assert torch.all(y == 0)                          # the good call wrote y (x = 0, so y = 0)
