@@ -17,11 +17,6 @@
 #include "ssd_internal.h"
 
 namespace ssd {
-
-hipError_t launch_chunk_scan_mfma(const FwdShape& s, const void* x, const void* B, const void* C,
-                                  const float* Acs, const float* dtq, const float* Hst,
-                                  const float* D, void* y, hipStream_t st, bool* launched);
-
 namespace {
 
 constexpr int kThreads = 256;
@@ -76,7 +71,7 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_generic(
     float acc = 0.f;
     for (int s = 0; s <= l; ++s) acc += sc[i][s] * to_f32(x[((size_t(b) * T + t0 + s) * H + h) * P + p]);
     float accH = 0.f;
-    for (int n = 0; n < N; ++n) accH += sC[i][n] * Hc[size_t(n) * P + p];
+    for (int n = 0; n < N; ++n) accH += sC[i][n] * Hc[size_t(p) * N + n];
     const size_t xi = ((size_t(b) * T + t0 + l) * H + h) * P + p;
     const float out = acc + expf(Acs[arow + l]) * accH + Dh * to_f32(x[xi]);
     y[xi] = from_f32<In>(out);
@@ -85,14 +80,11 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_generic(
 
 }  // namespace
 
-hipError_t launch_chunk_scan(const FwdShape& s, ssd_dtype type, const void* x, const void* B,
-                             const void* C, const float* Acs, const float* dtq, const float* Hst,
-                             const float* D, void* y, hipStream_t st) {
-  if (type == SSD_BF16) {
-    bool launched = false;
-    hipError_t e = launch_chunk_scan_mfma(s, x, B, C, Acs, dtq, Hst, D, y, st, &launched);
-    if (launched || e != hipSuccess) return e;
-  }
+hipError_t launch_chunk_scan(const FwdShape& s, ssd_dtype type, bool mfma, const void* x,
+                             const void* B, const void* C, const float* Acs, const float* dtq,
+                             const float* Hst, const uint16_t* Hb, const float* D, void* y,
+                             hipStream_t st) {
+  if (mfma) return launch_chunk_scan_mfma(s, x, B, C, Acs, dtq, Hb, D, y, st);
   dim3 grid(s.H * (s.Q / kRows), s.nc, s.b);
   if (type == SSD_BF16)
     hipLaunchKernelGGL(chunk_scan_generic<uint16_t>, grid, dim3(kThreads), 0, st,

@@ -2,6 +2,8 @@
 //
 //   S_c[n, p] = sum_{l in chunk c} B_l[n] * exp(Acs_{Q-1} - Acs_l) * dt_l * x_l[p]
 //
+// stored transposed, S_c^T [p][n] (n fastest), in [b, nc, H, P, N].
+//
 // i.e. B^T (N x Q) times diag(decay-to-chunk-end * dt) X (Q x P): the
 // final-state row of the semiseparable matrix restricted to one chunk
 // (h_T = sum_j abar_{T:j} bbar_j x_j^T with bbar_j = dt_j B_j; youngju.dev
@@ -15,10 +17,6 @@
 #include "ssd_internal.h"
 
 namespace ssd {
-
-hipError_t launch_chunk_state_mfma(const FwdShape& s, const void* x, const void* B, const float* Acs,
-                                   const float* dtq, float* S, hipStream_t st, bool* launched);
-
 namespace {
 
 constexpr int kThreads = 256;
@@ -69,7 +67,7 @@ __global__ __launch_bounds__(kThreads) void chunk_state_generic(
     for (int k = 0; k < kRows * SSD_MAX_HEADDIM / kThreads; ++k) {
       const int e = tid + k * kThreads;
       if (e < nout) {
-        const int n = e / P, p = e % P;
+        const int n = e % kRows, p = e / kRows;
         float a = acc[k];
 #pragma unroll
         for (int i = 0; i < kTok; ++i) a += sB[i][n] * sX[i][p];
@@ -82,21 +80,18 @@ __global__ __launch_bounds__(kThreads) void chunk_state_generic(
   for (int k = 0; k < kRows * SSD_MAX_HEADDIM / kThreads; ++k) {
     const int e = tid + k * kThreads;
     if (e < nout) {
-      const int n = n0 + e / P, p = e % P;
-      if (n < N) out[size_t(n) * P + p] = acc[k];
+      const int n = n0 + e % kRows, p = e / kRows;
+      if (n < N) out[size_t(p) * N + n] = acc[k];
     }
   }
 }
 
 }  // namespace
 
-hipError_t launch_chunk_state(const FwdShape& s, ssd_dtype type, const void* x, const void* B,
-                              const float* Acs, const float* dtq, float* S, hipStream_t st) {
-  if (type == SSD_BF16) {
-    bool launched = false;
-    hipError_t e = launch_chunk_state_mfma(s, x, B, Acs, dtq, S, st, &launched);
-    if (launched || e != hipSuccess) return e;
-  }
+hipError_t launch_chunk_state(const FwdShape& s, ssd_dtype type, bool mfma, const void* x,
+                              const void* B, const float* Acs, const float* dtq, float* S,
+                              hipStream_t st) {
+  if (mfma) return launch_chunk_state_mfma(s, x, B, Acs, dtq, S, st);
   const int ntn = (s.N + kRows - 1) / kRows;
   dim3 grid(s.H * ntn, s.nc, s.b);
   if (type == SSD_BF16)

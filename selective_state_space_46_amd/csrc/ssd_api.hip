@@ -73,7 +73,7 @@ size_t ssd_chunk_scan_fwd_workspace(int batch, int seqlen, int nheads, int headd
   if (check_dims(batch, seqlen, nheads, headdim, dstate, ngroups) != SSD_OK) return 0;
   const FwdShape s = make_shape(batch, seqlen, nheads, headdim, dstate, ngroups, chunk_len);
   if (s.nc > 65535) return 0;
-  return ws_layout(s).total;
+  return ws_layout(s, use_mfma_path(s, dtype)).total;
 }
 
 ssd_status ssd_chunk_scan_fwd_timed(const void* x, const void* dt, const float* A, const void* B,
@@ -95,7 +95,8 @@ ssd_status ssd_chunk_scan_fwd_timed(const void* x, const void* dt, const float* 
 
   const FwdShape s = make_shape(batch, seqlen, nheads, headdim, dstate, ngroups, chunk_len);
   if (s.nc > 65535) return SSD_ERR_SHAPE;
-  const WsLayout w = ws_layout(s);
+  const bool mfma = use_mfma_path(s, dtype);
+  const WsLayout w = ws_layout(s, mfma);
   if (workspace_bytes < w.total) return SSD_ERR_WORKSPACE;
 
   const size_t e = esize(dtype);
@@ -124,6 +125,7 @@ ssd_status ssd_chunk_scan_fwd_timed(const void* x, const void* dt, const float* 
   float* Acs = reinterpret_cast<float*>(ws + w.acs);
   float* dtq = reinterpret_cast<float*>(ws + w.dtq);
   float* S = reinterpret_cast<float*>(ws + w.st);
+  uint16_t* Hb = mfma ? reinterpret_cast<uint16_t*>(ws + w.hb) : nullptr;
 
   auto mark = [&](int i) {
     if (!stage_events || !stage_events[i]) return true;
@@ -132,11 +134,13 @@ ssd_status ssd_chunk_scan_fwd_timed(const void* x, const void* dt, const float* 
   if (!mark(0)) return SSD_ERR_HIP;
   if (launch_chunk_cumsum(s, dtype, dt, A, Acs, dtq, hs) != hipSuccess) return SSD_ERR_HIP;
   if (!mark(1)) return SSD_ERR_HIP;
-  if (launch_chunk_state(s, dtype, x, B, Acs, dtq, S, hs) != hipSuccess) return SSD_ERR_HIP;
+  if (launch_chunk_state(s, dtype, mfma, x, B, Acs, dtq, S, hs) != hipSuccess) return SSD_ERR_HIP;
   if (!mark(2)) return SSD_ERR_HIP;
-  if (launch_state_passing(s, S, Acs, init_state, final_state, hs) != hipSuccess) return SSD_ERR_HIP;
+  if (launch_state_passing(s, S, Hb, Acs, init_state, final_state, hs) != hipSuccess)
+    return SSD_ERR_HIP;
   if (!mark(3)) return SSD_ERR_HIP;
-  if (launch_chunk_scan(s, dtype, x, B, C, Acs, dtq, S, D, y, hs) != hipSuccess) return SSD_ERR_HIP;
+  if (launch_chunk_scan(s, dtype, mfma, x, B, C, Acs, dtq, S, Hb, D, y, hs) != hipSuccess)
+    return SSD_ERR_HIP;
   if (!mark(4)) return SSD_ERR_HIP;
   return SSD_OK;
 }

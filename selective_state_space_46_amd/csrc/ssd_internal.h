@@ -47,25 +47,48 @@ struct FwdShape {
   int b, T, H, P, N, G, Q, nc;  // batch, tokens, heads, headdim, dstate, groups, chunk, chunks
 };
 
+// Which kernels a forward call uses. The bf16 MFMA kernels cover dstate and
+// headdim that are multiples of 32 (dstate in {32, 64, 128, 256}, headdim in
+// {32, 64, 128}) and chunk_len >= 32; every other shape and the fp32 path run
+// the generic fp32-FMA kernels.
+inline bool use_mfma_path(const FwdShape& s, ssd_dtype t) {
+  const bool n_ok = s.N == 32 || s.N == 64 || s.N == 128 || s.N == 256;
+  const bool p_ok = s.P == 32 || s.P == 64 || s.P == 128;
+  return t == SSD_BF16 && n_ok && p_ok && s.Q >= 32;
+}
+
 // Workspace layout (byte offsets, each 256-byte aligned):
-//   Acs [b, H, nc, Q] f32  cumulative dt*A inside each chunk (inclusive)
-//   dtq [b, H, nc, Q] f32  dt widened to fp32, 0 past the end of the sequence
-//   st  [b, nc, H, N, P] f32 chunk states; overwritten in place by the states
-//                           entering each chunk
+//   acs [b, H, nc, Q] f32    cumulative dt*A inside each chunk (inclusive)
+//   dtq [b, H, nc, Q] f32    dt widened to fp32, 0 past the end of the sequence
+//   st  [b, nc, H, P, N] f32 chunk states, stored transposed (n fastest); on
+//                            the generic path overwritten in place by the
+//                            states entering each chunk
+//   hb  [b, nc, H, P, N] bf16 states entering each chunk (MFMA path only)
 struct WsLayout {
-  size_t acs, dtq, st, total;
+  size_t acs, dtq, st, hb, total;
 };
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-inline WsLayout ws_layout(const FwdShape& s) {
+inline WsLayout ws_layout(const FwdShape& s, bool mfma) {
   WsLayout w;
   const size_t row = size_t(s.b) * s.H * s.nc * s.Q * sizeof(float);
+  const size_t nst = size_t(s.b) * s.nc * s.H * s.N * s.P;
   w.acs = 0;
   w.dtq = align_up(w.acs + row, 256);
   w.st = align_up(w.dtq + row, 256);
-  w.total = align_up(w.st + size_t(s.b) * s.nc * s.H * s.N * s.P * sizeof(float), 256);
+  w.hb = align_up(w.st + nst * sizeof(float), 256);
+  w.total = mfma ? align_up(w.hb + nst * sizeof(uint16_t), 256) : w.hb;
   return w;
+}
+
+// XCD-aware block order: the hardware hands consecutive work-groups to the 8
+// XCDs round-robin, so block id k runs on XCD k % 8. Renumbering blocks so that
+// each XCD receives one contiguous range of logical ids keeps logical
+// neighbours (which share B/C rows) inside one XCD's L2.
+__device__ __forceinline__ int xcd_swizzle(int bid, int nblocks) {
+  if (nblocks % 8) return bid;
+  return (bid % 8) * (nblocks / 8) + bid / 8;
 }
 
 // ---------------------------------------------------------------------------
@@ -74,15 +97,26 @@ inline WsLayout ws_layout(const FwdShape& s) {
 hipError_t launch_chunk_cumsum(const FwdShape& s, ssd_dtype dt_type, const void* dt, const float* A,
                                float* Acs, float* dtq, hipStream_t st);
 
-hipError_t launch_chunk_state(const FwdShape& s, ssd_dtype type, const void* x, const void* B,
-                              const float* Acs, const float* dtq, float* S, hipStream_t st);
+// S: chunk states [b, nc, H, P, N] f32.
+hipError_t launch_chunk_state(const FwdShape& s, ssd_dtype type, bool mfma, const void* x,
+                              const void* B, const float* Acs, const float* dtq, float* S,
+                              hipStream_t st);
+hipError_t launch_chunk_state_mfma(const FwdShape& s, const void* x, const void* B,
+                                   const float* Acs, const float* dtq, float* S, hipStream_t st);
 
-hipError_t launch_state_passing(const FwdShape& s, float* S, const float* Acs, const float* init,
-                                float* final_state, hipStream_t st);
+// Hb == nullptr: states entering each chunk overwrite S in place (fp32);
+// otherwise they are written to Hb as bf16 and S is left as it was.
+hipError_t launch_state_passing(const FwdShape& s, float* S, uint16_t* Hb, const float* Acs,
+                                const float* init, float* final_state, hipStream_t st);
 
-hipError_t launch_chunk_scan(const FwdShape& s, ssd_dtype type, const void* x, const void* B,
-                             const void* C, const float* Acs, const float* dtq, const float* Hst,
-                             const float* D, void* y, hipStream_t st);
+// Generic path reads Hst (fp32, [b, nc, H, P, N]); MFMA path reads Hb (bf16).
+hipError_t launch_chunk_scan(const FwdShape& s, ssd_dtype type, bool mfma, const void* x,
+                             const void* B, const void* C, const float* Acs, const float* dtq,
+                             const float* Hst, const uint16_t* Hb, const float* D, void* y,
+                             hipStream_t st);
+hipError_t launch_chunk_scan_mfma(const FwdShape& s, const void* x, const void* B, const void* C,
+                                  const float* Acs, const float* dtq, const uint16_t* Hb,
+                                  const float* D, void* y, hipStream_t st);
 
 hipError_t launch_state_update(ssd_dtype type, float* state, const void* x, const void* dt,
                                const float* A, const void* B, const void* C, const float* D, void* y,

@@ -3,85 +3,137 @@
 //   H_0 = init (or 0);  for c = 0 .. nc-1:  out_c = H_c;  H_{c+1} = exp(Acs_c[Q-1]) H_c + S_c
 //   final = H_nc
 //
-// Chunk c's own state S_c (from chunk_state) is replaced in place by H_c, the
-// state entering chunk c, which chunk_scan reads. This is the "state passed
-// between chunks by the SSM recurrence" step (youngju.dev "Mamba / selective
-// SSM", section "SSDアルゴリズムとチャンク分割"; Qiita "Mamba-2" article,
-// section 4.2, step 3: scan across chunks). exp(Acs_c[Q-1]) is the decay of a
-// whole chunk, the product of its abar_t.
+// out_c, the state entering chunk c, is what chunk_scan reads. This is the
+// "state passed between chunks by the SSM recurrence" step (youngju.dev
+// "Mamba / selective SSM", section "SSDアルゴリズムとチャンク分割"; Qiita
+// "Mamba-2" article, section 4.2, step 3: scan across chunks).
+// exp(Acs_c[Q-1]) is the decay of a whole chunk, the product of its abar_t.
 //
-// Elementwise and HBM-bound: each thread owns 4 consecutive fp32 elements of
-// one (b, h) state and walks the chunks sequentially. The chunk states of
-// later chunks do not depend on the recurrence, so their loads are issued
-// kDepth chunks ahead of use to keep enough bytes in flight.
+// Chunk states are stored transposed ([p][n], n fastest); init_state and
+// final_state use the caller's [n][p] layout, so the work-group that owns a
+// 16 (p) x 64 (n) tile of one (b, h) state transposes them through LDS.
+// The running state stays fp32. out_c goes either back over S_c (fp32, the
+// generic path) or to a separate bf16 buffer (the MFMA path, whose chunk_scan
+// consumes it as a bf16 matrix operand).
+//
+// Elementwise and HBM-bound: each thread owns 4 consecutive n of one p and
+// walks the chunks in order. Chunk states of later chunks do not depend on
+// the recurrence, so their loads are issued kDepth chunks ahead of use.
 #include "ssd_internal.h"
 
 namespace ssd {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kDepth = 8;  // chunks of S in flight per thread
+constexpr int kDepth = 8;   // chunks of S in flight per thread
+constexpr int kTP = 16;     // p rows per tile
+constexpr int kTN = 64;     // n columns per tile (16 threads x 4)
 
-__global__ __launch_bounds__(kThreads) void state_passing_kernel(
-    float* __restrict__ S, const float* __restrict__ Acs, const float* __restrict__ init,
-    float* __restrict__ fin, int H, int NP, int Q, int nc, long nvec /* b*H*NP/4 */) {
-  const long v = long(blockIdx.x) * kThreads + threadIdx.x;
-  if (v >= nvec) return;
-  const int nvh = NP / 4;                  // f32x4 per (b,h) state
-  const long bh = v / nvh;
-  const int e = int(v % nvh) * 4;
-  const int b = int(bh / H), h = int(bh % H);
-  const size_t cstride = size_t(H) * NP;   // elements between chunk c and c+1
-  float* base = S + (size_t(b) * nc * H + h) * NP + e;
-  const float* arow = Acs + size_t(bh) * nc * Q + (Q - 1);
-
-  f32x4 cur = f32x4{0.f, 0.f, 0.f, 0.f};
-  if (init) cur = *reinterpret_cast<const f32x4*>(init + size_t(bh) * NP + e);
-
-  f32x4 ring[kDepth];
-  float dec[kDepth];
-#pragma unroll
-  for (int k = 0; k < kDepth; ++k) {
-    if (k < nc) {
-      ring[k] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(base + size_t(k) * cstride));
-      dec[k] = arow[size_t(k) * Q];
-    }
+__device__ __forceinline__ void store_out(float* S, uint16_t* Hb, size_t idx, const f32x4& v) {
+  if (Hb) {
+    const uint32_t lo = uint32_t(f32_to_bf16(v.x)) | (uint32_t(f32_to_bf16(v.y)) << 16);
+    const uint32_t hi = uint32_t(f32_to_bf16(v.z)) | (uint32_t(f32_to_bf16(v.w)) << 16);
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    *reinterpret_cast<u32x2*>(Hb + idx) = u32x2{lo, hi};
+  } else {
+    *reinterpret_cast<f32x4*>(S + idx) = v;
   }
-  for (int c0 = 0; c0 < nc; c0 += kDepth) {
+}
+
+// grid: b * H * ceil(P/kTP) * ceil(N/kTN) work-groups; requires N % 4 == 0.
+__global__ __launch_bounds__(kThreads) void state_passing_tiled(
+    float* __restrict__ S, uint16_t* __restrict__ Hb, const float* __restrict__ Acs,
+    const float* __restrict__ init, float* __restrict__ fin, int H, int P, int N, int Q, int nc) {
+  __shared__ float tile[kTN][kTP + 1];
+  const int tpn = (N + kTN - 1) / kTN, tpp = (P + kTP - 1) / kTP;
+  int bid = blockIdx.x;
+  const int tn = bid % tpn; bid /= tpn;
+  const int tp = bid % tpp; bid /= tpp;
+  const int bh = bid;                       // b * H + h
+  const int b = bh / H, h = bh % H;
+  const int tid = threadIdx.x;
+  const int pi = tid / 16, nq = tid % 16;
+  const int p0 = tp * kTP, n0 = tn * kTN;
+  const int p = p0 + pi, n = n0 + 4 * nq;
+  const bool active = p < P && n < N;
+  const size_t sbh = size_t(N) * P;         // elements of one (b, h) state
+
+  // H_0: init transposed through LDS (or zero)
+  f32x4 cur = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (init) {
+    for (int e = tid; e < kTN * kTP; e += kThreads) {
+      const int nn = e / kTP, pp = e % kTP;
+      float v = 0.f;
+      if (n0 + nn < N && p0 + pp < P) v = init[size_t(bh) * sbh + size_t(n0 + nn) * P + p0 + pp];
+      tile[nn][pp] = v;
+    }
+    __syncthreads();
+    cur = f32x4{tile[4 * nq][pi], tile[4 * nq + 1][pi], tile[4 * nq + 2][pi], tile[4 * nq + 3][pi]};
+    __syncthreads();
+  }
+
+  if (active) {
+    const size_t cstride = size_t(H) * sbh;  // elements between chunk c and c+1
+    const size_t off0 = (size_t(b) * nc * H + h) * sbh + size_t(p) * N + n;
+    const float* arow = Acs + size_t(bh) * nc * Q + (Q - 1);
+    f32x4 ring[kDepth];
+    float dec[kDepth];
 #pragma unroll
     for (int k = 0; k < kDepth; ++k) {
-      const int c = c0 + k;
-      if (c < nc) {
-        const f32x4 s = ring[k];
-        const float a = expf(dec[k]);
-        if (c + kDepth < nc) {
-          ring[k] = __builtin_nontemporal_load(
-              reinterpret_cast<const f32x4*>(base + size_t(c + kDepth) * cstride));
-          dec[k] = arow[size_t(c + kDepth) * Q];
+      if (k < nc) {
+        ring[k] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(S + off0 + size_t(k) * cstride));
+        dec[k] = arow[size_t(k) * Q];
+      }
+    }
+    for (int c0 = 0; c0 < nc; c0 += kDepth) {
+#pragma unroll
+      for (int k = 0; k < kDepth; ++k) {
+        const int c = c0 + k;
+        if (c < nc) {
+          const f32x4 s = ring[k];
+          const float a = expf(dec[k]);
+          if (c + kDepth < nc) {
+            ring[k] = __builtin_nontemporal_load(
+                reinterpret_cast<const f32x4*>(S + off0 + size_t(c + kDepth) * cstride));
+            dec[k] = arow[size_t(c + kDepth) * Q];
+          }
+          store_out(S, Hb, off0 + size_t(c) * cstride, cur);
+          cur.x = a * cur.x + s.x;
+          cur.y = a * cur.y + s.y;
+          cur.z = a * cur.z + s.z;
+          cur.w = a * cur.w + s.w;
         }
-        *reinterpret_cast<f32x4*>(base + size_t(c) * cstride) = cur;
-        cur.x = a * cur.x + s.x;
-        cur.y = a * cur.y + s.y;
-        cur.z = a * cur.z + s.z;
-        cur.w = a * cur.w + s.w;
       }
     }
   }
-  if (fin) *reinterpret_cast<f32x4*>(fin + size_t(bh) * NP + e) = cur;
+
+  // final state transposed back through LDS
+  if (fin) {
+    tile[4 * nq][pi] = cur.x;
+    tile[4 * nq + 1][pi] = cur.y;
+    tile[4 * nq + 2][pi] = cur.z;
+    tile[4 * nq + 3][pi] = cur.w;
+    __syncthreads();
+    for (int e = tid; e < kTN * kTP; e += kThreads) {
+      const int nn = e / kTP, pp = e % kTP;
+      if (n0 + nn < N && p0 + pp < P) fin[size_t(bh) * sbh + size_t(n0 + nn) * P + p0 + pp] = tile[nn][pp];
+    }
+  }
 }
 
-// Scalar variant for N*P not a multiple of 4.
+// Any N (small shapes): one element per thread, fp32 in place.
 __global__ __launch_bounds__(kThreads) void state_passing_scalar(
     float* __restrict__ S, const float* __restrict__ Acs, const float* __restrict__ init,
-    float* __restrict__ fin, int H, int NP, int Q, int nc, long total) {
+    float* __restrict__ fin, int H, int P, int N, int Q, int nc, long total) {
   const long i = long(blockIdx.x) * kThreads + threadIdx.x;
   if (i >= total) return;
-  const long bh = i / NP;
-  const int e = int(i % NP);
+  const long bh = i / (long(N) * P);
+  const int e = int(i % (long(N) * P));
+  const int n = e / P, p = e % P;            // i walks the caller's [n][p] layout
   const int b = int(bh / H), h = int(bh % H);
   float cur = init ? init[i] : 0.f;
   for (int c = 0; c < nc; ++c) {
-    const size_t si = ((size_t(b) * nc + c) * H + h) * NP + e;
+    const size_t si = ((size_t(b) * nc + c) * H + h) * size_t(N) * P + size_t(p) * N + n;
     const float s = S[si];
     S[si] = cur;
     cur = expf(Acs[(size_t(bh) * nc + c) * Q + Q - 1]) * cur + s;
@@ -91,19 +143,18 @@ __global__ __launch_bounds__(kThreads) void state_passing_scalar(
 
 }  // namespace
 
-hipError_t launch_state_passing(const FwdShape& s, float* S, const float* Acs, const float* init,
-                                float* final_state, hipStream_t st) {
-  const int NP = s.N * s.P;
-  if (NP % 4 == 0) {
-    const long nvec = long(s.b) * s.H * NP / 4;
-    const long blocks = (nvec + kThreads - 1) / kThreads;
-    hipLaunchKernelGGL(state_passing_kernel, dim3(unsigned(blocks)), dim3(kThreads), 0, st, S, Acs,
-                       init, final_state, s.H, NP, s.Q, s.nc, nvec);
+hipError_t launch_state_passing(const FwdShape& s, float* S, uint16_t* Hb, const float* Acs,
+                                const float* init, float* final_state, hipStream_t st) {
+  if (s.N % 4 == 0) {
+    const long tiles = long(s.b) * s.H * ((s.P + kTP - 1) / kTP) * ((s.N + kTN - 1) / kTN);
+    hipLaunchKernelGGL(state_passing_tiled, dim3(unsigned(tiles)), dim3(kThreads), 0, st, S, Hb, Acs,
+                       init, final_state, s.H, s.P, s.N, s.Q, s.nc);
   } else {
-    const long total = long(s.b) * s.H * NP;
+    if (Hb) return hipErrorInvalidValue;     // the MFMA path never has N % 4 != 0
+    const long total = long(s.b) * s.H * s.N * s.P;
     const long blocks = (total + kThreads - 1) / kThreads;
     hipLaunchKernelGGL(state_passing_scalar, dim3(unsigned(blocks)), dim3(kThreads), 0, st, S, Acs,
-                       init, final_state, s.H, NP, s.Q, s.nc, total);
+                       init, final_state, s.H, s.P, s.N, s.Q, s.nc, total);
   }
   return hipGetLastError();
 }
