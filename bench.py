@@ -4,15 +4,15 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--no-cpu-baseline] [--no-extra]
 
-One step = one ssd_chunk_scan_fwd call (chunk_cumsum, chunk_state,
-state_passing, chunk_scan) over one batch of the workload, inputs resident in
-HBM. The headline workload is the Mamba-2-130M-shaped layer (batch 8,
+One step = one ssd_chunk_scan_fwd call (chunk_cumsum, chunk_scores,
+chunk_state, state_passing, chunk_scan) over one batch of the workload, inputs
+resident in HBM. The headline workload is the Mamba-2-130M-shaped layer (batch 8,
 T 2048, H 24, P 64, N 128, 1 group, chunk 256, bf16 inputs, fp32
 accumulation and state). Prints ONE JSON line on stdout; progress goes to
 stderr.
 
 Kernel durations are measured live with hipEvents that the library records on
-its own stream between its four launches (ssd_chunk_scan_fwd_timed). The
+its own stream between its launches (ssd_chunk_scan_fwd_timed). The
 decode update (ssd_state_update) is measured on the batch-256 decode workload
 in the same run, and the fp64 CPU oracle is timed on the host's cores.
 """
@@ -44,9 +44,10 @@ KERNEL_SOURCES = {
     "chunk_state": ["chunk_state.hip", "chunk_state_mfma.hip"],
     "state_passing": ["state_passing.hip"],
     "chunk_scan": ["chunk_scan.hip", "chunk_scan_mfma.hip"],
+    "chunk_scores": ["chunk_scores.hip"],
     "state_update": ["state_update.hip"],
 }
-STAGES = ["chunk_cumsum", "chunk_state", "state_passing", "chunk_scan"]
+STAGES = ["chunk_cumsum", "chunk_scores", "chunk_state", "state_passing", "chunk_scan"]
 
 
 def log(*a):
@@ -108,13 +109,23 @@ def fwd_work(w: workloads.FwdWorkload, with_init: bool) -> dict:
     st = 4 * b * nc * H * N * P         # all chunk states, fp32
     fst = 4 * b * H * N * P             # one [b,H,N,P] fp32 state
     tri = Q * (Q + 1) // 2
+    # the bf16 matrix-core path (dstate, headdim multiples of 32, chunk >= 32)
+    # precomputes C B^T per chunk and group as bf16 32x32 tiles and hands the
+    # passed states to chunk_scan as bf16; the generic path does neither
+    mfma = w.dtype == "bf16" and N in (32, 64, 128, 256) and P in (32, 64, 128) and Q >= 32
+    lpc = Q // 32
+    cbt = b * nc * G * (lpc * (lpc + 1) // 2) * 1024 * 2 if mfma else 0
+    hst = st // 2 if mfma else st       # passed states as chunk_scan reads them
     return {
         "chunk_cumsum": {"bytes": dtb + 2 * acs, "flops": b * T * H * 2},
+        "chunk_scores": {"bytes": 2 * bc + cbt if mfma else 0,
+                         "flops": b * nc * G * 2 * N * tri if mfma else 0},
         "chunk_state": {"bytes": x + bc + 2 * acs + st, "flops": 2 * b * T * H * N * P},
-        "state_passing": {"bytes": 2 * st + 4 * b * H * nc + fst * (2 if with_init else 1),
+        "state_passing": {"bytes": st + hst + 4 * b * H * nc + fst * (2 if with_init else 1),
                           "flops": 2 * b * nc * H * N * P},
-        "chunk_scan": {"bytes": 2 * x + 2 * bc + 2 * acs + st,
-                       "flops": b * nc * (G * 2 * N * tri + H * (2 * P * tri + 2 * Q * N * P))},
+        "chunk_scan": {"bytes": 2 * x + (bc + cbt if mfma else 2 * bc) + 2 * acs + hst,
+                       "flops": b * nc * H * (2 * P * tri + 2 * Q * N * P)
+                       + (0 if mfma else b * nc * G * 2 * N * tri)},
     }
 
 
@@ -186,7 +197,7 @@ def bench_fwd(hip, w, steps, warmup, cold=False):
     for _ in range(warmup):
         call()
     torch.cuda.synchronize()
-    evs = [[hip.event() for _ in range(5)] for _ in range(steps)]
+    evs = [[hip.event() for _ in range(6)] for _ in range(steps)]
     t_start, t_end = hip.event(), hip.event()
     flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda") if cold else None
 
@@ -202,7 +213,7 @@ def bench_fwd(hip, w, steps, warmup, cold=False):
     wall = time.perf_counter() - wall0
 
     stage_ms = {s: float(np.mean([hip.ms(ev[i], ev[i + 1]) for ev in evs])) for i, s in enumerate(STAGES)}
-    call_ms = float(np.mean([hip.ms(ev[0], ev[4]) for ev in evs]))
+    call_ms = float(np.mean([hip.ms(ev[0], ev[5]) for ev in evs]))
     total_ms = hip.ms(t_start, t_end)
     for e in [t_start, t_end] + [e for ev in evs for e in ev]:
         hip.destroy(e)
@@ -298,7 +309,7 @@ def main():
     work = fwd_work(w, w.init != "zero")
     kernels = {}
     for s in STAGES:
-        ms = r["stage_ms"][s]
+        ms = max(r["stage_ms"][s], 1e-6)
         kernels[s] = {"ms": round(ms, 5),
                       "GB_per_s": round(work[s]["bytes"] / (ms * 1e-3) / 1e9, 1),
                       "TFLOP_per_s": round(work[s]["flops"] / (ms * 1e-3) / 1e12, 2),

@@ -82,9 +82,9 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_generic(
 
 hipError_t launch_chunk_scan(const FwdShape& s, ssd_dtype type, bool mfma, const void* x,
                              const void* B, const void* C, const float* Acs, const float* dtq,
-                             const float* Hst, const uint16_t* Hb, const float* D, void* y,
-                             hipStream_t st) {
-  if (mfma) return launch_chunk_scan_mfma(s, x, B, C, Acs, dtq, Hb, D, y, st);
+                             const float* Hst, const uint16_t* Hb, const uint16_t* CB,
+                             const float* D, void* y, hipStream_t st) {
+  if (mfma) return launch_chunk_scan_mfma(s, x, CB, C, Acs, dtq, Hb, D, y, st);
   dim3 grid(s.H * (s.Q / kRows), s.nc, s.b);
   if (type == SSD_BF16)
     hipLaunchKernelGGL(chunk_scan_generic<uint16_t>, grid, dim3(kThreads), 0, st,

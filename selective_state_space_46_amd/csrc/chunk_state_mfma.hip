@@ -9,21 +9,22 @@
 // ("SSDアルゴリズムとチャンク分割": inside a chunk, matrix products).
 //
 // Work-group: one (batch, chunk) and KH heads of one B/C group, 4 waves. The
-// token axis is the contraction axis, but x and B are stored token-major, so
-// each 32-token slice is transposed on its way into LDS (8 x 8 bf16 blocks
-// transposed in registers, W scaled in fp32 before its single bf16 rounding).
-// The B^T slice is shared by the KH heads. Each wave owns KH*(P/32)*(N/32)/4
-// output tiles of 32 x 32 (fp32 accumulators) and reads its operands from LDS
-// with 16-byte loads; row stride 40 bf16 (80 B) keeps 16 lanes on distinct
-// banks. Output tiles go to HBM as fp32 rows of 32 consecutive n.
+// token axis is the contraction axis while x and B are stored token-major, so
+// each 64-token slice is copied into LDS in its natural row-major order
+// (coalesced 16-byte rows; W = w_s x_s scaled in fp32 per token row before its
+// single bf16 rounding) and the MFMA operands are read transposed with
+// ds_read_b64_tr_b16 (see mfma_util.h). The B slice is shared by the KH
+// heads; the next slice's rows are loaded into registers while the current
+// one feeds the matrix cores. Each wave owns KH*(P/32)*(N/32)/4 output tiles
+// of 32 x 32 (fp32 accumulators). Output tiles go to HBM as fp32 rows of 32
+// consecutive n.
 #include "mfma_util.h"
 
 namespace ssd {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kSK = 32;          // tokens per contraction slice
-constexpr int kRS = kSK + 8;     // LDS row stride (bf16 elements)
+constexpr int kSK = 64;          // tokens per contraction slice
 constexpr int kMaxQ = 256;
 
 template <int N, int P, int KH>
@@ -31,8 +32,12 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ Bm, const float* __restrict__ Acs,
     const float* __restrict__ dtq, float* __restrict__ S, int T, int H, int G, int Q, int nc,
     int nhg) {
-  __shared__ __attribute__((aligned(16))) uint16_t sBt[N][kRS];
-  __shared__ __attribute__((aligned(16))) uint16_t sWt[KH][P][kRS];
+  constexpr int RBB = N / 8, RBW = P / 8;           // 16-byte chunks per row
+  constexpr int CB_ = kSK * RBB, CW = KH * kSK * RBW;  // chunks per slice
+  constexpr int PER = (CB_ + CW) / kThreads;         // chunks per thread
+  static_assert((CB_ + CW) % kThreads == 0, "slice must split evenly");
+  __shared__ __attribute__((aligned(16))) uint16_t sB[kSK * N];
+  __shared__ __attribute__((aligned(16))) uint16_t sW[KH][kSK * P];
   __shared__ float sw[KH][kMaxQ];
 
   constexpr int NT = N / 32, PT = P / 32;
@@ -45,7 +50,7 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma_kernel(
   const int h0 = hg * KH;
   const int g = h0 / (H / G);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int l32 = lane & 31, g2 = lane >> 5;
+  const int g2 = lane >> 5;
   const long t0 = long(c) * Q;
 
   // w_s = exp(Acs_{Q-1} - Acs_s) * dt_s for the whole chunk, per head
@@ -55,49 +60,55 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma_kernel(
     sw[kh][i] = exp_fast(Acs[arow + Q - 1] - Acs[arow + i]) * dtq[arow + i];
   }
 
+  // this thread's 16-byte chunks of a slice: B rows first, then W rows
+  auto load_slice = [&](int s0, u32x4 (&v)[PER]) {
+#pragma unroll
+    for (int m = 0; m < PER; ++m) {
+      const int e = tid + m * kThreads;
+      if (e < CB_) {
+        const int r = e / RBB, cc = e % RBB;
+        const long t = min(t0 + s0 + r, long(T) - 1);
+        v[m] = load16(Bm + ((size_t(b) * T + t) * G + g) * N + 8 * cc);
+      } else {
+        const int e2 = e - CB_;
+        const int kh = e2 / (kSK * RBW), r = (e2 / RBW) % kSK, cc = e2 % RBW;
+        const long t = min(t0 + s0 + r, long(T) - 1);
+        v[m] = load16(x + ((size_t(b) * T + t) * H + h0 + kh) * P + 8 * cc);
+      }
+    }
+  };
+  auto store_slice = [&](int s0, const u32x4 (&v)[PER]) {
+#pragma unroll
+    for (int m = 0; m < PER; ++m) {
+      const int e = tid + m * kThreads;
+      if (e < CB_) {
+        const int r = e / RBB, cc = e % RBB;
+        const bool in = r < Q - s0 && t0 + s0 + r < T;
+        *reinterpret_cast<u32x4*>(&sB[lds_off<RBB>(r, 8 * cc)]) = keep_or_zero(in, v[m]);
+      } else {
+        const int e2 = e - CB_;
+        const int kh = e2 / (kSK * RBW), r = (e2 / RBW) % kSK, cc = e2 % RBW;
+        const float w = (r < Q - s0 && t0 + s0 + r < T) ? sw[kh][s0 + r] : 0.f;
+        u32x4 o;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) o[q] = pack_bf16x2(bf16_lo(v[m][q]) * w, bf16_hi(v[m][q]) * w);
+        *reinterpret_cast<u32x4*>(&sW[kh][lds_off<RBW>(r, 8 * cc)]) = o;
+      }
+    }
+  };
+
   f32x16 acc[TPW];
 #pragma unroll
   for (int m = 0; m < TPW; ++m) acc[m] = zero16();
 
-  constexpr int NBB = (kSK / 8) * (N / 8);        // 8x8 blocks of the B slice
-  constexpr int NWB = KH * (kSK / 8) * (P / 8);   // 8x8 blocks of the W slices
-
+  u32x4 pre[PER];
+  load_slice(0, pre);
   for (int s0 = 0; s0 < Q; s0 += kSK) {
     __syncthreads();  // sw written / previous slice consumed
-    for (int blk = tid; blk < NBB + NWB; blk += kThreads) {
-      u32x4 in[8], out[8];
-      if (blk < NBB) {
-        const int tg = blk / (N / 8), ng = blk % (N / 8);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const long t = t0 + s0 + 8 * tg + i;
-          const long tc = t < T ? t : T - 1;
-          in[i] = keep_or_zero(t < T, load16(Bm + ((size_t(b) * T + tc) * G + g) * N + 8 * ng));
-        }
-        transpose8x8_b16(in, out);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) *reinterpret_cast<u32x4*>(&sBt[8 * ng + j][8 * tg]) = out[j];
-      } else {
-        const int wb = blk - NBB;
-        const int kh = wb / ((kSK / 8) * (P / 8));
-        const int r = wb % ((kSK / 8) * (P / 8));
-        const int tg = r / (P / 8), pg = r % (P / 8);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const long t = t0 + s0 + 8 * tg + i;
-          const long tc = t < T ? t : T - 1;
-          const u32x4 raw =
-              keep_or_zero(t < T, load16(x + ((size_t(b) * T + tc) * H + h0 + kh) * P + 8 * pg));
-          const float w = sw[kh][s0 + 8 * tg + i];
-#pragma unroll
-          for (int m = 0; m < 4; ++m) in[i][m] = pack_bf16x2(bf16_lo(raw[m]) * w, bf16_hi(raw[m]) * w);
-        }
-        transpose8x8_b16(in, out);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) *reinterpret_cast<u32x4*>(&sWt[kh][8 * pg + j][8 * tg]) = out[j];
-      }
-    }
+    store_slice(s0, pre);
+    if (s0 + kSK < Q) load_slice(s0 + kSK, pre);
     __syncthreads();
+    const int ksteps = min(kSK, Q - s0) / 16;
 #pragma unroll
     for (int m = 0; m < TPW; ++m) {
       const int tile = wave + 4 * m;
@@ -105,16 +116,17 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma_kernel(
         const int kh = tile / (PT * NT);
         const int r = tile % (PT * NT);
         const int pb = r / NT, nb = r % NT;
-#pragma unroll
-        for (int kk = 0; kk < kSK / 16; ++kk) {
-          const u32x4 a = *reinterpret_cast<const u32x4*>(&sWt[kh][32 * pb + l32][16 * kk + 8 * g2]);
-          const u32x4 bb = *reinterpret_cast<const u32x4*>(&sBt[32 * nb + l32][16 * kk + 8 * g2]);
+        for (int kk = 0; kk < ksteps; ++kk) {
+          const int kb = 16 * kk + 8 * g2;
+          const u32x4 a = frag_tr<RBW>(sW[kh], kb, kb + 4, 32 * pb, lane);
+          const u32x4 bb = frag_tr<RBB>(sB, kb, kb + 4, 32 * nb, lane);
           acc[m] = mfma32x32x16(a, bb, acc[m]);
         }
       }
     }
   }
 
+  const int l32 = lane & 31;
 #pragma unroll
   for (int m = 0; m < TPW; ++m) {
     const int tile = wave + 4 * m;
@@ -146,9 +158,9 @@ hipError_t launch_t(const FwdShape& s, const void* x, const void* B, const float
 template <int N, int P>
 hipError_t launch_np(const FwdShape& s, const void* x, const void* B, const float* Acs,
                      const float* dtq, float* S, hipStream_t st) {
-  // two heads per work-group share the staged B slice, while the fp32
-  // accumulators stay within 128 registers per lane
-  if constexpr ((P / 32) * (N / 32) * 2 <= 32) {
+  // two heads per work-group share the staged B slice while the fp32
+  // accumulators stay within 64 registers per lane (two waves per SIMD)
+  if constexpr ((P / 32) * (N / 32) * 2 <= 16) {
     if ((s.H / s.G) % 2 == 0) return launch_t<N, P, 2>(s, x, B, Acs, dtq, S, st);
   }
   return launch_t<N, P, 1>(s, x, B, Acs, dtq, S, st);

@@ -57,6 +57,61 @@ __device__ __forceinline__ void transpose8x8_b16(const u32x4 (&in)[8], u32x4 (&o
 
 __device__ __forceinline__ u32x4 load16(const uint16_t* p) { return *reinterpret_cast<const u32x4*>(p); }
 
+// ---------------------------------------------------------------------------
+// LDS tiles in natural (row-major, token-major) order, read transposed.
+//
+// ds_read_b64_tr_b16 (gfx950) works on groups of 16 lanes: destination lane
+// 4a + e of a group receives element e (16-bit) of the 8-byte chunks that
+// lanes a, a+4, a+8, a+12 of the group address (checked on MI355X). If lane
+// q of a group addresses row kb + q/4, columns m0 + 4 (q%4) .. +4, lane q
+// receives rows kb .. kb+3 of column m0 + q: four consecutive k of one MFMA
+// row/column. Two such reads give one 8-element operand fragment.
+//
+// Rows are stored as 16-byte chunks, chunk c of row r at chunk c ^ swz(r).
+// With RB 16-byte chunks per row, swz keeps the four rows one transposed read
+// touches on disjoint banks (64 banks of 4 bytes):
+//   RB = 4  (64 B rows):  rows start 16 banks apart            -> swz = 0
+//   RB = 8  (128 B rows): rows r, r+1 differ by 32 banks        -> swz = 4 ((r >> 1) & 1)
+//   RB >= 16 (256 B, 512 B rows): every row starts at bank 0    -> swz = 4 (r & 3)
+// Row-major 16-byte writes of consecutive chunks stay conflict-free under it.
+// ---------------------------------------------------------------------------
+template <int RB>
+__device__ __forceinline__ int lds_swz(int r) {
+  if constexpr (RB <= 4) return 0;
+  else if constexpr (RB == 8) return 4 * ((r >> 1) & 1);
+  else return 4 * (r & 3);
+}
+
+// Element offset of (row r, column col) in a swizzled tile with RB chunks/row.
+template <int RB>
+__device__ __forceinline__ int lds_off(int r, int col) {
+  return r * (RB * 8) + (((col >> 3) ^ lds_swz<RB>(r)) << 3) + (col & 7);
+}
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* tile, int elem_off) {
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  // the tile lives in LDS; cast the generic pointer to the local address space
+  const __attribute__((address_space(3))) char* p =
+      (const __attribute__((address_space(3))) char*)(tile) + 2 * elem_off;
+  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+  return __builtin_bit_cast(u32x2, v);
+}
+
+// One 32x32x16 operand fragment (8 consecutive k for MFMA row/column L % 32 of
+// the 32-wide block starting at column m0) from a swizzled natural tile whose
+// rows are the k axis: k rows kb1 .. kb1+3 and kb2 .. kb2+3 (kb1, kb2 already
+// include this lane's 8 (L/32) offset, so any k permutation shared with the
+// other operand can be expressed).
+template <int RB>
+__device__ __forceinline__ u32x4 frag_tr(const uint16_t* tile, int kb1, int kb2, int m0, int lane) {
+  const int q = lane & 15, m = m0 + 16 * ((lane >> 4) & 1) + 4 * (q & 3);
+  const u32x2 lo = lds_read_tr16(tile, lds_off<RB>(kb1 + (q >> 2), m));
+  const u32x2 hi = lds_read_tr16(tile, lds_off<RB>(kb2 + (q >> 2), m));
+  return u32x4{lo[0], lo[1], hi[0], hi[1]};
+}
+
 // Keep `v` when `keep`, else zeros. Loads stay unconditional (their row index
 // is clamped into the tensor by the caller) so the compiler can issue a batch
 // of them back to back; a branch around each load would serialise them.

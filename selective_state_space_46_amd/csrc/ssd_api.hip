@@ -126,6 +126,7 @@ ssd_status ssd_chunk_scan_fwd_timed(const void* x, const void* dt, const float* 
   float* dtq = reinterpret_cast<float*>(ws + w.dtq);
   float* S = reinterpret_cast<float*>(ws + w.st);
   uint16_t* Hb = mfma ? reinterpret_cast<uint16_t*>(ws + w.hb) : nullptr;
+  uint16_t* CB = mfma ? reinterpret_cast<uint16_t*>(ws + w.cb) : nullptr;
 
   auto mark = [&](int i) {
     if (!stage_events || !stage_events[i]) return true;
@@ -134,14 +135,16 @@ ssd_status ssd_chunk_scan_fwd_timed(const void* x, const void* dt, const float* 
   if (!mark(0)) return SSD_ERR_HIP;
   if (launch_chunk_cumsum(s, dtype, dt, A, Acs, dtq, hs) != hipSuccess) return SSD_ERR_HIP;
   if (!mark(1)) return SSD_ERR_HIP;
-  if (launch_chunk_state(s, dtype, mfma, x, B, Acs, dtq, S, hs) != hipSuccess) return SSD_ERR_HIP;
+  if (mfma && launch_chunk_scores(s, B, C, CB, hs) != hipSuccess) return SSD_ERR_HIP;
   if (!mark(2)) return SSD_ERR_HIP;
+  if (launch_chunk_state(s, dtype, mfma, x, B, Acs, dtq, S, hs) != hipSuccess) return SSD_ERR_HIP;
+  if (!mark(3)) return SSD_ERR_HIP;
   if (launch_state_passing(s, S, Hb, Acs, init_state, final_state, hs) != hipSuccess)
     return SSD_ERR_HIP;
-  if (!mark(3)) return SSD_ERR_HIP;
-  if (launch_chunk_scan(s, dtype, mfma, x, B, C, Acs, dtq, S, Hb, D, y, hs) != hipSuccess)
-    return SSD_ERR_HIP;
   if (!mark(4)) return SSD_ERR_HIP;
+  if (launch_chunk_scan(s, dtype, mfma, x, B, C, Acs, dtq, S, Hb, CB, D, y, hs) != hipSuccess)
+    return SSD_ERR_HIP;
+  if (!mark(5)) return SSD_ERR_HIP;
   return SSD_OK;
 }
 

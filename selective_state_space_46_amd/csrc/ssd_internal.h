@@ -64,8 +64,10 @@ inline bool use_mfma_path(const FwdShape& s, ssd_dtype t) {
 //                            the generic path overwritten in place by the
 //                            states entering each chunk
 //   hb  [b, nc, H, P, N] bf16 states entering each chunk (MFMA path only)
+//   cb  [b, nc, G, ntile, 64, 16] bf16 C B^T tiles of each chunk (MFMA path
+//       only; ntile = lpc (lpc + 1) / 2 lower-triangle tiles, lpc = Q / 32)
 struct WsLayout {
-  size_t acs, dtq, st, hb, total;
+  size_t acs, dtq, st, hb, cb, total;
 };
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -78,7 +80,10 @@ inline WsLayout ws_layout(const FwdShape& s, bool mfma) {
   w.dtq = align_up(w.acs + row, 256);
   w.st = align_up(w.dtq + row, 256);
   w.hb = align_up(w.st + nst * sizeof(float), 256);
-  w.total = mfma ? align_up(w.hb + nst * sizeof(uint16_t), 256) : w.hb;
+  w.cb = align_up(w.hb + nst * sizeof(uint16_t), 256);
+  const size_t lpc = size_t(s.Q) / 32, ntile = lpc * (lpc + 1) / 2;
+  w.total = mfma ? align_up(w.cb + size_t(s.b) * s.nc * s.G * ntile * 1024 * sizeof(uint16_t), 256)
+                 : w.hb;
   return w;
 }
 
@@ -109,14 +114,19 @@ hipError_t launch_chunk_state_mfma(const FwdShape& s, const void* x, const void*
 hipError_t launch_state_passing(const FwdShape& s, float* S, uint16_t* Hb, const float* Acs,
                                 const float* init, float* final_state, hipStream_t st);
 
-// Generic path reads Hst (fp32, [b, nc, H, P, N]); MFMA path reads Hb (bf16).
+// C B^T tiles per chunk and group (MFMA path).
+hipError_t launch_chunk_scores(const FwdShape& s, const void* B, const void* C, uint16_t* CB,
+                               hipStream_t st);
+
+// Generic path reads Hst (fp32, [b, nc, H, P, N]); MFMA path reads Hb (bf16)
+// and the C B^T tiles CB.
 hipError_t launch_chunk_scan(const FwdShape& s, ssd_dtype type, bool mfma, const void* x,
                              const void* B, const void* C, const float* Acs, const float* dtq,
-                             const float* Hst, const uint16_t* Hb, const float* D, void* y,
-                             hipStream_t st);
-hipError_t launch_chunk_scan_mfma(const FwdShape& s, const void* x, const void* B, const void* C,
-                                  const float* Acs, const float* dtq, const uint16_t* Hb,
-                                  const float* D, void* y, hipStream_t st);
+                             const float* Hst, const uint16_t* Hb, const uint16_t* CB,
+                             const float* D, void* y, hipStream_t st);
+hipError_t launch_chunk_scan_mfma(const FwdShape& s, const void* x, const uint16_t* CB,
+                                  const void* C, const float* Acs, const float* dtq,
+                                  const uint16_t* Hb, const float* D, void* y, hipStream_t st);
 
 hipError_t launch_state_update(ssd_dtype type, float* state, const void* x, const void* dt,
                                const float* A, const void* B, const void* C, const float* D, void* y,

@@ -51,14 +51,17 @@ def ws(b, T, H, P, N, G, Q, dt=ssd.SSD_BF16):
 def test_workspace_query():
     """Acs and dt rows (fp32), chunk states (fp32) and, on the bf16 matrix-core
     path (dstate in {32,64,128,256}, headdim in {32,64,128}, chunk >= 32), a bf16
-    copy of the passed states; each region 256-byte aligned."""
+    copy of the passed states and the bf16 C B^T tiles (2 KB per lower-triangle
+    32x32 tile per chunk and group); each region 256-byte aligned."""
     def expect(b, T, H, P, N, Q, dtype):
         nc = -(-T // Q)
         up = lambda v: -(-v // 256) * 256
         row = up(b * H * nc * Q * 4)
         nst = b * nc * H * N * P
         mfma = dtype == ssd.SSD_BF16 and N in (32, 64, 128, 256) and P in (32, 64, 128) and Q >= 32
-        return up(2 * row + up(nst * 4) + (nst * 2 if mfma else 0))
+        lpc = Q // 32
+        cbt = b * nc * G * (lpc * (lpc + 1) // 2) * 1024 * 2
+        return up(2 * row + up(nst * 4) + (up(nst * 2) + cbt if mfma else 0))
     for args in [(8, 2048, 24, 64, 128, 1, 256), (1, 131072, 24, 64, 256, 1, 256), (1, 1, 1, 1, 1, 1, 16),
                  (2, 100, 4, 3, 5, 2, 32), (2, 100, 4, 64, 128, 2, 16), (2, 100, 4, 32, 64, 2, 32)]:
         b, T, H, P, N, G, Q = args
