@@ -11,6 +11,14 @@
 // The second term brings in all earlier chunks through H_c, the state entering
 // chunk c (youngju.dev page, "SSDアルゴリズムとチャンク分割").
 //
+// Decay factorisation: for l, s in the same chunk and s in the 32-token block
+// that starts at s0,
+//   exp(Acs_l - Acs_s) dt_s = exp(Acs_l - Acs_s0) * [exp(Acs_s0 - Acs_s) dt_s]
+// The bracket depends on s only and is folded into X once per work-group
+// (X'_s = bracket_s x_s, at most exp(32 max|dt A|) x_s, well inside bf16
+// range); the first factor is <= 1 and depends on (l, block of s): one
+// exponential per lane and tile, one multiply per score.
+//
 // Work-group: one batch row, one 256-token super-chunk (256/Q chunks), one
 // head; 4 waves. The C B^T tiles come precomputed once per group
 // (chunk_scores.hip) in MFMA-fragment order. The super-chunk is cut into eight
@@ -18,15 +26,17 @@
 // splits evenly. The output is produced transposed (y^T: rows p, lane = token
 // l), which makes every per-token factor one multiplier per lane:
 //   1. y^T = H_c^T C_l^T (k = dstate): H_c^T staged once in LDS (bf16, from
-//      state_passing), C_l rows straight from HBM; then y^T *= exp(Acs_l).
+//      state_passing) when the super-chunk is one chunk, C_l rows straight from
+//      HBM; then y^T *= exp(Acs_l).
 //   2. for each column block s <= l of the chunk: the C B^T tile (lane =
-//      column l, registers = rows s in runs of 4) times exp(Acs_l - Acs_s) dt_s
-//      (factored per 32-block, see the staging below), masked to s <= l,
-//      rounded to bf16, is the B operand of y^T += X^T G^T under a k
-//      permutation that the X^T operand reproduces with two 8-byte LDS reads.
-//      X^T (token-contiguous rows) is staged once per work-group through 8 x 8
-//      register transposes.
-//   3. + D x, bf16 rounding, 8-byte stores of 4 consecutive p.
+//      column l, registers = rows s in runs of 4) times exp(Acs_l - Acs_s0),
+//      masked to s <= l on the diagonal tile only, rounded to bf16, is the B
+//      operand of y^T += X'^T G^T under a k permutation that the X' operand
+//      reproduces: X' sits in LDS in natural token-major order (swizzled
+//      16-byte chunks) and is read transposed with ds_read_b64_tr_b16. Tiles
+//      are loaded two blocks ahead of use.
+//   3. + D x (x re-read from L2), bf16 rounding, 8-byte stores of 4
+//      consecutive p.
 #include "mfma_util.h"
 
 namespace ssd {
@@ -34,18 +44,19 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kSC = 256;          // tokens per super-chunk
-constexpr int kXS = kSC + 4;      // X^T row stride (bf16): 520 B, 8-byte reads conflict-free
 constexpr float kLog2e = 1.4426950408889634f;
 
-template <int N, int P>
+template <int N, int P, bool HLDS>
 __global__ __launch_bounds__(kThreads) void chunk_scan_mfma_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ CB, const uint16_t* __restrict__ Cm,
     const float* __restrict__ Acs, const float* __restrict__ dtq, const uint16_t* __restrict__ Hb,
     const float* __restrict__ D, uint16_t* __restrict__ y, int T, int H, int G, int Q, int nc,
     int nsc) {
   constexpr int kHS = N + 8;  // H^T row stride (bf16): 16-byte reads of 16 lanes hit distinct banks
-  __shared__ __attribute__((aligned(16))) uint16_t sXt[P][kXS];
-  __shared__ __attribute__((aligned(16))) uint16_t sHt[P][kHS];
+  constexpr int RBX = P / 8;  // 16-byte chunks per X' row
+  constexpr int HROWS = HLDS ? P : 1;
+  __shared__ __attribute__((aligned(16))) uint16_t sX[kSC * P];
+  __shared__ __attribute__((aligned(16))) uint16_t sHt[HROWS][kHS];
   __shared__ __attribute__((aligned(16))) float sA[kSC];  // Acs * log2(e)
   __shared__ __attribute__((aligned(16))) float sF[kSC];  // exp(Acs[block start] - Acs_s) * dt_s
 
@@ -54,7 +65,8 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_mfma_kernel(
   const int bs = id / H;
   const int sc = bs % nsc, b = bs / nsc;
   const int g = h / (H / G);
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = wave_id();  // wave-uniform (scalar register)
   const int l32 = lane & 31, g2 = lane >> 5;
   const int t0 = sc * kSC;
   const int cps = kSC / Q;        // chunks per super-chunk
@@ -62,12 +74,32 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_mfma_kernel(
   const int lpc = Q / 32;         // 32-row blocks per chunk
   const int ntile = lpc * (lpc + 1) / 2;
   const bool full = t0 + kSC <= T;     // no token of this super-chunk is past the end
-  const bool hlds = cps == 1;          // one chunk: its H_c^T fits in LDS
 
-  // ---- staging. Decay factorisation: for l, s in the same chunk, s in the
-  // 32-block that starts at s0,  exp(Acs_l - Acs_s) = exp(Acs_l - Acs_s0) * exp(Acs_s0 - Acs_s);
-  // the first factor is <= 1 (one exponential per lane and tile), the second
-  // lies in [1, exp(32 * max |dt A|)] and is tabulated here with dt_s folded in.
+  // C B^T tiles of 32-row block i: tile jj (column block jfirst + jj) of the
+  // block's row of its chunk's lower triangle, this lane's 32 bytes
+  auto tile_src = [&](int i) {
+    const int jf = (i / lpc) * lpc, cgi = c0 + i / lpc, ir = i - jf;
+    return reinterpret_cast<const u32x4*>(
+        CB + (((size_t(b) * nc + cgi) * G + g) * ntile + size_t(ir) * (ir + 1) / 2) * 1024 +
+        size_t(lane) * 16);
+  };
+  // a block's first loads: its diagonal tile, its first tile, its C rows
+  // (k = dstate, rows clamped into the tensor; zeroed past the end at use)
+  auto issue_block_loads = [&](int i, u32x4 (&td)[2], u32x4 (&tn)[2], u32x4 (&cfv)[N / 16]) {
+    const u32x4* ts = tile_src(i);
+    const int ir = i - (i / lpc) * lpc;
+    td[0] = ts[ir * 128];
+    td[1] = ts[ir * 128 + 1];
+    tn[0] = ts[0];
+    tn[1] = ts[1];
+    const uint16_t* cr = Cm + ((size_t(b) * T + min(t0 + 32 * i + l32, T - 1)) * G + g) * N + 8 * g2;
+#pragma unroll
+    for (int ks = 0; ks < N / 16; ++ks) cfv[ks] = load16(cr + 16 * ks);
+  };
+  u32x4 pre_tdiag[2], pre_tnext[2], pre_cf[N / 16];
+  if (t0 + 32 * wave < T) issue_block_loads(wave, pre_tdiag, pre_tnext, pre_cf);
+
+  // ---- staging 1: Acs, the per-token factor, H_c^T
   for (int i = tid; i < kSC; i += kThreads) {
     const int c = c0 + i / Q;
     float a = 0.f, f = 0.f;
@@ -80,33 +112,19 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_mfma_kernel(
     sA[i] = a;
     sF[i] = f;
   }
-  if (hlds) {
+  if constexpr (HLDS) {
     const uint16_t* hsrc = Hb + ((size_t(b) * nc + c0) * H + h) * size_t(P) * N;
     for (int e = tid; e < P * (N / 8); e += kThreads) {
       const int p = e / (N / 8), seg = e % (N / 8);
       *reinterpret_cast<u32x4*>(&sHt[p][8 * seg]) = load16(hsrc + size_t(p) * N + 8 * seg);
     }
   }
-  constexpr int NXB = (kSC / 8) * (P / 8);
-  for (int blk = tid; blk < NXB; blk += kThreads) {
-    const int tg = blk / (P / 8), pg = blk % (P / 8);
-    u32x4 in[8], out[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int t = min(t0 + 8 * tg + i, T - 1);
-      in[i] = load16(x + ((size_t(b) * T + t) * H + h) * P + 8 * pg);
-    }
-    if (!full) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) in[i] = keep_or_zero(t0 + 8 * tg + i < T, in[i]);
-    }
-    transpose8x8_b16(in, out);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      u32x2* dst = reinterpret_cast<u32x2*>(&sXt[8 * pg + j][8 * tg]);
-      dst[0] = u32x2{out[j][0], out[j][1]};
-      dst[1] = u32x2{out[j][2], out[j][3]};
-    }
+  // raw x, token-major, swizzled: issued with the loads above
+  for (int e = tid; e < kSC * RBX; e += kThreads) {
+    const int r = e / RBX, cc = e % RBX;
+    u32x4 v = load16(x + ((size_t(b) * T + min(t0 + r, T - 1)) * H + h) * P + 8 * cc);
+    if (!full) v = keep_or_zero(t0 + r < T, v);
+    *reinterpret_cast<u32x4*>(&sX[lds_off<RBX>(r, 8 * cc)]) = v;
   }
   __syncthreads();
 
@@ -118,96 +136,110 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_mfma_kernel(
     const int jfirst = (i / lpc) * lpc;     // first column block of the same chunk
     const int cg = c0 + i / lpc;            // global chunk index (< nc)
     const int lcol = 32 * i + l32;          // this lane's output token in the super-chunk
-    const int irel = i - jfirst;
-    const uint16_t* tiles = CB + (((size_t(b) * nc + cg) * G + g) * ntile + size_t(irel) * (irel + 1) / 2) * 1024 +
-                            size_t(lane) * 16;
-    auto load_tile = [&](int j, u32x4 (&t)[2]) {
-      const u32x4* src = reinterpret_cast<const u32x4*>(tiles + size_t(j - jfirst) * 1024);
-      t[0] = src[0];
-      t[1] = src[1];
+    const int irel = i - jfirst;            // tiles of this block: jj = 0 .. irel
+    const int t = tl0 + l32;
+    const u32x4* tsrc = tile_src(i);
+    auto load_tile = [&](int jj, u32x4 (&tt)[2]) {
+      tt[0] = tsrc[jj * 128];
+      tt[1] = tsrc[jj * 128 + 1];
     };
-    u32x4 tnext[2];
-    load_tile(jfirst, tnext);
+    // this block's first loads: issued before the staging barrier for the
+    // first block, here for the second
+    u32x4 tdiag[2], tnext[2], cf[N / 16];
+    if (which == 0) {
+#pragma unroll
+      for (int m = 0; m < 2; ++m) { tdiag[m] = pre_tdiag[m]; tnext[m] = pre_tnext[m]; }
+#pragma unroll
+      for (int ks = 0; ks < N / 16; ++ks) cf[ks] = pre_cf[ks];
+    } else {
+      issue_block_loads(i, tdiag, tnext, cf);
+    }
+    if (!full) {
+#pragma unroll
+      for (int ks = 0; ks < N / 16; ++ks) cf[ks] = keep_or_zero(t < T, cf[ks]);
+    }
 
     // ---- y^T = H_c^T C_l^T, then * exp(Acs_l)
-    u32x4 cf[N / 16];
-    {
-      const uint16_t* cr = Cm + ((size_t(b) * T + min(tl0 + l32, T - 1)) * G + g) * N + 8 * g2;
-#pragma unroll
-      for (int ks = 0; ks < N / 16; ++ks) cf[ks] = load16(cr + 16 * ks);
-      if (!full) {
-#pragma unroll
-        for (int ks = 0; ks < N / 16; ++ks) cf[ks] = keep_or_zero(tl0 + l32 < T, cf[ks]);
-      }
-    }
     f32x16 acc[P / 32];
-    const uint16_t* hg = Hb + (((size_t(b) * nc + cg) * H + h) * P + l32) * size_t(N) + 8 * g2;
+    const float sl = __builtin_amdgcn_exp2f(sA[lcol]);
 #pragma unroll
     for (int pb = 0; pb < P / 32; ++pb) {
       f32x16 a = zero16();
 #pragma unroll
       for (int ks = 0; ks < N / 16; ++ks) {
-        const u32x4 hf = hlds ? *reinterpret_cast<const u32x4*>(&sHt[32 * pb + l32][16 * ks + 8 * g2])
-                              : load16(hg + size_t(32 * pb) * N + 16 * ks);
+        u32x4 hf;
+        if constexpr (HLDS) {
+          hf = *reinterpret_cast<const u32x4*>(&sHt[32 * pb + l32][16 * ks + 8 * g2]);
+        } else {
+          hf = load16(Hb + (((size_t(b) * nc + cg) * H + h) * P + 32 * pb + l32) * size_t(N) + 16 * ks +
+                      8 * g2);
+        }
         a = mfma32x32x16(hf, cf[ks], a);
       }
-      const float sl = __builtin_amdgcn_exp2f(sA[lcol]);
 #pragma unroll
       for (int r = 0; r < 16; ++r) a[r] *= sl;
       acc[pb] = a;
     }
 
-    // ---- y^T += X^T G^T over the column blocks of the chunk
-    for (int j = jfirst; j <= i; ++j) {
-      u32x4 tcur[2] = {tnext[0], tnext[1]};
-      if (j < i) load_tile(j + 1, tnext);
-      const bool diag = (j == i);
-      // exp(Acs_l - Acs_{32j}) <= 1, once per lane and tile
-      const float lfac = __builtin_amdgcn_exp2f(sA[lcol] - sA[32 * j]);
+    // ---- y^T += X'^T G^T over the column blocks of the chunk
+    const float al = sA[lcol];
+    // one column block: G^T = tile * exp(Acs_l - Acs_{32j}) (masked to s <= l
+    // on the diagonal block), then two MFMAs per 32 p
+    auto apply = [&](const int jj, const u32x4 (&tile)[2], const bool diag) {
+      const int j = jfirst + jj;
+      const float lfac = __builtin_amdgcn_exp2f(al - sA[32 * j]);  // exp(Acs_l - Acs_{32j}) <= 1
       uint32_t gw[8];
+      f32x4 fs[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int sb = 32 * j + 8 * q + 4 * g2;  // rows sb .. sb+3 of register run q
-        const f32x4 fs = *reinterpret_cast<const f32x4*>(&sF[sb]);
-        const uint32_t w0 = tcur[q / 2][2 * (q % 2)], w1 = tcur[q / 2][2 * (q % 2) + 1];
-        const float cb[4] = {bf16_lo(w0), bf16_hi(w0), bf16_lo(w1), bf16_hi(w1)};
-        float v[4];
+      for (int q = 0; q < 4; ++q) fs[q] = *reinterpret_cast<const f32x4*>(&sF[32 * j + 8 * q + 4 * g2]);
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          float e = cb[rr] * lfac * fs[rr];
-          if (diag && sb + rr > lcol) e = 0.f;   // causal mask
-          v[rr] = e;
+      for (int m = 0; m < 8; ++m) {
+        const uint32_t w = tile[m / 4][m % 4];
+        float lo = bf16_lo(w) * lfac * fs[m / 2][2 * (m % 2)];
+        float hi = bf16_hi(w) * lfac * fs[m / 2][2 * (m % 2) + 1];
+        if (diag) {
+          // register pair m holds rows 8 (m/2) + 4 g2 + 2 (m%2) + {0, 1} of the tile
+          const int s0 = 8 * (m / 2) + 4 * g2 + 2 * (m % 2);
+          lo = s0 <= l32 ? lo : 0.f;
+          hi = s0 + 1 <= l32 ? hi : 0.f;
         }
-        gw[2 * q] = pack_bf16x2(v[0], v[1]);
-        gw[2 * q + 1] = pack_bf16x2(v[2], v[3]);
+        gw[m] = pack_bf16x2(lo, hi);
       }
       const u32x4 ga = u32x4{gw[0], gw[1], gw[2], gw[3]};  // rows s = 32j + [0, 16)
       const u32x4 gb = u32x4{gw[4], gw[5], gw[6], gw[7]};  // rows s = 32j + [16, 32)
+      const int kb = 32 * j + 4 * g2;
 #pragma unroll
       for (int pb = 0; pb < P / 32; ++pb) {
-        const uint16_t* xr = &sXt[32 * pb + l32][32 * j + 4 * g2];
-        const u32x2 x0 = *reinterpret_cast<const u32x2*>(xr);
-        const u32x2 x1 = *reinterpret_cast<const u32x2*>(xr + 8);
-        const u32x2 x2 = *reinterpret_cast<const u32x2*>(xr + 16);
-        const u32x2 x3 = *reinterpret_cast<const u32x2*>(xr + 24);
-        acc[pb] = mfma32x32x16(u32x4{x0[0], x0[1], x1[0], x1[1]}, ga, acc[pb]);
-        acc[pb] = mfma32x32x16(u32x4{x2[0], x2[1], x3[0], x3[1]}, gb, acc[pb]);
+        acc[pb] = mfma32x32x16(frag_tr<RBX>(sX, kb, kb + 8, 32 * pb, lane), ga, acc[pb]);
+        acc[pb] = mfma32x32x16(frag_tr<RBX>(sX, kb + 16, kb + 24, 32 * pb, lane), gb, acc[pb]);
       }
+    };
+#pragma unroll 1
+    for (int jj = 0; jj < irel; ++jj) {
+      u32x4 tcur[2] = {tnext[0], tnext[1]};
+      if (jj + 1 < irel) load_tile(jj + 1, tnext);
+      apply(jj, tcur, false);
     }
+    apply(irel, tdiag, true);
 
-    // ---- epilogue: + D x, round, store 4 consecutive p (8 bytes) per run
-    const int t = tl0 + l32;
+    // ---- epilogue: + D x (x re-read, from L2), round, store 4 consecutive p (8 bytes) per run
     if (t < T) {
+      u32x2 xr[P / 32][4];
+#pragma unroll
+      for (int pb = 0; pb < P / 32; ++pb)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          xr[pb][q] = *reinterpret_cast<const u32x2*>(&sX[lds_off<RBX>(lcol, 32 * pb + 8 * q + 4 * g2)]);
       uint16_t* yr = y + ((size_t(b) * T + t) * H + h) * P + 4 * g2;
 #pragma unroll
       for (int pb = 0; pb < P / 32; ++pb) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int p = 32 * pb + 8 * q + 4 * g2;
+          const u32x2 xv = xr[pb][q];
+          const float xs[4] = {bf16_lo(xv[0]), bf16_hi(xv[0]), bf16_lo(xv[1]), bf16_hi(xv[1])};
           float o[4];
 #pragma unroll
-          for (int rr = 0; rr < 4; ++rr)
-            o[rr] = acc[pb][4 * q + rr] + Dh * bf16_to_f32(sXt[p + rr][lcol]);
+          for (int rr = 0; rr < 4; ++rr) o[rr] = acc[pb][4 * q + rr] + Dh * xs[rr];
           *reinterpret_cast<u32x2*>(yr + 32 * pb + 8 * q) =
               u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
         }
@@ -222,9 +254,14 @@ hipError_t launch_np(const FwdShape& s, const void* x, const uint16_t* CB, const
                      hipStream_t st) {
   const int nsc = (s.T + kSC - 1) / kSC;
   const long blocks = long(s.b) * nsc * s.H;
-  hipLaunchKernelGGL((chunk_scan_mfma_kernel<N, P>), dim3(unsigned(blocks)), dim3(kThreads), 0, st,
-                     static_cast<const uint16_t*>(x), CB, static_cast<const uint16_t*>(C), Acs, dtq, Hb,
-                     D, static_cast<uint16_t*>(y), s.T, s.H, s.G, s.Q, s.nc, nsc);
+  if (s.Q == kSC)  // one chunk per super-chunk: its H_c^T is staged in LDS
+    hipLaunchKernelGGL((chunk_scan_mfma_kernel<N, P, true>), dim3(unsigned(blocks)), dim3(kThreads), 0,
+                       st, static_cast<const uint16_t*>(x), CB, static_cast<const uint16_t*>(C), Acs,
+                       dtq, Hb, D, static_cast<uint16_t*>(y), s.T, s.H, s.G, s.Q, s.nc, nsc);
+  else
+    hipLaunchKernelGGL((chunk_scan_mfma_kernel<N, P, false>), dim3(unsigned(blocks)), dim3(kThreads),
+                       0, st, static_cast<const uint16_t*>(x), CB, static_cast<const uint16_t*>(C), Acs,
+                       dtq, Hb, D, static_cast<uint16_t*>(y), s.T, s.H, s.G, s.Q, s.nc, nsc);
   return hipGetLastError();
 }
 

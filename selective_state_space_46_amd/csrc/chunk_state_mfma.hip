@@ -49,7 +49,8 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma_kernel(
   const int c = bc % nc, b = bc / nc;
   const int h0 = hg * KH;
   const int g = h0 / (H / G);
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = wave_id();  // wave-uniform (scalar register)
   const int g2 = lane >> 5;
   const long t0 = long(c) * Q;
 

@@ -35,6 +35,14 @@ template <typename T> __device__ __forceinline__ T from_f32(float v);
 template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
 template <> __device__ __forceinline__ uint16_t from_f32<uint16_t>(float v) { return f32_to_bf16(v); }
 
+// Index of this wave inside its work-group, as a wave-uniform (scalar) value:
+// threadIdx.x / 64 is the same on every lane of a wave, but the compiler only
+// treats it as uniform -- and branches on it as scalar branches instead of
+// executing both sides under an exec mask -- when it comes from readfirstlane.
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6);
+}
+
 // exp(x) through the hardware base-2 exponential: exp(x) = 2^(x * log2(e)).
 __device__ __forceinline__ float exp_fast(float x) {
   return __builtin_amdgcn_exp2f(x * 1.4426950408889634f);
