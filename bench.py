@@ -271,6 +271,21 @@ def bench_decode(hip, w, warmup=4):
     }
 
 
+def traffic_probe(w):
+    """Three forward calls, then three copies of a 256 MiB buffer: a plain
+    copy kernel that reads and writes exactly 256 MiB, against which the
+    FETCH_SIZE / WRITE_SIZE counters are calibrated."""
+    import torch
+    bench_fwd(Hip(), w, 3, 0)
+    src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log("[bench] traffic probe done (copy of 268435456 bytes x3)")
+
+
 def cpu_baseline(w, min_seconds=10.0):
     import oracle
     inp = workloads.make_fwd_inputs(w)
@@ -304,6 +319,9 @@ def main():
                     choices=sorted(workloads.FWD_WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip decode / other workloads")
+    ap.add_argument("--traffic-probe", action="store_true",
+                    help="only run a few forward calls and three copies of a 256 MiB buffer (for "
+                         "rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs and their calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -314,6 +332,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     hip = Hip()
     w = workloads.FWD_WORKLOADS[args.workload]
+    if args.traffic_probe:
+        traffic_probe(w)
+        return
     log(f"[bench] {w.name}: warmup {args.warmup}, steps {args.steps}")
     r = bench_fwd(hip, w, args.steps, args.warmup)
     log(f"[bench] {r['ms_per_step']:.4f} ms/step, {r['tokens_per_s']:.4g} tok/s, stages {r['stage_ms']}")
