@@ -76,7 +76,9 @@ typedef enum { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype;
 /* Supported ranges (checked; anything else is SSD_ERR_SHAPE / SSD_ERR_CHUNK):
  *   1 <= headdim <= 256, 1 <= dstate <= 256, chunk_len in {16,32,64,128,256},
  *   batch, seqlen, nheads, ngroups >= 1, nheads % ngroups == 0,
- *   batch <= 65535, ceil(seqlen / chunk_len) <= 65535.                     */
+ *   batch <= 65535, ceil(seqlen / chunk_len) <= 65535, and every kernel grid
+ *   of the forward pass under 2^32 work-items (for the bf16 matrix-core path
+ *   about batch * nchunks * nheads < 2^23, e.g. 8.4M chunk-heads).          */
 #define SSD_MAX_HEADDIM 256
 #define SSD_MAX_DSTATE 256
 

@@ -8,60 +8,57 @@
 // W^T (P x Q) . B (Q x N) contracted over the chunk's tokens
 // ("SSDアルゴリズムとチャンク分割": inside a chunk, matrix products).
 //
-// Work-group: one (batch, chunk) and KH heads of one B/C group, 4 waves. The
+// Work-group: one (batch, chunk, head), 8 waves. The
 // token axis is the contraction axis while x and B are stored token-major, so
 // each 64-token slice is copied into LDS in its natural row-major order
 // (coalesced 16-byte rows; W = w_s x_s scaled in fp32 per token row before its
 // single bf16 rounding) and the MFMA operands are read transposed with
-// ds_read_b64_tr_b16 (see mfma_util.h). The B slice is shared by the KH
-// heads; the next slice's rows are loaded into registers while the current
-// one feeds the matrix cores. Each wave owns KH*(P/32)*(N/32)/4 output tiles
-// of 32 x 32 (fp32 accumulators). Output tiles go to HBM as fp32 rows of 32
-// consecutive n.
+// ds_read_b64_tr_b16 (see mfma_util.h). The next slice's rows are loaded
+// into registers while the current one feeds the matrix cores. Each wave owns
+// (P/32)*(N/32)/8 output tiles of 32 x 32 (fp32 accumulators; one for
+// headdim 64, dstate 128). One head per work-group and eight waves measured
+// faster on MI355X than a head pair sharing the B slice (fewer accumulators,
+// twice the work-groups) or four waves (half the loads in flight per CU).
+// Output tiles go to HBM as fp32 rows of 32 consecutive n.
 #include "mfma_util.h"
 
 namespace ssd {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;
+constexpr int kWaves = kThreads / 64;
 constexpr int kSK = 64;          // tokens per contraction slice
 constexpr int kMaxQ = 256;
 
-template <int N, int P, int KH>
+template <int N, int P>
 __global__ __launch_bounds__(kThreads) void chunk_state_mfma_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ Bm, const float* __restrict__ Acs,
-    const float* __restrict__ dtq, float* __restrict__ S, int T, int H, int G, int Q, int nc,
-    int nhg) {
-  constexpr int RBB = N / 8, RBW = P / 8;           // 16-byte chunks per row
-  constexpr int CB_ = kSK * RBB, CW = KH * kSK * RBW;  // chunks per slice
-  constexpr int PER = (CB_ + CW) / kThreads;         // chunks per thread
-  static_assert((CB_ + CW) % kThreads == 0, "slice must split evenly");
+    const float* __restrict__ dtq, float* __restrict__ S, int T, int H, int G, int Q, int nc) {
+  constexpr int RBB = N / 8, RBW = P / 8;            // 16-byte chunks per row
+  constexpr int CB_ = kSK * RBB, CW = kSK * RBW;     // chunks per slice
+  constexpr int PER = (CB_ + CW + kThreads - 1) / kThreads;  // chunks per thread
   __shared__ __attribute__((aligned(16))) uint16_t sB[kSK * N];
-  __shared__ __attribute__((aligned(16))) uint16_t sW[KH][kSK * P];
-  __shared__ float sw[KH][kMaxQ];
+  __shared__ __attribute__((aligned(16))) uint16_t sW[kSK * P];
+  __shared__ float sw[kMaxQ];
 
   constexpr int NT = N / 32, PT = P / 32;
-  constexpr int TILES = KH * PT * NT;
-  constexpr int TPW = (TILES + 3) / 4;
+  constexpr int TILES = PT * NT;
+  constexpr int TPW = (TILES + kWaves - 1) / kWaves;
   const int id = xcd_swizzle(blockIdx.x, gridDim.x);
-  const int hg = id % nhg;
-  const int bc = id / nhg;
+  const int h = id % H;
+  const int bc = id / H;
   const int c = bc % nc, b = bc / nc;
-  const int h0 = hg * KH;
-  const int g = h0 / (H / G);
+  const int g = h / (H / G);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = wave_id();  // wave-uniform (scalar register)
   const int g2 = lane >> 5;
   const long t0 = long(c) * Q;
 
-  // w_s = exp(Acs_{Q-1} - Acs_s) * dt_s for the whole chunk, per head
-  for (int e = tid; e < KH * Q; e += kThreads) {
-    const int kh = e / Q, i = e % Q;
-    const size_t arow = ((size_t(b) * H + h0 + kh) * nc + c) * Q;
-    sw[kh][i] = exp_fast(Acs[arow + Q - 1] - Acs[arow + i]) * dtq[arow + i];
-  }
+  // w_s = exp(Acs_{Q-1} - Acs_s) * dt_s for the whole chunk
+  const size_t arow = ((size_t(b) * H + h) * nc + c) * Q;
+  for (int i = tid; i < Q; i += kThreads) sw[i] = exp_fast(Acs[arow + Q - 1] - Acs[arow + i]) * dtq[arow + i];
 
-  // this thread's 16-byte chunks of a slice: B rows first, then W rows
+  // this thread's 16-byte chunks of a slice: B rows first, then x rows
   auto load_slice = [&](int s0, u32x4 (&v)[PER]) {
 #pragma unroll
     for (int m = 0; m < PER; ++m) {
@@ -70,14 +67,14 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma_kernel(
         const int r = e / RBB, cc = e % RBB;
         const long t = min(t0 + s0 + r, long(T) - 1);
         v[m] = load16(Bm + ((size_t(b) * T + t) * G + g) * N + 8 * cc);
-      } else {
-        const int e2 = e - CB_;
-        const int kh = e2 / (kSK * RBW), r = (e2 / RBW) % kSK, cc = e2 % RBW;
+      } else if (e < CB_ + CW) {
+        const int r = (e - CB_) / RBW, cc = (e - CB_) % RBW;
         const long t = min(t0 + s0 + r, long(T) - 1);
-        v[m] = load16(x + ((size_t(b) * T + t) * H + h0 + kh) * P + 8 * cc);
+        v[m] = load16(x + ((size_t(b) * T + t) * H + h) * P + 8 * cc);
       }
     }
   };
+  // rows past the chunk or the sequence become zeros; x rows are scaled by w_s
   auto store_slice = [&](int s0, const u32x4 (&v)[PER]) {
 #pragma unroll
     for (int m = 0; m < PER; ++m) {
@@ -86,14 +83,13 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma_kernel(
         const int r = e / RBB, cc = e % RBB;
         const bool in = r < Q - s0 && t0 + s0 + r < T;
         *reinterpret_cast<u32x4*>(&sB[lds_off<RBB>(r, 8 * cc)]) = keep_or_zero(in, v[m]);
-      } else {
-        const int e2 = e - CB_;
-        const int kh = e2 / (kSK * RBW), r = (e2 / RBW) % kSK, cc = e2 % RBW;
-        const float w = (r < Q - s0 && t0 + s0 + r < T) ? sw[kh][s0 + r] : 0.f;
+      } else if (e < CB_ + CW) {
+        const int r = (e - CB_) / RBW, cc = (e - CB_) % RBW;
+        const float w = (r < Q - s0 && t0 + s0 + r < T) ? sw[s0 + r] : 0.f;
         u32x4 o;
 #pragma unroll
         for (int q = 0; q < 4; ++q) o[q] = pack_bf16x2(bf16_lo(v[m][q]) * w, bf16_hi(v[m][q]) * w);
-        *reinterpret_cast<u32x4*>(&sW[kh][lds_off<RBW>(r, 8 * cc)]) = o;
+        *reinterpret_cast<u32x4*>(&sW[lds_off<RBW>(r, 8 * cc)]) = o;
       }
     }
   };
@@ -112,14 +108,12 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma_kernel(
     const int ksteps = min(kSK, Q - s0) / 16;
 #pragma unroll
     for (int m = 0; m < TPW; ++m) {
-      const int tile = wave + 4 * m;
+      const int tile = wave + kWaves * m;
       if (tile < TILES) {
-        const int kh = tile / (PT * NT);
-        const int r = tile % (PT * NT);
-        const int pb = r / NT, nb = r % NT;
+        const int pb = tile / NT, nb = tile % NT;
         for (int kk = 0; kk < ksteps; ++kk) {
           const int kb = 16 * kk + 8 * g2;
-          const u32x4 a = frag_tr<RBW>(sW[kh], kb, kb + 4, 32 * pb, lane);
+          const u32x4 a = frag_tr<RBW>(sW, kb, kb + 4, 32 * pb, lane);
           const u32x4 bb = frag_tr<RBB>(sB, kb, kb + 4, 32 * nb, lane);
           acc[m] = mfma32x32x16(a, bb, acc[m]);
         }
@@ -128,14 +122,12 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma_kernel(
   }
 
   const int l32 = lane & 31;
+  float* out = S + ((size_t(b) * nc + c) * H + h) * size_t(P) * N;
 #pragma unroll
   for (int m = 0; m < TPW; ++m) {
-    const int tile = wave + 4 * m;
+    const int tile = wave + kWaves * m;
     if (tile < TILES) {
-      const int kh = tile / (PT * NT);
-      const int r = tile % (PT * NT);
-      const int pb = r / NT, nb = r % NT;
-      float* out = S + ((size_t(b) * nc + c) * H + h0 + kh) * size_t(P) * N;
+      const int pb = tile / NT, nb = tile % NT;
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
         const int p = 32 * pb + 8 * (q / 4) + 4 * g2 + (q % 4);
@@ -145,26 +137,14 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma_kernel(
   }
 }
 
-template <int N, int P, int KH>
-hipError_t launch_t(const FwdShape& s, const void* x, const void* B, const float* Acs,
-                    const float* dtq, float* S, hipStream_t st) {
-  const int nhg = s.H / KH;
-  const long blocks = long(s.b) * s.nc * nhg;
-  hipLaunchKernelGGL((chunk_state_mfma_kernel<N, P, KH>), dim3(unsigned(blocks)), dim3(kThreads), 0,
-                     st, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(B), Acs, dtq, S,
-                     s.T, s.H, s.G, s.Q, s.nc, nhg);
-  return hipGetLastError();
-}
-
 template <int N, int P>
 hipError_t launch_np(const FwdShape& s, const void* x, const void* B, const float* Acs,
                      const float* dtq, float* S, hipStream_t st) {
-  // two heads per work-group share the staged B slice while the fp32
-  // accumulators stay within 64 registers per lane (two waves per SIMD)
-  if constexpr ((P / 32) * (N / 32) * 2 <= 16) {
-    if ((s.H / s.G) % 2 == 0) return launch_t<N, P, 2>(s, x, B, Acs, dtq, S, st);
-  }
-  return launch_t<N, P, 1>(s, x, B, Acs, dtq, S, st);
+  const long blocks = long(s.b) * s.nc * s.H;
+  hipLaunchKernelGGL((chunk_state_mfma_kernel<N, P>), dim3(unsigned(blocks)), dim3(kThreads), 0, st,
+                     static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(B), Acs, dtq, S,
+                     s.T, s.H, s.G, s.Q, s.nc);
+  return hipGetLastError();
 }
 
 template <int N>

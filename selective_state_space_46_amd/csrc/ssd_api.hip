@@ -3,6 +3,8 @@
 // nothing is launched or written.
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "ssd_internal.h"
 
 using namespace ssd;
@@ -48,6 +50,31 @@ FwdShape make_shape(int batch, int seqlen, int H, int P, int N, int G, int Q) {
   return s;
 }
 
+// The largest one-dimensional launch of the forward pass must stay below 2^32
+// work-items (the grid limit). Work-items per launch, from the launchers:
+//   chunk_cumsum      64 per (b, c, h) row
+//   chunk_scores      64 per 32 x 32 tile, lpc (lpc + 1) / 2 tiles per (b, c, g)
+//   chunk_state_mfma  512 per (b, c, h)
+//   state_passing     256 per 16 x 64 tile of each (b, h) state, or one per
+//                     state element when dstate % 4 != 0
+//   chunk_scan_mfma   256 per (b, 256-token super-chunk, h)
+// The generic kernels use three-dimensional grids and stay far below it.
+bool grids_fit(const FwdShape& s, bool mfma) {
+  const double lim = 4294967295.0;
+  const double bch = double(s.b) * s.nc * s.H;
+  const double bh = double(s.b) * s.H;
+  const int lpc = s.Q / 32;
+  double worst = 64.0 * bch;
+  worst = std::max(worst, s.N % 4 == 0 ? 256.0 * bh * ((s.P + 15) / 16) * ((s.N + 63) / 64)
+                                       : bh * s.P * s.N);
+  if (mfma) {
+    worst = std::max(worst, 64.0 * double(s.b) * s.nc * s.G * (lpc * (lpc + 1) / 2));
+    worst = std::max(worst, 512.0 * bch);
+    worst = std::max(worst, 256.0 * bh * ((s.T + 255) / 256));
+  }
+  return worst < lim;
+}
+
 }  // namespace
 
 extern "C" {
@@ -72,7 +99,7 @@ size_t ssd_chunk_scan_fwd_workspace(int batch, int seqlen, int nheads, int headd
   if (!dtype_ok(dtype) || !is_chunk_ok(chunk_len)) return 0;
   if (check_dims(batch, seqlen, nheads, headdim, dstate, ngroups) != SSD_OK) return 0;
   const FwdShape s = make_shape(batch, seqlen, nheads, headdim, dstate, ngroups, chunk_len);
-  if (s.nc > 65535) return 0;
+  if (s.nc > 65535 || !grids_fit(s, use_mfma_path(s, dtype))) return 0;
   return ws_layout(s, use_mfma_path(s, dtype)).total;
 }
 
@@ -96,6 +123,7 @@ ssd_status ssd_chunk_scan_fwd_timed(const void* x, const void* dt, const float* 
   const FwdShape s = make_shape(batch, seqlen, nheads, headdim, dstate, ngroups, chunk_len);
   if (s.nc > 65535) return SSD_ERR_SHAPE;
   const bool mfma = use_mfma_path(s, dtype);
+  if (!grids_fit(s, mfma)) return SSD_ERR_SHAPE;
   const WsLayout w = ws_layout(s, mfma);
   if (workspace_bytes < w.total) return SSD_ERR_WORKSPACE;
 

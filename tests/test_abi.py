@@ -72,6 +72,12 @@ def test_workspace_query():
     assert ws(1, 0, 2, 16, 16, 1, 64) == 0            # T = 0
     assert ws(1, 256, 2, 257, 16, 1, 64) == 0         # headdim too large
     assert ws(1, 256, 2, 16, 16, 1, 64, dt=5) == 0    # dtype
+    # 2^23 chunk-heads: the bf16 matrix-core chunk_state grid (512 work-items
+    # each) would reach 2^32 work-items; the fp32 path's grids stay below it
+    big = (1024, 16384, 128, 64, 128, 1, 256)
+    assert ws(*big, dt=ssd.SSD_BF16) == 0
+    assert ws(*big, dt=ssd.SSD_F32) == expect(1024, 16384, 128, 64, 128, 256, ssd.SSD_F32)
+    assert ws(1024, 16384 - 256, 128, 64, 128, 1, 256, dt=ssd.SSD_BF16) > 0
 
 
 def fwd(L, **kw):
@@ -94,6 +100,7 @@ def test_forward_argument_errors(L):
     assert fwd(L, Q=100) == 4
     assert fwd(L, Q=512) == 4
     assert fwd(L, T=16 * 65536, Q=16) == 2          # more chunks than the grid allows
+    assert fwd(L, b=1024, T=16384, H=128, P=64, N=128, Q=256, dtype=1) == 2   # 2^32 work-items
     for k in ("x", "dt", "A", "B", "C", "y"):
         assert fwd(L, **{k: None}) == 1, k
     assert fwd(L, ws=None) == 5
