@@ -36,6 +36,10 @@ def compile_flags() -> list:
         "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", f"--offload-arch={ARCH}",
         # keep hipcc from forming packed fp32 VALU instructions
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # matrix-core results in VGPRs: the kernels scale and round MFMA
+        # outputs with VALU code, which AGPR results would first have to
+        # copy out with v_accvgpr_read (and back with v_accvgpr_write)
+        "-mllvm", "-amdgpu-mfma-vgpr-form",
         "-Wall", "-Wno-unused-function",
         "-I", INCLUDE, "-I", CSRC,
     ]

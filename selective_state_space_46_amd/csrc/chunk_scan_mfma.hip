@@ -114,17 +114,38 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_mfma_kernel(
   }
   if constexpr (HLDS) {
     const uint16_t* hsrc = Hb + ((size_t(b) * nc + c0) * H + h) * size_t(P) * N;
-    for (int e = tid; e < P * (N / 8); e += kThreads) {
-      const int p = e / (N / 8), seg = e % (N / 8);
-      *reinterpret_cast<u32x4*>(&sHt[p][8 * seg]) = load16(hsrc + size_t(p) * N + 8 * seg);
-    }
+    static_assert(kThreads % (N / 8) == 0, "H staging shape");
+    constexpr int kStep = kThreads / (N / 8);        // rows p per pass
+    const int p0 = tid / (N / 8), seg = tid % (N / 8);
+#pragma unroll
+    for (int k = 0; k < (P + kStep - 1) / kStep; ++k)
+      if (P % kStep == 0 || p0 + k * kStep < P)
+        *reinterpret_cast<u32x4*>(&sHt[p0 + k * kStep][8 * seg]) =
+            load16(hsrc + size_t(p0 + k * kStep) * N + 8 * seg);
   }
-  // raw x, token-major, swizzled: issued with the loads above
-  for (int e = tid; e < kSC * RBX; e += kThreads) {
-    const int r = e / RBX, cc = e % RBX;
-    u32x4 v = load16(x + ((size_t(b) * T + min(t0 + r, T - 1)) * H + h) * P + 8 * cc);
-    if (!full) v = keep_or_zero(t0 + r < T, v);
-    *reinterpret_cast<u32x4*>(&sX[lds_off<RBX>(r, 8 * cc)]) = v;
+  // raw x, token-major, swizzled: issued with the loads above. Thread tid
+  // copies 16-byte chunk tid % RBX of rows tid / RBX + k kStep; kStep is a
+  // multiple of the swizzle period (16 rows), so every row of the thread has
+  // the same swizzle and its LDS offsets differ by constants.
+  static_assert(kThreads % RBX == 0 && (kThreads / RBX) % 16 == 0, "x staging shape");
+  {
+    constexpr int kStep = kThreads / RBX;
+    const int r0 = tid / RBX, cc = tid % RBX;
+    uint16_t* dst = &sX[lds_off<RBX, true>(r0, 8 * cc)];
+    if (full) {
+      const uint16_t* src = x + ((size_t(b) * T + t0 + r0) * H + h) * P + 8 * cc;
+      const size_t step = size_t(kStep) * H * P;
+#pragma unroll
+      for (int k = 0; k < RBX; ++k)
+        *reinterpret_cast<u32x4*>(dst + k * kStep * P) = load16(src + k * step);
+    } else {
+#pragma unroll
+      for (int k = 0; k < RBX; ++k) {
+        const int r = r0 + k * kStep;
+        const u32x4 v = load16(x + ((size_t(b) * T + min(t0 + r, T - 1)) * H + h) * P + 8 * cc);
+        *reinterpret_cast<u32x4*>(dst + k * kStep * P) = keep_or_zero(t0 + r < T, v);
+      }
+    }
   }
   __syncthreads();
 
@@ -210,8 +231,8 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_mfma_kernel(
       const int kb = 32 * j + 4 * g2;
 #pragma unroll
       for (int pb = 0; pb < P / 32; ++pb) {
-        acc[pb] = mfma32x32x16(frag_tr<RBX>(sX, kb, kb + 8, 32 * pb, lane), ga, acc[pb]);
-        acc[pb] = mfma32x32x16(frag_tr<RBX>(sX, kb + 16, kb + 24, 32 * pb, lane), gb, acc[pb]);
+        acc[pb] = mfma32x32x16(frag_tr<RBX, true>(sX, kb, kb + 8, 32 * pb, lane), ga, acc[pb]);
+        acc[pb] = mfma32x32x16(frag_tr<RBX, true>(sX, kb + 16, kb + 24, 32 * pb, lane), gb, acc[pb]);
       }
     };
 #pragma unroll 1
@@ -229,7 +250,7 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_mfma_kernel(
       for (int pb = 0; pb < P / 32; ++pb)
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-          xr[pb][q] = *reinterpret_cast<const u32x2*>(&sX[lds_off<RBX>(lcol, 32 * pb + 8 * q + 4 * g2)]);
+          xr[pb][q] = *reinterpret_cast<const u32x2*>(&sX[lds_off<RBX, true>(lcol, 32 * pb + 8 * q + 4 * g2)]);
       uint16_t* yr = y + ((size_t(b) * T + t) * H + h) * P + 4 * g2;
 #pragma unroll
       for (int pb = 0; pb < P / 32; ++pb) {

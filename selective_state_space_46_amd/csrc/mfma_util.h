@@ -68,24 +68,35 @@ __device__ __forceinline__ u32x4 load16(const uint16_t* p) { return *reinterpret
 // row/column. Two such reads give one 8-element operand fragment.
 //
 // Rows are stored as 16-byte chunks, chunk c of row r at chunk c ^ swz(r).
-// With RB 16-byte chunks per row, swz keeps the four rows one transposed read
-// touches on disjoint banks (64 banks of 4 bytes):
+// LDS has 64 banks of 4 bytes and serves an 8-byte read 32 lanes per cycle
+// (measured on MI355X with SQ_LDS_BANK_CONFLICT). Transposed reads: 32 lanes
+// read four rows kb .. kb+3 (kb % 4 == 0), 64 bytes (four aligned chunks) of
+// each, which must cover all 64 banks. With RB chunks per row:
 //   RB = 4  (64 B rows):  rows start 16 banks apart            -> swz = 0
 //   RB = 8  (128 B rows): rows r, r+1 differ by 32 banks        -> swz = 4 ((r >> 1) & 1)
 //   RB >= 16 (256 B, 512 B rows): every row starts at bank 0    -> swz = 4 (r & 3)
-// Row-major 16-byte writes of consecutive chunks stay conflict-free under it.
-// ---------------------------------------------------------------------------
-template <int RB>
+// ROWS = true adds a second access shape, row reads: 32 lanes read 8 bytes of
+// the same chunk in 32 consecutive rows (the chunk_scan epilogue). Under the
+// swizzle above they are 8-way conflicts; XOR-ing (r >> 2) & 3 into the low
+// chunk bits as well rotates chunks inside an aligned group of four across
+// row quads, which brings them to 2-way (the floor: 32 lanes x 8 bytes of one
+// half-chunk column fill only 32 two-bank slots) and leaves transposed reads
+// conflict-free. It costs a few more address instructions where the row
+// varies, so tiles without row reads keep the plain form.
+// Row-major 16-byte writes of whole rows are conflict-free under both (any
+// chunk permutation inside a row keeps them so).
+template <int RB, bool ROWS = false>
 __device__ __forceinline__ int lds_swz(int r) {
-  if constexpr (RB <= 4) return 0;
-  else if constexpr (RB == 8) return 4 * ((r >> 1) & 1);
-  else return 4 * (r & 3);
+  const int rot = ROWS ? ((r >> 2) & 3) : 0;
+  if constexpr (RB <= 4) return rot;
+  else if constexpr (RB == 8) return (4 * ((r >> 1) & 1)) | rot;
+  else return (4 * (r & 3)) | rot;
 }
 
 // Element offset of (row r, column col) in a swizzled tile with RB chunks/row.
-template <int RB>
+template <int RB, bool ROWS = false>
 __device__ __forceinline__ int lds_off(int r, int col) {
-  return r * (RB * 8) + (((col >> 3) ^ lds_swz<RB>(r)) << 3) + (col & 7);
+  return r * (RB * 8) + (((col >> 3) ^ lds_swz<RB, ROWS>(r)) << 3) + (col & 7);
 }
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -104,11 +115,11 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* tile, int elem_of
 // rows are the k axis: k rows kb1 .. kb1+3 and kb2 .. kb2+3 (kb1, kb2 already
 // include this lane's 8 (L/32) offset, so any k permutation shared with the
 // other operand can be expressed).
-template <int RB>
+template <int RB, bool ROWS = false>
 __device__ __forceinline__ u32x4 frag_tr(const uint16_t* tile, int kb1, int kb2, int m0, int lane) {
   const int q = lane & 15, m = m0 + 16 * ((lane >> 4) & 1) + 4 * (q & 3);
-  const u32x2 lo = lds_read_tr16(tile, lds_off<RB>(kb1 + (q >> 2), m));
-  const u32x2 hi = lds_read_tr16(tile, lds_off<RB>(kb2 + (q >> 2), m));
+  const u32x2 lo = lds_read_tr16(tile, lds_off<RB, ROWS>(kb1 + (q >> 2), m));
+  const u32x2 hi = lds_read_tr16(tile, lds_off<RB, ROWS>(kb2 + (q >> 2), m));
   return u32x4{lo[0], lo[1], hi[0], hi[1]};
 }
 
