@@ -11,13 +11,18 @@
 // The second term brings in all earlier chunks through H_c, the state entering
 // chunk c (youngju.dev page, "SSDアルゴリズムとチャンク分割").
 //
-// Decay factorisation: for l, s in the same chunk and s in the 32-token block
-// that starts at s0,
-//   exp(Acs_l - Acs_s) dt_s = exp(Acs_l - Acs_s0) * [exp(Acs_s0 - Acs_s) dt_s]
-// The bracket depends on s only and is folded into X once per work-group
-// (X'_s = bracket_s x_s, at most exp(32 max|dt A|) x_s, well inside bf16
-// range); the first factor is <= 1 and depends on (l, block of s): one
-// exponential per lane and tile, one multiply per score.
+// Decay. For l, s in the same chunk, s <= l, the weight exp(Acs_l - Acs_s)
+// dt_s is at most dt_s, but a product of per-token factors can overflow when
+// one factor has a positive exponent (a factor exp(Acs_a - Acs_s) with s
+// after a grows like exp(sum of dt |A|) over the span). Both factors used
+// here have exponents <= 0:
+//   s in an earlier 32-token column block that ends at token e:
+//     exp(Acs_l - Acs_s) dt_s = exp(Acs_l - Acs_e) * [exp(Acs_e - Acs_s) dt_s]
+//     the bracket depends on s only (a per-token table in LDS), the first
+//     factor is one exponential per lane and tile;
+//   s in the same 32-token block as l (the diagonal tile): one exponential
+//     per element, exp(min(Acs_l - Acs_s, 0)) dt_s, masked to s <= l.
+// Factors that underflow to zero stand for weights that are smaller still.
 //
 // Work-group: one batch row, one 256-token super-chunk (256/Q chunks), one
 // head; 4 waves. The C B^T tiles come precomputed once per group
@@ -29,13 +34,12 @@
 //      state_passing) when the super-chunk is one chunk, C_l rows straight from
 //      HBM; then y^T *= exp(Acs_l).
 //   2. for each column block s <= l of the chunk: the C B^T tile (lane =
-//      column l, registers = rows s in runs of 4) times exp(Acs_l - Acs_s0),
-//      masked to s <= l on the diagonal tile only, rounded to bf16, is the B
-//      operand of y^T += X'^T G^T under a k permutation that the X' operand
-//      reproduces: X' sits in LDS in natural token-major order (swizzled
-//      16-byte chunks) and is read transposed with ds_read_b64_tr_b16. Tiles
-//      are loaded two blocks ahead of use.
-//   3. + D x (x re-read from L2), bf16 rounding, 8-byte stores of 4
+//      column l, registers = rows s in runs of 4) times the decay, rounded to
+//      bf16, is the B operand of y^T += X^T G^T under a k permutation that the
+//      X operand reproduces: x sits in LDS in natural token-major order
+//      (swizzled 16-byte chunks) and is read transposed with
+//      ds_read_b64_tr_b16. Tiles are loaded one tile ahead of use.
+//   3. + D x (x from the same LDS tile), bf16 rounding, 8-byte stores of 4
 //      consecutive p.
 #include "mfma_util.h"
 
@@ -58,7 +62,8 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_mfma_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t sX[kSC * P];
   __shared__ __attribute__((aligned(16))) uint16_t sHt[HROWS][kHS];
   __shared__ __attribute__((aligned(16))) float sA[kSC];  // Acs * log2(e)
-  __shared__ __attribute__((aligned(16))) float sF[kSC];  // exp(Acs[block start] - Acs_s) * dt_s
+  __shared__ __attribute__((aligned(16))) float sF[kSC];  // exp(Acs[block end] - Acs_s) * dt_s
+  __shared__ __attribute__((aligned(16))) float sD[kSC];  // dt_s
 
   const int id = xcd_swizzle(blockIdx.x, gridDim.x);
   const int h = id % H;
@@ -102,15 +107,17 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_mfma_kernel(
   // ---- staging 1: Acs, the per-token factor, H_c^T
   for (int i = tid; i < kSC; i += kThreads) {
     const int c = c0 + i / Q;
-    float a = 0.f, f = 0.f;
+    float a = 0.f, f = 0.f, d = 0.f;
     if (c < nc) {
       const size_t row = ((size_t(b) * H + h) * nc + c) * Q;
       const int q = i % Q;
       a = Acs[row + q] * kLog2e;
-      f = __builtin_amdgcn_exp2f(Acs[row + (q & ~31)] * kLog2e - a) * dtq[row + q];
+      d = dtq[row + q];
+      f = __builtin_amdgcn_exp2f(Acs[row + (q | 31)] * kLog2e - a) * d;  // exponent <= 0
     }
     sA[i] = a;
     sF[i] = f;
+    sD[i] = d;
   }
   if constexpr (HLDS) {
     const uint16_t* hsrc = Hb + ((size_t(b) * nc + c0) * H + h) * size_t(P) * N;
@@ -204,25 +211,36 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_mfma_kernel(
 
     // ---- y^T += X'^T G^T over the column blocks of the chunk
     const float al = sA[lcol];
-    // one column block: G^T = tile * exp(Acs_l - Acs_{32j}) (masked to s <= l
-    // on the diagonal block), then two MFMAs per 32 p
+    // one column block j: G^T = tile * decay (register pair m of the tile
+    // holds rows s = 32 j + 8 (m/2) + 4 g2 + 2 (m%2) + {0, 1}), then two MFMAs
+    // per 32 p. Off the diagonal (every s < every l) the decay is
+    // exp(Acs_l - Acs_e) * [exp(Acs_e - Acs_s) dt_s] with e = 32 j + 31, the
+    // column block's last token: both factors are <= 1. On the diagonal it is
+    // exp(Acs_l - Acs_s) dt_s per element, masked to s <= l.
     auto apply = [&](const int jj, const u32x4 (&tile)[2], const bool diag) {
       const int j = jfirst + jj;
-      const float lfac = __builtin_amdgcn_exp2f(al - sA[32 * j]);  // exp(Acs_l - Acs_{32j}) <= 1
       uint32_t gw[8];
-      f32x4 fs[4];
+      f32x4 fa[4], fb[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) fs[q] = *reinterpret_cast<const f32x4*>(&sF[32 * j + 8 * q + 4 * g2]);
+      for (int q = 0; q < 4; ++q) {
+        fa[q] = *reinterpret_cast<const f32x4*>(&(diag ? sA : sF)[32 * j + 8 * q + 4 * g2]);
+        if (diag) fb[q] = *reinterpret_cast<const f32x4*>(&sD[32 * j + 8 * q + 4 * g2]);
+      }
+      const float lfac = diag ? 0.f : __builtin_amdgcn_exp2f(al - sA[32 * j + 31]);
 #pragma unroll
       for (int m = 0; m < 8; ++m) {
         const uint32_t w = tile[m / 4][m % 4];
-        float lo = bf16_lo(w) * lfac * fs[m / 2][2 * (m % 2)];
-        float hi = bf16_hi(w) * lfac * fs[m / 2][2 * (m % 2) + 1];
+        const int k = 2 * (m % 2);
+        float lo, hi;
         if (diag) {
-          // register pair m holds rows 8 (m/2) + 4 g2 + 2 (m%2) + {0, 1} of the tile
-          const int s0 = 8 * (m / 2) + 4 * g2 + 2 * (m % 2);
-          lo = s0 <= l32 ? lo : 0.f;
-          hi = s0 + 1 <= l32 ? hi : 0.f;
+          const int s0 = 8 * (m / 2) + 4 * g2 + k;
+          const float elo = __builtin_amdgcn_exp2f(fminf(al - fa[m / 2][k], 0.f)) * fb[m / 2][k];
+          const float ehi = __builtin_amdgcn_exp2f(fminf(al - fa[m / 2][k + 1], 0.f)) * fb[m / 2][k + 1];
+          lo = s0 <= l32 ? bf16_lo(w) * elo : 0.f;
+          hi = s0 + 1 <= l32 ? bf16_hi(w) * ehi : 0.f;
+        } else {
+          lo = bf16_lo(w) * lfac * fa[m / 2][k];
+          hi = bf16_hi(w) * lfac * fa[m / 2][k + 1];
         }
         gw[m] = pack_bf16x2(lo, hi);
       }

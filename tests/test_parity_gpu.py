@@ -68,6 +68,19 @@ def test_bf16_large_shape_small_batch(q):
     _check_full(w, workloads.make_fwd_inputs(w))
 
 
+@pytest.mark.parametrize("dtype,q", [("f32", 64), ("bf16", 64), ("bf16", 256)])
+def test_fast_decay(dtype, q):
+    """dt |A| up to 32 per token: the summed exponent over 31 tokens reaches
+    about 280 here, far outside the fp32 range (about 88), so any product of decay
+    factors in which one factor has a positive exponent overflows. Every
+    output must stay finite and within the bar."""
+    w = workloads.with_shape(workloads.MAMBA2_130M, batch=2, seqlen=2 * 256 + 77, dt_mode="fast",
+                             init="normal0.1", chunk_len=q, dtype=dtype, seed=1400 + q)
+    inp = workloads.make_fwd_inputs(w)
+    assert float(np.max(inp["dt"][..., None] * -inp["A"])) > 20.0
+    _check_full(w, inp)
+
+
 def test_long_context_shape_short_sequence():
     w = workloads.with_shape(workloads.LONG_128K, seqlen=4 * 256 + 3, seed=1300)
     _check_full(w, workloads.make_fwd_inputs(w))

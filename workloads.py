@@ -14,7 +14,8 @@ negative scalar per head, A = -exp(A_log)):
 
     x      ~ N(0, 1)
     dt     = clamp(softplus(N(0,1) - 4), 1e-3, 0.1)   (long-context workload:
-             dt = exp(U(ln 1e-4, ln 1e-1)), no clamp)
+             dt = exp(U(ln 1e-4, ln 1e-1)), no clamp; fast-decay test cases:
+             dt = exp(U(ln 1e-2, ln 2)), so dt |A| reaches 32 per token)
     A_h    = -exp(U(0, ln 16))                       in [-16, -1]
     B, C   ~ N(0, 1) / sqrt(N)
     D_h    ~ N(0, 1)
@@ -67,7 +68,7 @@ class FwdWorkload:
     ngroups: int
     chunk_len: int
     dtype: str                 # "f32" or "bf16": dtype of x, dt, B, C, y
-    dt_mode: str = "softplus"  # "softplus" (clamped) or "loguniform"
+    dt_mode: str = "softplus"  # "softplus" (clamped), "loguniform" or "fast"
     init: str = "zero"         # "zero" or "normal0.1"
     seed: int = 0
 
@@ -130,6 +131,9 @@ def draw_dt(rng: np.random.Generator, shape, mode: str) -> np.ndarray:
         return np.clip(_softplus(v), 1e-3, 0.1).astype(np.float32)
     if mode == "loguniform":
         u = rng.uniform(math.log(1e-4), math.log(1e-1), size=shape)
+        return np.exp(u).astype(np.float32)
+    if mode == "fast":
+        u = rng.uniform(math.log(1e-2), math.log(2.0), size=shape)
         return np.exp(u).astype(np.float32)
     raise ValueError(mode)
 
