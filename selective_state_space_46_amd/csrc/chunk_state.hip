@@ -88,10 +88,8 @@ __global__ __launch_bounds__(kThreads) void chunk_state_generic(
 
 }  // namespace
 
-hipError_t launch_chunk_state(const FwdShape& s, ssd_dtype type, bool mfma, const void* x,
-                              const void* B, const float* Acs, const float* dtq, float* S,
-                              hipStream_t st) {
-  if (mfma) return launch_chunk_state_mfma(s, x, B, Acs, dtq, S, st);
+hipError_t launch_chunk_state(const FwdShape& s, ssd_dtype type, const void* x, const void* B,
+                              const float* Acs, const float* dtq, float* S, hipStream_t st) {
   const int ntn = (s.N + kRows - 1) / kRows;
   dim3 grid(s.H * ntn, s.nc, s.b);
   if (type == SSD_BF16)

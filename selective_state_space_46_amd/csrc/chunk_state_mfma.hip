@@ -8,6 +8,11 @@
 // W^T (P x Q) . B (Q x N) contracted over the chunk's tokens
 // ("SSDアルゴリズムとチャンク分割": inside a chunk, matrix products).
 //
+// The work-group first computes its chunk's in-chunk cumulative sums
+// Acs_s = sum_{k <= s} dt_k A_h (the decay exponents; on this path it replaces
+// chunk_cumsum.hip) and writes them, with dt, for state_passing and
+// chunk_scan.
+//
 // Work-group: one (batch, chunk, head), 8 waves. The
 // token axis is the contraction axis while x and B are stored token-major, so
 // each 64-token slice is copied into LDS in its natural row-major order
@@ -32,14 +37,16 @@ constexpr int kMaxQ = 256;
 
 template <int N, int P>
 __global__ __launch_bounds__(kThreads) void chunk_state_mfma_kernel(
-    const uint16_t* __restrict__ x, const uint16_t* __restrict__ Bm, const float* __restrict__ Acs,
-    const float* __restrict__ dtq, float* __restrict__ S, int T, int H, int G, int Q, int nc) {
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ Bm, const uint16_t* __restrict__ dt,
+    const float* __restrict__ A, float* __restrict__ Acs, float* __restrict__ dtq, float* __restrict__ S,
+    int T, int H, int G, int Q, int nc) {
   constexpr int RBB = N / 8, RBW = P / 8;            // 16-byte chunks per row
   constexpr int CB_ = kSK * RBB, CW = kSK * RBW;     // chunks per slice
   constexpr int PER = (CB_ + CW + kThreads - 1) / kThreads;  // chunks per thread
   __shared__ __attribute__((aligned(16))) uint16_t sB[kSK * N];
   __shared__ __attribute__((aligned(16))) uint16_t sW[kSK * P];
   __shared__ float sw[kMaxQ];
+  __shared__ float sacs[kMaxQ], sdt[kMaxQ], sred[kWaves];
 
   constexpr int NT = N / 32, PT = P / 32;
   constexpr int TILES = PT * NT;
@@ -54,9 +61,34 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma_kernel(
   const int g2 = lane >> 5;
   const long t0 = long(c) * Q;
 
-  // w_s = exp(Acs_{Q-1} - Acs_s) * dt_s for the whole chunk
+  // Acs_s = sum_{k <= s} dt_k A_h inside the chunk (dt = 0 past the end of
+  // the sequence): one token per thread, a wave scan, then the totals of the
+  // waves before. Written out for state_passing and chunk_scan.
+  static_assert(kMaxQ <= kThreads, "one token per thread");
   const size_t arow = ((size_t(b) * H + h) * nc + c) * Q;
-  for (int i = tid; i < Q; i += kThreads) sw[i] = exp_fast(Acs[arow + Q - 1] - Acs[arow + i]) * dtq[arow + i];
+  {
+    const float Ah = A[h];
+    float d = 0.f;
+    if (tid < Q && t0 + tid < T) d = bf16_to_f32(dt[(size_t(b) * T + t0 + tid) * H + h]);
+    float v = d * Ah;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float o = __shfl_up(v, off, 64);
+      if (lane >= off) v += o;
+    }
+    if (lane == 63) sred[wave] = v;
+    __syncthreads();
+    for (int w = 0; w < wave; ++w) v += sred[w];
+    if (tid < Q) {
+      Acs[arow + tid] = v;
+      dtq[arow + tid] = d;
+      sacs[tid] = v;
+      sdt[tid] = d;
+    }
+    __syncthreads();
+  }
+  // w_s = exp(Acs_{Q-1} - Acs_s) * dt_s for the whole chunk
+  for (int i = tid; i < Q; i += kThreads) sw[i] = exp_fast(sacs[Q - 1] - sacs[i]) * sdt[i];
 
   // this thread's 16-byte chunks of a slice: B rows first, then x rows
   auto load_slice = [&](int s0, u32x4 (&v)[PER]) {
@@ -138,22 +170,22 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma_kernel(
 }
 
 template <int N, int P>
-hipError_t launch_np(const FwdShape& s, const void* x, const void* B, const float* Acs,
-                     const float* dtq, float* S, hipStream_t st) {
+hipError_t launch_np(const FwdShape& s, const void* x, const void* B, const void* dt, const float* A,
+                     float* Acs, float* dtq, float* S, hipStream_t st) {
   const long blocks = long(s.b) * s.nc * s.H;
   hipLaunchKernelGGL((chunk_state_mfma_kernel<N, P>), dim3(unsigned(blocks)), dim3(kThreads), 0, st,
-                     static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(B), Acs, dtq, S,
-                     s.T, s.H, s.G, s.Q, s.nc);
+                     static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(B),
+                     static_cast<const uint16_t*>(dt), A, Acs, dtq, S, s.T, s.H, s.G, s.Q, s.nc);
   return hipGetLastError();
 }
 
 template <int N>
-hipError_t launch_n(const FwdShape& s, const void* x, const void* B, const float* Acs,
-                    const float* dtq, float* S, hipStream_t st) {
+hipError_t launch_n(const FwdShape& s, const void* x, const void* B, const void* dt, const float* A,
+                    float* Acs, float* dtq, float* S, hipStream_t st) {
   switch (s.P) {
-    case 32: return launch_np<N, 32>(s, x, B, Acs, dtq, S, st);
-    case 64: return launch_np<N, 64>(s, x, B, Acs, dtq, S, st);
-    case 128: return launch_np<N, 128>(s, x, B, Acs, dtq, S, st);
+    case 32: return launch_np<N, 32>(s, x, B, dt, A, Acs, dtq, S, st);
+    case 64: return launch_np<N, 64>(s, x, B, dt, A, Acs, dtq, S, st);
+    case 128: return launch_np<N, 128>(s, x, B, dt, A, Acs, dtq, S, st);
   }
   return hipErrorInvalidValue;
 }
@@ -161,12 +193,13 @@ hipError_t launch_n(const FwdShape& s, const void* x, const void* B, const float
 }  // namespace
 
 hipError_t launch_chunk_state_mfma(const FwdShape& s, const void* x, const void* B,
-                                   const float* Acs, const float* dtq, float* S, hipStream_t st) {
+                                   const void* dt, const float* A, float* Acs, float* dtq,
+                                   float* S, hipStream_t st) {
   switch (s.N) {
-    case 32: return launch_n<32>(s, x, B, Acs, dtq, S, st);
-    case 64: return launch_n<64>(s, x, B, Acs, dtq, S, st);
-    case 128: return launch_n<128>(s, x, B, Acs, dtq, S, st);
-    case 256: return launch_n<256>(s, x, B, Acs, dtq, S, st);
+    case 32: return launch_n<32>(s, x, B, dt, A, Acs, dtq, S, st);
+    case 64: return launch_n<64>(s, x, B, dt, A, Acs, dtq, S, st);
+    case 128: return launch_n<128>(s, x, B, dt, A, Acs, dtq, S, st);
+    case 256: return launch_n<256>(s, x, B, dt, A, Acs, dtq, S, st);
   }
   return hipErrorInvalidValue;
 }

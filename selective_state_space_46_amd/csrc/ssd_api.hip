@@ -161,11 +161,15 @@ ssd_status ssd_chunk_scan_fwd_timed(const void* x, const void* dt, const float* 
     return hipEventRecord(static_cast<hipEvent_t>(stage_events[i]), hs) == hipSuccess;
   };
   if (!mark(0)) return SSD_ERR_HIP;
-  if (launch_chunk_cumsum(s, dtype, dt, A, Acs, dtq, hs) != hipSuccess) return SSD_ERR_HIP;
+  // the matrix-core chunk_state computes the cumulative sums itself: stage 0
+  // is empty on that path
+  if (!mfma && launch_chunk_cumsum(s, dtype, dt, A, Acs, dtq, hs) != hipSuccess) return SSD_ERR_HIP;
   if (!mark(1)) return SSD_ERR_HIP;
   if (mfma && launch_chunk_scores(s, B, C, CB, hs) != hipSuccess) return SSD_ERR_HIP;
   if (!mark(2)) return SSD_ERR_HIP;
-  if (launch_chunk_state(s, dtype, mfma, x, B, Acs, dtq, S, hs) != hipSuccess) return SSD_ERR_HIP;
+  const hipError_t se = mfma ? launch_chunk_state_mfma(s, x, B, dt, A, Acs, dtq, S, hs)
+                             : launch_chunk_state(s, dtype, x, B, Acs, dtq, S, hs);
+  if (se != hipSuccess) return SSD_ERR_HIP;
   if (!mark(3)) return SSD_ERR_HIP;
   if (launch_state_passing(s, S, Hb, Acs, init_state, final_state, hs) != hipSuccess)
     return SSD_ERR_HIP;

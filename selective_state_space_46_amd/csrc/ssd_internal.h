@@ -110,12 +110,15 @@ __device__ __forceinline__ int xcd_swizzle(int bid, int nblocks) {
 hipError_t launch_chunk_cumsum(const FwdShape& s, ssd_dtype dt_type, const void* dt, const float* A,
                                float* Acs, float* dtq, hipStream_t st);
 
-// S: chunk states [b, nc, H, P, N] f32.
-hipError_t launch_chunk_state(const FwdShape& s, ssd_dtype type, bool mfma, const void* x,
-                              const void* B, const float* Acs, const float* dtq, float* S,
-                              hipStream_t st);
+// S: chunk states [b, nc, H, P, N] f32 (generic path: from Acs / dtq that
+// chunk_cumsum wrote).
+hipError_t launch_chunk_state(const FwdShape& s, ssd_dtype type, const void* x, const void* B,
+                              const float* Acs, const float* dtq, float* S, hipStream_t st);
+// Matrix-core path: S^T [b, nc, H, P, N] f32; also computes the in-chunk
+// cumulative sums itself and writes Acs / dtq for the kernels after it.
 hipError_t launch_chunk_state_mfma(const FwdShape& s, const void* x, const void* B,
-                                   const float* Acs, const float* dtq, float* S, hipStream_t st);
+                                   const void* dt, const float* A, float* Acs, float* dtq,
+                                   float* S, hipStream_t st);
 
 // Hb == nullptr: states entering each chunk overwrite S in place (fp32);
 // otherwise they are written to Hb as bf16 and S is left as it was.
