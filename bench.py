@@ -4,9 +4,9 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--no-cpu-baseline] [--no-extra]
 
-One step = one ssd_chunk_scan_fwd call (chunk_cumsum, chunk_scores,
-chunk_state, state_passing, chunk_scan) over one batch of the workload, inputs
-resident in HBM. The headline workload is the Mamba-2-130M-shaped layer (batch 8,
+One step = one ssd_chunk_scan_fwd call over one batch of the workload (on the
+bf16 matrix-core path: chunk_state with the cumulative sums and C B^T tiles in
+the same launch, state_passing, chunk_scan), inputs resident in HBM. The headline workload is the Mamba-2-130M-shaped layer (batch 8,
 T 2048, H 24, P 64, N 128, 1 group, chunk 256, bf16 inputs, fp32
 accumulation and state). Prints ONE JSON line on stdout; progress goes to
 stderr.
@@ -41,13 +41,14 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = {
     "chunk_cumsum": ["chunk_cumsum.hip"],
-    "chunk_state": ["chunk_state.hip", "chunk_state_mfma.hip"],
+    "chunk_state": ["chunk_state.hip", "chunk_state_mfma.hip", "mfma_util.h"],
     "state_passing": ["state_passing.hip"],
-    "chunk_scan": ["chunk_scan.hip", "chunk_scan_mfma.hip"],
-    "chunk_scores": ["chunk_scores.hip"],
+    "chunk_scan": ["chunk_scan.hip", "chunk_scan_mfma.hip", "mfma_util.h"],
     "state_update": ["state_update.hip"],
 }
-STAGES = ["chunk_cumsum", "chunk_scores", "chunk_state", "state_passing", "chunk_scan"]
+# the library's event windows, in launch order (chunk_cumsum is empty on the
+# matrix-core path, where chunk_state does its work)
+STAGES = ["chunk_cumsum", "chunk_state", "state_passing", "chunk_scan"]
 
 
 def log(*a):
@@ -110,17 +111,22 @@ def fwd_work(w: workloads.FwdWorkload, with_init: bool) -> dict:
     fst = 4 * b * H * N * P             # one [b,H,N,P] fp32 state
     tri = Q * (Q + 1) // 2
     # the bf16 matrix-core path (dstate, headdim multiples of 32, chunk >= 32)
-    # precomputes C B^T per chunk and group as bf16 32x32 tiles and hands the
-    # passed states to chunk_scan as bf16; the generic path does neither
+    # computes the cumulative sums and C B^T per chunk and group (bf16 32x32
+    # tiles) in the chunk_state launch and hands the passed states to
+    # chunk_scan as bf16; the generic path does neither
     mfma = w.dtype == "bf16" and N in (32, 64, 128, 256) and P in (32, 64, 128) and Q >= 32
     lpc = Q // 32
     cbt = b * nc * G * (lpc * (lpc + 1) // 2) * 1024 * 2 if mfma else 0
     hst = st // 2 if mfma else st       # passed states as chunk_scan reads them
+    cumsum = {"bytes": dtb + 2 * acs, "flops": b * T * H * 2}
+    state = {"bytes": x + bc + 2 * acs + st, "flops": 2 * b * T * H * N * P}
+    if mfma:   # one launch: reads dt instead of Acs / dtq, writes them; C B^T tiles from B, C
+        state = {"bytes": x + 2 * bc + dtb + 2 * acs + st + cbt,
+                 "flops": 2 * b * T * H * N * P + b * T * H * 2 + b * nc * G * 2 * N * tri}
+        cumsum = {"bytes": 0, "flops": 0}
     return {
-        "chunk_cumsum": {"bytes": dtb + 2 * acs, "flops": b * T * H * 2},
-        "chunk_scores": {"bytes": 2 * bc + cbt if mfma else 0,
-                         "flops": b * nc * G * 2 * N * tri if mfma else 0},
-        "chunk_state": {"bytes": x + bc + 2 * acs + st, "flops": 2 * b * T * H * N * P},
+        "chunk_cumsum": cumsum,
+        "chunk_state": state,
         "state_passing": {"bytes": st + hst + 4 * b * H * nc + fst * (2 if with_init else 1),
                           "flops": 2 * b * nc * H * N * P},
         "chunk_scan": {"bytes": 2 * x + (bc + cbt if mfma else 2 * bc) + 2 * acs + hst,
@@ -224,12 +230,12 @@ def bench_fwd(hip, w, steps, warmup, cold=False):
         ms_per_step = hip.ms(t_start, t_end) / steps
 
     # pass 2: per-kernel durations from events the library records between its launches
-    evs = [[hip.event() for _ in range(6)] for _ in range(steps)]
+    evs = [[hip.event() for _ in range(len(STAGES) + 1)] for _ in range(steps)]
     for k in range(steps):
         call(evs[k])
     torch.cuda.synchronize()
     stage_ms = {s: float(np.mean([hip.ms(ev[i], ev[i + 1]) for ev in evs])) for i, s in enumerate(STAGES)}
-    call_ms = float(np.mean([hip.ms(ev[0], ev[5]) for ev in evs]))
+    call_ms = float(np.mean([hip.ms(ev[0], ev[-1]) for ev in evs]))
     for e in [t_start, t_end] + [e for ev in evs for e in ev]:
         hip.destroy(e)
     return dict(ms_per_step=ms_per_step, call_ms=call_ms, stage_ms=stage_ms, wall_s=wall,
@@ -344,6 +350,8 @@ def main():
     work = fwd_work(w, w.init != "zero")
     kernels = {}
     for s in STAGES:
+        if work[s]["bytes"] == 0:
+            continue                  # empty window on this path
         ms = max(r["stage_ms"][s], 1e-6)
         kernels[s] = {"ms": round(ms, 5),
                       "GB_per_s": round(work[s]["bytes"] / (ms * 1e-3) / 1e9, 1),

@@ -128,15 +128,14 @@ SSD_API ssd_status ssd_chunk_scan_fwd(const void *x, const void *dt, const float
 
 /*
  * Measurement variant of ssd_chunk_scan_fwd: identical computation, and it
- * records stage_events[0..5] (hipEvent_t handles created by the caller, e.g.
- * with hipEventCreate) on `stream` around its five stages, in launch order:
- *   [0] chunk_cumsum [1] chunk_scores [2] chunk_state [3] state_passing
- *   [4] chunk_scan [5]
- * so that hipEventElapsedTime gives each kernel's duration on the stream it
- * runs on (chunk_scores, C B^T once per chunk and group, runs only on the
- * bf16 matrix-core path; its window is empty otherwise). stage_events may be
- * NULL (then it is ssd_chunk_scan_fwd). A failed event record returns
- * SSD_ERR_HIP.
+ * records stage_events[0..4] (hipEvent_t handles created by the caller, e.g.
+ * with hipEventCreate) on `stream` around its four stages, in launch order:
+ *   [0] cumulative sums [1] chunk states [2] state passing [3] chunk outputs [4]
+ * so that hipEventElapsedTime gives each stage's duration on the stream it
+ * runs on. On the bf16 matrix-core path one launch computes the cumulative
+ * sums, the C B^T tiles and the chunk states, so window [0, 1] is empty
+ * there. stage_events may be NULL (then it is ssd_chunk_scan_fwd). A failed
+ * event record returns SSD_ERR_HIP.
  */
 SSD_API ssd_status ssd_chunk_scan_fwd_timed(const void *x, const void *dt, const float *A,
                                             const void *B, const void *C, const float *D,

@@ -26,7 +26,7 @@
 //
 // Work-group: one batch row, one 256-token super-chunk (256/Q chunks), one
 // head; 4 waves. The C B^T tiles come precomputed once per group
-// (chunk_scores.hip) in MFMA-fragment order. The super-chunk is cut into eight
+// (by the chunk_state launch, chunk_state_mfma.hip) in MFMA-fragment order. The super-chunk is cut into eight
 // 32-row blocks l; wave w owns blocks w and 7-w so that the causal triangle
 // splits evenly. The output is produced transposed (y^T: rows p, lane = token
 // l), which makes every per-token factor one multiplier per lane:

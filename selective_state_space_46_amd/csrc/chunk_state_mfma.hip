@@ -35,11 +35,80 @@ constexpr int kWaves = kThreads / 64;
 constexpr int kSK = 64;          // tokens per contraction slice
 constexpr int kMaxQ = 256;
 
+// C B^T inside each chunk, once per B/C group (the same launch, work-groups
+// placed before the chunk-state ones):
+//   CB[l][s] = C_l . B_s      for l, s in the same chunk, s <= l (32 x 32 tiles)
+// These are the dot products of the semiseparable matrix M_ij = C_i^T
+// abar_{i:j} B_j before its decay (youngju.dev "Mamba / selective SSM",
+// section "State Space Dualityの発見"); they depend only on B and C, which the
+// heads of one group share (Qiita "Mamba-2" article, section 4.1: heads like
+// multi-head attention, B/C per group). chunk_scan applies the per-head decay
+// and causal mask to them.
+//
+// One wave per tile (batch, chunk, group, 32-row block l, 32-column block
+// s <= l): the C_l and B_s rows load straight from memory (k = dstate; rows are
+// dstate-contiguous) as one batch, N/16 MFMAs follow, and the tile is written
+// as bf16 in MFMA result order: lane L holds rows 8(r/4) + 4(L/32) + r%4 of
+// column L%32, exactly the B-operand fragments chunk_scan feeds to its next
+// MFMA, loaded there with two coalesced 16-byte reads per lane.
+// Layout: CB [b, nc, G, ntile, 64, 16] bf16 with ntile = lpc(lpc+1)/2,
+// lpc = Q/32, tile (s, l) of a chunk at index l(l+1)/2 + s.
+template <int N>
+__device__ __forceinline__ void chunk_scores_tile(const uint16_t* __restrict__ Bm,
+                                                  const uint16_t* __restrict__ Cm,
+                                                  uint16_t* __restrict__ CB, int T, int G, int Q, int nc,
+                                                  long wid, int lane) {
+  const int lpc = Q / 32;
+  const int ntile = lpc * (lpc + 1) / 2;
+  const int l32 = lane & 31, g2 = lane >> 5;
+  long rest = wid;
+  const int ti = int(rest % ntile); rest /= ntile;
+  const int g = int(rest % G); rest /= G;
+  const int c = int(rest % nc);
+  const int b = int(rest / nc);
+  int i = 0;                                    // tile ti = i (i + 1) / 2 + j, j <= i
+  while ((i + 1) * (i + 2) / 2 <= ti) ++i;
+  const int j = ti - i * (i + 1) / 2;
+  const int tc0 = c * Q;                        // first token of the chunk
+  if (tc0 + 32 * i >= T) return;                // row block past the end: never read
+
+  const int tl = tc0 + 32 * i + l32, ts = tc0 + 32 * j + l32;
+  const uint16_t* cr = Cm + ((size_t(b) * T + min(tl, T - 1)) * G + g) * N + 8 * g2;
+  const uint16_t* br = Bm + ((size_t(b) * T + min(ts, T - 1)) * G + g) * N + 8 * g2;
+  u32x4 cf[N / 16], bf[N / 16];
+#pragma unroll
+  for (int ks = 0; ks < N / 16; ++ks) {
+    cf[ks] = load16(cr + 16 * ks);
+    bf[ks] = load16(br + 16 * ks);
+  }
+  f32x16 acc = zero16();
+#pragma unroll
+  for (int ks = 0; ks < N / 16; ++ks)
+    acc = mfma32x32x16(keep_or_zero(ts < T, bf[ks]), keep_or_zero(tl < T, cf[ks]), acc);  // rows s, column l
+  u32x4 lo, hi;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    lo[m] = pack_bf16x2(acc[2 * m], acc[2 * m + 1]);
+    hi[m] = pack_bf16x2(acc[8 + 2 * m], acc[8 + 2 * m + 1]);
+  }
+  u32x4* dst = reinterpret_cast<u32x4*>(CB + (((size_t(b) * nc + c) * G + g) * ntile + ti) * 1024 +
+                                        size_t(lane) * 16);
+  dst[0] = lo;
+  dst[1] = hi;
+}
+
 template <int N, int P>
 __global__ __launch_bounds__(kThreads) void chunk_state_mfma_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ Bm, const uint16_t* __restrict__ dt,
     const float* __restrict__ A, float* __restrict__ Acs, float* __restrict__ dtq, float* __restrict__ S,
-    int T, int H, int G, int Q, int nc) {
+    const uint16_t* __restrict__ Cm, uint16_t* __restrict__ CB, int T, int H, int G, int Q, int nc,
+    int nscore_wg, long ntiles) {
+  // the first nscore_wg work-groups compute C B^T tiles, one per wave
+  if (int(blockIdx.x) < nscore_wg) {
+    const long wid = long(blockIdx.x) * kWaves + (threadIdx.x >> 6);
+    if (wid < ntiles) chunk_scores_tile<N>(Bm, Cm, CB, T, G, Q, nc, wid, threadIdx.x & 63);
+    return;                                     // no barrier on this path
+  }
   constexpr int RBB = N / 8, RBW = P / 8;            // 16-byte chunks per row
   constexpr int CB_ = kSK * RBB, CW = kSK * RBW;     // chunks per slice
   constexpr int PER = (CB_ + CW + kThreads - 1) / kThreads;  // chunks per thread
@@ -51,7 +120,7 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma_kernel(
   constexpr int NT = N / 32, PT = P / 32;
   constexpr int TILES = PT * NT;
   constexpr int TPW = (TILES + kWaves - 1) / kWaves;
-  const int id = xcd_swizzle(blockIdx.x, gridDim.x);
+  const int id = xcd_swizzle(int(blockIdx.x) - nscore_wg, int(gridDim.x) - nscore_wg);
   const int h = id % H;
   const int bc = id / H;
   const int c = bc % nc, b = bc / nc;
@@ -170,36 +239,42 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma_kernel(
 }
 
 template <int N, int P>
-hipError_t launch_np(const FwdShape& s, const void* x, const void* B, const void* dt, const float* A,
-                     float* Acs, float* dtq, float* S, hipStream_t st) {
-  const long blocks = long(s.b) * s.nc * s.H;
+hipError_t launch_np(const FwdShape& s, const void* x, const void* B, const void* C, const void* dt,
+                     const float* A, float* Acs, float* dtq, float* S, uint16_t* CB, hipStream_t st) {
+  const int lpc = s.Q / 32;
+  const long ntiles = long(s.b) * s.nc * s.G * (lpc * (lpc + 1) / 2);
+  // score work-groups first (they start with the first wave of work-groups),
+  // padded to a multiple of 8 so the chunk-state work-groups keep their XCD
+  const long nscore = ((ntiles + kWaves - 1) / kWaves + 7) / 8 * 8;
+  const long blocks = nscore + long(s.b) * s.nc * s.H;
   hipLaunchKernelGGL((chunk_state_mfma_kernel<N, P>), dim3(unsigned(blocks)), dim3(kThreads), 0, st,
                      static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(B),
-                     static_cast<const uint16_t*>(dt), A, Acs, dtq, S, s.T, s.H, s.G, s.Q, s.nc);
+                     static_cast<const uint16_t*>(dt), A, Acs, dtq, S, static_cast<const uint16_t*>(C), CB,
+                     s.T, s.H, s.G, s.Q, s.nc, int(nscore), ntiles);
   return hipGetLastError();
 }
 
 template <int N>
-hipError_t launch_n(const FwdShape& s, const void* x, const void* B, const void* dt, const float* A,
-                    float* Acs, float* dtq, float* S, hipStream_t st) {
+hipError_t launch_n(const FwdShape& s, const void* x, const void* B, const void* C, const void* dt,
+                    const float* A, float* Acs, float* dtq, float* S, uint16_t* CB, hipStream_t st) {
   switch (s.P) {
-    case 32: return launch_np<N, 32>(s, x, B, dt, A, Acs, dtq, S, st);
-    case 64: return launch_np<N, 64>(s, x, B, dt, A, Acs, dtq, S, st);
-    case 128: return launch_np<N, 128>(s, x, B, dt, A, Acs, dtq, S, st);
+    case 32: return launch_np<N, 32>(s, x, B, C, dt, A, Acs, dtq, S, CB, st);
+    case 64: return launch_np<N, 64>(s, x, B, C, dt, A, Acs, dtq, S, CB, st);
+    case 128: return launch_np<N, 128>(s, x, B, C, dt, A, Acs, dtq, S, CB, st);
   }
   return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-hipError_t launch_chunk_state_mfma(const FwdShape& s, const void* x, const void* B,
+hipError_t launch_chunk_state_mfma(const FwdShape& s, const void* x, const void* B, const void* C,
                                    const void* dt, const float* A, float* Acs, float* dtq,
-                                   float* S, hipStream_t st) {
+                                   float* S, uint16_t* CB, hipStream_t st) {
   switch (s.N) {
-    case 32: return launch_n<32>(s, x, B, dt, A, Acs, dtq, S, st);
-    case 64: return launch_n<64>(s, x, B, dt, A, Acs, dtq, S, st);
-    case 128: return launch_n<128>(s, x, B, dt, A, Acs, dtq, S, st);
-    case 256: return launch_n<256>(s, x, B, dt, A, Acs, dtq, S, st);
+    case 32: return launch_n<32>(s, x, B, C, dt, A, Acs, dtq, S, CB, st);
+    case 64: return launch_n<64>(s, x, B, C, dt, A, Acs, dtq, S, CB, st);
+    case 128: return launch_n<128>(s, x, B, C, dt, A, Acs, dtq, S, CB, st);
+    case 256: return launch_n<256>(s, x, B, C, dt, A, Acs, dtq, S, CB, st);
   }
   return hipErrorInvalidValue;
 }

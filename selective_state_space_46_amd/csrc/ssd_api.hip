@@ -53,8 +53,8 @@ FwdShape make_shape(int batch, int seqlen, int H, int P, int N, int G, int Q) {
 // The largest one-dimensional launch of the forward pass must stay below 2^32
 // work-items (the grid limit). Work-items per launch, from the launchers:
 //   chunk_cumsum      64 per (b, c, h) row
-//   chunk_scores      64 per 32 x 32 tile, lpc (lpc + 1) / 2 tiles per (b, c, g)
-//   chunk_state_mfma  512 per (b, c, h)
+//   chunk_state_mfma  512 per (b, c, h), plus 64 per C B^T tile (lpc (lpc + 1) / 2
+//                     tiles per (b, c, g)) rounded up to 512-thread work-groups
 //   state_passing     256 per 16 x 64 tile of each (b, h) state, or one per
 //                     state element when dstate % 4 != 0
 //   chunk_scan_mfma   256 per (b, 256-token super-chunk, h)
@@ -68,8 +68,8 @@ bool grids_fit(const FwdShape& s, bool mfma) {
   worst = std::max(worst, s.N % 4 == 0 ? 256.0 * bh * ((s.P + 15) / 16) * ((s.N + 63) / 64)
                                        : bh * s.P * s.N);
   if (mfma) {
-    worst = std::max(worst, 64.0 * double(s.b) * s.nc * s.G * (lpc * (lpc + 1) / 2));
-    worst = std::max(worst, 512.0 * bch);
+    worst = std::max(worst, 64.0 * double(s.b) * s.nc * s.G * (lpc * (lpc + 1) / 2) + 4096.0 +
+                                512.0 * bch);
     worst = std::max(worst, 256.0 * bh * ((s.T + 255) / 256));
   }
   return worst < lim;
@@ -160,23 +160,22 @@ ssd_status ssd_chunk_scan_fwd_timed(const void* x, const void* dt, const float* 
     if (!stage_events || !stage_events[i]) return true;
     return hipEventRecord(static_cast<hipEvent_t>(stage_events[i]), hs) == hipSuccess;
   };
+  // stage 0: cumulative sums, stage 1: chunk states. The matrix-core
+  // chunk_state launch also computes the cumulative sums and the C B^T tiles,
+  // so stage 0 is empty on that path.
   if (!mark(0)) return SSD_ERR_HIP;
-  // the matrix-core chunk_state computes the cumulative sums itself: stage 0
-  // is empty on that path
   if (!mfma && launch_chunk_cumsum(s, dtype, dt, A, Acs, dtq, hs) != hipSuccess) return SSD_ERR_HIP;
   if (!mark(1)) return SSD_ERR_HIP;
-  if (mfma && launch_chunk_scores(s, B, C, CB, hs) != hipSuccess) return SSD_ERR_HIP;
-  if (!mark(2)) return SSD_ERR_HIP;
-  const hipError_t se = mfma ? launch_chunk_state_mfma(s, x, B, dt, A, Acs, dtq, S, hs)
+  const hipError_t se = mfma ? launch_chunk_state_mfma(s, x, B, C, dt, A, Acs, dtq, S, CB, hs)
                              : launch_chunk_state(s, dtype, x, B, Acs, dtq, S, hs);
   if (se != hipSuccess) return SSD_ERR_HIP;
-  if (!mark(3)) return SSD_ERR_HIP;
+  if (!mark(2)) return SSD_ERR_HIP;
   if (launch_state_passing(s, S, Hb, Acs, init_state, final_state, hs) != hipSuccess)
     return SSD_ERR_HIP;
-  if (!mark(4)) return SSD_ERR_HIP;
+  if (!mark(3)) return SSD_ERR_HIP;
   if (launch_chunk_scan(s, dtype, mfma, x, B, C, Acs, dtq, S, Hb, CB, D, y, hs) != hipSuccess)
     return SSD_ERR_HIP;
-  if (!mark(5)) return SSD_ERR_HIP;
+  if (!mark(4)) return SSD_ERR_HIP;
   return SSD_OK;
 }
 

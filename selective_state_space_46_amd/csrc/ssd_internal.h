@@ -114,20 +114,17 @@ hipError_t launch_chunk_cumsum(const FwdShape& s, ssd_dtype dt_type, const void*
 // chunk_cumsum wrote).
 hipError_t launch_chunk_state(const FwdShape& s, ssd_dtype type, const void* x, const void* B,
                               const float* Acs, const float* dtq, float* S, hipStream_t st);
-// Matrix-core path: S^T [b, nc, H, P, N] f32; also computes the in-chunk
-// cumulative sums itself and writes Acs / dtq for the kernels after it.
-hipError_t launch_chunk_state_mfma(const FwdShape& s, const void* x, const void* B,
+// Matrix-core path: S^T [b, nc, H, P, N] f32; the same launch also computes
+// the in-chunk cumulative sums (written to Acs / dtq) and the C B^T tiles
+// (CB [b, nc, G, ntile, 64, 16] bf16) for the kernels after it.
+hipError_t launch_chunk_state_mfma(const FwdShape& s, const void* x, const void* B, const void* C,
                                    const void* dt, const float* A, float* Acs, float* dtq,
-                                   float* S, hipStream_t st);
+                                   float* S, uint16_t* CB, hipStream_t st);
 
 // Hb == nullptr: states entering each chunk overwrite S in place (fp32);
 // otherwise they are written to Hb as bf16 and S is left as it was.
 hipError_t launch_state_passing(const FwdShape& s, float* S, uint16_t* Hb, const float* Acs,
                                 const float* init, float* final_state, hipStream_t st);
-
-// C B^T tiles per chunk and group (MFMA path).
-hipError_t launch_chunk_scores(const FwdShape& s, const void* B, const void* C, uint16_t* CB,
-                               hipStream_t st);
 
 // Generic path reads Hst (fp32, [b, nc, H, P, N]); MFMA path reads Hb (bf16)
 // and the C B^T tiles CB.

@@ -72,12 +72,13 @@ def test_workspace_query():
     assert ws(1, 0, 2, 16, 16, 1, 64) == 0            # T = 0
     assert ws(1, 256, 2, 257, 16, 1, 64) == 0         # headdim too large
     assert ws(1, 256, 2, 16, 16, 1, 64, dt=5) == 0    # dtype
-    # 2^23 chunk-heads: the bf16 matrix-core chunk_state grid (512 work-items
-    # each) would reach 2^32 work-items; the fp32 path's grids stay below it
+    # 2^23 chunk-heads: the bf16 matrix-core chunk_state launch (512 work-items
+    # per chunk-head plus 64 per C B^T tile) would reach 2^32 work-items; the
+    # fp32 path's grids stay below it. 61 chunks instead of 64 fit.
     big = (1024, 16384, 128, 64, 128, 1, 256)
     assert ws(*big, dt=ssd.SSD_BF16) == 0
     assert ws(*big, dt=ssd.SSD_F32) == expect(1024, 16384, 128, 64, 128, 256, ssd.SSD_F32)
-    assert ws(1024, 16384 - 256, 128, 64, 128, 1, 256, dt=ssd.SSD_BF16) > 0
+    assert ws(1024, 61 * 256, 128, 64, 128, 1, 256, dt=ssd.SSD_BF16) > 0
 
 
 def fwd(L, **kw):
