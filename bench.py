@@ -11,8 +11,9 @@ T 2048, H 24, P 64, N 128, 1 group, chunk 256, bf16 inputs, fp32
 accumulation and state). Prints ONE JSON line on stdout; progress goes to
 stderr.
 
-Kernel durations are measured live with hipEvents that the library records on
-its own stream between its launches (ssd_chunk_scan_fwd_timed). The
+Kernel durations are measured live with hipEvents that each kernel's own
+dispatch records at its start and end (ssd_chunk_scan_fwd_timed, through
+hipExtLaunchKernel). The
 decode update (ssd_state_update) is measured on the batch-256 decode workload
 in the same run, and the fp64 CPU oracle is timed on the host's cores.
 """
@@ -229,12 +230,13 @@ def bench_fwd(hip, w, steps, warmup, cold=False):
         wall = time.perf_counter() - wall0
         ms_per_step = hip.ms(t_start, t_end) / steps
 
-    # pass 2: per-kernel durations from events the library records between its launches
-    evs = [[hip.event() for _ in range(len(STAGES) + 1)] for _ in range(steps)]
+    # pass 2: per-kernel durations from start / end events recorded by each kernel's dispatch
+    evs = [[hip.event() for _ in range(2 * len(STAGES))] for _ in range(steps)]
     for k in range(steps):
         call(evs[k])
     torch.cuda.synchronize()
-    stage_ms = {s: float(np.mean([hip.ms(ev[i], ev[i + 1]) for ev in evs])) for i, s in enumerate(STAGES)}
+    stage_ms = {s: float(np.mean([hip.ms(ev[2 * i], ev[2 * i + 1]) for ev in evs]))
+                for i, s in enumerate(STAGES)}
     call_ms = float(np.mean([hip.ms(ev[0], ev[-1]) for ev in evs]))
     for e in [t_start, t_end] + [e for ev in evs for e in ev]:
         hip.destroy(e)

@@ -128,14 +128,17 @@ SSD_API ssd_status ssd_chunk_scan_fwd(const void *x, const void *dt, const float
 
 /*
  * Measurement variant of ssd_chunk_scan_fwd: identical computation, and it
- * records stage_events[0..4] (hipEvent_t handles created by the caller, e.g.
- * with hipEventCreate) on `stream` around its four stages, in launch order:
- *   [0] cumulative sums [1] chunk states [2] state passing [3] chunk outputs [4]
- * so that hipEventElapsedTime gives each stage's duration on the stream it
- * runs on. On the bf16 matrix-core path one launch computes the cumulative
- * sums, the C B^T tiles and the chunk states, so window [0, 1] is empty
- * there. stage_events may be NULL (then it is ssd_chunk_scan_fwd). A failed
- * event record returns SSD_ERR_HIP.
+ * times its four stages, in launch order: [0] cumulative sums, [1] chunk
+ * states, [2] state passing, [3] chunk outputs. stage_events holds 8
+ * hipEvent_t handles created by the caller (e.g. with hipEventCreate):
+ * stage_events[2 i] and stage_events[2 i + 1] are recorded at the start and
+ * the end of stage i's kernel by that kernel's own dispatch
+ * (hipExtLaunchKernel), so hipEventElapsedTime on the pair gives the kernel's
+ * execution time on `stream`. On the bf16 matrix-core path one launch
+ * computes the cumulative sums, the C B^T tiles and the chunk states; stage 0
+ * launches nothing there and its two events are recorded back to back.
+ * stage_events may be NULL (then it is ssd_chunk_scan_fwd). A failed event
+ * record returns SSD_ERR_HIP.
  */
 SSD_API ssd_status ssd_chunk_scan_fwd_timed(const void *x, const void *dt, const float *A,
                                             const void *B, const void *C, const float *D,

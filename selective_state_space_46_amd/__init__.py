@@ -134,10 +134,11 @@ def ssd_chunk_scan_fwd(x, dt, A, B, C, D=None, init_state=None, chunk_len: int =
 def ssd_chunk_scan_fwd_timed(x, dt, A, B, C, D=None, init_state=None, chunk_len: int = 256, *,
                              y=None, final_state=None, return_final_state: bool = True,
                              workspace=None, stream=None, stage_events=None):
-    """ssd_chunk_scan_fwd that also records 5 caller-created hipEvent_t handles
-    (ints) around its four stages (cumulative sums, chunk states, state
-    passing, chunk outputs; on the bf16 matrix-core path the first is empty,
-    its work done by the chunk-state launch); stage_events=None skips them."""
+    """ssd_chunk_scan_fwd that also records 8 caller-created hipEvent_t handles
+    (ints), a start / end pair per stage (cumulative sums, chunk states, state
+    passing, chunk outputs), recorded by each kernel's own dispatch; on the
+    bf16 matrix-core path the first pair is recorded back to back (the
+    chunk-state launch does that work). stage_events=None skips them."""
     import torch
     dev = x.device
     x = _dev(x, dev, "x")
@@ -170,9 +171,9 @@ def ssd_chunk_scan_fwd_timed(x, dt, A, B, C, D=None, init_state=None, chunk_len:
     if stage_events is None:
         r = lib().ssd_chunk_scan_fwd(*args)
     else:
-        if len(stage_events) != 5:
-            raise ValueError("stage_events needs 5 hipEvent_t handles")
-        ev = (ctypes.c_void_p * 5)(*[int(e) if e else None for e in stage_events])
+        if len(stage_events) != 8:
+            raise ValueError("stage_events needs 8 hipEvent_t handles")
+        ev = (ctypes.c_void_p * 8)(*[int(e) if e else None for e in stage_events])
         r = lib().ssd_chunk_scan_fwd_timed(*args, ev)
     if r != 0:
         raise SSDError(r, "ssd_chunk_scan_fwd")

@@ -78,14 +78,14 @@ __global__ __launch_bounds__(kThreads) void chunk_cumsum_kernel(const In* __rest
 }  // namespace
 
 hipError_t launch_chunk_cumsum(const FwdShape& s, ssd_dtype type, const void* dt, const float* A,
-                               float* Acs, float* dtq, hipStream_t st) {
+                               float* Acs, float* dtq, hipStream_t st, const StageEv& ev) {
   const long nrows = long(s.b) * s.nc * s.H;
   const long blocks = (nrows + kThreads / 64 - 1) / (kThreads / 64);
   if (type == SSD_BF16)
-    hipLaunchKernelGGL(chunk_cumsum_kernel<uint16_t>, dim3(unsigned(blocks)), dim3(kThreads), 0, st,
+    hipExtLaunchKernelGGL(chunk_cumsum_kernel<uint16_t>, dim3(unsigned(blocks)), dim3(kThreads), 0, st, ev.start, ev.stop, 0,
                        static_cast<const uint16_t*>(dt), A, Acs, dtq, s.T, s.H, s.Q, s.nc, nrows);
   else
-    hipLaunchKernelGGL(chunk_cumsum_kernel<float>, dim3(unsigned(blocks)), dim3(kThreads), 0, st,
+    hipExtLaunchKernelGGL(chunk_cumsum_kernel<float>, dim3(unsigned(blocks)), dim3(kThreads), 0, st, ev.start, ev.stop, 0,
                        static_cast<const float*>(dt), A, Acs, dtq, s.T, s.H, s.Q, s.nc, nrows);
   return hipGetLastError();
 }

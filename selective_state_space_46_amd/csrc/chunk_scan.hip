@@ -83,16 +83,16 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_generic(
 hipError_t launch_chunk_scan(const FwdShape& s, ssd_dtype type, bool mfma, const void* x,
                              const void* B, const void* C, const float* Acs, const float* dtq,
                              const float* Hst, const uint16_t* Hb, const uint16_t* CB,
-                             const float* D, void* y, hipStream_t st) {
-  if (mfma) return launch_chunk_scan_mfma(s, x, CB, C, Acs, dtq, Hb, D, y, st);
+                             const float* D, void* y, hipStream_t st, const StageEv& ev) {
+  if (mfma) return launch_chunk_scan_mfma(s, x, CB, C, Acs, dtq, Hb, D, y, st, ev);
   dim3 grid(s.H * (s.Q / kRows), s.nc, s.b);
   if (type == SSD_BF16)
-    hipLaunchKernelGGL(chunk_scan_generic<uint16_t>, grid, dim3(kThreads), 0, st,
+    hipExtLaunchKernelGGL(chunk_scan_generic<uint16_t>, grid, dim3(kThreads), 0, st, ev.start, ev.stop, 0,
                        static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(B),
                        static_cast<const uint16_t*>(C), Acs, dtq, Hst, D,
                        static_cast<uint16_t*>(y), s.T, s.H, s.P, s.N, s.G, s.Q, s.nc);
   else
-    hipLaunchKernelGGL(chunk_scan_generic<float>, grid, dim3(kThreads), 0, st,
+    hipExtLaunchKernelGGL(chunk_scan_generic<float>, grid, dim3(kThreads), 0, st, ev.start, ev.stop, 0,
                        static_cast<const float*>(x), static_cast<const float*>(B),
                        static_cast<const float*>(C), Acs, dtq, Hst, D, static_cast<float*>(y), s.T,
                        s.H, s.P, s.N, s.G, s.Q, s.nc);

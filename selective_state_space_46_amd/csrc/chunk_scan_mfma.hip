@@ -290,16 +290,16 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_mfma_kernel(
 template <int N, int P>
 hipError_t launch_np(const FwdShape& s, const void* x, const uint16_t* CB, const void* C,
                      const float* Acs, const float* dtq, const uint16_t* Hb, const float* D, void* y,
-                     hipStream_t st) {
+                     hipStream_t st, const StageEv& ev) {
   const int nsc = (s.T + kSC - 1) / kSC;
   const long blocks = long(s.b) * nsc * s.H;
   if (s.Q == kSC)  // one chunk per super-chunk: its H_c^T is staged in LDS
-    hipLaunchKernelGGL((chunk_scan_mfma_kernel<N, P, true>), dim3(unsigned(blocks)), dim3(kThreads), 0,
-                       st, static_cast<const uint16_t*>(x), CB, static_cast<const uint16_t*>(C), Acs,
+    hipExtLaunchKernelGGL((chunk_scan_mfma_kernel<N, P, true>), dim3(unsigned(blocks)), dim3(kThreads), 0,
+                       st, ev.start, ev.stop, 0, static_cast<const uint16_t*>(x), CB, static_cast<const uint16_t*>(C), Acs,
                        dtq, Hb, D, static_cast<uint16_t*>(y), s.T, s.H, s.G, s.Q, s.nc, nsc);
   else
-    hipLaunchKernelGGL((chunk_scan_mfma_kernel<N, P, false>), dim3(unsigned(blocks)), dim3(kThreads),
-                       0, st, static_cast<const uint16_t*>(x), CB, static_cast<const uint16_t*>(C), Acs,
+    hipExtLaunchKernelGGL((chunk_scan_mfma_kernel<N, P, false>), dim3(unsigned(blocks)), dim3(kThreads),
+                          0, st, ev.start, ev.stop, 0, static_cast<const uint16_t*>(x), CB, static_cast<const uint16_t*>(C), Acs,
                        dtq, Hb, D, static_cast<uint16_t*>(y), s.T, s.H, s.G, s.Q, s.nc, nsc);
   return hipGetLastError();
 }
@@ -307,11 +307,11 @@ hipError_t launch_np(const FwdShape& s, const void* x, const uint16_t* CB, const
 template <int N>
 hipError_t launch_n(const FwdShape& s, const void* x, const uint16_t* CB, const void* C,
                     const float* Acs, const float* dtq, const uint16_t* Hb, const float* D, void* y,
-                    hipStream_t st) {
+                    hipStream_t st, const StageEv& ev) {
   switch (s.P) {
-    case 32: return launch_np<N, 32>(s, x, CB, C, Acs, dtq, Hb, D, y, st);
-    case 64: return launch_np<N, 64>(s, x, CB, C, Acs, dtq, Hb, D, y, st);
-    case 128: return launch_np<N, 128>(s, x, CB, C, Acs, dtq, Hb, D, y, st);
+    case 32: return launch_np<N, 32>(s, x, CB, C, Acs, dtq, Hb, D, y, st, ev);
+    case 64: return launch_np<N, 64>(s, x, CB, C, Acs, dtq, Hb, D, y, st, ev);
+    case 128: return launch_np<N, 128>(s, x, CB, C, Acs, dtq, Hb, D, y, st, ev);
   }
   return hipErrorInvalidValue;
 }
@@ -320,12 +320,12 @@ hipError_t launch_n(const FwdShape& s, const void* x, const uint16_t* CB, const 
 
 hipError_t launch_chunk_scan_mfma(const FwdShape& s, const void* x, const uint16_t* CB,
                                   const void* C, const float* Acs, const float* dtq,
-                                  const uint16_t* Hb, const float* D, void* y, hipStream_t st) {
+                                  const uint16_t* Hb, const float* D, void* y, hipStream_t st, const StageEv& ev) {
   switch (s.N) {
-    case 32: return launch_n<32>(s, x, CB, C, Acs, dtq, Hb, D, y, st);
-    case 64: return launch_n<64>(s, x, CB, C, Acs, dtq, Hb, D, y, st);
-    case 128: return launch_n<128>(s, x, CB, C, Acs, dtq, Hb, D, y, st);
-    case 256: return launch_n<256>(s, x, CB, C, Acs, dtq, Hb, D, y, st);
+    case 32: return launch_n<32>(s, x, CB, C, Acs, dtq, Hb, D, y, st, ev);
+    case 64: return launch_n<64>(s, x, CB, C, Acs, dtq, Hb, D, y, st, ev);
+    case 128: return launch_n<128>(s, x, CB, C, Acs, dtq, Hb, D, y, st, ev);
+    case 256: return launch_n<256>(s, x, CB, C, Acs, dtq, Hb, D, y, st, ev);
   }
   return hipErrorInvalidValue;
 }

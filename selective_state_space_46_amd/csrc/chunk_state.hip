@@ -89,15 +89,15 @@ __global__ __launch_bounds__(kThreads) void chunk_state_generic(
 }  // namespace
 
 hipError_t launch_chunk_state(const FwdShape& s, ssd_dtype type, const void* x, const void* B,
-                              const float* Acs, const float* dtq, float* S, hipStream_t st) {
+                              const float* Acs, const float* dtq, float* S, hipStream_t st, const StageEv& ev) {
   const int ntn = (s.N + kRows - 1) / kRows;
   dim3 grid(s.H * ntn, s.nc, s.b);
   if (type == SSD_BF16)
-    hipLaunchKernelGGL(chunk_state_generic<uint16_t>, grid, dim3(kThreads), 0, st,
+    hipExtLaunchKernelGGL(chunk_state_generic<uint16_t>, grid, dim3(kThreads), 0, st, ev.start, ev.stop, 0,
                        static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(B), Acs, dtq, S,
                        s.T, s.H, s.P, s.N, s.G, s.Q, s.nc);
   else
-    hipLaunchKernelGGL(chunk_state_generic<float>, grid, dim3(kThreads), 0, st,
+    hipExtLaunchKernelGGL(chunk_state_generic<float>, grid, dim3(kThreads), 0, st, ev.start, ev.stop, 0,
                        static_cast<const float*>(x), static_cast<const float*>(B), Acs, dtq, S, s.T,
                        s.H, s.P, s.N, s.G, s.Q, s.nc);
   return hipGetLastError();

@@ -240,14 +240,14 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma_kernel(
 
 template <int N, int P>
 hipError_t launch_np(const FwdShape& s, const void* x, const void* B, const void* C, const void* dt,
-                     const float* A, float* Acs, float* dtq, float* S, uint16_t* CB, hipStream_t st) {
+                     const float* A, float* Acs, float* dtq, float* S, uint16_t* CB, hipStream_t st, const StageEv& ev) {
   const int lpc = s.Q / 32;
   const long ntiles = long(s.b) * s.nc * s.G * (lpc * (lpc + 1) / 2);
   // score work-groups first (they start with the first wave of work-groups),
   // padded to a multiple of 8 so the chunk-state work-groups keep their XCD
   const long nscore = ((ntiles + kWaves - 1) / kWaves + 7) / 8 * 8;
   const long blocks = nscore + long(s.b) * s.nc * s.H;
-  hipLaunchKernelGGL((chunk_state_mfma_kernel<N, P>), dim3(unsigned(blocks)), dim3(kThreads), 0, st,
+  hipExtLaunchKernelGGL((chunk_state_mfma_kernel<N, P>), dim3(unsigned(blocks)), dim3(kThreads), 0, st, ev.start, ev.stop, 0,
                      static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(B),
                      static_cast<const uint16_t*>(dt), A, Acs, dtq, S, static_cast<const uint16_t*>(C), CB,
                      s.T, s.H, s.G, s.Q, s.nc, int(nscore), ntiles);
@@ -256,11 +256,11 @@ hipError_t launch_np(const FwdShape& s, const void* x, const void* B, const void
 
 template <int N>
 hipError_t launch_n(const FwdShape& s, const void* x, const void* B, const void* C, const void* dt,
-                    const float* A, float* Acs, float* dtq, float* S, uint16_t* CB, hipStream_t st) {
+                    const float* A, float* Acs, float* dtq, float* S, uint16_t* CB, hipStream_t st, const StageEv& ev) {
   switch (s.P) {
-    case 32: return launch_np<N, 32>(s, x, B, C, dt, A, Acs, dtq, S, CB, st);
-    case 64: return launch_np<N, 64>(s, x, B, C, dt, A, Acs, dtq, S, CB, st);
-    case 128: return launch_np<N, 128>(s, x, B, C, dt, A, Acs, dtq, S, CB, st);
+    case 32: return launch_np<N, 32>(s, x, B, C, dt, A, Acs, dtq, S, CB, st, ev);
+    case 64: return launch_np<N, 64>(s, x, B, C, dt, A, Acs, dtq, S, CB, st, ev);
+    case 128: return launch_np<N, 128>(s, x, B, C, dt, A, Acs, dtq, S, CB, st, ev);
   }
   return hipErrorInvalidValue;
 }
@@ -269,12 +269,12 @@ hipError_t launch_n(const FwdShape& s, const void* x, const void* B, const void*
 
 hipError_t launch_chunk_state_mfma(const FwdShape& s, const void* x, const void* B, const void* C,
                                    const void* dt, const float* A, float* Acs, float* dtq,
-                                   float* S, uint16_t* CB, hipStream_t st) {
+                                   float* S, uint16_t* CB, hipStream_t st, const StageEv& ev) {
   switch (s.N) {
-    case 32: return launch_n<32>(s, x, B, C, dt, A, Acs, dtq, S, CB, st);
-    case 64: return launch_n<64>(s, x, B, C, dt, A, Acs, dtq, S, CB, st);
-    case 128: return launch_n<128>(s, x, B, C, dt, A, Acs, dtq, S, CB, st);
-    case 256: return launch_n<256>(s, x, B, C, dt, A, Acs, dtq, S, CB, st);
+    case 32: return launch_n<32>(s, x, B, C, dt, A, Acs, dtq, S, CB, st, ev);
+    case 64: return launch_n<64>(s, x, B, C, dt, A, Acs, dtq, S, CB, st, ev);
+    case 128: return launch_n<128>(s, x, B, C, dt, A, Acs, dtq, S, CB, st, ev);
+    case 256: return launch_n<256>(s, x, B, C, dt, A, Acs, dtq, S, CB, st, ev);
   }
   return hipErrorInvalidValue;
 }

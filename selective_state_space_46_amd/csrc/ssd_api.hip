@@ -156,26 +156,34 @@ ssd_status ssd_chunk_scan_fwd_timed(const void* x, const void* dt, const float* 
   uint16_t* Hb = mfma ? reinterpret_cast<uint16_t*>(ws + w.hb) : nullptr;
   uint16_t* CB = mfma ? reinterpret_cast<uint16_t*>(ws + w.cb) : nullptr;
 
-  auto mark = [&](int i) {
-    if (!stage_events || !stage_events[i]) return true;
-    return hipEventRecord(static_cast<hipEvent_t>(stage_events[i]), hs) == hipSuccess;
+  // stage i's events: stage_events[2 i] (start), stage_events[2 i + 1] (stop),
+  // recorded by the kernel's own dispatch
+  auto ev = [&](int i) {
+    StageEv e;
+    if (stage_events) {
+      e.start = static_cast<hipEvent_t>(stage_events[2 * i]);
+      e.stop = static_cast<hipEvent_t>(stage_events[2 * i + 1]);
+    }
+    return e;
   };
-  // stage 0: cumulative sums, stage 1: chunk states. The matrix-core
-  // chunk_state launch also computes the cumulative sums and the C B^T tiles,
-  // so stage 0 is empty on that path.
-  if (!mark(0)) return SSD_ERR_HIP;
-  if (!mfma && launch_chunk_cumsum(s, dtype, dt, A, Acs, dtq, hs) != hipSuccess) return SSD_ERR_HIP;
-  if (!mark(1)) return SSD_ERR_HIP;
-  const hipError_t se = mfma ? launch_chunk_state_mfma(s, x, B, C, dt, A, Acs, dtq, S, CB, hs)
-                             : launch_chunk_state(s, dtype, x, B, Acs, dtq, S, hs);
+  // stage 0: cumulative sums, 1: chunk states, 2: state passing, 3: chunk
+  // outputs. The matrix-core chunk_state launch also computes the cumulative
+  // sums and the C B^T tiles, so stage 0 launches nothing on that path: its
+  // two events are recorded back to back.
+  if (mfma) {
+    const StageEv e0 = ev(0);
+    if (e0.start && hipEventRecord(e0.start, hs) != hipSuccess) return SSD_ERR_HIP;
+    if (e0.stop && hipEventRecord(e0.stop, hs) != hipSuccess) return SSD_ERR_HIP;
+  } else if (launch_chunk_cumsum(s, dtype, dt, A, Acs, dtq, hs, ev(0)) != hipSuccess) {
+    return SSD_ERR_HIP;
+  }
+  const hipError_t se = mfma ? launch_chunk_state_mfma(s, x, B, C, dt, A, Acs, dtq, S, CB, hs, ev(1))
+                             : launch_chunk_state(s, dtype, x, B, Acs, dtq, S, hs, ev(1));
   if (se != hipSuccess) return SSD_ERR_HIP;
-  if (!mark(2)) return SSD_ERR_HIP;
-  if (launch_state_passing(s, S, Hb, Acs, init_state, final_state, hs) != hipSuccess)
+  if (launch_state_passing(s, S, Hb, Acs, init_state, final_state, hs, ev(2)) != hipSuccess)
     return SSD_ERR_HIP;
-  if (!mark(3)) return SSD_ERR_HIP;
-  if (launch_chunk_scan(s, dtype, mfma, x, B, C, Acs, dtq, S, Hb, CB, D, y, hs) != hipSuccess)
+  if (launch_chunk_scan(s, dtype, mfma, x, B, C, Acs, dtq, S, Hb, CB, D, y, hs, ev(3)) != hipSuccess)
     return SSD_ERR_HIP;
-  if (!mark(4)) return SSD_ERR_HIP;
   return SSD_OK;
 }
 

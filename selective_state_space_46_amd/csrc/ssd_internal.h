@@ -2,6 +2,7 @@
 // libssd.so (device helpers, problem shape, workspace layout, launchers).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -104,37 +105,46 @@ __device__ __forceinline__ int xcd_swizzle(int bid, int nblocks) {
   return (bid % 8) * (nblocks / 8) + bid / 8;
 }
 
+// Optional start / stop events of one forward launch. The launchers pass them
+// to hipExtLaunchKernel, which records them as part of the kernel's own
+// dispatch, so the pair brackets exactly that kernel's execution (null: no
+// events).
+struct StageEv {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+
 // ---------------------------------------------------------------------------
 // Launchers (one translation unit each). All return the launch status.
 // ---------------------------------------------------------------------------
 hipError_t launch_chunk_cumsum(const FwdShape& s, ssd_dtype dt_type, const void* dt, const float* A,
-                               float* Acs, float* dtq, hipStream_t st);
+                               float* Acs, float* dtq, hipStream_t st, const StageEv& ev = StageEv{});
 
 // S: chunk states [b, nc, H, P, N] f32 (generic path: from Acs / dtq that
 // chunk_cumsum wrote).
 hipError_t launch_chunk_state(const FwdShape& s, ssd_dtype type, const void* x, const void* B,
-                              const float* Acs, const float* dtq, float* S, hipStream_t st);
+                              const float* Acs, const float* dtq, float* S, hipStream_t st, const StageEv& ev = StageEv{});
 // Matrix-core path: S^T [b, nc, H, P, N] f32; the same launch also computes
 // the in-chunk cumulative sums (written to Acs / dtq) and the C B^T tiles
 // (CB [b, nc, G, ntile, 64, 16] bf16) for the kernels after it.
 hipError_t launch_chunk_state_mfma(const FwdShape& s, const void* x, const void* B, const void* C,
                                    const void* dt, const float* A, float* Acs, float* dtq,
-                                   float* S, uint16_t* CB, hipStream_t st);
+                                   float* S, uint16_t* CB, hipStream_t st, const StageEv& ev = StageEv{});
 
 // Hb == nullptr: states entering each chunk overwrite S in place (fp32);
 // otherwise they are written to Hb as bf16 and S is left as it was.
 hipError_t launch_state_passing(const FwdShape& s, float* S, uint16_t* Hb, const float* Acs,
-                                const float* init, float* final_state, hipStream_t st);
+                                const float* init, float* final_state, hipStream_t st, const StageEv& ev = StageEv{});
 
 // Generic path reads Hst (fp32, [b, nc, H, P, N]); MFMA path reads Hb (bf16)
 // and the C B^T tiles CB.
 hipError_t launch_chunk_scan(const FwdShape& s, ssd_dtype type, bool mfma, const void* x,
                              const void* B, const void* C, const float* Acs, const float* dtq,
                              const float* Hst, const uint16_t* Hb, const uint16_t* CB,
-                             const float* D, void* y, hipStream_t st);
+                             const float* D, void* y, hipStream_t st, const StageEv& ev = StageEv{});
 hipError_t launch_chunk_scan_mfma(const FwdShape& s, const void* x, const uint16_t* CB,
                                   const void* C, const float* Acs, const float* dtq,
-                                  const uint16_t* Hb, const float* D, void* y, hipStream_t st);
+                                  const uint16_t* Hb, const float* D, void* y, hipStream_t st, const StageEv& ev = StageEv{});
 
 hipError_t launch_state_update(ssd_dtype type, float* state, const void* x, const void* dt,
                                const float* A, const void* B, const void* C, const float* D, void* y,

@@ -144,16 +144,16 @@ __global__ __launch_bounds__(kThreads) void state_passing_scalar(
 }  // namespace
 
 hipError_t launch_state_passing(const FwdShape& s, float* S, uint16_t* Hb, const float* Acs,
-                                const float* init, float* final_state, hipStream_t st) {
+                                const float* init, float* final_state, hipStream_t st, const StageEv& ev) {
   if (s.N % 4 == 0) {
     const long tiles = long(s.b) * s.H * ((s.P + kTP - 1) / kTP) * ((s.N + kTN - 1) / kTN);
-    hipLaunchKernelGGL(state_passing_tiled, dim3(unsigned(tiles)), dim3(kThreads), 0, st, S, Hb, Acs,
+    hipExtLaunchKernelGGL(state_passing_tiled, dim3(unsigned(tiles)), dim3(kThreads), 0, st, ev.start, ev.stop, 0, S, Hb, Acs,
                        init, final_state, s.H, s.P, s.N, s.Q, s.nc);
   } else {
     if (Hb) return hipErrorInvalidValue;     // the MFMA path never has N % 4 != 0
     const long total = long(s.b) * s.H * s.N * s.P;
     const long blocks = (total + kThreads - 1) / kThreads;
-    hipLaunchKernelGGL(state_passing_scalar, dim3(unsigned(blocks)), dim3(kThreads), 0, st, S, Acs,
+    hipExtLaunchKernelGGL(state_passing_scalar, dim3(unsigned(blocks)), dim3(kThreads), 0, st, ev.start, ev.stop, 0, S, Acs,
                        init, final_state, s.H, s.P, s.N, s.Q, s.nc, total);
   }
   return hipGetLastError();

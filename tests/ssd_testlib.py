@@ -58,3 +58,34 @@ def columns_of(y, fin, cols):
 
 
 rel_l2 = oracle.rel_l2
+
+
+class HipEvents:
+    """hipEvent_t handles through the HIP runtime's C API (for the timed entry
+    point, which takes raw handles)."""
+
+    def __init__(self):
+        import ctypes
+        self.ct = ctypes
+        self.rt = ctypes.CDLL("libamdhip64.so")
+        self.rt.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.rt.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                ctypes.c_void_p]
+        self.rt.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self, n):
+        out = []
+        for _ in range(n):
+            e = self.ct.c_void_p()
+            assert self.rt.hipEventCreate(self.ct.byref(e)) == 0
+            out.append(e.value)
+        return out
+
+    def ms(self, a, b):
+        v = self.ct.c_float()
+        assert self.rt.hipEventElapsedTime(self.ct.byref(v), a, b) == 0
+        return float(v.value)
+
+    def destroy(self, evs):
+        for e in evs:
+            self.rt.hipEventDestroy(e)

@@ -130,6 +130,34 @@ def test_deterministic():
     np.testing.assert_array_equal(f1, f2)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_timed_entry_point(dtype):
+    """The timed entry point computes bit-for-bit what the plain one does, and
+    its per-stage event pairs give ordered, non-negative kernel times."""
+    import torch
+    import selective_state_space_46_amd as ssd
+    from ssd_testlib import HipEvents
+    w = workloads.with_shape(workloads.MAMBA2_130M, batch=2, seqlen=700, dtype=dtype,
+                             init="normal0.1", seed=1750)
+    inp = workloads.make_fwd_inputs(w)
+    x, dt, B, C = (dev(inp[k], dtype) for k in ("x", "dt", "B", "C"))
+    A, D, init = dev(inp["A"]), dev(inp["D"]), dev(inp["init"])
+    y1, f1 = ssd.ssd_chunk_scan_fwd(x, dt, A, B, C, D, init, 256)
+    hip = HipEvents()
+    ev = hip.create(8)
+    y2, f2 = ssd.ssd_chunk_scan_fwd_timed(x, dt, A, B, C, D, init, 256, stage_events=ev)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2) and torch.equal(f1, f2)
+    stage = [hip.ms(ev[2 * i], ev[2 * i + 1]) for i in range(4)]
+    gaps = [hip.ms(ev[2 * i + 1], ev[2 * i + 2]) for i in range(3)]
+    hip.destroy(ev)
+    print(f"[timed {dtype}] stage ms {stage} gaps {gaps}", flush=True)
+    assert all(t >= 0.0 for t in stage) and all(g >= 0.0 for g in gaps)
+    assert all(t > 0.0 for t in stage[1:])          # stages 1..3 always launch a kernel
+    with pytest.raises(ValueError):
+        ssd.ssd_chunk_scan_fwd_timed(x, dt, A, B, C, D, init, 256, stage_events=ev[:5])
+
+
 # ---------------------------------------------------------------- decode
 
 def _gpu_decode(inp, dtype, steps=None):
