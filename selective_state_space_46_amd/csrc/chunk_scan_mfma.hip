@@ -63,7 +63,7 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_mfma_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t sHt[HROWS][kHS];
   __shared__ __attribute__((aligned(16))) float sA[kSC];  // Acs * log2(e)
   __shared__ __attribute__((aligned(16))) float sF[kSC];  // exp(Acs[block end] - Acs_s) * dt_s
-  __shared__ __attribute__((aligned(16))) float sD[kSC];  // dt_s
+  __shared__ __attribute__((aligned(16))) float sL[kSC];  // log2(dt_s) - Acs_s log2(e)
 
   const int id = xcd_swizzle(blockIdx.x, gridDim.x);
   const int h = id % H;
@@ -117,7 +117,7 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_mfma_kernel(
     }
     sA[i] = a;
     sF[i] = f;
-    sD[i] = d;
+    sL[i] = __builtin_amdgcn_logf(d) - a;    // log2; -inf where dt = 0
   }
   if constexpr (HLDS) {
     const uint16_t* hsrc = Hb + ((size_t(b) * nc + c0) * H + h) * size_t(P) * N;
@@ -156,6 +156,20 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_mfma_kernel(
   }
   __syncthreads();
 
+  // The transposed x reads of column block j start at row 32 j; the x tile's
+  // swizzle repeats every 16 rows, so their addresses are lane constants (per
+  // 32-column half pb and per 8-row half of a 16-row group) plus 32 j rows,
+  // and the second fragment of a block sits 16 rows further.
+  int xo[P / 32][2];
+  {
+    const int q16 = lane & 15;
+    const int mcol = 16 * ((lane >> 4) & 1) + 4 * (q16 & 3);
+#pragma unroll
+    for (int pb = 0; pb < P / 32; ++pb)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) xo[pb][u] = lds_off<RBX, true>(4 * g2 + 8 * u + (q16 >> 2), 32 * pb + mcol);
+  }
+
   const float Dh = D ? D[h] : 0.f;
   for (int which = 0; which < 2; ++which) {
     const int i = which ? 7 - wave : wave;  // 32-row block of the super-chunk
@@ -192,7 +206,7 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_mfma_kernel(
     const float sl = __builtin_amdgcn_exp2f(sA[lcol]);
 #pragma unroll
     for (int pb = 0; pb < P / 32; ++pb) {
-      f32x16 a = zero16();
+      acc[pb] = zero16();
 #pragma unroll
       for (int ks = 0; ks < N / 16; ++ks) {
         u32x4 hf;
@@ -202,11 +216,10 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_mfma_kernel(
           hf = load16(Hb + (((size_t(b) * nc + cg) * H + h) * P + 32 * pb + l32) * size_t(N) + 16 * ks +
                       8 * g2);
         }
-        a = mfma32x32x16(hf, cf[ks], a);
+        acc[pb] = mfma32x32x16(hf, cf[ks], acc[pb]);
       }
 #pragma unroll
-      for (int r = 0; r < 16; ++r) a[r] *= sl;
-      acc[pb] = a;
+      for (int r = 0; r < 16; ++r) acc[pb][r] *= sl;
     }
 
     // ---- y^T += X'^T G^T over the column blocks of the chunk
@@ -216,16 +229,16 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_mfma_kernel(
     // per 32 p. Off the diagonal (every s < every l) the decay is
     // exp(Acs_l - Acs_e) * [exp(Acs_e - Acs_s) dt_s] with e = 32 j + 31, the
     // column block's last token: both factors are <= 1. On the diagonal it is
-    // exp(Acs_l - Acs_s) dt_s per element, masked to s <= l.
+    // exp(Acs_l - Acs_s) dt_s = 2^(Acs_l log2 e + [log2 dt_s - Acs_s log2 e])
+    // per element (bracket from LDS; exponent <= log2 dt_s for s <= l), and
+    // elements with s > l are replaced by zero, whatever their product.
     auto apply = [&](const int jj, const u32x4 (&tile)[2], const bool diag) {
       const int j = jfirst + jj;
       uint32_t gw[8];
-      f32x4 fa[4], fb[4];
+      f32x4 fa[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        fa[q] = *reinterpret_cast<const f32x4*>(&(diag ? sA : sF)[32 * j + 8 * q + 4 * g2]);
-        if (diag) fb[q] = *reinterpret_cast<const f32x4*>(&sD[32 * j + 8 * q + 4 * g2]);
-      }
+      for (int q = 0; q < 4; ++q)
+        fa[q] = *reinterpret_cast<const f32x4*>(&(diag ? sL : sF)[32 * j + 8 * q + 4 * g2]);
       const float lfac = diag ? 0.f : __builtin_amdgcn_exp2f(al - sA[32 * j + 31]);
 #pragma unroll
       for (int m = 0; m < 8; ++m) {
@@ -234,10 +247,10 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_mfma_kernel(
         float lo, hi;
         if (diag) {
           const int s0 = 8 * (m / 2) + 4 * g2 + k;
-          const float elo = __builtin_amdgcn_exp2f(fminf(al - fa[m / 2][k], 0.f)) * fb[m / 2][k];
-          const float ehi = __builtin_amdgcn_exp2f(fminf(al - fa[m / 2][k + 1], 0.f)) * fb[m / 2][k + 1];
-          lo = s0 <= l32 ? bf16_lo(w) * elo : 0.f;
-          hi = s0 + 1 <= l32 ? bf16_hi(w) * ehi : 0.f;
+          const float plo = bf16_lo(w) * __builtin_amdgcn_exp2f(al + fa[m / 2][k]);
+          const float phi = bf16_hi(w) * __builtin_amdgcn_exp2f(al + fa[m / 2][k + 1]);
+          lo = s0 <= l32 ? plo : 0.f;
+          hi = s0 + 1 <= l32 ? phi : 0.f;
         } else {
           lo = bf16_lo(w) * lfac * fa[m / 2][k];
           hi = bf16_hi(w) * lfac * fa[m / 2][k + 1];
@@ -246,11 +259,14 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_mfma_kernel(
       }
       const u32x4 ga = u32x4{gw[0], gw[1], gw[2], gw[3]};  // rows s = 32j + [0, 16)
       const u32x4 gb = u32x4{gw[4], gw[5], gw[6], gw[7]};  // rows s = 32j + [16, 32)
-      const int kb = 32 * j + 4 * g2;
+      const int jo = 32 * j * P;              // element offset of row 32 j (P elements per row)
 #pragma unroll
       for (int pb = 0; pb < P / 32; ++pb) {
-        acc[pb] = mfma32x32x16(frag_tr<RBX, true>(sX, kb, kb + 8, 32 * pb, lane), ga, acc[pb]);
-        acc[pb] = mfma32x32x16(frag_tr<RBX, true>(sX, kb + 16, kb + 24, 32 * pb, lane), gb, acc[pb]);
+        const u32x2 a0 = lds_read_tr16(sX, xo[pb][0] + jo), a1 = lds_read_tr16(sX, xo[pb][1] + jo);
+        const u32x2 b0 = lds_read_tr16(sX, xo[pb][0] + jo + 16 * P);
+        const u32x2 b1 = lds_read_tr16(sX, xo[pb][1] + jo + 16 * P);
+        acc[pb] = mfma32x32x16(u32x4{a0[0], a0[1], a1[0], a1[1]}, ga, acc[pb]);
+        acc[pb] = mfma32x32x16(u32x4{b0[0], b0[1], b1[0], b1[1]}, gb, acc[pb]);
       }
     };
 #pragma unroll 1
