@@ -19,6 +19,10 @@ Every function here is pinned by the closed forms and invariants in
 ``tests/test_oracle_pins.py`` (quadratic semiseparable form, A=0 linear
 attention, T=1, constant dt, dt=0 identity, large-decay reset, split/resume,
 decode chain == forward).
+
+``oracle.epilogue`` holds the two element-wise stages next to the core (the
+gated RMS normalisation after it, the depthwise causal convolution before
+it), pinned in ``tests/test_oracle_epilogue_pins.py``.
 """
 from __future__ import annotations
 
