@@ -68,7 +68,8 @@ typedef enum {
     SSD_ERR_WORKSPACE = 5, /* workspace NULL or smaller than the query's answer   */
     SSD_ERR_HIP = 6,       /* a kernel launch failed                              */
     SSD_ERR_ALIAS = 7,     /* an output overlaps an input it must not overlap     */
-    SSD_ERR_ALIGN = 8      /* a pointer is not 16-byte aligned                    */
+    SSD_ERR_ALIGN = 8,     /* a pointer is not 16-byte aligned                    */
+    SSD_ERR_VALUE = 9      /* a scalar argument is out of range (eps, activation) */
 } ssd_status;
 
 typedef enum { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype;

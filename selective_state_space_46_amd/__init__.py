@@ -12,6 +12,10 @@ Entry points (same names as the C ABI):
     ssd_chunk_scan_fwd(x, dt, A, B, C, D, init_state, chunk_len) -> (y, final_state)
     ssd_state_update(state, x, dt, A, B, C, D) -> y     (state updated in place)
     ssd_status_string(code) -> str
+and, from ``include/ssd_epilogue.h``, the element-wise stages next to the core:
+    ssd_gated_rmsnorm(y, z, weight, group, eps) -> out
+    ssd_causal_conv1d_fwd(x, weight, bias, init_state, activation) -> (out, final_state)
+    ssd_causal_conv1d_update(state, x, weight, bias, activation) -> out   (state in place)
 """
 from __future__ import annotations
 
@@ -22,7 +26,8 @@ from typing import Optional, Tuple
 __all__ = [
     "SSD_F32", "SSD_BF16", "SSDError", "lib", "lib_path",
     "ssd_chunk_scan_fwd_workspace", "ssd_chunk_scan_fwd", "ssd_chunk_scan_fwd_timed",
-    "ssd_state_update", "ssd_status_string",
+    "ssd_state_update", "ssd_status_string", "ssd_gated_rmsnorm", "ssd_causal_conv1d_fwd",
+    "ssd_causal_conv1d_update",
 ]
 
 SSD_F32 = 0
@@ -31,6 +36,7 @@ SSD_BF16 = 1
 STATUS_NAMES = {
     0: "SSD_OK", 1: "SSD_ERR_NULL", 2: "SSD_ERR_SHAPE", 3: "SSD_ERR_DTYPE", 4: "SSD_ERR_CHUNK",
     5: "SSD_ERR_WORKSPACE", 6: "SSD_ERR_HIP", 7: "SSD_ERR_ALIAS", 8: "SSD_ERR_ALIGN",
+    9: "SSD_ERR_VALUE",
 }
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -69,6 +75,13 @@ def lib() -> ctypes.CDLL:
     L.ssd_state_update.restype = i32
     L.ssd_status_string.argtypes = [i32]
     L.ssd_status_string.restype = ctypes.c_char_p
+    i64, f32 = ctypes.c_long, ctypes.c_float
+    L.ssd_gated_rmsnorm.argtypes = [vp] * 4 + [i64, i32, i32, f32, i32, vp]
+    L.ssd_gated_rmsnorm.restype = i32
+    L.ssd_causal_conv1d_fwd.argtypes = [vp] * 6 + [i32] * 5 + [i32, vp]
+    L.ssd_causal_conv1d_fwd.restype = i32
+    L.ssd_causal_conv1d_update.argtypes = [vp] * 5 + [i32] * 4 + [i32, vp]
+    L.ssd_causal_conv1d_update.restype = i32
     _lib = L
     return L
 
@@ -205,3 +218,115 @@ def ssd_state_update(state, x, dt, A, B, C, D=None, *, y=None, stream=None):
     if r != 0:
         raise SSDError(r, "ssd_state_update")
     return y
+
+
+# --------------------------------------------------------------------------
+# element-wise stages next to the core (include/ssd_epilogue.h)
+# --------------------------------------------------------------------------
+
+def _inout(t, dev, name):
+    """A buffer the call writes: it must already be dense on the device."""
+    if t is None:
+        return None
+    if not t.is_cuda or t.device != dev or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous tensor on {dev}")
+    return t
+
+
+def ssd_gated_rmsnorm(y, z, weight, group: Optional[int] = None, eps: float = 1e-5, *, out=None,
+                      stream=None):
+    """rmsnorm(y) * silu(z) over groups of `group` channels of the last axis
+    (default: the whole last axis). y, z [..., dim] fp32 or bf16, weight [dim]
+    fp32. Returns out (y's shape and dtype); out may be y itself."""
+    import torch
+    dev = y.device
+    y = _dev(y, dev, "y")
+    z = _dev(z, dev, "z")
+    weight = _dev(weight, dev, "weight")
+    code = _dtype_code(y)
+    _same(z, y.dtype, "z")
+    _same(weight, torch.float32, "weight")
+    if z.shape != y.shape or weight.dim() != 1 or weight.shape[0] != y.shape[-1]:
+        raise ValueError("z must match y and weight must be [dim]")
+    dim = int(y.shape[-1])
+    ntok = y.numel() // max(dim, 1)
+    group = dim if group is None else int(group)
+    out = torch.empty_like(y) if out is None else _inout(out, dev, "out")
+    _same(out, y.dtype, "out")
+    r = lib().ssd_gated_rmsnorm(_ptr(y), _ptr(z), _ptr(weight), _ptr(out), ntok, dim, group, float(eps),
+                                code, _stream(dev, stream))
+    if r != 0:
+        raise SSDError(r, "ssd_gated_rmsnorm")
+    return out
+
+
+def _act_code(activation) -> int:
+    if activation in ("silu", 1, True):
+        return 1
+    if activation in (None, "none", 0, False):
+        return 0
+    raise ValueError(f"activation must be 'silu' or None, got {activation!r}")
+
+
+def ssd_causal_conv1d_fwd(x, weight, bias=None, init_state=None, activation="silu", *, out=None,
+                          final_state=None, return_final_state: bool = False, stream=None):
+    """Depthwise causal convolution over tokens. x [b, T, C] fp32 or bf16,
+    weight [C, K] fp32, bias [C] fp32 or None, init_state [b, K-1, C] (x's
+    dtype) or None. Returns (out [b, T, C], final_state [b, K-1, C] or None);
+    final_state may be passed as init_state itself to carry it in place."""
+    import torch
+    dev = x.device
+    x = _dev(x, dev, "x")
+    weight, bias = _dev(weight, dev, "weight"), _dev(bias, dev, "bias")
+    code = _dtype_code(x)
+    _same(weight, torch.float32, "weight")
+    _same(bias, torch.float32, "bias")
+    if x.dim() != 3 or weight.dim() != 2 or weight.shape[0] != x.shape[2]:
+        raise ValueError("x must be [b, T, C] and weight [C, K]")
+    b, T, C = (int(v) for v in x.shape)
+    K = int(weight.shape[1])
+    if init_state is not None:
+        init_state = _inout(init_state, dev, "init_state")
+        _same(init_state, x.dtype, "init_state")
+        if tuple(init_state.shape) != (b, K - 1, C):
+            raise ValueError("init_state must be [b, K-1, C]")
+    out = torch.empty_like(x) if out is None else _inout(out, dev, "out")
+    _same(out, x.dtype, "out")
+    if final_state is None and return_final_state:
+        final_state = torch.empty((b, K - 1, C), dtype=x.dtype, device=dev)
+    elif final_state is not None:
+        final_state = _inout(final_state, dev, "final_state")
+        _same(final_state, x.dtype, "final_state")
+    r = lib().ssd_causal_conv1d_fwd(_ptr(x), _ptr(weight), _ptr(bias), _ptr(init_state), _ptr(out),
+                                    _ptr(final_state), b, T, C, K, _act_code(activation), code,
+                                    _stream(dev, stream))
+    if r != 0:
+        raise SSDError(r, "ssd_causal_conv1d_fwd")
+    return out, final_state
+
+
+def ssd_causal_conv1d_update(state, x, weight, bias=None, activation="silu", *, out=None, stream=None):
+    """One token of the convolution: state [b, K-1, C] (x's dtype) updated in
+    place, x [b, C]. Returns out [b, C]."""
+    import torch
+    dev = x.device
+    x = _dev(x, dev, "x")
+    weight, bias = _dev(weight, dev, "weight"), _dev(bias, dev, "bias")
+    code = _dtype_code(x)
+    _same(weight, torch.float32, "weight")
+    _same(bias, torch.float32, "bias")
+    if x.dim() != 2 or weight.dim() != 2 or weight.shape[0] != x.shape[1]:
+        raise ValueError("x must be [b, C] and weight [C, K]")
+    b, C = (int(v) for v in x.shape)
+    K = int(weight.shape[1])
+    if state is not None:
+        state = _inout(state, dev, "state")
+        _same(state, x.dtype, "state")
+        if tuple(state.shape) != (b, K - 1, C):
+            raise ValueError("state must be [b, K-1, C]")
+    out = torch.empty_like(x) if out is None else _inout(out, dev, "out")
+    r = lib().ssd_causal_conv1d_update(_ptr(state), _ptr(x), _ptr(weight), _ptr(bias), _ptr(out), b, C, K,
+                                       _act_code(activation), code, _stream(dev, stream))
+    if r != 0:
+        raise SSDError(r, "ssd_causal_conv1d_update")
+    return out

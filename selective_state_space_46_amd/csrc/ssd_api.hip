@@ -4,7 +4,9 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <cmath>
 
+#include "ssd_epilogue.h"
 #include "ssd_internal.h"
 
 using namespace ssd;
@@ -90,6 +92,7 @@ const char* ssd_status_string(ssd_status status) {
     case SSD_ERR_HIP: return "HIP kernel launch failed";
     case SSD_ERR_ALIAS: return "an output overlaps an input";
     case SSD_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case SSD_ERR_VALUE: return "a scalar argument is out of range";
   }
   return "unknown status";
 }
@@ -223,6 +226,91 @@ ssd_status ssd_state_update(float* state, const void* x, const void* dt, const f
   if (overlaps(y, xb, state, stb)) return SSD_ERR_ALIAS;
   if (launch_state_update(dtype, state, x, dt, A, B, C, D, y, batch, nheads, headdim, dstate,
                           ngroups, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return SSD_ERR_HIP;
+  return SSD_OK;
+}
+
+ssd_status ssd_gated_rmsnorm(const void* y, const void* z, const float* weight, void* out, long ntokens,
+                             int dim, int group, float eps, ssd_dtype dtype, void* stream) {
+  if (!dtype_ok(dtype)) return SSD_ERR_DTYPE;
+  if (ntokens < 1 || dim < 1 || group < 1 || dim % group) return SSD_ERR_SHAPE;
+  const double rows = double(ntokens) * (dim / group);
+  if (rows > double(1L << 26)) return SSD_ERR_SHAPE;     // one wave per row, 64 lanes each
+  if (!(eps >= 0.f) || !std::isfinite(eps)) return SSD_ERR_VALUE;
+  if (!y || !z || !weight || !out) return SSD_ERR_NULL;
+  const void* ptrs[] = {y, z, weight, out};
+  for (const void* p : ptrs)
+    if (misaligned(p)) return SSD_ERR_ALIGN;
+  const size_t nb = size_t(ntokens) * dim * esize(dtype), wb = size_t(dim) * sizeof(float);
+  if (out != y && overlaps(out, nb, y, nb)) return SSD_ERR_ALIAS;
+  if (overlaps(out, nb, z, nb) || overlaps(out, nb, weight, wb)) return SSD_ERR_ALIAS;
+  if (launch_gated_rmsnorm(dtype, y, z, weight, out, ntokens, dim, group, eps,
+                           static_cast<hipStream_t>(stream)) != hipSuccess)
+    return SSD_ERR_HIP;
+  return SSD_OK;
+}
+
+ssd_status ssd_causal_conv1d_fwd(const void* x, const float* weight, const float* bias,
+                                 const void* init_state, void* out, void* final_state, int batch,
+                                 int seqlen, int channels, int kernel_width, int activation,
+                                 ssd_dtype dtype, void* stream) {
+  if (!dtype_ok(dtype)) return SSD_ERR_DTYPE;
+  if (batch < 1 || seqlen < 1 || channels < 1 || kernel_width < 1 || kernel_width > SSD_CONV_MAX_WIDTH)
+    return SSD_ERR_SHAPE;
+  if (double(batch) * ((seqlen + 15) / 16) * channels > double(0x7fffffff)) return SSD_ERR_SHAPE;
+  if (activation != 0 && activation != 1) return SSD_ERR_VALUE;
+  if (!x || !weight || !out) return SSD_ERR_NULL;
+  const void* ptrs[] = {x, weight, bias, init_state, out, final_state};
+  for (const void* p : ptrs)
+    if (misaligned(p)) return SSD_ERR_ALIGN;
+  const size_t e = esize(dtype);
+  const size_t xb = size_t(batch) * seqlen * channels * e;
+  const size_t sb = size_t(batch) * (kernel_width - 1) * channels * e;
+  const size_t wb = size_t(channels) * kernel_width * sizeof(float), bb = size_t(channels) * sizeof(float);
+  struct In {
+    const void* p;
+    size_t n;
+  } ins[] = {{x, xb}, {weight, wb}, {bias, bb}, {init_state, sb}, {final_state, sb}};
+  for (const In& in : ins)
+    if (overlaps(out, xb, in.p, in.n)) return SSD_ERR_ALIAS;
+  if (final_state && sb) {
+    if (overlaps(final_state, sb, x, xb) || overlaps(final_state, sb, weight, wb) ||
+        overlaps(final_state, sb, bias, bb))
+      return SSD_ERR_ALIAS;
+    if (final_state != init_state && overlaps(final_state, sb, init_state, sb)) return SSD_ERR_ALIAS;
+  }
+  if (launch_causal_conv1d(dtype, x, weight, bias, init_state, out, sb ? final_state : nullptr, batch,
+                           seqlen, channels, kernel_width, activation,
+                           static_cast<hipStream_t>(stream)) != hipSuccess)
+    return SSD_ERR_HIP;
+  return SSD_OK;
+}
+
+ssd_status ssd_causal_conv1d_update(void* state, const void* x, const float* weight, const float* bias,
+                                    void* out, int batch, int channels, int kernel_width, int activation,
+                                    ssd_dtype dtype, void* stream) {
+  if (!dtype_ok(dtype)) return SSD_ERR_DTYPE;
+  if (batch < 1 || channels < 1 || kernel_width < 1 || kernel_width > SSD_CONV_MAX_WIDTH)
+    return SSD_ERR_SHAPE;
+  if (double(batch) * channels > double(0x7fffffff)) return SSD_ERR_SHAPE;
+  if (activation != 0 && activation != 1) return SSD_ERR_VALUE;
+  if (!x || !weight || !out || (!state && kernel_width > 1)) return SSD_ERR_NULL;
+  const void* ptrs[] = {state, x, weight, bias, out};
+  for (const void* p : ptrs)
+    if (misaligned(p)) return SSD_ERR_ALIGN;
+  const size_t e = esize(dtype);
+  const size_t xb = size_t(batch) * channels * e;
+  const size_t sb = size_t(batch) * (kernel_width - 1) * channels * e;
+  const size_t wb = size_t(channels) * kernel_width * sizeof(float), bb = size_t(channels) * sizeof(float);
+  struct In {
+    const void* p;
+    size_t n;
+  } ins[] = {{x, xb}, {weight, wb}, {bias, bb}};
+  for (const In& in : ins)
+    if (overlaps(out, xb, in.p, in.n) || overlaps(state, sb, in.p, in.n)) return SSD_ERR_ALIAS;
+  if (overlaps(out, xb, state, sb)) return SSD_ERR_ALIAS;
+  if (launch_causal_conv1d_update(dtype, state, x, weight, bias, out, batch, channels, kernel_width,
+                                  activation, static_cast<hipStream_t>(stream)) != hipSuccess)
     return SSD_ERR_HIP;
   return SSD_OK;
 }

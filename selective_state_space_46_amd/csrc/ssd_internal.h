@@ -146,6 +146,16 @@ hipError_t launch_chunk_scan_mfma(const FwdShape& s, const void* x, const uint16
                                   const void* C, const float* Acs, const float* dtq,
                                   const uint16_t* Hb, const float* D, void* y, hipStream_t st, const StageEv& ev = StageEv{});
 
+// Element-wise stages next to the core (epilogue.hip).
+hipError_t launch_gated_rmsnorm(ssd_dtype type, const void* y, const void* z, const float* w, void* out,
+                                long ntok, int dim, int group, float eps, hipStream_t st);
+hipError_t launch_causal_conv1d(ssd_dtype type, const void* x, const float* w, const float* bias,
+                                const void* init, void* out, void* fin, int b, int T, int C, int K, int act,
+                                hipStream_t st);
+hipError_t launch_causal_conv1d_update(ssd_dtype type, void* state, const void* x, const float* w,
+                                       const float* bias, void* out, int b, int C, int K, int act,
+                                       hipStream_t st);
+
 hipError_t launch_state_update(ssd_dtype type, float* state, const void* x, const void* dt,
                                const float* A, const void* B, const void* C, const float* D, void* y,
                                int batch, int H, int P, int N, int G, hipStream_t st);

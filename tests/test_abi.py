@@ -22,14 +22,18 @@ def L():
 
 
 def declared_symbols():
-    text = open(os.path.join(ROOT, "include", "ssd_api.h")).read()
-    return re.findall(r"SSD_API\s+[\w\s\*]*?\b(ssd_\w+)\s*\(", text)
+    out = []
+    for h in ("ssd_api.h", "ssd_epilogue.h"):
+        text = open(os.path.join(ROOT, "include", h)).read()
+        out += re.findall(r"SSD_API\s+[\w\s\*]*?\b(ssd_\w+)\s*\(", text)
+    return out
 
 
 def test_header_declares_the_entry_points():
     assert set(declared_symbols()) == {"ssd_chunk_scan_fwd_workspace", "ssd_chunk_scan_fwd",
                                        "ssd_chunk_scan_fwd_timed", "ssd_state_update",
-                                       "ssd_status_string"}
+                                       "ssd_status_string", "ssd_gated_rmsnorm",
+                                       "ssd_causal_conv1d_fwd", "ssd_causal_conv1d_update"}
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -38,7 +42,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_status_strings(L):
-    for code in range(9):
+    for code in range(10):
         s = ssd.ssd_status_string(code)
         assert s and s != "unknown status"
     assert ssd.ssd_status_string(99) == "unknown status"
@@ -133,3 +137,74 @@ def test_decode_argument_errors(L):
     assert upd(L, y=FAKE + 0x100000) == 7             # y over x
     assert upd(L, state=FAKE + 0x600000) == 7         # state over y
     assert upd(L, x=FAKE + 0x100002) == 8
+
+
+def norm(L, **kw):
+    a = dict(y=FAKE, z=FAKE + 0x100000, w=FAKE + 0x200000, out=FAKE + 0x300000, n=16, dim=64, group=64,
+             eps=1e-5, dtype=1, stream=None)
+    a.update(kw)
+    return L.ssd_gated_rmsnorm(a["y"], a["z"], a["w"], a["out"], a["n"], a["dim"], a["group"], a["eps"],
+                               a["dtype"], a["stream"])
+
+
+def test_gated_rmsnorm_argument_errors(L):
+    assert norm(L, dtype=4) == 3
+    assert norm(L, n=0) == 2
+    assert norm(L, dim=0) == 2
+    assert norm(L, group=0) == 2
+    assert norm(L, dim=64, group=48) == 2             # dim % group
+    assert norm(L, n=1 << 27, dim=64, group=1) == 2   # more rows than the grid allows
+    assert norm(L, eps=-1.0) == 9
+    assert norm(L, eps=float("inf")) == 9
+    assert norm(L, eps=float("nan")) == 9
+    for k in ("y", "z", "w", "out"):
+        assert norm(L, **{k: None}) == 1, k
+    assert norm(L, z=FAKE + 0x100008) == 8
+    assert norm(L, out=FAKE + 0x40) == 7              # out partly over y
+    assert norm(L, out=FAKE + 0x100000) == 7          # out over z
+    assert norm(L, out=FAKE + 0x200000) == 7          # out over the weight
+
+
+def conv(L, **kw):
+    a = dict(x=FAKE, w=FAKE + 0x100000, bias=None, init=None, out=FAKE + 0x300000, fin=None, b=2, T=64,
+             C=32, K=4, act=1, dtype=1, stream=None)
+    a.update(kw)
+    return L.ssd_causal_conv1d_fwd(a["x"], a["w"], a["bias"], a["init"], a["out"], a["fin"], a["b"], a["T"],
+                                   a["C"], a["K"], a["act"], a["dtype"], a["stream"])
+
+
+def test_conv1d_argument_errors(L):
+    assert conv(L, dtype=2) == 3
+    assert conv(L, T=0) == 2
+    assert conv(L, C=0) == 2
+    assert conv(L, K=0) == 2
+    assert conv(L, K=9) == 2
+    assert conv(L, b=65536, T=65536 * 16, C=16) == 2  # more threads than allowed
+    assert conv(L, act=2) == 9
+    for k in ("x", "w", "out"):
+        assert conv(L, **{k: None}) == 1, k
+    assert conv(L, init=FAKE + 0x400004) == 8
+    assert conv(L, out=FAKE + 0x100) == 7             # out over x
+    assert conv(L, fin=FAKE + 0x10) == 7              # final state over x
+    assert conv(L, init=FAKE + 0x400000, fin=FAKE + 0x400010) == 7   # partial overlap
+    assert conv(L, bias=FAKE + 0x300000) == 7         # out over the bias
+
+
+def upd1(L, **kw):
+    a = dict(state=FAKE, x=FAKE + 0x100000, w=FAKE + 0x200000, bias=None, out=FAKE + 0x300000, b=2, C=32,
+             K=4, act=1, dtype=1, stream=None)
+    a.update(kw)
+    return L.ssd_causal_conv1d_update(a["state"], a["x"], a["w"], a["bias"], a["out"], a["b"], a["C"],
+                                      a["K"], a["act"], a["dtype"], a["stream"])
+
+
+def test_conv1d_update_argument_errors(L):
+    assert upd1(L, dtype=5) == 3
+    assert upd1(L, C=0) == 2
+    assert upd1(L, K=9) == 2
+    assert upd1(L, act=-1) == 9
+    for k in ("state", "x", "w", "out"):
+        assert upd1(L, **{k: None}) == 1, k
+    assert upd1(L, out=FAKE + 0x100000) == 7          # out over x
+    assert upd1(L, state=FAKE + 0x300000) == 7        # state over out
+    assert upd1(L, x=FAKE + 0x100002) == 8

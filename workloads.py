@@ -181,3 +181,64 @@ def make_decode_inputs(w: DecodeWorkload, seed: Optional[int] = None) -> dict:
     Bs = _store(rng.standard_normal((S, b, G, N), dtype=np.float32) * s, w.dtype)
     Cs = _store(rng.standard_normal((S, b, G, N), dtype=np.float32) * s, w.dtype)
     return dict(state=state, xs=xs, dts=dts, A=A, Bs=Bs, Cs=Cs, D=D)
+
+
+# --------------------------------------------------------------------------
+# The element-wise stages next to the core (gated RMS normalisation after it,
+# depthwise causal convolution before it). Distributions: activations N(0,1);
+# normalisation weights 1 + N(0, 0.1); convolution weights and bias
+# U(-1/sqrt(K), 1/sqrt(K)) (the default initialisation of a Conv1d with
+# fan-in K); carried convolution state N(0, 1).
+# --------------------------------------------------------------------------
+
+@dataclasses.dataclass(frozen=True)
+class NormWorkload:
+    name: str
+    ntokens: int
+    dim: int
+    group: int
+    dtype: str = "bf16"
+    eps: float = 1e-5
+    seed: int = 0
+
+
+@dataclasses.dataclass(frozen=True)
+class ConvWorkload:
+    name: str
+    batch: int
+    seqlen: int
+    channels: int
+    width: int = 4
+    dtype: str = "bf16"
+    with_init: bool = False
+    seed: int = 0
+
+
+# the 130M-shaped layer: y and z are [b*T, H*P] = [16384, 1536], normalised
+# over the whole feature vector; the convolution runs over x, B and C
+# together, H*P + 2*G*N = 1792 channels, kernel width 4
+NORM_130M = NormWorkload("gated_norm_130m_16384x1536_bf16", 8 * 2048, 24 * 64, 24 * 64, seed=4610)
+CONV_130M = ConvWorkload("conv_xbc_130m_b8_T2048_C1792_K4_bf16", 8, 2048, 24 * 64 + 2 * 128, seed=4611)
+
+
+def make_norm_inputs(w: NormWorkload, seed: Optional[int] = None) -> dict:
+    """y, z [ntokens, dim] (dtype carriers), weight [dim] fp32."""
+    rng = np.random.default_rng(w.seed if seed is None else seed)
+    y = _store(rng.standard_normal((w.ntokens, w.dim), dtype=np.float32), w.dtype)
+    z = _store(rng.standard_normal((w.ntokens, w.dim), dtype=np.float32), w.dtype)
+    weight = (1.0 + 0.1 * rng.standard_normal(w.dim)).astype(np.float32)
+    return dict(y=y, z=z, weight=weight)
+
+
+def make_conv_inputs(w: ConvWorkload, seed: Optional[int] = None) -> dict:
+    """x [b, T, C] (dtype carrier), weight [C, K] and bias [C] fp32, init
+    [b, K-1, C] (dtype carrier) or None."""
+    rng = np.random.default_rng(w.seed if seed is None else seed)
+    x = _store(rng.standard_normal((w.batch, w.seqlen, w.channels), dtype=np.float32), w.dtype)
+    bound = 1.0 / math.sqrt(w.width)
+    weight = rng.uniform(-bound, bound, size=(w.channels, w.width)).astype(np.float32)
+    bias = rng.uniform(-bound, bound, size=w.channels).astype(np.float32)
+    init = None
+    if w.with_init:
+        init = _store(rng.standard_normal((w.batch, w.width - 1, w.channels), dtype=np.float32), w.dtype)
+    return dict(x=x, weight=weight, bias=bias, init=init)
