@@ -279,6 +279,73 @@ def bench_decode(hip, w, warmup=4):
     }
 
 
+def bench_next_to_core(hip, steps=20, warmup=3):
+    """The element-wise stages next to the core on the 130M-shaped layer: the
+    depthwise causal conv1d over x, B, C (1792 channels, width 4) before it,
+    the gated RMS normalisation of y (16384 x 1536, whole-vector groups)
+    after it, and the conv's decode update on the batch-256 decode layer
+    (128 x 64 + 2 x 8 x 128 = 10240 channels). Algorithmic bytes: every
+    tensor element read or written once (weights included)."""
+    import torch
+    import selective_state_space_46_amd as ssd
+    stream = torch.cuda.current_stream().cuda_stream
+    out = {}
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        a, b = hip.event(), hip.event()
+        hip.record(a, stream)
+        for _ in range(steps):
+            fn()
+        hip.record(b, stream)
+        torch.cuda.synchronize()
+        ms = hip.ms(a, b) / steps
+        hip.destroy(a)
+        hip.destroy(b)
+        return ms
+
+    def entry(ms, nbytes, extra):
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        return dict(extra, ms=round(ms, 5), alg_bytes=nbytes, GB_per_s=round(gbs, 1),
+                    hbm_frac=round(gbs / HBM_PEAK_GBS, 4))
+
+    cw = workloads.CONV_130M
+    ci = workloads.make_conv_inputs(cw)
+    x = to_dev(ci["x"], cw.dtype)
+    wt, bias = to_dev(ci["weight"], "f32"), to_dev(ci["bias"], "f32")
+    y = torch.empty_like(x)
+    state = torch.zeros((cw.batch, cw.width - 1, cw.channels), dtype=x.dtype, device="cuda")
+    ms = timed(lambda: ssd.ssd_causal_conv1d_fwd(x, wt, bias, None, out=y, final_state=state, stream=stream))
+    e = x.element_size()
+    out["causal_conv1d"] = entry(ms, 2 * x.numel() * e + state.numel() * e + 4 * (wt.numel() + bias.numel()),
+                                 {"workload": cw.name})
+    del x, y
+
+    nw = workloads.NORM_130M
+    ni = workloads.make_norm_inputs(nw)
+    yv, zv, nwt = to_dev(ni["y"], nw.dtype), to_dev(ni["z"], nw.dtype), to_dev(ni["weight"], "f32")
+    o = torch.empty_like(yv)
+    ms = timed(lambda: ssd.ssd_gated_rmsnorm(yv, zv, nwt, nw.group, nw.eps, out=o, stream=stream))
+    out["gated_rmsnorm"] = entry(ms, 3 * yv.numel() * yv.element_size() + 4 * nwt.numel(),
+                                 {"workload": nw.name, "group": nw.group})
+    del yv, zv, o
+
+    dw = workloads.DECODE_B256
+    C = dw.nheads * dw.headdim + 2 * dw.ngroups * dw.dstate
+    uw = workloads.ConvWorkload("conv_decode_b256_C10240_K4_bf16", dw.batch, 1, C, 4, "bf16", True, seed=4612)
+    ui = workloads.make_conv_inputs(uw)
+    st = to_dev(ui["init"], "bf16")
+    xt = to_dev(ui["x"][:, 0], "bf16")
+    uwt, ub = to_dev(ui["weight"], "f32"), to_dev(ui["bias"], "f32")
+    ot = torch.empty_like(xt)
+    ms = timed(lambda: ssd.ssd_causal_conv1d_update(st, xt, uwt, ub, out=ot, stream=stream))
+    out["causal_conv1d_update"] = entry(ms, 2 * st.numel() * 2 + 2 * xt.numel() * 2 + 4 * (uwt.numel() + ub.numel()),
+                                        {"workload": uw.name})
+    return out
+
+
 def traffic_probe(w):
     """Three forward calls, then three copies of a 256 MiB buffer: a plain
     copy kernel that reads and writes exactly 256 MiB, against which the
@@ -393,6 +460,9 @@ def main():
                                "stage_ms": {k: round(v, 4) for k, v in rr["stage_ms"].items()}}
             log(f"[bench]   {rr['ms_per_step']:.4f} ms/step")
         out["other_workloads"] = others
+        log("[bench] stages next to the core (conv1d, gated RMSNorm, conv decode update)")
+        out["next_to_core"] = bench_next_to_core(hip)
+        log(f"[bench]   {out['next_to_core']}")
     if not args.no_cpu_baseline:
         log("[bench] timing the fp64 oracle on host cores")
         out["cpu_baseline"] = cpu_baseline(w)

@@ -63,7 +63,7 @@ __device__ __forceinline__ u32x4_t pack(const float (&f)[Vec<T>::n]) {
   u32x4_t v;
   if constexpr (sizeof(T) == 2) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = uint32_t(f32_to_bf16(f[2 * i])) | (uint32_t(f32_to_bf16(f[2 * i + 1])) << 16);
+    for (int i = 0; i < 4; ++i) v[i] = f32x2_to_bf16x2(f[2 * i], f[2 * i + 1]);
   } else {
 #pragma unroll
     for (int i = 0; i < 4; ++i) v[i] = __float_as_uint(f[i]);
@@ -147,18 +147,54 @@ __global__ __launch_bounds__(kThreads) void gated_rmsnorm_scalar(const T* y,
 }
 
 // ---------------------------------------------------------------------------
-// Depthwise causal convolution. Thread per (batch, run of kConvTok tokens,
-// V channels) with V = Vec<T>::n on the vector path (C % V == 0) and V = 1
-// otherwise; the K-1 tokens before the run come from x (or from the carried
-// state before token 0) and then slide through registers, so x is read once
-// plus a K-1-token halo per run.
-template <typename T, int K, bool VECP>
+// Depthwise causal convolution. Thread per (batch, run of kConvTok tokens, V
+// channels) with V = 4 on the vector path (C % 4 == 0: 8-byte bf16 or 16-byte
+// fp32 accesses) and V = 1 otherwise. The K-1 tokens before the run come from
+// x (or from the carried state before token 0) and then slide through
+// registers, so x is read once plus a K-1-token halo per run; on a full run
+// all token loads are issued before the first use (one memory latency per
+// run, not per token).
+template <typename T, int V> struct Chunk;          // V elements of T in one access
+template <> struct Chunk<uint16_t, 4> { typedef uint32_t raw __attribute__((ext_vector_type(2))); };
+template <> struct Chunk<float, 4> { typedef uint32_t raw __attribute__((ext_vector_type(4))); };
+template <typename T> struct Chunk<T, 1> { typedef T raw; };
+
+template <typename T, int V>
+__device__ __forceinline__ void chunk_to_f(const typename Chunk<T, V>::raw& r, float (&f)[V]) {
+  if constexpr (V == 1) {
+    f[0] = to_float(r);
+  } else if constexpr (sizeof(T) == 2) {
+    f[0] = __uint_as_float(r[0] << 16);
+    f[1] = __uint_as_float(r[0] & 0xffff0000u);
+    f[2] = __uint_as_float(r[1] << 16);
+    f[3] = __uint_as_float(r[1] & 0xffff0000u);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f[i] = __uint_as_float(r[i]);
+  }
+}
+template <typename T, int V>
+__device__ __forceinline__ typename Chunk<T, V>::raw f_to_chunk(const float (&f)[V]) {
+  typename Chunk<T, V>::raw r;
+  if constexpr (V == 1) {
+    r = from_float<T>(f[0]);
+  } else if constexpr (sizeof(T) == 2) {
+    r[0] = f32x2_to_bf16x2(f[0], f[1]);
+    r[1] = f32x2_to_bf16x2(f[2], f[3]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = __float_as_uint(f[i]);
+  }
+  return r;
+}
+
+template <typename T, int K, int V>
 __global__ __launch_bounds__(kThreads) void conv1d_fwd(const T* __restrict__ x,
                                                        const float* __restrict__ w,
                                                        const float* __restrict__ bias,
                                                        const T* __restrict__ init, T* __restrict__ out,
                                                        int b_, int T_, int C, int nruns, int act) {
-  constexpr int V = VECP ? Vec<T>::n : 1;
+  typedef typename Chunk<T, V>::raw raw_t;
   const int nv = C / V;
   const long total = long(b_) * nruns * nv;
   const long gid = long(blockIdx.x) * kThreads + threadIdx.x;
@@ -171,36 +207,35 @@ __global__ __launch_bounds__(kThreads) void conv1d_fwd(const T* __restrict__ x,
 #pragma unroll
   for (int i = 0; i < V; ++i) {
     bv[i] = bias ? bias[c0 + i] : 0.f;
+    if constexpr (K == 4) {            // one 16-byte load per channel (weight rows are 16-byte aligned)
+      const f32x4 wv = *reinterpret_cast<const f32x4*>(w + size_t(c0 + i) * 4);
 #pragma unroll
-    for (int k = 0; k < K; ++k) wk[k][i] = w[size_t(c0 + i) * K + k];
-  }
-  auto load = [&](const T* p, float (&f)[V]) {
-    if constexpr (VECP) {
-      unpack<T>(*reinterpret_cast<const u32x4_t*>(p), f);
+      for (int k = 0; k < 4; ++k) wk[k][i] = wv[k];
     } else {
-      f[0] = to_float(*p);
+#pragma unroll
+      for (int k = 0; k < K; ++k) wk[k][i] = w[size_t(c0 + i) * K + k];
     }
-  };
+  }
   const int t0 = run * kConvTok;
   const T* xb = x + size_t(b) * T_ * C + c0;
   T* ob = out + size_t(b) * T_ * C + c0;
+  auto ld = [&](const T* p) { return *reinterpret_cast<const raw_t*>(p); };
   // win[k] holds token t - (K-1) + k for the next output t
   float win[K][V];
 #pragma unroll
   for (int k = 0; k < K - 1; ++k) {
     const int t = t0 - (K - 1) + k;
     if (t >= 0) {
-      load(xb + size_t(t) * C, win[k]);
+      chunk_to_f<T, V>(ld(xb + size_t(t) * C), win[k]);
     } else if (init) {
-      load(init + (size_t(b) * (K - 1) + (t + K - 1)) * C + c0, win[k]);
+      chunk_to_f<T, V>(ld(init + (size_t(b) * (K - 1) + (t + K - 1)) * C + c0), win[k]);
     } else {
 #pragma unroll
       for (int i = 0; i < V; ++i) win[k][i] = 0.f;
     }
   }
-  const int tend = min(t0 + kConvTok, T_);
-  for (int t = t0; t < tend; ++t) {
-    load(xb + size_t(t) * C, win[K - 1]);
+  // one output token from the window (win[K-1] just filled), then slide
+  auto step = [&](int t) {
     float o[V];
 #pragma unroll
     for (int i = 0; i < V; ++i) {
@@ -209,15 +244,26 @@ __global__ __launch_bounds__(kThreads) void conv1d_fwd(const T* __restrict__ x,
       for (int k = 0; k < K; ++k) a += wk[k][i] * win[k][i];
       o[i] = act ? silu_f(a) : a;
     }
-    if constexpr (VECP) {
-      *reinterpret_cast<u32x4_t*>(ob + size_t(t) * C) = pack<T>(o);
-    } else {
-      ob[size_t(t) * C] = from_float<T>(o[0]);
-    }
+    *reinterpret_cast<raw_t*>(ob + size_t(t) * C) = f_to_chunk<T, V>(o);
 #pragma unroll
     for (int k = 0; k < K - 1; ++k)
 #pragma unroll
       for (int i = 0; i < V; ++i) win[k][i] = win[k + 1][i];
+  };
+  if (t0 + kConvTok <= T_) {
+    raw_t r[kConvTok];
+#pragma unroll
+    for (int j = 0; j < kConvTok; ++j) r[j] = ld(xb + size_t(t0 + j) * C);
+#pragma unroll
+    for (int j = 0; j < kConvTok; ++j) {
+      chunk_to_f<T, V>(r[j], win[K - 1]);
+      step(t0 + j);
+    }
+  } else {
+    for (int t = t0; t < T_; ++t) {
+      chunk_to_f<T, V>(ld(xb + size_t(t) * C), win[K - 1]);
+      step(t);
+    }
   }
 }
 
@@ -241,7 +287,9 @@ __global__ __launch_bounds__(kThreads) void conv1d_final(const T* __restrict__ x
   for (int k = 0; k < K - 1; ++k) fin[(size_t(b) * (K - 1) + k) * C + c] = col[k];
 }
 
-// one token, recurrent form: thread per (batch, channel), state column in place
+// one token, recurrent form: thread per (batch, channel), state column in
+// place (measured faster than 4-channel vectors per thread: more threads in
+// flight for this short stream)
 template <typename T, int K>
 __global__ __launch_bounds__(kThreads) void conv1d_update(T* state, const T* __restrict__ x,
                                                           const float* __restrict__ w,
@@ -301,15 +349,15 @@ template <typename T, int K>
 hipError_t conv_k(const void* x, const float* w, const float* bias, const void* init, void* out, void* fin,
                   int b, int T_, int C, int act, hipStream_t st) {
   const int nruns = (T_ + kConvTok - 1) / kConvTok;
-  const bool vec = C % Vec<T>::n == 0;
-  const long total = long(b) * nruns * (vec ? C / Vec<T>::n : C);
+  const bool vec = C % 4 == 0;
+  const long total = long(b) * nruns * (vec ? C / 4 : C);
   const long blocks = (total + kThreads - 1) / kThreads;
   if (vec)
-    hipLaunchKernelGGL((conv1d_fwd<T, K, true>), dim3(unsigned(blocks)), dim3(kThreads), 0, st,
+    hipLaunchKernelGGL((conv1d_fwd<T, K, 4>), dim3(unsigned(blocks)), dim3(kThreads), 0, st,
                        static_cast<const T*>(x), w, bias, static_cast<const T*>(init), static_cast<T*>(out),
                        b, T_, C, nruns, act);
   else
-    hipLaunchKernelGGL((conv1d_fwd<T, K, false>), dim3(unsigned(blocks)), dim3(kThreads), 0, st,
+    hipLaunchKernelGGL((conv1d_fwd<T, K, 1>), dim3(unsigned(blocks)), dim3(kThreads), 0, st,
                        static_cast<const T*>(x), w, bias, static_cast<const T*>(init), static_cast<T*>(out),
                        b, T_, C, nruns, act);
   if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;

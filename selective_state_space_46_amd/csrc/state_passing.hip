@@ -31,8 +31,8 @@ constexpr int kTN = 64;     // n columns per tile (16 threads x 4)
 
 __device__ __forceinline__ void store_out(float* S, uint16_t* Hb, size_t idx, const f32x4& v) {
   if (Hb) {
-    const uint32_t lo = uint32_t(f32_to_bf16(v.x)) | (uint32_t(f32_to_bf16(v.y)) << 16);
-    const uint32_t hi = uint32_t(f32_to_bf16(v.z)) | (uint32_t(f32_to_bf16(v.w)) << 16);
+    const uint32_t lo = f32x2_to_bf16x2(v.x, v.y);
+    const uint32_t hi = f32x2_to_bf16x2(v.z, v.w);
     typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
     *reinterpret_cast<u32x2*>(Hb + idx) = u32x2{lo, hi};
   } else {
