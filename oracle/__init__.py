@@ -67,6 +67,8 @@ def _load():
     lib.oracle_ssd_fwd_columns.restype = I
     lib.oracle_ssd_decode.argtypes = [P] * 9 + [I, I, I, I, I, I, I, P, P, I]
     lib.oracle_ssd_decode.restype = I
+    lib.oracle_ssd_fwd_varlen.argtypes = [P] * 7 + [I, P, P, P, L, I, I, I, I, I]
+    lib.oracle_ssd_fwd_varlen.restype = I
     _lib = lib
     return lib
 
@@ -176,6 +178,30 @@ def ssd_state_update(state, x, dt, A, B, C, D=None, nthreads: Optional[int] = No
     ys, st = ssd_decode(state, np.asarray(x)[None], np.asarray(dt)[None], A,
                         np.asarray(B)[None], np.asarray(C)[None], D, nthreads=nthreads)
     return ys[0], st
+
+
+def ssd_fwd_varlen(x, dt, A, B, C, D, cu_seqlens, init=None, nthreads: Optional[int] = None,
+                   want_y: bool = True, want_final: bool = True):
+    """Packed variable-length sequences (one token axis): x [T,H,P], dt [T,H],
+    B/C [T,G,N], cu_seqlens [nseq+1] (0 = cu[0] <= ... <= cu[nseq] = T),
+    init [nseq,H,N,P] or None. The state restarts from init[i] (or zeros) at
+    the first token of sequence i. Returns (y [T,H,P], final [nseq,H,N,P])
+    float64 (None where not wanted)."""
+    x, dt, A, B, C = (_f32(v) for v in (x, dt, A, B, C))
+    D = _f32(D) if D is not None else None
+    cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+    T, H, P = x.shape
+    G, N = B.shape[1], B.shape[2]
+    nseq = cu.shape[0] - 1
+    init = _f64(init) if init is not None else None
+    y = np.empty((T, H, P)) if want_y else None
+    fin = np.empty((nseq, H, N, P)) if want_final else None
+    r = _load().oracle_ssd_fwd_varlen(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(cu),
+                                      nseq, _ptr(init), _ptr(y), _ptr(fin), T, H, P, N, G,
+                                      nthreads or default_threads())
+    if r != 0:
+        raise ValueError(f"oracle_ssd_fwd_varlen failed ({r})")
+    return y, fin
 
 
 def rel_l2(got, ref) -> float:

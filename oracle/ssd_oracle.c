@@ -288,3 +288,121 @@ int oracle_ssd_decode(const double *state0, const float *xs, const float *dts,
     free(tasks);
     return r;
 }
+
+
+/*
+ * Packed variable-length sequences: sequence i is tokens cu[i] .. cu[i+1]-1
+ * of one token axis (x [T,H,P], dt [T,H], B/C [T,G,N]). Each sequence starts
+ * from its own state, init[i] (zeros when init is NULL), so nothing of one
+ * sequence reaches the next (youngju.dev "Mamba / selective SSM" page,
+ * section "状態初期化とシーケンス境界": the state is set explicitly at the start
+ * of every sequence so that sequences in one batch do not mix). The
+ * recurrence is the same as above; y [T,H,P], final [nseq,H,N,P] (either may
+ * be NULL). A sequence with no tokens leaves its initial state as its final
+ * state.
+ */
+typedef struct {
+    const float *x, *dt, *A, *B, *C, *D;
+    const double *init;
+    const int *cu;
+    int nseq;
+    long T;
+    int H, P, N, G;
+    double *y, *fin;
+    long ntasks, next;   /* tasks: (h, column block), handed out atomically */
+} vproblem;
+
+static void run_vtask(vproblem *pb, long task_id, double *S)
+{
+    const int H = pb->H, P = pb->P, N = pb->N;
+    const long nblk = (P + PBLK - 1) / PBLK;
+    const int h = (int)(task_id / nblk);
+    const int p0 = (int)(task_id % nblk) * PBLK;
+    const int p1 = p0 + PBLK < P ? p0 + PBLK : P;
+    const int w = p1 - p0;
+    const int g = h / (H / pb->G);
+    const double Ah = (double)pb->A[h];
+    const double Dh = pb->D ? (double)pb->D[h] : 0.0;
+    for (int i = 0; i < pb->nseq; ++i) {
+        for (int n = 0; n < N; ++n)
+            for (int j = 0; j < w; ++j)
+                S[n * w + j] = pb->init ? pb->init[(((long)i * H + h) * N + n) * P + p0 + j] : 0.0;
+        for (long t = pb->cu[i]; t < pb->cu[i + 1]; ++t) {
+            const float *xr = pb->x + (t * H + h) * P + p0;
+            const double dtv = (double)pb->dt[t * H + h];
+            const float *Br = pb->B + (t * pb->G + g) * N;
+            const float *Cr = pb->C + (t * pb->G + g) * N;
+            const double abar = exp(dtv * Ah);
+            for (int n = 0; n < N; ++n) {
+                const double bbar = dtv * (double)Br[n];
+                double *Sn = S + n * w;
+                for (int j = 0; j < w; ++j)
+                    Sn[j] = abar * Sn[j] + bbar * (double)xr[j];
+            }
+            if (pb->y)
+                for (int j = 0; j < w; ++j) {
+                    double acc = 0.0;
+                    for (int n = 0; n < N; ++n)
+                        acc += (double)Cr[n] * S[n * w + j];
+                    pb->y[(t * H + h) * P + p0 + j] = acc + Dh * (double)xr[j];
+                }
+        }
+        if (pb->fin)
+            for (int n = 0; n < N; ++n)
+                for (int j = 0; j < w; ++j)
+                    pb->fin[(((long)i * H + h) * N + n) * P + p0 + j] = S[n * w + j];
+    }
+}
+
+static void *vworker(void *arg)
+{
+    vproblem *pb = (vproblem *)arg;
+    double *S = (double *)malloc(sizeof(double) * (size_t)pb->N * PBLK);
+    if (!S)
+        return (void *)1;
+    for (;;) {
+        long i = __atomic_fetch_add(&pb->next, 1, __ATOMIC_RELAXED);
+        if (i >= pb->ntasks)
+            break;
+        run_vtask(pb, i, S);
+    }
+    free(S);
+    return NULL;
+}
+
+int oracle_ssd_fwd_varlen(const float *x, const float *dt, const float *A, const float *B,
+                          const float *C, const float *D, const int *cu, int nseq,
+                          const double *init, double *y, double *final_state,
+                          long T, int H, int P, int N, int G, int nthreads)
+{
+    if (check_dims(1, T, H, P, N, G) || nseq < 1 || cu[0] != 0 || cu[nseq] != T)
+        return 2;
+    for (int i = 0; i < nseq; ++i)
+        if (cu[i + 1] < cu[i])
+            return 2;
+    vproblem pb = {x, dt, A, B, C, D, init, cu, nseq, T, H, P, N, G, y, final_state,
+                   (long)H * ((P + PBLK - 1) / PBLK), 0};
+    if (nthreads < 1)
+        nthreads = 1;
+    if (nthreads > pb.ntasks)
+        nthreads = (int)pb.ntasks;
+    pthread_t *th = (pthread_t *)malloc(sizeof(pthread_t) * (size_t)nthreads);
+    if (!th)
+        return 1;
+    int err = 0, started = 0;
+    for (int i = 0; i < nthreads; ++i) {
+        if (pthread_create(&th[i], NULL, vworker, &pb) != 0) {
+            err = 1;
+            break;
+        }
+        ++started;
+    }
+    for (int i = 0; i < started; ++i) {
+        void *r = NULL;
+        pthread_join(th[i], &r);
+        if (r)
+            err = 1;
+    }
+    free(th);
+    return err;
+}

@@ -305,3 +305,90 @@ def test_rejects_bad_shapes():
     B2 = np.concatenate([B, B], axis=2)
     with pytest.raises(RuntimeError):
         oracle.ssd_fwd(x, dt, A, B2, B2, D, init)   # H=3 not divisible by G=2
+
+
+# ------------------------------------------------------------ packed variable-length sequences
+
+def _quadratic_form_varlen(x, dt, A, B, C, D, cu, init):
+    """Brute force over one token axis with sequence boundaries cu: the
+    semiseparable M restricted to pairs of tokens in the same sequence, each
+    sequence's initial state entering before its first token."""
+    x, dt, A, B, C = (np.asarray(v, np.float64) for v in (x, dt, A, B, C))
+    T, H, P = x.shape
+    G, N = B.shape[1], B.shape[2]
+    seq = np.zeros(T, dtype=int)
+    for i in range(len(cu) - 1):
+        seq[cu[i]:cu[i + 1]] = i
+    y = np.zeros((T, H, P))
+    fin = np.zeros((len(cu) - 1, H, N, P))
+    for h in range(H):
+        g = h // (H // G)
+        a = dt[:, h] * A[h]
+        for i in range(T):
+            s0 = cu[seq[i]]
+            for j in range(s0, i + 1):
+                decay = math.exp(sum(a[k] for k in range(j + 1, i + 1)))
+                y[i, h] += float(C[i, g] @ B[j, g]) * decay * dt[j, h] * x[j, h]
+            if init is not None:
+                y[i, h] += math.exp(sum(a[k] for k in range(s0, i + 1))) * (C[i, g] @ init[seq[i], h])
+            if D is not None:
+                y[i, h] += float(D[h]) * x[i, h]
+        for q in range(len(cu) - 1):
+            for j in range(cu[q], cu[q + 1]):
+                decay = math.exp(sum(a[k] for k in range(j + 1, cu[q + 1])))
+                fin[q, h] += decay * dt[j, h] * np.outer(B[j, g], x[j, h])
+            if init is not None:
+                fin[q, h] += math.exp(sum(a[k] for k in range(cu[q], cu[q + 1]))) * init[q, h]
+    return y, fin
+
+
+@pytest.mark.parametrize("cu", [[0, 9], [0, 3, 9], [0, 1, 5, 5, 12], [0, 0, 4, 11, 12]])
+def test_varlen_quadratic_form(cu):
+    rng = np.random.default_rng(400 + sum(cu))
+    T, H, P, N, G = cu[-1], 2, 3, 4, 1
+    x, dt, A, B, C, D, _ = (v[0] if isinstance(v, np.ndarray) and v.ndim > 1 else v
+                            for v in _rand_problem(rng, 1, T, H, P, N, G))
+    init = rng.standard_normal((len(cu) - 1, H, N, P))
+    y, fin = oracle.ssd_fwd_varlen(x, dt, A, B, C, D, cu, init)
+    y_ref, fin_ref = _quadratic_form_varlen(x, dt, A, B, C, D, cu, init)
+    _close(y, y_ref)
+    _close(fin, fin_ref)
+
+
+def test_varlen_matches_independent_sequences_and_single_sequence():
+    rng = np.random.default_rng(410)
+    cu = [0, 7, 7, 20, 41]
+    T, H, P, N, G = cu[-1], 4, 5, 3, 2
+    x, dt, A, B, C, D, _ = _rand_problem(rng, 1, T, H, P, N, G)
+    x, dt, B, C = x[0], dt[0], B[0], C[0]
+    init = rng.standard_normal((len(cu) - 1, H, N, P))
+    y, fin = oracle.ssd_fwd_varlen(x, dt, A, B, C, D, cu, init)
+    for i in range(len(cu) - 1):
+        s, e = cu[i], cu[i + 1]
+        if e > s:   # each sequence run alone from its own initial state
+            yi, fi = oracle.ssd_fwd(x[None, s:e], dt[None, s:e], A, B[None, s:e], C[None, s:e], D,
+                                    init[i:i + 1])
+            np.testing.assert_array_equal(y[s:e], yi[0])
+            np.testing.assert_array_equal(fin[i], fi[0])
+        else:       # an empty sequence keeps its initial state
+            np.testing.assert_array_equal(fin[i], init[i])
+    # what precedes a sequence does not matter: change everything before sequence 3
+    x2, dt2 = x.copy(), dt.copy()
+    x2[:20] = rng.standard_normal((20, H, P)).astype(np.float32)
+    dt2[:20] *= np.float32(0.5)
+    y2, fin2 = oracle.ssd_fwd_varlen(x2, dt2, A, B, C, D, cu, init)
+    np.testing.assert_array_equal(y2[20:], y[20:])
+    np.testing.assert_array_equal(fin2[3], fin[3])
+    # one sequence is the plain forward
+    y1, f1 = oracle.ssd_fwd_varlen(x, dt, A, B, C, D, [0, T], init[:1])
+    yr, fr = oracle.ssd_fwd(x[None], dt[None], A, B[None], C[None], D, init[:1])
+    np.testing.assert_array_equal(y1, yr[0])
+    np.testing.assert_array_equal(f1, fr)
+
+
+def test_varlen_rejects_bad_offsets():
+    rng = np.random.default_rng(420)
+    x, dt, A, B, C, D, _ = _rand_problem(rng, 1, 6, 2, 2, 2, 1)
+    for cu in ([0, 3], [1, 6], [0, 4, 3, 6]):
+        with pytest.raises(ValueError):
+            oracle.ssd_fwd_varlen(x[0], dt[0], A, B[0], C[0], D, cu)
