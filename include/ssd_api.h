@@ -168,6 +168,44 @@ SSD_API ssd_status ssd_state_update(float *state, const void *x, const void *dt,
                             ssd_dtype dtype, void *stream);
 
 /* Static, NUL-terminated description of a status code. */
+/*
+ * Packed variable-length sequences. nseq sequences are packed along one token
+ * axis of total_tokens tokens: sequence i is tokens cu_seqlens[i] ..
+ * cu_seqlens[i+1] - 1, and each starts from its own initial state, so
+ * nothing of one sequence reaches another (youngju.dev "Mamba / selective
+ * SSM" page, section "状態初期化とシーケンス境界": the state is set explicitly
+ * at the start of every sequence of a batch). The result for sequence i is
+ * ssd_chunk_scan_fwd on its tokens alone from init_states[i]:
+ *   x, y   [total_tokens, nheads, headdim]        dtype
+ *   dt     [total_tokens, nheads]                 dtype
+ *   B, C   [total_tokens, ngroups, dstate]        dtype
+ *   cu_seqlens   [nseq + 1] int32 DEVICE array, 0 = cu[0] <= cu[1] <= ...
+ *                <= cu[nseq] = total_tokens (empty sequences allowed). It is
+ *                not read on the host: offsets outside [0, total_tokens] or
+ *                decreasing ones are clamped on the device, which keeps every
+ *                access in bounds but gives unspecified results.
+ *   init_states  [nseq, nheads, dstate, headdim] fp32 or NULL (= zeros)
+ *   final_states [nseq, nheads, dstate, headdim] fp32 or NULL; may be the
+ *                init_states buffer itself. An empty sequence's final state
+ *                is its initial state.
+ * Chunks never straddle two sequences: sequence i takes ceil(len_i /
+ * chunk_len) chunks, the last one partly filled. Only the bf16 matrix-core
+ * configuration is supported (dtype SSD_BF16, dstate in {32, 64, 128, 256},
+ * headdim in {32, 64, 128}, chunk_len >= 32); others return SSD_ERR_SHAPE, as
+ * does nseq outside 1 .. 65535. Other errors as for ssd_chunk_scan_fwd
+ * (cu_seqlens must be 4-byte aligned). The workspace size comes from
+ * ssd_chunk_scan_fwd_varlen_workspace (0 when the sizes are not supported).
+ */
+SSD_API size_t ssd_chunk_scan_fwd_varlen_workspace(int total_tokens, int nseq, int nheads, int headdim,
+                                                   int dstate, int ngroups, int chunk_len,
+                                                   ssd_dtype dtype);
+SSD_API ssd_status ssd_chunk_scan_fwd_varlen(const void *x, const void *dt, const float *A, const void *B,
+                                             const void *C, const float *D, const int *cu_seqlens,
+                                             const float *init_states, void *y, float *final_states,
+                                             int total_tokens, int nseq, int nheads, int headdim,
+                                             int dstate, int ngroups, int chunk_len, ssd_dtype dtype,
+                                             void *workspace, size_t workspace_bytes, void *stream);
+
 SSD_API const char *ssd_status_string(ssd_status status);
 
 #ifdef __cplusplus

@@ -12,6 +12,8 @@ Entry points (same names as the C ABI):
     ssd_chunk_scan_fwd(x, dt, A, B, C, D, init_state, chunk_len) -> (y, final_state)
     ssd_state_update(state, x, dt, A, B, C, D) -> y     (state updated in place)
     ssd_status_string(code) -> str
+    ssd_chunk_scan_fwd_varlen(x, dt, A, B, C, D, cu_seqlens, init_states, chunk_len)
+        -> (y, final_states)                          (packed variable-length sequences)
 and, from ``include/ssd_epilogue.h``, the element-wise stages next to the core:
     ssd_gated_rmsnorm(y, z, weight, group, eps) -> out
     ssd_causal_conv1d_fwd(x, weight, bias, init_state, activation) -> (out, final_state)
@@ -26,7 +28,8 @@ from typing import Optional, Tuple
 __all__ = [
     "SSD_F32", "SSD_BF16", "SSDError", "lib", "lib_path",
     "ssd_chunk_scan_fwd_workspace", "ssd_chunk_scan_fwd", "ssd_chunk_scan_fwd_timed",
-    "ssd_state_update", "ssd_status_string", "ssd_gated_rmsnorm", "ssd_causal_conv1d_fwd",
+    "ssd_state_update", "ssd_status_string", "ssd_chunk_scan_fwd_varlen",
+    "ssd_chunk_scan_fwd_varlen_workspace", "ssd_gated_rmsnorm", "ssd_causal_conv1d_fwd",
     "ssd_causal_conv1d_update",
 ]
 
@@ -76,6 +79,10 @@ def lib() -> ctypes.CDLL:
     L.ssd_status_string.argtypes = [i32]
     L.ssd_status_string.restype = ctypes.c_char_p
     i64, f32 = ctypes.c_long, ctypes.c_float
+    L.ssd_chunk_scan_fwd_varlen_workspace.argtypes = [i32] * 8
+    L.ssd_chunk_scan_fwd_varlen_workspace.restype = sz
+    L.ssd_chunk_scan_fwd_varlen.argtypes = [vp] * 10 + [i32] * 8 + [vp, sz, vp]
+    L.ssd_chunk_scan_fwd_varlen.restype = i32
     L.ssd_gated_rmsnorm.argtypes = [vp] * 4 + [i64, i32, i32, f32, i32, vp]
     L.ssd_gated_rmsnorm.restype = i32
     L.ssd_causal_conv1d_fwd.argtypes = [vp] * 6 + [i32] * 5 + [i32, vp]
@@ -330,3 +337,59 @@ def ssd_causal_conv1d_update(state, x, weight, bias=None, activation="silu", *, 
     if r != 0:
         raise SSDError(r, "ssd_causal_conv1d_update")
     return out
+
+
+# --------------------------------------------------------------------------
+# packed variable-length sequences
+# --------------------------------------------------------------------------
+
+def ssd_chunk_scan_fwd_varlen_workspace(total_tokens: int, nseq: int, nheads: int, headdim: int, dstate: int,
+                                        ngroups: int, chunk_len: int, dtype: int) -> int:
+    return int(lib().ssd_chunk_scan_fwd_varlen_workspace(total_tokens, nseq, nheads, headdim, dstate, ngroups,
+                                                         chunk_len, dtype))
+
+
+def ssd_chunk_scan_fwd_varlen(x, dt, A, B, C, D, cu_seqlens, init_states=None, chunk_len: int = 256, *,
+                              y=None, final_states=None, return_final_states: bool = True, workspace=None,
+                              stream=None):
+    """Packed sequences: x [T,H,P], dt [T,H], B/C [T,G,N] (bf16), A/D [H] fp32,
+    cu_seqlens [nseq+1] int32 on the device, init_states [nseq,H,N,P] fp32 or
+    None. Returns (y [T,H,P], final_states [nseq,H,N,P] or None)."""
+    import torch
+    dev = x.device
+    x = _dev(x, dev, "x")
+    dt, A, B, C = (_dev(v, dev, n) for v, n in ((dt, "dt"), (A, "A"), (B, "B"), (C, "C")))
+    D = _dev(D, dev, "D")
+    cu = _dev(cu_seqlens, dev, "cu_seqlens")
+    if cu.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
+    init_states = _dev(init_states, dev, "init_states")
+    code = _dtype_code(x)
+    for v, n in ((dt, "dt"), (B, "B"), (C, "C")):
+        _same(v, x.dtype, n)
+    for v, n in ((A, "A"), (D, "D"), (init_states, "init_states")):
+        _same(v, torch.float32, n)
+    T, H, P = x.shape
+    G, N = B.shape[1], B.shape[2]
+    nseq = cu.numel() - 1
+    if tuple(dt.shape) != (T, H) or tuple(B.shape) != (T, G, N) or tuple(C.shape) != (T, G, N):
+        raise ValueError("shape mismatch among x, dt, B, C")
+    if init_states is not None and tuple(init_states.shape) != (nseq, H, N, P):
+        raise ValueError("init_states must be [nseq,H,N,P]")
+    y = torch.empty_like(x) if y is None else _inout(y, dev, "y")
+    if final_states is None and return_final_states:
+        final_states = torch.empty((nseq, H, N, P), dtype=torch.float32, device=dev)
+    elif final_states is not None:
+        final_states = _inout(final_states, dev, "final_states")
+    need = ssd_chunk_scan_fwd_varlen_workspace(T, nseq, H, P, N, G, chunk_len, code)
+    if need == 0:
+        raise SSDError(2, "ssd_chunk_scan_fwd_varlen_workspace")
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    r = lib().ssd_chunk_scan_fwd_varlen(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(cu),
+                                        _ptr(init_states), _ptr(y), _ptr(final_states), T, nseq, H, P, N, G,
+                                        chunk_len, code, _ptr(workspace),
+                                        workspace.numel() * workspace.element_size(), _stream(dev, stream))
+    if r != 0:
+        raise SSDError(r, "ssd_chunk_scan_fwd_varlen")
+    return y, final_states

@@ -84,7 +84,7 @@ hipError_t launch_chunk_scan(const FwdShape& s, ssd_dtype type, bool mfma, const
                              const void* B, const void* C, const float* Acs, const float* dtq,
                              const float* Hst, const uint16_t* Hb, const uint16_t* CB,
                              const float* D, void* y, hipStream_t st, const StageEv& ev) {
-  if (mfma) return launch_chunk_scan_mfma(s, x, CB, C, Acs, dtq, Hb, D, y, st, ev);
+  if (mfma) return launch_chunk_scan_mfma(s, x, CB, C, Acs, dtq, Hb, D, y, nullptr, st, ev);
   dim3 grid(s.H * (s.Q / kRows), s.nc, s.b);
   if (type == SSD_BF16)
     hipExtLaunchKernelGGL(chunk_scan_generic<uint16_t>, grid, dim3(kThreads), 0, st, ev.start, ev.stop, 0,

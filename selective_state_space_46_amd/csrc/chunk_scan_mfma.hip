@@ -54,8 +54,8 @@ template <int N, int P, bool HLDS>
 __global__ __launch_bounds__(kThreads) void chunk_scan_mfma_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ CB, const uint16_t* __restrict__ Cm,
     const float* __restrict__ Acs, const float* __restrict__ dtq, const uint16_t* __restrict__ Hb,
-    const float* __restrict__ D, uint16_t* __restrict__ y, int T, int H, int G, int Q, int nc,
-    int nsc) {
+    const float* __restrict__ D, uint16_t* __restrict__ y, const int4* __restrict__ tab, int T, int H,
+    int G, int Q, int nc, int nsc) {
   constexpr int kHS = N + 8;  // H^T row stride (bf16): 16-byte reads of 16 lanes hit distinct banks
   constexpr int RBX = P / 8;  // 16-byte chunks per X' row
   constexpr int HROWS = HLDS ? P : 1;
@@ -73,12 +73,23 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_mfma_kernel(
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = wave_id();  // wave-uniform (scalar register)
   const int l32 = lane & 31, g2 = lane >> 5;
-  const int t0 = sc * kSC;
   const int cps = kSC / Q;        // chunks per super-chunk
   const int c0 = sc * cps;        // first chunk of the super-chunk
   const int lpc = Q / 32;         // 32-row blocks per chunk
   const int ntile = lpc * (lpc + 1) / 2;
-  const bool full = t0 + kSC <= T;     // no token of this super-chunk is past the end
+  // token rows of the super-chunk's chunks (ci = 0 .. cps-1); n = 0 past the last chunk
+  auto crows = [&](int ci) {
+    return c0 + ci < nc ? chunk_rows(tab, b, c0 + ci, T, Q) : ChunkRows{0, 0};
+  };
+  const ChunkRows rows0 = crows(0);
+  if (rows0.n <= 0) return;            // unused slot of a chunk table: uniform, before any barrier
+  // fast: every row of the super-chunk is a valid token and the rows are
+  // consecutive token rows (always so for equal-length batch rows)
+  bool fast = true;
+  for (int ci = 0; ci < cps; ++ci) {
+    const ChunkRows r = crows(ci);
+    fast = fast && r.n == Q && r.r0 == rows0.r0 + long(ci) * Q;
+  }
 
   // C B^T tiles of 32-row block i: tile jj (column block jfirst + jj) of the
   // block's row of its chunk's lower triangle, this lane's 32 bytes
@@ -97,18 +108,20 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_mfma_kernel(
     td[1] = ts[ir * 128 + 1];
     tn[0] = ts[0];
     tn[1] = ts[1];
-    const uint16_t* cr = Cm + ((size_t(b) * T + min(t0 + 32 * i + l32, T - 1)) * G + g) * N + 8 * g2;
+    const ChunkRows r = crows(i / lpc);
+    const long row = r.r0 + min((i % lpc) * 32 + l32, r.n - 1);
+    const uint16_t* cr = Cm + (row * G + g) * size_t(N) + 8 * g2;
 #pragma unroll
     for (int ks = 0; ks < N / 16; ++ks) cfv[ks] = load16(cr + 16 * ks);
   };
   u32x4 pre_tdiag[2], pre_tnext[2], pre_cf[N / 16];
-  if (t0 + 32 * wave < T) issue_block_loads(wave, pre_tdiag, pre_tnext, pre_cf);
+  if ((wave % lpc) * 32 < crows(wave / lpc).n) issue_block_loads(wave, pre_tdiag, pre_tnext, pre_cf);
 
   // ---- staging 1: Acs, the per-token factor, H_c^T
   for (int i = tid; i < kSC; i += kThreads) {
     const int c = c0 + i / Q;
     float a = 0.f, f = 0.f, d = 0.f;
-    if (c < nc) {
+    if (crows(i / Q).n > 0) {
       const size_t row = ((size_t(b) * H + h) * nc + c) * Q;
       const int q = i % Q;
       a = Acs[row + q] * kLog2e;
@@ -139,8 +152,8 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_mfma_kernel(
     constexpr int kStep = kThreads / RBX;
     const int r0 = tid / RBX, cc = tid % RBX;
     uint16_t* dst = &sX[lds_off<RBX, true>(r0, 8 * cc)];
-    if (full) {
-      const uint16_t* src = x + ((size_t(b) * T + t0 + r0) * H + h) * P + 8 * cc;
+    if (fast) {
+      const uint16_t* src = x + ((rows0.r0 + r0) * H + h) * size_t(P) + 8 * cc;
       const size_t step = size_t(kStep) * H * P;
 #pragma unroll
       for (int k = 0; k < RBX; ++k)
@@ -149,8 +162,13 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_mfma_kernel(
 #pragma unroll
       for (int k = 0; k < RBX; ++k) {
         const int r = r0 + k * kStep;
-        const u32x4 v = load16(x + ((size_t(b) * T + min(t0 + r, T - 1)) * H + h) * P + 8 * cc);
-        *reinterpret_cast<u32x4*>(dst + k * kStep * P) = keep_or_zero(t0 + r < T, v);
+        const ChunkRows cr = crows(r / Q);
+        const int rq = r % Q;
+        // a chunk with no valid rows (past the last chunk, or an unused table
+        // slot) reads the super-chunk's first row instead: any in-bounds row
+        const long row = cr.n > 0 ? cr.r0 + min(rq, cr.n - 1) : rows0.r0;
+        const u32x4 v = load16(x + (row * H + h) * size_t(P) + 8 * cc);
+        *reinterpret_cast<u32x4*>(dst + k * kStep * P) = keep_or_zero(rq < cr.n, v);
       }
     }
   }
@@ -173,13 +191,15 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_mfma_kernel(
   const float Dh = D ? D[h] : 0.f;
   for (int which = 0; which < 2; ++which) {
     const int i = which ? 7 - wave : wave;  // 32-row block of the super-chunk
-    const int tl0 = t0 + 32 * i;
-    if (tl0 >= T) continue;                 // wave-uniform: nothing to produce
+    const ChunkRows cr = crows(i / lpc);
+    const int rq0 = (i % lpc) * 32;         // first row of the block inside its chunk
+    if (rq0 >= cr.n) continue;              // wave-uniform: nothing to produce
     const int jfirst = (i / lpc) * lpc;     // first column block of the same chunk
     const int cg = c0 + i / lpc;            // global chunk index (< nc)
     const int lcol = 32 * i + l32;          // this lane's output token in the super-chunk
     const int irel = i - jfirst;            // tiles of this block: jj = 0 .. irel
-    const int t = tl0 + l32;
+    const bool tok_ok = rq0 + l32 < cr.n;   // this lane's token is a valid one
+    const long trow = cr.r0 + rq0 + l32;    // and its token row
     const u32x4* tsrc = tile_src(i);
     auto load_tile = [&](int jj, u32x4 (&tt)[2]) {
       tt[0] = tsrc[jj * 128];
@@ -196,9 +216,9 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_mfma_kernel(
     } else {
       issue_block_loads(i, tdiag, tnext, cf);
     }
-    if (!full) {
+    if (!fast) {
 #pragma unroll
-      for (int ks = 0; ks < N / 16; ++ks) cf[ks] = keep_or_zero(t < T, cf[ks]);
+      for (int ks = 0; ks < N / 16; ++ks) cf[ks] = keep_or_zero(tok_ok, cf[ks]);
     }
 
     // ---- y^T = H_c^T C_l^T, then * exp(Acs_l)
@@ -278,14 +298,14 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_mfma_kernel(
     apply(irel, tdiag, true);
 
     // ---- epilogue: + D x (x re-read, from L2), round, store 4 consecutive p (8 bytes) per run
-    if (t < T) {
+    if (tok_ok) {
       u32x2 xr[P / 32][4];
 #pragma unroll
       for (int pb = 0; pb < P / 32; ++pb)
 #pragma unroll
         for (int q = 0; q < 4; ++q)
           xr[pb][q] = *reinterpret_cast<const u32x2*>(&sX[lds_off<RBX, true>(lcol, 32 * pb + 8 * q + 4 * g2)]);
-      uint16_t* yr = y + ((size_t(b) * T + t) * H + h) * P + 4 * g2;
+      uint16_t* yr = y + (trow * H + h) * size_t(P) + 4 * g2;
 #pragma unroll
       for (int pb = 0; pb < P / 32; ++pb) {
 #pragma unroll
@@ -306,28 +326,31 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_mfma_kernel(
 template <int N, int P>
 hipError_t launch_np(const FwdShape& s, const void* x, const uint16_t* CB, const void* C,
                      const float* Acs, const float* dtq, const uint16_t* Hb, const float* D, void* y,
-                     hipStream_t st, const StageEv& ev) {
-  const int nsc = (s.T + kSC - 1) / kSC;
+                     const int4* tab, hipStream_t st, const StageEv& ev) {
+  const int cps = kSC / s.Q;
+  const int nsc = (s.nc + cps - 1) / cps;   // = ceil(T / 256) for equal-length rows
   const long blocks = long(s.b) * nsc * s.H;
   if (s.Q == kSC)  // one chunk per super-chunk: its H_c^T is staged in LDS
     hipExtLaunchKernelGGL((chunk_scan_mfma_kernel<N, P, true>), dim3(unsigned(blocks)), dim3(kThreads), 0,
-                       st, ev.start, ev.stop, 0, static_cast<const uint16_t*>(x), CB, static_cast<const uint16_t*>(C), Acs,
-                       dtq, Hb, D, static_cast<uint16_t*>(y), s.T, s.H, s.G, s.Q, s.nc, nsc);
+                          st, ev.start, ev.stop, 0, static_cast<const uint16_t*>(x), CB,
+                          static_cast<const uint16_t*>(C), Acs, dtq, Hb, D, static_cast<uint16_t*>(y), tab,
+                          s.T, s.H, s.G, s.Q, s.nc, nsc);
   else
-    hipExtLaunchKernelGGL((chunk_scan_mfma_kernel<N, P, false>), dim3(unsigned(blocks)), dim3(kThreads),
-                          0, st, ev.start, ev.stop, 0, static_cast<const uint16_t*>(x), CB, static_cast<const uint16_t*>(C), Acs,
-                       dtq, Hb, D, static_cast<uint16_t*>(y), s.T, s.H, s.G, s.Q, s.nc, nsc);
+    hipExtLaunchKernelGGL((chunk_scan_mfma_kernel<N, P, false>), dim3(unsigned(blocks)), dim3(kThreads), 0,
+                          st, ev.start, ev.stop, 0, static_cast<const uint16_t*>(x), CB,
+                          static_cast<const uint16_t*>(C), Acs, dtq, Hb, D, static_cast<uint16_t*>(y), tab,
+                          s.T, s.H, s.G, s.Q, s.nc, nsc);
   return hipGetLastError();
 }
 
 template <int N>
 hipError_t launch_n(const FwdShape& s, const void* x, const uint16_t* CB, const void* C,
                     const float* Acs, const float* dtq, const uint16_t* Hb, const float* D, void* y,
-                    hipStream_t st, const StageEv& ev) {
+                    const int4* tab, hipStream_t st, const StageEv& ev) {
   switch (s.P) {
-    case 32: return launch_np<N, 32>(s, x, CB, C, Acs, dtq, Hb, D, y, st, ev);
-    case 64: return launch_np<N, 64>(s, x, CB, C, Acs, dtq, Hb, D, y, st, ev);
-    case 128: return launch_np<N, 128>(s, x, CB, C, Acs, dtq, Hb, D, y, st, ev);
+    case 32: return launch_np<N, 32>(s, x, CB, C, Acs, dtq, Hb, D, y, tab, st, ev);
+    case 64: return launch_np<N, 64>(s, x, CB, C, Acs, dtq, Hb, D, y, tab, st, ev);
+    case 128: return launch_np<N, 128>(s, x, CB, C, Acs, dtq, Hb, D, y, tab, st, ev);
   }
   return hipErrorInvalidValue;
 }
@@ -336,12 +359,13 @@ hipError_t launch_n(const FwdShape& s, const void* x, const uint16_t* CB, const 
 
 hipError_t launch_chunk_scan_mfma(const FwdShape& s, const void* x, const uint16_t* CB,
                                   const void* C, const float* Acs, const float* dtq,
-                                  const uint16_t* Hb, const float* D, void* y, hipStream_t st, const StageEv& ev) {
+                                  const uint16_t* Hb, const float* D, void* y, const int4* tab,
+                                  hipStream_t st, const StageEv& ev) {
   switch (s.N) {
-    case 32: return launch_n<32>(s, x, CB, C, Acs, dtq, Hb, D, y, st, ev);
-    case 64: return launch_n<64>(s, x, CB, C, Acs, dtq, Hb, D, y, st, ev);
-    case 128: return launch_n<128>(s, x, CB, C, Acs, dtq, Hb, D, y, st, ev);
-    case 256: return launch_n<256>(s, x, CB, C, Acs, dtq, Hb, D, y, st, ev);
+    case 32: return launch_n<32>(s, x, CB, C, Acs, dtq, Hb, D, y, tab, st, ev);
+    case 64: return launch_n<64>(s, x, CB, C, Acs, dtq, Hb, D, y, tab, st, ev);
+    case 128: return launch_n<128>(s, x, CB, C, Acs, dtq, Hb, D, y, tab, st, ev);
+    case 256: return launch_n<256>(s, x, CB, C, Acs, dtq, Hb, D, y, tab, st, ev);
   }
   return hipErrorInvalidValue;
 }

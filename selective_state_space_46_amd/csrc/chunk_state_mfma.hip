@@ -56,8 +56,8 @@ constexpr int kMaxQ = 256;
 template <int N>
 __device__ __forceinline__ void chunk_scores_tile(const uint16_t* __restrict__ Bm,
                                                   const uint16_t* __restrict__ Cm,
-                                                  uint16_t* __restrict__ CB, int T, int G, int Q, int nc,
-                                                  long wid, int lane) {
+                                                  uint16_t* __restrict__ CB, const int4* __restrict__ tab,
+                                                  int T, int G, int Q, int nc, long wid, int lane) {
   const int lpc = Q / 32;
   const int ntile = lpc * (lpc + 1) / 2;
   const int l32 = lane & 31, g2 = lane >> 5;
@@ -69,12 +69,12 @@ __device__ __forceinline__ void chunk_scores_tile(const uint16_t* __restrict__ B
   int i = 0;                                    // tile ti = i (i + 1) / 2 + j, j <= i
   while ((i + 1) * (i + 2) / 2 <= ti) ++i;
   const int j = ti - i * (i + 1) / 2;
-  const int tc0 = c * Q;                        // first token of the chunk
-  if (tc0 + 32 * i >= T) return;                // row block past the end: never read
+  const ChunkRows cr0 = chunk_rows(tab, b, c, T, Q);
+  if (32 * i >= cr0.n) return;                  // row block past the valid tokens: never read
 
-  const int tl = tc0 + 32 * i + l32, ts = tc0 + 32 * j + l32;
-  const uint16_t* cr = Cm + ((size_t(b) * T + min(tl, T - 1)) * G + g) * N + 8 * g2;
-  const uint16_t* br = Bm + ((size_t(b) * T + min(ts, T - 1)) * G + g) * N + 8 * g2;
+  const int tl = 32 * i + l32, ts = 32 * j + l32;   // rows inside the chunk
+  const uint16_t* cr = Cm + ((cr0.r0 + min(tl, cr0.n - 1)) * G + g) * size_t(N) + 8 * g2;
+  const uint16_t* br = Bm + ((cr0.r0 + min(ts, cr0.n - 1)) * G + g) * size_t(N) + 8 * g2;
   u32x4 cf[N / 16], bf[N / 16];
 #pragma unroll
   for (int ks = 0; ks < N / 16; ++ks) {
@@ -84,7 +84,7 @@ __device__ __forceinline__ void chunk_scores_tile(const uint16_t* __restrict__ B
   f32x16 acc = zero16();
 #pragma unroll
   for (int ks = 0; ks < N / 16; ++ks)
-    acc = mfma32x32x16(keep_or_zero(ts < T, bf[ks]), keep_or_zero(tl < T, cf[ks]), acc);  // rows s, column l
+    acc = mfma32x32x16(keep_or_zero(ts < cr0.n, bf[ks]), keep_or_zero(tl < cr0.n, cf[ks]), acc);  // rows s, column l
   u32x4 lo, hi;
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
@@ -101,12 +101,12 @@ template <int N, int P>
 __global__ __launch_bounds__(kThreads) void chunk_state_mfma_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ Bm, const uint16_t* __restrict__ dt,
     const float* __restrict__ A, float* __restrict__ Acs, float* __restrict__ dtq, float* __restrict__ S,
-    const uint16_t* __restrict__ Cm, uint16_t* __restrict__ CB, int T, int H, int G, int Q, int nc,
-    int nscore_wg, long ntiles) {
+    const uint16_t* __restrict__ Cm, uint16_t* __restrict__ CB, const int4* __restrict__ tab, int T, int H,
+    int G, int Q, int nc, int nscore_wg, long ntiles) {
   // the first nscore_wg work-groups compute C B^T tiles, one per wave
   if (int(blockIdx.x) < nscore_wg) {
     const long wid = long(blockIdx.x) * kWaves + (threadIdx.x >> 6);
-    if (wid < ntiles) chunk_scores_tile<N>(Bm, Cm, CB, T, G, Q, nc, wid, threadIdx.x & 63);
+    if (wid < ntiles) chunk_scores_tile<N>(Bm, Cm, CB, tab, T, G, Q, nc, wid, threadIdx.x & 63);
     return;                                     // no barrier on this path
   }
   constexpr int RBB = N / 8, RBW = P / 8;            // 16-byte chunks per row
@@ -128,7 +128,8 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma_kernel(
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = wave_id();  // wave-uniform (scalar register)
   const int g2 = lane >> 5;
-  const long t0 = long(c) * Q;
+  const ChunkRows rows = chunk_rows(tab, b, c, T, Q);
+  if (rows.n <= 0) return;                      // unused table slot: uniform, before any barrier
 
   // Acs_s = sum_{k <= s} dt_k A_h inside the chunk (dt = 0 past the end of
   // the sequence): one token per thread, a wave scan, then the totals of the
@@ -138,7 +139,7 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma_kernel(
   {
     const float Ah = A[h];
     float d = 0.f;
-    if (tid < Q && t0 + tid < T) d = bf16_to_f32(dt[(size_t(b) * T + t0 + tid) * H + h]);
+    if (tid < rows.n) d = bf16_to_f32(dt[(rows.r0 + tid) * H + h]);
     float v = d * Ah;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
@@ -166,12 +167,12 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma_kernel(
       const int e = tid + m * kThreads;
       if (e < CB_) {
         const int r = e / RBB, cc = e % RBB;
-        const long t = min(t0 + s0 + r, long(T) - 1);
-        v[m] = load16(Bm + ((size_t(b) * T + t) * G + g) * N + 8 * cc);
+        const long row = rows.r0 + min(s0 + r, rows.n - 1);
+        v[m] = load16(Bm + (row * G + g) * size_t(N) + 8 * cc);
       } else if (e < CB_ + CW) {
         const int r = (e - CB_) / RBW, cc = (e - CB_) % RBW;
-        const long t = min(t0 + s0 + r, long(T) - 1);
-        v[m] = load16(x + ((size_t(b) * T + t) * H + h) * P + 8 * cc);
+        const long row = rows.r0 + min(s0 + r, rows.n - 1);
+        v[m] = load16(x + (row * H + h) * size_t(P) + 8 * cc);
       }
     }
   };
@@ -182,11 +183,11 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma_kernel(
       const int e = tid + m * kThreads;
       if (e < CB_) {
         const int r = e / RBB, cc = e % RBB;
-        const bool in = r < Q - s0 && t0 + s0 + r < T;
+        const bool in = s0 + r < rows.n;           // rows.n <= Q
         *reinterpret_cast<u32x4*>(&sB[lds_off<RBB>(r, 8 * cc)]) = keep_or_zero(in, v[m]);
       } else if (e < CB_ + CW) {
         const int r = (e - CB_) / RBW, cc = (e - CB_) % RBW;
-        const float w = (r < Q - s0 && t0 + s0 + r < T) ? sw[s0 + r] : 0.f;
+        const float w = s0 + r < rows.n ? sw[s0 + r] : 0.f;
         u32x4 o;
 #pragma unroll
         for (int q = 0; q < 4; ++q) o[q] = pack_bf16x2(bf16_lo(v[m][q]) * w, bf16_hi(v[m][q]) * w);
@@ -240,7 +241,8 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma_kernel(
 
 template <int N, int P>
 hipError_t launch_np(const FwdShape& s, const void* x, const void* B, const void* C, const void* dt,
-                     const float* A, float* Acs, float* dtq, float* S, uint16_t* CB, hipStream_t st, const StageEv& ev) {
+                     const float* A, float* Acs, float* dtq, float* S, uint16_t* CB, const int4* tab, hipStream_t st,
+                     const StageEv& ev) {
   const int lpc = s.Q / 32;
   const long ntiles = long(s.b) * s.nc * s.G * (lpc * (lpc + 1) / 2);
   // score work-groups first (they start with the first wave of work-groups),
@@ -250,17 +252,18 @@ hipError_t launch_np(const FwdShape& s, const void* x, const void* B, const void
   hipExtLaunchKernelGGL((chunk_state_mfma_kernel<N, P>), dim3(unsigned(blocks)), dim3(kThreads), 0, st, ev.start, ev.stop, 0,
                      static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(B),
                      static_cast<const uint16_t*>(dt), A, Acs, dtq, S, static_cast<const uint16_t*>(C), CB,
-                     s.T, s.H, s.G, s.Q, s.nc, int(nscore), ntiles);
+                     tab, s.T, s.H, s.G, s.Q, s.nc, int(nscore), ntiles);
   return hipGetLastError();
 }
 
 template <int N>
 hipError_t launch_n(const FwdShape& s, const void* x, const void* B, const void* C, const void* dt,
-                    const float* A, float* Acs, float* dtq, float* S, uint16_t* CB, hipStream_t st, const StageEv& ev) {
+                    const float* A, float* Acs, float* dtq, float* S, uint16_t* CB, const int4* tab, hipStream_t st,
+                     const StageEv& ev) {
   switch (s.P) {
-    case 32: return launch_np<N, 32>(s, x, B, C, dt, A, Acs, dtq, S, CB, st, ev);
-    case 64: return launch_np<N, 64>(s, x, B, C, dt, A, Acs, dtq, S, CB, st, ev);
-    case 128: return launch_np<N, 128>(s, x, B, C, dt, A, Acs, dtq, S, CB, st, ev);
+    case 32: return launch_np<N, 32>(s, x, B, C, dt, A, Acs, dtq, S, CB, tab, st, ev);
+    case 64: return launch_np<N, 64>(s, x, B, C, dt, A, Acs, dtq, S, CB, tab, st, ev);
+    case 128: return launch_np<N, 128>(s, x, B, C, dt, A, Acs, dtq, S, CB, tab, st, ev);
   }
   return hipErrorInvalidValue;
 }
@@ -269,12 +272,13 @@ hipError_t launch_n(const FwdShape& s, const void* x, const void* B, const void*
 
 hipError_t launch_chunk_state_mfma(const FwdShape& s, const void* x, const void* B, const void* C,
                                    const void* dt, const float* A, float* Acs, float* dtq,
-                                   float* S, uint16_t* CB, hipStream_t st, const StageEv& ev) {
+                                   float* S, uint16_t* CB, const int4* tab, hipStream_t st,
+                                   const StageEv& ev) {
   switch (s.N) {
-    case 32: return launch_n<32>(s, x, B, C, dt, A, Acs, dtq, S, CB, st, ev);
-    case 64: return launch_n<64>(s, x, B, C, dt, A, Acs, dtq, S, CB, st, ev);
-    case 128: return launch_n<128>(s, x, B, C, dt, A, Acs, dtq, S, CB, st, ev);
-    case 256: return launch_n<256>(s, x, B, C, dt, A, Acs, dtq, S, CB, st, ev);
+    case 32: return launch_n<32>(s, x, B, C, dt, A, Acs, dtq, S, CB, tab, st, ev);
+    case 64: return launch_n<64>(s, x, B, C, dt, A, Acs, dtq, S, CB, tab, st, ev);
+    case 128: return launch_n<128>(s, x, B, C, dt, A, Acs, dtq, S, CB, tab, st, ev);
+    case 256: return launch_n<256>(s, x, B, C, dt, A, Acs, dtq, S, CB, tab, st, ev);
   }
   return hipErrorInvalidValue;
 }

@@ -72,7 +72,8 @@ bool grids_fit(const FwdShape& s, bool mfma) {
   if (mfma) {
     worst = std::max(worst, 64.0 * double(s.b) * s.nc * s.G * (lpc * (lpc + 1) / 2) + 4096.0 +
                                 512.0 * bch);
-    worst = std::max(worst, 256.0 * bh * ((s.T + 255) / 256));
+    const int cps = 256 / s.Q;
+    worst = std::max(worst, 256.0 * bh * ((s.nc + cps - 1) / cps));
   }
   return worst < lim;
 }
@@ -180,7 +181,7 @@ ssd_status ssd_chunk_scan_fwd_timed(const void* x, const void* dt, const float* 
   } else if (launch_chunk_cumsum(s, dtype, dt, A, Acs, dtq, hs, ev(0)) != hipSuccess) {
     return SSD_ERR_HIP;
   }
-  const hipError_t se = mfma ? launch_chunk_state_mfma(s, x, B, C, dt, A, Acs, dtq, S, CB, hs, ev(1))
+  const hipError_t se = mfma ? launch_chunk_state_mfma(s, x, B, C, dt, A, Acs, dtq, S, CB, nullptr, hs, ev(1))
                              : launch_chunk_state(s, dtype, x, B, Acs, dtq, S, hs, ev(1));
   if (se != hipSuccess) return SSD_ERR_HIP;
   if (launch_state_passing(s, S, Hb, Acs, init_state, final_state, hs, ev(2)) != hipSuccess)
@@ -226,6 +227,97 @@ ssd_status ssd_state_update(float* state, const void* x, const void* dt, const f
   if (overlaps(y, xb, state, stb)) return SSD_ERR_ALIAS;
   if (launch_state_update(dtype, state, x, dt, A, B, C, D, y, batch, nheads, headdim, dstate,
                           ngroups, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return SSD_ERR_HIP;
+  return SSD_OK;
+}
+
+// ---------------------------------------------------------------------------
+// packed variable-length sequences
+// ---------------------------------------------------------------------------
+namespace {
+// one batch row of `total` tokens cut into table slots
+FwdShape varlen_shape(int total, int nseq, int H, int P, int N, int G, int Q) {
+  FwdShape s = make_shape(1, total, H, P, N, G, Q);
+  s.nc = varlen_slots(total, nseq, Q);
+  return s;
+}
+size_t varlen_table_offset(const WsLayout& w) { return (w.total + 255) / 256 * 256; }
+}  // namespace
+
+size_t ssd_chunk_scan_fwd_varlen_workspace(int total_tokens, int nseq, int nheads, int headdim, int dstate,
+                                           int ngroups, int chunk_len, ssd_dtype dtype) {
+  if (!dtype_ok(dtype) || !is_chunk_ok(chunk_len) || nseq < 1 || nseq > 65535) return 0;
+  if (check_dims(1, total_tokens, nheads, headdim, dstate, ngroups) != SSD_OK) return 0;
+  const FwdShape s = varlen_shape(total_tokens, nseq, nheads, headdim, dstate, ngroups, chunk_len);
+  if (!use_mfma_path(s, dtype) || !grids_fit(s, true)) return 0;
+  const WsLayout w = ws_layout(s, true);
+  return varlen_table_offset(w) + size_t(s.nc) * sizeof(int4);
+}
+
+ssd_status ssd_chunk_scan_fwd_varlen(const void* x, const void* dt, const float* A, const void* B,
+                                     const void* C, const float* D, const int* cu_seqlens,
+                                     const float* init_states, void* y, float* final_states,
+                                     int total_tokens, int nseq, int nheads, int headdim, int dstate,
+                                     int ngroups, int chunk_len, ssd_dtype dtype, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  if (!dtype_ok(dtype)) return SSD_ERR_DTYPE;
+  ssd_status st = check_dims(1, total_tokens, nheads, headdim, dstate, ngroups);
+  if (st != SSD_OK) return st;
+  if (nseq < 1 || nseq > 65535) return SSD_ERR_SHAPE;
+  if (!is_chunk_ok(chunk_len)) return SSD_ERR_CHUNK;
+  if (!x || !dt || !A || !B || !C || !y || !cu_seqlens) return SSD_ERR_NULL;
+  if (!workspace) return SSD_ERR_WORKSPACE;
+  const void* ptrs[] = {x, dt, A, B, C, D, init_states, y, final_states, workspace};
+  for (const void* p : ptrs)
+    if (misaligned(p)) return SSD_ERR_ALIGN;
+  if (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) return SSD_ERR_ALIGN;
+  const FwdShape s = varlen_shape(total_tokens, nseq, nheads, headdim, dstate, ngroups, chunk_len);
+  if (!use_mfma_path(s, dtype) || !grids_fit(s, true)) return SSD_ERR_SHAPE;
+  const WsLayout w = ws_layout(s, true);
+  const size_t tab_off = varlen_table_offset(w);
+  if (workspace_bytes < tab_off + size_t(s.nc) * sizeof(int4)) return SSD_ERR_WORKSPACE;
+
+  const size_t e = esize(dtype);
+  const size_t tok = size_t(total_tokens);
+  const size_t xb = tok * nheads * headdim * e, dtb = tok * nheads * e;
+  const size_t bcb = tok * ngroups * dstate * e, hb = size_t(nheads) * sizeof(float);
+  const size_t stb = size_t(nseq) * nheads * dstate * headdim * sizeof(float);
+  const size_t cub = size_t(nseq + 1) * sizeof(int);
+  const size_t wsb = tab_off + size_t(s.nc) * sizeof(int4);
+  struct In {
+    const void* p;
+    size_t n;
+  } ins[] = {{x, xb}, {dt, dtb}, {A, hb}, {B, bcb}, {C, bcb}, {D, hb}, {init_states, stb}, {cu_seqlens, cub}};
+  for (const In& in : ins) {
+    if (overlaps(y, xb, in.p, in.n) || overlaps(workspace, wsb, in.p, in.n)) return SSD_ERR_ALIAS;
+    if (in.p != init_states && overlaps(final_states, stb, in.p, in.n)) return SSD_ERR_ALIAS;
+  }
+  if (overlaps(y, xb, final_states, stb) || overlaps(y, xb, workspace, wsb) ||
+      overlaps(final_states, stb, workspace, wsb))
+    return SSD_ERR_ALIAS;
+  if (final_states && init_states && final_states != init_states && overlaps(final_states, stb, init_states, stb))
+    return SSD_ERR_ALIAS;
+
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  float* Acs = reinterpret_cast<float*>(ws + w.acs);
+  float* dtq = reinterpret_cast<float*>(ws + w.dtq);
+  float* S = reinterpret_cast<float*>(ws + w.st);
+  uint16_t* Hb = reinterpret_cast<uint16_t*>(ws + w.hb);
+  uint16_t* CB = reinterpret_cast<uint16_t*>(ws + w.cb);
+  int4* tab = reinterpret_cast<int4*>(ws + tab_off);
+  // The empty-sequence finals read cu_seqlens and init_states and write
+  // final_states only for sequences without tokens; state_passing writes the
+  // others, and reads init_states before any of its own final writes of the
+  // same sequence, so final_states may be init_states.
+  if (launch_varlen_table(cu_seqlens, nseq, total_tokens, chunk_len, tab, hs) != hipSuccess) return SSD_ERR_HIP;
+  if (launch_chunk_state_mfma(s, x, B, C, dt, A, Acs, dtq, S, CB, tab, hs) != hipSuccess) return SSD_ERR_HIP;
+  if (launch_state_passing_varlen(s, S, Hb, Acs, tab, init_states, final_states, hs) != hipSuccess)
+    return SSD_ERR_HIP;
+  if (launch_chunk_scan_mfma(s, x, CB, C, Acs, dtq, Hb, D, y, tab, hs) != hipSuccess) return SSD_ERR_HIP;
+  if (final_states &&
+      launch_varlen_empty_finals(cu_seqlens, nseq, total_tokens, init_states, final_states,
+                                 long(nheads) * dstate * headdim, hs) != hipSuccess)
     return SSD_ERR_HIP;
   return SSD_OK;
 }

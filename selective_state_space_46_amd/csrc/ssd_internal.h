@@ -53,6 +53,28 @@ __device__ __forceinline__ float exp_fast(float x) {
 }
 
 // ---------------------------------------------------------------------------
+// Chunks of a forward call. Every kernel sees a chunk as its first token
+// row in the token-major tensors (row = b * T + t) and its number of valid
+// tokens; tokens past them count as dt = 0 (nothing enters the state). For
+// a batch of equal-length rows both follow from (b, c); for packed
+// variable-length sequences each chunk lies inside one sequence and a table
+// gives them: tab[c] = {first row, valid tokens (0: unused slot), sequence,
+// flags} with flags bit 0 = first chunk of its sequence, bit 1 = last.
+// ---------------------------------------------------------------------------
+struct ChunkRows {
+  long r0;   // first token row
+  int n;     // valid tokens (0 .. Q)
+};
+
+__device__ __forceinline__ ChunkRows chunk_rows(const int4* tab, int b, int c, int T, int Q) {
+  if (tab) {
+    const int4 e = tab[c];
+    return ChunkRows{long(e.x), e.y};
+  }
+  return ChunkRows{long(b) * T + long(c) * Q, min(Q, T - c * Q)};
+}
+
+// ---------------------------------------------------------------------------
 // Problem shape of one forward call.
 // ---------------------------------------------------------------------------
 struct FwdShape {
@@ -130,14 +152,22 @@ hipError_t launch_chunk_state(const FwdShape& s, ssd_dtype type, const void* x, 
 // Matrix-core path: S^T [b, nc, H, P, N] f32; the same launch also computes
 // the in-chunk cumulative sums (written to Acs / dtq) and the C B^T tiles
 // (CB [b, nc, G, ntile, 64, 16] bf16) for the kernels after it.
+// tab: the chunk table of packed variable-length sequences, or nullptr.
 hipError_t launch_chunk_state_mfma(const FwdShape& s, const void* x, const void* B, const void* C,
                                    const void* dt, const float* A, float* Acs, float* dtq,
-                                   float* S, uint16_t* CB, hipStream_t st, const StageEv& ev = StageEv{});
+                                   float* S, uint16_t* CB, const int4* tab, hipStream_t st,
+                                   const StageEv& ev = StageEv{});
 
 // Hb == nullptr: states entering each chunk overwrite S in place (fp32);
 // otherwise they are written to Hb as bf16 and S is left as it was.
 hipError_t launch_state_passing(const FwdShape& s, float* S, uint16_t* Hb, const float* Acs,
                                 const float* init, float* final_state, hipStream_t st, const StageEv& ev = StageEv{});
+
+// Packed variable-length sequences (batch 1, chunk table tab, matrix-core
+// path): init / final_state are [nseq, H, N, P].
+hipError_t launch_state_passing_varlen(const FwdShape& s, const float* S, uint16_t* Hb, const float* Acs,
+                                       const int4* tab, const float* init, float* final_state,
+                                       hipStream_t st, const StageEv& ev = StageEv{});
 
 // Generic path reads Hst (fp32, [b, nc, H, P, N]); MFMA path reads Hb (bf16)
 // and the C B^T tiles CB.
@@ -147,7 +177,15 @@ hipError_t launch_chunk_scan(const FwdShape& s, ssd_dtype type, bool mfma, const
                              const float* D, void* y, hipStream_t st, const StageEv& ev = StageEv{});
 hipError_t launch_chunk_scan_mfma(const FwdShape& s, const void* x, const uint16_t* CB,
                                   const void* C, const float* Acs, const float* dtq,
-                                  const uint16_t* Hb, const float* D, void* y, hipStream_t st, const StageEv& ev = StageEv{});
+                                  const uint16_t* Hb, const float* D, void* y, const int4* tab,
+                                  hipStream_t st, const StageEv& ev = StageEv{});
+
+// Packed variable-length sequences (varlen.hip): the chunk table has
+// varlen_slots(T, nseq, Q) int4 entries.
+int varlen_slots(int T, int nseq, int Q);
+hipError_t launch_varlen_table(const int* cu, int nseq, int T, int Q, int4* tab, hipStream_t st);
+hipError_t launch_varlen_empty_finals(const int* cu, int nseq, int T, const float* init, float* fin,
+                                      long per_seq, hipStream_t st);
 
 // Element-wise stages next to the core (epilogue.hip).
 hipError_t launch_gated_rmsnorm(ssd_dtype type, const void* y, const void* z, const float* w, void* out,

@@ -33,7 +33,8 @@ def test_header_declares_the_entry_points():
     assert set(declared_symbols()) == {"ssd_chunk_scan_fwd_workspace", "ssd_chunk_scan_fwd",
                                        "ssd_chunk_scan_fwd_timed", "ssd_state_update",
                                        "ssd_status_string", "ssd_gated_rmsnorm",
-                                       "ssd_causal_conv1d_fwd", "ssd_causal_conv1d_update"}
+                                       "ssd_causal_conv1d_fwd", "ssd_causal_conv1d_update",
+                                       "ssd_chunk_scan_fwd_varlen", "ssd_chunk_scan_fwd_varlen_workspace"}
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -208,3 +209,38 @@ def test_conv1d_update_argument_errors(L):
     assert upd1(L, out=FAKE + 0x100000) == 7          # out over x
     assert upd1(L, state=FAKE + 0x300000) == 7        # state over out
     assert upd1(L, x=FAKE + 0x100002) == 8
+
+
+def vl(L, **kw):
+    a = dict(x=FAKE, dt=FAKE + 0x100000, A=FAKE + 0x200000, B=FAKE + 0x300000, C=FAKE + 0x400000, D=None,
+             cu=FAKE + 0x500000, init=None, y=FAKE + 0x600000, fin=None, T=300, nseq=3, H=2, P=64, N=128,
+             G=1, Q=64, dtype=1, ws=FAKE + 0x800000, nbytes=1 << 30, stream=None)
+    a.update(kw)
+    return L.ssd_chunk_scan_fwd_varlen(a["x"], a["dt"], a["A"], a["B"], a["C"], a["D"], a["cu"], a["init"],
+                                       a["y"], a["fin"], a["T"], a["nseq"], a["H"], a["P"], a["N"], a["G"],
+                                       a["Q"], a["dtype"], a["ws"], a["nbytes"], a["stream"])
+
+
+def test_varlen_workspace_and_errors(L):
+    wsq = ssd.ssd_chunk_scan_fwd_varlen_workspace
+    assert wsq(300, 3, 2, 64, 128, 1, 64, ssd.SSD_BF16) > 0
+    assert wsq(300, 3, 2, 64, 128, 1, 64, ssd.SSD_F32) == 0      # matrix-core configuration only
+    assert wsq(300, 3, 2, 16, 16, 1, 64, ssd.SSD_BF16) == 0      # headdim 16: no matrix-core path
+    assert wsq(300, 0, 2, 64, 128, 1, 64, ssd.SSD_BF16) == 0
+    assert wsq(300, 70000, 2, 64, 128, 1, 64, ssd.SSD_BF16) == 0
+    # more sequences need more chunk slots (one partial chunk each at most)
+    assert wsq(300, 9, 2, 64, 128, 1, 64, ssd.SSD_BF16) > wsq(300, 3, 2, 64, 128, 1, 64, ssd.SSD_BF16)
+    assert vl(L, dtype=3) == 3
+    assert vl(L, dtype=0) == 2          # fp32: not the matrix-core configuration
+    assert vl(L, nseq=0) == 2
+    assert vl(L, T=0) == 2
+    assert vl(L, Q=48) == 4
+    for k in ("x", "dt", "A", "B", "C", "y", "cu"):
+        assert vl(L, **{k: None}) == 1, k
+    assert vl(L, ws=None) == 5
+    assert vl(L, nbytes=1000) == 5
+    assert vl(L, cu=FAKE + 0x500002) == 8
+    assert vl(L, x=FAKE + 0x8) == 8
+    assert vl(L, y=FAKE) == 7                                    # y over x
+    assert vl(L, fin=FAKE + 0x500000) == 7                       # final states over cu_seqlens
+    assert vl(L, ws=FAKE + 0x300000) == 7                        # workspace over B
