@@ -346,6 +346,46 @@ def bench_next_to_core(hip, steps=20, warmup=3):
     return out
 
 
+def bench_varlen(hip, vw, steps=20, warmup=3):
+    """The forward over packed variable-length sequences (one token axis, a
+    per-sequence initial and final state): the whole call, chunk table build
+    included, timed with HIP events around `steps` calls on one stream."""
+    import torch
+    import selective_state_space_46_amd as ssd
+    stream = torch.cuda.current_stream().cuda_stream
+    vi = workloads.make_varlen_inputs(vw)
+    x, dt, B, C = (to_dev(vi[k], vw.dtype) for k in ("x", "dt", "B", "C"))
+    A, D = to_dev(vi["A"], "f32"), to_dev(vi["D"], "f32")
+    init = to_dev(vi["init"], "f32") if vi["init"] is not None else None
+    cu = torch.from_numpy(vi["cu_seqlens"]).cuda()
+    nseq = cu.numel() - 1
+    y = torch.empty_like(x)
+    fin = torch.empty((nseq, vw.nheads, vw.dstate, vw.headdim), dtype=torch.float32, device="cuda")
+    need = ssd.ssd_chunk_scan_fwd_varlen_workspace(vw.total, nseq, vw.nheads, vw.headdim, vw.dstate,
+                                                   vw.ngroups, vw.chunk_len, 1 if vw.dtype == "bf16" else 0)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+
+    def call():
+        ssd.ssd_chunk_scan_fwd_varlen(x, dt, A, B, C, D, cu, init, vw.chunk_len, y=y, final_states=fin,
+                                      workspace=ws, stream=stream)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    a, b = hip.event(), hip.event()
+    hip.record(a, stream)
+    for _ in range(steps):
+        call()
+    hip.record(b, stream)
+    torch.cuda.synchronize()
+    ms = hip.ms(a, b) / steps
+    hip.destroy(a)
+    hip.destroy(b)
+    lens = np.diff(vi["cu_seqlens"])
+    return {"workload": vw.name, "nseq": nseq, "min_len": int(lens.min()), "max_len": int(lens.max()),
+            "ms_per_call": round(ms, 5), "tokens_per_s": round(vw.total / (ms * 1e-3), 1)}
+
+
 def traffic_probe(w):
     """Three forward calls, then three copies of a 256 MiB buffer: a plain
     copy kernel that reads and writes exactly 256 MiB, against which the
@@ -460,6 +500,9 @@ def main():
                                "stage_ms": {k: round(v, 4) for k, v in rr["stage_ms"].items()}}
             log(f"[bench]   {rr['ms_per_step']:.4f} ms/step")
         out["other_workloads"] = others
+        log(f"[bench] packed sequences {workloads.VARLEN_130M.name}")
+        out["varlen"] = bench_varlen(hip, workloads.VARLEN_130M)
+        log(f"[bench]   {out['varlen']}")
         log("[bench] stages next to the core (conv1d, gated RMSNorm, conv decode update)")
         out["next_to_core"] = bench_next_to_core(hip)
         log(f"[bench]   {out['next_to_core']}")

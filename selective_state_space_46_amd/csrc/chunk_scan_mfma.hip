@@ -81,15 +81,19 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_mfma_kernel(
   auto crows = [&](int ci) {
     return c0 + ci < nc ? chunk_rows(tab, b, c0 + ci, T, Q) : ChunkRows{0, 0};
   };
-  const ChunkRows rows0 = crows(0);
-  if (rows0.n <= 0) return;            // unused slot of a chunk table: uniform, before any barrier
   // fast: every row of the super-chunk is a valid token and the rows are
-  // consecutive token rows (always so for equal-length batch rows)
+  // consecutive token rows (always so for equal-length batch rows);
+  // rowsv: the first chunk with valid rows (a chunk table may leave any slot
+  // unused)
+  const ChunkRows rows0 = crows(0);
+  ChunkRows rowsv = rows0;
   bool fast = true;
   for (int ci = 0; ci < cps; ++ci) {
     const ChunkRows r = crows(ci);
     fast = fast && r.n == Q && r.r0 == rows0.r0 + long(ci) * Q;
+    if (rowsv.n <= 0) rowsv = r;
   }
+  if (rowsv.n <= 0) return;            // no valid chunk: uniform, before any barrier
 
   // C B^T tiles of 32-row block i: tile jj (column block jfirst + jj) of the
   // block's row of its chunk's lower triangle, this lane's 32 bytes
@@ -165,8 +169,8 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_mfma_kernel(
         const ChunkRows cr = crows(r / Q);
         const int rq = r % Q;
         // a chunk with no valid rows (past the last chunk, or an unused table
-        // slot) reads the super-chunk's first row instead: any in-bounds row
-        const long row = cr.n > 0 ? cr.r0 + min(rq, cr.n - 1) : rows0.r0;
+        // slot) reads a valid row of another chunk instead: any in-bounds row
+        const long row = cr.n > 0 ? cr.r0 + min(rq, cr.n - 1) : rowsv.r0;
         const u32x4 v = load16(x + (row * H + h) * size_t(P) + 8 * cc);
         *reinterpret_cast<u32x4*>(dst + k * kStep * P) = keep_or_zero(rq < cr.n, v);
       }

@@ -242,6 +242,12 @@ FwdShape varlen_shape(int total, int nseq, int H, int P, int N, int G, int Q) {
   return s;
 }
 size_t varlen_table_offset(const WsLayout& w) { return (w.total + 255) / 256 * 256; }
+// the per-sequence state passing launches 256 threads per (sequence, head,
+// 16 x 64 state tile)
+bool varlen_grids_fit(const FwdShape& s, int nseq) {
+  return grids_fit(s, true) &&
+         256.0 * nseq * s.H * ((s.P + 15) / 16) * ((s.N + 63) / 64) < 4294967295.0;
+}
 }  // namespace
 
 size_t ssd_chunk_scan_fwd_varlen_workspace(int total_tokens, int nseq, int nheads, int headdim, int dstate,
@@ -249,7 +255,7 @@ size_t ssd_chunk_scan_fwd_varlen_workspace(int total_tokens, int nseq, int nhead
   if (!dtype_ok(dtype) || !is_chunk_ok(chunk_len) || nseq < 1 || nseq > 65535) return 0;
   if (check_dims(1, total_tokens, nheads, headdim, dstate, ngroups) != SSD_OK) return 0;
   const FwdShape s = varlen_shape(total_tokens, nseq, nheads, headdim, dstate, ngroups, chunk_len);
-  if (!use_mfma_path(s, dtype) || !grids_fit(s, true)) return 0;
+  if (!use_mfma_path(s, dtype) || !varlen_grids_fit(s, nseq)) return 0;
   const WsLayout w = ws_layout(s, true);
   return varlen_table_offset(w) + size_t(s.nc) * sizeof(int4);
 }
@@ -272,7 +278,7 @@ ssd_status ssd_chunk_scan_fwd_varlen(const void* x, const void* dt, const float*
     if (misaligned(p)) return SSD_ERR_ALIGN;
   if (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) return SSD_ERR_ALIGN;
   const FwdShape s = varlen_shape(total_tokens, nseq, nheads, headdim, dstate, ngroups, chunk_len);
-  if (!use_mfma_path(s, dtype) || !grids_fit(s, true)) return SSD_ERR_SHAPE;
+  if (!use_mfma_path(s, dtype) || !varlen_grids_fit(s, nseq)) return SSD_ERR_SHAPE;
   const WsLayout w = ws_layout(s, true);
   const size_t tab_off = varlen_table_offset(w);
   if (workspace_bytes < tab_off + size_t(s.nc) * sizeof(int4)) return SSD_ERR_WORKSPACE;
@@ -306,19 +312,14 @@ ssd_status ssd_chunk_scan_fwd_varlen(const void* x, const void* dt, const float*
   uint16_t* Hb = reinterpret_cast<uint16_t*>(ws + w.hb);
   uint16_t* CB = reinterpret_cast<uint16_t*>(ws + w.cb);
   int4* tab = reinterpret_cast<int4*>(ws + tab_off);
-  // The empty-sequence finals read cu_seqlens and init_states and write
-  // final_states only for sequences without tokens; state_passing writes the
-  // others, and reads init_states before any of its own final writes of the
-  // same sequence, so final_states may be init_states.
+  // state_passing reads each sequence's initial state (whole tile, into
+  // LDS) before it writes that sequence's final state, so final_states may
+  // be init_states.
   if (launch_varlen_table(cu_seqlens, nseq, total_tokens, chunk_len, tab, hs) != hipSuccess) return SSD_ERR_HIP;
   if (launch_chunk_state_mfma(s, x, B, C, dt, A, Acs, dtq, S, CB, tab, hs) != hipSuccess) return SSD_ERR_HIP;
-  if (launch_state_passing_varlen(s, S, Hb, Acs, tab, init_states, final_states, hs) != hipSuccess)
+  if (launch_state_passing_varlen(s, S, Hb, Acs, cu_seqlens, nseq, init_states, final_states, hs) != hipSuccess)
     return SSD_ERR_HIP;
   if (launch_chunk_scan_mfma(s, x, CB, C, Acs, dtq, Hb, D, y, tab, hs) != hipSuccess) return SSD_ERR_HIP;
-  if (final_states &&
-      launch_varlen_empty_finals(cu_seqlens, nseq, total_tokens, init_states, final_states,
-                                 long(nheads) * dstate * headdim, hs) != hipSuccess)
-    return SSD_ERR_HIP;
   return SSD_OK;
 }
 

@@ -56,10 +56,16 @@ __device__ __forceinline__ float exp_fast(float x) {
 // Chunks of a forward call. Every kernel sees a chunk as its first token
 // row in the token-major tensors (row = b * T + t) and its number of valid
 // tokens; tokens past them count as dt = 0 (nothing enters the state). For
-// a batch of equal-length rows both follow from (b, c); for packed
-// variable-length sequences each chunk lies inside one sequence and a table
-// gives them: tab[c] = {first row, valid tokens (0: unused slot), sequence,
-// flags} with flags bit 0 = first chunk of its sequence, bit 1 = last.
+// a batch of equal-length rows both follow from (b, c).
+//
+// Packed variable-length sequences (one row of T tokens, sequence i being
+// tokens cu[i] .. cu[i+1]-1) are cut into chunks that each lie inside one
+// sequence; chunk k of sequence i takes slot floor(cu[i] / Q) + i + k. The
+// slots of one sequence are consecutive, later sequences take later slots
+// (a chunk of sequence i starts before sequence i+1 does, and i grows by
+// one), and the last slot is below ceil(T / Q) + nseq. A table gives each
+// slot tab[c] = {first row, valid tokens (0: unused slot), sequence, flags
+// (bit 0: first chunk of its sequence, bit 1: last)}.
 // ---------------------------------------------------------------------------
 struct ChunkRows {
   long r0;   // first token row
@@ -69,10 +75,22 @@ struct ChunkRows {
 __device__ __forceinline__ ChunkRows chunk_rows(const int4* tab, int b, int c, int T, int Q) {
   if (tab) {
     const int4 e = tab[c];
-    return ChunkRows{long(e.x), e.y};
+    return ChunkRows{long(e.x), min(e.y, T - e.x)};   // rows stay inside [0, T) whatever the entry
   }
   return ChunkRows{long(b) * T + long(c) * Q, min(Q, T - c * Q)};
 }
+
+// The token span of sequence i: offsets are clamped into [0, T] and a span
+// never ends before it starts, so any offsets give in-bounds spans.
+// Well-formed offsets (0 = cu[0] <= ... <= cu[nseq] = T) are used as given.
+__device__ __forceinline__ void varlen_span(const int* cu, int i, int T, int& s0, int& len) {
+  s0 = min(max(cu[i], 0), T);
+  const int s1 = max(s0, min(max(cu[i + 1], 0), T));
+  len = s1 - s0;
+}
+
+// first chunk slot of sequence i, which starts at token s0
+__device__ __forceinline__ int varlen_first_slot(int s0, int i, int Q) { return s0 / Q + i; }
 
 // ---------------------------------------------------------------------------
 // Problem shape of one forward call.
@@ -163,10 +181,11 @@ hipError_t launch_chunk_state_mfma(const FwdShape& s, const void* x, const void*
 hipError_t launch_state_passing(const FwdShape& s, float* S, uint16_t* Hb, const float* Acs,
                                 const float* init, float* final_state, hipStream_t st, const StageEv& ev = StageEv{});
 
-// Packed variable-length sequences (batch 1, chunk table tab, matrix-core
-// path): init / final_state are [nseq, H, N, P].
+// Packed variable-length sequences (batch 1, chunk slots as above, matrix-core
+// path): one recurrence per sequence over its own slots; init / final_state
+// are [nseq, H, N, P] (a sequence without tokens: final = init, or zero).
 hipError_t launch_state_passing_varlen(const FwdShape& s, const float* S, uint16_t* Hb, const float* Acs,
-                                       const int4* tab, const float* init, float* final_state,
+                                       const int* cu, int nseq, const float* init, float* final_state,
                                        hipStream_t st, const StageEv& ev = StageEv{});
 
 // Generic path reads Hst (fp32, [b, nc, H, P, N]); MFMA path reads Hb (bf16)
@@ -184,8 +203,6 @@ hipError_t launch_chunk_scan_mfma(const FwdShape& s, const void* x, const uint16
 // varlen_slots(T, nseq, Q) int4 entries.
 int varlen_slots(int T, int nseq, int Q);
 hipError_t launch_varlen_table(const int* cu, int nseq, int T, int Q, int4* tab, hipStream_t st);
-hipError_t launch_varlen_empty_finals(const int* cu, int nseq, int T, const float* init, float* fin,
-                                      long per_seq, hipStream_t st);
 
 // Element-wise stages next to the core (epilogue.hip).
 hipError_t launch_gated_rmsnorm(ssd_dtype type, const void* y, const void* z, const float* w, void* out,

@@ -16,6 +16,13 @@
 // generic path) or to a separate bf16 buffer (the MFMA path, whose chunk_scan
 // consumes it as a bf16 matrix operand).
 //
+// Packed variable-length sequences run the same recurrence once per
+// sequence, over that sequence's own chunk slots, from its initial state (or
+// zero), and its last state is its final state (youngju.dev page, section on
+// state initialisation and sequence boundaries: no state crosses from one
+// sequence into the next); a sequence without tokens passes its initial
+// state through.
+//
 // Elementwise and HBM-bound: each thread owns 4 consecutive n of one p and
 // walks the chunks in order. Chunk states of later chunks do not depend on
 // the recurrence, so their loads are issued kDepth chunks ahead of use.
@@ -41,9 +48,14 @@ __device__ __forceinline__ void store_out(float* S, uint16_t* Hb, size_t idx, co
 }
 
 // grid: b * H * ceil(P/kTP) * ceil(N/kTN) work-groups; requires N % 4 == 0.
+// VARLEN: b counts sequences instead of batch rows, and the chunks of
+// sequence b are its slots of the one packed row (cu: sequence offsets, T:
+// packed tokens); init / fin are [nseq, H, N, P] like a batch of nseq rows.
+template <bool VARLEN>
 __global__ __launch_bounds__(kThreads) void state_passing_tiled(
     float* __restrict__ S, uint16_t* __restrict__ Hb, const float* __restrict__ Acs,
-    const float* __restrict__ init, float* __restrict__ fin, int H, int P, int N, int Q, int nc) {
+    const float* __restrict__ init, float* __restrict__ fin, int H, int P, int N, int Q, int nc,
+    const int* __restrict__ cu, int T) {
   __shared__ float tile[kTN][kTP + 1];
   const int tpn = (N + kTN - 1) / kTN, tpp = (P + kTP - 1) / kTP;
   int bid = blockIdx.x;
@@ -72,27 +84,38 @@ __global__ __launch_bounds__(kThreads) void state_passing_tiled(
     __syncthreads();
   }
 
+  // the chunks this work-group walks: rows [crow, crow + ncw) of the chunk
+  // arrays of batch row brow
+  int brow = b, crow = 0, ncw = nc;
+  if constexpr (VARLEN) {
+    int s0, len;
+    varlen_span(cu, b, T, s0, len);
+    brow = 0;
+    crow = varlen_first_slot(s0, b, Q);
+    ncw = (len + Q - 1) / Q;
+  }
+
   if (active) {
     const size_t cstride = size_t(H) * sbh;  // elements between chunk c and c+1
-    const size_t off0 = (size_t(b) * nc * H + h) * sbh + size_t(p) * N + n;
-    const float* arow = Acs + size_t(bh) * nc * Q + (Q - 1);
+    const size_t off0 = ((size_t(brow) * nc + crow) * H + h) * sbh + size_t(p) * N + n;
+    const float* arow = Acs + ((size_t(brow) * H + h) * nc + crow) * Q + (Q - 1);
     f32x4 ring[kDepth];
     float dec[kDepth];
 #pragma unroll
     for (int k = 0; k < kDepth; ++k) {
-      if (k < nc) {
+      if (k < ncw) {
         ring[k] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(S + off0 + size_t(k) * cstride));
         dec[k] = arow[size_t(k) * Q];
       }
     }
-    for (int c0 = 0; c0 < nc; c0 += kDepth) {
+    for (int c0 = 0; c0 < ncw; c0 += kDepth) {
 #pragma unroll
       for (int k = 0; k < kDepth; ++k) {
         const int c = c0 + k;
-        if (c < nc) {
+        if (c < ncw) {
           const f32x4 s = ring[k];
           const float a = expf(dec[k]);
-          if (c + kDepth < nc) {
+          if (c + kDepth < ncw) {
             ring[k] = __builtin_nontemporal_load(
                 reinterpret_cast<const f32x4*>(S + off0 + size_t(c + kDepth) * cstride));
             dec[k] = arow[size_t(c + kDepth) * Q];
@@ -141,87 +164,17 @@ __global__ __launch_bounds__(kThreads) void state_passing_scalar(
   if (fin) fin[i] = cur;
 }
 
-// Packed variable-length sequences (batch 1, chunk table tab): the same
-// recurrence, restarted at the first chunk of every sequence from that
-// sequence's initial state (or zero), and the state after its last chunk
-// written as its final state (youngju.dev page, section on state
-// initialisation and sequence boundaries: no state crosses from one sequence
-// into the next). Initial and final states are [nseq, H, N, P]; they are
-// touched once per sequence, so they are read and written in place of the
-// LDS transposes the equal-length kernel uses. Table slots are filled from
-// slot 0 on, so the walk stops at the first unused one.
-__global__ __launch_bounds__(kThreads) void state_passing_varlen(
-    const float* __restrict__ S, uint16_t* __restrict__ Hb, const float* __restrict__ Acs,
-    const int4* __restrict__ tab, const float* __restrict__ init, float* __restrict__ fin, int H, int P,
-    int N, int Q, int nc) {
-  const int tpn = (N + kTN - 1) / kTN, tpp = (P + kTP - 1) / kTP;
-  int bid = blockIdx.x;
-  const int tn = bid % tpn; bid /= tpn;
-  const int tp = bid % tpp; bid /= tpp;
-  const int h = bid;
-  const int tid = threadIdx.x;
-  const int p = tp * kTP + tid / 16, n = tn * kTN + 4 * (tid % 16);
-  if (p >= P || n >= N) return;              // no barriers in this kernel
-  const size_t sbh = size_t(N) * P;
-  const size_t cstride = size_t(H) * sbh;
-  const size_t off0 = size_t(h) * sbh + size_t(p) * N + n;
-  const float* arow = Acs + size_t(h) * nc * Q + (Q - 1);
-  f32x4 ring[kDepth];
-  float dec[kDepth];
-  int4 ent[kDepth];
-#pragma unroll
-  for (int k = 0; k < kDepth; ++k) {
-    if (k < nc) {
-      ent[k] = tab[k];
-      ring[k] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(S + off0 + size_t(k) * cstride));
-      dec[k] = arow[size_t(k) * Q];
-    }
-  }
-  f32x4 cur = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int c0 = 0; c0 < nc; c0 += kDepth) {
-#pragma unroll
-    for (int k = 0; k < kDepth; ++k) {
-      const int c = c0 + k;
-      if (c >= nc) return;
-      const int4 e = ent[k];
-      if (e.y == 0) return;                   // first unused slot: every chunk is done
-      const f32x4 sv = ring[k];
-      const float a = expf(dec[k]);
-      if (c + kDepth < nc) {
-        ent[k] = tab[c + kDepth];
-        ring[k] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(S + off0 + size_t(c + kDepth) * cstride));
-        dec[k] = arow[size_t(c + kDepth) * Q];
-      }
-      if (e.w & 1) {                          // first chunk of sequence e.z: its initial state
-        const size_t ii = (size_t(e.z) * H + h) * sbh + size_t(n) * P + p;
-        cur = init ? f32x4{init[ii], init[ii + P], init[ii + 2 * P], init[ii + 3 * P]}
-                   : f32x4{0.f, 0.f, 0.f, 0.f};
-      }
-      store_out(nullptr, Hb, off0 + size_t(c) * cstride, cur);
-      cur.x = a * cur.x + sv.x;
-      cur.y = a * cur.y + sv.y;
-      cur.z = a * cur.z + sv.z;
-      cur.w = a * cur.w + sv.w;
-      if ((e.w & 2) && fin) {                 // last chunk of sequence e.z: its final state
-        const size_t fi = (size_t(e.z) * H + h) * sbh + size_t(n) * P + p;
-        fin[fi] = cur.x;
-        fin[fi + P] = cur.y;
-        fin[fi + 2 * P] = cur.z;
-        fin[fi + 3 * P] = cur.w;
-      }
-    }
-  }
-}
-
 }  // namespace
 
 hipError_t launch_state_passing_varlen(const FwdShape& s, const float* S, uint16_t* Hb, const float* Acs,
-                                       const int4* tab, const float* init, float* final_state,
+                                       const int* cu, int nseq, const float* init, float* final_state,
                                        hipStream_t st, const StageEv& ev) {
   if (s.N % 4 || !Hb) return hipErrorInvalidValue;   // matrix-core path only
-  const long tiles = long(s.H) * ((s.P + kTP - 1) / kTP) * ((s.N + kTN - 1) / kTN);
-  hipExtLaunchKernelGGL(state_passing_varlen, dim3(unsigned(tiles)), dim3(kThreads), 0, st, ev.start, ev.stop,
-                        0, S, Hb, Acs, tab, init, final_state, s.H, s.P, s.N, s.Q, s.nc);
+  const long tiles = long(nseq) * s.H * ((s.P + kTP - 1) / kTP) * ((s.N + kTN - 1) / kTN);
+  // S is only read: the passed states go to Hb
+  hipExtLaunchKernelGGL(state_passing_tiled<true>, dim3(unsigned(tiles)), dim3(kThreads), 0, st, ev.start,
+                        ev.stop, 0, const_cast<float*>(S), Hb, Acs, init, final_state, s.H, s.P, s.N, s.Q,
+                        s.nc, cu, s.T);
   return hipGetLastError();
 }
 
@@ -229,8 +182,9 @@ hipError_t launch_state_passing(const FwdShape& s, float* S, uint16_t* Hb, const
                                 const float* init, float* final_state, hipStream_t st, const StageEv& ev) {
   if (s.N % 4 == 0) {
     const long tiles = long(s.b) * s.H * ((s.P + kTP - 1) / kTP) * ((s.N + kTN - 1) / kTN);
-    hipExtLaunchKernelGGL(state_passing_tiled, dim3(unsigned(tiles)), dim3(kThreads), 0, st, ev.start, ev.stop, 0, S, Hb, Acs,
-                       init, final_state, s.H, s.P, s.N, s.Q, s.nc);
+    hipExtLaunchKernelGGL(state_passing_tiled<false>, dim3(unsigned(tiles)), dim3(kThreads), 0, st, ev.start,
+                          ev.stop, 0, S, Hb, Acs, init, final_state, s.H, s.P, s.N, s.Q, s.nc,
+                          static_cast<const int*>(nullptr), 0);
   } else {
     if (Hb) return hipErrorInvalidValue;     // the MFMA path never has N % 4 != 0
     const long total = long(s.b) * s.H * s.N * s.P;

@@ -97,14 +97,15 @@ def test_varlen_equals_equal_length_batch():
         assert torch.equal(fv, fb), Q
 
 
-def test_varlen_130m_shaped_many_sequences():
-    """The 130M layer's heads and state size over about 16K packed tokens in
-    twelve sequences of mixed length (whole-output comparison)."""
-    rng = np.random.default_rng(6400)
-    lens = rng.integers(1, 3000, size=12)
-    cu = np.concatenate([[0], np.cumsum(lens)]).tolist()
-    inp = _inputs(cu[-1], 24, 64, 128, 1, len(lens), seed=6401)
-    _check(inp, cu, 256)
+def test_varlen_130m_packed_workload():
+    """The packed 130M-shaped workload that bench.py times (16384 tokens,
+    sequences of 64 .. 4096 tokens, per-sequence initial states), whole
+    output against the oracle."""
+    vw = workloads.VARLEN_130M
+    vi = workloads.make_varlen_inputs(vw)
+    cu = vi["cu_seqlens"].tolist()
+    inp = {k: vi[k] for k in ("x", "dt", "A", "B", "C", "D", "init")}
+    _check(inp, cu, vw.chunk_len)
 
 
 def test_varlen_malformed_offsets_stay_in_bounds():

@@ -242,3 +242,63 @@ def make_conv_inputs(w: ConvWorkload, seed: Optional[int] = None) -> dict:
     if w.with_init:
         init = _store(rng.standard_normal((w.batch, w.width - 1, w.channels), dtype=np.float32), w.dtype)
     return dict(x=x, weight=weight, bias=bias, init=init)
+
+
+# --------------------------------------------------------------------------
+# Packed variable-length sequences: one token axis holding sequences of mixed
+# length, each with its own initial state.
+# --------------------------------------------------------------------------
+
+@dataclasses.dataclass(frozen=True)
+class VarlenWorkload:
+    name: str
+    total: int                 # packed tokens
+    nheads: int
+    headdim: int
+    dstate: int
+    ngroups: int
+    chunk_len: int
+    min_len: int = 64          # sequence lengths: log-uniform in [min_len, max_len],
+    max_len: int = 4096        # the last one cut so that they sum to `total`
+    dtype: str = "bf16"
+    init: str = "normal0.1"    # "zero" or "normal0.1"
+    seed: int = 0
+
+
+# the 130M-shaped layer over 16384 packed tokens (the token count of the
+# batched 8 x 2048 layer), sequences of 64 .. 4096 tokens
+VARLEN_130M = VarlenWorkload("varlen_130m_T16384_H24_P64_N128_Q256_len64-4096", 16384, 24, 64, 128, 1, 256,
+                             seed=4620)
+
+
+def draw_seqlens(rng: np.random.Generator, total: int, lo: int, hi: int) -> np.ndarray:
+    lens = []
+    left = total
+    while left > 0:
+        n = int(round(math.exp(rng.uniform(math.log(lo), math.log(hi)))))
+        n = max(1, min(n, left))
+        lens.append(n)
+        left -= n
+    return np.asarray(lens, dtype=np.int64)
+
+
+def make_varlen_inputs(w: VarlenWorkload, seed: Optional[int] = None) -> dict:
+    """x [T,H,P], dt [T,H], B/C [T,G,N] (dtype carriers), A, D [H] fp32,
+    cu_seqlens [nseq+1] int32, init [nseq,H,N,P] fp32 or None."""
+    rng = np.random.default_rng(w.seed if seed is None else seed)
+    lens = draw_seqlens(rng, w.total, w.min_len, w.max_len)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T, H, P, N, G = w.total, w.nheads, w.headdim, w.dstate, w.ngroups
+    x = _store(rng.standard_normal((T, H, P), dtype=np.float32), w.dtype)
+    dt = _store(draw_dt(rng, (T, H), "softplus"), w.dtype)
+    A = draw_A(rng, H)
+    s = np.float32(1.0 / math.sqrt(N))
+    B = _store(rng.standard_normal((T, G, N), dtype=np.float32) * s, w.dtype)
+    C = _store(rng.standard_normal((T, G, N), dtype=np.float32) * s, w.dtype)
+    D = rng.standard_normal(H, dtype=np.float32)
+    init = None
+    if w.init == "normal0.1":
+        init = rng.standard_normal((len(lens), H, N, P), dtype=np.float32) * np.float32(0.1)
+    elif w.init != "zero":
+        raise ValueError(w.init)
+    return dict(x=x, dt=dt, A=A, B=B, C=C, D=D, cu_seqlens=cu, init=init)
