@@ -20,6 +20,11 @@ Every function here is pinned by the closed forms and invariants in
 attention, T=1, constant dt, dt=0 identity, large-decay reset, split/resume,
 decode chain == forward).
 
+``ssd_bwd`` (``ssd_oracle_bwd.c``) gives the gradients of the forward by
+reverse-mode differentiation of the same per-token recurrence, pinned in
+``tests/test_oracle_bwd_pins.py`` against torch autograd of an independent
+fp64 forward, central finite differences of ``ssd_fwd`` and closed forms.
+
 ``oracle.epilogue`` holds the two element-wise stages next to the core (the
 gated RMS normalisation after it, the depthwise causal convolution before
 it), pinned in ``tests/test_oracle_epilogue_pins.py``.
@@ -35,17 +40,19 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "ssd_oracle.c")
+_SRC_BWD = os.path.join(_HERE, "ssd_oracle_bwd.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle_ssd.so")
 _lib = None
 
 
 def build(force: bool = True) -> str:
-    """Compile ssd_oracle.c into liboracle_ssd.so next to it (gcc, -O3)."""
+    """Compile ssd_oracle.c and ssd_oracle_bwd.c into liboracle_ssd.so next
+    to them (gcc, -O3)."""
     if not force and os.path.exists(_LIB_PATH):
         return _LIB_PATH
     tmp = _LIB_PATH + ".tmp"
     cmd = ["gcc", "-O3", "-march=x86-64-v3", "-ffp-contract=off", "-fPIC", "-shared",
-           "-std=c11", "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm", "-lpthread"]
+           "-std=c11", "-Wall", "-Wextra", "-o", tmp, _SRC, _SRC_BWD, "-lm", "-lpthread"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, _LIB_PATH)
     return _LIB_PATH
@@ -69,6 +76,8 @@ def _load():
     lib.oracle_ssd_decode.restype = I
     lib.oracle_ssd_fwd_varlen.argtypes = [P] * 7 + [I, P, P, P, L, I, I, I, I, I]
     lib.oracle_ssd_fwd_varlen.restype = I
+    lib.oracle_ssd_bwd.argtypes = [P] * 16 + [L, L, I, I, I, I, I]
+    lib.oracle_ssd_bwd.restype = I
     _lib = lib
     return lib
 
@@ -202,6 +211,32 @@ def ssd_fwd_varlen(x, dt, A, B, C, D, cu_seqlens, init=None, nthreads: Optional[
     if r != 0:
         raise ValueError(f"oracle_ssd_fwd_varlen failed ({r})")
     return y, fin
+
+
+def ssd_bwd(x, dt, A, B, C, D, init, dy, dfinal=None, nthreads: Optional[int] = None,
+            want_dinit: bool = True) -> dict:
+    """Gradients of ssd_fwd (ssd_oracle_bwd.c): for upstream dy [b,T,H,P] and
+    dfinal [b,H,N,P] (None = 0), returns float64 dx [b,T,H,P], ddt [b,T,H],
+    dA [H], dB [b,T,G,N], dC [b,T,G,N], dD [H] and dinit [b,H,N,P] (None
+    unless wanted). Inputs as for ssd_fwd."""
+    x, dt, A, B, C, dy = (_f32(v) for v in (x, dt, A, B, C, dy))
+    D = None if D is None else _f32(D)
+    init = None if init is None else _f64(init)
+    dfinal = None if dfinal is None else _f64(dfinal)
+    b, T, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    assert dt.shape == (b, T, H) and A.shape == (H,) and B.shape == (b, T, G, N) == C.shape
+    assert dy.shape == x.shape
+    out = dict(dx=np.empty((b, T, H, P)), ddt=np.empty((b, T, H)), dA=np.empty(H),
+               dB=np.empty((b, T, G, N)), dC=np.empty((b, T, G, N)), dD=np.empty(H),
+               dinit=np.empty((b, H, N, P)) if want_dinit else None)
+    r = _load().oracle_ssd_bwd(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(init),
+                               _ptr(dy), _ptr(dfinal), _ptr(out["dx"]), _ptr(out["ddt"]), _ptr(out["dA"]),
+                               _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["dD"]), _ptr(out["dinit"]),
+                               b, T, H, P, N, G, nthreads or default_threads())
+    if r != 0:
+        raise RuntimeError(f"oracle_ssd_bwd failed ({r})")
+    return out
 
 
 def rel_l2(got, ref) -> float:
