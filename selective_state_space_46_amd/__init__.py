@@ -14,6 +14,9 @@ Entry points (same names as the C ABI):
     ssd_status_string(code) -> str
     ssd_chunk_scan_fwd_varlen(x, dt, A, B, C, D, cu_seqlens, init_states, chunk_len)
         -> (y, final_states)                          (packed variable-length sequences)
+and, from ``include/ssd_backward.h``, the backward pass:
+    ssd_chunk_scan_bwd(x, dt, A, B, C, D, init_state, dy, dfinal)
+        -> dict(dx, ddt, dA, dB, dC, dD, dinit)
 and, from ``include/ssd_epilogue.h``, the element-wise stages next to the core:
     ssd_gated_rmsnorm(y, z, weight, group, eps) -> out
     ssd_causal_conv1d_fwd(x, weight, bias, init_state, activation) -> (out, final_state)
@@ -30,7 +33,7 @@ __all__ = [
     "ssd_chunk_scan_fwd_workspace", "ssd_chunk_scan_fwd", "ssd_chunk_scan_fwd_timed",
     "ssd_state_update", "ssd_status_string", "ssd_chunk_scan_fwd_varlen",
     "ssd_chunk_scan_fwd_varlen_workspace", "ssd_gated_rmsnorm", "ssd_causal_conv1d_fwd",
-    "ssd_causal_conv1d_update",
+    "ssd_causal_conv1d_update", "ssd_chunk_scan_bwd_workspace", "ssd_chunk_scan_bwd",
 ]
 
 SSD_F32 = 0
@@ -89,6 +92,10 @@ def lib() -> ctypes.CDLL:
     L.ssd_causal_conv1d_fwd.restype = i32
     L.ssd_causal_conv1d_update.argtypes = [vp] * 5 + [i32] * 4 + [i32, vp]
     L.ssd_causal_conv1d_update.restype = i32
+    L.ssd_chunk_scan_bwd_workspace.argtypes = [i32] * 7
+    L.ssd_chunk_scan_bwd_workspace.restype = sz
+    L.ssd_chunk_scan_bwd.argtypes = [vp] * 16 + [i32] * 7 + [vp, sz, vp]
+    L.ssd_chunk_scan_bwd.restype = i32
     _lib = L
     return L
 
@@ -393,3 +400,59 @@ def ssd_chunk_scan_fwd_varlen(x, dt, A, B, C, D, cu_seqlens, init_states=None, c
     if r != 0:
         raise SSDError(r, "ssd_chunk_scan_fwd_varlen")
     return y, final_states
+
+
+def ssd_chunk_scan_bwd_workspace(batch: int, seqlen: int, nheads: int, headdim: int, dstate: int,
+                                 ngroups: int, dtype: int) -> int:
+    return int(lib().ssd_chunk_scan_bwd_workspace(batch, seqlen, nheads, headdim, dstate, ngroups, dtype))
+
+
+def ssd_chunk_scan_bwd(x, dt, A, B, C, D=None, init_state=None, dy=None, dfinal=None, *, out=None,
+                       want_dD: bool = True, want_dinit: bool = True, workspace=None, stream=None) -> dict:
+    """Gradients of ssd_chunk_scan_fwd for upstream dy [b,T,H,P] (x's dtype)
+    and dfinal [b,H,N,P] fp32 or None. Returns dict(dx, ddt, dB, dC in x's
+    dtype, dA [H] fp32, dD [H] fp32 or None, dinit [b,H,N,P] fp32 or None).
+    `out` may hold preallocated outputs under the same names."""
+    import torch
+    if dy is None:
+        raise ValueError("dy is required")
+    dev = x.device
+    x = _dev(x, dev, "x")
+    dt, A, B, C, dy = (_dev(v, dev, n) for v, n in ((dt, "dt"), (A, "A"), (B, "B"), (C, "C"), (dy, "dy")))
+    D, init_state, dfinal = (_dev(v, dev, n) for v, n in ((D, "D"), (init_state, "init_state"),
+                                                          (dfinal, "dfinal")))
+    code = _dtype_code(x)
+    for v, n in ((dt, "dt"), (B, "B"), (C, "C"), (dy, "dy")):
+        _same(v, x.dtype, n)
+    for v, n in ((A, "A"), (D, "D"), (init_state, "init_state"), (dfinal, "dfinal")):
+        _same(v, torch.float32, n)
+    b, T, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    if tuple(dt.shape) != (b, T, H) or tuple(B.shape) != (b, T, G, N) or tuple(C.shape) != (b, T, G, N) \
+            or tuple(dy.shape) != (b, T, H, P):
+        raise ValueError("shape mismatch among x, dt, B, C, dy")
+    o = dict(out or {})
+    f32 = torch.float32
+    shapes = dict(dx=((b, T, H, P), x.dtype), ddt=((b, T, H), x.dtype), dA=((H,), f32),
+                  dB=((b, T, G, N), x.dtype), dC=((b, T, G, N), x.dtype), dD=((H,), f32),
+                  dinit=((b, H, N, P), f32))
+    for k, (shp, dty) in shapes.items():
+        if k == "dD" and not want_dD or k == "dinit" and not want_dinit:
+            o[k] = None
+        elif o.get(k) is None:
+            o[k] = torch.empty(shp, dtype=dty, device=dev)
+        else:
+            o[k] = _inout(o[k], dev, k)
+    need = ssd_chunk_scan_bwd_workspace(b, T, H, P, N, G, code)
+    if need == 0:
+        raise SSDError(2, "ssd_chunk_scan_bwd_workspace")
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    r = lib().ssd_chunk_scan_bwd(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(init_state),
+                                 _ptr(dy), _ptr(dfinal), _ptr(o["dx"]), _ptr(o["ddt"]), _ptr(o["dA"]),
+                                 _ptr(o["dB"]), _ptr(o["dC"]), _ptr(o["dD"]), _ptr(o["dinit"]), b, T, H, P, N,
+                                 G, code, _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                 _stream(dev, stream))
+    if r != 0:
+        raise SSDError(r, "ssd_chunk_scan_bwd")
+    return o

@@ -53,11 +53,17 @@ constexpr int kMaxQ = 256;
 // MFMA, loaded there with two coalesced 16-byte reads per lane.
 // Layout: CB [b, nc, G, ntile, 64, 16] bf16 with ntile = lpc(lpc+1)/2,
 // lpc = Q/32, tile (s, l) of a chunk at index l(l+1)/2 + s.
-template <int N>
+// BOTH (the backward's recomputation): the tiles stay fp32 (16 floats per
+// lane, 4 KB per tile, at the same index), and the same products with the
+// roles of the two operands swapped go to CBt, where lane L holds column
+// s = L%32 and the registers run over rows l. The backward takes sums of
+// these products that largely cancel, so they are not rounded to bf16.
+template <int N, bool BOTH = false>
 __device__ __forceinline__ void chunk_scores_tile(const uint16_t* __restrict__ Bm,
                                                   const uint16_t* __restrict__ Cm,
-                                                  uint16_t* __restrict__ CB, const int4* __restrict__ tab,
-                                                  int T, int G, int Q, int nc, long wid, int lane) {
+                                                  uint16_t* __restrict__ CB, uint16_t* __restrict__ CBt,
+                                                  const int4* __restrict__ tab, int T, int G, int Q, int nc,
+                                                  long wid, int lane) {
   const int lpc = Q / 32;
   const int ntile = lpc * (lpc + 1) / 2;
   const int l32 = lane & 31, g2 = lane >> 5;
@@ -78,35 +84,58 @@ __device__ __forceinline__ void chunk_scores_tile(const uint16_t* __restrict__ B
   u32x4 cf[N / 16], bf[N / 16];
 #pragma unroll
   for (int ks = 0; ks < N / 16; ++ks) {
-    cf[ks] = load16(cr + 16 * ks);
-    bf[ks] = load16(br + 16 * ks);
+    cf[ks] = keep_or_zero(tl < cr0.n, load16(cr + 16 * ks));
+    bf[ks] = keep_or_zero(ts < cr0.n, load16(br + 16 * ks));
   }
+  const size_t at = (((size_t(b) * nc + c) * G + g) * ntile + ti) * 1024 + size_t(lane) * 16;
+  auto store32 = [&](uint16_t* dstbase, const f32x16& acc) {
+    f32x4* dst = reinterpret_cast<f32x4*>(reinterpret_cast<float*>(dstbase) + at);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) dst[m] = f32x4{acc[4 * m], acc[4 * m + 1], acc[4 * m + 2], acc[4 * m + 3]};
+  };
+  auto store = [&](uint16_t* dstbase, const f32x16& acc) {
+    u32x4 lo, hi;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      lo[m] = pack_bf16x2(acc[2 * m], acc[2 * m + 1]);
+      hi[m] = pack_bf16x2(acc[8 + 2 * m], acc[8 + 2 * m + 1]);
+    }
+    u32x4* dst = reinterpret_cast<u32x4*>(dstbase + at);
+    dst[0] = lo;
+    dst[1] = hi;
+  };
   f32x16 acc = zero16();
 #pragma unroll
-  for (int ks = 0; ks < N / 16; ++ks)
-    acc = mfma32x32x16(keep_or_zero(ts < cr0.n, bf[ks]), keep_or_zero(tl < cr0.n, cf[ks]), acc);  // rows s, column l
-  u32x4 lo, hi;
+  for (int ks = 0; ks < N / 16; ++ks) acc = mfma32x32x16(bf[ks], cf[ks], acc);   // rows s, column l
+  if constexpr (BOTH) {
+    store32(CB, acc);
+    f32x16 acct = zero16();
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    lo[m] = pack_bf16x2(acc[2 * m], acc[2 * m + 1]);
-    hi[m] = pack_bf16x2(acc[8 + 2 * m], acc[8 + 2 * m + 1]);
+    for (int ks = 0; ks < N / 16; ++ks) acct = mfma32x32x16(cf[ks], bf[ks], acct);   // rows l, column s
+    store32(CBt, acct);
+  } else {
+    store(CB, acc);
   }
-  u32x4* dst = reinterpret_cast<u32x4*>(CB + (((size_t(b) * nc + c) * G + g) * ntile + ti) * 1024 +
-                                        size_t(lane) * 16);
-  dst[0] = lo;
-  dst[1] = hi;
 }
 
-template <int N, int P>
+// MODE 0: the forward launch described above. MODE 1: the same, with the C B^T
+// tiles also in the transposed orientation (CBt; the backward's
+// recomputation of the forward). MODE 2 (backward): the state gradient each
+// chunk contributes,
+//   dS_c^T[p][n] = sum_{l in chunk c} exp(Acs_l) dy_l[p] C_l[n],
+// the same product with x -> dy, B -> C and the per-token weight exp(Acs_l)
+// (the chunk's inclusive cumulative decay up to l): no score tiles, and Acs /
+// dt, recomputed here as in the forward, are not written again.
+template <int N, int P, int MODE>
 __global__ __launch_bounds__(kThreads) void chunk_state_mfma_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ Bm, const uint16_t* __restrict__ dt,
     const float* __restrict__ A, float* __restrict__ Acs, float* __restrict__ dtq, float* __restrict__ S,
-    const uint16_t* __restrict__ Cm, uint16_t* __restrict__ CB, const int4* __restrict__ tab, int T, int H,
-    int G, int Q, int nc, int nscore_wg, long ntiles) {
+    const uint16_t* __restrict__ Cm, uint16_t* __restrict__ CB, uint16_t* __restrict__ CBt,
+    const int4* __restrict__ tab, int T, int H, int G, int Q, int nc, int nscore_wg, long ntiles) {
   // the first nscore_wg work-groups compute C B^T tiles, one per wave
   if (int(blockIdx.x) < nscore_wg) {
     const long wid = long(blockIdx.x) * kWaves + (threadIdx.x >> 6);
-    if (wid < ntiles) chunk_scores_tile<N>(Bm, Cm, CB, tab, T, G, Q, nc, wid, threadIdx.x & 63);
+    if (wid < ntiles) chunk_scores_tile<N, MODE == 1>(Bm, Cm, CB, CBt, tab, T, G, Q, nc, wid, threadIdx.x & 63);
     return;                                     // no barrier on this path
   }
   constexpr int RBB = N / 8, RBW = P / 8;            // 16-byte chunks per row
@@ -150,15 +179,18 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma_kernel(
     __syncthreads();
     for (int w = 0; w < wave; ++w) v += sred[w];
     if (tid < Q) {
-      Acs[arow + tid] = v;
-      dtq[arow + tid] = d;
+      if constexpr (MODE != 2) {
+        Acs[arow + tid] = v;
+        dtq[arow + tid] = d;
+      }
       sacs[tid] = v;
       sdt[tid] = d;
     }
     __syncthreads();
   }
-  // w_s = exp(Acs_{Q-1} - Acs_s) * dt_s for the whole chunk
-  for (int i = tid; i < Q; i += kThreads) sw[i] = exp_fast(sacs[Q - 1] - sacs[i]) * sdt[i];
+  // w_s = exp(Acs_{Q-1} - Acs_s) * dt_s for the whole chunk (MODE 2: exp(Acs_s))
+  for (int i = tid; i < Q; i += kThreads)
+    sw[i] = MODE == 2 ? exp_fast(sacs[i]) : exp_fast(sacs[Q - 1] - sacs[i]) * sdt[i];
 
   // this thread's 16-byte chunks of a slice: B rows first, then x rows
   auto load_slice = [&](int s0, u32x4 (&v)[PER]) {
@@ -239,31 +271,44 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma_kernel(
   }
 }
 
-template <int N, int P>
+template <int N, int P, int MODE>
 hipError_t launch_np(const FwdShape& s, const void* x, const void* B, const void* C, const void* dt,
-                     const float* A, float* Acs, float* dtq, float* S, uint16_t* CB, const int4* tab, hipStream_t st,
-                     const StageEv& ev) {
+                     const float* A, float* Acs, float* dtq, float* S, uint16_t* CB, uint16_t* CBt, const int4* tab,
+                     hipStream_t st, const StageEv& ev) {
   const int lpc = s.Q / 32;
-  const long ntiles = long(s.b) * s.nc * s.G * (lpc * (lpc + 1) / 2);
+  const long ntiles = MODE == 2 ? 0 : long(s.b) * s.nc * s.G * (lpc * (lpc + 1) / 2);
   // score work-groups first (they start with the first wave of work-groups),
   // padded to a multiple of 8 so the chunk-state work-groups keep their XCD
   const long nscore = ((ntiles + kWaves - 1) / kWaves + 7) / 8 * 8;
   const long blocks = nscore + long(s.b) * s.nc * s.H;
-  hipExtLaunchKernelGGL((chunk_state_mfma_kernel<N, P>), dim3(unsigned(blocks)), dim3(kThreads), 0, st, ev.start, ev.stop, 0,
-                     static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(B),
-                     static_cast<const uint16_t*>(dt), A, Acs, dtq, S, static_cast<const uint16_t*>(C), CB,
-                     tab, s.T, s.H, s.G, s.Q, s.nc, int(nscore), ntiles);
+  hipExtLaunchKernelGGL((chunk_state_mfma_kernel<N, P, MODE>), dim3(unsigned(blocks)), dim3(kThreads), 0, st,
+                        ev.start, ev.stop, 0, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(B),
+                        static_cast<const uint16_t*>(dt), A, Acs, dtq, S, static_cast<const uint16_t*>(C), CB,
+                        CBt, tab, s.T, s.H, s.G, s.Q, s.nc, int(nscore), ntiles);
   return hipGetLastError();
 }
 
-template <int N>
+template <int N, int MODE>
 hipError_t launch_n(const FwdShape& s, const void* x, const void* B, const void* C, const void* dt,
-                    const float* A, float* Acs, float* dtq, float* S, uint16_t* CB, const int4* tab, hipStream_t st,
-                     const StageEv& ev) {
+                    const float* A, float* Acs, float* dtq, float* S, uint16_t* CB, uint16_t* CBt, const int4* tab,
+                    hipStream_t st, const StageEv& ev) {
   switch (s.P) {
-    case 32: return launch_np<N, 32>(s, x, B, C, dt, A, Acs, dtq, S, CB, tab, st, ev);
-    case 64: return launch_np<N, 64>(s, x, B, C, dt, A, Acs, dtq, S, CB, tab, st, ev);
-    case 128: return launch_np<N, 128>(s, x, B, C, dt, A, Acs, dtq, S, CB, tab, st, ev);
+    case 32: return launch_np<N, 32, MODE>(s, x, B, C, dt, A, Acs, dtq, S, CB, CBt, tab, st, ev);
+    case 64: return launch_np<N, 64, MODE>(s, x, B, C, dt, A, Acs, dtq, S, CB, CBt, tab, st, ev);
+    case 128: return launch_np<N, 128, MODE>(s, x, B, C, dt, A, Acs, dtq, S, CB, CBt, tab, st, ev);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int MODE>
+hipError_t launch_mode(const FwdShape& s, const void* x, const void* B, const void* C, const void* dt,
+                       const float* A, float* Acs, float* dtq, float* S, uint16_t* CB, uint16_t* CBt,
+                       const int4* tab, hipStream_t st, const StageEv& ev) {
+  switch (s.N) {
+    case 32: return launch_n<32, MODE>(s, x, B, C, dt, A, Acs, dtq, S, CB, CBt, tab, st, ev);
+    case 64: return launch_n<64, MODE>(s, x, B, C, dt, A, Acs, dtq, S, CB, CBt, tab, st, ev);
+    case 128: return launch_n<128, MODE>(s, x, B, C, dt, A, Acs, dtq, S, CB, CBt, tab, st, ev);
+    case 256: return launch_n<256, MODE>(s, x, B, C, dt, A, Acs, dtq, S, CB, CBt, tab, st, ev);
   }
   return hipErrorInvalidValue;
 }
@@ -274,13 +319,18 @@ hipError_t launch_chunk_state_mfma(const FwdShape& s, const void* x, const void*
                                    const void* dt, const float* A, float* Acs, float* dtq,
                                    float* S, uint16_t* CB, const int4* tab, hipStream_t st,
                                    const StageEv& ev) {
-  switch (s.N) {
-    case 32: return launch_n<32>(s, x, B, C, dt, A, Acs, dtq, S, CB, tab, st, ev);
-    case 64: return launch_n<64>(s, x, B, C, dt, A, Acs, dtq, S, CB, tab, st, ev);
-    case 128: return launch_n<128>(s, x, B, C, dt, A, Acs, dtq, S, CB, tab, st, ev);
-    case 256: return launch_n<256>(s, x, B, C, dt, A, Acs, dtq, S, CB, tab, st, ev);
-  }
-  return hipErrorInvalidValue;
+  return launch_mode<0>(s, x, B, C, dt, A, Acs, dtq, S, CB, nullptr, tab, st, ev);
+}
+
+hipError_t launch_chunk_state_mfma_bwd(const FwdShape& s, const void* x, const void* B, const void* C,
+                                       const void* dt, const float* A, float* Acs, float* dtq, float* S,
+                                       uint16_t* CB, uint16_t* CBt, hipStream_t st) {
+  return launch_mode<1>(s, x, B, C, dt, A, Acs, dtq, S, CB, CBt, nullptr, st, StageEv{});
+}
+
+hipError_t launch_chunk_dstates_mfma(const FwdShape& s, const void* dy, const void* C, const void* dt,
+                                     const float* A, float* dS, hipStream_t st) {
+  return launch_mode<2>(s, dy, C, nullptr, dt, A, nullptr, nullptr, dS, nullptr, nullptr, nullptr, st, StageEv{});
 }
 
 }  // namespace ssd

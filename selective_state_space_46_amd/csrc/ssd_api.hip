@@ -6,6 +6,7 @@
 #include <algorithm>
 #include <cmath>
 
+#include "ssd_backward.h"
 #include "ssd_epilogue.h"
 #include "ssd_internal.h"
 
@@ -76,6 +77,57 @@ bool grids_fit(const FwdShape& s, bool mfma) {
     worst = std::max(worst, 256.0 * bh * ((s.nc + cps - 1) / cps));
   }
   return worst < lim;
+}
+
+// Backward workspace (byte offsets, 256-byte aligned), chunk length
+// bwd_chunk_len(P, N):
+//   acs, dtq [b,H,nc,Q] f32; st [b,nc,H,P,N] f32 (chunk states, then the states
+//   entering each chunk); ds [b,nc,H,P,N] f32; gb [b,nc,H,P,N] and
+//   gbt [b,nc,H,N,P] bf16; cb, cbt [b,nc,G,ntile,64,16] f32 (C B^T tiles, both
+//   orientations);
+//   fin [b,H,N,P] f32; ghp [b,H,nc,nghp] f32;
+//   dbp, dcp [b,T,H,N] f32; dap, ddp [b,H,nc] f32
+struct BwdLayout {
+  size_t acs, dtq, st, ds, gb, gbt, cb, cbt, fin, ghp, dbp, dcp, dap, ddp, total;
+};
+
+BwdLayout bwd_layout(const FwdShape& s, int nghp) {
+  BwdLayout w;
+  const size_t row = size_t(s.b) * s.H * s.nc * s.Q * sizeof(float);
+  const size_t nst = size_t(s.b) * s.nc * s.H * s.N * s.P;
+  const size_t lpc = size_t(s.Q) / 32, ntile = lpc * (lpc + 1) / 2;
+  const size_t bhc = size_t(s.b) * s.H * s.nc;
+  size_t o = 0;
+  auto take = [&](size_t bytes) { const size_t at = o; o = align_up(o + bytes, 256); return at; };
+  w.acs = take(row);
+  w.dtq = take(row);
+  w.st = take(nst * sizeof(float));
+  w.ds = take(nst * sizeof(float));
+  w.gb = take(nst * sizeof(uint16_t));
+  w.gbt = take(nst * sizeof(uint16_t));
+  w.cb = take(size_t(s.b) * s.nc * s.G * ntile * 1024 * sizeof(float));
+  w.cbt = take(size_t(s.b) * s.nc * s.G * ntile * 1024 * sizeof(float));
+  w.fin = take(size_t(s.b) * s.H * s.N * s.P * sizeof(float));
+  w.ghp = take(bhc * nghp * sizeof(float));
+  w.dbp = take(size_t(s.b) * s.T * s.H * s.N * sizeof(float));
+  w.dcp = take(size_t(s.b) * s.T * s.H * s.N * sizeof(float));
+  w.dap = take(bhc * sizeof(float));
+  w.ddp = take(bhc * sizeof(float));
+  w.total = o;
+  return w;
+}
+
+// shapes the backward supports, and its launches within the grid limit
+// (bwd_chunk_kernel: 4 Q work-items per (b, c, h); the reduction: one per
+// 4 elements of dB)
+bool bwd_supported(int batch, int seqlen, int H, int P, int N, int G, ssd_dtype dtype, FwdShape& s) {
+  if (dtype != SSD_BF16) return false;
+  const int Qb = bwd_chunk_len(P, N);
+  if (Qb == 0) return false;
+  s = make_shape(batch, seqlen, H, P, N, G, Qb);
+  if (!use_mfma_path(s, dtype) || !grids_fit(s, true)) return false;
+  const double bch = double(s.b) * s.nc * s.H;
+  return 4.0 * Qb * bch < 4294967295.0 && double(batch) * seqlen * G * (N / 4) < 4294967295.0;
 }
 
 }  // namespace
@@ -405,6 +457,87 @@ ssd_status ssd_causal_conv1d_update(void* state, const void* x, const float* wei
   if (launch_causal_conv1d_update(dtype, state, x, weight, bias, out, batch, channels, kernel_width,
                                   activation, static_cast<hipStream_t>(stream)) != hipSuccess)
     return SSD_ERR_HIP;
+  return SSD_OK;
+}
+
+size_t ssd_chunk_scan_bwd_workspace(int batch, int seqlen, int nheads, int headdim, int dstate, int ngroups,
+                                    ssd_dtype dtype) {
+  if (!dtype_ok(dtype) || check_dims(batch, seqlen, nheads, headdim, dstate, ngroups) != SSD_OK) return 0;
+  FwdShape s;
+  if (!bwd_supported(batch, seqlen, nheads, headdim, dstate, ngroups, dtype, s)) return 0;
+  return bwd_layout(s, state_passing_bwd_partials(s)).total;
+}
+
+ssd_status ssd_chunk_scan_bwd(const void* x, const void* dt, const float* A, const void* B, const void* C,
+                              const float* D, const float* init_state, const void* dy, const float* dfinal,
+                              void* dx, void* ddt, float* dA, void* dB, void* dC, float* dD, float* dinit,
+                              int batch, int seqlen, int nheads, int headdim, int dstate, int ngroups,
+                              ssd_dtype dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!dtype_ok(dtype)) return SSD_ERR_DTYPE;
+  ssd_status st = check_dims(batch, seqlen, nheads, headdim, dstate, ngroups);
+  if (st != SSD_OK) return st;
+  FwdShape s;
+  if (!bwd_supported(batch, seqlen, nheads, headdim, dstate, ngroups, dtype, s)) return SSD_ERR_SHAPE;
+  if (!x || !dt || !A || !B || !C || !dy || !dx || !ddt || !dA || !dB || !dC) return SSD_ERR_NULL;
+  if (!workspace) return SSD_ERR_WORKSPACE;
+  const void* ptrs[] = {x, dt, A, B, C, D, init_state, dy, dfinal, dx, ddt, dA, dB, dC, dD, dinit, workspace};
+  for (const void* p : ptrs)
+    if (misaligned(p)) return SSD_ERR_ALIGN;
+  const int nghp = state_passing_bwd_partials(s);
+  const BwdLayout w = bwd_layout(s, nghp);
+  if (workspace_bytes < w.total) return SSD_ERR_WORKSPACE;
+
+  const size_t e = esize(dtype);
+  const size_t tok = size_t(batch) * seqlen;
+  const size_t xb = tok * nheads * headdim * e, dtb = tok * nheads * e, bcb = tok * ngroups * dstate * e;
+  const size_t hb = size_t(nheads) * sizeof(float);
+  const size_t stb = size_t(batch) * nheads * dstate * headdim * sizeof(float);
+  struct Buf {
+    const void* p;
+    size_t n;
+  };
+  const Buf ins[] = {{x, xb}, {dt, dtb}, {A, hb}, {B, bcb}, {C, bcb}, {D, hb}, {init_state, stb}, {dy, xb},
+                     {dfinal, stb}, {workspace, w.total}};
+  const Buf outs[] = {{dx, xb}, {ddt, dtb}, {dA, hb}, {dB, bcb}, {dC, bcb}, {dD, hb}, {dinit, stb}};
+  for (const Buf& o : outs) {
+    for (const Buf& in : ins)
+      if (overlaps(o.p, o.n, in.p, in.n)) return SSD_ERR_ALIAS;
+    for (const Buf& o2 : outs)
+      if (&o2 != &o && overlaps(o.p, o.n, o2.p, o2.n)) return SSD_ERR_ALIAS;
+  }
+
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  float* Acs = reinterpret_cast<float*>(ws + w.acs);
+  float* dtq = reinterpret_cast<float*>(ws + w.dtq);
+  float* Sst = reinterpret_cast<float*>(ws + w.st);
+  float* dS = reinterpret_cast<float*>(ws + w.ds);
+  uint16_t* Gb = reinterpret_cast<uint16_t*>(ws + w.gb);
+  uint16_t* GbT = reinterpret_cast<uint16_t*>(ws + w.gbt);
+  uint16_t* CBf = reinterpret_cast<uint16_t*>(ws + w.cb);
+  uint16_t* CBt = reinterpret_cast<uint16_t*>(ws + w.cbt);
+  float* fin = reinterpret_cast<float*>(ws + w.fin);
+  float* ghp = reinterpret_cast<float*>(ws + w.ghp);
+  float* dBp = reinterpret_cast<float*>(ws + w.dbp);
+  float* dCp = reinterpret_cast<float*>(ws + w.dcp);
+  float* dAp = reinterpret_cast<float*>(ws + w.dap);
+  float* dDp = reinterpret_cast<float*>(ws + w.ddp);
+
+  // recomputation: in-chunk decays, chunk states, then the states entering
+  // each chunk (fp32, over the chunk states) and the final state
+  if (launch_chunk_state_mfma_bwd(s, x, B, C, dt, A, Acs, dtq, Sst, CBf, CBt, hs) != hipSuccess)
+    return SSD_ERR_HIP;
+  if (launch_state_passing(s, Sst, nullptr, Acs, init_state, fin, hs) != hipSuccess) return SSD_ERR_HIP;
+  // what each chunk's outputs give the state entering it, then the reverse pass
+  if (launch_chunk_dstates_mfma(s, dy, C, dt, A, dS, hs) != hipSuccess) return SSD_ERR_HIP;
+  if (launch_state_passing_bwd(s, dS, Sst, Acs, dfinal, Gb, GbT, ghp, dinit, hs) != hipSuccess)
+    return SSD_ERR_HIP;
+  BwdArgs a;
+  a.x = x; a.B = B; a.C = C; a.dy = dy; a.Acs = Acs; a.dtq = dtq; a.CB = reinterpret_cast<const float*>(CBf); a.CBt = reinterpret_cast<const float*>(CBt); a.Hst = Sst; a.Gb = Gb; a.GbT = GbT;
+  a.ghp = ghp; a.nghp = nghp; a.A = A; a.D = D; a.dx = dx; a.ddt = ddt; a.dBp = dBp; a.dCp = dCp;
+  a.dAp = dAp; a.dDp = dDp;
+  if (launch_bwd_chunk(s, a, hs) != hipSuccess) return SSD_ERR_HIP;
+  if (launch_bwd_reduce(s, dBp, dCp, dAp, dDp, dB, dC, dA, dD, hs) != hipSuccess) return SSD_ERR_HIP;
   return SSD_OK;
 }
 

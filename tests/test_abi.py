@@ -23,7 +23,7 @@ def L():
 
 def declared_symbols():
     out = []
-    for h in ("ssd_api.h", "ssd_epilogue.h"):
+    for h in ("ssd_api.h", "ssd_epilogue.h", "ssd_backward.h"):
         text = open(os.path.join(ROOT, "include", h)).read()
         out += re.findall(r"SSD_API\s+[\w\s\*]*?\b(ssd_\w+)\s*\(", text)
     return out
@@ -34,7 +34,8 @@ def test_header_declares_the_entry_points():
                                        "ssd_chunk_scan_fwd_timed", "ssd_state_update",
                                        "ssd_status_string", "ssd_gated_rmsnorm",
                                        "ssd_causal_conv1d_fwd", "ssd_causal_conv1d_update",
-                                       "ssd_chunk_scan_fwd_varlen", "ssd_chunk_scan_fwd_varlen_workspace"}
+                                       "ssd_chunk_scan_fwd_varlen", "ssd_chunk_scan_fwd_varlen_workspace",
+                                       "ssd_chunk_scan_bwd", "ssd_chunk_scan_bwd_workspace"}
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -244,3 +245,40 @@ def test_varlen_workspace_and_errors(L):
     assert vl(L, y=FAKE) == 7                                    # y over x
     assert vl(L, fin=FAKE + 0x500000) == 7                       # final states over cu_seqlens
     assert vl(L, ws=FAKE + 0x300000) == 7                        # workspace over B
+
+
+def bw(L, **kw):
+    a = dict(x=FAKE, dt=FAKE + 0x100000, A=FAKE + 0x200000, B=FAKE + 0x300000, C=FAKE + 0x400000, D=None,
+             init=None, dy=FAKE + 0x500000, dfinal=None, dx=FAKE + 0x600000, ddt=FAKE + 0x700000,
+             dA=FAKE + 0x800000, dB=FAKE + 0x900000, dC=FAKE + 0xa00000, dD=None, dinit=None, b=1, T=300, H=2,
+             P=64, N=128, G=1, dtype=1, ws=FAKE + 0x1000000, nbytes=1 << 30, stream=None)
+    a.update(kw)
+    return L.ssd_chunk_scan_bwd(a["x"], a["dt"], a["A"], a["B"], a["C"], a["D"], a["init"], a["dy"], a["dfinal"],
+                                a["dx"], a["ddt"], a["dA"], a["dB"], a["dC"], a["dD"], a["dinit"], a["b"], a["T"],
+                                a["H"], a["P"], a["N"], a["G"], a["dtype"], a["ws"], a["nbytes"], a["stream"])
+
+
+def test_bwd_workspace_and_errors(L):
+    wsq = ssd.ssd_chunk_scan_bwd_workspace
+    assert wsq(1, 300, 2, 64, 128, 1, ssd.SSD_BF16) > 0
+    assert wsq(1, 300, 2, 64, 128, 1, ssd.SSD_F32) == 0       # bf16 matrix-core configuration only
+    assert wsq(1, 300, 2, 128, 256, 1, ssd.SSD_BF16) == 0     # tiles too large for one CU's LDS
+    assert wsq(1, 300, 2, 16, 16, 1, ssd.SSD_BF16) == 0
+    assert wsq(1, 300, 3, 64, 128, 2, ssd.SSD_BF16) == 0      # H % G
+    # per-head dB / dC partials grow with the heads
+    assert wsq(1, 300, 8, 64, 128, 1, ssd.SSD_BF16) > wsq(1, 300, 2, 64, 128, 1, ssd.SSD_BF16)
+    assert bw(L, dtype=3) == 3
+    assert bw(L, dtype=0) == 2
+    assert bw(L, P=128, N=256) == 2
+    assert bw(L, T=0) == 2
+    for k in ("x", "dt", "A", "B", "C", "dy", "dx", "ddt", "dA", "dB", "dC"):
+        assert bw(L, **{k: None}) == 1, k
+    assert bw(L, ws=None) == 5
+    assert bw(L, nbytes=1000) == 5
+    assert bw(L, dy=FAKE + 0x500008) == 8
+    assert bw(L, dx=FAKE) == 7                                    # dx over x
+    assert bw(L, dB=FAKE + 0x600000) == 7                         # dB over dx
+    assert bw(L, dD=FAKE + 0x200000) == 7                         # dD over A
+    assert bw(L, dinit=FAKE + 0x1000000) == 7                     # dinit over the workspace
+    assert bw(L, ws=FAKE + 0x500000) == 7                         # workspace over dy
+
