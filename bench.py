@@ -386,6 +386,52 @@ def bench_varlen(hip, vw, steps=20, warmup=3):
             "ms_per_call": round(ms, 5), "tokens_per_s": round(vw.total / (ms * 1e-3), 1)}
 
 
+def bench_backward(hip, w, steps=10, warmup=3):
+    """The backward pass on a forward workload: one ssd_chunk_scan_bwd call
+    (recomputation included) per step, upstream dy ~ N(0, 1) in bf16, timed
+    with HIP events around `steps` calls on one stream. Algorithmic bytes: its
+    minimal I/O, every input and output element once (x, dy, B, C, dt, A, D
+    and init read; dx, ddt, dB, dC, dA, dD and dinit written)."""
+    import torch
+    import selective_state_space_46_amd as ssd
+    stream = torch.cuda.current_stream().cuda_stream
+    inp = workloads.make_fwd_inputs(w)
+    x, dt, B, C = (to_dev(inp[k], w.dtype) for k in ("x", "dt", "B", "C"))
+    A, D = to_dev(inp["A"], "f32"), to_dev(inp["D"], "f32")
+    init = to_dev(inp["init"], "f32") if inp["init"] is not None else None
+    rng = np.random.default_rng(w.seed + 100)
+    dy = to_dev(workloads.round_to_bf16(rng.standard_normal(inp["x"].shape, dtype=np.float32)), w.dtype)
+    code = 1 if w.dtype == "bf16" else 0
+    need = ssd.ssd_chunk_scan_bwd_workspace(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, code)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    out = ssd.ssd_chunk_scan_bwd(x, dt, A, B, C, D, init, dy, None, workspace=ws, stream=stream)
+
+    def call():
+        ssd.ssd_chunk_scan_bwd(x, dt, A, B, C, D, init, dy, None, out=out, workspace=ws, stream=stream)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    a, b = hip.event(), hip.event()
+    hip.record(a, stream)
+    for _ in range(steps):
+        call()
+    hip.record(b, stream)
+    torch.cuda.synchronize()
+    ms = hip.ms(a, b) / steps
+    hip.destroy(a)
+    hip.destroy(b)
+    e = 2 if w.dtype == "bf16" else 4
+    tok = w.batch * w.seqlen
+    st = w.batch * w.nheads * w.dstate * w.headdim * 4
+    nbytes = (3 * tok * w.nheads * w.headdim * e + 4 * tok * w.ngroups * w.dstate * e + 2 * tok * w.nheads * e
+              + 4 * w.nheads * 4 + (2 * st if init is not None else st))
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"workload": w.name, "ms_per_call": round(ms, 5), "tokens_per_s": round(tok / (ms * 1e-3), 1),
+            "alg_bytes": nbytes, "GB_per_s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+            "workspace_bytes": need}
+
+
 def traffic_probe(w):
     """Three forward calls, then three copies of a 256 MiB buffer: a plain
     copy kernel that reads and writes exactly 256 MiB, against which the
@@ -500,6 +546,10 @@ def main():
                                "stage_ms": {k: round(v, 4) for k, v in rr["stage_ms"].items()}}
             log(f"[bench]   {rr['ms_per_step']:.4f} ms/step")
         out["other_workloads"] = others
+        if w.dtype == "bf16":
+            log(f"[bench] backward {w.name}")
+            out["backward"] = bench_backward(hip, w)
+            log(f"[bench]   {out['backward']}")
         log(f"[bench] packed sequences {workloads.VARLEN_130M.name}")
         out["varlen"] = bench_varlen(hip, workloads.VARLEN_130M)
         log(f"[bench]   {out['varlen']}")

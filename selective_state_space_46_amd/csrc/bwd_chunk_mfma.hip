@@ -11,34 +11,38 @@
 //   dx_s  = sum_{l>=s} (C_l . B_s) e_ls dt_s dy_l + dt_s e_{Q-1,s} G_c^T B_s + D dy_s
 //   dB'_s = sum_{l>=s} e_ls Sxy_sl C_l + e_{Q-1,s} G_c x_s          (dB_s = dt_s dB'_s)
 //   dC_l  = sum_{s<=l} e_ls dt_s Sxy_sl B_s + exp(Acs_l) H_c dy_l
-// The decay exponents get (the row and column sums of the quadratic form)
+// The decay exponents get
 //   dAcs_t = C_t . dC_t - dt_t (B_t . dB'_t) + [t = Q-1] <G_c, H_{c+1}>
-// where, with H_{c+1} = exp(Acs_{Q-1}) H_c + sum_s e_{Q-1,s} dt_s B_s x_s^T,
-//   <G_c, H_{c+1}> = exp(Acs_{Q-1}) <G_c, H_c> + sum_s dt_s B_s . (e_{Q-1,s} G_c x_s)
-// is formed from the same per-token state dots that the second term
-// subtracts, so those cancel exactly in the reverse sum.
-// whose in-chunk parts are the row and column sums of W_ls = (C_l . B_s) e_ls
-// Sxy_sl (dt_s W_ls summed over s for C_l . dC_l, W_ls over l for B_s . dB'_s).
-// In the reverse cumulative sum below most of those cancel (the diagonal
-// exactly), so both are taken in fp32 from the same fp32 products (fp32 C B^T
-// tiles from the recomputation), never from the bf16 operands of the dB' / dC
-// contractions; likewise H_c enters the state term of dC as a bf16 pair
-// hi + lo, so that C_l . dC_l keeps fp32 accuracy.
 // and, since Acs_t = A sum_{k<=t} dt_k,
 //   ddt_t = B_t . dB'_t + A R_t,  dA = sum_t dt_t R_t,  R_t = sum_{t'>=t} dAcs_t'.
-// dB and dC of one head go out as fp32 partials; a later kernel sums the
-// heads of each group (and dA, dD over the chunks) in a fixed order.
 //
-// Work-group: one (batch, chunk, head), 2 NB waves for NB 32-token blocks
-// (Q = 32 NB). Wave i < NB owns block i as the s side (dx, dB': tiles of
-// l-blocks j >= i); wave NB + i owns it as the l side (dC: tiles of s-blocks
-// j <= i); every wave sees NB + 1 tiles' worth of work. The s side works in
-// tiles whose lanes are tokens s (registers over rows l), so its two
-// contractions over l take the tile as the B operand under the k permutation
-// the A operand reproduces with transposed LDS reads (as chunk_scan does);
-// the l side mirrors it with lanes = l. C B^T comes from the recomputation,
-// already in the s-lane orientation. Every decay factor has a non-positive
-// exponent (off the diagonal split at a block boundary, on it masked).
+// Precision of R. The in-chunk parts of C_t . dC_t and B_t . dB'_t are the
+// row and column sums of W_ls = (C_l . B_s) e_ls Sxy_sl (dt_s W_ls over s;
+// W_ls over l), which cancel in R except on the cross block s < t <= l, so
+// both are taken in fp32 from the same fp32 products (fp32 C B^T tiles from
+// the recomputation), never from the bf16 operands of the dB / dC products.
+// Likewise H_c enters the dot C_l . (state term of dC_l) as a bf16 pair
+// hi + lo. And with H_{c+1} = exp(Acs_{Q-1}) H_c + sum_s e_{Q-1,s} dt_s B_s x_s^T,
+//   <G_c, H_{c+1}> = exp(Acs_{Q-1}) <G_c, H_c> + sum_s dt_s B_s . (e_{Q-1,s} G_c x_s)
+// is formed from the same per-token state dots that the second term of
+// dAcs subtracts, so those cancel exactly as well.
+//
+// dB and dC sum over the heads of a group: a work-group takes one (batch,
+// chunk, group) and a slice of its heads, one head after the other, and keeps
+// the sums in its accumulators (dt_s and the decays folded into the bf16
+// operands), writing bf16 when it holds the whole group, else an fp32 partial
+// per slice that a last kernel adds in a fixed order (as dA, dD over chunks).
+//
+// Three kernels: the s side (dx, dB; NB waves, wave i owns 32-token block i
+// as the tokens s and the tiles of l-blocks j >= i), the l side (dC; wave i
+// owns block i as the tokens l and the tiles of s-blocks j <= i) and a last
+// one per (batch, chunk, head) that turns the per-token dots of both into
+// ddt, dA and dD. The s side works in tiles whose lanes are tokens s
+// (registers over rows l), so its two contractions over l take the tile as
+// the B operand under the k permutation the A operand reproduces with
+// transposed LDS reads (as chunk_scan does); the l side mirrors it with
+// lanes = l. Every decay factor has a non-positive exponent (off the
+// diagonal split at a block boundary, on it masked).
 #include <type_traits>
 
 #include "mfma_util.h"
@@ -48,77 +52,82 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+// Rows r of a token-major tensor (row stride `stride` elements, `len`
+// elements from `col0`) of the chunk into a swizzled natural LDS tile, rows
+// past the valid tokens as zeros. All threads of the work-group take part.
+template <int RB, int kThr>
+__device__ __forceinline__ void stage_rows(uint16_t* tile, const uint16_t* __restrict__ src, long r0, int nv,
+                                           int rows, size_t stride, size_t col0, int tid) {
+  for (int e = tid; e < rows * RB; e += kThr) {
+    const int r = e / RB, cc = e % RB;
+    const u32x4 v = load16(src + (r0 + min(r, nv - 1)) * stride + col0 + 8 * cc);
+    *reinterpret_cast<u32x4*>(&tile[lds_off<RB>(r, 8 * cc)]) = keep_or_zero(r < nv, v);
+  }
+}
+
+// The C B^T tiles of one (batch, chunk, group) (ntile x 1024 fp32, lane L's 16
+// values contiguous) into LDS as [tile][4][64 lanes] f32x4, so that lane L
+// reads its 4 quads at consecutive 16-byte slots (no bank conflicts).
+template <int ntile, int kThr>
+__device__ __forceinline__ void stage_tiles(f32x4* sT, const float* __restrict__ src, int tid) {
+  for (int e = tid; e < ntile * 256; e += kThr) {
+    const int t = e / 256, L = (e / 4) % 64, q = e % 4;
+    sT[(t * 4 + q) * 64 + L] = reinterpret_cast<const f32x4*>(src)[e];
+  }
+}
+
+// 16 bytes (8 consecutive columns from col) of row r of a swizzled natural tile
+template <int RB>
+__device__ __forceinline__ u32x4 lds_row16(const uint16_t* tile, int r, int col) {
+  return *reinterpret_cast<const u32x4*>(&tile[lds_off<RB>(r, col)]);
+}
+template <int RB>
+__device__ __forceinline__ u32x2 lds_row8(const uint16_t* tile, int r, int col) {
+  return *reinterpret_cast<const u32x2*>(&tile[lds_off<RB>(r, col)]);
+}
+
+// s side: dx, dB (summed over the work-group's heads) and, per head and
+// token s, B_s . dB'_s (sds), dt_s B_s . (e_{Q-1,s} G_c x_s) (sdst) and
+// dy_s . x_s (sdd), for the last kernel. Wave i owns tokens s of block i and
+// the tiles of l-blocks j >= i. Every operand comes from LDS: B, C and the
+// C B^T tiles once per work-group, and per head x, dy and G_c, loaded by all
+// threads at once.
 template <int N, int P, int NB>
-__global__ __launch_bounds__(128 * NB) void bwd_chunk_kernel(
+__global__ __launch_bounds__(64 * NB) void bwd_s_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ Bm, const uint16_t* __restrict__ Cm,
     const uint16_t* __restrict__ dy, const float* __restrict__ Acs, const float* __restrict__ dtq,
-    const float* __restrict__ CBf, const float* __restrict__ CBt, const float* __restrict__ Hst,
-    const uint16_t* __restrict__ Gb, const uint16_t* __restrict__ GbT,
-    const float* __restrict__ ghp, const float* __restrict__ A, const float* __restrict__ D,
-    uint16_t* __restrict__ dx, uint16_t* __restrict__ ddt, float* __restrict__ dBp, float* __restrict__ dCp,
-    float* __restrict__ dAp, float* __restrict__ dDp, int T, int H, int G, int nc, int nghp) {
+    const float* __restrict__ CBt, const uint16_t* __restrict__ Gb, const float* __restrict__ D,
+    uint16_t* __restrict__ dx, uint16_t* __restrict__ dBo, float* __restrict__ dBs, float* __restrict__ gsds,
+    float* __restrict__ gsdst, float* __restrict__ gsdd, int T, int H, int G, int nc, int nslice) {
   constexpr int Q = 32 * NB;
-  constexpr int kThr = 128 * NB;
+  constexpr int kThr = 64 * NB;
   constexpr int RBP = P / 8, RBN = N / 8;   // 16-byte chunks per row
   constexpr int ntile = NB * (NB + 1) / 2;
-  __shared__ __attribute__((aligned(16))) uint16_t sDY[Q * P];
   __shared__ __attribute__((aligned(16))) uint16_t sB[Q * N];
   __shared__ __attribute__((aligned(16))) uint16_t sC[Q * N];
-  __shared__ __attribute__((aligned(16))) uint16_t sH[P * N];
-  __shared__ __attribute__((aligned(16))) uint16_t sHlo[P * N];   // H_c - bf16(H_c), rounded
-  __shared__ float sA2[Q], sdt[Q], sF[Q], sL[Q], sEL[Q], sEl[Q];
-  __shared__ float sds[Q], sdl[Q], sdd[Q], sdst[Q];
-  __shared__ float sred[2 * NB][2];
+  __shared__ __attribute__((aligned(16))) uint16_t sX[Q * P];
+  __shared__ __attribute__((aligned(16))) uint16_t sDY[Q * P];
+  __shared__ __attribute__((aligned(16))) uint16_t sG[P * N];     // G_c, rows p
+  __shared__ f32x4 sT[ntile * 4 * 64];                            // C B^T tiles, lanes = s
+  __shared__ float sA2[Q], sdt[Q], sEL[Q], sEl[Q];
 
   const int id = xcd_swizzle(blockIdx.x, gridDim.x);
-  const int h = id % H;
-  const int bc = id / H;
+  const int sl = id % nslice;
+  const int rest = id / nslice;
+  const int g = rest % G;
+  const int bc = rest / G;
   const int c = bc % nc, b = bc / nc;
-  const int g = h / (H / G);
+  const int hps = H / G / nslice;               // heads of this work-group
+  const int h0 = g * (H / G) + sl * hps;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = wave_id();
   const int l32 = lane & 31, g2 = lane >> 5;
   const long r0 = long(b) * T + long(c) * Q;        // first token row of the chunk
   const int nv = min(Q, T - c * Q);                 // valid tokens
-  const size_t arow = ((size_t(b) * H + h) * nc + c) * Q;
-  const size_t sbase = ((size_t(b) * nc + c) * H + h) * size_t(P) * N;
 
-  // ---- tables (exponents in base 2)
-  for (int t = tid; t < Q; t += kThr) {
-    const float a2 = Acs[arow + t] * kLog2e, d = dtq[arow + t];
-    sA2[t] = a2;
-    sdt[t] = d;
-    sF[t] = __builtin_amdgcn_exp2f(Acs[arow + (t | 31)] * kLog2e - a2) * d;   // <= dt
-    sL[t] = __builtin_amdgcn_logf(d) - a2;                                     // -inf where dt = 0
-    sEL[t] = __builtin_amdgcn_exp2f(a2 - Acs[arow + (t & ~31)] * kLog2e);    // <= 1
-    sEl[t] = __builtin_amdgcn_exp2f(Acs[arow + Q - 1] * kLog2e - a2);         // <= 1
-  }
-  // ---- natural row-major tiles: dy, B, C (rows past the chunk are zeros), H_c (hi and lo)
-  for (int e = tid; e < Q * RBP; e += kThr) {
-    const int r = e / RBP, cc = e % RBP;
-    const u32x4 v = load16(dy + ((r0 + min(r, nv - 1)) * H + h) * size_t(P) + 8 * cc);
-    *reinterpret_cast<u32x4*>(&sDY[lds_off<RBP>(r, 8 * cc)]) = keep_or_zero(r < nv, v);
-  }
-  for (int e = tid; e < Q * RBN; e += kThr) {
-    const int r = e / RBN, cc = e % RBN;
-    const size_t ro = ((r0 + min(r, nv - 1)) * G + g) * size_t(N) + 8 * cc;
-    *reinterpret_cast<u32x4*>(&sB[lds_off<RBN>(r, 8 * cc)]) = keep_or_zero(r < nv, load16(Bm + ro));
-    *reinterpret_cast<u32x4*>(&sC[lds_off<RBN>(r, 8 * cc)]) = keep_or_zero(r < nv, load16(Cm + ro));
-  }
-  for (int e = tid; e < P * RBN; e += kThr) {
-    const int r = e / RBN, cc = e % RBN;
-    const f32x4 h0 = *reinterpret_cast<const f32x4*>(Hst + sbase + size_t(r) * N + 8 * cc);
-    const f32x4 h1 = *reinterpret_cast<const f32x4*>(Hst + sbase + size_t(r) * N + 8 * cc + 4);
-    const u32x4 hi = u32x4{pack_bf16x2(h0[0], h0[1]), pack_bf16x2(h0[2], h0[3]), pack_bf16x2(h1[0], h1[1]),
-                           pack_bf16x2(h1[2], h1[3])};
-    const u32x4 lo = u32x4{pack_bf16x2(h0[0] - bf16_lo(hi[0]), h0[1] - bf16_hi(hi[0])),
-                           pack_bf16x2(h0[2] - bf16_lo(hi[1]), h0[3] - bf16_hi(hi[1])),
-                           pack_bf16x2(h1[0] - bf16_lo(hi[2]), h1[1] - bf16_hi(hi[2])),
-                           pack_bf16x2(h1[2] - bf16_lo(hi[3]), h1[3] - bf16_hi(hi[3]))};
-    *reinterpret_cast<u32x4*>(&sH[lds_off<RBN>(r, 8 * cc)]) = hi;
-    *reinterpret_cast<u32x4*>(&sHlo[lds_off<RBN>(r, 8 * cc)]) = lo;
-  }
-  __syncthreads();
+  stage_rows<RBN, kThr>(sB, Bm, r0, nv, Q, size_t(G) * N, size_t(g) * N, tid);
+  stage_rows<RBN, kThr>(sC, Cm, r0, nv, Q, size_t(G) * N, size_t(g) * N, tid);
+  stage_tiles<ntile, kThr>(sT, CBt + ((size_t(b) * nc + c) * G + g) * ntile * 1024, tid);
 
   // lane constants of the permuted transposed reads (k = rows of a 32-row
   // block, in the order of the accumulator rows), per 32-column block
@@ -131,75 +140,92 @@ __global__ __launch_bounds__(128 * NB) void bwd_chunk_kernel(
   using RBPc = std::integral_constant<int, RBP>;
   using RBNc = std::integral_constant<int, RBN>;
 
-  const float Ah = A[h];
-  const float Dh = D ? D[h] : 0.f;
+  const int i = wave;
+  const int s = 32 * i + l32;
+  const bool sok = s < nv;
+  const long srow = r0 + min(s, nv - 1);
+  const int jend = min(NB, (nv + 31) / 32);   // l-blocks past the valid tokens add nothing
 
-  if (wave < NB) {
-    // ================= s side: block i as the tokens s
-    const int i = wave;
-    const int s = 32 * i + l32;
-    const bool sok = s < nv;
-    const long srow = r0 + min(s, nv - 1);
+  // dB of this wave's 32 tokens summed over the work-group's heads:
+  // transposed, rows n, lane = s
+  f32x16 accT[N / 32];
+#pragma unroll
+  for (int nt = 0; nt < N / 32; ++nt) accT[nt] = zero16();
+
+  for (int hk = 0; hk < hps; ++hk) {
+    const int h = h0 + hk;
+    const size_t arow = ((size_t(b) * H + h) * nc + c) * Q;
+    const size_t sbase = ((size_t(b) * nc + c) * H + h) * size_t(P) * N;
+    __syncthreads();   // the previous head's tiles and tables are consumed
+    for (int t = tid; t < Q; t += kThr) {
+      const float a2 = Acs[arow + t] * kLog2e;
+      sA2[t] = a2;
+      sdt[t] = dtq[arow + t];
+      sEL[t] = __builtin_amdgcn_exp2f(a2 - Acs[arow + (t & ~31)] * kLog2e);    // <= 1
+      sEl[t] = __builtin_amdgcn_exp2f(Acs[arow + Q - 1] * kLog2e - a2);         // <= 1
+    }
+    stage_rows<RBP, kThr>(sX, x, r0, nv, Q, size_t(H) * P, size_t(h) * P, tid);
+    stage_rows<RBP, kThr>(sDY, dy, r0, nv, Q, size_t(H) * P, size_t(h) * P, tid);
+    for (int e = tid; e < P * RBN; e += kThr) {
+      const int r = e / RBN, cc = e % RBN;
+      *reinterpret_cast<u32x4*>(&sG[lds_off<RBN>(r, 8 * cc)]) = load16(Gb + sbase + size_t(r) * N + 8 * cc);
+    }
+    __syncthreads();
+
     const float dts = sdt[s], a2s = sA2[s], els = sEl[s];
     u32x4 xr[P / 16];
 #pragma unroll
-    for (int kk = 0; kk < P / 16; ++kk)
-      xr[kk] = keep_or_zero(sok, load16(x + (srow * H + h) * size_t(P) + 16 * kk + 8 * g2));
+    for (int kk = 0; kk < P / 16; ++kk) xr[kk] = lds_row16<RBP>(sX, s, 16 * kk + 8 * g2);
 
-    f32x16 adx[P / 32], adb[N / 32];
-    // state terms: dx^T(p, s) = sum_n G(n, p) B_s[n];  dB'^T(n, s) = sum_p G(n, p) x_s[p]
+    // state terms. dx^T(p, s) = e_{Q-1,s} dt_s sum_n G(n, p) B_s[n]; the same
+    // product dotted with x_s is this head's B_s . (e_{Q-1,s} G_c x_s)
+    f32x16 adx[P / 32];
 #pragma unroll
     for (int pt = 0; pt < P / 32; ++pt) {
       adx[pt] = zero16();
 #pragma unroll
-      for (int kk = 0; kk < N / 16; ++kk) {
-        const u32x4 ga = load16(Gb + sbase + size_t(32 * pt + l32) * N + 16 * kk + 8 * g2);
-        const u32x4 bs = keep_or_zero(sok, load16(Bm + (srow * G + g) * size_t(N) + 16 * kk + 8 * g2));
-        adx[pt] = mfma32x32x16(ga, bs, adx[pt]);
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) adx[pt][r] *= dts * els;
+      for (int kk = 0; kk < N / 16; ++kk)
+        adx[pt] = mfma32x32x16(lds_row16<RBN>(sG, 32 * pt + l32, 16 * kk + 8 * g2),
+                               lds_row16<RBN>(sB, s, 16 * kk + 8 * g2), adx[pt]);
     }
+    float bdst = 0.f;
 #pragma unroll
-    for (int nt = 0; nt < N / 32; ++nt) {
-      adb[nt] = zero16();
-#pragma unroll
-      for (int kk = 0; kk < P / 16; ++kk) {
-        const u32x4 ga = load16(GbT + sbase + size_t(32 * nt + l32) * P + 16 * kk + 8 * g2);   // G rows n
-        adb[nt] = mfma32x32x16(ga, xr[kk], adb[nt]);
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) adb[nt][r] *= els;
-    }
-    // B_s . dB'_s of the state term (rows n = 32 nt + 8 q + 4 g2 + 0..3 of lane s)
-    float bd = 0.f;
-#pragma unroll
-    for (int nt = 0; nt < N / 32; ++nt)
+    for (int pt = 0; pt < P / 32; ++pt)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int n = 32 * nt + 8 * q + 4 * g2;
-        const u32x2 bv = *reinterpret_cast<const u32x2*>(Bm + (srow * G + g) * size_t(N) + n);
-        bd += adb[nt][4 * q] * bf16_lo(bv[0]) + adb[nt][4 * q + 1] * bf16_hi(bv[0]) +
-              adb[nt][4 * q + 2] * bf16_lo(bv[1]) + adb[nt][4 * q + 3] * bf16_hi(bv[1]);
+        const u32x2 xv = lds_row8<RBP>(sX, s, 32 * pt + 8 * q + 4 * g2);
+        bdst += adx[pt][4 * q] * bf16_lo(xv[0]) + adx[pt][4 * q + 1] * bf16_hi(xv[0]) +
+                adx[pt][4 * q + 2] * bf16_lo(xv[1]) + adx[pt][4 * q + 3] * bf16_hi(xv[1]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) adx[pt][4 * q + r] *= dts * els;
       }
-    const float bdst = bd + __shfl_xor(bd, 32, 64);   // the state term's B_s . dB'_s
+    bdst = els * (bdst + __shfl_xor(bdst, 32, 64));
+    // dB^T(n, s) += sum_p G(n, p) (dt_s e_{Q-1,s} x_s[p])   (G rows n: transposed reads)
+    {
+      u32x4 xs[P / 16];
+      const float f = dts * els;
+#pragma unroll
+      for (int kk = 0; kk < P / 16; ++kk)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) xs[kk][w] = pack_bf16x2(bf16_lo(xr[kk][w]) * f, bf16_hi(xr[kk][w]) * f);
+#pragma unroll
+      for (int nt = 0; nt < N / 32; ++nt)
+#pragma unroll
+        for (int kk = 0; kk < P / 16; ++kk) {
+          const int kb = 16 * kk + 8 * g2;
+          accT[nt] = mfma32x32x16(frag_tr<RBN>(sG, kb, kb + 4, 32 * nt, lane), xs[kk], accT[nt]);
+        }
+    }
 
-    // intra-chunk terms, one 32 x 32 tile (rows l of block j, lanes s) at a time;
-    // l-blocks wholly past the valid tokens add nothing (dy = 0 there) and
-    // their C B^T tiles are never computed
-    const int jend = min(NB, (nv + 31) / 32);
+    // intra-chunk terms, one 32 x 32 tile (rows l of block j, lanes s) at a time
+    float bd = 0.f;                              // this head's sum_l W_ls
     for (int j = i; j < jend; ++j) {
-      const int lrow_l = 32 * j + l32;
+      const f32x4* tsrc = sT + (j * (j + 1) / 2 + i) * 256 + lane;
+      const f32x4 cb4[4] = {tsrc[0], tsrc[64], tsrc[128], tsrc[192]};   // C_l . B_s, rows l in accumulator order
       f32x16 accS = zero16();
 #pragma unroll
-      for (int kk = 0; kk < P / 16; ++kk) {
-        const u32x4 dyl = keep_or_zero(lrow_l < nv, load16(dy + ((r0 + min(lrow_l, nv - 1)) * H + h) * size_t(P) +
-                                                         16 * kk + 8 * g2));
-        accS = mfma32x32x16(dyl, xr[kk], accS);                         // Sxy^T: rows l, lane s
-      }
-      const f32x4* tsrc = reinterpret_cast<const f32x4*>(
-          CBt + (((size_t(b) * nc + c) * G + g) * ntile + size_t(j) * (j + 1) / 2 + i) * 1024 + size_t(lane) * 16);
-      const f32x4 cb4[4] = {tsrc[0], tsrc[1], tsrc[2], tsrc[3]};   // C_l . B_s, rows l in accumulator order
+      for (int kk = 0; kk < P / 16; ++kk)
+        accS = mfma32x32x16(lds_row16<RBP>(sDY, 32 * j + l32, 16 * kk + 8 * g2), xr[kk], accS);   // Sxy^T
       const bool diag = j == i;
       const float lf = diag ? 0.f : __builtin_amdgcn_exp2f(sA2[32 * j] - a2s);
       uint32_t zw[8], mw[8];
@@ -220,7 +246,7 @@ __global__ __launch_bounds__(128 * NB) void bwd_chunk_kernel(
         }
         const float z0 = e2[0] * accS[2 * m], z1 = e2[1] * accS[2 * m + 1];
         bd += z0 * cb_lo + z1 * cb_hi;                              // column sum of W
-        zw[m] = pack_bf16x2(z0, z1);
+        zw[m] = pack_bf16x2(dts * z0, dts * z1);
         mw[m] = pack_bf16x2(e2[0] * dts * cb_lo, e2[1] * dts * cb_hi);
       }
       const u32x4 zga = u32x4{zw[0], zw[1], zw[2], zw[3]}, zgb = u32x4{zw[4], zw[5], zw[6], zw[7]};
@@ -235,113 +261,223 @@ __global__ __launch_bounds__(128 * NB) void bwd_chunk_kernel(
         adx[pt] = mfma32x32x16(u32x4{a0[0], a0[1], a1[0], a1[1]}, mga, adx[pt]);
         adx[pt] = mfma32x32x16(u32x4{b0[0], b0[1], b1[0], b1[1]}, mgb, adx[pt]);
       }
-      // dB'^T(n, s) += sum_l C^T(n, l) Z(l, s)
+      // dB^T(n, s) += sum_l C^T(n, l) dt_s Z(l, s)
       const int joN = 32 * j * N;
 #pragma unroll
       for (int nt = 0; nt < N / 32; ++nt) {
         const int o0 = toff(RBNc{}, 0, nt) + joN, o1 = toff(RBNc{}, 1, nt) + joN;
         const u32x2 a0 = lds_read_tr16(sC, o0), a1 = lds_read_tr16(sC, o1);
         const u32x2 b0 = lds_read_tr16(sC, o0 + 16 * N), b1 = lds_read_tr16(sC, o1 + 16 * N);
-        adb[nt] = mfma32x32x16(u32x4{a0[0], a0[1], a1[0], a1[1]}, zga, adb[nt]);
-        adb[nt] = mfma32x32x16(u32x4{b0[0], b0[1], b1[0], b1[1]}, zgb, adb[nt]);
+        accT[nt] = mfma32x32x16(u32x4{a0[0], a0[1], a1[0], a1[1]}, zga, accT[nt]);
+        accT[nt] = mfma32x32x16(u32x4{b0[0], b0[1], b1[0], b1[1]}, zgb, accT[nt]);
       }
     }
 
     // dx = ... + D dy (rows p = 32 pt + 8 q + 4 g2 + 0..3 of lane s), stored as bf16
+    const float Dh = D ? D[h] : 0.f;
 #pragma unroll
     for (int pt = 0; pt < P / 32; ++pt)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int p = 32 * pt + 8 * q + 4 * g2;
-        const u32x2 dv = *reinterpret_cast<const u32x2*>(dy + (srow * H + h) * size_t(P) + p);
+        const u32x2 dv = lds_row8<RBP>(sDY, s, p);
         const float v0 = adx[pt][4 * q] + Dh * bf16_lo(dv[0]), v1 = adx[pt][4 * q + 1] + Dh * bf16_hi(dv[0]);
         const float v2 = adx[pt][4 * q + 2] + Dh * bf16_lo(dv[1]), v3 = adx[pt][4 * q + 3] + Dh * bf16_hi(dv[1]);
         if (sok)
           *reinterpret_cast<u32x2*>(dx + (srow * H + h) * size_t(P) + p) =
               u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
       }
-    // dB_s = dt_s dB'_s as an fp32 partial of this head
-#pragma unroll
-    for (int nt = 0; nt < N / 32; ++nt)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int n = 32 * nt + 8 * q + 4 * g2;
-        if (sok)
-          *reinterpret_cast<f32x4*>(dBp + (srow * H + h) * size_t(N) + n) =
-              f32x4{dts * adb[nt][4 * q], dts * adb[nt][4 * q + 1], dts * adb[nt][4 * q + 2],
-                    dts * adb[nt][4 * q + 3]};
-      }
     bd += __shfl_xor(bd, 32, 64);
     // dy_s . x_s (for dD)
     float dd = 0.f;
 #pragma unroll
     for (int kk = 0; kk < P / 16; ++kk) {
-      const u32x4 dv = keep_or_zero(sok, load16(dy + (srow * H + h) * size_t(P) + 16 * kk + 8 * g2));
+      const u32x4 dv = lds_row16<RBP>(sDY, s, 16 * kk + 8 * g2);
 #pragma unroll
       for (int w = 0; w < 4; ++w)
         dd += bf16_lo(dv[w]) * bf16_lo(xr[kk][w]) + bf16_hi(dv[w]) * bf16_hi(xr[kk][w]);
     }
     dd += __shfl_xor(dd, 32, 64);
     if (g2 == 0) {
-      sds[s] = sok ? bd : 0.f;
-      sdst[s] = sok ? dts * bdst : 0.f;
-      sdd[s] = dd;
+      gsds[arow + s] = sok ? bd + bdst : 0.f;     // B_s . dB'_s of this head
+      gsdst[arow + s] = sok ? dts * bdst : 0.f;
+      gsdd[arow + s] = dd;
     }
-  } else {
-    // ================= l side: block i as the tokens l
-    const int i = wave - NB;
-    const int l = 32 * i + l32;
-    const bool lok = l < nv;
-    const long lrow = r0 + min(l, nv - 1);
-    const float a2l = sA2[l];
-    u32x4 dyr[P / 16];
-#pragma unroll
-    for (int kk = 0; kk < P / 16; ++kk)
-      dyr[kk] = keep_or_zero(lok, load16(dy + (lrow * H + h) * size_t(P) + 16 * kk + 8 * g2));
-    // state term: dC^T(n, l) = exp(Acs_l) sum_p H(n, p) dy_l[p]
-    f32x16 adc[N / 32];
-    const float el = __builtin_amdgcn_exp2f(a2l);
-#pragma unroll
-    for (int nt = 0; nt < N / 32; ++nt) {
-      adc[nt] = zero16();
-#pragma unroll
-      for (int kk = 0; kk < P / 16; ++kk) {
-        const int kb = 16 * kk + 8 * g2;
-        adc[nt] = mfma32x32x16(frag_tr<RBN>(sH, kb, kb + 4, 32 * nt, lane), dyr[kk], adc[nt]);
-        adc[nt] = mfma32x32x16(frag_tr<RBN>(sHlo, kb, kb + 4, 32 * nt, lane), dyr[kk], adc[nt]);
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) adc[nt][r] *= el;
-    }
-    // C_l . dC_l of the state term
-    float cd = 0.f;
+  }
+
+  // ---- the work-group's sum over its heads: bf16 when it holds all heads
+  //      of the group, else an fp32 partial of its slice
+  if (sok) {
+    const size_t row = size_t(srow) * G + g;
+    const long rows = long(gridDim.x / nslice / G / nc) * T;   // batch rows x tokens
 #pragma unroll
     for (int nt = 0; nt < N / 32; ++nt)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int n = 32 * nt + 8 * q + 4 * g2;
-        const u32x2 cv = *reinterpret_cast<const u32x2*>(Cm + (lrow * G + g) * size_t(N) + n);
-        cd += adc[nt][4 * q] * bf16_lo(cv[0]) + adc[nt][4 * q + 1] * bf16_hi(cv[0]) +
-              adc[nt][4 * q + 2] * bf16_lo(cv[1]) + adc[nt][4 * q + 3] * bf16_hi(cv[1]);
+        const f32x4 v4 = f32x4{accT[nt][4 * q], accT[nt][4 * q + 1], accT[nt][4 * q + 2], accT[nt][4 * q + 3]};
+        if (nslice == 1)
+          *reinterpret_cast<u32x2*>(dBo + row * N + n) = u32x2{pack_bf16x2(v4[0], v4[1]), pack_bf16x2(v4[2], v4[3])};
+        else
+          *reinterpret_cast<f32x4*>(dBs + (size_t(sl) * rows * G + row) * N + n) = v4;
       }
-    // intra-chunk terms, tiles of rows s (block j) and lanes l (none when the
-    // whole block l is past the valid tokens)
-    const int jlast = 32 * i < nv ? i : -1;
+  }
+}
+
+// l side: dC (summed over the work-group's heads) and, per head and token l,
+// C_l . dC_l (sdl) for the last kernel. Wave i owns tokens l of block i and
+// the tiles of s-blocks j <= i. Operands from LDS as on the s side (B, C and
+// the tiles once; x, dy and bf16(H_c) per head; the hi + lo pair of H_c for
+// the dot straight from its fp32 rows).
+template <int N, int P, int NB>
+__global__ __launch_bounds__(64 * NB) void bwd_l_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ Bm, const uint16_t* __restrict__ Cm,
+    const uint16_t* __restrict__ dy, const float* __restrict__ Acs, const float* __restrict__ dtq,
+    const float* __restrict__ CBf, const float* __restrict__ Hst, uint16_t* __restrict__ dCo,
+    float* __restrict__ dCs, float* __restrict__ gsdl, int T, int H, int G, int nc, int nslice) {
+  constexpr int Q = 32 * NB;
+  constexpr int kThr = 64 * NB;
+  constexpr int RBP = P / 8, RBN = N / 8;   // 16-byte chunks per row
+  constexpr int ntile = NB * (NB + 1) / 2;
+  __shared__ __attribute__((aligned(16))) uint16_t sB[Q * N];
+  __shared__ __attribute__((aligned(16))) uint16_t sC[Q * N];
+  __shared__ __attribute__((aligned(16))) uint16_t sX[Q * P];
+  __shared__ __attribute__((aligned(16))) uint16_t sDY[Q * P];
+  __shared__ __attribute__((aligned(16))) uint16_t sH[P * N];     // bf16(H_c), rows p
+  __shared__ f32x4 sT[ntile * 4 * 64];                            // C B^T tiles, lanes = l
+  __shared__ float sA2[Q], sF[Q], sL[Q];
+
+  const int id = xcd_swizzle(blockIdx.x, gridDim.x);
+  const int sl = id % nslice;
+  const int rest = id / nslice;
+  const int g = rest % G;
+  const int bc = rest / G;
+  const int c = bc % nc, b = bc / nc;
+  const int hps = H / G / nslice;               // heads of this work-group
+  const int h0 = g * (H / G) + sl * hps;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = wave_id();
+  const int l32 = lane & 31, g2 = lane >> 5;
+  const long r0 = long(b) * T + long(c) * Q;        // first token row of the chunk
+  const int nv = min(Q, T - c * Q);                 // valid tokens
+
+  stage_rows<RBN, kThr>(sB, Bm, r0, nv, Q, size_t(G) * N, size_t(g) * N, tid);
+  stage_rows<RBN, kThr>(sC, Cm, r0, nv, Q, size_t(G) * N, size_t(g) * N, tid);
+  stage_tiles<ntile, kThr>(sT, CBf + ((size_t(b) * nc + c) * G + g) * ntile * 1024, tid);
+
+  const int q16 = lane & 15;
+  const int mcol = 16 * ((lane >> 4) & 1) + 4 * (q16 & 3);
+  auto toff = [&](auto rb, int u, int mt) {
+    constexpr int RB = decltype(rb)::value;
+    return lds_off<RB>(4 * g2 + 8 * u + (q16 >> 2), 32 * mt + mcol);
+  };
+  using RBNc = std::integral_constant<int, RBN>;
+
+  const int i = wave;
+  const int l = 32 * i + l32;
+  const bool lok = l < nv;
+  const long lrow = r0 + min(l, nv - 1);
+  const int jlast = 32 * i < nv ? i : -1;       // no tiles when the whole block is past the tokens
+
+  // dC of this wave's 32 tokens summed over the work-group's heads:
+  // transposed, rows n, lane = l
+  f32x16 accT[N / 32];
+#pragma unroll
+  for (int nt = 0; nt < N / 32; ++nt) accT[nt] = zero16();
+
+  for (int hk = 0; hk < hps; ++hk) {
+    const int h = h0 + hk;
+    const size_t arow = ((size_t(b) * H + h) * nc + c) * Q;
+    const size_t sbase = ((size_t(b) * nc + c) * H + h) * size_t(P) * N;
+    __syncthreads();   // the previous head's tiles and tables are consumed
+    for (int t = tid; t < Q; t += kThr) {
+      const float a2 = Acs[arow + t] * kLog2e, d = dtq[arow + t];
+      sA2[t] = a2;
+      sF[t] = __builtin_amdgcn_exp2f(Acs[arow + (t | 31)] * kLog2e - a2) * d;   // <= dt
+      sL[t] = __builtin_amdgcn_logf(d) - a2;                                     // -inf where dt = 0
+    }
+    stage_rows<RBP, kThr>(sX, x, r0, nv, Q, size_t(H) * P, size_t(h) * P, tid);
+    stage_rows<RBP, kThr>(sDY, dy, r0, nv, Q, size_t(H) * P, size_t(h) * P, tid);
+    for (int e = tid; e < P * RBN; e += kThr) {
+      const int r = e / RBN, cc = e % RBN;
+      const f32x4 h0v = *reinterpret_cast<const f32x4*>(Hst + sbase + size_t(r) * N + 8 * cc);
+      const f32x4 h1v = *reinterpret_cast<const f32x4*>(Hst + sbase + size_t(r) * N + 8 * cc + 4);
+      *reinterpret_cast<u32x4*>(&sH[lds_off<RBN>(r, 8 * cc)]) =
+          u32x4{pack_bf16x2(h0v[0], h0v[1]), pack_bf16x2(h0v[2], h0v[3]), pack_bf16x2(h1v[0], h1v[1]),
+                pack_bf16x2(h1v[2], h1v[3])};
+    }
+    __syncthreads();
+
+    const float a2l = sA2[l];
+    const float el = __builtin_amdgcn_exp2f(a2l);
+    u32x4 dyr[P / 16];
+#pragma unroll
+    for (int kk = 0; kk < P / 16; ++kk) dyr[kk] = lds_row16<RBP>(sDY, l, 16 * kk + 8 * g2);
+    // state term of dC: dC^T(n, l) += sum_p H(n, p) (exp(Acs_l) dy_l[p])
+    {
+      u32x4 dys[P / 16];
+#pragma unroll
+      for (int kk = 0; kk < P / 16; ++kk)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) dys[kk][w] = pack_bf16x2(bf16_lo(dyr[kk][w]) * el, bf16_hi(dyr[kk][w]) * el);
+#pragma unroll
+      for (int nt = 0; nt < N / 32; ++nt)
+#pragma unroll
+        for (int kk = 0; kk < P / 16; ++kk) {
+          const int kb = 16 * kk + 8 * g2;
+          accT[nt] = mfma32x32x16(frag_tr<RBN>(sH, kb, kb + 4, 32 * nt, lane), dys[kk], accT[nt]);
+        }
+    }
+    // this head's C_l . (state term of dC_l) = exp(Acs_l) dy_l . (H^T C_l),
+    // with H as hi + lo (from its fp32 rows p): y^T(p, l) = sum_n H(n, p) C_l[n]
+    float cd = 0.f;
+    {
+      f32x16 yst[P / 32];
+#pragma unroll
+      for (int pt = 0; pt < P / 32; ++pt) {
+        f32x4 hv[N / 16][2];
+#pragma unroll
+        for (int kk = 0; kk < N / 16; ++kk) {
+          const float* hr = Hst + sbase + size_t(32 * pt + l32) * N + 16 * kk + 8 * g2;
+          hv[kk][0] = *reinterpret_cast<const f32x4*>(hr);
+          hv[kk][1] = *reinterpret_cast<const f32x4*>(hr + 4);
+        }
+        yst[pt] = zero16();
+#pragma unroll
+        for (int kk = 0; kk < N / 16; ++kk) {
+          const u32x4 cl = lds_row16<RBN>(sC, l, 16 * kk + 8 * g2);
+          u32x4 hi, lo;
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const float v0 = hv[kk][w / 2][2 * (w % 2)], v1 = hv[kk][w / 2][2 * (w % 2) + 1];
+            hi[w] = pack_bf16x2(v0, v1);
+            lo[w] = pack_bf16x2(v0 - bf16_lo(hi[w]), v1 - bf16_hi(hi[w]));
+          }
+          yst[pt] = mfma32x32x16(hi, cl, yst[pt]);
+          yst[pt] = mfma32x32x16(lo, cl, yst[pt]);
+        }
+      }
+#pragma unroll
+      for (int pt = 0; pt < P / 32; ++pt)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const u32x2 dv = lds_row8<RBP>(sDY, l, 32 * pt + 8 * q + 4 * g2);
+          cd += yst[pt][4 * q] * bf16_lo(dv[0]) + yst[pt][4 * q + 1] * bf16_hi(dv[0]) +
+                yst[pt][4 * q + 2] * bf16_lo(dv[1]) + yst[pt][4 * q + 3] * bf16_hi(dv[1]);
+        }
+      cd *= el;
+    }
+    // intra-chunk terms, tiles of rows s (block j) and lanes l
     for (int j = 0; j <= jlast; ++j) {
-      const int srw = 32 * j + l32;
+      // C B^T in the forward orientation (rows s, lane l)
+      const f32x4* fsrc = sT + (i * (i + 1) / 2 + j) * 256 + lane;
+      const f32x4 cf4[4] = {fsrc[0], fsrc[64], fsrc[128], fsrc[192]};
       f32x16 accS = zero16();
 #pragma unroll
-      for (int kk = 0; kk < P / 16; ++kk) {
-        const u32x4 xs = keep_or_zero(srw < nv, load16(x + ((r0 + min(srw, nv - 1)) * H + h) * size_t(P) +
-                                                       16 * kk + 8 * g2));
-        accS = mfma32x32x16(xs, dyr[kk], accS);                         // Sxy: rows s, lane l
-      }
+      for (int kk = 0; kk < P / 16; ++kk)
+        accS = mfma32x32x16(lds_row16<RBP>(sX, 32 * j + l32, 16 * kk + 8 * g2), dyr[kk], accS);   // Sxy
       const bool diag = j == i;
       const float lfac = diag ? 0.f : __builtin_amdgcn_exp2f(a2l - sA2[32 * j + 31]);
-      // C B^T in the forward orientation (rows s, lane l)
-      const f32x4* fsrc = reinterpret_cast<const f32x4*>(
-          CBf + (((size_t(b) * nc + c) * G + g) * ntile + size_t(i) * (i + 1) / 2 + j) * 1024 + size_t(lane) * 16);
-      const f32x4 cf4[4] = {fsrc[0], fsrc[1], fsrc[2], fsrc[3]};
       uint32_t zw[8];
 #pragma unroll
       for (int m = 0; m < 8; ++m) {
@@ -370,41 +506,58 @@ __global__ __launch_bounds__(128 * NB) void bwd_chunk_kernel(
         const int o0 = toff(RBNc{}, 0, nt) + joN, o1 = toff(RBNc{}, 1, nt) + joN;
         const u32x2 a0 = lds_read_tr16(sB, o0), a1 = lds_read_tr16(sB, o1);
         const u32x2 b0 = lds_read_tr16(sB, o0 + 16 * N), b1 = lds_read_tr16(sB, o1 + 16 * N);
-        adc[nt] = mfma32x32x16(u32x4{a0[0], a0[1], a1[0], a1[1]}, zga, adc[nt]);
-        adc[nt] = mfma32x32x16(u32x4{b0[0], b0[1], b1[0], b1[1]}, zgb, adc[nt]);
+        accT[nt] = mfma32x32x16(u32x4{a0[0], a0[1], a1[0], a1[1]}, zga, accT[nt]);
+        accT[nt] = mfma32x32x16(u32x4{b0[0], b0[1], b1[0], b1[1]}, zgb, accT[nt]);
       }
     }
-    // dC_l as an fp32 partial of this head
+    cd += __shfl_xor(cd, 32, 64);
+    if (g2 == 0) gsdl[arow + l] = lok ? cd : 0.f;   // C_l . dC_l of this head
+  }
+
+  if (lok) {
+    const size_t row = size_t(lrow) * G + g;
+    const long rows = long(gridDim.x / nslice / G / nc) * T;   // batch rows x tokens
 #pragma unroll
     for (int nt = 0; nt < N / 32; ++nt)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int n = 32 * nt + 8 * q + 4 * g2;
-        if (lok)
-          *reinterpret_cast<f32x4*>(dCp + (lrow * H + h) * size_t(N) + n) =
-              f32x4{adc[nt][4 * q], adc[nt][4 * q + 1], adc[nt][4 * q + 2], adc[nt][4 * q + 3]};
+        const f32x4 v4 = f32x4{accT[nt][4 * q], accT[nt][4 * q + 1], accT[nt][4 * q + 2], accT[nt][4 * q + 3]};
+        if (nslice == 1)
+          *reinterpret_cast<u32x2*>(dCo + row * N + n) = u32x2{pack_bf16x2(v4[0], v4[1]), pack_bf16x2(v4[2], v4[3])};
+        else
+          *reinterpret_cast<f32x4*>(dCs + (size_t(sl) * rows * G + row) * N + n) = v4;
       }
-    cd += __shfl_xor(cd, 32, 64);
-    if (g2 == 0) sdl[l] = lok ? cd : 0.f;
   }
-  __syncthreads();
+}
 
-  // ---- dAcs, its reverse cumulative sum R, ddt, and this chunk's dA / dD
-  //      terms: thread k < Q takes token t = Q-1-k, so an inclusive scan over k
-  //      is the sum over t' >= t. The chunk-end term (dAcs_{Q-1} only, so a
-  //      constant K added to every R_t) is a block sum: the per-token state
-  //      dots and exp(Acs_{Q-1}) <G_c, H_c> from the reverse pass's partials.
-  float dacs = 0.f, dtv = 0.f, ddv = 0.f, sdsv = 0.f, kpart = 0.f;
+// Last per-chunk step, one (batch, chunk, head) per work-group: dAcs, its
+// reverse cumulative sum R, ddt and the chunk's dA / dD terms. Thread k < Q
+// takes token t = Q-1-k, so an inclusive scan over k is the sum over t' >= t.
+// The chunk-end term (dAcs_{Q-1} only, so a constant K added to every R_t)
+// is a block sum: the per-token state dots and exp(Acs_{Q-1}) <G_c, H_c>
+// from the reverse pass's partials.
+template <int Q>
+__global__ __launch_bounds__(Q) void bwd_ddt_kernel(const float* __restrict__ Acs, const float* __restrict__ dtq,
+                                                    const float* __restrict__ gsds, const float* __restrict__ gsdst,
+                                                    const float* __restrict__ gsdd, const float* __restrict__ gsdl,
+                                                    const float* __restrict__ ghp, const float* __restrict__ A,
+                                                    uint16_t* __restrict__ ddt, float* __restrict__ dAp,
+                                                    float* __restrict__ dDp, int T, int H, int nc, int nghp) {
+  constexpr int kW = Q / 64 > 0 ? Q / 64 : 1;
+  __shared__ float sred[kW][2];
+  const int id = blockIdx.x;                     // (b * H + h) * nc + c
+  const int c = id % nc, bh = id / nc;
+  const int h = bh % H, b = bh / H;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const size_t arow = size_t(id) * Q;
+  const int nv = min(Q, T - c * Q);
   const int t = Q - 1 - tid;
-  if (tid < Q) {
-    dtv = sdt[t];
-    sdsv = sds[t];
-    ddv = sdd[t];
-    dacs = sdl[t] - dtv * sdsv;
-    kpart = sdst[t];
-  }
-  if (tid < nghp)
-    kpart += __builtin_amdgcn_exp2f(sA2[Q - 1]) * ghp[((size_t(b) * H + h) * nc + c) * nghp + tid];
+  const float dtv = dtq[arow + t], sdsv = gsds[arow + t];
+  const float dacs = gsdl[arow + t] - dtv * sdsv;
+  float kpart = gsdst[arow + t];
+  for (int k = tid; k < nghp; k += Q)
+    kpart += __builtin_amdgcn_exp2f(Acs[arow + Q - 1] * kLog2e) * ghp[size_t(id) * nghp + k];
   float v = dacs;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
@@ -417,17 +570,13 @@ __global__ __launch_bounds__(128 * NB) void bwd_chunk_kernel(
   if (lane == 0) sred[wave][1] = kpart;
   __syncthreads();
   float K = 0.f;
-  for (int w = 0; w < 2 * NB; ++w) {
+  for (int w = 0; w < kW; ++w) {
     if (w < wave) v += sred[w][0];
     K += sred[w][1];
   }
   v += K;
-  float pa = 0.f, pd = 0.f;
-  if (tid < Q) {
-    if (t < nv) ddt[(r0 + t) * H + h] = f32_to_bf16(sdsv + Ah * v);
-    pa = dtv * v;
-    pd = ddv;
-  }
+  if (t < nv) ddt[(long(b) * T + long(c) * Q + t) * H + h] = f32_to_bf16(sdsv + A[h] * v);
+  float pa = dtv * v, pd = gsdd[arow + t];
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {
     pa += __shfl_xor(pa, off, 64);
@@ -441,41 +590,31 @@ __global__ __launch_bounds__(128 * NB) void bwd_chunk_kernel(
   __syncthreads();
   if (tid == 0) {
     float a = 0.f, d = 0.f;
-    for (int w = 0; w < 2 * NB; ++w) {
+    for (int w = 0; w < kW; ++w) {
       a += sred[w][0];
       d += sred[w][1];
     }
-    dAp[((size_t(b) * H + h) * nc + c)] = a;
-    dDp[((size_t(b) * H + h) * nc + c)] = d;
+    dAp[id] = a;
+    dDp[id] = d;
   }
 }
 
-// dB, dC: sum over the heads of each group of the per-head fp32 partials
-// (fixed order), rounded to bf16; dA, dD: sums over batch rows and chunks.
-__global__ __launch_bounds__(256) void bwd_reduce_bc(const float* __restrict__ dBp, const float* __restrict__ dCp,
+// dB, dC: sum of the per-slice fp32 partials (fixed order), rounded to bf16.
+__global__ __launch_bounds__(256) void bwd_reduce_bc(const float* __restrict__ dBs, const float* __restrict__ dCs,
                                                      uint16_t* __restrict__ dB, uint16_t* __restrict__ dC,
-                                                     long rows, int H, int G, int N) {
-  const long e = long(blockIdx.x) * 256 + threadIdx.x;   // (row, group, 4 n)
-  const int n4 = N / 4;
-  if (e >= rows * G * n4) return;
-  const int nq = int(e % n4);
-  const long rg = e / n4;
-  const int g = int(rg % G);
-  const long row = rg / G;
-  const int hpg = H / G;
+                                                     long n4, int nslice) {
+  const long e = long(blockIdx.x) * 256 + threadIdx.x;   // 4 elements of [b, T, G, N]
+  if (e >= n4) return;
   f32x4 sb = f32x4{0.f, 0.f, 0.f, 0.f}, sc = sb;
-  for (int k = 0; k < hpg; ++k) {
-    const size_t o = (size_t(row) * H + g * hpg + k) * N + 4 * nq;
-    const f32x4 vb = *reinterpret_cast<const f32x4*>(dBp + o);
-    const f32x4 vc = *reinterpret_cast<const f32x4*>(dCp + o);
-    sb += vb;
-    sc += vc;
+  for (int k = 0; k < nslice; ++k) {
+    sb += *reinterpret_cast<const f32x4*>(dBs + (size_t(k) * n4 + e) * 4);
+    sc += *reinterpret_cast<const f32x4*>(dCs + (size_t(k) * n4 + e) * 4);
   }
-  const size_t oo = (size_t(row) * G + g) * N + 4 * nq;
-  *reinterpret_cast<u32x2*>(dB + oo) = u32x2{pack_bf16x2(sb[0], sb[1]), pack_bf16x2(sb[2], sb[3])};
-  *reinterpret_cast<u32x2*>(dC + oo) = u32x2{pack_bf16x2(sc[0], sc[1]), pack_bf16x2(sc[2], sc[3])};
+  *reinterpret_cast<u32x2*>(dB + size_t(e) * 4) = u32x2{pack_bf16x2(sb[0], sb[1]), pack_bf16x2(sb[2], sb[3])};
+  *reinterpret_cast<u32x2*>(dC + size_t(e) * 4) = u32x2{pack_bf16x2(sc[0], sc[1]), pack_bf16x2(sc[2], sc[3])};
 }
 
+// dA, dD: sums over batch rows and chunks of the per-(b, h, c) partials.
 __global__ __launch_bounds__(64) void bwd_reduce_ad(const float* __restrict__ dAp, const float* __restrict__ dDp,
                                                     float* __restrict__ dA, float* __restrict__ dD, int batch,
                                                     int H, int nc) {
@@ -499,12 +638,19 @@ __global__ __launch_bounds__(64) void bwd_reduce_ad(const float* __restrict__ dA
 
 template <int N, int P, int NB>
 hipError_t launch_npq(const FwdShape& s, const BwdArgs& a, hipStream_t st) {
-  const long blocks = long(s.b) * s.nc * s.H;
-  hipLaunchKernelGGL((bwd_chunk_kernel<N, P, NB>), dim3(unsigned(blocks)), dim3(128 * NB), 0, st,
+  const long blocks = long(s.b) * s.nc * s.G * a.nslice;
+  hipLaunchKernelGGL((bwd_s_kernel<N, P, NB>), dim3(unsigned(blocks)), dim3(64 * NB), 0, st,
                      static_cast<const uint16_t*>(a.x), static_cast<const uint16_t*>(a.B),
-                     static_cast<const uint16_t*>(a.C), static_cast<const uint16_t*>(a.dy), a.Acs, a.dtq, a.CB, a.CBt,
-                     a.Hst, a.Gb, a.GbT, a.ghp, a.A, a.D, static_cast<uint16_t*>(a.dx), static_cast<uint16_t*>(a.ddt),
-                     a.dBp, a.dCp, a.dAp, a.dDp, s.T, s.H, s.G, s.nc, a.nghp);
+                     static_cast<const uint16_t*>(a.C), static_cast<const uint16_t*>(a.dy), a.Acs, a.dtq, a.CBt,
+                     a.Gb, a.D, static_cast<uint16_t*>(a.dx), static_cast<uint16_t*>(a.dB), a.dBs, a.tsds,
+                     a.tsdst, a.tsdd, s.T, s.H, s.G, s.nc, a.nslice);
+  hipLaunchKernelGGL((bwd_l_kernel<N, P, NB>), dim3(unsigned(blocks)), dim3(64 * NB), 0, st,
+                     static_cast<const uint16_t*>(a.x), static_cast<const uint16_t*>(a.B),
+                     static_cast<const uint16_t*>(a.C), static_cast<const uint16_t*>(a.dy), a.Acs, a.dtq, a.CB,
+                     a.Hst, static_cast<uint16_t*>(a.dC), a.dCs, a.tsdl, s.T, s.H, s.G, s.nc, a.nslice);
+  hipLaunchKernelGGL((bwd_ddt_kernel<32 * NB>), dim3(unsigned(long(s.b) * s.H * s.nc)), dim3(32 * NB), 0, st,
+                     a.Acs, a.dtq, a.tsds, a.tsdst, a.tsdd, a.tsdl, a.ghp, a.A, static_cast<uint16_t*>(a.ddt),
+                     a.dAp, a.dDp, s.T, s.H, s.nc, a.nghp);
   return hipGetLastError();
 }
 
@@ -527,8 +673,18 @@ hipError_t launch_n(const FwdShape& s, const BwdArgs& a, hipStream_t st) {
 
 }  // namespace
 
+int bwd_slices(const FwdShape& s) {
+  // heads of a group split over work-groups until the grid has ~2 work-groups
+  // per compute unit (slices divide the group's heads)
+  const int hpg = s.H / s.G;
+  const long base = long(s.b) * s.nc * s.G;
+  for (int d = 1; d <= hpg; ++d)
+    if (hpg % d == 0 && base * d >= 512) return d;
+  return hpg;
+}
+
 hipError_t launch_bwd_chunk(const FwdShape& s, const BwdArgs& a, hipStream_t st) {
-  if (s.Q != bwd_chunk_len(s.P, s.N)) return hipErrorInvalidValue;
+  if (s.Q != bwd_chunk_len(s.P, s.N) || a.nslice < 1 || (s.H / s.G) % a.nslice) return hipErrorInvalidValue;
   switch (s.N) {
     case 32: return launch_n<32>(s, a, st);
     case 64: return launch_n<64>(s, a, st);
@@ -538,13 +694,13 @@ hipError_t launch_bwd_chunk(const FwdShape& s, const BwdArgs& a, hipStream_t st)
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_bwd_reduce(const FwdShape& s, const float* dBp, const float* dCp, const float* dAp,
-                             const float* dDp, void* dB, void* dC, float* dA, float* dD, hipStream_t st) {
-  const long rows = long(s.b) * s.T;
-  const long n = rows * s.G * (s.N / 4);
-  hipLaunchKernelGGL(bwd_reduce_bc, dim3(unsigned((n + 255) / 256)), dim3(256), 0, st, dBp, dCp,
-                     static_cast<uint16_t*>(dB), static_cast<uint16_t*>(dC), rows, s.H, s.G, s.N);
-  hipLaunchKernelGGL(bwd_reduce_ad, dim3(unsigned(s.H)), dim3(64), 0, st, dAp, dDp, dA, dD, s.b, s.H, s.nc);
+hipError_t launch_bwd_reduce(const FwdShape& s, const BwdArgs& a, float* dA, float* dD, hipStream_t st) {
+  if (a.nslice > 1) {
+    const long n4 = long(s.b) * s.T * s.G * (s.N / 4);
+    hipLaunchKernelGGL(bwd_reduce_bc, dim3(unsigned((n4 + 255) / 256)), dim3(256), 0, st, a.dBs, a.dCs,
+                       static_cast<uint16_t*>(a.dB), static_cast<uint16_t*>(a.dC), n4, a.nslice);
+  }
+  hipLaunchKernelGGL(bwd_reduce_ad, dim3(unsigned(s.H)), dim3(64), 0, st, a.dAp, a.dDp, dA, dD, s.b, s.H, s.nc);
   return hipGetLastError();
 }
 

@@ -82,16 +82,16 @@ bool grids_fit(const FwdShape& s, bool mfma) {
 // Backward workspace (byte offsets, 256-byte aligned), chunk length
 // bwd_chunk_len(P, N):
 //   acs, dtq [b,H,nc,Q] f32; st [b,nc,H,P,N] f32 (chunk states, then the states
-//   entering each chunk); ds [b,nc,H,P,N] f32; gb [b,nc,H,P,N] and
-//   gbt [b,nc,H,N,P] bf16; cb, cbt [b,nc,G,ntile,64,16] f32 (C B^T tiles, both
-//   orientations);
+//   entering each chunk); ds [b,nc,H,P,N] f32; gb [b,nc,H,P,N] bf16;
+//   cb, cbt [b,nc,G,ntile,64,16] f32 (C B^T tiles, both orientations);
 //   fin [b,H,N,P] f32; ghp [b,H,nc,nghp] f32;
-//   dbp, dcp [b,T,H,N] f32; dap, ddp [b,H,nc] f32
+//   dbs, dcs [nslice,b,T,G,N] f32 (only with nslice > 1); dap, ddp [b,H,nc] f32;
+//   tok [4, b,H,nc,Q] f32 (per-token dots of each head)
 struct BwdLayout {
-  size_t acs, dtq, st, ds, gb, gbt, cb, cbt, fin, ghp, dbp, dcp, dap, ddp, total;
+  size_t acs, dtq, st, ds, gb, cb, cbt, fin, ghp, dbs, dcs, dap, ddp, tok, total;
 };
 
-BwdLayout bwd_layout(const FwdShape& s, int nghp) {
+BwdLayout bwd_layout(const FwdShape& s, int nghp, int nslice) {
   BwdLayout w;
   const size_t row = size_t(s.b) * s.H * s.nc * s.Q * sizeof(float);
   const size_t nst = size_t(s.b) * s.nc * s.H * s.N * s.P;
@@ -104,15 +104,16 @@ BwdLayout bwd_layout(const FwdShape& s, int nghp) {
   w.st = take(nst * sizeof(float));
   w.ds = take(nst * sizeof(float));
   w.gb = take(nst * sizeof(uint16_t));
-  w.gbt = take(nst * sizeof(uint16_t));
   w.cb = take(size_t(s.b) * s.nc * s.G * ntile * 1024 * sizeof(float));
   w.cbt = take(size_t(s.b) * s.nc * s.G * ntile * 1024 * sizeof(float));
   w.fin = take(size_t(s.b) * s.H * s.N * s.P * sizeof(float));
   w.ghp = take(bhc * nghp * sizeof(float));
-  w.dbp = take(size_t(s.b) * s.T * s.H * s.N * sizeof(float));
-  w.dcp = take(size_t(s.b) * s.T * s.H * s.N * sizeof(float));
+  const size_t part = nslice > 1 ? size_t(nslice) * s.b * s.T * s.G * s.N * sizeof(float) : 0;
+  w.dbs = take(part);
+  w.dcs = take(part);
   w.dap = take(bhc * sizeof(float));
   w.ddp = take(bhc * sizeof(float));
+  w.tok = take(4 * row);
   w.total = o;
   return w;
 }
@@ -465,7 +466,7 @@ size_t ssd_chunk_scan_bwd_workspace(int batch, int seqlen, int nheads, int headd
   if (!dtype_ok(dtype) || check_dims(batch, seqlen, nheads, headdim, dstate, ngroups) != SSD_OK) return 0;
   FwdShape s;
   if (!bwd_supported(batch, seqlen, nheads, headdim, dstate, ngroups, dtype, s)) return 0;
-  return bwd_layout(s, state_passing_bwd_partials(s)).total;
+  return bwd_layout(s, state_passing_bwd_partials(s), bwd_slices(s)).total;
 }
 
 ssd_status ssd_chunk_scan_bwd(const void* x, const void* dt, const float* A, const void* B, const void* C,
@@ -484,7 +485,8 @@ ssd_status ssd_chunk_scan_bwd(const void* x, const void* dt, const float* A, con
   for (const void* p : ptrs)
     if (misaligned(p)) return SSD_ERR_ALIGN;
   const int nghp = state_passing_bwd_partials(s);
-  const BwdLayout w = bwd_layout(s, nghp);
+  const int nslice = bwd_slices(s);
+  const BwdLayout w = bwd_layout(s, nghp, nslice);
   if (workspace_bytes < w.total) return SSD_ERR_WORKSPACE;
 
   const size_t e = esize(dtype);
@@ -513,13 +515,12 @@ ssd_status ssd_chunk_scan_bwd(const void* x, const void* dt, const float* A, con
   float* Sst = reinterpret_cast<float*>(ws + w.st);
   float* dS = reinterpret_cast<float*>(ws + w.ds);
   uint16_t* Gb = reinterpret_cast<uint16_t*>(ws + w.gb);
-  uint16_t* GbT = reinterpret_cast<uint16_t*>(ws + w.gbt);
   uint16_t* CBf = reinterpret_cast<uint16_t*>(ws + w.cb);
   uint16_t* CBt = reinterpret_cast<uint16_t*>(ws + w.cbt);
   float* fin = reinterpret_cast<float*>(ws + w.fin);
   float* ghp = reinterpret_cast<float*>(ws + w.ghp);
-  float* dBp = reinterpret_cast<float*>(ws + w.dbp);
-  float* dCp = reinterpret_cast<float*>(ws + w.dcp);
+  float* dBs = reinterpret_cast<float*>(ws + w.dbs);
+  float* dCs = reinterpret_cast<float*>(ws + w.dcs);
   float* dAp = reinterpret_cast<float*>(ws + w.dap);
   float* dDp = reinterpret_cast<float*>(ws + w.ddp);
 
@@ -530,14 +531,17 @@ ssd_status ssd_chunk_scan_bwd(const void* x, const void* dt, const float* A, con
   if (launch_state_passing(s, Sst, nullptr, Acs, init_state, fin, hs) != hipSuccess) return SSD_ERR_HIP;
   // what each chunk's outputs give the state entering it, then the reverse pass
   if (launch_chunk_dstates_mfma(s, dy, C, dt, A, dS, hs) != hipSuccess) return SSD_ERR_HIP;
-  if (launch_state_passing_bwd(s, dS, Sst, Acs, dfinal, Gb, GbT, ghp, dinit, hs) != hipSuccess)
+  if (launch_state_passing_bwd(s, dS, Sst, Acs, dfinal, Gb, ghp, dinit, hs) != hipSuccess)
     return SSD_ERR_HIP;
   BwdArgs a;
-  a.x = x; a.B = B; a.C = C; a.dy = dy; a.Acs = Acs; a.dtq = dtq; a.CB = reinterpret_cast<const float*>(CBf); a.CBt = reinterpret_cast<const float*>(CBt); a.Hst = Sst; a.Gb = Gb; a.GbT = GbT;
-  a.ghp = ghp; a.nghp = nghp; a.A = A; a.D = D; a.dx = dx; a.ddt = ddt; a.dBp = dBp; a.dCp = dCp;
-  a.dAp = dAp; a.dDp = dDp;
+  a.x = x; a.B = B; a.C = C; a.dy = dy; a.Acs = Acs; a.dtq = dtq; a.CB = reinterpret_cast<const float*>(CBf); a.CBt = reinterpret_cast<const float*>(CBt); a.Hst = Sst; a.Gb = Gb;
+  a.ghp = ghp; a.nghp = nghp; a.A = A; a.D = D; a.dx = dx; a.ddt = ddt; a.dB = dB; a.dC = dC;
+  a.nslice = nslice; a.dBs = dBs; a.dCs = dCs; a.dAp = dAp; a.dDp = dDp;
+  float* tokd = reinterpret_cast<float*>(ws + w.tok);
+  const size_t rowf = size_t(s.b) * s.H * s.nc * s.Q;
+  a.tsds = tokd; a.tsdst = tokd + rowf; a.tsdd = tokd + 2 * rowf; a.tsdl = tokd + 3 * rowf;
   if (launch_bwd_chunk(s, a, hs) != hipSuccess) return SSD_ERR_HIP;
-  if (launch_bwd_reduce(s, dBp, dCp, dAp, dDp, dB, dC, dA, dD, hs) != hipSuccess) return SSD_ERR_HIP;
+  if (launch_bwd_reduce(s, a, dA, dD, hs) != hipSuccess) return SSD_ERR_HIP;
   return SSD_OK;
 }
 

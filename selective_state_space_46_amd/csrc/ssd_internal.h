@@ -217,16 +217,19 @@ hipError_t launch_causal_conv1d_update(ssd_dtype type, void* state, const void* 
 // ---------------------------------------------------------------------------
 // Backward pass (bwd_chunk_mfma.hip, state_passing.hip, chunk_state_mfma.hip).
 // The backward recomputes the forward with its own chunk length, the largest
-// of 128, 64, 32 whose per-chunk tiles fit the 160 KB of LDS of a CU (dy, B,
-// C rows of the chunk, and H_c, G_c), so one kernel serves each (headdim,
-// dstate); 0: shape not supported. 128 at most: its work-group has 4 waves
+// of 128, 64, 32 whose per-chunk tiles fit the 160 KB of LDS of a CU (x, dy,
+// B, C rows of the chunk, one P x N state and the chunk's fp32 C B^T tiles),
+// so one kernel serves each (headdim, dstate); 0: shape not supported. 128 at most: its work-group has 4 waves
 // per 128 tokens, and 1024-thread work-groups would leave 128 registers per
 // lane, too few for the accumulators.
 // ---------------------------------------------------------------------------
 constexpr int kBwdLdsMax = 160 * 1024;
-constexpr long bwd_lds_bytes(int P, int N, int Q) { return 2L * Q * (P + 2 * N) + 4L * P * N + 40L * Q; }
+constexpr long bwd_lds_bytes(int P, int N, int Q) {
+  return 4L * Q * (P + N) + 2L * P * N + 4096L * (Q / 32) * (Q / 32 + 1) / 2 + 16L * Q;
+}
 constexpr int bwd_chunk_len(int P, int N) {
-  return bwd_lds_bytes(P, N, 128) <= kBwdLdsMax   ? 128
+  return P * N > 128 * 128                        ? 0     // states beyond 64 KB in bf16: not supported
+         : bwd_lds_bytes(P, N, 128) <= kBwdLdsMax ? 128
          : bwd_lds_bytes(P, N, 64) <= kBwdLdsMax  ? 64
          : bwd_lds_bytes(P, N, 32) <= kBwdLdsMax  ? 32
                                                   : 0;
@@ -241,13 +244,11 @@ hipError_t launch_chunk_state_mfma_bwd(const FwdShape& s, const void* x, const v
 // dS_c^T [b, nc, H, P, N] f32 = sum_l exp(Acs_l) dy_l C_l^T per chunk.
 hipError_t launch_chunk_dstates_mfma(const FwdShape& s, const void* dy, const void* C, const void* dt,
                                      const float* A, float* dS, hipStream_t st);
-// Reverse inter-chunk pass: G_c (bf16 [b, nc, H, P, N] and [b, nc, H, N, P]),
-// per-wave partials of <G_c, H_c> (ghp [b, H, nc, state_passing_bwd_partials])
-// and dinit.
+// Reverse inter-chunk pass: G_c (bf16 [b, nc, H, P, N]), per-wave partials of
+// <G_c, H_c> (ghp [b, H, nc, state_passing_bwd_partials]) and dinit.
 int state_passing_bwd_partials(const FwdShape& s);
 hipError_t launch_state_passing_bwd(const FwdShape& s, const float* dS, const float* Hst, const float* Acs,
-                                    const float* dfinal, uint16_t* Gb, uint16_t* GbT, float* ghp, float* dinit,
-                                    hipStream_t st);
+                                    const float* dfinal, uint16_t* Gb, float* ghp, float* dinit, hipStream_t st);
 
 struct BwdArgs {
   const void *x, *B, *C, *dy;
@@ -256,17 +257,19 @@ struct BwdArgs {
   const float* CBt;      // the same, transposed (lanes = s)
   const float* Hst;      // states entering each chunk, fp32 [b, nc, H, P, N]
   const uint16_t* Gb;    // gradients of the states leaving each chunk, bf16 [b, nc, H, P, N]
-  const uint16_t* GbT;   // the same, [b, nc, H, N, P]
   const float* ghp;      // partials of <G_c, H_c>
   int nghp;              // partials per (b, h, c)
   const float *A, *D;
   void *dx, *ddt;        // bf16 [b, T, H, P], [b, T, H]
-  float *dBp, *dCp;      // per-head fp32 partials [b, T, H, N]
+  void *dB, *dC;         // bf16 [b, T, G, N]
+  int nslice;            // work-groups sharing one (batch, chunk, group): bwd_slices
+  float *dBs, *dCs;      // nslice > 1: per-slice fp32 partials [nslice, b, T, G, N]
+  float *tsds, *tsdst, *tsdd, *tsdl;   // per-token dots of each head, fp32 [b, H, nc, Q]
   float *dAp, *dDp;      // per-chunk fp32 partials [b, H, nc]
 };
+int bwd_slices(const FwdShape& s);
 hipError_t launch_bwd_chunk(const FwdShape& s, const BwdArgs& a, hipStream_t st);
-hipError_t launch_bwd_reduce(const FwdShape& s, const float* dBp, const float* dCp, const float* dAp,
-                             const float* dDp, void* dB, void* dC, float* dA, float* dD, hipStream_t st);
+hipError_t launch_bwd_reduce(const FwdShape& s, const BwdArgs& a, float* dA, float* dD, hipStream_t st);
 
 hipError_t launch_state_update(ssd_dtype type, float* state, const void* x, const void* dt,
                                const float* A, const void* B, const void* C, const float* D, void* y,

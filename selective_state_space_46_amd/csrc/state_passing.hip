@@ -168,19 +168,18 @@ __global__ __launch_bounds__(kThreads) void state_passing_scalar(
 // respect to H_{c+1} (the state leaving chunk c), runs backwards:
 //   G_{nc-1} = dfinal;  G_{c-1} = exp(Acs_c[Q-1]) G_c + dS_c;  dinit = G_{-1}
 // where dS_c is what chunk c's outputs contribute to the gradient of the
-// state entering it. Each G_c goes out as bf16, [p][n] like the chunk states
-// (Gb) and [n][p] (GbT), for the per-chunk gradient kernel, which takes it as
-// a matrix operand in both orientations, together with the partial sums
+// state entering it. Each G_c goes out as bf16, [p][n] like the chunk states,
+// for the per-chunk gradient kernels, together with the partial sums
 // of <G_c, H_c> (H_c the state entering chunk c: times exp(Acs_c[Q-1]), the
 // part of the gradient of the chunk's total decay exponent that passes
 // through H_c) of each wave of the work-group: ghp[b, c, h, tile, wave]. Hst
 // holds the states entering each chunk (fp32, [p][n]). Same tiling as the
-// forward kernel.
+// forward kernel; dS, H_c and the decays of the chunks ahead (in reverse
+// order) do not depend on the recurrence and are loaded kDepth chunks early.
 __global__ __launch_bounds__(kThreads) void state_passing_bwd_tiled(
     const float* __restrict__ dS, const float* __restrict__ Hst,
     const float* __restrict__ Acs, const float* __restrict__ dfinal, uint16_t* __restrict__ Gb,
-    uint16_t* __restrict__ GbT, float* __restrict__ ghp, float* __restrict__ dinit, int H, int P, int N, int Q,
-    int nc) {
+    float* __restrict__ ghp, float* __restrict__ dinit, int H, int P, int N, int Q, int nc) {
   __shared__ float tile[kTN][kTP + 1];
   const int tpn = (N + kTN - 1) / kTN, tpp = (P + kTP - 1) / kTP;
   int bid = blockIdx.x;
@@ -214,29 +213,43 @@ __global__ __launch_bounds__(kThreads) void state_passing_bwd_tiled(
   const size_t cstride = size_t(H) * sbh;
   const size_t off0 = (size_t(b) * nc * H + h) * sbh + size_t(p) * N + n;
   const float* arow = Acs + size_t(bh) * nc * Q + (Q - 1);
-  for (int c = nc - 1; c >= 0; --c) {
-    f32x4 ds = f32x4{0.f, 0.f, 0.f, 0.f}, hc = ds;
-    float a = 1.f;
+  // ring of the chunks ahead: slot k holds chunk nc-1-(m+k) for step m
+  f32x4 rds[kDepth], rhc[kDepth];
+  float rdec[kDepth];
+  auto fetch = [&](int k, int c) {
     if (active) {
       const size_t o = off0 + size_t(c) * cstride;
-      ds = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(dS + o));
-      hc = *reinterpret_cast<const f32x4*>(Hst + o);
-      a = expf(arow[size_t(c) * Q]);
-      store_out(nullptr, Gb, o, G);
-      uint16_t* gt = GbT + (size_t(b) * nc + c) * cstride + size_t(h) * sbh + size_t(n) * P + p;
-      gt[0] = f32_to_bf16(G.x);
-      gt[P] = f32_to_bf16(G.y);
-      gt[2 * P] = f32_to_bf16(G.z);
-      gt[3 * P] = f32_to_bf16(G.w);
+      rds[k] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(dS + o));
+      rhc[k] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Hst + o));
+    } else {
+      rds[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+      rhc[k] = rds[k];
     }
-    float dot = active ? G.x * hc.x + G.y * hc.y + G.z * hc.z + G.w * hc.w : 0.f;
+    rdec[k] = arow[size_t(c) * Q];
+  };
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) dot += __shfl_xor(dot, off, 64);
-    if (lane == 0) ghp[((size_t(bh) * nc + c) * ntiles + tileid) * (kThreads / 64) + wave] = dot;
-    G.x = a * G.x + ds.x;
-    G.y = a * G.y + ds.y;
-    G.z = a * G.z + ds.z;
-    G.w = a * G.w + ds.w;
+  for (int k = 0; k < kDepth; ++k)
+    if (k < nc) fetch(k, nc - 1 - k);
+  for (int m0 = 0; m0 < nc; m0 += kDepth) {
+#pragma unroll
+    for (int k = 0; k < kDepth; ++k) {
+      const int m = m0 + k;
+      if (m < nc) {
+        const int c = nc - 1 - m;
+        const f32x4 ds = rds[k], hc = rhc[k];
+        const float a = expf(rdec[k]);
+        if (m + kDepth < nc) fetch(k, c - kDepth);
+        if (active) store_out(nullptr, Gb, off0 + size_t(c) * cstride, G);
+        float dot = active ? G.x * hc.x + G.y * hc.y + G.z * hc.z + G.w * hc.w : 0.f;
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) dot += __shfl_xor(dot, off, 64);
+        if (lane == 0) ghp[((size_t(bh) * nc + c) * ntiles + tileid) * (kThreads / 64) + wave] = dot;
+        G.x = a * G.x + ds.x;
+        G.y = a * G.y + ds.y;
+        G.z = a * G.z + ds.z;
+        G.w = a * G.w + ds.w;
+      }
+    }
   }
 
   if (dinit) {
@@ -259,12 +272,11 @@ int state_passing_bwd_partials(const FwdShape& s) {
 }
 
 hipError_t launch_state_passing_bwd(const FwdShape& s, const float* dS, const float* Hst, const float* Acs,
-                                    const float* dfinal, uint16_t* Gb, uint16_t* GbT, float* ghp, float* dinit,
-                                    hipStream_t st) {
+                                    const float* dfinal, uint16_t* Gb, float* ghp, float* dinit, hipStream_t st) {
   if (s.N % 4) return hipErrorInvalidValue;
   const long tiles = long(s.b) * s.H * ((s.P + kTP - 1) / kTP) * ((s.N + kTN - 1) / kTN);
   hipLaunchKernelGGL(state_passing_bwd_tiled, dim3(unsigned(tiles)), dim3(kThreads), 0, st, dS, Hst, Acs,
-                     dfinal, Gb, GbT, ghp, dinit, s.H, s.P, s.N, s.Q, s.nc);
+                     dfinal, Gb, ghp, dinit, s.H, s.P, s.N, s.Q, s.nc);
   return hipGetLastError();
 }
 
