@@ -52,18 +52,34 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
-// Rows r of a token-major tensor (row stride `stride` elements, `len`
-// elements from `col0`) of the chunk into a swizzled natural LDS tile, rows
-// past the valid tokens as zeros. All threads of the work-group take part.
-template <int RB, int kThr>
-__device__ __forceinline__ void stage_rows(uint16_t* tile, const uint16_t* __restrict__ src, long r0, int nv,
-                                           int rows, size_t stride, size_t col0, int tid) {
-  for (int e = tid; e < rows * RB; e += kThr) {
-    const int r = e / RB, cc = e % RB;
-    const u32x4 v = load16(src + (r0 + min(r, nv - 1)) * stride + col0 + 8 * cc);
-    *reinterpret_cast<u32x4*>(&tile[lds_off<RB>(r, 8 * cc)]) = keep_or_zero(r < nv, v);
+// Rows 0 .. NROW-1 of a token-major tensor (row stride `stride` elements,
+// RB 16-byte chunks from `col0`) of the chunk, into registers (rows past the
+// valid tokens as zeros) and then into a swizzled natural LDS tile. All
+// threads of the work-group take part; the loads of several tensors are
+// issued together before any store, so one round trip covers them all.
+template <int RB, int NROW, int kThr>
+struct RowStage {
+  static constexpr int PER = (NROW * RB + kThr - 1) / kThr;
+  u32x4 v[PER];
+  __device__ __forceinline__ void load(const uint16_t* __restrict__ src, long r0, int nv, size_t stride,
+                                       size_t col0, int tid) {
+#pragma unroll
+    for (int m = 0; m < PER; ++m) {
+      const int e = tid + m * kThr;
+      const int r = e / RB, cc = e % RB;
+      if (e < NROW * RB)
+        v[m] = keep_or_zero(r < nv, load16(src + (r0 + min(r, nv - 1)) * stride + col0 + 8 * cc));
+    }
   }
-}
+  template <bool ROWS>
+  __device__ __forceinline__ void store(uint16_t* tile, int tid) const {
+#pragma unroll
+    for (int m = 0; m < PER; ++m) {
+      const int e = tid + m * kThr;
+      if (e < NROW * RB) *reinterpret_cast<u32x4*>(&tile[lds_off<RB, ROWS>(e / RB, 8 * (e % RB))]) = v[m];
+    }
+  }
+};
 
 // The C B^T tiles of one (batch, chunk, group) (ntile x 1024 fp32, lane L's 16
 // values contiguous) into LDS as [tile][4][64 lanes] f32x4, so that lane L
@@ -77,13 +93,15 @@ __device__ __forceinline__ void stage_tiles(f32x4* sT, const float* __restrict__
 }
 
 // 16 bytes (8 consecutive columns from col) of row r of a swizzled natural tile
+// (tiles read by rows use the ROWS swizzle of mfma_util.h: 32 lanes reading
+// one chunk column of 32 rows hit 2-way bank conflicts instead of 8-way)
 template <int RB>
 __device__ __forceinline__ u32x4 lds_row16(const uint16_t* tile, int r, int col) {
-  return *reinterpret_cast<const u32x4*>(&tile[lds_off<RB>(r, col)]);
+  return *reinterpret_cast<const u32x4*>(&tile[lds_off<RB, true>(r, col)]);
 }
 template <int RB>
 __device__ __forceinline__ u32x2 lds_row8(const uint16_t* tile, int r, int col) {
-  return *reinterpret_cast<const u32x2*>(&tile[lds_off<RB>(r, col)]);
+  return *reinterpret_cast<const u32x2*>(&tile[lds_off<RB, true>(r, col)]);
 }
 
 // s side: dx, dB (summed over the work-group's heads) and, per head and
@@ -125,20 +143,27 @@ __global__ __launch_bounds__(64 * NB) void bwd_s_kernel(
   const long r0 = long(b) * T + long(c) * Q;        // first token row of the chunk
   const int nv = min(Q, T - c * Q);                 // valid tokens
 
-  stage_rows<RBN, kThr>(sB, Bm, r0, nv, Q, size_t(G) * N, size_t(g) * N, tid);
-  stage_rows<RBN, kThr>(sC, Cm, r0, nv, Q, size_t(G) * N, size_t(g) * N, tid);
+  {
+    RowStage<RBN, Q, kThr> rb, rc;
+    rb.load(Bm, r0, nv, size_t(G) * N, size_t(g) * N, tid);
+    rc.load(Cm, r0, nv, size_t(G) * N, size_t(g) * N, tid);
+    rb.template store<true>(sB, tid);              // read by rows
+    rc.template store<false>(sC, tid);             // read transposed only
+  }
   stage_tiles<ntile, kThr>(sT, CBt + ((size_t(b) * nc + c) * G + g) * ntile * 1024, tid);
 
   // lane constants of the permuted transposed reads (k = rows of a 32-row
   // block, in the order of the accumulator rows), per 32-column block
   const int q16 = lane & 15;
   const int mcol = 16 * ((lane >> 4) & 1) + 4 * (q16 & 3);
-  auto toff = [&](auto rb, int u, int mt) {
+  auto toff = [&](auto rb, auto rows, int u, int mt) {
     constexpr int RB = decltype(rb)::value;
-    return lds_off<RB>(4 * g2 + 8 * u + (q16 >> 2), 32 * mt + mcol);
+    return lds_off<RB, decltype(rows)::value>(4 * g2 + 8 * u + (q16 >> 2), 32 * mt + mcol);
   };
   using RBPc = std::integral_constant<int, RBP>;
   using RBNc = std::integral_constant<int, RBN>;
+  using kRows = std::integral_constant<bool, true>;
+  using kPlain = std::integral_constant<bool, false>;
 
   const int i = wave;
   const int s = 32 * i + l32;
@@ -152,25 +177,47 @@ __global__ __launch_bounds__(64 * NB) void bwd_s_kernel(
 #pragma unroll
   for (int nt = 0; nt < N / 32; ++nt) accT[nt] = zero16();
 
+  // A head's operands: its decay tables (thread t < Q takes token t), x and
+  // dy rows and G_c. All loads of a head are issued together; with few
+  // registers per thread (kAhead) the next head's loads are issued right after
+  // this head's staging, so they run under this head's compute.
+  RowStage<RBP, Q, kThr> rx, rd;
+  RowStage<RBN, P, kThr> rg;
+  constexpr bool kAhead = 2 * RowStage<RBP, Q, kThr>::PER + RowStage<RBN, P, kThr>::PER <= 12;
+  float ta = 0.f, tb = 0.f, tc = 0.f, td = 0.f;
+  auto fetch = [&](int h) {
+    const size_t arow = ((size_t(b) * H + h) * nc + c) * Q;
+    if (tid < Q) {
+      ta = Acs[arow + tid];
+      tb = Acs[arow + (tid & ~31)];
+      tc = Acs[arow + Q - 1];
+      td = dtq[arow + tid];
+    }
+    rx.load(x, r0, nv, size_t(H) * P, size_t(h) * P, tid);
+    rd.load(dy, r0, nv, size_t(H) * P, size_t(h) * P, tid);
+    if constexpr (kAhead)
+      rg.load(Gb + ((size_t(b) * nc + c) * H + h) * size_t(P) * N, 0, P, N, 0, tid);   // G_c rows p
+  };
+  if (hps > 0) fetch(h0);
+
   for (int hk = 0; hk < hps; ++hk) {
     const int h = h0 + hk;
     const size_t arow = ((size_t(b) * H + h) * nc + c) * Q;
     const size_t sbase = ((size_t(b) * nc + c) * H + h) * size_t(P) * N;
     __syncthreads();   // the previous head's tiles and tables are consumed
-    for (int t = tid; t < Q; t += kThr) {
-      const float a2 = Acs[arow + t] * kLog2e;
-      sA2[t] = a2;
-      sdt[t] = dtq[arow + t];
-      sEL[t] = __builtin_amdgcn_exp2f(a2 - Acs[arow + (t & ~31)] * kLog2e);    // <= 1
-      sEl[t] = __builtin_amdgcn_exp2f(Acs[arow + Q - 1] * kLog2e - a2);         // <= 1
+    if (tid < Q) {
+      const float a2 = ta * kLog2e;
+      sA2[tid] = a2;
+      sdt[tid] = td;
+      sEL[tid] = __builtin_amdgcn_exp2f(a2 - tb * kLog2e);    // <= 1
+      sEl[tid] = __builtin_amdgcn_exp2f(tc * kLog2e - a2);    // <= 1
     }
-    stage_rows<RBP, kThr>(sX, x, r0, nv, Q, size_t(H) * P, size_t(h) * P, tid);
-    stage_rows<RBP, kThr>(sDY, dy, r0, nv, Q, size_t(H) * P, size_t(h) * P, tid);
-    for (int e = tid; e < P * RBN; e += kThr) {
-      const int r = e / RBN, cc = e % RBN;
-      *reinterpret_cast<u32x4*>(&sG[lds_off<RBN>(r, 8 * cc)]) = load16(Gb + sbase + size_t(r) * N + 8 * cc);
-    }
+    rx.template store<true>(sX, tid);
+    rd.template store<true>(sDY, tid);             // read by rows and transposed
+    if constexpr (!kAhead) rg.load(Gb + sbase, 0, P, N, 0, tid);
+    rg.template store<true>(sG, tid);              // read by rows and transposed
     __syncthreads();
+    if (kAhead && hk + 1 < hps) fetch(h + 1);
 
     const float dts = sdt[s], a2s = sA2[s], els = sEl[s];
     u32x4 xr[P / 16];
@@ -213,7 +260,7 @@ __global__ __launch_bounds__(64 * NB) void bwd_s_kernel(
 #pragma unroll
         for (int kk = 0; kk < P / 16; ++kk) {
           const int kb = 16 * kk + 8 * g2;
-          accT[nt] = mfma32x32x16(frag_tr<RBN>(sG, kb, kb + 4, 32 * nt, lane), xs[kk], accT[nt]);
+          accT[nt] = mfma32x32x16(frag_tr<RBN, true>(sG, kb, kb + 4, 32 * nt, lane), xs[kk], accT[nt]);
         }
     }
 
@@ -255,7 +302,7 @@ __global__ __launch_bounds__(64 * NB) void bwd_s_kernel(
       const int joP = 32 * j * P;
 #pragma unroll
       for (int pt = 0; pt < P / 32; ++pt) {
-        const int o0 = toff(RBPc{}, 0, pt) + joP, o1 = toff(RBPc{}, 1, pt) + joP;
+        const int o0 = toff(RBPc{}, kRows{}, 0, pt) + joP, o1 = toff(RBPc{}, kRows{}, 1, pt) + joP;
         const u32x2 a0 = lds_read_tr16(sDY, o0), a1 = lds_read_tr16(sDY, o1);
         const u32x2 b0 = lds_read_tr16(sDY, o0 + 16 * P), b1 = lds_read_tr16(sDY, o1 + 16 * P);
         adx[pt] = mfma32x32x16(u32x4{a0[0], a0[1], a1[0], a1[1]}, mga, adx[pt]);
@@ -265,7 +312,7 @@ __global__ __launch_bounds__(64 * NB) void bwd_s_kernel(
       const int joN = 32 * j * N;
 #pragma unroll
       for (int nt = 0; nt < N / 32; ++nt) {
-        const int o0 = toff(RBNc{}, 0, nt) + joN, o1 = toff(RBNc{}, 1, nt) + joN;
+        const int o0 = toff(RBNc{}, kPlain{}, 0, nt) + joN, o1 = toff(RBNc{}, kPlain{}, 1, nt) + joN;
         const u32x2 a0 = lds_read_tr16(sC, o0), a1 = lds_read_tr16(sC, o1);
         const u32x2 b0 = lds_read_tr16(sC, o0 + 16 * N), b1 = lds_read_tr16(sC, o1 + 16 * N);
         accT[nt] = mfma32x32x16(u32x4{a0[0], a0[1], a1[0], a1[1]}, zga, accT[nt]);
@@ -361,15 +408,20 @@ __global__ __launch_bounds__(64 * NB) void bwd_l_kernel(
   const long r0 = long(b) * T + long(c) * Q;        // first token row of the chunk
   const int nv = min(Q, T - c * Q);                 // valid tokens
 
-  stage_rows<RBN, kThr>(sB, Bm, r0, nv, Q, size_t(G) * N, size_t(g) * N, tid);
-  stage_rows<RBN, kThr>(sC, Cm, r0, nv, Q, size_t(G) * N, size_t(g) * N, tid);
+  {
+    RowStage<RBN, Q, kThr> rb, rc;
+    rb.load(Bm, r0, nv, size_t(G) * N, size_t(g) * N, tid);
+    rc.load(Cm, r0, nv, size_t(G) * N, size_t(g) * N, tid);
+    rb.template store<false>(sB, tid);             // read transposed only
+    rc.template store<true>(sC, tid);              // read by rows
+  }
   stage_tiles<ntile, kThr>(sT, CBf + ((size_t(b) * nc + c) * G + g) * ntile * 1024, tid);
 
   const int q16 = lane & 15;
   const int mcol = 16 * ((lane >> 4) & 1) + 4 * (q16 & 3);
   auto toff = [&](auto rb, int u, int mt) {
     constexpr int RB = decltype(rb)::value;
-    return lds_off<RB>(4 * g2 + 8 * u + (q16 >> 2), 32 * mt + mcol);
+    return lds_off<RB>(4 * g2 + 8 * u + (q16 >> 2), 32 * mt + mcol);   // sB: plain swizzle
   };
   using RBNc = std::integral_constant<int, RBN>;
 
@@ -385,28 +437,62 @@ __global__ __launch_bounds__(64 * NB) void bwd_l_kernel(
 #pragma unroll
   for (int nt = 0; nt < N / 32; ++nt) accT[nt] = zero16();
 
+  // A head's operands (tables, x and dy rows, H_c), loaded together; with
+  // few registers per thread (kAhead) the next head's loads are issued right
+  // after this head's staging, under this head's compute.
+  constexpr int PH = (P * RBN + kThr - 1) / kThr;
+  RowStage<RBP, Q, kThr> rx, rd;
+  f32x4 hv[PH][2];
+  constexpr bool kAhead = 2 * RowStage<RBP, Q, kThr>::PER + 2 * PH <= 16;
+  float ta = 0.f, tb = 0.f, td = 0.f;
+  auto fetch_h = [&](size_t sbase) {
+#pragma unroll
+    for (int m = 0; m < PH; ++m) {
+      const int e = tid + m * kThr;
+      if (e < P * RBN) {
+        const float* hr = Hst + sbase + size_t(e / RBN) * N + 8 * (e % RBN);
+        hv[m][0] = *reinterpret_cast<const f32x4*>(hr);
+        hv[m][1] = *reinterpret_cast<const f32x4*>(hr + 4);
+      }
+    }
+  };
+  auto fetch = [&](int h) {
+    const size_t arow = ((size_t(b) * H + h) * nc + c) * Q;
+    if (tid < Q) {
+      ta = Acs[arow + tid];
+      tb = Acs[arow + (tid | 31)];
+      td = dtq[arow + tid];
+    }
+    rx.load(x, r0, nv, size_t(H) * P, size_t(h) * P, tid);
+    rd.load(dy, r0, nv, size_t(H) * P, size_t(h) * P, tid);
+    if constexpr (kAhead) fetch_h(((size_t(b) * nc + c) * H + h) * size_t(P) * N);
+  };
+  if (hps > 0) fetch(h0);
+
   for (int hk = 0; hk < hps; ++hk) {
     const int h = h0 + hk;
     const size_t arow = ((size_t(b) * H + h) * nc + c) * Q;
     const size_t sbase = ((size_t(b) * nc + c) * H + h) * size_t(P) * N;
     __syncthreads();   // the previous head's tiles and tables are consumed
-    for (int t = tid; t < Q; t += kThr) {
-      const float a2 = Acs[arow + t] * kLog2e, d = dtq[arow + t];
-      sA2[t] = a2;
-      sF[t] = __builtin_amdgcn_exp2f(Acs[arow + (t | 31)] * kLog2e - a2) * d;   // <= dt
-      sL[t] = __builtin_amdgcn_logf(d) - a2;                                     // -inf where dt = 0
+    if (tid < Q) {
+      const float a2 = ta * kLog2e;
+      sA2[tid] = a2;
+      sF[tid] = __builtin_amdgcn_exp2f(tb * kLog2e - a2) * td;   // <= dt
+      sL[tid] = __builtin_amdgcn_logf(td) - a2;                    // -inf where dt = 0
     }
-    stage_rows<RBP, kThr>(sX, x, r0, nv, Q, size_t(H) * P, size_t(h) * P, tid);
-    stage_rows<RBP, kThr>(sDY, dy, r0, nv, Q, size_t(H) * P, size_t(h) * P, tid);
-    for (int e = tid; e < P * RBN; e += kThr) {
-      const int r = e / RBN, cc = e % RBN;
-      const f32x4 h0v = *reinterpret_cast<const f32x4*>(Hst + sbase + size_t(r) * N + 8 * cc);
-      const f32x4 h1v = *reinterpret_cast<const f32x4*>(Hst + sbase + size_t(r) * N + 8 * cc + 4);
-      *reinterpret_cast<u32x4*>(&sH[lds_off<RBN>(r, 8 * cc)]) =
-          u32x4{pack_bf16x2(h0v[0], h0v[1]), pack_bf16x2(h0v[2], h0v[3]), pack_bf16x2(h1v[0], h1v[1]),
-                pack_bf16x2(h1v[2], h1v[3])};
+    rx.template store<true>(sX, tid);
+    rd.template store<true>(sDY, tid);
+    if constexpr (!kAhead) fetch_h(sbase);
+#pragma unroll
+    for (int m = 0; m < PH; ++m) {
+      const int e = tid + m * kThr;
+      if (e < P * RBN)
+        *reinterpret_cast<u32x4*>(&sH[lds_off<RBN>(e / RBN, 8 * (e % RBN))]) =
+            u32x4{pack_bf16x2(hv[m][0][0], hv[m][0][1]), pack_bf16x2(hv[m][0][2], hv[m][0][3]),
+                  pack_bf16x2(hv[m][1][0], hv[m][1][1]), pack_bf16x2(hv[m][1][2], hv[m][1][3])};
     }
     __syncthreads();
+    if (kAhead && hk + 1 < hps) fetch(h + 1);
 
     const float a2l = sA2[l];
     const float el = __builtin_amdgcn_exp2f(a2l);

@@ -38,7 +38,8 @@
 //      bf16, is the B operand of y^T += X^T G^T under a k permutation that the
 //      X operand reproduces: x sits in LDS in natural token-major order
 //      (swizzled 16-byte chunks) and is read transposed with
-//      ds_read_b64_tr_b16. Tiles are loaded one tile ahead of use.
+//      ds_read_b64_tr_b16. Tiles are loaded one tile ahead of use, into two
+//      buffers used in turn.
 //   3. + D x (x from the same LDS tile), bf16 rounding, 8-byte stores of 4
 //      consecutive p.
 #include "mfma_util.h"
@@ -50,7 +51,9 @@ constexpr int kThreads = 256;
 constexpr int kSC = 256;          // tokens per super-chunk
 constexpr float kLog2e = 1.4426950408889634f;
 
-template <int N, int P, bool HLDS>
+// VARLEN: chunk rows from the chunk table tab (packed sequences), else the
+// equal-length layout (tab unused).
+template <int N, int P, bool HLDS, bool VARLEN>
 __global__ __launch_bounds__(kThreads) void chunk_scan_mfma_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ CB, const uint16_t* __restrict__ Cm,
     const float* __restrict__ Acs, const float* __restrict__ dtq, const uint16_t* __restrict__ Hb,
@@ -79,7 +82,8 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_mfma_kernel(
   const int ntile = lpc * (lpc + 1) / 2;
   // token rows of the super-chunk's chunks (ci = 0 .. cps-1); n = 0 past the last chunk
   auto crows = [&](int ci) {
-    return c0 + ci < nc ? chunk_rows(tab, b, c0 + ci, T, Q) : ChunkRows{0, 0};
+    return c0 + ci < nc ? chunk_rows(VARLEN ? tab : static_cast<const int4*>(nullptr), b, c0 + ci, T, Q)
+                        : ChunkRows{0, 0};
   };
   // fast: every row of the super-chunk is a valid token and the rows are
   // consecutive token rows (always so for equal-length batch rows);
@@ -293,12 +297,18 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_mfma_kernel(
         acc[pb] = mfma32x32x16(u32x4{b0[0], b0[1], b1[0], b1[1]}, gb, acc[pb]);
       }
     };
+    // off-diagonal tiles two at a time, ping-pong buffers (the tile after
+    // next loads while the current one is applied; no register copies)
+    u32x4 tB[2];
+    int jj = 0;
 #pragma unroll 1
-    for (int jj = 0; jj < irel; ++jj) {
-      u32x4 tcur[2] = {tnext[0], tnext[1]};
-      if (jj + 1 < irel) load_tile(jj + 1, tnext);
-      apply(jj, tcur, false);
+    for (; jj + 1 < irel; jj += 2) {
+      load_tile(jj + 1, tB);
+      apply(jj, tnext, false);
+      if (jj + 2 < irel) load_tile(jj + 2, tnext);
+      apply(jj + 1, tB, false);
     }
+    if (jj < irel) apply(jj, tnext, false);
     apply(irel, tdiag, true);
 
     // ---- epilogue: + D x (x re-read, from L2), round, store 4 consecutive p (8 bytes) per run
@@ -334,16 +344,16 @@ hipError_t launch_np(const FwdShape& s, const void* x, const uint16_t* CB, const
   const int cps = kSC / s.Q;
   const int nsc = (s.nc + cps - 1) / cps;   // = ceil(T / 256) for equal-length rows
   const long blocks = long(s.b) * nsc * s.H;
-  if (s.Q == kSC)  // one chunk per super-chunk: its H_c^T is staged in LDS
-    hipExtLaunchKernelGGL((chunk_scan_mfma_kernel<N, P, true>), dim3(unsigned(blocks)), dim3(kThreads), 0,
-                          st, ev.start, ev.stop, 0, static_cast<const uint16_t*>(x), CB,
-                          static_cast<const uint16_t*>(C), Acs, dtq, Hb, D, static_cast<uint16_t*>(y), tab,
-                          s.T, s.H, s.G, s.Q, s.nc, nsc);
+  auto go = [&](auto kern) {
+    hipExtLaunchKernelGGL(kern, dim3(unsigned(blocks)), dim3(kThreads), 0, st, ev.start, ev.stop, 0,
+                          static_cast<const uint16_t*>(x), CB, static_cast<const uint16_t*>(C), Acs, dtq, Hb, D,
+                          static_cast<uint16_t*>(y), tab, s.T, s.H, s.G, s.Q, s.nc, nsc);
+  };
+  // one chunk per super-chunk: its H_c^T is staged in LDS
+  if (s.Q == kSC)
+    tab ? go(chunk_scan_mfma_kernel<N, P, true, true>) : go(chunk_scan_mfma_kernel<N, P, true, false>);
   else
-    hipExtLaunchKernelGGL((chunk_scan_mfma_kernel<N, P, false>), dim3(unsigned(blocks)), dim3(kThreads), 0,
-                          st, ev.start, ev.stop, 0, static_cast<const uint16_t*>(x), CB,
-                          static_cast<const uint16_t*>(C), Acs, dtq, Hb, D, static_cast<uint16_t*>(y), tab,
-                          s.T, s.H, s.G, s.Q, s.nc, nsc);
+    tab ? go(chunk_scan_mfma_kernel<N, P, false, true>) : go(chunk_scan_mfma_kernel<N, P, false, false>);
   return hipGetLastError();
 }
 
