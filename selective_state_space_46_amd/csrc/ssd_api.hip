@@ -234,11 +234,21 @@ ssd_status ssd_chunk_scan_fwd_timed(const void* x, const void* dt, const float* 
   } else if (launch_chunk_cumsum(s, dtype, dt, A, Acs, dtq, hs, ev(0)) != hipSuccess) {
     return SSD_ERR_HIP;
   }
-  const hipError_t se = mfma ? launch_chunk_state_mfma(s, x, B, C, dt, A, Acs, dtq, S, CB, nullptr, hs, ev(1))
-                             : launch_chunk_state(s, dtype, x, B, Acs, dtq, S, hs, ev(1));
-  if (se != hipSuccess) return SSD_ERR_HIP;
-  if (launch_state_passing(s, S, Hb, Acs, init_state, final_state, hs, ev(2)) != hipSuccess)
-    return SSD_ERR_HIP;
+  if (mfma && chunk_state_chain_ok(s)) {
+    // chunk states and state passing in one launch: stage 2 launches nothing
+    if (launch_chunk_state_chain(s, x, B, C, dt, A, Acs, dtq, Hb, init_state, final_state, CB, hs, ev(1)) !=
+        hipSuccess)
+      return SSD_ERR_HIP;
+    const StageEv e2 = ev(2);
+    if (e2.start && hipEventRecord(e2.start, hs) != hipSuccess) return SSD_ERR_HIP;
+    if (e2.stop && hipEventRecord(e2.stop, hs) != hipSuccess) return SSD_ERR_HIP;
+  } else {
+    const hipError_t se = mfma ? launch_chunk_state_mfma(s, x, B, C, dt, A, Acs, dtq, S, CB, nullptr, hs, ev(1))
+                               : launch_chunk_state(s, dtype, x, B, Acs, dtq, S, hs, ev(1));
+    if (se != hipSuccess) return SSD_ERR_HIP;
+    if (launch_state_passing(s, S, Hb, Acs, init_state, final_state, hs, ev(2)) != hipSuccess)
+      return SSD_ERR_HIP;
+  }
   if (launch_chunk_scan(s, dtype, mfma, x, B, C, Acs, dtq, S, Hb, CB, D, y, hs, ev(3)) != hipSuccess)
     return SSD_ERR_HIP;
   return SSD_OK;

@@ -176,6 +176,17 @@ hipError_t launch_chunk_state_mfma(const FwdShape& s, const void* x, const void*
                                    float* S, uint16_t* CB, const int4* tab, hipStream_t st,
                                    const StageEv& ev = StageEv{});
 
+// Chunk states and state passing fused (equal-length rows, bf16 MFMA path):
+// writes Acs, dtq, the C B^T tiles and Hb (states entering each chunk, bf16)
+// and final (fp32, may be null), without the fp32 chunk states. Only for the
+// shapes chunk_state_chain_ok accepts (enough (b, h, 32-column) chains to
+// fill the chip; dstate 128 or 256; chunk_len a multiple of 64).
+bool chunk_state_chain_ok(const FwdShape& s);
+hipError_t launch_chunk_state_chain(const FwdShape& s, const void* x, const void* B, const void* C,
+                                    const void* dt, const float* A, float* Acs, float* dtq, uint16_t* Hb,
+                                    const float* init, float* fin, uint16_t* CB, hipStream_t st,
+                                    const StageEv& ev = StageEv{});
+
 // Hb == nullptr: states entering each chunk overwrite S in place (fp32);
 // otherwise they are written to Hb as bf16 and S is left as it was.
 hipError_t launch_state_passing(const FwdShape& s, float* S, uint16_t* Hb, const float* Acs,

@@ -1,0 +1,80 @@
+"""GPU parity of the fused chunk-state + state-passing launch (the forward
+path for equal-length rows with dstate 128 or 256 and chunk_len a multiple
+of 64 whose (batch, head, 32-column) chains fill a 256-unit MI355X in one
+round: 256 .. 512 chains at dstate 128, 256 at dstate 256) against the fp64
+oracle, through the C ABI.
+
+Every shape here takes that path. Bar as for the other
+bf16 forward cases: relative L2 <= 1e-2 on y and on the final state. Cases
+span several chunks with a ragged tail, every chunk length the path takes,
+both dstate values, every headdim (one to four 32-column chains per head),
+groups, no initial state, the shortest rows, fast decays and long rows."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from ssd_testlib import columns_of, gpu_fwd, rel_l2, sample_columns
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-2
+
+
+def _w(b, T, H, P, N, G, q, seed, init=True, dt_mode="softplus"):
+    chains = b * H * (P // 32)
+    assert 256 <= chains <= (512 if N == 128 else 256), "shape must take the fused path"
+    return workloads.with_shape(workloads.MAMBA2_130M, batch=b, seqlen=T, nheads=H, headdim=P, dstate=N,
+                                ngroups=G, chunk_len=q, init="normal0.1" if init else "zero",
+                                dt_mode=dt_mode, seed=seed)
+
+
+def _check(w):
+    inp = workloads.make_fwd_inputs(w)
+    y, fin = gpu_fwd(inp, "bf16", w.chunk_len)
+    y_ref, fin_ref = oracle.ssd_fwd(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"], inp["init"])
+    ey, ef = rel_l2(y, y_ref), rel_l2(fin, fin_ref)
+    print(f"[chain b={w.batch} T={w.seqlen} H={w.nheads} P={w.headdim} N={w.dstate} G={w.ngroups} "
+          f"Q={w.chunk_len}] y={ey:.3e} final={ef:.3e}", flush=True)
+    assert np.all(np.isfinite(y)) and np.all(np.isfinite(fin))
+    assert ey <= TOL and ef <= TOL, (ey, ef)
+
+
+@pytest.mark.parametrize("q", [64, 128, 256])
+def test_chain_chunk_lengths_ragged(q):
+    _check(_w(2, 3 * 256 + 77, 64, 64, 128, 1, q, seed=8000 + q))
+
+
+@pytest.mark.parametrize("P,N,H", [(32, 128, 128), (128, 128, 32), (32, 256, 128), (64, 256, 64), (128, 256, 32)])
+def test_chain_shapes(P, N, H):
+    _check(_w(2, 300, H, P, N, 1, 256, seed=8100 + P + N))
+
+
+def test_chain_groups_no_init():
+    _check(_w(2, 520, 64, 64, 128, 4, 128, seed=8200, init=False))
+
+
+@pytest.mark.parametrize("T", [1, 63, 64, 65])
+def test_chain_short_rows(T):
+    _check(_w(4, T, 64, 64, 128, 2, 64, seed=8300 + T))
+
+
+def test_chain_fast_decay():
+    """dt |A| up to 32 per token: the chunk decays underflow toward zero"""
+    _check(_w(2, 600, 64, 64, 128, 1, 256, seed=8400, dt_mode="fast"))
+
+
+def test_chain_long_row():
+    """8192-token rows: 128 slices walked in order by every chain (checked on
+    sampled (b, h, p) columns, which the oracle computes one by one)"""
+    w = _w(2, 8192, 64, 64, 128, 1, 256, seed=8500)
+    inp = workloads.make_fwd_inputs(w)
+    y, fin = gpu_fwd(inp, "bf16", w.chunk_len)
+    cols = sample_columns(w.batch, w.nheads, w.headdim, 32, seed=w.seed)
+    yc_ref, fc_ref = oracle.ssd_fwd_columns(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"],
+                                            inp["init"], cols)
+    yc, fc = columns_of(y, fin, cols)
+    ey, ef = rel_l2(yc, yc_ref), rel_l2(fc, fc_ref)
+    print(f"[chain long row] sampled {len(cols)} columns: y={ey:.3e} final={ef:.3e}", flush=True)
+    assert np.all(np.isfinite(y))
+    assert ey <= TOL and ef <= TOL, (ey, ef)
