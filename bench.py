@@ -6,8 +6,10 @@
 
 One step = one ssd_chunk_scan_fwd call over one batch of the workload (on the
 bf16 matrix-core path: chunk_state with the cumulative sums and C B^T tiles in
-the same launch, state_passing, chunk_scan), inputs resident in HBM. The headline workload is the Mamba-2-130M-shaped layer (batch 8,
-T 2048, H 24, P 64, N 128, 1 group, chunk 256, bf16 inputs, fp32
+the same launch -- for the headline shape also the passing of states between
+chunks, see ssd_chunk_scan_fwd_fused_states -- then chunk_scan), inputs
+resident in HBM. The headline workload is the Mamba-2-130M-shaped layer
+(batch 8, T 2048, H 24, P 64, N 128, 1 group, chunk 256, bf16 inputs, fp32
 accumulation and state). Prints ONE JSON line on stdout; progress goes to
 stderr.
 
@@ -100,7 +102,7 @@ class Hip:
 # Algorithmic work per launch (each kernel's minimal I/O and useful flops)
 # --------------------------------------------------------------------------
 
-def fwd_work(w: workloads.FwdWorkload, with_init: bool) -> dict:
+def fwd_work(w: workloads.FwdWorkload, with_init: bool, fused: bool = False) -> dict:
     b, T, H, P, N, G, Q = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk_len
     nc = -(-T // Q)
     e = 2 if w.dtype == "bf16" else 4
@@ -125,11 +127,16 @@ def fwd_work(w: workloads.FwdWorkload, with_init: bool) -> dict:
         state = {"bytes": x + 2 * bc + dtb + 2 * acs + st + cbt,
                  "flops": 2 * b * T * H * N * P + b * T * H * 2 + b * nc * G * 2 * N * tri}
         cumsum = {"bytes": 0, "flops": 0}
+    passing = {"bytes": st + hst + 4 * b * H * nc + fst * (2 if with_init else 1),
+               "flops": 2 * b * nc * H * N * P}
+    if fused:  # one launch: the fp32 chunk states stay on chip; it writes the bf16 passed states and final
+        state = {"bytes": x + 2 * bc + dtb + 2 * acs + cbt + hst + fst * (2 if with_init else 1),
+                 "flops": state["flops"] + passing["flops"]}
+        passing = {"bytes": 0, "flops": 0}
     return {
         "chunk_cumsum": cumsum,
         "chunk_state": state,
-        "state_passing": {"bytes": st + hst + 4 * b * H * nc + fst * (2 if with_init else 1),
-                          "flops": 2 * b * nc * H * N * P},
+        "state_passing": passing,
         "chunk_scan": {"bytes": 2 * x + (bc + cbt if mfma else 2 * bc) + 2 * acs + hst,
                        "flops": b * nc * H * (2 * P * tri + 2 * Q * N * P)
                        + (0 if mfma else b * nc * G * 2 * N * tri)},
@@ -502,7 +509,10 @@ def main():
     cold = bench_fwd(hip, w, max(3, args.steps // 4), 1, cold=True)
     log(f"[bench] cold (Infinity Cache flushed): {cold['ms_per_step']:.4f} ms/step")
 
-    work = fwd_work(w, w.init != "zero")
+    import selective_state_space_46_amd as ssd
+    fused = ssd.ssd_chunk_scan_fwd_fused_states(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups,
+                                                w.chunk_len, ssd.SSD_BF16 if w.dtype == "bf16" else ssd.SSD_F32)
+    work = fwd_work(w, w.init != "zero", fused)
     kernels = {}
     for s in STAGES:
         if work[s]["bytes"] == 0:
@@ -512,7 +522,7 @@ def main():
                       "GB_per_s": round(work[s]["bytes"] / (ms * 1e-3) / 1e9, 1),
                       "TFLOP_per_s": round(work[s]["flops"] / (ms * 1e-3) / 1e12, 2),
                       "alg_bytes": work[s]["bytes"], "alg_flops": work[s]["flops"]}
-    dom = max(STAGES, key=lambda s: r["stage_ms"][s])
+    dom = max((s for s in STAGES if work[s]["bytes"]), key=lambda s: r["stage_ms"][s])
     dms = r["stage_ms"][dom]
     achieved = work[dom]["bytes"] / (dms * 1e-3) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",

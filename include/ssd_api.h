@@ -128,6 +128,21 @@ SSD_API ssd_status ssd_chunk_scan_fwd(const void *x, const void *dt, const float
                               void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * Whether ssd_chunk_scan_fwd with these sizes runs the chunk states and the
+ * passing of states between chunks as one launch on the current HIP device
+ * (1) or as two (0; also for sizes the call would reject). The results agree
+ * up to rounding either way. The fused launch walks each (batch row, head,
+ * 32 columns of headdim) through its chunks in order with the running state
+ * on chip and writes only the bf16 states entering each chunk; it is used for
+ * the bf16 matrix-core path with dstate 128 or 256 and chunk_len a multiple
+ * of 64 when those walks fill the device in one round (between one and two
+ * per compute unit at dstate 128, one at dstate 256). It reads the device's
+ * compute-unit count, so it needs a current HIP device (0 without one).
+ */
+SSD_API int ssd_chunk_scan_fwd_fused_states(int batch, int seqlen, int nheads, int headdim, int dstate,
+                                            int ngroups, int chunk_len, ssd_dtype dtype);
+
+/*
  * Measurement variant of ssd_chunk_scan_fwd: identical computation, and it
  * times its four stages, in launch order: [0] cumulative sums, [1] chunk
  * states, [2] state passing, [3] chunk outputs. stage_events holds 8
@@ -137,7 +152,9 @@ SSD_API ssd_status ssd_chunk_scan_fwd(const void *x, const void *dt, const float
  * (hipExtLaunchKernel), so hipEventElapsedTime on the pair gives the kernel's
  * execution time on `stream`. On the bf16 matrix-core path one launch
  * computes the cumulative sums, the C B^T tiles and the chunk states; stage 0
- * launches nothing there and its two events are recorded back to back.
+ * launches nothing there and its two events are recorded back to back. Where
+ * ssd_chunk_scan_fwd_fused_states is 1, stage [1] also passes the states
+ * between chunks and stage [2] launches nothing the same way.
  * stage_events may be NULL (then it is ssd_chunk_scan_fwd). A failed event
  * record returns SSD_ERR_HIP.
  */

@@ -9,6 +9,7 @@ the entry points raises.
 
 Entry points (same names as the C ABI):
     ssd_chunk_scan_fwd_workspace(...) -> bytes
+    ssd_chunk_scan_fwd_fused_states(...) -> bool (one launch for chunk states + passing)
     ssd_chunk_scan_fwd(x, dt, A, B, C, D, init_state, chunk_len) -> (y, final_state)
     ssd_state_update(state, x, dt, A, B, C, D) -> y     (state updated in place)
     ssd_status_string(code) -> str
@@ -31,6 +32,7 @@ from typing import Optional, Tuple
 __all__ = [
     "SSD_F32", "SSD_BF16", "SSDError", "lib", "lib_path",
     "ssd_chunk_scan_fwd_workspace", "ssd_chunk_scan_fwd", "ssd_chunk_scan_fwd_timed",
+    "ssd_chunk_scan_fwd_fused_states",
     "ssd_state_update", "ssd_status_string", "ssd_chunk_scan_fwd_varlen",
     "ssd_chunk_scan_fwd_varlen_workspace", "ssd_gated_rmsnorm", "ssd_causal_conv1d_fwd",
     "ssd_causal_conv1d_update", "ssd_chunk_scan_bwd_workspace", "ssd_chunk_scan_bwd",
@@ -73,6 +75,8 @@ def lib() -> ctypes.CDLL:
     vp, i32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
     L.ssd_chunk_scan_fwd_workspace.argtypes = [i32] * 7 + [i32]
     L.ssd_chunk_scan_fwd_workspace.restype = sz
+    L.ssd_chunk_scan_fwd_fused_states.argtypes = [i32] * 7 + [i32]
+    L.ssd_chunk_scan_fwd_fused_states.restype = i32
     L.ssd_chunk_scan_fwd.argtypes = [vp] * 9 + [i32] * 7 + [i32, vp, sz, vp]
     L.ssd_chunk_scan_fwd.restype = i32
     L.ssd_chunk_scan_fwd_timed.argtypes = [vp] * 9 + [i32] * 7 + [i32, vp, sz, vp, vp]
@@ -108,6 +112,14 @@ def ssd_chunk_scan_fwd_workspace(batch: int, seqlen: int, nheads: int, headdim: 
                                  ngroups: int, chunk_len: int, dtype: int) -> int:
     return int(lib().ssd_chunk_scan_fwd_workspace(batch, seqlen, nheads, headdim, dstate, ngroups,
                                                   chunk_len, dtype))
+
+
+def ssd_chunk_scan_fwd_fused_states(batch: int, seqlen: int, nheads: int, headdim: int, dstate: int,
+                                    ngroups: int, chunk_len: int, dtype: int) -> bool:
+    """True when the forward runs chunk states and state passing as one launch
+    on the current device (see ssd_api.h)."""
+    return bool(lib().ssd_chunk_scan_fwd_fused_states(batch, seqlen, nheads, headdim, dstate, ngroups,
+                                                      chunk_len, dtype))
 
 
 # --------------------------------------------------------------------------

@@ -160,6 +160,15 @@ size_t ssd_chunk_scan_fwd_workspace(int batch, int seqlen, int nheads, int headd
   return ws_layout(s, use_mfma_path(s, dtype)).total;
 }
 
+int ssd_chunk_scan_fwd_fused_states(int batch, int seqlen, int nheads, int headdim, int dstate,
+                                    int ngroups, int chunk_len, ssd_dtype dtype) {
+  if (!dtype_ok(dtype) || !is_chunk_ok(chunk_len)) return 0;
+  if (check_dims(batch, seqlen, nheads, headdim, dstate, ngroups) != SSD_OK) return 0;
+  const FwdShape s = make_shape(batch, seqlen, nheads, headdim, dstate, ngroups, chunk_len);
+  if (s.nc > 65535 || !use_mfma_path(s, dtype) || !grids_fit(s, true)) return 0;
+  return chunk_state_chain_ok(s) ? 1 : 0;
+}
+
 ssd_status ssd_chunk_scan_fwd_timed(const void* x, const void* dt, const float* A, const void* B,
                                     const void* C, const float* D, const float* init_state,
                                     void* y, float* final_state, int batch, int seqlen,

@@ -35,7 +35,19 @@ def test_header_declares_the_entry_points():
                                        "ssd_status_string", "ssd_gated_rmsnorm",
                                        "ssd_causal_conv1d_fwd", "ssd_causal_conv1d_update",
                                        "ssd_chunk_scan_fwd_varlen", "ssd_chunk_scan_fwd_varlen_workspace",
-                                       "ssd_chunk_scan_bwd", "ssd_chunk_scan_bwd_workspace"}
+                                       "ssd_chunk_scan_bwd", "ssd_chunk_scan_bwd_workspace",
+                                       "ssd_chunk_scan_fwd_fused_states"}
+
+
+def test_fused_states_query_rejects_what_the_forward_rejects():
+    """0 for sizes the forward would reject (answered before any device query)
+    and for the generic fp32 path, which never fuses."""
+    q = ssd.ssd_chunk_scan_fwd_fused_states
+    assert not q(8, 2048, 24, 64, 128, 1, 256, 7)            # bad dtype
+    assert not q(8, 2048, 24, 64, 128, 1, 48, ssd.SSD_BF16)  # bad chunk length
+    assert not q(0, 2048, 24, 64, 128, 1, 256, ssd.SSD_BF16)
+    assert not q(8, 2048, 24, 64, 128, 5, 256, ssd.SSD_BF16)  # groups must divide heads
+    assert not q(8, 2048, 24, 64, 128, 1, 256, ssd.SSD_F32)
 
 
 def test_library_exports_every_declared_symbol(L):

@@ -30,6 +30,9 @@ def _w(b, T, H, P, N, G, q, seed, init=True, dt_mode="softplus"):
 
 
 def _check(w):
+    import selective_state_space_46_amd as ssd
+    assert ssd.ssd_chunk_scan_fwd_fused_states(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups,
+                                               w.chunk_len, ssd.SSD_BF16)
     inp = workloads.make_fwd_inputs(w)
     y, fin = gpu_fwd(inp, "bf16", w.chunk_len)
     y_ref, fin_ref = oracle.ssd_fwd(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"], inp["init"])
@@ -67,7 +70,9 @@ def test_chain_fast_decay():
 def test_chain_long_row():
     """8192-token rows: 128 slices walked in order by every chain (checked on
     sampled (b, h, p) columns, which the oracle computes one by one)"""
+    import selective_state_space_46_amd as ssd
     w = _w(2, 8192, 64, 64, 128, 1, 256, seed=8500)
+    assert ssd.ssd_chunk_scan_fwd_fused_states(2, 8192, 64, 64, 128, 1, 256, ssd.SSD_BF16)
     inp = workloads.make_fwd_inputs(w)
     y, fin = gpu_fwd(inp, "bf16", w.chunk_len)
     cols = sample_columns(w.batch, w.nheads, w.headdim, 32, seed=w.seed)
@@ -78,3 +83,13 @@ def test_chain_long_row():
     print(f"[chain long row] sampled {len(cols)} columns: y={ey:.3e} final={ef:.3e}", flush=True)
     assert np.all(np.isfinite(y))
     assert ey <= TOL and ef <= TOL, (ey, ef)
+
+
+def test_fused_path_choice_on_the_workloads():
+    """The 130M-shaped layer (384 chains) takes the fused launch; the 2.7B-shaped
+    one (640 chains: two rounds) and the 128K-token row (48 chains) do not."""
+    import selective_state_space_46_amd as ssd
+    for w, want in ((workloads.MAMBA2_130M, True), (workloads.MAMBA2_2P7B, False), (workloads.LONG_128K, False)):
+        got = ssd.ssd_chunk_scan_fwd_fused_states(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups,
+                                                  w.chunk_len, ssd.SSD_BF16)
+        assert got == want, w.name
