@@ -117,7 +117,13 @@ def ssd_chunk_scan_fwd_workspace(batch: int, seqlen: int, nheads: int, headdim: 
 def ssd_chunk_scan_fwd_fused_states(batch: int, seqlen: int, nheads: int, headdim: int, dstate: int,
                                     ngroups: int, chunk_len: int, dtype: int) -> bool:
     """True when the forward runs chunk states and state passing as one launch
-    on the current device (see ssd_api.h)."""
+    on the current device (see ssd_api.h). The library asks the HIP runtime
+    for the device's compute units; torch's runtime is brought up first (as
+    every tensor-taking call here does implicitly), since a process whose
+    first HIP call comes from the library leaves torch without a device."""
+    import torch
+    if torch.cuda.is_available():
+        torch.cuda.current_device()
     return bool(lib().ssd_chunk_scan_fwd_fused_states(batch, seqlen, nheads, headdim, dstate, ngroups,
                                                       chunk_len, dtype))
 

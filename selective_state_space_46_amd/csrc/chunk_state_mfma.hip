@@ -280,37 +280,51 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma_kernel(
 // the recurrence of state_passing.hip folded into the chunk-state product
 // (youngju.dev "Mamba / selective SSM", "SSDアルゴリズムとチャンク分割": the
 // state handed from chunk to chunk; Qiita "Mamba-2" article, section 4.2,
-// steps 2 and 3). A work-group owns one (batch row, head, 32 columns p of the
-// head) and walks that row's chunks in order, its running state held in the
-// fp32 accumulators of the matrix cores: at a chunk's start the accumulators
-// (= H_c) go out as bf16 for chunk_scan, are scaled by the chunk's decay, and
-// the chunk's products then accumulate on top, leaving H_{c+1}. The fp32 chunk
-// states S_c never reach HBM (the two-kernel form writes and re-reads them).
+// steps 2 and 3). A work-group owns one batch row and 64 consecutive columns
+// of the flattened (head, p) axis -- two 32-column blocks of one head, or two
+// heads of headdim 32 in one B/C group -- and walks that row's chunks in
+// order, its running states held in the fp32 accumulators of the matrix
+// cores: at a chunk's start the accumulators (= H_c) go out as bf16 for
+// chunk_scan, are scaled by the chunk's decay, and the chunk's products then
+// accumulate on top, leaving H_{c+1}. The fp32 chunk states S_c never reach
+// HBM (the two-kernel form writes and re-reads them).
 //
-// Tokens stream through 64-row slices of B (all of dstate) and x (the 32
-// columns), copied straight from global memory into LDS (global_load_lds,
-// 16 bytes per lane) in their natural swizzled row-major layout, three slices
-// resident: one read while the next two load. The copies use no registers, so
-// two slices stay in flight behind the one being multiplied. The MFMA
-// operands are read transposed (ds_read_b64_tr_b16); the x fragment is scaled
-// by w_s = exp(Acs_{Q-1} - Acs_s) dt_s there and rounded to bf16 once (the
-// same W = w x as chunk_state_mfma_kernel). The product is taken as S[n][p]
-// (rows n, lanes p), so a lane holds four consecutive n of one p: H_c leaves
-// as runs of its [p][n] rows, init and final ([n][p]) as whole rows of p.
+// Tokens stream through 64-row slices of B (all of dstate, shared by the two
+// column blocks) and x (the 64 columns), copied straight from global memory
+// into LDS (global_load_lds, 16 bytes per lane) in a swizzled row-major
+// layout, STAGES slices resident: one read while the others load. The copies
+// use no registers. The MFMA operands are read transposed
+// (ds_read_b64_tr_b16); the x fragment is scaled by
+// w_s = exp(Acs_{Q-1} - Acs_s) dt_s there and rounded to bf16 once (the same
+// W = w x as chunk_state_mfma_kernel). The product is taken as S[n][p] (rows
+// n, lanes p), so a lane holds four consecutive n of one p: H_c leaves as
+// runs of its [p][n] rows, init and final ([n][p]) as whole rows of p.
 //
-// Four compute waves issue only the slice copies; a fifth wave does every
-// global store (H_c through LDS, the chunk's Acs / dt rows) and loads the dt
-// rows two chunks ahead. The vector memory counter counts loads and stores
-// together and the two may complete out of order, so a wave with both in
-// flight waits for all of them at its next wait; the compute waves wait only
-// for their own copies, by count. The two kinds of wave run separate loops
-// that pass the same barriers.
+// Waves: four compute waves (wave w: column block w & 1, n tiles w >> 1,
+// (w >> 1) + 2, ...), one table wave and three copy waves. The table wave
+// builds each chunk's weights and decay one chunk ahead from dt loaded one
+// chunk before that, and writes the Acs / dt rows; the copy waves issue the
+// slice copies and wait for them by count. The vector memory counter counts
+// loads and stores together, and a wait the compiler places for a register
+// load covers everything issued after it, so each kind of memory work sits
+// in a wave of its own: the copy waves hold nothing but copies, the table
+// wave's dt loads are a chunk old when used, and the compute waves only
+// store. All waves pass the same barriers, one per slice.
 // ---------------------------------------------------------------------------
-constexpr int kChainWaves = 8;      // 4 compute waves + 4 store waves
+constexpr int kChainWaves = 8;      // 4 compute, 1 table, 3 copy
 constexpr int kChainThreads = 64 * kChainWaves;
-constexpr int kChainCT = 256;        // compute threads (waves 0..3)
-constexpr int kChainSK = 64;         // tokens per slice
-constexpr int kChainStages = 3;      // slices resident in LDS
+constexpr int kChainSK = 64;        // tokens per slice
+constexpr int kChainCols = 64;      // flattened (head, p) columns per work-group
+
+template <int N>
+struct ChainCfg {
+  static constexpr int STAGES = N == 128 ? 5 : 3;               // slices resident (120 KB)
+  static constexpr int RBB = N / 8, RBX = kChainCols / 8;        // 16-byte chunks per B / x row
+  static constexpr int NCB = kChainSK * RBB / 64, NCX = kChainSK * RBX / 64;   // wave copies per slice
+  static constexpr int OPS = (NCB + NCX + 2) / 3;                // copies per copy wave and slice
+  static constexpr int TPW = N / 64;                             // n tiles per compute wave
+  static_assert((STAGES - 2) * OPS < 64, "copies in flight fit the counter");
+};
 
 // vmcnt(n), the other counters left alone (low four bits of n in bits 3..0,
 // high two in bits 15..14)
@@ -342,6 +356,10 @@ __global__ __launch_bounds__(kChainThreads) void chunk_state_chain_kernel(
     const float* __restrict__ A, float* __restrict__ Acs, float* __restrict__ dtq, uint16_t* __restrict__ Hb,
     const float* __restrict__ init, float* __restrict__ fin, const uint16_t* __restrict__ Cm,
     uint16_t* __restrict__ CB, int T, int H, int G, int Q, int nc, int nchain, long ntiles) {
+  using Cfg = ChainCfg<N>;
+  constexpr int S = Cfg::STAGES, RBB = Cfg::RBB, RBX = Cfg::RBX, NCB = Cfg::NCB, NCX = Cfg::NCX;
+  constexpr int OPS = Cfg::OPS, TPW = Cfg::TPW;
+  constexpr int NHW = P == 32 ? 2 : 1;          // heads per work-group
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = wave_id();  // wave-uniform (scalar register)
   // work-groups past the chains compute C B^T tiles, one per wave
@@ -350,266 +368,267 @@ __global__ __launch_bounds__(kChainThreads) void chunk_state_chain_kernel(
     if (wid < ntiles) chunk_scores_tile<N, false>(Bm, Cm, CB, nullptr, nullptr, T, G, Q, nc, wid, lane);
     return;                                     // no barrier on this path
   }
-  constexpr int PB = 32, NPB = P / PB;
-  constexpr int RBB = N / 8, RBX = PB / 8;      // 16-byte chunks per B row / x row slice
-  constexpr int NCB = kChainSK * RBB / 64;      // wave copies per B slice
-  static_assert(NCB % 4 == 0 && kChainSK * RBX == 256, "slice shape");
-  constexpr int OPS = NCB / 4 + 1;              // copies per compute wave and slice
-  constexpr int TPW = N / 128;                  // 32 x 32 tiles per compute wave
-  constexpr int kHS = N + 8;                    // sH row stride (bf16): aligned 16-byte rows, 2-way writes
-  constexpr int kDtL = kMaxQ / 64;              // dt values per store-wave lane and chunk
-  // one array per slot: distinct LDS objects let the compiler see that reads
-  // of one slot do not alias copies in flight into another
-  __shared__ __attribute__((aligned(16))) uint16_t sB0[kChainSK * N], sB1[kChainSK * N], sB2[kChainSK * N];
-  __shared__ __attribute__((aligned(16))) uint16_t sX0[kChainSK * PB], sX1[kChainSK * PB], sX2[kChainSK * PB];
-  auto slotB = [&](int s) { return s == 0 ? sB0 : s == 1 ? sB1 : sB2; };
-  auto slotX = [&](int s) { return s == 0 ? sX0 : s == 1 ? sX1 : sX2; };
-  __shared__ __attribute__((aligned(16))) uint16_t sH[PB * kHS];
-  __shared__ __attribute__((aligned(16))) float sacs[kMaxQ], sdt[kMaxQ], sw[kMaxQ];
-  __shared__ float sdtq[2][kMaxQ], sred[4];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[S][kChainSK * N];
+  __shared__ __attribute__((aligned(16))) uint16_t sX[S][kChainSK * kChainCols];
+  // chunk c's token weights w_s = exp(Acs_{Q-1} - Acs_s) dt_s and decay
+  // exp(Acs_{Q-1}) of head h0 + q in [q][c & 1]
+  __shared__ __attribute__((aligned(16))) float sw[NHW][2][kMaxQ];
+  __shared__ float sdecay[NHW][2];
 
   const int id = xcd_swizzle(int(blockIdx.x), nchain);
-  const int pb = id % NPB;
-  const int bh = id / NPB;                      // b * H + h
-  const int h = bh % H, b = bh / H;
-  const int g = h / (H / G);
+  const int cpr = H * P / kChainCols;           // work-groups per batch row
+  const int b = id / cpr, c0 = (id % cpr) * kChainCols;   // first flattened column
+  const int h0 = c0 / P;                        // first head
+  const int g = h0 / (H / G);                   // the B group (both heads share it)
   const int l32 = lane & 31, g2 = lane >> 5;
   const int nsl = nc * SPC;                     // slices of the row
   const size_t hstate = size_t(P) * N;          // elements of one (b, h) state
+  // column block j (32 columns): head h0 + (NHW == 2 ? j : 0), columns from pcol(j) of that head
+  auto pcol = [&](int j) { return (c0 + 32 * j) % P; };
 
-  if (wave >= 4) {
-    // ---- store waves: dt of chunks 0 and 1 first (store wave 0), then the
-    // same barriers as the compute waves, in the same order. Four of them
-    // (rather than one) keep the work-group a whole number of waves per SIMD,
-    // which lets two work-groups share a compute unit.
-    const int sv = wave - 4;
-    // dt of chunk c, token lane + 64 i (0 past the row)
-    auto dt_load = [&](int c, float (&v)[kDtL]) {
+  if (wave == 4) {
+    // ---- table wave: each chunk's tables one chunk ahead, from dt loaded one
+    // chunk before that. It issues no copies, so its loads (dt) and stores
+    // (the Acs / dt rows) are all its memory counter holds: the wait for a
+    // chunk's dt finds only operations a chunk old.
+    float Ah[NHW];
+#pragma unroll
+    for (int q = 0; q < NHW; ++q) Ah[q] = A[h0 + q];
+    // dt of tokens 4 lane .. 4 lane + 3 of chunk c, head h0 + q (rows clamped
+    // into the row; the tables zero those past its end), each as the aligned
+    // 32-bit word that holds it (a word that holds an element of the tensor is
+    // readable) and, in bit i of hi, whether it is that word's upper half.
+    // 32-bit loads need no widening, which would wait for them at once.
+    auto dt_load = [&](int c, uint32_t (&v)[NHW][4], uint32_t (&hi)[NHW]) {
       const ChunkRows cr = chunk_rows(nullptr, b, c, T, Q);
 #pragma unroll
-      for (int i = 0; i < kDtL; ++i) {
-        const int t = lane + 64 * i;
-        const float raw = bf16_to_f32(dt[(cr.r0 + min(t, cr.n - 1)) * H + h]);
-        v[i] = t < cr.n ? raw : 0.f;
-      }
-    };
-    auto dt_put = [&](int slot, const float (&v)[kDtL]) {
+      for (int q = 0; q < NHW; ++q) {
+        hi[q] = 0u;
 #pragma unroll
-      for (int i = 0; i < kDtL; ++i)
-        if (lane + 64 * i < Q) sdtq[slot][lane + 64 * i] = v[i];
-    };
-    float pend[kDtL];
-    if (sv == 0) {
-      dt_load(0, pend);
-      dt_put(0, pend);
-      if (nc > 1) {
-        dt_load(1, pend);
-        dt_put(1, pend);
-      }
-    }
-    lds_barrier();                            // [0]
-    const int nsteps = (nsl + 2) / 3 * 3;
-    for (int k = 0; k < nsteps; ++k) {
-      lds_barrier();                            // [4] slice k in LDS
-      if (k < nsl && k % SPC == 0) {
-        const int c = k / SPC;
-        if (sv == 0 && c >= 1 && c + 1 < nc) dt_put((c + 1) & 1, pend);   // loaded during chunk c - 1
-        lds_barrier();                          // [1]
-        if (sv == 0 && c + 2 < nc) dt_load(c + 2, pend);
-        lds_barrier();                          // [2] sacs, sdt = chunk c
-        const int t = 64 * sv + lane;
-        if (pb == 0 && t < Q) {
-          const size_t arow = (size_t(bh) * nc + c) * Q;
-          Acs[arow + t] = sacs[t];
-          dtq[arow + t] = sdt[t];
-        }
-        lds_barrier();                          // [3] sH = H_c
-        // rows 8 sv .. 8 sv + 7 of H_c, and tokens 64 sv .. 64 sv + 63 of
-        // the chunk's Acs / dt rows
-        uint16_t* hdst = Hb + ((size_t(b) * nc + c) * H + h) * hstate + size_t(PB) * pb * N;
-#pragma unroll
-        for (int i = 0; i < PB / 4 * RBB / 64; ++i) {
-          const int e = lane + 64 * i, pr = PB / 4 * sv + e / RBB, cc = e % RBB;
-          *reinterpret_cast<u32x4*>(hdst + size_t(pr) * N + 8 * cc) =
-              *reinterpret_cast<const u32x4*>(&sH[pr * kHS + 8 * cc]);
+        for (int i = 0; i < 4; ++i) {
+          const uint16_t* e = dt + (cr.r0 + min(4 * lane + i, cr.n - 1)) * H + h0 + q;
+          const uint32_t up = uint32_t(reinterpret_cast<uintptr_t>(e) >> 1) & 1u;
+          v[q][i] = *reinterpret_cast<const uint32_t*>(e - up);
+          hi[q] |= up << i;
         }
       }
+    };
+    // chunk c's tables for head h0 + q (four tokens per lane: a serial sum per
+    // lane and one wave scan of the lane totals) into slot c & 1; Acs and dt
+    // of this lane's tokens into acs / v for the rows written after the next
+    // dt loads
+    auto tables = [&](int c, int q, const uint32_t (&raw)[4], uint32_t hi, float (&acs)[4], float (&v)[4]) {
+      const ChunkRows cr = chunk_rows(nullptr, b, c, T, Q);
+      float tot = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t bits = (hi >> i) & 1 ? raw[i] & 0xffff0000u : raw[i] << 16;
+        v[i] = 4 * lane + i < cr.n ? __uint_as_float(bits) : 0.f;
+        tot += v[i] * Ah[q];
+      }
+      float run = wave_incl_scan(tot) - tot;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        run += v[i] * Ah[q];
+        acs[i] = run;
+      }
+      // Acs_{Q-1}: element (Q - 1) % 4 of lane (Q - 1) / 4 (Q is a multiple of 64)
+      const float last = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(acs[3]), (Q - 1) / 4));
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (4 * lane + i < Q) sw[q][c & 1][4 * lane + i] = exp_fast(last - acs[i]) * v[i];
+      if (lane == 0) sdecay[q][c & 1] = expf(last);
+    };
+    // the Acs / dt rows of chunk c, head h0 + q (by the work-group holding
+    // the head's first columns)
+    auto rows_out = [&](int c, int q, const float (&acs)[4], const float (&v)[4]) {
+      if (pcol(q) != 0) return;
+      const size_t arow = ((size_t(b) * H + h0 + q) * nc + c) * Q;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = 4 * lane + i;
+        if (t < Q) {
+          Acs[arow + t] = acs[i];
+          dtq[arow + t] = v[i];
+        }
+      }
+    };
+    uint32_t dnext[NHW][4], dhi[NHW];
+#pragma unroll
+    for (int q = 0; q < NHW; ++q) {
+      dhi[q] = 0u;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dnext[q][i] = 0u;
     }
-    lds_barrier();                              // [5]
-    lds_barrier();                              // [6]
+    float tacs[NHW][4], tdt[NHW][4];
+    // chunk c's tables, then chunk c + 1's dt, then chunk c's rows (stores
+    // after the loads)
+    auto chunk = [&](int c) {
+#pragma unroll
+      for (int q = 0; q < NHW; ++q) tables(c, q, dnext[q], dhi[q], tacs[q], tdt[q]);
+      if (c + 1 < nc) dt_load(c + 1, dnext, dhi);
+#pragma unroll
+      for (int q = 0; q < NHW; ++q) rows_out(c, q, tacs[q], tdt[q]);
+    };
+    dt_load(0, dnext, dhi);
+    chunk(0);
+    for (int k0 = 0; k0 < nsl; k0 += S) {
+#pragma unroll
+      for (int d = 0; d < S; ++d) {
+        const int k = k0 + d;
+        lds_barrier();                          // [4]
+        // at chunk c's start, chunk c + 1's tables (slot (c + 1) & 1 last
+        // served chunk c - 1, whose slices are consumed by now; the compute
+        // waves read it one barrier later at the earliest)
+        if (k < nsl && k % SPC == 0 && k / SPC + 1 < nc) chunk(k / SPC + 1);
+      }
+    }
     return;
   }
 
-  // ---- compute waves (threads 0 .. kChainCT - 1; the mask tells the
-  // compiler so, which keeps the per-thread index arithmetic branch-free).
-  // Compute wave w = 2 kh + th takes k steps 2 kh, 2 kh + 1 of every slice
-  // (tokens 32 kh .. 32 kh + 31) for n tiles th NT/2 .. th NT/2 + NT/2 - 1:
-  // its products for different tiles are independent, and each x fragment
-  // is scaled by two waves instead of four. Waves kh = 1 so hold partial
-  // states over their half of the tokens; they hand them to waves kh = 0
-  // (the decay scaling is linear, so it applies to the partials alike) where
-  // H_c leaves, and restart from zero.
-  const int ct = tid & (kChainCT - 1);
-  const float Ah = A[h];
-  constexpr int NT = N / 32, NH = NT / 2;
-  const int th = wave & 1, kh = wave >> 1;
-  // partial state, local tile u (tile t = th NH + u): n = 32 t + 8 (r / 4) + 4 g2 + r % 4, p = 32 pb + l32
-  f32x16 acc[NH];
-#pragma unroll
-  for (int u = 0; u < NH; ++u) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int n = 32 * (th * NH + u) + 8 * (r / 4) + 4 * g2 + r % 4;
-      acc[u][r] = init && kh == 0 ? init[(size_t(bh) * N + n) * P + PB * pb + l32] : 0.f;
-    }
-  }
-  // copy addresses: a uniform slice base plus this lane's 32-bit element
-  // offset. Copy j of B covers rows rB0 + j (256 / RBB) of the slice (64
-  // lanes x 16 bytes of RBB-chunk rows; the row swizzle is the same for
-  // every j); the x copy covers rows rX.
-  static_assert((256 / RBB) % 4 == 0, "copies keep the row swizzle");
-  const int rB0 = (64 * wave + lane) / RBB;
-  const int cB = 8 * ((lane % RBB) ^ lds_swz<RBB>(rB0));
-  const int rX = (64 * wave + lane) / RBX, cX = 8 * ((64 * wave + lane) % RBX);
-  const int offB = rB0 * G * N + cB, stepB = (256 / RBB) * G * N;
-  const int offX = rX * H * P + cX;
-  auto issue = [&](int k, int s) {
-    k = min(k, nsl - 1);
-    const ChunkRows cr = chunk_rows(nullptr, b, k / SPC, T, Q);
-    const int s0 = (k % SPC) * kChainSK;
-    const long row0 = cr.r0 + s0;
-    const uint16_t* bbase = Bm + (row0 * G + g) * size_t(N);
-    const uint16_t* xbase = x + (row0 * H + h) * size_t(P) + PB * pb;
-    if (s0 + kChainSK <= cr.n) {                 // uniform: every row is a token of the row
-#pragma unroll
-      for (int j = 0; j < NCB / 4; ++j)
-        copy_to_lds16(bbase + unsigned(offB + j * stepB), slotB(s) + 512 * (wave + 4 * j));
-      copy_to_lds16(xbase + unsigned(offX), slotX(s) + 512 * wave);
-    } else {
-      // the row's last chunk: rows past its last token repeat that token.
-      // rmax is negative for a slice that starts past the last token, so the
-      // offsets here are signed.
+  if (wave > 4) {
+    // ---- copy waves: the slice copies into LDS. Copy q of a slice (q < NCB:
+    // B, else x) covers 1 KB of its slot; copy wave v takes q = v, v + 3, ...,
+    // the last index repeated where the count falls short (the repeat writes
+    // the same bytes again).
+    const int sv = wave - 5;
+    // slice k (clamped into the row: copies past its end repeat the last
+    // slice into a free slot) into slot s
+    auto issue = [&](int k, int s) {
+      k = min(k, nsl - 1);
+      const ChunkRows cr = chunk_rows(nullptr, b, k / SPC, T, Q);
+      const int s0 = (k % SPC) * kChainSK;
+      const long row0 = cr.r0 + s0;
+      const uint16_t* bbase = Bm + (row0 * G + g) * size_t(N);
+      const uint16_t* xbase = x + row0 * size_t(H) * P + c0;
+      // rows past the row's last token repeat that token (rmax is negative
+      // for a slice that starts past it, so those offsets are signed)
+      const bool full = s0 + kChainSK <= cr.n;  // uniform
       const int rmax = cr.n - 1 - s0;
 #pragma unroll
-      for (int j = 0; j < NCB / 4; ++j)
-        copy_to_lds16(bbase + (long(min(rB0 + j * (256 / RBB), rmax)) * G * N + cB),
-                      slotB(s) + 512 * (wave + 4 * j));
-      copy_to_lds16(xbase + (long(min(rX, rmax)) * H * P + cX), slotX(s) + 512 * wave);
-    }
-  };
-  // partials of waves kh = 1 handed to waves kh = 0 through a free slot,
-  // fp32 in fragment order (register r of tile t of lane L at (16 t + r) 64
-  // + L: lanes consecutive, no bank conflicts)
-  static_assert(PB * N * 4 == kChainSK * N * 2, "an fp32 state fills one B slot");
-  auto hand_over = [&](float* scr) {
-#pragma unroll
-    for (int u = 0; u < NH; ++u)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        scr[(16 * (th * NH + u) + r) * 64 + lane] = acc[u][r];
-        acc[u][r] = 0.f;
-      }
-  };
-  auto take_over = [&](const float* scr) {
-#pragma unroll
-    for (int u = 0; u < NH; ++u)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[u][r] += scr[(16 * (th * NH + u) + r) * 64 + lane];
-  };
-  // chunk c's start (scratch: the free slot): H_c into sH as bf16 for the
-  // store waves, cumulative sums and w_s of the chunk, then the running
-  // state scaled by the chunk's decay
-  auto chunk_start = [&](int c, float* scr) {
-    if (kh == 1) hand_over(scr);
-    const float d = ct < Q ? sdtq[c & 1][ct] : 0.f;
-    float v = d * Ah;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const float o = __shfl_up(v, off, 64);
-      if (lane >= off) v += o;
-    }
-    if (lane == 63) sred[wave] = v;
-    lds_barrier();                              // [1] partials of kh = 1 in scratch
-    if (kh == 0) {
-      take_over(scr);                           // acc = H_c for this wave's tiles
-#pragma unroll
-      for (int u = 0; u < NH; ++u) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int n = 32 * (th * NH + u) + 8 * j + 4 * g2;
-          *reinterpret_cast<u32x2*>(&sH[l32 * kHS + n]) =
-              u32x2{pack_bf16x2(acc[u][4 * j], acc[u][4 * j + 1]), pack_bf16x2(acc[u][4 * j + 2], acc[u][4 * j + 3])};
+      for (int i = 0; i < OPS; ++i) {
+        const int q = min(sv + 3 * i, NCB + NCX - 1);   // uniform
+        if (q < NCB) {
+          // rows q (512 / N) + lane / RBB, 16-byte chunk lane % RBB, stored swizzled
+          const int r = q * (512 / N) + lane / RBB;
+          const int cb = 8 * ((lane % RBB) ^ lds_swz<RBB>(r));
+          const uint16_t* src = full ? bbase + unsigned(r * G * N + cb) : bbase + (long(min(r, rmax)) * G * N + cb);
+          copy_to_lds16(src, &sB[s][512 * q]);
+        } else {
+          const int qx = q - NCB;
+          const int r = qx * (512 / kChainCols) + lane / RBX;
+          const int cx = 8 * ((lane % RBX) ^ lds_swz<RBX>(r));
+          const uint16_t* src =
+              full ? xbase + unsigned(r * H * P + cx) : xbase + (long(min(r, rmax)) * H * P + cx);
+          copy_to_lds16(src, &sX[s][512 * qx]);
         }
       }
-    }
-    for (int w = 0; w < wave; ++w) v += sred[w];
-    if (ct < Q) {
-      sacs[ct] = v;
-      sdt[ct] = d;
-    }
-    lds_barrier();                              // [2] sacs, sdt = chunk c; scratch read
-    if (ct < Q) sw[ct] = exp_fast(sacs[Q - 1] - sacs[ct]) * sdt[ct];
-    const float a = expf(sacs[Q - 1]);
+    };
 #pragma unroll
-    for (int u = 0; u < NH; ++u)
+    for (int k = 0; k < S - 1; ++k) issue(k, k);
+    // Slice k's copies were issued S - 1 steps earlier; this wave's copies
+    // complete in order, so waiting until at most the S - 2 slices issued
+    // after it (OPS copies each) are outstanding leaves slice k in LDS.
+    for (int k0 = 0; k0 < nsl; k0 += S) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[u][r] *= a;
-    lds_barrier();                              // [3] sH = H_c, sw = chunk c
+      for (int d = 0; d < S; ++d) {
+        const int k = k0 + d;
+        wait_vmcnt<(S - 2) * OPS>();
+        lds_barrier();                          // [4] slice k in LDS; slice k - 1 consumed
+        issue(k + S - 1, (d + S - 1) % S);      // into the slot slice k - 1 used
+      }
+    }
+    wait_vmcnt<0>();                            // the last (repeated) copies
+    return;
+  }
+
+  // ---- compute waves (waves 0 .. 3): column block j = wave & 1 of head
+  // hj = h0 + (NHW == 2 ? j : 0), n tiles (wave >> 1) + 2 u. Each owns its
+  // tiles over every token, so the running states need no exchange between
+  // waves; they issue no loads inside the walk, so their stores (H_c, the
+  // final state) cost no waits.
+  const int j = wave & 1, hq = NHW == 2 ? j : 0, hj = h0 + hq;
+  const int pj = pcol(j);
+  const size_t bhj = size_t(b) * H + hj;
+  auto ntile = [&](int u) { return (wave >> 1) + 2 * u; };
+  // running state, tile u: n = 32 ntile(u) + 8 (r / 4) + 4 g2 + r % 4, p = pj + l32 of head hj
+  f32x16 acc[TPW];
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int n = 32 * ntile(u) + 8 * (r / 4) + 4 * g2 + r % 4;
+      acc[u][r] = init ? init[(bhj * N + n) * P + pj + l32] : 0.f;
+    }
+  }
+  // chunk c's start: H_c out as bf16 ([p][n] rows, four consecutive n of
+  // p = pj + l32 per register run), then the running state scaled by the
+  // chunk's decay
+  auto chunk_start = [&](int c) {
+    uint16_t* hrow = Hb + ((size_t(b) * nc + c) * H + hj) * hstate + size_t(pj + l32) * N;
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int n = 32 * ntile(u) + 8 * jj + 4 * g2;
+        *reinterpret_cast<u32x2*>(hrow + n) = u32x2{pack_bf16x2(acc[u][4 * jj], acc[u][4 * jj + 1]),
+                                                    pack_bf16x2(acc[u][4 * jj + 2], acc[u][4 * jj + 3])};
+      }
+    }
+    const float decay = sdecay[hq][c & 1];
+#pragma unroll
+    for (int u = 0; u < TPW; ++u)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[u][r] *= decay;
   };
-  // slice k from slot s: k steps 2 kh, 2 kh + 1, this wave's tiles
+  // slice k from slot s, all four k steps
   auto compute = [&](int k, int s) {
-    // padding steps past the last slice multiply by zero weights (no branch:
-    // the copies and waits keep one fixed pattern)
+    // padding steps past the last slice multiply by zero weights (the
+    // barriers keep one fixed pattern)
     const float live = k < nsl ? 1.f : 0.f;
     const int s0 = (k % SPC) * kChainSK;
+    const float* swc = sw[hq][(min(k, nsl - 1) / SPC) & 1];
+    constexpr int KS = kChainSK / 16;
+    // every LDS read of the slice first, so that one wait covers them all
+    u32x4 xr[KS], bf[KS][TPW];
+    f32x4 w0[KS], w1[KS];
 #pragma unroll
-    for (int kq = 0; kq < 2; ++kq) {
-      const int kb = 16 * (2 * kh + kq) + 8 * g2;
-      const u32x4 xr = frag_tr<RBX>(slotX(s), kb, kb + 4, 0, lane);   // x rows kb .. kb+7 of column l32
-      const f32x4 w0 = *reinterpret_cast<const f32x4*>(&sw[s0 + kb]) * live;
-      const f32x4 w1 = *reinterpret_cast<const f32x4*>(&sw[s0 + kb + 4]) * live;
-      const u32x4 a = u32x4{pack_bf16x2(bf16_lo(xr[0]) * w0[0], bf16_hi(xr[0]) * w0[1]),
-                            pack_bf16x2(bf16_lo(xr[1]) * w0[2], bf16_hi(xr[1]) * w0[3]),
-                            pack_bf16x2(bf16_lo(xr[2]) * w1[0], bf16_hi(xr[2]) * w1[1]),
-                            pack_bf16x2(bf16_lo(xr[3]) * w1[2], bf16_hi(xr[3]) * w1[3])};
+    for (int kk = 0; kk < KS; ++kk) {
+      const int kb = 16 * kk + 8 * g2;
+      xr[kk] = frag_tr<RBX>(sX[s], kb, kb + 4, 32 * j, lane);   // x rows kb .. kb+7 of column 32 j + l32
+      w0[kk] = *reinterpret_cast<const f32x4*>(&swc[s0 + kb]);
+      w1[kk] = *reinterpret_cast<const f32x4*>(&swc[s0 + kb + 4]);
 #pragma unroll
-      for (int u = 0; u < NH; ++u)
-        acc[u] = mfma32x32x16(frag_tr<RBB>(slotB(s), kb, kb + 4, 32 * (th * NH + u), lane), a, acc[u]);
+      for (int u = 0; u < TPW; ++u) bf[kk][u] = frag_tr<RBB>(sB[s], kb, kb + 4, 32 * ntile(u), lane);
+    }
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      const f32x4 v0 = w0[kk] * live, v1 = w1[kk] * live;
+      const u32x4 a = u32x4{pack_bf16x2(bf16_lo(xr[kk][0]) * v0[0], bf16_hi(xr[kk][0]) * v0[1]),
+                            pack_bf16x2(bf16_lo(xr[kk][1]) * v0[2], bf16_hi(xr[kk][1]) * v0[3]),
+                            pack_bf16x2(bf16_lo(xr[kk][2]) * v1[0], bf16_hi(xr[kk][2]) * v1[1]),
+                            pack_bf16x2(bf16_lo(xr[kk][3]) * v1[2], bf16_hi(xr[kk][3]) * v1[3])};
+#pragma unroll
+      for (int u = 0; u < TPW; ++u) acc[u] = mfma32x32x16(bf[kk][u], a, acc[u]);
     }
   };
 
-  issue(0, 0);
-  issue(1, 1);
-  lds_barrier();                                // [0] dt of chunks 0 and 1 in sdtq
-  static_assert(kChainStages == 3 && kChainSK == 64, "slot rotation and k split below");
-  // whole groups of three steps (padding steps past the last slice only
-  // copy), so every iteration issues the same copies in the same order
-  for (int k0 = 0; k0 < nsl; k0 += 3) {
+  for (int k0 = 0; k0 < nsl; k0 += S) {
 #pragma unroll
-    for (int d = 0; d < 3; ++d) {
+    for (int d = 0; d < S; ++d) {
       const int k = k0 + d;
-      wait_vmcnt<OPS>();                        // this wave's copies of slice k are in
-      lds_barrier();                            // [4] everyone's are; slice k - 1 is consumed
-      const int sn = (d + 2) % 3;               // the slot slice k - 1 used: free
-      if (k < nsl && k % SPC == 0) chunk_start(k / SPC, reinterpret_cast<float*>(slotB(sn)));
-      issue(k + kChainStages - 1, sn);
+      lds_barrier();                            // [4] slice k in LDS; slice k - 1 consumed
+      if (k < nsl && k % SPC == 0) chunk_start(k / SPC);
       compute(k, d);
     }
   }
-  wait_vmcnt<0>();                              // the last (repeated) copies
-  // final = the sum of the partials
-  lds_barrier();                                // [5] every slot free
-  float* scr = reinterpret_cast<float*>(slotB(0));
-  if (kh == 1) hand_over(scr);
-  lds_barrier();                                // [6]
-  if (kh == 0 && fin) {
-    take_over(scr);
+  if (fin) {
 #pragma unroll
-    for (int u = 0; u < NH; ++u) {
+    for (int u = 0; u < TPW; ++u) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int n = 32 * (th * NH + u) + 8 * (r / 4) + 4 * g2 + r % 4;
-        fin[(size_t(bh) * N + n) * P + PB * pb + l32] = acc[u][r];
+        const int n = 32 * ntile(u) + 8 * (r / 4) + 4 * g2 + r % 4;
+        fin[(bhj * N + n) * P + pj + l32] = acc[u][r];
       }
     }
   }
@@ -621,7 +640,7 @@ hipError_t launch_chain_np(const FwdShape& s, const void* x, const void* B, cons
                            uint16_t* CB, hipStream_t st, const StageEv& ev) {
   const int lpc = s.Q / 32;
   const long ntiles = long(s.b) * s.nc * s.G * (lpc * (lpc + 1) / 2);
-  const long nchain = long(s.b) * s.H * (P / 32);
+  const long nchain = long(s.b) * s.H * P / kChainCols;
   const long blocks = nchain + (ntiles + kChainWaves - 1) / kChainWaves;
   hipExtLaunchKernelGGL((chunk_state_chain_kernel<N, P, SPC>), dim3(unsigned(blocks)), dim3(kChainThreads), 0, st,
                         ev.start, ev.stop, 0, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(B),
@@ -686,20 +705,21 @@ struct ChainNP {
   static constexpr int n = N_, p = P_;
 };
 
-// The fused launch pays off when its chains fill the chip in one round: each
-// chain is a serial walk over its row's slices, so fewer chains than
-// compute units leave units idle and more than fit at once (two work-groups
-// per unit at dstate 128, one at 256 for their local memory) run in two
-// rounds of the whole walk; such shapes take the two-kernel path.
+// The fused launch pays off when its work-groups (one per batch row and 64
+// columns) fill the chip in one round: each is a serial walk over its row's
+// slices, so fewer than half the compute units leave too many idle, and more
+// than fit at once (one per unit for its local memory) run in two rounds of
+// the whole walk; such shapes take the two-kernel path. Headdim 32 pairs two
+// heads, which must share a B/C group.
 bool chunk_state_chain_ok(const FwdShape& s) {
   if (!((s.N == 128 || s.N == 256) && (s.P == 32 || s.P == 64 || s.P == 128) && s.Q % kChainSK == 0)) return false;
+  if (s.P == 32 && (s.H / s.G) % 2 != 0) return false;
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
     return false;
-  const long chains = long(s.b) * s.H * (s.P / 32);
-  const long per_cu = s.N == 128 ? 2 : 1;
-  return chains >= cus && chains <= per_cu * cus;
+  const long wgs = long(s.b) * s.H * s.P / kChainCols;
+  return 2 * wgs >= cus && wgs <= cus;
 }
 
 hipError_t launch_chunk_state_chain(const FwdShape& s, const void* x, const void* B, const void* C,

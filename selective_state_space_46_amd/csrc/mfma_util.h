@@ -57,6 +57,30 @@ __device__ __forceinline__ void transpose8x8_b16(const u32x4 (&in)[8], u32x4 (&o
 
 __device__ __forceinline__ u32x4 load16(const uint16_t* p) { return *reinterpret_cast<const u32x4*>(p); }
 
+// Lane moves within a wave by DPP (no LDS traffic, unlike a shuffle, which
+// goes through the LDS crossbar and queues behind its other work). CTRL is the
+// DPP control (0x111 + n - 1: row_shr:n; 0x142: row_bcast:15; 0x143:
+// row_bcast:31) and ROWS the rows of 16 lanes written; every other lane,
+// and a lane whose source lies outside its row, receives 0.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_move(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROWS, 0xF, false));
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave: shifts by 1, 2, 4 and 8
+// lanes give the sums inside each row of 16; broadcasting lane 15's value to
+// row 1 and lane 47's to row 3, then lane 31's to rows 2 and 3, carries the
+// totals of the rows before.
+__device__ __forceinline__ float wave_incl_scan(float x) {
+  x += dpp_move<0x111, 0xF>(x);
+  x += dpp_move<0x112, 0xF>(x);
+  x += dpp_move<0x114, 0xF>(x);
+  x += dpp_move<0x118, 0xF>(x);
+  x += dpp_move<0x142, 0xA>(x);
+  x += dpp_move<0x143, 0xC>(x);
+  return x;
+}
+
 // ---------------------------------------------------------------------------
 // LDS tiles in natural (row-major, token-major) order, read transposed.
 //

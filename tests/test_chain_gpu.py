@@ -1,14 +1,15 @@
 """GPU parity of the fused chunk-state + state-passing launch (the forward
 path for equal-length rows with dstate 128 or 256 and chunk_len a multiple
-of 64 whose (batch, head, 32-column) chains fill a 256-unit MI355X in one
-round: 256 .. 512 chains at dstate 128, 256 at dstate 256) against the fp64
-oracle, through the C ABI.
+of 64 whose work-groups -- one per batch row and 64 columns of the flattened
+(head, headdim) axis -- fill a 256-unit MI355X in one round: 128 .. 256 of
+them) against the fp64 oracle, through the C ABI.
 
 Every shape here takes that path. Bar as for the other
 bf16 forward cases: relative L2 <= 1e-2 on y and on the final state. Cases
 span several chunks with a ragged tail, every chunk length the path takes,
-both dstate values, every headdim (one to four 32-column chains per head),
-groups, no initial state, the shortest rows, fast decays and long rows."""
+both dstate values, every headdim (two heads per work-group at headdim 32,
+one to two work-groups per head above), groups, no initial state, the
+shortest rows, fast decays, long rows and the 130M layer's head layout."""
 import numpy as np
 import pytest
 
@@ -22,8 +23,8 @@ TOL = 1e-2
 
 
 def _w(b, T, H, P, N, G, q, seed, init=True, dt_mode="softplus"):
-    chains = b * H * (P // 32)
-    assert 256 <= chains <= (512 if N == 128 else 256), "shape must take the fused path"
+    wgs = b * H * P // 64
+    assert 128 <= wgs <= 256 and (P != 32 or (H // G) % 2 == 0), "shape must take the fused path"
     return workloads.with_shape(workloads.MAMBA2_130M, batch=b, seqlen=T, nheads=H, headdim=P, dstate=N,
                                 ngroups=G, chunk_len=q, init="normal0.1" if init else "zero",
                                 dt_mode=dt_mode, seed=seed)
@@ -57,6 +58,16 @@ def test_chain_groups_no_init():
     _check(_w(2, 520, 64, 64, 128, 4, 128, seed=8200, init=False))
 
 
+def test_chain_head_pairs_in_groups():
+    """headdim 32: each work-group takes two heads, which share their B/C group"""
+    _check(_w(2, 410, 128, 32, 128, 4, 128, seed=8250))
+
+
+def test_chain_130m_head_layout():
+    """the 130M layer's batch and heads (192 work-groups) on a shorter row"""
+    _check(_w(8, 700, 24, 64, 128, 1, 256, seed=8260))
+
+
 @pytest.mark.parametrize("T", [1, 63, 64, 65])
 def test_chain_short_rows(T):
     _check(_w(4, T, 64, 64, 128, 2, 64, seed=8300 + T))
@@ -86,8 +97,8 @@ def test_chain_long_row():
 
 
 def test_fused_path_choice_on_the_workloads():
-    """The 130M-shaped layer (384 chains) takes the fused launch; the 2.7B-shaped
-    one (640 chains: two rounds) and the 128K-token row (48 chains) do not."""
+    """The 130M-shaped layer (192 work-groups) takes the fused launch; the
+    2.7B-shaped one (320: two rounds) and the 128K-token row (24) do not."""
     import selective_state_space_46_amd as ssd
     for w, want in ((workloads.MAMBA2_130M, True), (workloads.MAMBA2_2P7B, False), (workloads.LONG_128K, False)):
         got = ssd.ssd_chunk_scan_fwd_fused_states(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups,
