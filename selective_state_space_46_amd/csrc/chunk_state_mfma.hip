@@ -316,6 +316,11 @@ constexpr int kChainThreads = 64 * kChainWaves;
 constexpr int kChainSK = 64;        // tokens per slice
 constexpr int kChainCols = 64;      // flattened (head, p) columns per work-group
 
+template <int V>
+struct IntC {
+  static constexpr int value = V;
+};
+
 template <int N>
 struct ChainCfg {
   static constexpr int STAGES = N == 128 ? 5 : 3;               // slices resident (120 KB)
@@ -490,55 +495,79 @@ __global__ __launch_bounds__(kChainThreads) void chunk_state_chain_kernel(
     // ---- copy waves: the slice copies into LDS. Copy q of a slice (q < NCB:
     // B, else x) covers 1 KB of its slot; copy wave v takes q = v, v + 3, ...,
     // the last index repeated where the count falls short (the repeat writes
-    // the same bytes again).
-    const int sv = wave - 5;
-    // slice k (clamped into the row: copies past its end repeat the last
-    // slice into a free slot) into slot s
-    auto issue = [&](int k, int s) {
-      k = min(k, nsl - 1);
-      const ChunkRows cr = chunk_rows(nullptr, b, k / SPC, T, Q);
-      const int s0 = (k % SPC) * kChainSK;
-      const long row0 = cr.r0 + s0;
-      const uint16_t* bbase = Bm + (row0 * G + g) * size_t(N);
-      const uint16_t* xbase = x + row0 * size_t(H) * P + c0;
-      // rows past the row's last token repeat that token (rmax is negative
-      // for a slice that starts past it, so those offsets are signed)
-      const bool full = s0 + kChainSK <= cr.n;  // uniform
-      const int rmax = cr.n - 1 - s0;
+    // the same bytes again). Each copy wave's loop is compiled for its own
+    // copies, so a copy is a uniform slice base plus a per-lane offset
+    // computed once.
+    auto copy_loop = [&](auto svc) {
+      constexpr int SV = decltype(svc)::value;
+      // lane offsets (elements) of this wave's copies inside a whole slice:
+      // B rows q (512 / N) + lane / RBB, x rows qx (512 / 64) + lane / RBX,
+      // each lane fetching the 16-byte chunk the swizzle places at its LDS
+      // position; and the rows, for the clamped copies of a partial slice
+      unsigned off[OPS];
+      int row[OPS], cc[OPS];
 #pragma unroll
       for (int i = 0; i < OPS; ++i) {
-        const int q = min(sv + 3 * i, NCB + NCX - 1);   // uniform
+        const int q = min(SV + 3 * i, NCB + NCX - 1);
         if (q < NCB) {
-          // rows q (512 / N) + lane / RBB, 16-byte chunk lane % RBB, stored swizzled
-          const int r = q * (512 / N) + lane / RBB;
-          const int cb = 8 * ((lane % RBB) ^ lds_swz<RBB>(r));
-          const uint16_t* src = full ? bbase + unsigned(r * G * N + cb) : bbase + (long(min(r, rmax)) * G * N + cb);
-          copy_to_lds16(src, &sB[s][512 * q]);
+          row[i] = q * (512 / N) + lane / RBB;
+          cc[i] = 8 * ((lane % RBB) ^ lds_swz<RBB>(row[i]));
+          off[i] = unsigned(row[i] * G * N + cc[i]);
         } else {
-          const int qx = q - NCB;
-          const int r = qx * (512 / kChainCols) + lane / RBX;
-          const int cx = 8 * ((lane % RBX) ^ lds_swz<RBX>(r));
-          const uint16_t* src =
-              full ? xbase + unsigned(r * H * P + cx) : xbase + (long(min(r, rmax)) * H * P + cx);
-          copy_to_lds16(src, &sX[s][512 * qx]);
+          row[i] = (q - NCB) * (512 / kChainCols) + lane / RBX;
+          cc[i] = 8 * ((lane % RBX) ^ lds_swz<RBX>(row[i]));
+          off[i] = unsigned(row[i] * H * P + cc[i]);
         }
       }
-    };
+      // slice k (clamped into the row: copies past its end repeat the last
+      // slice into a free slot) into slot s
+      auto issue = [&](int k, int s) {
+        k = min(k, nsl - 1);
+        const ChunkRows cr = chunk_rows(nullptr, b, k / SPC, T, Q);
+        const int s0 = (k % SPC) * kChainSK;
+        const long row0 = cr.r0 + s0;
+        const uint16_t* bbase = Bm + (row0 * G + g) * size_t(N);
+        const uint16_t* xbase = x + row0 * size_t(H) * P + c0;
+        if (s0 + kChainSK <= cr.n) {            // uniform: every row is a token of the row
 #pragma unroll
-    for (int k = 0; k < S - 1; ++k) issue(k, k);
-    // Slice k's copies were issued S - 1 steps earlier; this wave's copies
-    // complete in order, so waiting until at most the S - 2 slices issued
-    // after it (OPS copies each) are outstanding leaves slice k in LDS.
-    for (int k0 = 0; k0 < nsl; k0 += S) {
+          for (int i = 0; i < OPS; ++i) {
+            const int q = min(SV + 3 * i, NCB + NCX - 1);
+            if (q < NCB) copy_to_lds16(bbase + off[i], &sB[s][512 * q]);
+            else copy_to_lds16(xbase + off[i], &sX[s][512 * (q - NCB)]);
+          }
+        } else {
+          // rows past the row's last token repeat that token (rmax is
+          // negative for a slice that starts past it: signed offsets)
+          const int rmax = cr.n - 1 - s0;
 #pragma unroll
-      for (int d = 0; d < S; ++d) {
-        const int k = k0 + d;
-        wait_vmcnt<(S - 2) * OPS>();
-        lds_barrier();                          // [4] slice k in LDS; slice k - 1 consumed
-        issue(k + S - 1, (d + S - 1) % S);      // into the slot slice k - 1 used
+          for (int i = 0; i < OPS; ++i) {
+            const int q = min(SV + 3 * i, NCB + NCX - 1);
+            if (q < NCB)
+              copy_to_lds16(bbase + (long(min(row[i], rmax)) * G * N + cc[i]), &sB[s][512 * q]);
+            else
+              copy_to_lds16(xbase + (long(min(row[i], rmax)) * H * P + cc[i]), &sX[s][512 * (q - NCB)]);
+          }
+        }
+      };
+#pragma unroll
+      for (int k = 0; k < S - 1; ++k) issue(k, k);
+      // Slice k's copies were issued S - 1 steps earlier; this wave's copies
+      // complete in order, so waiting until at most the S - 2 slices issued
+      // after it (OPS copies each) are outstanding leaves slice k in LDS.
+      for (int k0 = 0; k0 < nsl; k0 += S) {
+#pragma unroll
+        for (int d = 0; d < S; ++d) {
+          const int k = k0 + d;
+          wait_vmcnt<(S - 2) * OPS>();
+          lds_barrier();                        // [4] slice k in LDS; slice k - 1 consumed
+          issue(k + S - 1, (d + S - 1) % S);    // into the slot slice k - 1 used
+        }
       }
-    }
-    wait_vmcnt<0>();                            // the last (repeated) copies
+      wait_vmcnt<0>();                          // the last (repeated) copies
+    };
+    if (wave == 5) copy_loop(IntC<0>{});
+    else if (wave == 6) copy_loop(IntC<1>{});
+    else copy_loop(IntC<2>{});
     return;
   }
 
