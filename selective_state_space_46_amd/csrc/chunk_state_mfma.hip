@@ -612,11 +612,11 @@ __global__ __launch_bounds__(kChainThreads) void chunk_state_chain_kernel(
   };
   // slice k from slot s, all four k steps
   auto compute = [&](int k, int s) {
-    // padding steps past the last slice multiply by zero weights (the
-    // barriers keep one fixed pattern)
-    const float live = k < nsl ? 1.f : 0.f;
+    // padding steps past the last slice (they keep the barrier pattern
+    // fixed) compute nothing
+    if (k >= nsl) return;
     const int s0 = (k % SPC) * kChainSK;
-    const float* swc = sw[hq][(min(k, nsl - 1) / SPC) & 1];
+    const float* swc = sw[hq][(k / SPC) & 1];
     constexpr int KS = kChainSK / 16;
     // every LDS read of the slice first, so that one wait covers them all
     u32x4 xr[KS], bf[KS][TPW];
@@ -632,7 +632,7 @@ __global__ __launch_bounds__(kChainThreads) void chunk_state_chain_kernel(
     }
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
-      const f32x4 v0 = w0[kk] * live, v1 = w1[kk] * live;
+      const f32x4 v0 = w0[kk], v1 = w1[kk];
       const u32x4 a = u32x4{pack_bf16x2(bf16_lo(xr[kk][0]) * v0[0], bf16_hi(xr[kk][0]) * v0[1]),
                             pack_bf16x2(bf16_lo(xr[kk][1]) * v0[2], bf16_hi(xr[kk][1]) * v0[3]),
                             pack_bf16x2(bf16_lo(xr[kk][2]) * v1[0], bf16_hi(xr[kk][2]) * v1[1]),
