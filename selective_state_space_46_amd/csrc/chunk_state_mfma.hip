@@ -321,9 +321,12 @@ struct IntC {
   static constexpr int value = V;
 };
 
-template <int N>
+// ST slices resident: 5 at dstate 128 (120 KB: one work-group per compute
+// unit), 3 there when two work-groups share a unit (72 KB each), 3 at
+// dstate 256 (120 KB)
+template <int N, int ST>
 struct ChainCfg {
-  static constexpr int STAGES = N == 128 ? 5 : 3;               // slices resident (120 KB)
+  static constexpr int STAGES = ST;
   static constexpr int RBB = N / 8, RBX = kChainCols / 8;        // 16-byte chunks per B / x row
   static constexpr int NCB = kChainSK * RBB / 64, NCX = kChainSK * RBX / 64;   // wave copies per slice
   static constexpr int OPS = (NCB + NCX + 2) / 3;                // copies per copy wave and slice
@@ -355,13 +358,14 @@ __device__ __forceinline__ void copy_to_lds16(const uint16_t* src, uint16_t* dst
   __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(dst), 16, 0, 0);
 }
 
-template <int N, int P, int SPC>
-__global__ __launch_bounds__(kChainThreads) void chunk_state_chain_kernel(
+template <int N, int P, int SPC, int ST>
+__global__ __launch_bounds__(kChainThreads) __attribute__((amdgpu_waves_per_eu(N == 128 && ST <= 3 ? 4 : 1)))
+void chunk_state_chain_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ Bm, const uint16_t* __restrict__ dt,
     const float* __restrict__ A, float* __restrict__ Acs, float* __restrict__ dtq, uint16_t* __restrict__ Hb,
     const float* __restrict__ init, float* __restrict__ fin, const uint16_t* __restrict__ Cm,
     uint16_t* __restrict__ CB, int T, int H, int G, int Q, int nc, int nchain, long ntiles) {
-  using Cfg = ChainCfg<N>;
+  using Cfg = ChainCfg<N, ST>;
   constexpr int S = Cfg::STAGES, RBB = Cfg::RBB, RBX = Cfg::RBX, NCB = Cfg::NCB, NCX = Cfg::NCX;
   constexpr int OPS = Cfg::OPS, TPW = Cfg::TPW;
   constexpr int NHW = P == 32 ? 2 : 1;          // heads per work-group
@@ -663,7 +667,7 @@ __global__ __launch_bounds__(kChainThreads) void chunk_state_chain_kernel(
   }
 }
 
-template <int N, int P, int SPC>
+template <int N, int P, int SPC, int ST>
 hipError_t launch_chain_np(const FwdShape& s, const void* x, const void* B, const void* C, const void* dt,
                            const float* A, float* Acs, float* dtq, uint16_t* Hb, const float* init, float* fin,
                            uint16_t* CB, hipStream_t st, const StageEv& ev) {
@@ -671,7 +675,7 @@ hipError_t launch_chain_np(const FwdShape& s, const void* x, const void* B, cons
   const long ntiles = long(s.b) * s.nc * s.G * (lpc * (lpc + 1) / 2);
   const long nchain = long(s.b) * s.H * P / kChainCols;
   const long blocks = nchain + (ntiles + kChainWaves - 1) / kChainWaves;
-  hipExtLaunchKernelGGL((chunk_state_chain_kernel<N, P, SPC>), dim3(unsigned(blocks)), dim3(kChainThreads), 0, st,
+  hipExtLaunchKernelGGL((chunk_state_chain_kernel<N, P, SPC, ST>), dim3(unsigned(blocks)), dim3(kChainThreads), 0, st,
                         ev.start, ev.stop, 0, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(B),
                         static_cast<const uint16_t*>(dt), A, Acs, dtq, Hb, init, fin,
                         static_cast<const uint16_t*>(C), CB, s.T, s.H, s.G, s.Q, s.nc, int(nchain), ntiles);
@@ -737,18 +741,28 @@ struct ChainNP {
 // The fused launch pays off when its work-groups (one per batch row and 64
 // columns) fill the chip in one round: each is a serial walk over its row's
 // slices, so fewer than half the compute units leave too many idle, and more
-// than fit at once (one per unit for its local memory) run in two rounds of
-// the whole walk; such shapes take the two-kernel path. Headdim 32 pairs two
-// heads, which must share a B/C group.
-bool chunk_state_chain_ok(const FwdShape& s) {
-  if (!((s.N == 128 || s.N == 256) && (s.P == 32 || s.P == 64 || s.P == 128) && s.Q % kChainSK == 0)) return false;
-  if (s.P == 32 && (s.H / s.G) % 2 != 0) return false;
+// than fit at once (one per unit with five slices resident; at dstate 128
+// two per unit with three) run in two rounds of the whole walk; such shapes
+// take the two-kernel path. Headdim 32 pairs two heads, which must share a
+// B/C group.
+static int chain_units() {
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-    return false;
+    return 0;
+  return cus;
+}
+
+bool chunk_state_chain_ok(const FwdShape& s) {
+  if (!((s.N == 128 || s.N == 256) && (s.P == 32 || s.P == 64 || s.P == 128) && s.Q % kChainSK == 0)) return false;
+  if (s.P == 32 && (s.H / s.G) % 2 != 0) return false;
+  const int cus = chain_units();
+  if (cus <= 0) return false;
   const long wgs = long(s.b) * s.H * s.P / kChainCols;
-  return 2 * wgs >= cus && wgs <= cus;
+  // two per unit: dstate 128 with a chunk start at most every other slice
+  // (the registers of a chunk start every slice do not fit that occupancy)
+  const long per_unit = s.N == 128 && s.Q >= 2 * kChainSK ? 2 : 1;
+  return 2 * wgs >= cus && wgs <= per_unit * cus;
 }
 
 hipError_t launch_chunk_state_chain(const FwdShape& s, const void* x, const void* B, const void* C,
@@ -756,12 +770,24 @@ hipError_t launch_chunk_state_chain(const FwdShape& s, const void* x, const void
                                     const float* init, float* fin, uint16_t* CB, hipStream_t st,
                                     const StageEv& ev) {
   if (!chunk_state_chain_ok(s)) return hipErrorInvalidValue;
+  // two work-groups per unit (three slices resident; chunks of two or four
+  // slices, which the check above ensures) where one per unit would not
+  // hold them all
+  const bool two = long(s.b) * s.H * s.P / kChainCols > chain_units();
   auto by_q = [&](auto np) -> hipError_t {
     using NP = decltype(np);
+    constexpr int S1 = NP::n == 128 ? 5 : 3;
+    if (two && NP::n == 128) {
+      switch (s.Q / kChainSK) {
+        case 2: return launch_chain_np<NP::n, NP::p, 2, 3>(s, x, B, C, dt, A, Acs, dtq, Hb, init, fin, CB, st, ev);
+        case 4: return launch_chain_np<NP::n, NP::p, 4, 3>(s, x, B, C, dt, A, Acs, dtq, Hb, init, fin, CB, st, ev);
+      }
+      return hipErrorInvalidValue;
+    }
     switch (s.Q / kChainSK) {
-      case 1: return launch_chain_np<NP::n, NP::p, 1>(s, x, B, C, dt, A, Acs, dtq, Hb, init, fin, CB, st, ev);
-      case 2: return launch_chain_np<NP::n, NP::p, 2>(s, x, B, C, dt, A, Acs, dtq, Hb, init, fin, CB, st, ev);
-      case 4: return launch_chain_np<NP::n, NP::p, 4>(s, x, B, C, dt, A, Acs, dtq, Hb, init, fin, CB, st, ev);
+      case 1: return launch_chain_np<NP::n, NP::p, 1, S1>(s, x, B, C, dt, A, Acs, dtq, Hb, init, fin, CB, st, ev);
+      case 2: return launch_chain_np<NP::n, NP::p, 2, S1>(s, x, B, C, dt, A, Acs, dtq, Hb, init, fin, CB, st, ev);
+      case 4: return launch_chain_np<NP::n, NP::p, 4, S1>(s, x, B, C, dt, A, Acs, dtq, Hb, init, fin, CB, st, ev);
     }
     return hipErrorInvalidValue;
   };

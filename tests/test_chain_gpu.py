@@ -2,14 +2,16 @@
 path for equal-length rows with dstate 128 or 256 and chunk_len a multiple
 of 64 whose work-groups -- one per batch row and 64 columns of the flattened
 (head, headdim) axis -- fill a 256-unit MI355X in one round: 128 .. 256 of
-them) against the fp64 oracle, through the C ABI.
+them, one per unit, or at dstate 128 with chunk_len >= 128 up to 512, two per
+unit) against the fp64 oracle, through the C ABI.
 
 Every shape here takes that path. Bar as for the other
 bf16 forward cases: relative L2 <= 1e-2 on y and on the final state. Cases
 span several chunks with a ragged tail, every chunk length the path takes,
 both dstate values, every headdim (two heads per work-group at headdim 32,
 one to two work-groups per head above), groups, no initial state, the
-shortest rows, fast decays, long rows and the 130M layer's head layout."""
+shortest rows, fast decays, long rows, the 130M and 2.7B layers' head
+layouts, and the two-per-unit regime."""
 import numpy as np
 import pytest
 
@@ -24,7 +26,8 @@ TOL = 1e-2
 
 def _w(b, T, H, P, N, G, q, seed, init=True, dt_mode="softplus"):
     wgs = b * H * P // 64
-    assert 128 <= wgs <= 256 and (P != 32 or (H // G) % 2 == 0), "shape must take the fused path"
+    top = 512 if (N == 128 and q >= 128) else 256
+    assert 128 <= wgs <= top and (P != 32 or (H // G) % 2 == 0), "shape must take the fused path"
     return workloads.with_shape(workloads.MAMBA2_130M, batch=b, seqlen=T, nheads=H, headdim=P, dstate=N,
                                 ngroups=G, chunk_len=q, init="normal0.1" if init else "zero",
                                 dt_mode=dt_mode, seed=seed)
@@ -68,6 +71,18 @@ def test_chain_130m_head_layout():
     _check(_w(8, 700, 24, 64, 128, 1, 256, seed=8260))
 
 
+def test_chain_2p7b_head_layout_two_per_unit():
+    """the 2.7B layer's batch and heads (320 work-groups: two per unit, three
+    slices resident) with an initial state, on a shorter ragged row"""
+    _check(_w(4, 777, 80, 64, 128, 1, 256, seed=8270))
+
+
+@pytest.mark.parametrize("P,H,G", [(32, 192, 2), (64, 96, 1), (128, 48, 4)])
+def test_chain_two_per_unit_shapes(P, H, G):
+    """384 work-groups at chunk length 128, every headdim"""
+    _check(_w(4, 500, H, P, 128, G, 128, seed=8280 + P))
+
+
 @pytest.mark.parametrize("T", [1, 63, 64, 65])
 def test_chain_short_rows(T):
     _check(_w(4, T, 64, 64, 128, 2, 64, seed=8300 + T))
@@ -97,10 +112,11 @@ def test_chain_long_row():
 
 
 def test_fused_path_choice_on_the_workloads():
-    """The 130M-shaped layer (192 work-groups) takes the fused launch; the
-    2.7B-shaped one (320: two rounds) and the 128K-token row (24) do not."""
+    """The 130M-shaped layer (192 work-groups, one per unit) and the 2.7B-shaped
+    one (320, two per unit) take the fused launch; the 128K-token row (24
+    work-groups) does not."""
     import selective_state_space_46_amd as ssd
-    for w, want in ((workloads.MAMBA2_130M, True), (workloads.MAMBA2_2P7B, False), (workloads.LONG_128K, False)):
+    for w, want in ((workloads.MAMBA2_130M, True), (workloads.MAMBA2_2P7B, True), (workloads.LONG_128K, False)):
         got = ssd.ssd_chunk_scan_fwd_fused_states(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups,
                                                   w.chunk_len, ssd.SSD_BF16)
         assert got == want, w.name
