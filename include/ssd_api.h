@@ -131,13 +131,15 @@ SSD_API ssd_status ssd_chunk_scan_fwd(const void *x, const void *dt, const float
  * Whether ssd_chunk_scan_fwd with these sizes runs the chunk states and the
  * passing of states between chunks as one launch on the current HIP device
  * (1) or as two (0; also for sizes the call would reject). The results agree
- * up to rounding either way. The fused launch walks each (batch row, head,
- * 32 columns of headdim) through its chunks in order with the running state
+ * up to rounding either way. The fused launch walks each batch row and 64
+ * columns of the flattened (head, headdim) axis (headdim 32: two heads, which
+ * must share a B/C group) through its chunks in order with the running state
  * on chip and writes only the bf16 states entering each chunk; it is used for
  * the bf16 matrix-core path with dstate 128 or 256 and chunk_len a multiple
- * of 64 when those walks fill the device in one round (between one and two
- * per compute unit at dstate 128, one at dstate 256). It reads the device's
- * compute-unit count, so it needs a current HIP device (0 without one).
+ * of 64 when those walks fill the device in one round: between half and all
+ * of the compute units, or, at dstate 128 with chunk_len >= 128, up to two
+ * per unit. It reads the device's compute-unit count, so it needs a current
+ * HIP device (0 without one).
  */
 SSD_API int ssd_chunk_scan_fwd_fused_states(int batch, int seqlen, int nheads, int headdim, int dstate,
                                             int ngroups, int chunk_len, ssd_dtype dtype);
