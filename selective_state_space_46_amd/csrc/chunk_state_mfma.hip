@@ -358,13 +358,18 @@ __device__ __forceinline__ void copy_to_lds16(const uint16_t* src, uint16_t* dst
   __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(dst), 16, 0, 0);
 }
 
-template <int N, int P, int SPC, int ST>
+// F32S (the backward's recomputation): the states entering each chunk go
+// out as fp32 ([b, c, h, p, n], as state_passing leaves them over the chunk
+// states) and the C B^T tiles as fp32 in both orientations (CB and CBt, as
+// chunk_state_mfma_kernel's MODE 1); else bf16 states and bf16 tiles.
+template <int N, int P, int SPC, int ST, bool F32S>
 __global__ __launch_bounds__(kChainThreads) __attribute__((amdgpu_waves_per_eu(N == 128 && ST <= 3 ? 4 : 1)))
 void chunk_state_chain_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ Bm, const uint16_t* __restrict__ dt,
-    const float* __restrict__ A, float* __restrict__ Acs, float* __restrict__ dtq, uint16_t* __restrict__ Hb,
+    const float* __restrict__ A, float* __restrict__ Acs, float* __restrict__ dtq, void* __restrict__ Hs,
     const float* __restrict__ init, float* __restrict__ fin, const uint16_t* __restrict__ Cm,
-    uint16_t* __restrict__ CB, int T, int H, int G, int Q, int nc, int nchain, long ntiles) {
+    uint16_t* __restrict__ CB, uint16_t* __restrict__ CBt, int T, int H, int G, int Q, int nc, int nchain,
+    long ntiles) {
   using Cfg = ChainCfg<N, ST>;
   constexpr int S = Cfg::STAGES, RBB = Cfg::RBB, RBX = Cfg::RBX, NCB = Cfg::NCB, NCX = Cfg::NCX;
   constexpr int OPS = Cfg::OPS, TPW = Cfg::TPW;
@@ -374,7 +379,7 @@ void chunk_state_chain_kernel(
   // work-groups past the chains compute C B^T tiles, one per wave
   if (int(blockIdx.x) >= nchain) {
     const long wid = long(int(blockIdx.x) - nchain) * kChainWaves + wave;
-    if (wid < ntiles) chunk_scores_tile<N, false>(Bm, Cm, CB, nullptr, nullptr, T, G, Q, nc, wid, lane);
+    if (wid < ntiles) chunk_scores_tile<N, F32S>(Bm, Cm, CB, CBt, nullptr, T, G, Q, nc, wid, lane);
     return;                                     // no barrier on this path
   }
   __shared__ __attribute__((aligned(16))) uint16_t sB[S][kChainSK * N];
@@ -598,14 +603,19 @@ void chunk_state_chain_kernel(
   // p = pj + l32 per register run), then the running state scaled by the
   // chunk's decay
   auto chunk_start = [&](int c) {
-    uint16_t* hrow = Hb + ((size_t(b) * nc + c) * H + hj) * hstate + size_t(pj + l32) * N;
+    const size_t hoff = ((size_t(b) * nc + c) * H + hj) * hstate + size_t(pj + l32) * N;
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         const int n = 32 * ntile(u) + 8 * jj + 4 * g2;
-        *reinterpret_cast<u32x2*>(hrow + n) = u32x2{pack_bf16x2(acc[u][4 * jj], acc[u][4 * jj + 1]),
-                                                    pack_bf16x2(acc[u][4 * jj + 2], acc[u][4 * jj + 3])};
+        if constexpr (F32S) {
+          *reinterpret_cast<f32x4*>(static_cast<float*>(Hs) + hoff + n) =
+              f32x4{acc[u][4 * jj], acc[u][4 * jj + 1], acc[u][4 * jj + 2], acc[u][4 * jj + 3]};
+        } else {
+          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(Hs) + hoff + n) =
+              u32x2{pack_bf16x2(acc[u][4 * jj], acc[u][4 * jj + 1]), pack_bf16x2(acc[u][4 * jj + 2], acc[u][4 * jj + 3])};
+        }
       }
     }
     const float decay = sdecay[hq][c & 1];
@@ -667,18 +677,18 @@ void chunk_state_chain_kernel(
   }
 }
 
-template <int N, int P, int SPC, int ST>
+template <int N, int P, int SPC, int ST, bool F32S>
 hipError_t launch_chain_np(const FwdShape& s, const void* x, const void* B, const void* C, const void* dt,
-                           const float* A, float* Acs, float* dtq, uint16_t* Hb, const float* init, float* fin,
-                           uint16_t* CB, hipStream_t st, const StageEv& ev) {
+                           const float* A, float* Acs, float* dtq, void* Hs, const float* init, float* fin,
+                           uint16_t* CB, uint16_t* CBt, hipStream_t st, const StageEv& ev) {
   const int lpc = s.Q / 32;
   const long ntiles = long(s.b) * s.nc * s.G * (lpc * (lpc + 1) / 2);
   const long nchain = long(s.b) * s.H * P / kChainCols;
   const long blocks = nchain + (ntiles + kChainWaves - 1) / kChainWaves;
-  hipExtLaunchKernelGGL((chunk_state_chain_kernel<N, P, SPC, ST>), dim3(unsigned(blocks)), dim3(kChainThreads), 0, st,
-                        ev.start, ev.stop, 0, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(B),
-                        static_cast<const uint16_t*>(dt), A, Acs, dtq, Hb, init, fin,
-                        static_cast<const uint16_t*>(C), CB, s.T, s.H, s.G, s.Q, s.nc, int(nchain), ntiles);
+  hipExtLaunchKernelGGL((chunk_state_chain_kernel<N, P, SPC, ST, F32S>), dim3(unsigned(blocks)), dim3(kChainThreads),
+                        0, st, ev.start, ev.stop, 0, static_cast<const uint16_t*>(x),
+                        static_cast<const uint16_t*>(B), static_cast<const uint16_t*>(dt), A, Acs, dtq, Hs, init, fin,
+                        static_cast<const uint16_t*>(C), CB, CBt, s.T, s.H, s.G, s.Q, s.nc, int(nchain), ntiles);
   return hipGetLastError();
 }
 
@@ -765,10 +775,10 @@ bool chunk_state_chain_ok(const FwdShape& s) {
   return 2 * wgs >= cus && wgs <= per_unit * cus;
 }
 
-hipError_t launch_chunk_state_chain(const FwdShape& s, const void* x, const void* B, const void* C,
-                                    const void* dt, const float* A, float* Acs, float* dtq, uint16_t* Hb,
-                                    const float* init, float* fin, uint16_t* CB, hipStream_t st,
-                                    const StageEv& ev) {
+template <bool F32S>
+hipError_t launch_chain(const FwdShape& s, const void* x, const void* B, const void* C, const void* dt,
+                        const float* A, float* Acs, float* dtq, void* Hs, const float* init, float* fin,
+                        uint16_t* CB, uint16_t* CBt, hipStream_t st, const StageEv& ev) {
   if (!chunk_state_chain_ok(s)) return hipErrorInvalidValue;
   // two work-groups per unit (three slices resident; chunks of two or four
   // slices, which the check above ensures) where one per unit would not
@@ -779,15 +789,20 @@ hipError_t launch_chunk_state_chain(const FwdShape& s, const void* x, const void
     constexpr int S1 = NP::n == 128 ? 5 : 3;
     if (two && NP::n == 128) {
       switch (s.Q / kChainSK) {
-        case 2: return launch_chain_np<NP::n, NP::p, 2, 3>(s, x, B, C, dt, A, Acs, dtq, Hb, init, fin, CB, st, ev);
-        case 4: return launch_chain_np<NP::n, NP::p, 4, 3>(s, x, B, C, dt, A, Acs, dtq, Hb, init, fin, CB, st, ev);
+        case 2:
+          return launch_chain_np<NP::n, NP::p, 2, 3, F32S>(s, x, B, C, dt, A, Acs, dtq, Hs, init, fin, CB, CBt, st, ev);
+        case 4:
+          return launch_chain_np<NP::n, NP::p, 4, 3, F32S>(s, x, B, C, dt, A, Acs, dtq, Hs, init, fin, CB, CBt, st, ev);
       }
       return hipErrorInvalidValue;
     }
     switch (s.Q / kChainSK) {
-      case 1: return launch_chain_np<NP::n, NP::p, 1, S1>(s, x, B, C, dt, A, Acs, dtq, Hb, init, fin, CB, st, ev);
-      case 2: return launch_chain_np<NP::n, NP::p, 2, S1>(s, x, B, C, dt, A, Acs, dtq, Hb, init, fin, CB, st, ev);
-      case 4: return launch_chain_np<NP::n, NP::p, 4, S1>(s, x, B, C, dt, A, Acs, dtq, Hb, init, fin, CB, st, ev);
+      case 1:
+        return launch_chain_np<NP::n, NP::p, 1, S1, F32S>(s, x, B, C, dt, A, Acs, dtq, Hs, init, fin, CB, CBt, st, ev);
+      case 2:
+        return launch_chain_np<NP::n, NP::p, 2, S1, F32S>(s, x, B, C, dt, A, Acs, dtq, Hs, init, fin, CB, CBt, st, ev);
+      case 4:
+        return launch_chain_np<NP::n, NP::p, 4, S1, F32S>(s, x, B, C, dt, A, Acs, dtq, Hs, init, fin, CB, CBt, st, ev);
     }
     return hipErrorInvalidValue;
   };
@@ -799,6 +814,20 @@ hipError_t launch_chunk_state_chain(const FwdShape& s, const void* x, const void
   if (s.P == 32) return by_q(ChainNP<256, 32>{});
   if (s.P == 64) return by_q(ChainNP<256, 64>{});
   return by_q(ChainNP<256, 128>{});
+}
+
+hipError_t launch_chunk_state_chain(const FwdShape& s, const void* x, const void* B, const void* C,
+                                    const void* dt, const float* A, float* Acs, float* dtq, uint16_t* Hb,
+                                    const float* init, float* fin, uint16_t* CB, hipStream_t st,
+                                    const StageEv& ev) {
+  return launch_chain<false>(s, x, B, C, dt, A, Acs, dtq, Hb, init, fin, CB, nullptr, st, ev);
+}
+
+hipError_t launch_chunk_state_chain_bwd(const FwdShape& s, const void* x, const void* B, const void* C,
+                                        const void* dt, const float* A, float* Acs, float* dtq, float* Hst,
+                                        const float* init, float* fin, uint16_t* CBf, uint16_t* CBt,
+                                        hipStream_t st) {
+  return launch_chain<true>(s, x, B, C, dt, A, Acs, dtq, Hst, init, fin, CBf, CBt, st, StageEv{});
 }
 
 hipError_t launch_chunk_state_mfma_bwd(const FwdShape& s, const void* x, const void* B, const void* C,

@@ -544,10 +544,17 @@ ssd_status ssd_chunk_scan_bwd(const void* x, const void* dt, const float* A, con
   float* dDp = reinterpret_cast<float*>(ws + w.ddp);
 
   // recomputation: in-chunk decays, chunk states, then the states entering
-  // each chunk (fp32, over the chunk states) and the final state
-  if (launch_chunk_state_mfma_bwd(s, x, B, C, dt, A, Acs, dtq, Sst, CBf, CBt, hs) != hipSuccess)
-    return SSD_ERR_HIP;
-  if (launch_state_passing(s, Sst, nullptr, Acs, init_state, fin, hs) != hipSuccess) return SSD_ERR_HIP;
+  // each chunk (fp32, over the chunk states) and the final state -- in one
+  // launch where the fused walk applies
+  if (chunk_state_chain_ok(s)) {
+    if (launch_chunk_state_chain_bwd(s, x, B, C, dt, A, Acs, dtq, Sst, init_state, fin, CBf, CBt, hs) !=
+        hipSuccess)
+      return SSD_ERR_HIP;
+  } else {
+    if (launch_chunk_state_mfma_bwd(s, x, B, C, dt, A, Acs, dtq, Sst, CBf, CBt, hs) != hipSuccess)
+      return SSD_ERR_HIP;
+    if (launch_state_passing(s, Sst, nullptr, Acs, init_state, fin, hs) != hipSuccess) return SSD_ERR_HIP;
+  }
   // what each chunk's outputs give the state entering it, then the reverse pass
   if (launch_chunk_dstates_mfma(s, dy, C, dt, A, dS, hs) != hipSuccess) return SSD_ERR_HIP;
   if (launch_state_passing_bwd(s, dS, Sst, Acs, dfinal, Gb, ghp, dinit, hs) != hipSuccess)

@@ -179,13 +179,22 @@ hipError_t launch_chunk_state_mfma(const FwdShape& s, const void* x, const void*
 // Chunk states and state passing fused (equal-length rows, bf16 MFMA path):
 // writes Acs, dtq, the C B^T tiles and Hb (states entering each chunk, bf16)
 // and final (fp32, may be null), without the fp32 chunk states. Only for the
-// shapes chunk_state_chain_ok accepts (enough (b, h, 32-column) chains to
-// fill the chip; dstate 128 or 256; chunk_len a multiple of 64).
+// shapes chunk_state_chain_ok accepts (enough (batch row, 64-column) walks
+// to fill the chip in one round; dstate 128 or 256; chunk_len a multiple of
+// 64).
 bool chunk_state_chain_ok(const FwdShape& s);
 hipError_t launch_chunk_state_chain(const FwdShape& s, const void* x, const void* B, const void* C,
                                     const void* dt, const float* A, float* Acs, float* dtq, uint16_t* Hb,
                                     const float* init, float* fin, uint16_t* CB, hipStream_t st,
                                     const StageEv& ev = StageEv{});
+// The same for the backward's recomputation: the states entering each chunk
+// as fp32 in Hst ([b, c, h, p, n], what state_passing leaves over the chunk
+// states) and the C B^T tiles as fp32 in both orientations (CBf, CBt, as
+// launch_chunk_state_mfma_bwd writes them).
+hipError_t launch_chunk_state_chain_bwd(const FwdShape& s, const void* x, const void* B, const void* C,
+                                        const void* dt, const float* A, float* Acs, float* dtq, float* Hst,
+                                        const float* init, float* fin, uint16_t* CBf, uint16_t* CBt,
+                                        hipStream_t st);
 
 // Hb == nullptr: states entering each chunk overwrite S in place (fp32);
 // otherwise they are written to Hb as bf16 and S is left as it was.
