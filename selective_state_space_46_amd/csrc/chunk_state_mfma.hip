@@ -409,10 +409,13 @@ void chunk_state_chain_kernel(
 #pragma unroll
     for (int q = 0; q < NHW; ++q) Ah[q] = A[h0 + q];
     // dt of tokens 4 lane .. 4 lane + 3 of chunk c, head h0 + q (rows clamped
-    // into the row; the tables zero those past its end), each as the aligned
-    // 32-bit word that holds it (a word that holds an element of the tensor is
-    // readable) and, in bit i of hi, whether it is that word's upper half.
-    // 32-bit loads need no widening, which would wait for them at once.
+    // into the row; the tables zero those past its end), each as an aligned
+    // 32-bit word of the tensor that holds it (dt is 16-byte aligned, so the
+    // word of element e starts at e & ~1, except for the tensor's last
+    // element at an even index, read through the word before it) and, in bit
+    // i of hi, whether it is that word's upper half. 32-bit loads need no
+    // widening, which would wait for them at once.
+    const long last = long(nchain / (H * P / kChainCols)) * T * H - 1;   // the tensor's last element
     auto dt_load = [&](int c, uint32_t (&v)[NHW][4], uint32_t (&hi)[NHW]) {
       const ChunkRows cr = chunk_rows(nullptr, b, c, T, Q);
 #pragma unroll
@@ -420,9 +423,9 @@ void chunk_state_chain_kernel(
         hi[q] = 0u;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const uint16_t* e = dt + (cr.r0 + min(4 * lane + i, cr.n - 1)) * H + h0 + q;
-          const uint32_t up = uint32_t(reinterpret_cast<uintptr_t>(e) >> 1) & 1u;
-          v[q][i] = *reinterpret_cast<const uint32_t*>(e - up);
+          const long e = (cr.r0 + min(4 * lane + i, cr.n - 1)) * H + h0 + q;
+          const uint32_t up = (e & 1) || e == last ? 1u : 0u;
+          v[q][i] = *reinterpret_cast<const uint32_t*>(dt + (e - up));
           hi[q] |= up << i;
         }
       }
