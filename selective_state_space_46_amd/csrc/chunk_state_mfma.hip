@@ -362,14 +362,23 @@ __device__ __forceinline__ void copy_to_lds16(const uint16_t* src, uint16_t* dst
 // out as fp32 ([b, c, h, p, n], as state_passing leaves them over the chunk
 // states) and the C B^T tiles as fp32 in both orientations (CB and CBt, as
 // chunk_state_mfma_kernel's MODE 1); else bf16 states and bf16 tiles.
-template <int N, int P, int SPC, int ST, bool F32S>
+//
+// REV (the backward's reverse pass): the same walk over the chunks in
+// reverse order with x -> dy, B -> C and the token weights exp(Acs_l) (the
+// chunk's inclusive cumulative decay), which carries the gradient G_c of the
+// state leaving chunk c backwards: G_{nc-1} = dfinal (init),
+// G_{c-1} = exp(Acs_c[Q-1]) G_c + sum_l exp(Acs_l) C_l dy_l^T, d init = G_{-1}
+// (fin). Each G_c goes out as bf16 in Hs ([b, c, h, p, n]) with its dot
+// products with H_c (fp32 states entering each chunk, Hst) in per-wave
+// partials: ghp[((b H + h) nc + c) P / 16 + part]. No tiles, Acs or dt rows.
+template <int N, int P, int SPC, int ST, bool F32S, bool REV>
 __global__ __launch_bounds__(kChainThreads) __attribute__((amdgpu_waves_per_eu(N == 128 && ST <= 3 ? 4 : 1)))
 void chunk_state_chain_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ Bm, const uint16_t* __restrict__ dt,
     const float* __restrict__ A, float* __restrict__ Acs, float* __restrict__ dtq, void* __restrict__ Hs,
     const float* __restrict__ init, float* __restrict__ fin, const uint16_t* __restrict__ Cm,
-    uint16_t* __restrict__ CB, uint16_t* __restrict__ CBt, int T, int H, int G, int Q, int nc, int nchain,
-    long ntiles) {
+    uint16_t* __restrict__ CB, uint16_t* __restrict__ CBt, const float* __restrict__ Hst, float* __restrict__ ghp,
+    int T, int H, int G, int Q, int nc, int nchain, long ntiles) {
   using Cfg = ChainCfg<N, ST>;
   constexpr int S = Cfg::STAGES, RBB = Cfg::RBB, RBX = Cfg::RBX, NCB = Cfg::NCB, NCX = Cfg::NCX;
   constexpr int OPS = Cfg::OPS, TPW = Cfg::TPW;
@@ -396,6 +405,10 @@ void chunk_state_chain_kernel(
   const int g = h0 / (H / G);                   // the B group (both heads share it)
   const int l32 = lane & 31, g2 = lane >> 5;
   const int nsl = nc * SPC;                     // slices of the row
+  // the walk's step k visits slice ks(k) and its chunk wc = k / SPC is
+  // chunk rc(wc) of the row (reversed in the reverse pass)
+  auto ks = [&](int k) { return REV ? nsl - 1 - k : k; };
+  auto rc = [&](int wc) { return REV ? nc - 1 - wc : wc; };
   const size_t hstate = size_t(P) * N;          // elements of one (b, h) state
   // column block j (32 columns): head h0 + (NHW == 2 ? j : 0), columns from pcol(j) of that head
   auto pcol = [&](int j) { return (c0 + 32 * j) % P; };
@@ -416,8 +429,8 @@ void chunk_state_chain_kernel(
     // i of hi, whether it is that word's upper half. 32-bit loads need no
     // widening, which would wait for them at once.
     const long last = long(nchain / (H * P / kChainCols)) * T * H - 1;   // the tensor's last element
-    auto dt_load = [&](int c, uint32_t (&v)[NHW][4], uint32_t (&hi)[NHW]) {
-      const ChunkRows cr = chunk_rows(nullptr, b, c, T, Q);
+    auto dt_load = [&](int wc, uint32_t (&v)[NHW][4], uint32_t (&hi)[NHW]) {
+      const ChunkRows cr = chunk_rows(nullptr, b, rc(wc), T, Q);
 #pragma unroll
       for (int q = 0; q < NHW; ++q) {
         hi[q] = 0u;
@@ -434,8 +447,8 @@ void chunk_state_chain_kernel(
     // lane and one wave scan of the lane totals) into slot c & 1; Acs and dt
     // of this lane's tokens into acs / v for the rows written after the next
     // dt loads
-    auto tables = [&](int c, int q, const uint32_t (&raw)[4], uint32_t hi, float (&acs)[4], float (&v)[4]) {
-      const ChunkRows cr = chunk_rows(nullptr, b, c, T, Q);
+    auto tables = [&](int wc, int q, const uint32_t (&raw)[4], uint32_t hi, float (&acs)[4], float (&v)[4]) {
+      const ChunkRows cr = chunk_rows(nullptr, b, rc(wc), T, Q);
       float tot = 0.f;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -453,8 +466,10 @@ void chunk_state_chain_kernel(
       const float last = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(acs[3]), (Q - 1) / 4));
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        if (4 * lane + i < Q) sw[q][c & 1][4 * lane + i] = exp_fast(last - acs[i]) * v[i];
-      if (lane == 0) sdecay[q][c & 1] = expf(last);
+        if (4 * lane + i < Q)
+          sw[q][wc & 1][4 * lane + i] =
+              REV ? (4 * lane + i < cr.n ? exp_fast(acs[i]) : 0.f) : exp_fast(last - acs[i]) * v[i];
+      if (lane == 0) sdecay[q][wc & 1] = expf(last);
     };
     // the Acs / dt rows of chunk c, head h0 + q (by the work-group holding
     // the head's first columns)
@@ -480,12 +495,14 @@ void chunk_state_chain_kernel(
     float tacs[NHW][4], tdt[NHW][4];
     // chunk c's tables, then chunk c + 1's dt, then chunk c's rows (stores
     // after the loads)
-    auto chunk = [&](int c) {
+    auto chunk = [&](int wc) {
 #pragma unroll
-      for (int q = 0; q < NHW; ++q) tables(c, q, dnext[q], dhi[q], tacs[q], tdt[q]);
-      if (c + 1 < nc) dt_load(c + 1, dnext, dhi);
+      for (int q = 0; q < NHW; ++q) tables(wc, q, dnext[q], dhi[q], tacs[q], tdt[q]);
+      if (wc + 1 < nc) dt_load(wc + 1, dnext, dhi);
+      if constexpr (!REV) {
 #pragma unroll
-      for (int q = 0; q < NHW; ++q) rows_out(c, q, tacs[q], tdt[q]);
+        for (int q = 0; q < NHW; ++q) rows_out(rc(wc), q, tacs[q], tdt[q]);
+      }
     };
     dt_load(0, dnext, dhi);
     chunk(0);
@@ -534,7 +551,7 @@ void chunk_state_chain_kernel(
       // slice k (clamped into the row: copies past its end repeat the last
       // slice into a free slot) into slot s
       auto issue = [&](int k, int s) {
-        k = min(k, nsl - 1);
+        k = ks(min(k, nsl - 1));
         const ChunkRows cr = chunk_rows(nullptr, b, k / SPC, T, Q);
         const int s0 = (k % SPC) * kChainSK;
         const long row0 = cr.r0 + s0;
@@ -605,7 +622,35 @@ void chunk_state_chain_kernel(
   // chunk c's start: H_c out as bf16 ([p][n] rows, four consecutive n of
   // p = pj + l32 per register run), then the running state scaled by the
   // chunk's decay
-  auto chunk_start = [&](int c) {
+  // REV: this lane's part of H_c (fp32, the runs of the accumulator layout),
+  // loaded one chunk ahead of its dot product with G_c
+  f32x4 hnext[REV ? TPW * 4 : 1];
+  auto h_load = [&](int c) {
+    if constexpr (REV) {
+      const float* hrow = Hst + ((size_t(b) * nc + c) * H + hj) * hstate + size_t(pj + l32) * N;
+#pragma unroll
+      for (int u = 0; u < TPW; ++u)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+          hnext[4 * u + jj] = *reinterpret_cast<const f32x4*>(hrow + 32 * ntile(u) + 8 * jj + 4 * g2);
+    }
+  };
+  if constexpr (REV) h_load(rc(0));
+  auto chunk_start = [&](int wc) {
+    const int c = rc(wc);
+    if constexpr (REV) {
+      // <G_c, H_c>: this wave's part, one partial per wave
+      float dot = 0.f;
+#pragma unroll
+      for (int u = 0; u < TPW; ++u)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) dot += acc[u][4 * jj + e] * hnext[4 * u + jj][e];
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) dot += __shfl_xor(dot, off, 64);
+      if (lane == 0) ghp[((size_t(b) * H + hj) * nc + c) * (P / 16) + 2 * (pj / 32) + (wave >> 1)] = dot;
+    }
     const size_t hoff = ((size_t(b) * nc + c) * H + hj) * hstate + size_t(pj + l32) * N;
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
@@ -621,18 +666,21 @@ void chunk_state_chain_kernel(
         }
       }
     }
-    const float decay = sdecay[hq][c & 1];
+    const float decay = sdecay[hq][wc & 1];
 #pragma unroll
     for (int u = 0; u < TPW; ++u)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[u][r] *= decay;
+    // the next chunk's H (after this chunk's stores: a later wait for the
+    // loads then finds only older stores)
+    if (REV && wc + 1 < nc) h_load(rc(wc + 1));
   };
   // slice k from slot s, all four k steps
   auto compute = [&](int k, int s) {
     // padding steps past the last slice (they keep the barrier pattern
     // fixed) compute nothing
     if (k >= nsl) return;
-    const int s0 = (k % SPC) * kChainSK;
+    const int s0 = (ks(k) % SPC) * kChainSK;
     const float* swc = sw[hq][(k / SPC) & 1];
     constexpr int KS = kChainSK / 16;
     // every LDS read of the slice first, so that one wait covers them all
@@ -680,18 +728,20 @@ void chunk_state_chain_kernel(
   }
 }
 
-template <int N, int P, int SPC, int ST, bool F32S>
+template <int N, int P, int SPC, int ST, bool F32S, bool REV>
 hipError_t launch_chain_np(const FwdShape& s, const void* x, const void* B, const void* C, const void* dt,
                            const float* A, float* Acs, float* dtq, void* Hs, const float* init, float* fin,
-                           uint16_t* CB, uint16_t* CBt, hipStream_t st, const StageEv& ev) {
+                           uint16_t* CB, uint16_t* CBt, const float* Hst, float* ghp, hipStream_t st,
+                           const StageEv& ev) {
   const int lpc = s.Q / 32;
-  const long ntiles = long(s.b) * s.nc * s.G * (lpc * (lpc + 1) / 2);
+  const long ntiles = REV ? 0 : long(s.b) * s.nc * s.G * (lpc * (lpc + 1) / 2);
   const long nchain = long(s.b) * s.H * P / kChainCols;
   const long blocks = nchain + (ntiles + kChainWaves - 1) / kChainWaves;
-  hipExtLaunchKernelGGL((chunk_state_chain_kernel<N, P, SPC, ST, F32S>), dim3(unsigned(blocks)), dim3(kChainThreads),
-                        0, st, ev.start, ev.stop, 0, static_cast<const uint16_t*>(x),
+  hipExtLaunchKernelGGL((chunk_state_chain_kernel<N, P, SPC, ST, F32S, REV>), dim3(unsigned(blocks)),
+                        dim3(kChainThreads), 0, st, ev.start, ev.stop, 0, static_cast<const uint16_t*>(x),
                         static_cast<const uint16_t*>(B), static_cast<const uint16_t*>(dt), A, Acs, dtq, Hs, init, fin,
-                        static_cast<const uint16_t*>(C), CB, CBt, s.T, s.H, s.G, s.Q, s.nc, int(nchain), ntiles);
+                        static_cast<const uint16_t*>(C), CB, CBt, Hst, ghp, s.T, s.H, s.G, s.Q, s.nc, int(nchain),
+                        ntiles);
   return hipGetLastError();
 }
 
@@ -778,10 +828,11 @@ bool chunk_state_chain_ok(const FwdShape& s) {
   return 2 * wgs >= cus && wgs <= per_unit * cus;
 }
 
-template <bool F32S>
+template <bool F32S, bool REV>
 hipError_t launch_chain(const FwdShape& s, const void* x, const void* B, const void* C, const void* dt,
                         const float* A, float* Acs, float* dtq, void* Hs, const float* init, float* fin,
-                        uint16_t* CB, uint16_t* CBt, hipStream_t st, const StageEv& ev) {
+                        uint16_t* CB, uint16_t* CBt, const float* Hst, float* ghp, hipStream_t st,
+                        const StageEv& ev) {
   if (!chunk_state_chain_ok(s)) return hipErrorInvalidValue;
   // two work-groups per unit (three slices resident; chunks of two or four
   // slices, which the check above ensures) where one per unit would not
@@ -791,21 +842,27 @@ hipError_t launch_chain(const FwdShape& s, const void* x, const void* B, const v
     using NP = decltype(np);
     constexpr int S1 = NP::n == 128 ? 5 : 3;
     if (two && NP::n == 128) {
-      switch (s.Q / kChainSK) {
-        case 2:
-          return launch_chain_np<NP::n, NP::p, 2, 3, F32S>(s, x, B, C, dt, A, Acs, dtq, Hs, init, fin, CB, CBt, st, ev);
-        case 4:
-          return launch_chain_np<NP::n, NP::p, 4, 3, F32S>(s, x, B, C, dt, A, Acs, dtq, Hs, init, fin, CB, CBt, st, ev);
+      if constexpr (REV) {
+        return hipErrorInvalidValue;            // one per unit only (registers)
+      } else {
+        switch (s.Q / kChainSK) {
+          case 2:
+            return launch_chain_np<NP::n, NP::p, 2, 3, F32S, REV>(s, x, B, C, dt, A, Acs, dtq, Hs, init, fin, CB, CBt,
+                                                                  Hst, ghp, st, ev);
+          case 4:
+            return launch_chain_np<NP::n, NP::p, 4, 3, F32S, REV>(s, x, B, C, dt, A, Acs, dtq, Hs, init, fin, CB, CBt,
+                                                                  Hst, ghp, st, ev);
+        }
+        return hipErrorInvalidValue;
       }
-      return hipErrorInvalidValue;
     }
     switch (s.Q / kChainSK) {
       case 1:
-        return launch_chain_np<NP::n, NP::p, 1, S1, F32S>(s, x, B, C, dt, A, Acs, dtq, Hs, init, fin, CB, CBt, st, ev);
+        return launch_chain_np<NP::n, NP::p, 1, S1, F32S, REV>(s, x, B, C, dt, A, Acs, dtq, Hs, init, fin, CB, CBt, Hst, ghp, st, ev);
       case 2:
-        return launch_chain_np<NP::n, NP::p, 2, S1, F32S>(s, x, B, C, dt, A, Acs, dtq, Hs, init, fin, CB, CBt, st, ev);
+        return launch_chain_np<NP::n, NP::p, 2, S1, F32S, REV>(s, x, B, C, dt, A, Acs, dtq, Hs, init, fin, CB, CBt, Hst, ghp, st, ev);
       case 4:
-        return launch_chain_np<NP::n, NP::p, 4, S1, F32S>(s, x, B, C, dt, A, Acs, dtq, Hs, init, fin, CB, CBt, st, ev);
+        return launch_chain_np<NP::n, NP::p, 4, S1, F32S, REV>(s, x, B, C, dt, A, Acs, dtq, Hs, init, fin, CB, CBt, Hst, ghp, st, ev);
     }
     return hipErrorInvalidValue;
   };
@@ -823,14 +880,30 @@ hipError_t launch_chunk_state_chain(const FwdShape& s, const void* x, const void
                                     const void* dt, const float* A, float* Acs, float* dtq, uint16_t* Hb,
                                     const float* init, float* fin, uint16_t* CB, hipStream_t st,
                                     const StageEv& ev) {
-  return launch_chain<false>(s, x, B, C, dt, A, Acs, dtq, Hb, init, fin, CB, nullptr, st, ev);
+  return launch_chain<false, false>(s, x, B, C, dt, A, Acs, dtq, Hb, init, fin, CB, nullptr, nullptr, nullptr, st,
+                                    ev);
 }
 
 hipError_t launch_chunk_state_chain_bwd(const FwdShape& s, const void* x, const void* B, const void* C,
                                         const void* dt, const float* A, float* Acs, float* dtq, float* Hst,
                                         const float* init, float* fin, uint16_t* CBf, uint16_t* CBt,
                                         hipStream_t st) {
-  return launch_chain<true>(s, x, B, C, dt, A, Acs, dtq, Hst, init, fin, CBf, CBt, st, StageEv{});
+  return launch_chain<true, false>(s, x, B, C, dt, A, Acs, dtq, Hst, init, fin, CBf, CBt, nullptr, nullptr, st,
+                                   StageEv{});
+}
+
+// The reverse walk holds a run of H_c per lane besides the accumulators, which
+// the two-per-unit occupancy leaves no room for: one work-group per unit.
+bool chunk_grad_chain_ok(const FwdShape& s) {
+  return chunk_state_chain_ok(s) && long(s.b) * s.H * s.P / kChainCols <= chain_units();
+}
+
+hipError_t launch_chunk_grad_chain_bwd(const FwdShape& s, const void* dy, const void* C, const void* dt,
+                                       const float* A, const float* dfinal, uint16_t* Gb, float* dinit,
+                                       const float* Hst, float* ghp, hipStream_t st) {
+  if (!chunk_grad_chain_ok(s)) return hipErrorInvalidValue;
+  return launch_chain<false, true>(s, dy, C, nullptr, dt, A, nullptr, nullptr, Gb, dfinal, dinit, nullptr, nullptr,
+                                   Hst, ghp, st, StageEv{});
 }
 
 hipError_t launch_chunk_state_mfma_bwd(const FwdShape& s, const void* x, const void* B, const void* C,

@@ -555,13 +555,21 @@ ssd_status ssd_chunk_scan_bwd(const void* x, const void* dt, const float* A, con
       return SSD_ERR_HIP;
     if (launch_state_passing(s, Sst, nullptr, Acs, init_state, fin, hs) != hipSuccess) return SSD_ERR_HIP;
   }
-  // what each chunk's outputs give the state entering it, then the reverse pass
-  if (launch_chunk_dstates_mfma(s, dy, C, dt, A, dS, hs) != hipSuccess) return SSD_ERR_HIP;
-  if (launch_state_passing_bwd(s, dS, Sst, Acs, dfinal, Gb, ghp, dinit, hs) != hipSuccess)
-    return SSD_ERR_HIP;
+  // what each chunk's outputs give the state entering it, then the reverse
+  // pass -- in one reverse walk where the fused walk applies
+  const bool rev_walk = chunk_grad_chain_ok(s);
+  if (rev_walk) {
+    if (launch_chunk_grad_chain_bwd(s, dy, C, dt, A, dfinal, Gb, dinit, Sst, ghp, hs) != hipSuccess)
+      return SSD_ERR_HIP;
+  } else {
+    if (launch_chunk_dstates_mfma(s, dy, C, dt, A, dS, hs) != hipSuccess) return SSD_ERR_HIP;
+    if (launch_state_passing_bwd(s, dS, Sst, Acs, dfinal, Gb, ghp, dinit, hs) != hipSuccess)
+      return SSD_ERR_HIP;
+  }
   BwdArgs a;
   a.x = x; a.B = B; a.C = C; a.dy = dy; a.Acs = Acs; a.dtq = dtq; a.CB = reinterpret_cast<const float*>(CBf); a.CBt = reinterpret_cast<const float*>(CBt); a.Hst = Sst; a.Gb = Gb;
-  a.ghp = ghp; a.nghp = nghp; a.A = A; a.D = D; a.dx = dx; a.ddt = ddt; a.dB = dB; a.dC = dC;
+  a.ghp = ghp; a.nghp = rev_walk ? s.P / 16 : nghp;   // the reverse walk's partials per (b, h, c)
+  a.A = A; a.D = D; a.dx = dx; a.ddt = ddt; a.dB = dB; a.dC = dC;
   a.nslice = nslice; a.dBs = dBs; a.dCs = dCs; a.dAp = dAp; a.dDp = dDp;
   float* tokd = reinterpret_cast<float*>(ws + w.tok);
   const size_t rowf = size_t(s.b) * s.H * s.nc * s.Q;

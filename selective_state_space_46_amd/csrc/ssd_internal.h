@@ -195,6 +195,16 @@ hipError_t launch_chunk_state_chain_bwd(const FwdShape& s, const void* x, const 
                                         const void* dt, const float* A, float* Acs, float* dtq, float* Hst,
                                         const float* init, float* fin, uint16_t* CBf, uint16_t* CBt,
                                         hipStream_t st);
+// The backward's reverse pass through the same walk in reverse (shapes
+// chunk_state_chain_ok accepts): the gradients G_c of the states leaving each
+// chunk as bf16 in Gb ([b, c, h, p, n]), their dot products with Hst (the
+// fp32 states entering each chunk) in P / 16 partials per (b, h, c) in ghp,
+// and d init (fp32 [b, h, n, p], may be null), from dy, C and dfinal (may
+// be null).
+bool chunk_grad_chain_ok(const FwdShape& s);   // one work-group per compute unit
+hipError_t launch_chunk_grad_chain_bwd(const FwdShape& s, const void* dy, const void* C, const void* dt,
+                                       const float* A, const float* dfinal, uint16_t* Gb, float* dinit,
+                                       const float* Hst, float* ghp, hipStream_t st);
 
 // Hb == nullptr: states entering each chunk overwrite S in place (fp32);
 // otherwise they are written to Hb as bf16 and S is left as it was.

@@ -99,3 +99,16 @@ def test_bwd_full_130m_layer():
     w = workloads.MAMBA2_130M
     inp = _inputs(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, seed=7600)
     _check(inp)
+
+
+@pytest.mark.parametrize("b,T,H,P,N,G", [(4, 300, 32, 64, 128, 2), (4, 330, 64, 32, 128, 4),
+                                         (2, 200, 64, 128, 128, 2), (2, 260, 64, 64, 256, 4)])
+def test_bwd_reverse_walk_shapes(b, T, H, P, N, G):
+    """128..256 work-groups of 64 (head, p) columns: the gradients of the
+    chunk states come from the one reverse walk (several chunks, ragged
+    tail, head pairs at headdim 32, dstate 256)"""
+    _check(_inputs(b, T, H, P, N, G, seed=7700 + P + N + H))
+
+
+def test_bwd_reverse_walk_without_optional_inputs():
+    _check(_inputs(4, 300, 32, 64, 128, 2, seed=7800, init=False, dfinal=False, D=False))
