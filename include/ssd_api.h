@@ -87,9 +87,15 @@ typedef enum { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype;
  * Bytes of device workspace ssd_chunk_scan_fwd needs for these sizes; 0 when
  * the sizes are invalid. The workspace holds the per-chunk cumulative decay
  * (fp32 [batch, nheads, nchunks, chunk_len], nchunks = ceil(seqlen/chunk_len)),
- * the step sizes widened to fp32 in the same layout, and the per-chunk states
- * (fp32 [batch, nchunks, nheads, dstate, headdim]). It carries nothing from
- * one call to the next.
+ * the step sizes widened to fp32 in the same layout, and the states entering
+ * each chunk (fp32 [batch, nchunks, nheads, dstate, headdim] on the generic
+ * path; on the bf16 matrix-core path bf16, plus the chunk states in fp32 when
+ * they are passed by a separate launch, plus the C B^T products of each
+ * chunk). It carries nothing from one call to the next. `dtype` is an
+ * argument because the two paths need different amounts. The answer depends
+ * on the current HIP device (its compute-unit count chooses the launches,
+ * see ssd_chunk_scan_fwd_fused_states): query on the device that runs the
+ * call.
  */
 SSD_API size_t ssd_chunk_scan_fwd_workspace(int batch, int seqlen, int nheads, int headdim,
                                     int dstate, int ngroups, int chunk_len, ssd_dtype dtype);
@@ -128,21 +134,40 @@ SSD_API ssd_status ssd_chunk_scan_fwd(const void *x, const void *dt, const float
                               void *workspace, size_t workspace_bytes, void *stream);
 
 /*
- * Whether ssd_chunk_scan_fwd with these sizes runs the chunk states and the
- * passing of states between chunks as one launch on the current HIP device
- * (1) or as two (0; also for sizes the call would reject). The results agree
- * up to rounding either way. The fused launch walks each batch row and 64
- * columns of the flattened (head, headdim) axis (headdim 32: two heads, which
- * must share a B/C group) through its chunks in order with the running state
- * on chip and writes only the bf16 states entering each chunk; it is used for
- * the bf16 matrix-core path with dstate 128 or 256 and chunk_len a multiple
- * of 64 when those walks fill the device in one round: between half and all
- * of the compute units, or, at dstate 128 with chunk_len >= 128, up to two
- * per unit. It reads the device's compute-unit count, so it needs a current
- * HIP device (0 without one).
+ * How ssd_chunk_scan_fwd with these sizes forms the states entering each
+ * chunk on the current HIP device: 0 = a chunk-state launch and a separate
+ * state-passing launch (also for sizes the call would reject); k >= 1 = one
+ * fused launch of walks, each batch row cut into k segments of consecutive
+ * chunks (1: whole rows). The results agree up to rounding either way.
+ *
+ * A walk takes one batch row (or one segment of it) and 64 columns of the
+ * flattened (head, headdim) axis (headdim 32: two heads, which must share a
+ * B/C group) through its chunks in order with the running state on chip and
+ * writes only the bf16 states entering each chunk. It is used for the bf16
+ * matrix-core path with dstate 128 or 256 and chunk_len a multiple of 64 when
+ * the walks fill the device in one round: between half and all of the
+ * compute units, or, at dstate 128 with chunk_len >= 128, up to two per unit.
+ * Where whole rows give fewer walks than half the units (a few long rows),
+ * each row is cut into k > 1 segments, about one walk per unit; every segment
+ * starts from zero, a short recurrence over the segments gives the state
+ * entering each one, and the chunk outputs add its decayed contribution (the
+ * state handed from chunk to chunk composes associatively; youngju.dev page,
+ * "SSDアルゴリズムとチャンク分割"). It reads the device's compute-unit count,
+ * so it needs a current HIP device (0 without one).
  */
 SSD_API int ssd_chunk_scan_fwd_fused_states(int batch, int seqlen, int nheads, int headdim, int dstate,
                                             int ngroups, int chunk_len, ssd_dtype dtype);
+
+/*
+ * The same choice for a device with `compute_units` compute units (no device
+ * needed): returns what ssd_chunk_scan_fwd_fused_states returns on such a
+ * device, and, when it is above 0, the number of chunks per segment in
+ * *seglen (the last segment may have fewer; segment k covers chunks
+ * k * seglen .. min(nchunks, (k + 1) * seglen) - 1). *seglen is 0 otherwise;
+ * seglen may be NULL. Sizes the forward rejects give 0.
+ */
+SSD_API int ssd_chunk_scan_fwd_plan(int batch, int seqlen, int nheads, int headdim, int dstate, int ngroups,
+                                    int chunk_len, ssd_dtype dtype, int compute_units, int *seglen);
 
 /*
  * Measurement variant of ssd_chunk_scan_fwd: identical computation, and it
@@ -156,7 +181,9 @@ SSD_API int ssd_chunk_scan_fwd_fused_states(int batch, int seqlen, int nheads, i
  * computes the cumulative sums, the C B^T tiles and the chunk states; stage 0
  * launches nothing there and its two events are recorded back to back. Where
  * ssd_chunk_scan_fwd_fused_states is 1, stage [1] also passes the states
- * between chunks and stage [2] launches nothing the same way.
+ * between chunks and stage [2] launches nothing the same way; where it is
+ * above 1, stage [1] is the segmented walk and stage [2] the recurrence over
+ * the segments.
  * stage_events may be NULL (then it is ssd_chunk_scan_fwd). A failed event
  * record returns SSD_ERR_HIP.
  */
@@ -186,7 +213,6 @@ SSD_API ssd_status ssd_state_update(float *state, const void *x, const void *dt,
                             int batch, int nheads, int headdim, int dstate, int ngroups,
                             ssd_dtype dtype, void *stream);
 
-/* Static, NUL-terminated description of a status code. */
 /*
  * Packed variable-length sequences. nseq sequences are packed along one token
  * axis of total_tokens tokens: sequence i is tokens cu_seqlens[i] ..
@@ -225,6 +251,7 @@ SSD_API ssd_status ssd_chunk_scan_fwd_varlen(const void *x, const void *dt, cons
                                              int dstate, int ngroups, int chunk_len, ssd_dtype dtype,
                                              void *workspace, size_t workspace_bytes, void *stream);
 
+/* Static, NUL-terminated description of a status code. */
 SSD_API const char *ssd_status_string(ssd_status status);
 
 #ifdef __cplusplus

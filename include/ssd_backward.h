@@ -25,9 +25,24 @@
 extern "C" {
 #endif
 
-/* Workspace bytes for ssd_chunk_scan_bwd; 0 when the sizes are not supported. */
+/* Workspace bytes for ssd_chunk_scan_bwd; 0 when the sizes are not supported.
+ * Like the forward's query it depends on the current HIP device (its
+ * compute-unit count chooses the launches, see below). */
 SSD_API size_t ssd_chunk_scan_bwd_workspace(int batch, int seqlen, int nheads, int headdim, int dstate,
                                             int ngroups, ssd_dtype dtype);
+
+/*
+ * Which launches ssd_chunk_scan_bwd uses for these sizes on the current HIP
+ * device (0 for sizes it rejects): bit 0 set = the recomputation of the chunk
+ * states and of the states entering each chunk runs as one walk per (batch
+ * row, 64 columns of the flattened (head, headdim) axis), as in the forward
+ * (else a chunk-state and a state-passing launch); bit 1 set = the gradients
+ * of those states come from the same walk run over the chunks in reverse
+ * (else a per-chunk launch and a reverse state-passing launch). The
+ * gradients agree up to rounding either way.
+ */
+SSD_API int ssd_chunk_scan_bwd_fused_walks(int batch, int seqlen, int nheads, int headdim, int dstate,
+                                           int ngroups, ssd_dtype dtype);
 
 /*
  * Gradients of the loss L through y = ssd_chunk_scan_fwd(x, dt, A, B, C, D,

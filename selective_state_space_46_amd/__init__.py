@@ -9,7 +9,8 @@ the entry points raises.
 
 Entry points (same names as the C ABI):
     ssd_chunk_scan_fwd_workspace(...) -> bytes
-    ssd_chunk_scan_fwd_fused_states(...) -> bool (one launch for chunk states + passing)
+    ssd_chunk_scan_fwd_fused_states(...) -> int (0: two launches for chunk states + passing;
+                                                 k: one fused launch, k segments per row)
     ssd_chunk_scan_fwd(x, dt, A, B, C, D, init_state, chunk_len) -> (y, final_state)
     ssd_state_update(state, x, dt, A, B, C, D) -> y     (state updated in place)
     ssd_status_string(code) -> str
@@ -32,10 +33,11 @@ from typing import Optional, Tuple
 __all__ = [
     "SSD_F32", "SSD_BF16", "SSDError", "lib", "lib_path",
     "ssd_chunk_scan_fwd_workspace", "ssd_chunk_scan_fwd", "ssd_chunk_scan_fwd_timed",
-    "ssd_chunk_scan_fwd_fused_states",
+    "ssd_chunk_scan_fwd_fused_states", "ssd_chunk_scan_fwd_plan",
     "ssd_state_update", "ssd_status_string", "ssd_chunk_scan_fwd_varlen",
     "ssd_chunk_scan_fwd_varlen_workspace", "ssd_gated_rmsnorm", "ssd_causal_conv1d_fwd",
     "ssd_causal_conv1d_update", "ssd_chunk_scan_bwd_workspace", "ssd_chunk_scan_bwd",
+    "ssd_chunk_scan_bwd_fused_walks",
 ]
 
 SSD_F32 = 0
@@ -77,6 +79,8 @@ def lib() -> ctypes.CDLL:
     L.ssd_chunk_scan_fwd_workspace.restype = sz
     L.ssd_chunk_scan_fwd_fused_states.argtypes = [i32] * 7 + [i32]
     L.ssd_chunk_scan_fwd_fused_states.restype = i32
+    L.ssd_chunk_scan_fwd_plan.argtypes = [i32] * 7 + [i32, i32, ctypes.POINTER(i32)]
+    L.ssd_chunk_scan_fwd_plan.restype = i32
     L.ssd_chunk_scan_fwd.argtypes = [vp] * 9 + [i32] * 7 + [i32, vp, sz, vp]
     L.ssd_chunk_scan_fwd.restype = i32
     L.ssd_chunk_scan_fwd_timed.argtypes = [vp] * 9 + [i32] * 7 + [i32, vp, sz, vp, vp]
@@ -98,6 +102,8 @@ def lib() -> ctypes.CDLL:
     L.ssd_causal_conv1d_update.restype = i32
     L.ssd_chunk_scan_bwd_workspace.argtypes = [i32] * 7
     L.ssd_chunk_scan_bwd_workspace.restype = sz
+    L.ssd_chunk_scan_bwd_fused_walks.argtypes = [i32] * 7
+    L.ssd_chunk_scan_bwd_fused_walks.restype = i32
     L.ssd_chunk_scan_bwd.argtypes = [vp] * 16 + [i32] * 7 + [vp, sz, vp]
     L.ssd_chunk_scan_bwd.restype = i32
     _lib = L
@@ -110,22 +116,40 @@ def ssd_status_string(code: int) -> str:
 
 def ssd_chunk_scan_fwd_workspace(batch: int, seqlen: int, nheads: int, headdim: int, dstate: int,
                                  ngroups: int, chunk_len: int, dtype: int) -> int:
+    _bring_up_device()
     return int(lib().ssd_chunk_scan_fwd_workspace(batch, seqlen, nheads, headdim, dstate, ngroups,
                                                   chunk_len, dtype))
 
 
-def ssd_chunk_scan_fwd_fused_states(batch: int, seqlen: int, nheads: int, headdim: int, dstate: int,
-                                    ngroups: int, chunk_len: int, dtype: int) -> bool:
-    """True when the forward runs chunk states and state passing as one launch
-    on the current device (see ssd_api.h). The library asks the HIP runtime
-    for the device's compute units; torch's runtime is brought up first (as
-    every tensor-taking call here does implicitly), since a process whose
-    first HIP call comes from the library leaves torch without a device."""
+def _bring_up_device():
+    """The library asks the HIP runtime for the device's compute units; torch's
+    runtime is brought up first (as every tensor-taking call here does
+    implicitly), since a process whose first HIP call comes from the library
+    leaves torch without a device."""
     import torch
     if torch.cuda.is_available():
         torch.cuda.current_device()
-    return bool(lib().ssd_chunk_scan_fwd_fused_states(batch, seqlen, nheads, headdim, dstate, ngroups,
-                                                      chunk_len, dtype))
+
+
+def ssd_chunk_scan_fwd_fused_states(batch: int, seqlen: int, nheads: int, headdim: int, dstate: int,
+                                    ngroups: int, chunk_len: int, dtype: int) -> int:
+    """How the forward forms the states entering each chunk on the current
+    device (see ssd_api.h): 0 = chunk-state and state-passing launches,
+    k >= 1 = one fused launch of walks over k segments per batch row."""
+    _bring_up_device()
+    return int(lib().ssd_chunk_scan_fwd_fused_states(batch, seqlen, nheads, headdim, dstate, ngroups,
+                                                     chunk_len, dtype))
+
+
+def ssd_chunk_scan_fwd_plan(batch: int, seqlen: int, nheads: int, headdim: int, dstate: int, ngroups: int,
+                            chunk_len: int, dtype: int, compute_units: int) -> Tuple[int, int]:
+    """(segments per row, chunks per segment) the forward chooses on a device
+    with `compute_units` compute units; (0, 0) = chunk-state and
+    state-passing launches. Needs no device."""
+    sl = ctypes.c_int(0)
+    n = int(lib().ssd_chunk_scan_fwd_plan(batch, seqlen, nheads, headdim, dstate, ngroups, chunk_len, dtype,
+                                          compute_units, ctypes.byref(sl)))
+    return n, int(sl.value)
 
 
 # --------------------------------------------------------------------------
@@ -422,7 +446,16 @@ def ssd_chunk_scan_fwd_varlen(x, dt, A, B, C, D, cu_seqlens, init_states=None, c
 
 def ssd_chunk_scan_bwd_workspace(batch: int, seqlen: int, nheads: int, headdim: int, dstate: int,
                                  ngroups: int, dtype: int) -> int:
+    _bring_up_device()
     return int(lib().ssd_chunk_scan_bwd_workspace(batch, seqlen, nheads, headdim, dstate, ngroups, dtype))
+
+
+def ssd_chunk_scan_bwd_fused_walks(batch: int, seqlen: int, nheads: int, headdim: int, dstate: int,
+                                   ngroups: int, dtype: int) -> int:
+    """Bit 0: the backward's recomputation runs as one walk launch; bit 1: its
+    state gradients come from the reverse walk (see ssd_backward.h)."""
+    _bring_up_device()
+    return int(lib().ssd_chunk_scan_bwd_fused_walks(batch, seqlen, nheads, headdim, dstate, ngroups, dtype))
 
 
 def ssd_chunk_scan_bwd(x, dt, A, B, C, D=None, init_state=None, dy=None, dfinal=None, *, out=None,

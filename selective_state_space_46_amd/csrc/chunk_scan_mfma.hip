@@ -42,6 +42,11 @@
 //      buffers used in turn.
 //   3. + D x (x from the same LDS tile), bf16 rounding, 8-byte stores of 4
 //      consecutive p.
+// SEG (rows cut into segments by the fused chunk-state walk): Hb holds the
+// local states, from zero at each segment's start; the state entering chunk
+// c of segment k >= 1 is Hb_c + exp(cdec_c) Hin_k (Hin fp32 [b, nseg, H, P,
+// N], the state entering each segment; cdec_c <= 0), formed in fp32 where
+// H_c is staged or loaded and rounded to bf16 once.
 #include "mfma_util.h"
 
 namespace ssd {
@@ -51,14 +56,26 @@ constexpr int kThreads = 256;
 constexpr int kSC = 256;          // tokens per super-chunk
 constexpr float kLog2e = 1.4426950408889634f;
 
+// 8 bf16 of a local state plus alpha times the 8 matching fp32 of Hin, rounded
+// to bf16 once
+__device__ __forceinline__ u32x4 seg_combine(const u32x4& v, const float* hin, float alpha) {
+  const f32x4 a = *reinterpret_cast<const f32x4*>(hin);
+  const f32x4 b = *reinterpret_cast<const f32x4*>(hin + 4);
+  return u32x4{pack_bf16x2(bf16_lo(v[0]) + alpha * a[0], bf16_hi(v[0]) + alpha * a[1]),
+               pack_bf16x2(bf16_lo(v[1]) + alpha * a[2], bf16_hi(v[1]) + alpha * a[3]),
+               pack_bf16x2(bf16_lo(v[2]) + alpha * b[0], bf16_hi(v[2]) + alpha * b[1]),
+               pack_bf16x2(bf16_lo(v[3]) + alpha * b[2], bf16_hi(v[3]) + alpha * b[3])};
+}
+
 // VARLEN: chunk rows from the chunk table tab (packed sequences), else the
-// equal-length layout (tab unused).
-template <int N, int P, bool HLDS, bool VARLEN>
+// equal-length layout (tab unused). SEG: the segment correction above.
+template <int N, int P, bool HLDS, bool VARLEN, bool SEG>
 __global__ __launch_bounds__(kThreads) void chunk_scan_mfma_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ CB, const uint16_t* __restrict__ Cm,
     const float* __restrict__ Acs, const float* __restrict__ dtq, const uint16_t* __restrict__ Hb,
     const float* __restrict__ D, uint16_t* __restrict__ y, const int4* __restrict__ tab, int T, int H,
-    int G, int Q, int nc, int nsc) {
+    int G, int Q, int nc, int nsc, const float* __restrict__ Hin, const float* __restrict__ cdec, int nseg,
+    int seglen) {
   constexpr int kHS = N + 8;  // H^T row stride (bf16): 16-byte reads of 16 lanes hit distinct banks
   constexpr int RBX = P / 8;  // 16-byte chunks per X' row
   constexpr int HROWS = HLDS ? P : 1;
@@ -145,11 +162,23 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_mfma_kernel(
     static_assert(kThreads % (N / 8) == 0, "H staging shape");
     constexpr int kStep = kThreads / (N / 8);        // rows p per pass
     const int p0 = tid / (N / 8), seg = tid % (N / 8);
+    const int sg = SEG ? c0 / seglen : 0;            // the chunk's segment (uniform)
+    if (SEG && sg > 0) {
+      const float alpha = exp_fast(cdec[(size_t(b) * H + h) * nc + c0]);
+      const float* hin = Hin + ((size_t(b) * nseg + sg) * H + h) * size_t(P) * N;
 #pragma unroll
-    for (int k = 0; k < (P + kStep - 1) / kStep; ++k)
-      if (P % kStep == 0 || p0 + k * kStep < P)
-        *reinterpret_cast<u32x4*>(&sHt[p0 + k * kStep][8 * seg]) =
-            load16(hsrc + size_t(p0 + k * kStep) * N + 8 * seg);
+      for (int k = 0; k < (P + kStep - 1) / kStep; ++k)
+        if (P % kStep == 0 || p0 + k * kStep < P) {
+          const size_t o = size_t(p0 + k * kStep) * N + 8 * seg;
+          *reinterpret_cast<u32x4*>(&sHt[p0 + k * kStep][8 * seg]) = seg_combine(load16(hsrc + o), hin + o, alpha);
+        }
+    } else {
+#pragma unroll
+      for (int k = 0; k < (P + kStep - 1) / kStep; ++k)
+        if (P % kStep == 0 || p0 + k * kStep < P)
+          *reinterpret_cast<u32x4*>(&sHt[p0 + k * kStep][8 * seg]) =
+              load16(hsrc + size_t(p0 + k * kStep) * N + 8 * seg);
+    }
   }
   // raw x, token-major, swizzled: issued with the loads above. Thread tid
   // copies 16-byte chunk tid % RBX of rows tid / RBX + k kStep; kStep is a
@@ -232,6 +261,10 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_mfma_kernel(
     // ---- y^T = H_c^T C_l^T, then * exp(Acs_l)
     f32x16 acc[P / 32];
     const float sl = __builtin_amdgcn_exp2f(sA[lcol]);
+    // segments, per-fragment path: this block's chunk's segment and the
+    // weight of the state entering it (uniform)
+    const int sgb = SEG && !HLDS ? cg / seglen : 0;
+    const float alpha_b = SEG && !HLDS && sgb > 0 ? exp_fast(cdec[(size_t(b) * H + h) * nc + cg]) : 0.f;
 #pragma unroll
     for (int pb = 0; pb < P / 32; ++pb) {
       acc[pb] = zero16();
@@ -241,8 +274,9 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_mfma_kernel(
         if constexpr (HLDS) {
           hf = *reinterpret_cast<const u32x4*>(&sHt[32 * pb + l32][16 * ks + 8 * g2]);
         } else {
-          hf = load16(Hb + (((size_t(b) * nc + cg) * H + h) * P + 32 * pb + l32) * size_t(N) + 16 * ks +
-                      8 * g2);
+          const size_t o = (size_t(32 * pb + l32)) * N + 16 * ks + 8 * g2;
+          hf = load16(Hb + ((size_t(b) * nc + cg) * H + h) * size_t(P) * N + o);
+          if (SEG && sgb > 0) hf = seg_combine(hf, Hin + ((size_t(b) * nseg + sgb) * H + h) * size_t(P) * N + o, alpha_b);
         }
         acc[pb] = mfma32x32x16(hf, cf[ks], acc[pb]);
       }
@@ -340,31 +374,37 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_mfma_kernel(
 template <int N, int P>
 hipError_t launch_np(const FwdShape& s, const void* x, const uint16_t* CB, const void* C,
                      const float* Acs, const float* dtq, const uint16_t* Hb, const float* D, void* y,
-                     const int4* tab, hipStream_t st, const StageEv& ev) {
+                     const int4* tab, hipStream_t st, const StageEv& ev, const SegStates& sg) {
   const int cps = kSC / s.Q;
   const int nsc = (s.nc + cps - 1) / cps;   // = ceil(T / 256) for equal-length rows
   const long blocks = long(s.b) * nsc * s.H;
   auto go = [&](auto kern) {
     hipExtLaunchKernelGGL(kern, dim3(unsigned(blocks)), dim3(kThreads), 0, st, ev.start, ev.stop, 0,
                           static_cast<const uint16_t*>(x), CB, static_cast<const uint16_t*>(C), Acs, dtq, Hb, D,
-                          static_cast<uint16_t*>(y), tab, s.T, s.H, s.G, s.Q, s.nc, nsc);
+                          static_cast<uint16_t*>(y), tab, s.T, s.H, s.G, s.Q, s.nc, nsc, sg.Hin, sg.cdec, sg.nseg,
+                          sg.seglen);
   };
+  const bool seg = sg.nseg > 1;
+  if (seg && (tab || !sg.Hin || !sg.cdec || sg.seglen < 1)) return hipErrorInvalidValue;
   // one chunk per super-chunk: its H_c^T is staged in LDS
-  if (s.Q == kSC)
-    tab ? go(chunk_scan_mfma_kernel<N, P, true, true>) : go(chunk_scan_mfma_kernel<N, P, true, false>);
-  else
-    tab ? go(chunk_scan_mfma_kernel<N, P, false, true>) : go(chunk_scan_mfma_kernel<N, P, false, false>);
+  if (s.Q == kSC) {
+    if (seg) go(chunk_scan_mfma_kernel<N, P, true, false, true>);
+    else tab ? go(chunk_scan_mfma_kernel<N, P, true, true, false>) : go(chunk_scan_mfma_kernel<N, P, true, false, false>);
+  } else {
+    if (seg) go(chunk_scan_mfma_kernel<N, P, false, false, true>);
+    else tab ? go(chunk_scan_mfma_kernel<N, P, false, true, false>) : go(chunk_scan_mfma_kernel<N, P, false, false, false>);
+  }
   return hipGetLastError();
 }
 
 template <int N>
 hipError_t launch_n(const FwdShape& s, const void* x, const uint16_t* CB, const void* C,
                     const float* Acs, const float* dtq, const uint16_t* Hb, const float* D, void* y,
-                    const int4* tab, hipStream_t st, const StageEv& ev) {
+                    const int4* tab, hipStream_t st, const StageEv& ev, const SegStates& sg) {
   switch (s.P) {
-    case 32: return launch_np<N, 32>(s, x, CB, C, Acs, dtq, Hb, D, y, tab, st, ev);
-    case 64: return launch_np<N, 64>(s, x, CB, C, Acs, dtq, Hb, D, y, tab, st, ev);
-    case 128: return launch_np<N, 128>(s, x, CB, C, Acs, dtq, Hb, D, y, tab, st, ev);
+    case 32: return launch_np<N, 32>(s, x, CB, C, Acs, dtq, Hb, D, y, tab, st, ev, sg);
+    case 64: return launch_np<N, 64>(s, x, CB, C, Acs, dtq, Hb, D, y, tab, st, ev, sg);
+    case 128: return launch_np<N, 128>(s, x, CB, C, Acs, dtq, Hb, D, y, tab, st, ev, sg);
   }
   return hipErrorInvalidValue;
 }
@@ -374,12 +414,12 @@ hipError_t launch_n(const FwdShape& s, const void* x, const uint16_t* CB, const 
 hipError_t launch_chunk_scan_mfma(const FwdShape& s, const void* x, const uint16_t* CB,
                                   const void* C, const float* Acs, const float* dtq,
                                   const uint16_t* Hb, const float* D, void* y, const int4* tab,
-                                  hipStream_t st, const StageEv& ev) {
+                                  hipStream_t st, const StageEv& ev, const SegStates& sg) {
   switch (s.N) {
-    case 32: return launch_n<32>(s, x, CB, C, Acs, dtq, Hb, D, y, tab, st, ev);
-    case 64: return launch_n<64>(s, x, CB, C, Acs, dtq, Hb, D, y, tab, st, ev);
-    case 128: return launch_n<128>(s, x, CB, C, Acs, dtq, Hb, D, y, tab, st, ev);
-    case 256: return launch_n<256>(s, x, CB, C, Acs, dtq, Hb, D, y, tab, st, ev);
+    case 32: return launch_n<32>(s, x, CB, C, Acs, dtq, Hb, D, y, tab, st, ev, sg);
+    case 64: return launch_n<64>(s, x, CB, C, Acs, dtq, Hb, D, y, tab, st, ev, sg);
+    case 128: return launch_n<128>(s, x, CB, C, Acs, dtq, Hb, D, y, tab, st, ev, sg);
+    case 256: return launch_n<256>(s, x, CB, C, Acs, dtq, Hb, D, y, tab, st, ev, sg);
   }
   return hipErrorInvalidValue;
 }

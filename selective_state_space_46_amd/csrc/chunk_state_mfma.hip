@@ -25,6 +25,9 @@
 // faster on MI355X than a head pair sharing the B slice (fewer accumulators,
 // twice the work-groups) or four waves (half the loads in flight per CU).
 // Output tiles go to HBM as fp32 rows of 32 consecutive n.
+#include <algorithm>
+#include <atomic>
+
 #include "mfma_util.h"
 
 namespace ssd {
@@ -289,6 +292,25 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma_kernel(
 // accumulate on top, leaving H_{c+1}. The fp32 chunk states S_c never reach
 // HBM (the two-kernel form writes and re-reads them).
 //
+// Segments (forward only). Where one walk per (batch row, 64 columns) leaves
+// most compute units idle (a few long rows), each row is cut into nseg
+// segments of seglen consecutive chunks (the last may be shorter) and every
+// (row, 64 columns, segment) walks its own segment: segment 0 from the
+// initial state, the others from zero. The state handed from chunk to chunk
+// is linear in the state a segment starts from, and the summaries compose
+// associatively ((decay_1, S_1) then (decay_2, S_2) gives (decay_1 decay_2,
+// decay_2 S_1 + S_2); youngju.dev "Mamba / selective SSM",
+// "SSDアルゴリズムとチャンク分割": the state passed between chunks by the
+// recurrence), so the true state entering chunk c of segment k is
+//   H_c = H_c^local + exp(cdec_c) Hin_k,
+// with cdec_c the summed chunk decay exponents from the segment's start to c
+// and Hin_k the state entering segment k. A segmented walk writes H_c^local
+// (bf16), cdec (fp32 [b, H, nc]), its segment's total decay exponent (segdec,
+// fp32 [b, H, nseg]) and its last local state (fp32 [b, nseg, H, P, N], the
+// layout of the states entering each chunk) in place of the final state;
+// state_passing then runs the recurrence over the segments, and chunk_scan
+// adds exp(cdec_c) Hin_k where it stages H_c.
+//
 // Tokens stream through 64-row slices of B (all of dstate, shared by the two
 // column blocks) and x (the 64 columns), copied straight from global memory
 // into LDS (global_load_lds, 16 bytes per lane) in a swizzled row-major
@@ -378,7 +400,8 @@ void chunk_state_chain_kernel(
     const float* __restrict__ A, float* __restrict__ Acs, float* __restrict__ dtq, void* __restrict__ Hs,
     const float* __restrict__ init, float* __restrict__ fin, const uint16_t* __restrict__ Cm,
     uint16_t* __restrict__ CB, uint16_t* __restrict__ CBt, const float* __restrict__ Hst, float* __restrict__ ghp,
-    int T, int H, int G, int Q, int nc, int nchain, long ntiles) {
+    float* __restrict__ cdec, float* __restrict__ segdec, int T, int H, int G, int Q, int nc, int nb, int nseg,
+    int seglen, int nchain, long ntiles) {
   using Cfg = ChainCfg<N, ST>;
   constexpr int S = Cfg::STAGES, RBB = Cfg::RBB, RBX = Cfg::RBX, NCB = Cfg::NCB, NCX = Cfg::NCX;
   constexpr int OPS = Cfg::OPS, TPW = Cfg::TPW;
@@ -398,17 +421,22 @@ void chunk_state_chain_kernel(
   __shared__ __attribute__((aligned(16))) float sw[NHW][2][kMaxQ];
   __shared__ float sdecay[NHW][2];
 
+  // walk id = ((b nseg + seg) cpr + column block): the walks of one (row,
+  // segment) share every B slice and sit next to each other (one XCD's L2)
   const int id = xcd_swizzle(int(blockIdx.x), nchain);
-  const int cpr = H * P / kChainCols;           // work-groups per batch row
-  const int b = id / cpr, c0 = (id % cpr) * kChainCols;   // first flattened column
+  const int cpr = H * P / kChainCols;           // work-groups per batch row and segment
+  const int c0 = (id % cpr) * kChainCols;       // first flattened column
+  const int seg = (id / cpr) % nseg, b = id / cpr / nseg;
   const int h0 = c0 / P;                        // first head
   const int g = h0 / (H / G);                   // the B group (both heads share it)
   const int l32 = lane & 31, g2 = lane >> 5;
-  const int nsl = nc * SPC;                     // slices of the row
-  // the walk's step k visits slice ks(k) and its chunk wc = k / SPC is
-  // chunk rc(wc) of the row (reversed in the reverse pass)
-  auto ks = [&](int k) { return REV ? nsl - 1 - k : k; };
-  auto rc = [&](int wc) { return REV ? nc - 1 - wc : wc; };
+  const int cbeg = seg * seglen;                // first chunk of the walk
+  const int ncw = min(nc, cbeg + seglen) - cbeg;   // chunks of the walk
+  const int nsl = ncw * SPC;                    // slices of the walk
+  // the walk's step k visits slice ks(k) of the row and its chunk wc = k / SPC
+  // is chunk rc(wc) of the row (reversed in the reverse pass)
+  auto ks = [&](int k) { return REV ? (cbeg + ncw) * SPC - 1 - k : cbeg * SPC + k; };
+  auto rc = [&](int wc) { return REV ? cbeg + ncw - 1 - wc : cbeg + wc; };
   const size_t hstate = size_t(P) * N;          // elements of one (b, h) state
   // column block j (32 columns): head h0 + (NHW == 2 ? j : 0), columns from pcol(j) of that head
   auto pcol = [&](int j) { return (c0 + 32 * j) % P; };
@@ -422,22 +450,41 @@ void chunk_state_chain_kernel(
 #pragma unroll
     for (int q = 0; q < NHW; ++q) Ah[q] = A[h0 + q];
     // dt of tokens 4 lane .. 4 lane + 3 of chunk c, head h0 + q (rows clamped
-    // into the row; the tables zero those past its end), each as an aligned
+    // into the row; the tables zero those past its end), each as the aligned
     // 32-bit word of the tensor that holds it (dt is 16-byte aligned, so the
-    // word of element e starts at e & ~1, except for the tensor's last
-    // element at an even index, read through the word before it) and, in bit
-    // i of hi, whether it is that word's upper half. 32-bit loads need no
-    // widening, which would wait for them at once.
-    const long last = long(nchain / (H * P / kChainCols)) * T * H - 1;   // the tensor's last element
+    // word of element e starts at e & ~1) and, in bit i of hi, whether it is
+    // that word's upper half. 32-bit loads need no widening, which would wait
+    // for them at once. The one exception is the tensor's last element when
+    // its index is even: its word would end past the tensor, so it is read
+    // alone (16 bits, in the low half). Only the chunk that holds the
+    // tensor's last token row, in the work-group that holds its last head,
+    // can meet it; that case is a separate, uniform branch, so every other
+    // chunk's loads are whole aligned words.
+    const long last_e = long(nb) * T * H - 1;   // the tensor's last element
     auto dt_load = [&](int wc, uint32_t (&v)[NHW][4], uint32_t (&hi)[NHW]) {
       const ChunkRows cr = chunk_rows(nullptr, b, rc(wc), T, Q);
+      const bool tail = (last_e & 1) == 0 && cr.r0 + cr.n == long(nb) * T && h0 + NHW == H;
+      if (tail) {
+#pragma unroll
+        for (int q = 0; q < NHW; ++q) {
+          hi[q] = 0u;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const long e = (cr.r0 + min(4 * lane + i, cr.n - 1)) * H + h0 + q;
+            const uint32_t up = uint32_t(e & 1);
+            v[q][i] = e == last_e ? uint32_t(dt[e]) : *reinterpret_cast<const uint32_t*>(dt + (e - up));
+            hi[q] |= up << i;
+          }
+        }
+        return;
+      }
 #pragma unroll
       for (int q = 0; q < NHW; ++q) {
         hi[q] = 0u;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const long e = (cr.r0 + min(4 * lane + i, cr.n - 1)) * H + h0 + q;
-          const uint32_t up = (e & 1) || e == last ? 1u : 0u;
+          const uint32_t up = uint32_t(e & 1);
           v[q][i] = *reinterpret_cast<const uint32_t*>(dt + (e - up));
           hi[q] |= up << i;
         }
@@ -447,7 +494,7 @@ void chunk_state_chain_kernel(
     // lane and one wave scan of the lane totals) into slot c & 1; Acs and dt
     // of this lane's tokens into acs / v for the rows written after the next
     // dt loads
-    auto tables = [&](int wc, int q, const uint32_t (&raw)[4], uint32_t hi, float (&acs)[4], float (&v)[4]) {
+    auto tables = [&](int wc, int q, const uint32_t (&raw)[4], uint32_t hi, float (&acs)[4], float (&v)[4]) -> float {
       const ChunkRows cr = chunk_rows(nullptr, b, rc(wc), T, Q);
       float tot = 0.f;
 #pragma unroll
@@ -470,6 +517,7 @@ void chunk_state_chain_kernel(
           sw[q][wc & 1][4 * lane + i] =
               REV ? (4 * lane + i < cr.n ? exp_fast(acs[i]) : 0.f) : exp_fast(last - acs[i]) * v[i];
       if (lane == 0) sdecay[q][wc & 1] = expf(last);
+      return last;
     };
     // the Acs / dt rows of chunk c, head h0 + q (by the work-group holding
     // the head's first columns)
@@ -493,15 +541,26 @@ void chunk_state_chain_kernel(
       for (int i = 0; i < 4; ++i) dnext[q][i] = 0u;
     }
     float tacs[NHW][4], tdt[NHW][4];
+    // segmented walks: the summed decay exponents of the segment's chunks
+    // before chunk c (cdec), and of all its chunks (segdec), per head, by the
+    // work-group that holds the head's first columns
+    float run[NHW];
+#pragma unroll
+    for (int q = 0; q < NHW; ++q) run[q] = 0.f;
     // chunk c's tables, then chunk c + 1's dt, then chunk c's rows (stores
     // after the loads)
     auto chunk = [&](int wc) {
+      float lastq[NHW];
 #pragma unroll
-      for (int q = 0; q < NHW; ++q) tables(wc, q, dnext[q], dhi[q], tacs[q], tdt[q]);
-      if (wc + 1 < nc) dt_load(wc + 1, dnext, dhi);
+      for (int q = 0; q < NHW; ++q) lastq[q] = tables(wc, q, dnext[q], dhi[q], tacs[q], tdt[q]);
+      if (wc + 1 < ncw) dt_load(wc + 1, dnext, dhi);
       if constexpr (!REV) {
 #pragma unroll
-        for (int q = 0; q < NHW; ++q) rows_out(rc(wc), q, tacs[q], tdt[q]);
+        for (int q = 0; q < NHW; ++q) {
+          rows_out(rc(wc), q, tacs[q], tdt[q]);
+          if (cdec && pcol(q) == 0 && lane == 0) cdec[(size_t(b) * H + h0 + q) * nc + rc(wc)] = run[q];
+          run[q] += lastq[q];
+        }
       }
     };
     dt_load(0, dnext, dhi);
@@ -514,8 +573,13 @@ void chunk_state_chain_kernel(
         // at chunk c's start, chunk c + 1's tables (slot (c + 1) & 1 last
         // served chunk c - 1, whose slices are consumed by now; the compute
         // waves read it one barrier later at the earliest)
-        if (k < nsl && k % SPC == 0 && k / SPC + 1 < nc) chunk(k / SPC + 1);
+        if (k < nsl && k % SPC == 0 && k / SPC + 1 < ncw) chunk(k / SPC + 1);
       }
+    }
+    if (segdec) {
+#pragma unroll
+      for (int q = 0; q < NHW; ++q)
+        if (pcol(q) == 0 && lane == 0) segdec[(size_t(b) * H + h0 + q) * nseg + seg] = run[q];
     }
     return;
   }
@@ -616,7 +680,7 @@ void chunk_state_chain_kernel(
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int n = 32 * ntile(u) + 8 * (r / 4) + 4 * g2 + r % 4;
-      acc[u][r] = init ? init[(bhj * N + n) * P + pj + l32] : 0.f;
+      acc[u][r] = init && seg == 0 ? init[(bhj * N + n) * P + pj + l32] : 0.f;
     }
   }
   // chunk c's start: H_c out as bf16 ([p][n] rows, four consecutive n of
@@ -673,7 +737,7 @@ void chunk_state_chain_kernel(
       for (int r = 0; r < 16; ++r) acc[u][r] *= decay;
     // the next chunk's H (after this chunk's stores: a later wait for the
     // loads then finds only older stores)
-    if (REV && wc + 1 < nc) h_load(rc(wc + 1));
+    if (REV && wc + 1 < ncw) h_load(rc(wc + 1));
   };
   // slice k from slot s, all four k steps
   auto compute = [&](int k, int s) {
@@ -716,7 +780,16 @@ void chunk_state_chain_kernel(
       compute(k, d);
     }
   }
-  if (fin) {
+  if (fin && nseg > 1) {
+    // a segment's last local state, [b, nseg, H, P, N] (runs of four n)
+    float* dst = fin + ((size_t(b) * nseg + seg) * H + hj) * hstate + size_t(pj + l32) * N;
+#pragma unroll
+    for (int u = 0; u < TPW; ++u)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+        *reinterpret_cast<f32x4*>(dst + 32 * ntile(u) + 8 * jj + 4 * g2) =
+            f32x4{acc[u][4 * jj], acc[u][4 * jj + 1], acc[u][4 * jj + 2], acc[u][4 * jj + 3]};
+  } else if (fin) {
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
 #pragma unroll
@@ -729,18 +802,20 @@ void chunk_state_chain_kernel(
 }
 
 template <int N, int P, int SPC, int ST, bool F32S, bool REV>
-hipError_t launch_chain_np(const FwdShape& s, const void* x, const void* B, const void* C, const void* dt,
-                           const float* A, float* Acs, float* dtq, void* Hs, const float* init, float* fin,
-                           uint16_t* CB, uint16_t* CBt, const float* Hst, float* ghp, hipStream_t st,
-                           const StageEv& ev) {
+hipError_t launch_chain_np(const FwdShape& s, const ChainPlan& pl, const void* x, const void* B, const void* C,
+                           const void* dt, const float* A, float* Acs, float* dtq, void* Hs, const float* init,
+                           float* fin, uint16_t* CB, uint16_t* CBt, const float* Hst, float* ghp, float* cdec,
+                           float* segdec, hipStream_t st, const StageEv& ev) {
   const int lpc = s.Q / 32;
   const long ntiles = REV ? 0 : long(s.b) * s.nc * s.G * (lpc * (lpc + 1) / 2);
-  const long nchain = long(s.b) * s.H * P / kChainCols;
+  const long nchain = long(s.b) * s.H * P / kChainCols * pl.nseg;
   const long blocks = nchain + (ntiles + kChainWaves - 1) / kChainWaves;
+  const bool segd = pl.nseg > 1;
   hipExtLaunchKernelGGL((chunk_state_chain_kernel<N, P, SPC, ST, F32S, REV>), dim3(unsigned(blocks)),
                         dim3(kChainThreads), 0, st, ev.start, ev.stop, 0, static_cast<const uint16_t*>(x),
                         static_cast<const uint16_t*>(B), static_cast<const uint16_t*>(dt), A, Acs, dtq, Hs, init, fin,
-                        static_cast<const uint16_t*>(C), CB, CBt, Hst, ghp, s.T, s.H, s.G, s.Q, s.nc, int(nchain),
+                        static_cast<const uint16_t*>(C), CB, CBt, Hst, ghp, segd ? cdec : nullptr,
+                        segd ? segdec : nullptr, s.T, s.H, s.G, s.Q, s.nc, s.b, pl.nseg, pl.seglen, int(nchain),
                         ntiles);
   return hipGetLastError();
 }
@@ -801,68 +876,110 @@ struct ChainNP {
   static constexpr int n = N_, p = P_;
 };
 
-// The fused launch pays off when its work-groups (one per batch row and 64
-// columns) fill the chip in one round: each is a serial walk over its row's
-// slices, so fewer than half the compute units leave too many idle, and more
-// than fit at once (one per unit with five slices resident; at dstate 128
-// two per unit with three) run in two rounds of the whole walk; such shapes
-// take the two-kernel path. Headdim 32 pairs two heads, which must share a
-// B/C group.
-static int chain_units() {
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-    return 0;
+// Compute units of the current device, read once per device.
+int device_units() {
+  static std::atomic<int> cache[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < kMaxDevices) {
+    const int v = cache[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) return 0;
+  if (dev < kMaxDevices) cache[dev].store(cus, std::memory_order_relaxed);
   return cus;
 }
 
-bool chunk_state_chain_ok(const FwdShape& s) {
-  if (!((s.N == 128 || s.N == 256) && (s.P == 32 || s.P == 64 || s.P == 128) && s.Q % kChainSK == 0)) return false;
-  if (s.P == 32 && (s.H / s.G) % 2 != 0) return false;
-  const int cus = chain_units();
-  if (cus <= 0) return false;
+// The fused launch pays off when its work-groups (one per batch row, 64
+// columns and segment) fill the chip in one round: each is a serial walk
+// over its slices, so fewer than half the compute units leave too many
+// idle, and more than fit at once (one per unit with five slices resident;
+// at dstate 128 two per unit with three) run in two rounds of the whole
+// walk; such shapes take the two-kernel path. Headdim 32 pairs two heads,
+// which must share a B/C group. Where whole rows give fewer walks than half
+// the units (few, long rows), the forward cuts each row into segments of
+// equal chunk counts (the last may be shorter), as many as one walk per unit
+// allows and at most one per chunk; if that still leaves more than half the
+// units idle, the two-kernel path runs.
+ChainPlan chunk_state_chain_plan_for(const FwdShape& s, int cus, bool allow_segments) {
+  ChainPlan pl;
+  if (!((s.N == 128 || s.N == 256) && (s.P == 32 || s.P == 64 || s.P == 128) && s.Q % kChainSK == 0)) return pl;
+  if (s.P == 32 && (s.H / s.G) % 2 != 0) return pl;
+  if (cus <= 0 || s.nc < 1) return pl;
   const long wgs = long(s.b) * s.H * s.P / kChainCols;
   // two per unit: dstate 128 with a chunk start at most every other slice
   // (the registers of a chunk start every slice do not fit that occupancy)
   const long per_unit = s.N == 128 && s.Q >= 2 * kChainSK ? 2 : 1;
-  return 2 * wgs >= cus && wgs <= per_unit * cus;
+  if (wgs > per_unit * cus) return pl;
+  if (2 * wgs >= cus) {
+    pl.ok = true;
+    pl.nseg = 1;
+    pl.seglen = s.nc;                      // one segment: the whole row
+    pl.two = wgs > cus;
+    return pl;
+  }
+  if (!allow_segments) return pl;
+  // segments: one walk per unit
+  const int want = int(std::min<long>(s.nc, cus / wgs));
+  const int seglen = (s.nc + want - 1) / want;
+  const int nseg = (s.nc + seglen - 1) / seglen;
+  if (2 * wgs * nseg < cus) return pl;   // too little work to fill half the chip
+  pl.ok = true;
+  pl.nseg = nseg;
+  pl.seglen = seglen;
+  return pl;
 }
 
+ChainPlan chunk_state_chain_plan(const FwdShape& s, bool allow_segments) {
+  return chunk_state_chain_plan_for(s, device_units(), allow_segments);
+}
+
+bool chain_plan_valid(const FwdShape& s, const ChainPlan& pl) {
+  return pl.ok && pl.nseg >= 1 && pl.seglen >= 1 && long(pl.nseg - 1) * pl.seglen < s.nc &&
+         long(pl.nseg) * pl.seglen >= s.nc;
+}
+
+bool chunk_state_chain_ok(const FwdShape& s) { return chunk_state_chain_plan(s, false).ok; }
+
 template <bool F32S, bool REV>
-hipError_t launch_chain(const FwdShape& s, const void* x, const void* B, const void* C, const void* dt,
-                        const float* A, float* Acs, float* dtq, void* Hs, const float* init, float* fin,
-                        uint16_t* CB, uint16_t* CBt, const float* Hst, float* ghp, hipStream_t st,
-                        const StageEv& ev) {
-  if (!chunk_state_chain_ok(s)) return hipErrorInvalidValue;
+hipError_t launch_chain(const FwdShape& s, const ChainPlan& pl, const void* x, const void* B, const void* C,
+                        const void* dt, const float* A, float* Acs, float* dtq, void* Hs, const float* init,
+                        float* fin, uint16_t* CB, uint16_t* CBt, const float* Hst, float* ghp, float* cdec,
+                        float* segdec, hipStream_t st, const StageEv& ev) {
+  // every walk must own at least one chunk and the segments must cover the
+  // row exactly: a walk without slices would clamp its copies to slice -1
+  if (!chain_plan_valid(s, pl) || ((F32S || REV) && pl.nseg != 1)) return hipErrorInvalidValue;
   // two work-groups per unit (three slices resident; chunks of two or four
-  // slices, which the check above ensures) where one per unit would not
-  // hold them all
-  const bool two = long(s.b) * s.H * s.P / kChainCols > chain_units();
+  // slices, which the plan ensures) where one per unit would not hold them all
   auto by_q = [&](auto np) -> hipError_t {
     using NP = decltype(np);
     constexpr int S1 = NP::n == 128 ? 5 : 3;
-    if (two && NP::n == 128) {
+    if (pl.two && NP::n == 128) {
       if constexpr (REV) {
         return hipErrorInvalidValue;            // one per unit only (registers)
       } else {
         switch (s.Q / kChainSK) {
           case 2:
-            return launch_chain_np<NP::n, NP::p, 2, 3, F32S, REV>(s, x, B, C, dt, A, Acs, dtq, Hs, init, fin, CB, CBt,
-                                                                  Hst, ghp, st, ev);
+            return launch_chain_np<NP::n, NP::p, 2, 3, F32S, REV>(s, pl, x, B, C, dt, A, Acs, dtq, Hs, init, fin, CB,
+                                                                  CBt, Hst, ghp, cdec, segdec, st, ev);
           case 4:
-            return launch_chain_np<NP::n, NP::p, 4, 3, F32S, REV>(s, x, B, C, dt, A, Acs, dtq, Hs, init, fin, CB, CBt,
-                                                                  Hst, ghp, st, ev);
+            return launch_chain_np<NP::n, NP::p, 4, 3, F32S, REV>(s, pl, x, B, C, dt, A, Acs, dtq, Hs, init, fin, CB,
+                                                                  CBt, Hst, ghp, cdec, segdec, st, ev);
         }
         return hipErrorInvalidValue;
       }
     }
     switch (s.Q / kChainSK) {
       case 1:
-        return launch_chain_np<NP::n, NP::p, 1, S1, F32S, REV>(s, x, B, C, dt, A, Acs, dtq, Hs, init, fin, CB, CBt, Hst, ghp, st, ev);
+        return launch_chain_np<NP::n, NP::p, 1, S1, F32S, REV>(s, pl, x, B, C, dt, A, Acs, dtq, Hs, init, fin, CB,
+                                                               CBt, Hst, ghp, cdec, segdec, st, ev);
       case 2:
-        return launch_chain_np<NP::n, NP::p, 2, S1, F32S, REV>(s, x, B, C, dt, A, Acs, dtq, Hs, init, fin, CB, CBt, Hst, ghp, st, ev);
+        return launch_chain_np<NP::n, NP::p, 2, S1, F32S, REV>(s, pl, x, B, C, dt, A, Acs, dtq, Hs, init, fin, CB,
+                                                               CBt, Hst, ghp, cdec, segdec, st, ev);
       case 4:
-        return launch_chain_np<NP::n, NP::p, 4, S1, F32S, REV>(s, x, B, C, dt, A, Acs, dtq, Hs, init, fin, CB, CBt, Hst, ghp, st, ev);
+        return launch_chain_np<NP::n, NP::p, 4, S1, F32S, REV>(s, pl, x, B, C, dt, A, Acs, dtq, Hs, init, fin, CB,
+                                                               CBt, Hst, ghp, cdec, segdec, st, ev);
     }
     return hipErrorInvalidValue;
   };
@@ -876,34 +993,35 @@ hipError_t launch_chain(const FwdShape& s, const void* x, const void* B, const v
   return by_q(ChainNP<256, 128>{});
 }
 
-hipError_t launch_chunk_state_chain(const FwdShape& s, const void* x, const void* B, const void* C,
-                                    const void* dt, const float* A, float* Acs, float* dtq, uint16_t* Hb,
-                                    const float* init, float* fin, uint16_t* CB, hipStream_t st,
-                                    const StageEv& ev) {
-  return launch_chain<false, false>(s, x, B, C, dt, A, Acs, dtq, Hb, init, fin, CB, nullptr, nullptr, nullptr, st,
-                                    ev);
+hipError_t launch_chunk_state_chain(const FwdShape& s, const ChainPlan& pl, const void* x, const void* B,
+                                    const void* C, const void* dt, const float* A, float* Acs, float* dtq,
+                                    uint16_t* Hb, const float* init, float* fin, uint16_t* CB, float* cdec,
+                                    float* segdec, hipStream_t st, const StageEv& ev) {
+  return launch_chain<false, false>(s, pl, x, B, C, dt, A, Acs, dtq, Hb, init, fin, CB, nullptr, nullptr, nullptr,
+                                    cdec, segdec, st, ev);
 }
 
 hipError_t launch_chunk_state_chain_bwd(const FwdShape& s, const void* x, const void* B, const void* C,
                                         const void* dt, const float* A, float* Acs, float* dtq, float* Hst,
                                         const float* init, float* fin, uint16_t* CBf, uint16_t* CBt,
                                         hipStream_t st) {
-  return launch_chain<true, false>(s, x, B, C, dt, A, Acs, dtq, Hst, init, fin, CBf, CBt, nullptr, nullptr, st,
-                                   StageEv{});
+  return launch_chain<true, false>(s, chunk_state_chain_plan(s, false), x, B, C, dt, A, Acs, dtq, Hst, init, fin,
+                                   CBf, CBt, nullptr, nullptr, nullptr, nullptr, st, StageEv{});
 }
 
 // The reverse walk holds a run of H_c per lane besides the accumulators, which
 // the two-per-unit occupancy leaves no room for: one work-group per unit.
 bool chunk_grad_chain_ok(const FwdShape& s) {
-  return chunk_state_chain_ok(s) && long(s.b) * s.H * s.P / kChainCols <= chain_units();
+  const ChainPlan pl = chunk_state_chain_plan(s, false);
+  return pl.ok && !pl.two;
 }
 
 hipError_t launch_chunk_grad_chain_bwd(const FwdShape& s, const void* dy, const void* C, const void* dt,
                                        const float* A, const float* dfinal, uint16_t* Gb, float* dinit,
                                        const float* Hst, float* ghp, hipStream_t st) {
   if (!chunk_grad_chain_ok(s)) return hipErrorInvalidValue;
-  return launch_chain<false, true>(s, dy, C, nullptr, dt, A, nullptr, nullptr, Gb, dfinal, dinit, nullptr, nullptr,
-                                   Hst, ghp, st, StageEv{});
+  return launch_chain<false, true>(s, chunk_state_chain_plan(s, false), dy, C, nullptr, dt, A, nullptr, nullptr, Gb,
+                                   dfinal, dinit, nullptr, nullptr, Hst, ghp, nullptr, nullptr, st, StageEv{});
 }
 
 hipError_t launch_chunk_state_mfma_bwd(const FwdShape& s, const void* x, const void* B, const void* C,

@@ -79,10 +79,17 @@ bool grids_fit(const FwdShape& s, bool mfma) {
   return worst < lim;
 }
 
+// The forward's plan for the states entering each chunk (bf16 matrix-core
+// path only; segments allowed)
+ChainPlan fwd_plan(const FwdShape& s, bool mfma) {
+  return mfma ? chunk_state_chain_plan(s, true) : ChainPlan{};
+}
+
 // Backward workspace (byte offsets, 256-byte aligned), chunk length
 // bwd_chunk_len(P, N):
 //   acs, dtq [b,H,nc,Q] f32; st [b,nc,H,P,N] f32 (chunk states, then the states
-//   entering each chunk); ds [b,nc,H,P,N] f32; gb [b,nc,H,P,N] bf16;
+//   entering each chunk); ds [b,nc,H,P,N] f32 (absent where the reverse walk
+//   forms the state gradients: it never stores them); gb [b,nc,H,P,N] bf16;
 //   cb, cbt [b,nc,G,ntile,64,16] f32 (C B^T tiles, both orientations);
 //   fin [b,H,N,P] f32; ghp [b,H,nc,nghp] f32;
 //   dbs, dcs [nslice,b,T,G,N] f32 (only with nslice > 1); dap, ddp [b,H,nc] f32;
@@ -91,7 +98,7 @@ struct BwdLayout {
   size_t acs, dtq, st, ds, gb, cb, cbt, fin, ghp, dbs, dcs, dap, ddp, tok, total;
 };
 
-BwdLayout bwd_layout(const FwdShape& s, int nghp, int nslice) {
+BwdLayout bwd_layout(const FwdShape& s, int nghp, int nslice, bool rev_walk) {
   BwdLayout w;
   const size_t row = size_t(s.b) * s.H * s.nc * s.Q * sizeof(float);
   const size_t nst = size_t(s.b) * s.nc * s.H * s.N * s.P;
@@ -102,7 +109,7 @@ BwdLayout bwd_layout(const FwdShape& s, int nghp, int nslice) {
   w.acs = take(row);
   w.dtq = take(row);
   w.st = take(nst * sizeof(float));
-  w.ds = take(nst * sizeof(float));
+  w.ds = take(rev_walk ? 0 : nst * sizeof(float));
   w.gb = take(nst * sizeof(uint16_t));
   w.cb = take(size_t(s.b) * s.nc * s.G * ntile * 1024 * sizeof(float));
   w.cbt = take(size_t(s.b) * s.nc * s.G * ntile * 1024 * sizeof(float));
@@ -156,8 +163,9 @@ size_t ssd_chunk_scan_fwd_workspace(int batch, int seqlen, int nheads, int headd
   if (!dtype_ok(dtype) || !is_chunk_ok(chunk_len)) return 0;
   if (check_dims(batch, seqlen, nheads, headdim, dstate, ngroups) != SSD_OK) return 0;
   const FwdShape s = make_shape(batch, seqlen, nheads, headdim, dstate, ngroups, chunk_len);
-  if (s.nc > 65535 || !grids_fit(s, use_mfma_path(s, dtype))) return 0;
-  return ws_layout(s, use_mfma_path(s, dtype)).total;
+  const bool mfma = use_mfma_path(s, dtype);
+  if (s.nc > 65535 || !grids_fit(s, mfma)) return 0;
+  return ws_layout(s, mfma, fwd_plan(s, mfma)).total;
 }
 
 int ssd_chunk_scan_fwd_fused_states(int batch, int seqlen, int nheads, int headdim, int dstate,
@@ -166,7 +174,21 @@ int ssd_chunk_scan_fwd_fused_states(int batch, int seqlen, int nheads, int headd
   if (check_dims(batch, seqlen, nheads, headdim, dstate, ngroups) != SSD_OK) return 0;
   const FwdShape s = make_shape(batch, seqlen, nheads, headdim, dstate, ngroups, chunk_len);
   if (s.nc > 65535 || !use_mfma_path(s, dtype) || !grids_fit(s, true)) return 0;
-  return chunk_state_chain_ok(s) ? 1 : 0;
+  const ChainPlan pl = fwd_plan(s, true);
+  return pl.ok ? pl.nseg : 0;
+}
+
+int ssd_chunk_scan_fwd_plan(int batch, int seqlen, int nheads, int headdim, int dstate, int ngroups,
+                            int chunk_len, ssd_dtype dtype, int compute_units, int* seglen) {
+  if (seglen) *seglen = 0;
+  if (!dtype_ok(dtype) || !is_chunk_ok(chunk_len)) return 0;
+  if (check_dims(batch, seqlen, nheads, headdim, dstate, ngroups) != SSD_OK) return 0;
+  const FwdShape s = make_shape(batch, seqlen, nheads, headdim, dstate, ngroups, chunk_len);
+  if (s.nc > 65535 || !use_mfma_path(s, dtype) || !grids_fit(s, true)) return 0;
+  const ChainPlan pl = chunk_state_chain_plan_for(s, compute_units, true);
+  if (!pl.ok) return 0;
+  if (seglen) *seglen = pl.seglen;
+  return pl.nseg;
 }
 
 ssd_status ssd_chunk_scan_fwd_timed(const void* x, const void* dt, const float* A, const void* B,
@@ -190,7 +212,8 @@ ssd_status ssd_chunk_scan_fwd_timed(const void* x, const void* dt, const float* 
   if (s.nc > 65535) return SSD_ERR_SHAPE;
   const bool mfma = use_mfma_path(s, dtype);
   if (!grids_fit(s, mfma)) return SSD_ERR_SHAPE;
-  const WsLayout w = ws_layout(s, mfma);
+  const ChainPlan pl = fwd_plan(s, mfma);
+  const WsLayout w = ws_layout(s, mfma, pl);
   if (workspace_bytes < w.total) return SSD_ERR_WORKSPACE;
 
   const size_t e = esize(dtype);
@@ -221,6 +244,8 @@ ssd_status ssd_chunk_scan_fwd_timed(const void* x, const void* dt, const float* 
   float* S = reinterpret_cast<float*>(ws + w.st);
   uint16_t* Hb = mfma ? reinterpret_cast<uint16_t*>(ws + w.hb) : nullptr;
   uint16_t* CB = mfma ? reinterpret_cast<uint16_t*>(ws + w.cb) : nullptr;
+  float* cdec = reinterpret_cast<float*>(ws + w.cdec);
+  float* segdec = reinterpret_cast<float*>(ws + w.segdec);
 
   // stage i's events: stage_events[2 i] (start), stage_events[2 i + 1] (stop),
   // recorded by the kernel's own dispatch
@@ -243,10 +268,33 @@ ssd_status ssd_chunk_scan_fwd_timed(const void* x, const void* dt, const float* 
   } else if (launch_chunk_cumsum(s, dtype, dt, A, Acs, dtq, hs, ev(0)) != hipSuccess) {
     return SSD_ERR_HIP;
   }
-  if (mfma && chunk_state_chain_ok(s)) {
+  if (pl.ok) {
+    if (pl.nseg > 1) {
+      // segmented walks (each segment's last local state into S), then the
+      // recurrence over the segments: S[k] becomes the state entering segment
+      // k, with segment k's summed decay exponent as its "chunk" decay (a
+      // chunk length of 1 over segdec), from zero (segment 0 started from
+      // init_state itself)
+      if (launch_chunk_state_chain(s, pl, x, B, C, dt, A, Acs, dtq, Hb, init_state, S, CB, cdec, segdec, hs,
+                                   ev(1)) != hipSuccess)
+        return SSD_ERR_HIP;
+      FwdShape ss = s;
+      ss.nc = pl.nseg;
+      ss.Q = 1;
+      if (launch_state_passing(ss, S, nullptr, segdec, nullptr, final_state, hs, ev(2)) != hipSuccess)
+        return SSD_ERR_HIP;
+      SegStates sg;
+      sg.Hin = S;
+      sg.cdec = cdec;
+      sg.nseg = pl.nseg;
+      sg.seglen = pl.seglen;
+      if (launch_chunk_scan_mfma(s, x, CB, C, Acs, dtq, Hb, D, y, nullptr, hs, ev(3), sg) != hipSuccess)
+        return SSD_ERR_HIP;
+      return SSD_OK;
+    }
     // chunk states and state passing in one launch: stage 2 launches nothing
-    if (launch_chunk_state_chain(s, x, B, C, dt, A, Acs, dtq, Hb, init_state, final_state, CB, hs, ev(1)) !=
-        hipSuccess)
+    if (launch_chunk_state_chain(s, pl, x, B, C, dt, A, Acs, dtq, Hb, init_state, final_state, CB, nullptr,
+                                 nullptr, hs, ev(1)) != hipSuccess)
       return SSD_ERR_HIP;
     const StageEv e2 = ev(2);
     if (e2.start && hipEventRecord(e2.start, hs) != hipSuccess) return SSD_ERR_HIP;
@@ -328,7 +376,7 @@ size_t ssd_chunk_scan_fwd_varlen_workspace(int total_tokens, int nseq, int nhead
   if (check_dims(1, total_tokens, nheads, headdim, dstate, ngroups) != SSD_OK) return 0;
   const FwdShape s = varlen_shape(total_tokens, nseq, nheads, headdim, dstate, ngroups, chunk_len);
   if (!use_mfma_path(s, dtype) || !varlen_grids_fit(s, nseq)) return 0;
-  const WsLayout w = ws_layout(s, true);
+  const WsLayout w = ws_layout(s, true, ChainPlan{});
   return varlen_table_offset(w) + size_t(s.nc) * sizeof(int4);
 }
 
@@ -351,7 +399,7 @@ ssd_status ssd_chunk_scan_fwd_varlen(const void* x, const void* dt, const float*
   if (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) return SSD_ERR_ALIGN;
   const FwdShape s = varlen_shape(total_tokens, nseq, nheads, headdim, dstate, ngroups, chunk_len);
   if (!use_mfma_path(s, dtype) || !varlen_grids_fit(s, nseq)) return SSD_ERR_SHAPE;
-  const WsLayout w = ws_layout(s, true);
+  const WsLayout w = ws_layout(s, true, ChainPlan{});
   const size_t tab_off = varlen_table_offset(w);
   if (workspace_bytes < tab_off + size_t(s.nc) * sizeof(int4)) return SSD_ERR_WORKSPACE;
 
@@ -485,7 +533,15 @@ size_t ssd_chunk_scan_bwd_workspace(int batch, int seqlen, int nheads, int headd
   if (!dtype_ok(dtype) || check_dims(batch, seqlen, nheads, headdim, dstate, ngroups) != SSD_OK) return 0;
   FwdShape s;
   if (!bwd_supported(batch, seqlen, nheads, headdim, dstate, ngroups, dtype, s)) return 0;
-  return bwd_layout(s, state_passing_bwd_partials(s), bwd_slices(s)).total;
+  return bwd_layout(s, state_passing_bwd_partials(s), bwd_slices(s), chunk_grad_chain_ok(s)).total;
+}
+
+int ssd_chunk_scan_bwd_fused_walks(int batch, int seqlen, int nheads, int headdim, int dstate, int ngroups,
+                                   ssd_dtype dtype) {
+  if (!dtype_ok(dtype) || check_dims(batch, seqlen, nheads, headdim, dstate, ngroups) != SSD_OK) return 0;
+  FwdShape s;
+  if (!bwd_supported(batch, seqlen, nheads, headdim, dstate, ngroups, dtype, s)) return 0;
+  return (chunk_state_chain_ok(s) ? 1 : 0) | (chunk_grad_chain_ok(s) ? 2 : 0);
 }
 
 ssd_status ssd_chunk_scan_bwd(const void* x, const void* dt, const float* A, const void* B, const void* C,
@@ -505,7 +561,8 @@ ssd_status ssd_chunk_scan_bwd(const void* x, const void* dt, const float* A, con
     if (misaligned(p)) return SSD_ERR_ALIGN;
   const int nghp = state_passing_bwd_partials(s);
   const int nslice = bwd_slices(s);
-  const BwdLayout w = bwd_layout(s, nghp, nslice);
+  const bool rev_walk = chunk_grad_chain_ok(s);
+  const BwdLayout w = bwd_layout(s, nghp, nslice, rev_walk);
   if (workspace_bytes < w.total) return SSD_ERR_WORKSPACE;
 
   const size_t e = esize(dtype);
@@ -557,7 +614,6 @@ ssd_status ssd_chunk_scan_bwd(const void* x, const void* dt, const float* A, con
   }
   // what each chunk's outputs give the state entering it, then the reverse
   // pass -- in one reverse walk where the fused walk applies
-  const bool rev_walk = chunk_grad_chain_ok(s);
   if (rev_walk) {
     if (launch_chunk_grad_chain_bwd(s, dy, C, dt, A, dfinal, Gb, dinit, Sst, ghp, hs) != hipSuccess)
       return SSD_ERR_HIP;

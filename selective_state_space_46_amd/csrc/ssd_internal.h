@@ -109,33 +109,67 @@ inline bool use_mfma_path(const FwdShape& s, ssd_dtype t) {
   return t == SSD_BF16 && n_ok && p_ok && s.Q >= 32;
 }
 
+// How the bf16 matrix-core forward computes the states entering each chunk
+// (chunk_state_mfma.hip): ok = the fused chunk-state + state-passing walk
+// (else a chunk_state and a state_passing launch); nseg segments of seglen
+// chunks per batch row (1: whole rows); two = two walks per compute unit.
+struct ChainPlan {
+  bool ok = false;
+  int nseg = 1, seglen = 0;
+  bool two = false;
+};
+// allow_segments = false: whole rows only (the backward's walks). The plan
+// for a device with `cus` compute units, and for the current device.
+ChainPlan chunk_state_chain_plan_for(const FwdShape& s, int cus, bool allow_segments);
+ChainPlan chunk_state_chain_plan(const FwdShape& s, bool allow_segments);
+// pl.ok and its segments cover the row's chunks exactly, each at least one
+bool chain_plan_valid(const FwdShape& s, const ChainPlan& pl);
+// compute units of the current device (read once per device; 0 without one)
+constexpr int kMaxDevices = 64;
+int device_units();
+
 // Workspace layout (byte offsets, each 256-byte aligned):
 //   acs [b, H, nc, Q] f32    cumulative dt*A inside each chunk (inclusive)
 //   dtq [b, H, nc, Q] f32    dt widened to fp32, 0 past the end of the sequence
 //   st  [b, nc, H, P, N] f32 chunk states, stored transposed (n fastest); on
 //                            the generic path overwritten in place by the
-//                            states entering each chunk
-//   hb  [b, nc, H, P, N] bf16 states entering each chunk (MFMA path only)
+//                            states entering each chunk. Absent on the fused
+//                            path, except with segments: [b, nseg, H, P, N],
+//                            each segment's last local state, then (in place)
+//                            the state entering each segment
+//   hb  [b, nc, H, P, N] bf16 states entering each chunk (MFMA path only;
+//                            with segments, the local ones)
 //   cb  [b, nc, G, ntile, 64, 16] bf16 C B^T tiles of each chunk (MFMA path
 //       only; ntile = lpc (lpc + 1) / 2 lower-triangle tiles, lpc = Q / 32)
+//   cdec [b, H, nc] f32, segdec [b, H, nseg] f32 (segments only): summed
+//       chunk decay exponents from the segment's start to each chunk, and over
+//       each segment
 struct WsLayout {
-  size_t acs, dtq, st, hb, cb, total;
+  size_t acs, dtq, st, hb, cb, cdec, segdec, total;
 };
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-inline WsLayout ws_layout(const FwdShape& s, bool mfma) {
+inline WsLayout ws_layout(const FwdShape& s, bool mfma, const ChainPlan& pl) {
   WsLayout w;
   const size_t row = size_t(s.b) * s.H * s.nc * s.Q * sizeof(float);
   const size_t nst = size_t(s.b) * s.nc * s.H * s.N * s.P;
+  const bool fused = mfma && pl.ok;
+  const size_t nstf = !fused ? nst : pl.nseg > 1 ? size_t(s.b) * pl.nseg * s.H * s.N * s.P : 0;
   w.acs = 0;
   w.dtq = align_up(w.acs + row, 256);
   w.st = align_up(w.dtq + row, 256);
-  w.hb = align_up(w.st + nst * sizeof(float), 256);
+  w.hb = align_up(w.st + nstf * sizeof(float), 256);
+  if (!mfma) {
+    w.cb = w.cdec = w.segdec = w.total = w.hb;
+    return w;
+  }
   w.cb = align_up(w.hb + nst * sizeof(uint16_t), 256);
   const size_t lpc = size_t(s.Q) / 32, ntile = lpc * (lpc + 1) / 2;
-  w.total = mfma ? align_up(w.cb + size_t(s.b) * s.nc * s.G * ntile * 1024 * sizeof(uint16_t), 256)
-                 : w.hb;
+  w.cdec = align_up(w.cb + size_t(s.b) * s.nc * s.G * ntile * 1024 * sizeof(uint16_t), 256);
+  const bool seg = fused && pl.nseg > 1;
+  w.segdec = align_up(w.cdec + (seg ? size_t(s.b) * s.H * s.nc * sizeof(float) : 0), 256);
+  w.total = align_up(w.segdec + (seg ? size_t(s.b) * s.H * pl.nseg * sizeof(float) : 0), 256);
   return w;
 }
 
@@ -179,14 +213,16 @@ hipError_t launch_chunk_state_mfma(const FwdShape& s, const void* x, const void*
 // Chunk states and state passing fused (equal-length rows, bf16 MFMA path):
 // writes Acs, dtq, the C B^T tiles and Hb (states entering each chunk, bf16)
 // and final (fp32, may be null), without the fp32 chunk states. Only for the
-// shapes chunk_state_chain_ok accepts (enough (batch row, 64-column) walks
-// to fill the chip in one round; dstate 128 or 256; chunk_len a multiple of
-// 64).
-bool chunk_state_chain_ok(const FwdShape& s);
-hipError_t launch_chunk_state_chain(const FwdShape& s, const void* x, const void* B, const void* C,
-                                    const void* dt, const float* A, float* Acs, float* dtq, uint16_t* Hb,
-                                    const float* init, float* fin, uint16_t* CB, hipStream_t st,
-                                    const StageEv& ev = StageEv{});
+// shapes chunk_state_chain_plan accepts (enough (batch row, 64-column,
+// segment) walks to fill the chip in one round; dstate 128 or 256;
+// chunk_len a multiple of 64). With segments (pl.nseg > 1), Hb holds the
+// local states, fin receives each segment's last local state
+// ([b, nseg, H, P, N] fp32) and cdec / segdec the summed decay exponents.
+bool chunk_state_chain_ok(const FwdShape& s);   // whole rows
+hipError_t launch_chunk_state_chain(const FwdShape& s, const ChainPlan& pl, const void* x, const void* B,
+                                    const void* C, const void* dt, const float* A, float* Acs, float* dtq,
+                                    uint16_t* Hb, const float* init, float* fin, uint16_t* CB, float* cdec,
+                                    float* segdec, hipStream_t st, const StageEv& ev = StageEv{});
 // The same for the backward's recomputation: the states entering each chunk
 // as fp32 in Hst ([b, c, h, p, n], what state_passing leaves over the chunk
 // states) and the C B^T tiles as fp32 in both orientations (CBf, CBt, as
@@ -224,10 +260,18 @@ hipError_t launch_chunk_scan(const FwdShape& s, ssd_dtype type, bool mfma, const
                              const void* B, const void* C, const float* Acs, const float* dtq,
                              const float* Hst, const uint16_t* Hb, const uint16_t* CB,
                              const float* D, void* y, hipStream_t st, const StageEv& ev = StageEv{});
+// Segmented states (ChainPlan::nseg > 1): the state entering chunk c of
+// segment k >= 1 is Hb_c + exp(cdec_c) Hin_k, Hin [b, nseg, H, P, N] fp32.
+struct SegStates {
+  const float* Hin = nullptr;
+  const float* cdec = nullptr;
+  int nseg = 1, seglen = 0;
+};
 hipError_t launch_chunk_scan_mfma(const FwdShape& s, const void* x, const uint16_t* CB,
                                   const void* C, const float* Acs, const float* dtq,
                                   const uint16_t* Hb, const float* D, void* y, const int4* tab,
-                                  hipStream_t st, const StageEv& ev = StageEv{});
+                                  hipStream_t st, const StageEv& ev = StageEv{},
+                                  const SegStates& seg = SegStates{});
 
 // Packed variable-length sequences (varlen.hip): the chunk table has
 // varlen_slots(T, nseq, Q) int4 entries.

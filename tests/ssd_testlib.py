@@ -60,6 +60,81 @@ def columns_of(y, fin, cols):
 rel_l2 = oracle.rel_l2
 
 
+def _np(a, sl=None):
+    """float64 numpy view of a numpy array or a device tensor (optionally a slice of it)."""
+    if sl is not None:
+        a = a[sl]
+    if isinstance(a, np.ndarray):
+        return a.astype(np.float64, copy=False)
+    return host(a)
+
+
+def fwd_errors(inp: dict, y, fin, Q: int, heads_per_block: int = 4) -> dict:
+    """Whole-tensor comparison of a forward result (y [b,T,H,P], fin [b,H,N,P]
+    or None; numpy arrays or device tensors) with the fp64 oracle on the same
+    inputs. Besides the global relative L2 of y and of the final state it
+    returns the worst relative L2 over every (batch row, head, chunk of Q
+    tokens) block of y and over every token row (all heads) of y, so that an
+    error confined to one chunk, one ragged tail or one token cannot hide in
+    the global norm. The oracle runs once on the whole problem; the
+    comparison walks head blocks to bound the host memory it takes."""
+    y_ref, fin_ref = oracle.ssd_fwd(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp.get("D"),
+                                    inp.get("init"), want_final=fin is not None)
+    b, T, H, P = inp["x"].shape
+    nc = -(-T // Q)
+    sd = sr = 0.0
+    row_d = np.zeros((b, T))
+    row_r = np.zeros((b, T))
+    worst_chunk = 0.0
+    for h0 in range(0, H, heads_per_block):
+        h1 = min(H, h0 + heads_per_block)
+        yg = _np(y, (slice(None), slice(None), slice(h0, h1)))
+        yr = y_ref[:, :, h0:h1]
+        d2 = (yg - yr) ** 2
+        r2 = yr * yr
+        sd += float(d2.sum())
+        sr += float(r2.sum())
+        row_d += d2.sum(axis=(2, 3))
+        row_r += r2.sum(axis=(2, 3))
+        pad = nc * Q - T
+        cd = np.pad(d2.sum(axis=3), ((0, 0), (0, pad), (0, 0))).reshape(b, nc, Q, h1 - h0).sum(axis=2)
+        cr = np.pad(r2.sum(axis=3), ((0, 0), (0, pad), (0, 0))).reshape(b, nc, Q, h1 - h0).sum(axis=2)
+        worst_chunk = max(worst_chunk, float(np.max(np.sqrt(cd / np.maximum(cr, 1e-300)))))
+        if not np.all(np.isfinite(yg)):
+            worst_chunk = float("inf")
+    out = {"y": float(np.sqrt(sd / sr)) if sr > 0 else float(np.sqrt(sd)),
+           "chunk": worst_chunk,
+           "row": float(np.max(np.sqrt(row_d / np.maximum(row_r, 1e-300)))),
+           "final": None}
+    if fin is not None:
+        out["final"] = rel_l2(_np(fin), fin_ref)
+    return out
+
+
+def assert_fwd_close(errs: dict, tol: float, label: str = ""):
+    print(f"[{label}] rel_l2 y={errs['y']:.3e} worst chunk={errs['chunk']:.3e} worst token row="
+          f"{errs['row']:.3e} final={errs['final'] if errs['final'] is None else format(errs['final'], '.3e')}",
+          flush=True)
+    assert errs["y"] <= tol, errs
+    assert errs["chunk"] <= tol, errs
+    assert errs["row"] <= tol, errs
+    if errs["final"] is not None:
+        assert errs["final"] <= tol, errs
+
+
+def fwd_dev(inp: dict, dtype: str, chunk_len: int):
+    """Run ssd_chunk_scan_fwd and keep (y, final) on the device (large shapes)."""
+    import torch
+    import selective_state_space_46_amd as ssd
+    x, dt, B, C = (dev(inp[k], dtype) for k in ("x", "dt", "B", "C"))
+    A, D = dev(inp["A"]), (dev(inp["D"]) if inp.get("D") is not None else None)
+    init = dev(inp["init"]) if inp.get("init") is not None else None
+    y, fin = ssd.ssd_chunk_scan_fwd(x, dt, A, B, C, D, init, chunk_len)
+    torch.cuda.synchronize()
+    del x, dt, B, C
+    return y, fin
+
+
 class HipEvents:
     """hipEvent_t handles through the HIP runtime's C API (for the timed entry
     point, which takes raw handles)."""

@@ -36,7 +36,8 @@ def test_header_declares_the_entry_points():
                                        "ssd_causal_conv1d_fwd", "ssd_causal_conv1d_update",
                                        "ssd_chunk_scan_fwd_varlen", "ssd_chunk_scan_fwd_varlen_workspace",
                                        "ssd_chunk_scan_bwd", "ssd_chunk_scan_bwd_workspace",
-                                       "ssd_chunk_scan_fwd_fused_states"}
+                                       "ssd_chunk_scan_fwd_fused_states", "ssd_chunk_scan_bwd_fused_walks",
+                                       "ssd_chunk_scan_fwd_plan"}
 
 
 def test_fused_states_query_rejects_what_the_forward_rejects():
@@ -70,7 +71,9 @@ def test_workspace_query():
     """Acs and dt rows (fp32), chunk states (fp32) and, on the bf16 matrix-core
     path (dstate in {32,64,128,256}, headdim in {32,64,128}, chunk >= 32), a bf16
     copy of the passed states and the bf16 C B^T tiles (2 KB per lower-triangle
-    32x32 tile per chunk and group); each region 256-byte aligned."""
+    32x32 tile per chunk and group); each region 256-byte aligned. Without a
+    GPU the library cannot choose the fused walk (it needs the device's
+    compute-unit count), so this is the two-launch layout."""
     def expect(b, T, H, P, N, Q, dtype):
         nc = -(-T // Q)
         up = lambda v: -(-v // 256) * 256
@@ -279,6 +282,10 @@ def test_bwd_workspace_and_errors(L):
     assert wsq(1, 300, 3, 64, 128, 2, ssd.SSD_BF16) == 0      # H % G
     # per-head dB / dC partials grow with the heads
     assert wsq(1, 300, 8, 64, 128, 1, ssd.SSD_BF16) > wsq(1, 300, 2, 64, 128, 1, ssd.SSD_BF16)
+    walks = ssd.ssd_chunk_scan_bwd_fused_walks
+    assert walks(1, 300, 2, 64, 128, 1, ssd.SSD_F32) == 0
+    assert walks(1, 300, 3, 64, 128, 2, ssd.SSD_BF16) == 0
+    assert walks(1, 300, 2, 128, 256, 1, ssd.SSD_BF16) == 0
     assert bw(L, dtype=3) == 3
     assert bw(L, dtype=0) == 2
     assert bw(L, P=128, N=256) == 2

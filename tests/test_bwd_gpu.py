@@ -101,14 +101,43 @@ def test_bwd_full_130m_layer():
     _check(inp)
 
 
+def _walks(b, T, H, P, N, G):
+    import selective_state_space_46_amd as ssd
+    return ssd.ssd_chunk_scan_bwd_fused_walks(b, T, H, P, N, G, ssd.SSD_BF16)
+
+
 @pytest.mark.parametrize("b,T,H,P,N,G", [(4, 300, 32, 64, 128, 2), (4, 330, 64, 32, 128, 4),
                                          (2, 200, 64, 128, 128, 2), (2, 260, 64, 64, 256, 4)])
 def test_bwd_reverse_walk_shapes(b, T, H, P, N, G):
-    """128..256 work-groups of 64 (head, p) columns: the gradients of the
-    chunk states come from the one reverse walk (several chunks, ragged
-    tail, head pairs at headdim 32, dstate 256)"""
+    """128..256 work-groups of 64 (head, p) columns: the recomputation is one
+    walk and the gradients of the chunk states come from the one reverse
+    walk (several chunks, ragged tail, head pairs at headdim 32, dstate 256)"""
+    assert _walks(b, T, H, P, N, G) == 3
     _check(_inputs(b, T, H, P, N, G, seed=7700 + P + N + H))
 
 
 def test_bwd_reverse_walk_without_optional_inputs():
+    assert _walks(4, 300, 32, 64, 128, 2) == 3
     _check(_inputs(4, 300, 32, 64, 128, 2, seed=7800, init=False, dfinal=False, D=False))
+
+
+def test_bwd_reverse_walk_odd_batch_tokens_heads():
+    """b, T, H all odd (135 walks): the dt tensor's last element at an even
+    index, read alone by both walks that reach it"""
+    assert _walks(3, 301, 45, 64, 128, 1) == 3
+    _check(_inputs(3, 301, 45, 64, 128, 1, seed=7850))
+
+
+def test_bwd_two_walks_per_unit():
+    """320 walks (the 2.7B layer's heads, batch 4): the recomputation runs two
+    walks per unit (three slices resident, fp32 states and tiles); the state
+    gradients take the per-chunk launch and the reverse state passing"""
+    assert _walks(4, 300, 80, 64, 128, 1) == 1
+    _check(_inputs(4, 300, 80, 64, 128, 1, seed=7900))
+
+
+def test_bwd_path_choice():
+    """the 130M layer's backward (chunk 128: 192 walks) takes both walks; a
+    small problem (8 walks) neither"""
+    assert _walks(8, 2048, 24, 64, 128, 1) == 3
+    assert _walks(1, 300, 8, 64, 128, 1) == 0

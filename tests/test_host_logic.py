@@ -1,0 +1,163 @@
+"""CPU checks of host-side index arithmetic that the GPU kernels rely on.
+
+The fused chunk-state walk reads dt (bf16, [b, T, H]) as aligned 32-bit words:
+element e lives in the word that starts at element e & ~1, and the tensor's
+last element, when its index is even, is read alone with a 16-bit load (its
+word would end past the tensor). These tests restate that addressing in
+numpy and check, over many shapes (odd and even b, T, H; one or two heads
+per walk; every chunk length the walk takes), that every 32-bit load is
+4-byte aligned and inside the tensor, that the one 16-bit load happens only
+on the uniform tail branch the kernel takes for it, and that the half picked
+out of each word is element e itself. A second group checks the cut of a
+row into segments (every chunk in exactly one segment, segments in order)."""
+import itertools
+
+import numpy as np
+import pytest
+
+
+def _dt_word_loads(nb, T, H, nhw, Q):
+    """Per (walk, chunk, head of the walk, lane, i): (byte address of the load,
+    its width in bytes, which half holds e, e), as the table wave forms them."""
+    last_e = nb * T * H - 1
+    nc = -(-T // Q)
+    out = []
+    for b, h0 in itertools.product(range(nb), range(0, H, nhw)):
+        for c in range(nc):
+            r0, n = b * T + c * Q, min(Q, T - c * Q)
+            tail = (last_e & 1) == 0 and r0 + n == nb * T and h0 + nhw == H
+            lanes = np.arange(64)[:, None] * 4 + np.arange(4)[None, :]        # tokens 4 lane + i
+            rows = r0 + np.minimum(lanes, n - 1)
+            for q in range(nhw):
+                e = rows * H + h0 + q
+                up = e & 1
+                alone = tail & (e == last_e)
+                addr = np.where(alone, 2 * e, 2 * (e - up))
+                width = np.where(alone, 2, 4)
+                out.append((addr.ravel(), width.ravel(), np.where(alone, 0, up).ravel(), e.ravel(), tail))
+    return out, last_e
+
+
+@pytest.mark.parametrize("nb,T,H,nhw,Q", [(5, 301, 27, 1, 256), (3, 301, 45, 1, 64), (2, 300, 24, 1, 128),
+                                          (3, 2801, 9, 1, 256), (1, 257, 3, 1, 64), (4, 63, 2, 2, 64),
+                                          (1, 1, 1, 1, 64), (3, 65, 6, 2, 128), (1, 131, 5, 1, 64)])
+def test_dt_word_loads_aligned_and_in_bounds(nb, T, H, nhw, Q):
+    loads, last_e = _dt_word_loads(nb, T, H, nhw, Q)
+    nbytes = 2 * (last_e + 1)
+    saw_alone = False
+    for addr, width, half, e, tail in loads:
+        assert np.all(addr >= 0) and np.all(addr + width <= nbytes), "load past the tensor"
+        four = width == 4
+        assert np.all(addr[four] % 4 == 0), "misaligned 32-bit load"
+        assert np.all(addr[~four] % 2 == 0)
+        # the half the kernel keeps is element e: byte offset 2 e
+        assert np.all(addr + 2 * half == 2 * e)
+        if np.any(~four):
+            assert tail, "a 16-bit load outside the tail branch"
+            assert np.all(e[~four] == last_e) and last_e % 2 == 0
+            saw_alone = True
+    assert saw_alone == (last_e % 2 == 0)
+
+
+def _segments(nc, want):
+    seglen = -(-nc // want)
+    nseg = -(-nc // seglen)
+    return [(k * seglen, min(nc, (k + 1) * seglen)) for k in range(nseg)], seglen
+
+
+@pytest.mark.parametrize("nc,want", [(512, 10), (41, 10), (11, 9), (5, 5), (1, 7), (28, 16), (7, 3)])
+def test_segments_cover_each_chunk_once(nc, want):
+    segs, seglen = _segments(nc, want)
+    covered = [c for a, b in segs for c in range(a, b)]
+    assert covered == list(range(nc))
+    assert all(b > a for a, b in segs)
+    assert len(segs) <= want
+    # chunk c's segment, as chunk_scan finds it
+    for c in range(nc):
+        k = c // seglen
+        assert segs[k][0] <= c < segs[k][1]
+
+
+# ---------------------------------------------------------------- fused walk plans
+
+PLAN_SHAPES = [
+    # b, T, H, P, N, G, Q: the named layers, odd shapes, segmented rows, short rows
+    (8, 2048, 24, 64, 128, 1, 256), (4, 4096, 80, 64, 128, 1, 256), (1, 131072, 24, 64, 256, 1, 256),
+    (8, 2048, 24, 64, 128, 1, 128), (5, 301, 27, 64, 128, 1, 256), (3, 301, 45, 64, 128, 1, 64),
+    (3, 2801, 9, 64, 128, 1, 256), (1, 10317, 24, 64, 256, 1, 64), (1, 10317, 24, 64, 256, 1, 128),
+    (2, 845, 24, 64, 128, 1, 256), (2, 845, 24, 64, 128, 1, 64), (1, 7000, 48, 32, 128, 2, 256),
+    (1, 7000, 8, 128, 128, 1, 256), (2, 5000, 8, 64, 256, 1, 128), (4, 1, 64, 64, 128, 2, 64),
+    (4, 63, 64, 64, 128, 2, 64), (4, 500, 96, 64, 128, 1, 128), (2, 300, 64, 128, 256, 1, 256),
+]
+
+
+def _plan(b, T, H, P, N, G, Q, cus=256):
+    import selective_state_space_46_amd as ssd
+    return ssd.ssd_chunk_scan_fwd_plan(b, T, H, P, N, G, Q, ssd.SSD_BF16, cus)
+
+
+@pytest.mark.parametrize("shape", PLAN_SHAPES)
+def test_walk_plan_covers_every_chunk(shape):
+    """The library's plan: segments of at least one chunk that cover the row
+    exactly, and walks that fill at least half of a 256-unit device and at
+    most what fits there in one round."""
+    b, T, H, P, N, G, Q = shape
+    nseg, seglen = _plan(*shape)
+    nc = -(-T // Q)
+    if nseg == 0:
+        assert seglen == 0
+        return
+    assert seglen >= 1 and (nseg - 1) * seglen < nc <= nseg * seglen
+    walks = b * H * P // 64 * nseg
+    assert 128 <= walks <= (512 if N == 128 and Q >= 128 else 256)
+    if nseg > 1:
+        assert walks <= 256
+
+
+@pytest.mark.parametrize("shape", PLAN_SHAPES)
+def test_walk_copies_stay_inside_the_tensors(shape):
+    """Every slice copy of every walk of the library's plan, restated from the
+    kernel: its token rows lie in the tensor (a partial slice repeats its
+    chunk's last token), its B and x element offsets lie inside B and x, and
+    the states it writes lie inside the state buffers."""
+    b, T, H, P, N, G, Q = shape
+    nseg, seglen = _plan(*shape)
+    if nseg == 0:
+        return
+    nc, SPC, cpr = -(-T // Q), Q // 64, H * P // 64
+    rows = np.arange(64)
+    for wid in range(b * cpr * nseg):
+        c0 = (wid % cpr) * 64
+        seg, bb = (wid // cpr) % nseg, wid // cpr // nseg
+        h0 = c0 // P
+        g = h0 // (H // G)
+        cbeg = seg * seglen
+        ncw = min(nc, cbeg + seglen) - cbeg
+        assert ncw >= 1
+        for k in range(ncw * SPC):                    # the clamped copies repeat these
+            ksl = cbeg * SPC + k
+            c, s0 = ksl // SPC, (ksl % SPC) * 64
+            r0, n = bb * T + c * Q, min(Q, T - c * Q)
+            assert 0 <= c < nc and n >= 1
+            tok = r0 + s0 + (rows if s0 + 64 <= n else np.minimum(rows, n - 1 - s0))
+            assert tok.min() >= bb * T and tok.max() < (bb + 1) * T
+            assert ((tok.max() * G + g) * N + N - 1) < b * T * G * N
+            assert tok.max() * H * P + c0 + 63 < b * T * H * P
+        # states entering each chunk, and a segment's last local state
+        hmax = ((bb * nc + cbeg + ncw - 1) * H + (h0 + (1 if P == 32 else 0))) * P * N + P * N - 1
+        assert hmax < b * nc * H * P * N
+        if nseg > 1:
+            assert ((bb * nseg + seg) * H + h0) * P * N + P * N - 1 < b * nseg * H * P * N
+    # chunk_scan: chunk c's segment and the state entering it
+    if nseg > 1:
+        assert all(c // seglen < nseg for c in range(nc))
+
+
+def test_walk_plan_on_other_unit_counts():
+    """the plan follows the unit count it is given (no device involved)"""
+    assert _plan(8, 2048, 24, 64, 128, 1, 256, cus=256) == (1, 8)
+    assert _plan(8, 2048, 24, 64, 128, 1, 256, cus=128) == (1, 8)      # 192 walks, two per unit
+    assert _plan(8, 2048, 24, 64, 128, 1, 256, cus=512) == (2, 4)      # under half the units: two segments
+    assert _plan(1, 300, 8, 64, 128, 1, 256, cus=256) == (0, 0)        # too little work even in segments
+    assert _plan(1, 131072, 24, 64, 256, 1, 256, cus=256) == (10, 52)
+    assert _plan(1, 131072, 24, 64, 256, 1, 256, cus=0) == (0, 0)
