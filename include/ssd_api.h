@@ -197,6 +197,29 @@ SSD_API ssd_status ssd_chunk_scan_fwd_timed(const void *x, const void *dt, const
                                             void *const *stage_events);
 
 /*
+ * ssd_chunk_scan_fwd without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation. It allocates nothing and calls no
+ * allocating routine; its workspace is a scratch array that the library
+ * holds in device memory, SSD_NOALLOC_SCRATCH_BYTES (64 MiB) per GPU, for the
+ * life of the process (the 130M-shaped layer, batch 8 x 2048 tokens, needs
+ * about 33 MiB of it). Sizes whose workspace (ssd_chunk_scan_fwd_workspace)
+ * exceeds that return SSD_ERR_WORKSPACE before any launch; every other
+ * argument and error is as for ssd_chunk_scan_fwd, and the results are
+ * bit-for-bit the same. The first call on a device looks up that device's
+ * array (SSD_ERR_HIP if there is no current device). Every call on one GPU
+ * uses the same array: calls that overlap on one GPU (other streams, other
+ * threads) race and give undefined results; calls ordered on one stream do
+ * not. No byte of the array needs to start at zero.
+ */
+#define SSD_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+SSD_API ssd_status ssd_chunk_scan_fwd_noalloc(const void *x, const void *dt, const float *A, const void *B,
+                                              const void *C, const float *D, const float *init_state,
+                                              void *y, float *final_state, int batch, int seqlen, int nheads,
+                                              int headdim, int dstate, int ngroups, int chunk_len,
+                                              ssd_dtype dtype, void *stream);
+
+/*
  * One recurrent step for every (batch row, head), in place on `state`
  * (Qiita article, section 3.3: inference runs as a recurrence with constant
  * memory; waylandz LLM book ch. 32, section 32.2.4, recurrent form):

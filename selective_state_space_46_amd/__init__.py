@@ -33,7 +33,8 @@ from typing import Optional, Tuple
 __all__ = [
     "SSD_F32", "SSD_BF16", "SSDError", "lib", "lib_path",
     "ssd_chunk_scan_fwd_workspace", "ssd_chunk_scan_fwd", "ssd_chunk_scan_fwd_timed",
-    "ssd_chunk_scan_fwd_fused_states", "ssd_chunk_scan_fwd_plan",
+    "ssd_chunk_scan_fwd_fused_states", "ssd_chunk_scan_fwd_plan", "ssd_chunk_scan_fwd_noalloc",
+    "SSD_NOALLOC_SCRATCH_BYTES",
     "ssd_state_update", "ssd_status_string", "ssd_chunk_scan_fwd_varlen",
     "ssd_chunk_scan_fwd_varlen_workspace", "ssd_gated_rmsnorm", "ssd_causal_conv1d_fwd",
     "ssd_causal_conv1d_update", "ssd_chunk_scan_bwd_workspace", "ssd_chunk_scan_bwd",
@@ -42,6 +43,7 @@ __all__ = [
 
 SSD_F32 = 0
 SSD_BF16 = 1
+SSD_NOALLOC_SCRATCH_BYTES = 64 << 20   # the scratch array of ssd_chunk_scan_fwd_noalloc, per GPU
 
 STATUS_NAMES = {
     0: "SSD_OK", 1: "SSD_ERR_NULL", 2: "SSD_ERR_SHAPE", 3: "SSD_ERR_DTYPE", 4: "SSD_ERR_CHUNK",
@@ -85,6 +87,8 @@ def lib() -> ctypes.CDLL:
     L.ssd_chunk_scan_fwd.restype = i32
     L.ssd_chunk_scan_fwd_timed.argtypes = [vp] * 9 + [i32] * 7 + [i32, vp, sz, vp, vp]
     L.ssd_chunk_scan_fwd_timed.restype = i32
+    L.ssd_chunk_scan_fwd_noalloc.argtypes = [vp] * 9 + [i32] * 7 + [i32, vp]
+    L.ssd_chunk_scan_fwd_noalloc.restype = i32
     L.ssd_state_update.argtypes = [vp] * 8 + [i32] * 5 + [i32, vp]
     L.ssd_state_update.restype = i32
     L.ssd_status_string.argtypes = [i32]
@@ -246,6 +250,45 @@ def ssd_chunk_scan_fwd_timed(x, dt, A, B, C, D=None, init_state=None, chunk_len:
         r = lib().ssd_chunk_scan_fwd_timed(*args, ev)
     if r != 0:
         raise SSDError(r, "ssd_chunk_scan_fwd")
+    return y, final_state
+
+
+def ssd_chunk_scan_fwd_noalloc(x, dt, A, B, C, D=None, init_state=None, chunk_len: int = 256, *,
+                               y, final_state=None, stream=None) -> Tuple[object, object]:
+    """ssd_chunk_scan_fwd through the allocation-free entry point: the caller
+    passes y (and final_state, or None) preallocated; the library runs on its
+    per-GPU scratch array (SSD_NOALLOC_SCRATCH_BYTES) and this wrapper
+    allocates nothing either. Raises SSDError (SSD_ERR_WORKSPACE) for sizes
+    whose workspace exceeds the scratch array."""
+    import torch
+    dev = x.device
+    for v, n in ((x, "x"), (dt, "dt"), (A, "A"), (B, "B"), (C, "C"), (D, "D"), (init_state, "init_state")):
+        if v is not None and not v.is_contiguous():
+            raise ValueError(f"{n} must be contiguous (this entry point makes no copies)")
+    x = _dev(x, dev, "x")
+    dt, A, B, C = (_dev(v, dev, n) for v, n in ((dt, "dt"), (A, "A"), (B, "B"), (C, "C")))
+    D = _dev(D, dev, "D")
+    init_state = _dev(init_state, dev, "init_state")
+    code = _dtype_code(x)
+    for v, n in ((dt, "dt"), (B, "B"), (C, "C"), (y, "y")):
+        _same(v, x.dtype, n)
+    for v, n in ((A, "A"), (D, "D"), (init_state, "init_state"), (final_state, "final_state")):
+        _same(v, torch.float32, n)
+    b, T, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    if tuple(dt.shape) != (b, T, H) or tuple(B.shape) != (b, T, G, N) or tuple(C.shape) != (b, T, G, N):
+        raise ValueError("shape mismatch among x, dt, B, C")
+    if tuple(A.shape) != (H,) or (D is not None and tuple(D.shape) != (H,)):
+        raise ValueError("A and D must be [nheads]")
+    for v, n, shp in ((init_state, "init_state", (b, H, N, P)), (final_state, "final_state", (b, H, N, P)),
+                      (y, "y", (b, T, H, P))):
+        if v is not None and (tuple(v.shape) != shp or not v.is_contiguous() or v.device != dev):
+            raise ValueError(f"{n} must be a contiguous {list(shp)} tensor on {dev}")
+    r = lib().ssd_chunk_scan_fwd_noalloc(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(init_state),
+                                         _ptr(y), _ptr(final_state), b, T, H, P, N, G, chunk_len, code,
+                                         _stream(dev, stream))
+    if r != 0:
+        raise SSDError(r, "ssd_chunk_scan_fwd_noalloc")
     return y, final_state
 
 

@@ -5,6 +5,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 
 #include "ssd_backward.h"
 #include "ssd_epilogue.h"
@@ -136,6 +137,38 @@ bool bwd_supported(int batch, int seqlen, int H, int P, int N, int G, ssd_dtype 
   if (!use_mfma_path(s, dtype) || !grids_fit(s, true)) return false;
   const double bch = double(s.b) * s.nc * s.H;
   return 4.0 * Qb * bch < 4294967295.0 && double(batch) * seqlen * G * (N / 4) < 4294967295.0;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// Scratch memory of the allocation-free forward (ssd_chunk_scan_fwd_noalloc):
+// one array per GPU, in the code object, held until the process ends. In
+// host code `scratch` names a host-side stand-in, not device memory: its
+// device address comes from hipGetSymbolAddress, taken once per device with
+// that device current, and only that address is ever handed to a kernel.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[SSD_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices];   // device address of `scratch` per device (set once)
+
+// The current device's scratch address (looked up on the first call on the
+// device); SSD_ERR_HIP when there is no usable device or the lookup fails.
+ssd_status scratch_address(void** out) {
+  *out = nullptr;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SSD_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return SSD_ERR_HIP;
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return SSD_OK;
 }
 
 }  // namespace
@@ -319,6 +352,20 @@ ssd_status ssd_chunk_scan_fwd(const void* x, const void* dt, const float* A, con
   return ssd_chunk_scan_fwd_timed(x, dt, A, B, C, D, init_state, y, final_state, batch, seqlen,
                                   nheads, headdim, dstate, ngroups, chunk_len, dtype, workspace,
                                   workspace_bytes, stream, nullptr);
+}
+
+ssd_status ssd_chunk_scan_fwd_noalloc(const void* x, const void* dt, const float* A, const void* B,
+                                      const void* C, const float* D, const float* init_state, void* y,
+                                      float* final_state, int batch, int seqlen, int nheads, int headdim,
+                                      int dstate, int ngroups, int chunk_len, ssd_dtype dtype, void* stream) {
+  void* ws = nullptr;
+  const ssd_status st = scratch_address(&ws);
+  if (st != SSD_OK) return st;
+  // the same checks and launches as ssd_chunk_scan_fwd, over this device's
+  // scratch: sizes whose workspace exceeds it return SSD_ERR_WORKSPACE before
+  // any launch; every byte of it that a call reads, the call writes first
+  return ssd_chunk_scan_fwd_timed(x, dt, A, B, C, D, init_state, y, final_state, batch, seqlen, nheads, headdim,
+                                  dstate, ngroups, chunk_len, dtype, ws, SSD_NOALLOC_SCRATCH_BYTES, stream, nullptr);
 }
 
 ssd_status ssd_state_update(float* state, const void* x, const void* dt, const float* A,
