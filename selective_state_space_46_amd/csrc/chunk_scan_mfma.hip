@@ -46,7 +46,9 @@
 // local states, from zero at each segment's start; the state entering chunk
 // c of segment k >= 1 is Hb_c + exp(cdec_c) Hin_k (Hin fp32 [b, nseg, H, P,
 // N], the state entering each segment; cdec_c <= 0), formed in fp32 where
-// H_c is staged or loaded and rounded to bf16 once.
+// H_c is staged or loaded and rounded to bf16 once. Where exp(cdec_c)
+// underflows to zero (a decayed segment start) the correction is exactly
+// zero and Hin is not read.
 #include "mfma_util.h"
 
 namespace ssd {
@@ -163,8 +165,10 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_mfma_kernel(
     constexpr int kStep = kThreads / (N / 8);        // rows p per pass
     const int p0 = tid / (N / 8), seg = tid % (N / 8);
     const int sg = SEG ? c0 / seglen : 0;            // the chunk's segment (uniform)
-    if (SEG && sg > 0) {
-      const float alpha = exp_fast(cdec[(size_t(b) * H + h) * nc + c0]);
+    // the weight of the state entering the segment (uniform; where it
+    // underflows to zero the correction adds exactly zero and is skipped)
+    const float alpha = SEG && sg > 0 ? exp_fast(cdec[(size_t(b) * H + h) * nc + c0]) : 0.f;
+    if (SEG && alpha != 0.f) {
       const float* hin = Hin + ((size_t(b) * nseg + sg) * H + h) * size_t(P) * N;
 #pragma unroll
       for (int k = 0; k < (P + kStep - 1) / kStep; ++k)
@@ -276,7 +280,8 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_mfma_kernel(
         } else {
           const size_t o = (size_t(32 * pb + l32)) * N + 16 * ks + 8 * g2;
           hf = load16(Hb + ((size_t(b) * nc + cg) * H + h) * size_t(P) * N + o);
-          if (SEG && sgb > 0) hf = seg_combine(hf, Hin + ((size_t(b) * nseg + sgb) * H + h) * size_t(P) * N + o, alpha_b);
+          if (SEG && alpha_b != 0.f)
+            hf = seg_combine(hf, Hin + ((size_t(b) * nseg + sgb) * H + h) * size_t(P) * N + o, alpha_b);
         }
         acc[pb] = mfma32x32x16(hf, cf[ks], acc[pb]);
       }

@@ -801,18 +801,85 @@ void chunk_state_chain_kernel(
   }
 }
 
+// The C B^T tiles alone, for segmented launches: their walks take nearly
+// every compute unit for the whole launch, so tile work-groups placed behind
+// them (as the whole-row launch does) would all run on the few units left.
+// A work-group per (batch, chunk, group) and a wave per pair of 32-row blocks
+// of C (i and lpc - 1 - i: 1 + lpc tiles per wave, balanced): the wave loads
+// its C rows once per block and streams the B row blocks j <= i, the next
+// one loading while the current one feeds the matrix cores. The tiles are
+// the ones chunk_scores_tile computes, at the same places.
+template <int N>
+__global__ __launch_bounds__(256) void chunk_scores_rows_kernel(const uint16_t* __restrict__ Bm,
+                                                                const uint16_t* __restrict__ Cm,
+                                                                uint16_t* __restrict__ CB, int T, int G, int Q,
+                                                                int nc) {
+  const int lpc = Q / 32, ntile = lpc * (lpc + 1) / 2;
+  const int wave = wave_id(), lane = threadIdx.x & 63;
+  const int l32 = lane & 31, g2 = lane >> 5;
+  const int g = int(blockIdx.x) % G;
+  const int c = (int(blockIdx.x) / G) % nc;
+  const int b = int(blockIdx.x) / G / nc;
+  const ChunkRows cr = chunk_rows(nullptr, b, c, T, Q);
+  // rows tl of C, ts of B inside the chunk (clamped into it; zeroed past it)
+  auto rows16 = [&](const uint16_t* M, int t, u32x4 (&f)[N / 16]) {
+    const uint16_t* r = M + ((cr.r0 + min(t, cr.n - 1)) * G + g) * size_t(N) + 8 * g2;
+#pragma unroll
+    for (int ks = 0; ks < N / 16; ++ks) f[ks] = keep_or_zero(t < cr.n, load16(r + 16 * ks));
+  };
+  const size_t base = ((size_t(b) * nc + c) * G + g) * ntile;
+  for (int which = 0; which < 2; ++which) {
+    const int i = which ? lpc - 1 - wave : wave;      // C row block (wave-uniform)
+    if (32 * i >= cr.n) continue;                     // past the valid tokens: never read
+    u32x4 cf[N / 16], bf[N / 16], bn[N / 16];
+    rows16(Cm, 32 * i + l32, cf);
+    rows16(Bm, l32, bf);                              // B row block 0
+    for (int j = 0; j <= i; ++j) {
+      if (j < i) rows16(Bm, 32 * (j + 1) + l32, bn);  // the next B row block
+      f32x16 acc = zero16();
+#pragma unroll
+      for (int ks = 0; ks < N / 16; ++ks) acc = mfma32x32x16(bf[ks], cf[ks], acc);   // rows s, column l
+      u32x4 lo, hi;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        lo[m] = pack_bf16x2(acc[2 * m], acc[2 * m + 1]);
+        hi[m] = pack_bf16x2(acc[8 + 2 * m], acc[8 + 2 * m + 1]);
+      }
+      u32x4* dst = reinterpret_cast<u32x4*>(CB + (base + size_t(i) * (i + 1) / 2 + j) * 1024 + size_t(lane) * 16);
+      dst[0] = lo;
+      dst[1] = hi;
+      if (j < i) {
+#pragma unroll
+        for (int ks = 0; ks < N / 16; ++ks) bf[ks] = bn[ks];
+      }
+    }
+  }
+}
+
 template <int N, int P, int SPC, int ST, bool F32S, bool REV>
 hipError_t launch_chain_np(const FwdShape& s, const ChainPlan& pl, const void* x, const void* B, const void* C,
                            const void* dt, const float* A, float* Acs, float* dtq, void* Hs, const float* init,
                            float* fin, uint16_t* CB, uint16_t* CBt, const float* Hst, float* ghp, float* cdec,
                            float* segdec, hipStream_t st, const StageEv& ev) {
   const int lpc = s.Q / 32;
-  const long ntiles = REV ? 0 : long(s.b) * s.nc * s.G * (lpc * (lpc + 1) / 2);
+  const long alltiles = REV ? 0 : long(s.b) * s.nc * s.G * (lpc * (lpc + 1) / 2);
   const long nchain = long(s.b) * s.H * P / kChainCols * pl.nseg;
-  const long blocks = nchain + (ntiles + kChainWaves - 1) / kChainWaves;
   const bool segd = pl.nseg > 1;
+  // segmented: the tiles first, as a launch of their own (the stage's start
+  // event on it, the stop event on the walk)
+  if (segd && alltiles > 0) {
+    // (segments need chunk_len a multiple of 64: an even number of row blocks)
+    hipExtLaunchKernelGGL((chunk_scores_rows_kernel<N>), dim3(unsigned(long(s.b) * s.nc * s.G)),
+                          dim3(64 * (s.Q / 64)), 0, st, ev.start, nullptr, 0, static_cast<const uint16_t*>(B),
+                          static_cast<const uint16_t*>(C), CB, s.T, s.G, s.Q, s.nc);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const long ntiles = segd ? 0 : alltiles;
+  const long blocks = nchain + (ntiles + kChainWaves - 1) / kChainWaves;
   hipExtLaunchKernelGGL((chunk_state_chain_kernel<N, P, SPC, ST, F32S, REV>), dim3(unsigned(blocks)),
-                        dim3(kChainThreads), 0, st, ev.start, ev.stop, 0, static_cast<const uint16_t*>(x),
+                        dim3(kChainThreads), 0, st, segd && alltiles > 0 ? nullptr : ev.start, ev.stop, 0,
+                        static_cast<const uint16_t*>(x),
                         static_cast<const uint16_t*>(B), static_cast<const uint16_t*>(dt), A, Acs, dtq, Hs, init, fin,
                         static_cast<const uint16_t*>(C), CB, CBt, Hst, ghp, segd ? cdec : nullptr,
                         segd ? segdec : nullptr, s.T, s.H, s.G, s.Q, s.nc, s.b, pl.nseg, pl.seglen, int(nchain),

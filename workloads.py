@@ -71,6 +71,7 @@ class FwdWorkload:
     dt_mode: str = "softplus"  # "softplus" (clamped), "loguniform" or "fast"
     init: str = "zero"         # "zero" or "normal0.1"
     seed: int = 0
+    tag: str = ""              # short name (profile summaries are named by it)
 
     @property
     def tokens(self) -> int:
@@ -94,13 +95,13 @@ class DecodeWorkload:
 # sizes: a tiny fp32 case, a 130M-shaped layer, a 2.7B-shaped layer with a
 # nonzero initial state, a 128K-token long-context case, and a decode batch).
 TINY_F32 = FwdWorkload("tiny_f32_b1_T256_H2_P16_N16_Q64", 1, 256, 2, 16, 16, 1, 64,
-                       "f32", seed=4600)
+                       "f32", seed=4600, tag="tiny_f32")
 MAMBA2_130M = FwdWorkload("mamba2_130m_b8_T2048_H24_P64_N128_Q256", 8, 2048, 24, 64, 128, 1, 256,
-                          "bf16", seed=4601)
+                          "bf16", seed=4601, tag="mamba2_130m")
 MAMBA2_2P7B = FwdWorkload("mamba2_2p7b_b4_T4096_H80_P64_N128_Q256_init", 4, 4096, 80, 64, 128, 1, 256,
-                          "bf16", init="normal0.1", seed=4602)
+                          "bf16", init="normal0.1", seed=4602, tag="mamba2_2p7b")
 LONG_128K = FwdWorkload("long_b1_T131072_H24_P64_N256_Q256", 1, 131072, 24, 64, 256, 1, 256,
-                        "bf16", dt_mode="loguniform", seed=4603)
+                        "bf16", dt_mode="loguniform", seed=4603, tag="long_128k")
 DECODE_B256 = DecodeWorkload("decode_b256_H128_P64_N128_G8_64steps", 256, 128, 64, 128, 8, 64,
                              "bf16", seed=4604)
 
@@ -108,6 +109,9 @@ FWD_WORKLOADS = {w.name: w for w in (TINY_F32, MAMBA2_130M, MAMBA2_2P7B, LONG_12
 
 
 def with_shape(w: FwdWorkload, **kw) -> FwdWorkload:
+    """A variant of w (a different shape is no longer the named workload, so
+    its tag is dropped unless given)."""
+    kw.setdefault("tag", "")
     return dataclasses.replace(w, **kw)
 
 
