@@ -25,14 +25,16 @@
 // Factors that underflow to zero stand for weights that are smaller still.
 //
 // Work-group: one batch row, one 256-token super-chunk (256/Q chunks), one
-// head; 4 waves. The C B^T tiles come precomputed once per group
-// (by the chunk_state launch, chunk_state_mfma.hip) in MFMA-fragment order. The super-chunk is cut into eight
-// 32-row blocks l; wave w owns blocks w and 7-w so that the causal triangle
-// splits evenly. The output is produced transposed (y^T: rows p, lane = token
+// head; W waves. The C B^T tiles come precomputed once per group (by the
+// chunk_state launch, chunk_state_mfma.hip) in MFMA-fragment order. The
+// super-chunk is cut into eight 32-row blocks l; with W = 4 wave w owns
+// blocks w and 7-w so that the causal triangle splits evenly, with W = 8 one
+// block each (twice the waves on the same LDS, for latency hiding). The output is produced transposed (y^T: rows p, lane = token
 // l), which makes every per-token factor one multiplier per lane:
-//   1. y^T = H_c^T C_l^T (k = dstate): H_c^T staged once in LDS (bf16, from
-//      state_passing) when the super-chunk is one chunk, C_l rows straight from
-//      HBM; then y^T *= exp(Acs_l).
+//   1. y^T = H_c^T C_l^T (k = dstate): H_c staged once in LDS as stored (bf16,
+//      fragment order, from the fused walk or state_passing, see hb_off) when
+//      the super-chunk is one chunk, C_l rows straight from HBM; then
+//      y^T *= exp(Acs_l).
 //   2. for each column block s <= l of the chunk: the C B^T tile (lane =
 //      column l, registers = rows s in runs of 4) times the decay, rounded to
 //      bf16, is the B operand of y^T += X^T G^T under a k permutation that the
@@ -44,8 +46,9 @@
 //      consecutive p.
 // SEG (rows cut into segments by the fused chunk-state walk): Hb holds the
 // local states, from zero at each segment's start; the state entering chunk
-// c of segment k >= 1 is Hb_c + exp(cdec_c) Hin_k (Hin fp32 [b, nseg, H, P,
-// N], the state entering each segment; cdec_c <= 0), formed in fp32 where
+// c of segment k >= 1 is Hb_c + exp(cdec_c) Hin_k (Hin fp32 [b, nseg, H,
+// P * N] in the same fragment order, the state entering each segment;
+// cdec_c <= 0), formed in fp32 where
 // H_c is staged or loaded and rounded to bf16 once. Where exp(cdec_c)
 // underflows to zero (a decayed segment start) the correction is exactly
 // zero and Hin is not read.
@@ -54,7 +57,6 @@
 namespace ssd {
 namespace {
 
-constexpr int kThreads = 256;
 constexpr int kSC = 256;          // tokens per super-chunk
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -71,18 +73,20 @@ __device__ __forceinline__ u32x4 seg_combine(const u32x4& v, const float* hin, f
 
 // VARLEN: chunk rows from the chunk table tab (packed sequences), else the
 // equal-length layout (tab unused). SEG: the segment correction above.
-template <int N, int P, bool HLDS, bool VARLEN, bool SEG>
-__global__ __launch_bounds__(kThreads) void chunk_scan_mfma_kernel(
+template <int N, int P, bool HLDS, bool VARLEN, bool SEG, int W>
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(W == 8 ? 4 : 1)))
+void chunk_scan_mfma_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ CB, const uint16_t* __restrict__ Cm,
     const float* __restrict__ Acs, const float* __restrict__ dtq, const uint16_t* __restrict__ Hb,
     const float* __restrict__ D, uint16_t* __restrict__ y, const int4* __restrict__ tab, int T, int H,
     int G, int Q, int nc, int nsc, const float* __restrict__ Hin, const float* __restrict__ cdec, int nseg,
     int seglen) {
-  constexpr int kHS = N + 8;  // H^T row stride (bf16): 16-byte reads of 16 lanes hit distinct banks
+  constexpr int kThreads = 64 * W;
+  constexpr int NB = 8 / W;   // 32-row blocks per wave
   constexpr int RBX = P / 8;  // 16-byte chunks per X' row
-  constexpr int HROWS = HLDS ? P : 1;
   __shared__ __attribute__((aligned(16))) uint16_t sX[kSC * P];
-  __shared__ __attribute__((aligned(16))) uint16_t sHt[HROWS][kHS];
+  // H_c staged as it is stored, in fragment order (hb_off)
+  __shared__ __attribute__((aligned(16))) uint16_t sH[HLDS ? P * N : 8];
   __shared__ __attribute__((aligned(16))) float sA[kSC];  // Acs * log2(e)
   __shared__ __attribute__((aligned(16))) float sF[kSC];  // exp(Acs[block end] - Acs_s) * dt_s
   __shared__ __attribute__((aligned(16))) float sL[kSC];  // log2(dt_s) - Acs_s log2(e)
@@ -160,28 +164,22 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_mfma_kernel(
     sL[i] = __builtin_amdgcn_logf(d) - a;    // log2; -inf where dt = 0
   }
   if constexpr (HLDS) {
+    // H_c in fragment order (hb_off), copied as it is (with segments, plus
+    // alpha times the state entering the segment, stored in the same order)
     const uint16_t* hsrc = Hb + ((size_t(b) * nc + c0) * H + h) * size_t(P) * N;
-    static_assert(kThreads % (N / 8) == 0, "H staging shape");
-    constexpr int kStep = kThreads / (N / 8);        // rows p per pass
-    const int p0 = tid / (N / 8), seg = tid % (N / 8);
+    constexpr int kPieces = P * N / 8;               // 16-byte pieces of one state
     const int sg = SEG ? c0 / seglen : 0;            // the chunk's segment (uniform)
     // the weight of the state entering the segment (uniform; where it
     // underflows to zero the correction adds exactly zero and is skipped)
     const float alpha = SEG && sg > 0 ? exp_fast(cdec[(size_t(b) * H + h) * nc + c0]) : 0.f;
-    if (SEG && alpha != 0.f) {
-      const float* hin = Hin + ((size_t(b) * nseg + sg) * H + h) * size_t(P) * N;
+    const float* hin = SEG ? Hin + ((size_t(b) * nseg + sg) * H + h) * size_t(P) * N : nullptr;
 #pragma unroll
-      for (int k = 0; k < (P + kStep - 1) / kStep; ++k)
-        if (P % kStep == 0 || p0 + k * kStep < P) {
-          const size_t o = size_t(p0 + k * kStep) * N + 8 * seg;
-          *reinterpret_cast<u32x4*>(&sHt[p0 + k * kStep][8 * seg]) = seg_combine(load16(hsrc + o), hin + o, alpha);
-        }
-    } else {
-#pragma unroll
-      for (int k = 0; k < (P + kStep - 1) / kStep; ++k)
-        if (P % kStep == 0 || p0 + k * kStep < P)
-          *reinterpret_cast<u32x4*>(&sHt[p0 + k * kStep][8 * seg]) =
-              load16(hsrc + size_t(p0 + k * kStep) * N + 8 * seg);
+    for (int k = 0; k < (kPieces + kThreads - 1) / kThreads; ++k) {
+      const int e = tid + k * kThreads;
+      if (kPieces % kThreads != 0 && e >= kPieces) break;
+      u32x4 v = load16(hsrc + 8 * size_t(e));
+      if (SEG && alpha != 0.f) v = seg_combine(v, hin + 8 * size_t(e), alpha);   // Hin: the same order
+      *reinterpret_cast<u32x4*>(&sH[8 * e]) = v;
     }
   }
   // raw x, token-major, swizzled: issued with the loads above. Thread tid
@@ -197,11 +195,11 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_mfma_kernel(
       const uint16_t* src = x + ((rows0.r0 + r0) * H + h) * size_t(P) + 8 * cc;
       const size_t step = size_t(kStep) * H * P;
 #pragma unroll
-      for (int k = 0; k < RBX; ++k)
+      for (int k = 0; k < kSC / kStep; ++k)
         *reinterpret_cast<u32x4*>(dst + k * kStep * P) = load16(src + k * step);
     } else {
 #pragma unroll
-      for (int k = 0; k < RBX; ++k) {
+      for (int k = 0; k < kSC / kStep; ++k) {
         const int r = r0 + k * kStep;
         const ChunkRows cr = crows(r / Q);
         const int rq = r % Q;
@@ -230,7 +228,7 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_mfma_kernel(
   }
 
   const float Dh = D ? D[h] : 0.f;
-  for (int which = 0; which < 2; ++which) {
+  for (int which = 0; which < NB; ++which) {
     const int i = which ? 7 - wave : wave;  // 32-row block of the super-chunk
     const ChunkRows cr = crows(i / lpc);
     const int rq0 = (i % lpc) * 32;         // first row of the block inside its chunk
@@ -265,6 +263,7 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_mfma_kernel(
     // ---- y^T = H_c^T C_l^T, then * exp(Acs_l)
     f32x16 acc[P / 32];
     const float sl = __builtin_amdgcn_exp2f(sA[lcol]);
+    const int hlane = 256 * g2 + 4 * l32;   // this lane's part of a fragment-order offset
     // segments, per-fragment path: this block's chunk's segment and the
     // weight of the state entering it (uniform)
     const int sgb = SEG && !HLDS ? cg / seglen : 0;
@@ -275,13 +274,31 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_mfma_kernel(
 #pragma unroll
       for (int ks = 0; ks < N / 16; ++ks) {
         u32x4 hf;
+        // eight consecutive n of row p: two runs of four in fragment order
+        // (in LDS: the 32 lanes of each half read 256 contiguous bytes per run).
+        // With n = 16 ks + 8 g2, hb_off(p, n) = hlane + 256 ((pb N / 32 + ks / 2) 4
+        // + 2 (ks % 2)) with the per-lane part hlane = 256 g2 + 4 l32, and the
+        // run of n + 4 sits 128 elements (32 runs) after it
+        const int p = 32 * pb + l32, n = 16 * ks + 8 * g2;
         if constexpr (HLDS) {
-          hf = *reinterpret_cast<const u32x4*>(&sHt[32 * pb + l32][16 * ks + 8 * g2]);
+          const int o = hlane + 256 * ((pb * (N / 32) + ks / 2) * 4 + 2 * (ks % 2));
+          const u32x2 lo = *reinterpret_cast<const u32x2*>(&sH[o]);
+          const u32x2 hi = *reinterpret_cast<const u32x2*>(&sH[o + 128]);
+          hf = u32x4{lo[0], lo[1], hi[0], hi[1]};
         } else {
-          const size_t o = (size_t(32 * pb + l32)) * N + 16 * ks + 8 * g2;
-          hf = load16(Hb + ((size_t(b) * nc + cg) * H + h) * size_t(P) * N + o);
-          if (SEG && alpha_b != 0.f)
-            hf = seg_combine(hf, Hin + ((size_t(b) * nseg + sgb) * H + h) * size_t(P) * N + o, alpha_b);
+          const uint16_t* hs = Hb + ((size_t(b) * nc + cg) * H + h) * size_t(P) * N;
+          const u32x2 lo = *reinterpret_cast<const u32x2*>(hs + hb_off(p, n, N));
+          const u32x2 hi = *reinterpret_cast<const u32x2*>(hs + hb_off(p, n + 4, N));
+          hf = u32x4{lo[0], lo[1], hi[0], hi[1]};
+          if (SEG && alpha_b != 0.f) {
+            const float* hin = Hin + ((size_t(b) * nseg + sgb) * H + h) * size_t(P) * N;
+            const f32x4 a = *reinterpret_cast<const f32x4*>(hin + hb_off(p, n, N));
+            const f32x4 c = *reinterpret_cast<const f32x4*>(hin + hb_off(p, n + 4, N));
+            hf = u32x4{pack_bf16x2(bf16_lo(hf[0]) + alpha_b * a[0], bf16_hi(hf[0]) + alpha_b * a[1]),
+                       pack_bf16x2(bf16_lo(hf[1]) + alpha_b * a[2], bf16_hi(hf[1]) + alpha_b * a[3]),
+                       pack_bf16x2(bf16_lo(hf[2]) + alpha_b * c[0], bf16_hi(hf[2]) + alpha_b * c[1]),
+                       pack_bf16x2(bf16_lo(hf[3]) + alpha_b * c[2], bf16_hi(hf[3]) + alpha_b * c[3])};
+          }
         }
         acc[pb] = mfma32x32x16(hf, cf[ks], acc[pb]);
       }
@@ -383,8 +400,12 @@ hipError_t launch_np(const FwdShape& s, const void* x, const uint16_t* CB, const
   const int cps = kSC / s.Q;
   const int nsc = (s.nc + cps - 1) / cps;   // = ceil(T / 256) for equal-length rows
   const long blocks = long(s.b) * nsc * s.H;
-  auto go = [&](auto kern) {
-    hipExtLaunchKernelGGL(kern, dim3(unsigned(blocks)), dim3(kThreads), 0, st, ev.start, ev.stop, 0,
+  // waves per work-group: 8 (one 32-row block each, 128 registers) where
+  // dstate 256 and the staged H_c leave two 4-wave work-groups per unit with
+  // 254 registers each; 4 elsewhere
+  constexpr int W = N == 256 ? 8 : 4;
+  auto go = [&](auto kern, int w) {
+    hipExtLaunchKernelGGL(kern, dim3(unsigned(blocks)), dim3(64 * w), 0, st, ev.start, ev.stop, 0,
                           static_cast<const uint16_t*>(x), CB, static_cast<const uint16_t*>(C), Acs, dtq, Hb, D,
                           static_cast<uint16_t*>(y), tab, s.T, s.H, s.G, s.Q, s.nc, nsc, sg.Hin, sg.cdec, sg.nseg,
                           sg.seglen);
@@ -393,11 +414,13 @@ hipError_t launch_np(const FwdShape& s, const void* x, const uint16_t* CB, const
   if (seg && (tab || !sg.Hin || !sg.cdec || sg.seglen < 1)) return hipErrorInvalidValue;
   // one chunk per super-chunk: its H_c^T is staged in LDS
   if (s.Q == kSC) {
-    if (seg) go(chunk_scan_mfma_kernel<N, P, true, false, true>);
-    else tab ? go(chunk_scan_mfma_kernel<N, P, true, true, false>) : go(chunk_scan_mfma_kernel<N, P, true, false, false>);
+    if (seg) go(chunk_scan_mfma_kernel<N, P, true, false, true, W>, W);
+    else if (tab) go(chunk_scan_mfma_kernel<N, P, true, true, false, W>, W);
+    else go(chunk_scan_mfma_kernel<N, P, true, false, false, W>, W);
   } else {
-    if (seg) go(chunk_scan_mfma_kernel<N, P, false, false, true>);
-    else tab ? go(chunk_scan_mfma_kernel<N, P, false, true, false>) : go(chunk_scan_mfma_kernel<N, P, false, false, false>);
+    if (seg) go(chunk_scan_mfma_kernel<N, P, false, false, true, 4>, 4);
+    else if (tab) go(chunk_scan_mfma_kernel<N, P, false, true, false, 4>, 4);
+    else go(chunk_scan_mfma_kernel<N, P, false, false, false, 4>, 4);
   }
   return hipGetLastError();
 }

@@ -306,8 +306,8 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma_kernel(
 // with cdec_c the summed chunk decay exponents from the segment's start to c
 // and Hin_k the state entering segment k. A segmented walk writes H_c^local
 // (bf16), cdec (fp32 [b, H, nc]), its segment's total decay exponent (segdec,
-// fp32 [b, H, nseg]) and its last local state (fp32 [b, nseg, H, P, N], the
-// layout of the states entering each chunk) in place of the final state;
+// fp32 [b, H, nseg]) and its last local state (fp32 [b, nseg, H, P * N] in
+// fragment order, as the bf16 states) in place of the final state;
 // state_passing then runs the recurrence over the segments, and chunk_scan
 // adds exp(cdec_c) Hin_k where it stages H_c.
 //
@@ -715,18 +715,24 @@ void chunk_state_chain_kernel(
       for (int off = 32; off >= 1; off >>= 1) dot += __shfl_xor(dot, off, 64);
       if (lane == 0) ghp[((size_t(b) * H + hj) * nc + c) * (P / 16) + 2 * (pj / 32) + (wave >> 1)] = dot;
     }
-    const size_t hoff = ((size_t(b) * nc + c) * H + hj) * hstate + size_t(pj + l32) * N;
+    // fp32 (F32S) and the reverse walk's gradients: [p][n] rows; the forward's
+    // bf16 states: fragment order (hb_off), the accumulators as they are
+    const size_t sbase = ((size_t(b) * nc + c) * H + hj) * hstate;
+    const size_t hoff = sbase + size_t(pj + l32) * N;
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         const int n = 32 * ntile(u) + 8 * jj + 4 * g2;
+        const u32x2 v2 = u32x2{pack_bf16x2(acc[u][4 * jj], acc[u][4 * jj + 1]),
+                               pack_bf16x2(acc[u][4 * jj + 2], acc[u][4 * jj + 3])};
         if constexpr (F32S) {
           *reinterpret_cast<f32x4*>(static_cast<float*>(Hs) + hoff + n) =
               f32x4{acc[u][4 * jj], acc[u][4 * jj + 1], acc[u][4 * jj + 2], acc[u][4 * jj + 3]};
+        } else if constexpr (REV) {
+          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(Hs) + hoff + n) = v2;
         } else {
-          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(Hs) + hoff + n) =
-              u32x2{pack_bf16x2(acc[u][4 * jj], acc[u][4 * jj + 1]), pack_bf16x2(acc[u][4 * jj + 2], acc[u][4 * jj + 3])};
+          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(Hs) + sbase + hb_off(pj + l32, n, N)) = v2;
         }
       }
     }
@@ -781,13 +787,14 @@ void chunk_state_chain_kernel(
     }
   }
   if (fin && nseg > 1) {
-    // a segment's last local state, [b, nseg, H, P, N] (runs of four n)
-    float* dst = fin + ((size_t(b) * nseg + seg) * H + hj) * hstate + size_t(pj + l32) * N;
+    // a segment's last local state, [b, nseg, H, P * N], each head's in
+    // fragment order (hb_off), fp32
+    float* dst = fin + ((size_t(b) * nseg + seg) * H + hj) * hstate;
 #pragma unroll
     for (int u = 0; u < TPW; ++u)
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj)
-        *reinterpret_cast<f32x4*>(dst + 32 * ntile(u) + 8 * jj + 4 * g2) =
+        *reinterpret_cast<f32x4*>(dst + hb_off(pj + l32, 32 * ntile(u) + 8 * jj + 4 * g2, N)) =
             f32x4{acc[u][4 * jj], acc[u][4 * jj + 1], acc[u][4 * jj + 2], acc[u][4 * jj + 3]};
   } else if (fin) {
 #pragma unroll

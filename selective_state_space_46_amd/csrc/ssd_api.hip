@@ -314,7 +314,7 @@ ssd_status ssd_chunk_scan_fwd_timed(const void* x, const void* dt, const float* 
       FwdShape ss = s;
       ss.nc = pl.nseg;
       ss.Q = 1;
-      if (launch_state_passing(ss, S, nullptr, segdec, nullptr, final_state, hs, ev(2)) != hipSuccess)
+      if (launch_state_passing(ss, S, nullptr, segdec, nullptr, final_state, hs, ev(2), true) != hipSuccess)
         return SSD_ERR_HIP;
       SegStates sg;
       sg.Hin = S;

@@ -128,17 +128,34 @@ bool chain_plan_valid(const FwdShape& s, const ChainPlan& pl);
 constexpr int kMaxDevices = 64;
 int device_units();
 
+// Layout of one head's bf16 state entering a chunk (the matrix-core path's
+// Hb, P x N per (batch, chunk, head)): matrix-core fragment order. Element
+// (p, n) sits at
+//   ((((p / 32) * (N / 32) + n / 32) * 4 + (n % 32) / 8) * 64
+//       + p % 32 + 32 * ((n % 8) / 4)) * 4 + n % 4,
+// i.e. runs of four consecutive n; each 32 x 32 block (p / 32, n / 32) is
+// 1024 consecutive elements, four groups of 64 runs. It is the order in
+// which the fused walk holds a state in its MFMA accumulators (lane
+// p % 32 + 32 ((n % 8) / 4), register 4 ((n % 32) / 8) + n % 4), so each
+// of its stores writes 512 contiguous bytes. Needs P and N multiples of 32.
+__host__ __device__ __forceinline__ size_t hb_off(int p, int n, int N) {
+  return ((size_t((p >> 5) * (N >> 5) + (n >> 5)) * 4 + ((n & 31) >> 3)) * 64 + (p & 31) + 32 * ((n & 7) >> 2)) * 4 +
+         (n & 3);
+}
+
 // Workspace layout (byte offsets, each 256-byte aligned):
 //   acs [b, H, nc, Q] f32    cumulative dt*A inside each chunk (inclusive)
 //   dtq [b, H, nc, Q] f32    dt widened to fp32, 0 past the end of the sequence
 //   st  [b, nc, H, P, N] f32 chunk states, stored transposed (n fastest); on
 //                            the generic path overwritten in place by the
 //                            states entering each chunk. Absent on the fused
-//                            path, except with segments: [b, nseg, H, P, N],
-//                            each segment's last local state, then (in place)
-//                            the state entering each segment
-//   hb  [b, nc, H, P, N] bf16 states entering each chunk (MFMA path only;
-//                            with segments, the local ones)
+//                            path, except with segments: [b, nseg, H, P * N]
+//                            (fragment order), each segment's last local
+//                            state, then (in place) the state entering each
+//                            segment
+//   hb  [b, nc, H, P * N] bf16 states entering each chunk, each head's in
+//                            fragment order (hb_off; MFMA path only; with
+//                            segments, the local ones)
 //   cb  [b, nc, G, ntile, 64, 16] bf16 C B^T tiles of each chunk (MFMA path
 //       only; ntile = lpc (lpc + 1) / 2 lower-triangle tiles, lpc = Q / 32)
 //   cdec [b, H, nc] f32, segdec [b, H, nseg] f32 (segments only): summed
@@ -243,9 +260,12 @@ hipError_t launch_chunk_grad_chain_bwd(const FwdShape& s, const void* dy, const 
                                        const float* Hst, float* ghp, hipStream_t st);
 
 // Hb == nullptr: states entering each chunk overwrite S in place (fp32);
-// otherwise they are written to Hb as bf16 and S is left as it was.
+// otherwise they are written to Hb as bf16 (fragment order, hb_off) and S is
+// left as it was. sfrag: each head's S is in fragment order (the segment
+// states of the fused walk) instead of [p][n] rows.
 hipError_t launch_state_passing(const FwdShape& s, float* S, uint16_t* Hb, const float* Acs,
-                                const float* init, float* final_state, hipStream_t st, const StageEv& ev = StageEv{});
+                                const float* init, float* final_state, hipStream_t st, const StageEv& ev = StageEv{},
+                                bool sfrag = false);
 
 // Packed variable-length sequences (batch 1, chunk slots as above, matrix-core
 // path): one recurrence per sequence over its own slots; init / final_state
@@ -261,7 +281,8 @@ hipError_t launch_chunk_scan(const FwdShape& s, ssd_dtype type, bool mfma, const
                              const float* Hst, const uint16_t* Hb, const uint16_t* CB,
                              const float* D, void* y, hipStream_t st, const StageEv& ev = StageEv{});
 // Segmented states (ChainPlan::nseg > 1): the state entering chunk c of
-// segment k >= 1 is Hb_c + exp(cdec_c) Hin_k, Hin [b, nseg, H, P, N] fp32.
+// segment k >= 1 is Hb_c + exp(cdec_c) Hin_k, Hin [b, nseg, H, P * N] fp32,
+// each head's in fragment order (hb_off).
 struct SegStates {
   const float* Hin = nullptr;
   const float* cdec = nullptr;

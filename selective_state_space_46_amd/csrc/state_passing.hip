@@ -36,12 +36,14 @@ constexpr int kDepth = 8;   // chunks of S in flight per thread
 constexpr int kTP = 16;     // p rows per tile
 constexpr int kTN = 64;     // n columns per tile (16 threads x 4)
 
-__device__ __forceinline__ void store_out(float* S, uint16_t* Hb, size_t idx, const f32x4& v) {
+// out_c: fp32 over S at idx ([p][n] rows), or bf16 to Hb at hidx (the
+// fragment order of hb_off; 4 consecutive n stay consecutive there)
+__device__ __forceinline__ void store_out(float* S, uint16_t* Hb, size_t idx, size_t hidx, const f32x4& v) {
   if (Hb) {
     const uint32_t lo = f32x2_to_bf16x2(v.x, v.y);
     const uint32_t hi = f32x2_to_bf16x2(v.z, v.w);
     typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-    *reinterpret_cast<u32x2*>(Hb + idx) = u32x2{lo, hi};
+    *reinterpret_cast<u32x2*>(Hb + hidx) = u32x2{lo, hi};
   } else {
     *reinterpret_cast<f32x4*>(S + idx) = v;
   }
@@ -55,7 +57,7 @@ template <bool VARLEN>
 __global__ __launch_bounds__(kThreads) void state_passing_tiled(
     float* __restrict__ S, uint16_t* __restrict__ Hb, const float* __restrict__ Acs,
     const float* __restrict__ init, float* __restrict__ fin, int H, int P, int N, int Q, int nc,
-    const int* __restrict__ cu, int T) {
+    const int* __restrict__ cu, int T, int sfrag) {
   __shared__ float tile[kTN][kTP + 1];
   const int tpn = (N + kTN - 1) / kTN, tpp = (P + kTP - 1) / kTP;
   int bid = blockIdx.x;
@@ -97,7 +99,11 @@ __global__ __launch_bounds__(kThreads) void state_passing_tiled(
 
   if (active) {
     const size_t cstride = size_t(H) * sbh;  // elements between chunk c and c+1
-    const size_t off0 = ((size_t(brow) * nc + crow) * H + h) * sbh + size_t(p) * N + n;
+    // S in fragment order (sfrag: the segment states) or [p][n] rows
+    const size_t off0 = ((size_t(brow) * nc + crow) * H + h) * sbh + (sfrag ? hb_off(p, n, N) : size_t(p) * N + n);
+    // the same element of Hb (bf16 states, fragment order; needs P, N
+    // multiples of 32, as the matrix-core path has)
+    const size_t hoff0 = ((size_t(brow) * nc + crow) * H + h) * sbh + (Hb ? hb_off(p, n, N) : 0);
     const float* arow = Acs + ((size_t(brow) * H + h) * nc + crow) * Q + (Q - 1);
     f32x4 ring[kDepth];
     float dec[kDepth];
@@ -120,7 +126,7 @@ __global__ __launch_bounds__(kThreads) void state_passing_tiled(
                 reinterpret_cast<const f32x4*>(S + off0 + size_t(c + kDepth) * cstride));
             dec[k] = arow[size_t(c + kDepth) * Q];
           }
-          store_out(S, Hb, off0 + size_t(c) * cstride, cur);
+          store_out(S, Hb, off0 + size_t(c) * cstride, hoff0 + size_t(c) * cstride, cur);
           cur.x = a * cur.x + s.x;
           cur.y = a * cur.y + s.y;
           cur.z = a * cur.z + s.z;
@@ -239,7 +245,7 @@ __global__ __launch_bounds__(kThreads) void state_passing_bwd_tiled(
         const f32x4 ds = rds[k], hc = rhc[k];
         const float a = expf(rdec[k]);
         if (m + kDepth < nc) fetch(k, c - kDepth);
-        if (active) store_out(nullptr, Gb, off0 + size_t(c) * cstride, G);
+        if (active) store_out(nullptr, Gb, 0, off0 + size_t(c) * cstride, G);
         float dot = active ? G.x * hc.x + G.y * hc.y + G.z * hc.z + G.w * hc.w : 0.f;
 #pragma unroll
         for (int off = 32; off >= 1; off >>= 1) dot += __shfl_xor(dot, off, 64);
@@ -288,17 +294,19 @@ hipError_t launch_state_passing_varlen(const FwdShape& s, const float* S, uint16
   // S is only read: the passed states go to Hb
   hipExtLaunchKernelGGL(state_passing_tiled<true>, dim3(unsigned(tiles)), dim3(kThreads), 0, st, ev.start,
                         ev.stop, 0, const_cast<float*>(S), Hb, Acs, init, final_state, s.H, s.P, s.N, s.Q,
-                        s.nc, cu, s.T);
+                        s.nc, cu, s.T, 0);
   return hipGetLastError();
 }
 
 hipError_t launch_state_passing(const FwdShape& s, float* S, uint16_t* Hb, const float* Acs,
-                                const float* init, float* final_state, hipStream_t st, const StageEv& ev) {
+                                const float* init, float* final_state, hipStream_t st, const StageEv& ev,
+                                bool sfrag) {
+  if (sfrag && (s.N % 32 || s.P % 32)) return hipErrorInvalidValue;
   if (s.N % 4 == 0) {
     const long tiles = long(s.b) * s.H * ((s.P + kTP - 1) / kTP) * ((s.N + kTN - 1) / kTN);
     hipExtLaunchKernelGGL(state_passing_tiled<false>, dim3(unsigned(tiles)), dim3(kThreads), 0, st, ev.start,
                           ev.stop, 0, S, Hb, Acs, init, final_state, s.H, s.P, s.N, s.Q, s.nc,
-                          static_cast<const int*>(nullptr), 0);
+                          static_cast<const int*>(nullptr), 0, sfrag ? 1 : 0);
   } else {
     if (Hb) return hipErrorInvalidValue;     // the MFMA path never has N % 4 != 0
     const long total = long(s.b) * s.H * s.N * s.P;

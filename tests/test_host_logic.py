@@ -161,3 +161,54 @@ def test_walk_plan_on_other_unit_counts():
     assert _plan(1, 300, 8, 64, 128, 1, 256, cus=256) == (0, 0)        # too little work even in segments
     assert _plan(1, 131072, 24, 64, 256, 1, 256, cus=256) == (10, 52)
     assert _plan(1, 131072, 24, 64, 256, 1, 256, cus=0) == (0, 0)
+
+
+# ---------------------------------------------------------------- bf16 chunk-entry states in fragment order
+
+def _hb_off(p, n, N):
+    """the fragment-order offset of element (p, n) of a P x N state (restated
+    from the library's layout description)"""
+    return ((((p >> 5) * (N >> 5) + (n >> 5)) * 4 + ((n & 31) >> 3)) * 64 + (p & 31) + 32 * ((n & 7) >> 2)) * 4 + (n & 3)
+
+
+@pytest.mark.parametrize("P,N", [(32, 32), (32, 64), (64, 128), (64, 256), (128, 128), (128, 256)])
+def test_fragment_order_is_a_bijection_with_runs_of_four(P, N):
+    p, n = np.meshgrid(np.arange(P), np.arange(N), indexing="ij")
+    off = _hb_off(p, n, N)
+    assert sorted(off.ravel().tolist()) == list(range(P * N))
+    assert np.all(off[:, 1:][:, (n[0, 1:] % 4) != 0] == off[:, :-1][:, (n[0, 1:] % 4) != 0] + 1)
+
+
+@pytest.mark.parametrize("P,N", [(32, 32), (64, 128), (64, 256), (128, 256)])
+def test_fragment_order_writers_and_readers_agree(P, N):
+    """the walk's stores (accumulator u of column block pj, register run jj,
+    lane), the staging in chunk_scan (16-byte piece e -> rows p, p + 1 at n)
+    and the per-fragment reads (two runs of four) all address hb_off."""
+    # walk: lane L holds p = pj + L % 32, n = 32 nt + 8 jj + 4 (L // 32) + 0..3
+    for pj in range(0, P, 32):
+        for nt in range(N // 32):
+            for jj in range(4):
+                for lane in range(64):
+                    at = (((pj // 32) * (N // 32) + nt) * 4 + jj) * 256 + lane * 4
+                    assert at == _hb_off(pj + lane % 32, 32 * nt + 8 * jj + 4 * (lane // 32), N)
+    # chunk_scan staging: piece e holds runs 2e, 2e + 1
+    for e in range(P * N // 8):
+        r = 2 * e
+        q, blk = r >> 6, (r >> 6) >> 2
+        p = 32 * (blk // (N // 32)) + (r & 31)
+        n = 32 * (blk % (N // 32)) + 8 * (q & 3) + 4 * ((r & 63) >> 5)
+        assert _hb_off(p, n, N) == 8 * e and _hb_off(p + 1, n, N) == 8 * e + 4
+
+
+@pytest.mark.parametrize("P,N", [(32, 32), (64, 128), (64, 256), (128, 256)])
+def test_fragment_order_operand_reads(P, N):
+    """chunk_scan's H^T operand: for lane (l32, g2), column block pb and k step
+    ks it reads n = 16 ks + 8 g2 .. + 7 of row 32 pb + l32 as two runs, at
+    256 g2 + 4 l32 + 256 ((pb N / 32 + ks / 2) 4 + 2 (ks % 2)) and 128 after"""
+    for pb in range(P // 32):
+        for ks in range(N // 16):
+            for lane in range(64):
+                l32, g2 = lane % 32, lane // 32
+                o = 256 * g2 + 4 * l32 + 256 * ((pb * (N // 32) + ks // 2) * 4 + 2 * (ks % 2))
+                p, n = 32 * pb + l32, 16 * ks + 8 * g2
+                assert o == _hb_off(p, n, N) and o + 128 == _hb_off(p, n + 4, N)
