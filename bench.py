@@ -475,6 +475,69 @@ def bench_backward(hip, w, steps=10, warmup=3):
             "workspace_bytes": need}
 
 
+def measured_peaks(hip, iters=2000):
+    """Achievable rates on this device, beside the published ones: the bf16
+    matrix-core probe of the library (ssd_mfma_bf16_probe: 8 independent
+    32x32x16 MFMA chains per wave, 4 work-groups of 4 waves per compute unit)
+    and a 1 GiB device-to-device copy (read + write)."""
+    import torch
+    import selective_state_space_46_amd as ssd
+    stream = torch.cuda.current_stream().cuda_stream
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    wg = 4 * cus
+    out = torch.empty(wg * 256, dtype=torch.float32, device="cuda")
+    L = ssd.lib()
+    for _ in range(2):
+        assert L.ssd_mfma_bf16_probe(wg, iters, out.data_ptr(), stream) == 0
+    torch.cuda.synchronize()
+    a, b = hip.event(), hip.event()
+    hip.record(a, stream)
+    assert L.ssd_mfma_bf16_probe(wg, iters, out.data_ptr(), stream) == 0
+    hip.record(b, stream)
+    torch.cuda.synchronize()
+    ms = hip.ms(a, b)
+    tflops = wg * 4 * iters * 8 * 32768 / (ms * 1e-3) / 1e12
+    src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    hip.record(a, stream)
+    for _ in range(5):
+        dst.copy_(src)
+    hip.record(b, stream)
+    torch.cuda.synchronize()
+    gbs = 5 * 2 * (1 << 30) / (hip.ms(a, b) * 1e-3) / 1e9
+    hip.destroy(a)
+    hip.destroy(b)
+    del src, dst
+    return {"mfma_bf16_TFLOP_per_s": round(tflops, 1), "mfma_bf16_frac_of_published": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+            "copy_GB_per_s": round(gbs, 1), "copy_frac_of_published": round(gbs / HBM_PEAK_GBS, 4),
+            "copy_bytes": 1 << 30, "mfma_probe": f"{wg} work-groups x 4 waves x {iters} x 8 MFMA 32x32x16 bf16"}
+
+
+def decode_probe():
+    """Eight chained decode updates, then three copies of a 256 MiB buffer (the
+    counter calibration of --traffic-probe)."""
+    import torch
+    import selective_state_space_46_amd as ssd
+    dw = workloads.DECODE_B256
+    inp = workloads.make_decode_inputs(workloads.DecodeWorkload(dw.name, dw.batch, dw.nheads, dw.headdim, dw.dstate,
+                                                                dw.ngroups, 8, dw.dtype, seed=dw.seed))
+    state = to_dev(inp["state"], "f32")
+    A, D = to_dev(inp["A"], "f32"), to_dev(inp["D"], "f32")
+    for s in range(8):
+        ssd.ssd_state_update(state, to_dev(inp["xs"][s], "bf16"), to_dev(inp["dts"][s], "bf16"), A,
+                             to_dev(inp["Bs"][s], "bf16"), to_dev(inp["Cs"][s], "bf16"), D)
+    torch.cuda.synchronize()
+    src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log("[bench] decode probe done (8 updates, copy of 268435456 bytes x3)")
+
+
 def traffic_probe(w):
     """Three forward calls, then three copies of a 256 MiB buffer: a plain
     copy kernel that reads and writes exactly 256 MiB, against which the
@@ -512,6 +575,26 @@ def cpu_baseline(w, min_seconds=10.0):
         pass
     return {"value": round(w.tokens * runs / el, 1), "unit": "tokens/s", "cores": n, "kind": "oracle",
             "sample": f"the whole {w.name} forward, {runs} run(s) in {el:.1f} s, fp64, {cpu}"}
+
+
+def extras(hip) -> dict:
+    """The sections beside the headline forward."""
+    out = {}
+    dw = workloads.DECODE_B256
+    log(f"[bench] decode {dw.name}")
+    out["decode"] = bench_decode(hip, dw)
+    log(f"[bench] decode {out['decode']['ms_per_update']:.4f} ms/update")
+    bw = workloads.MAMBA2_130M
+    log(f"[bench] backward {bw.name}")
+    out["backward"] = bench_backward(hip, bw)
+    log(f"[bench]   {out['backward']}")
+    log(f"[bench] packed sequences {workloads.VARLEN_130M.name}")
+    out["varlen"] = bench_varlen(hip, workloads.VARLEN_130M)
+    log(f"[bench]   {out['varlen']}")
+    log("[bench] stages next to the core (conv1d, gated RMSNorm, conv decode update)")
+    out["next_to_core"] = bench_next_to_core(hip)
+    log(f"[bench]   {out['next_to_core']}")
+    return out
 
 
 # which steps of the chunked algorithm each of the library's stage windows
@@ -576,6 +659,12 @@ def main():
     ap.add_argument("--traffic-probe", action="store_true",
                     help="only run a few forward calls and three copies of a 256 MiB buffer (for "
                          "rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs and their calibration)")
+    ap.add_argument("--decode-probe", action="store_true",
+                    help="only run eight decode updates and the calibration copies (for rocprofv3 --pmc)")
+    ap.add_argument("--extras-only", action="store_true",
+                    help="only the sections beside the headline (decode, backward, packed sequences, "
+                         "stages next to the core), one JSON line (for kernel traces of them)")
+    ap.add_argument("--peaks", action="store_true", help="only the measured MFMA and copy rates, one JSON line")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -588,6 +677,15 @@ def main():
     w = workloads.FWD_WORKLOADS[args.workload]
     if args.traffic_probe:
         traffic_probe(w)
+        return
+    if args.decode_probe:
+        decode_probe()
+        return
+    if args.peaks:
+        print(json.dumps(measured_peaks(hip)), flush=True)
+        return
+    if args.extras_only:
+        print(json.dumps(extras(hip)), flush=True)
         return
     log(f"[bench] {w.name}: warmup {args.warmup}, steps {args.steps}")
     r = bench_fwd(hip, w, args.steps, args.warmup)
@@ -625,20 +723,10 @@ def main():
                                "segments_per_row": plan_of(ow), "kernels": ok, "roofline": oroof}
             log(f"[bench]   {rr['ms_per_step']:.4f} ms/step (cold {rc['ms_per_step']:.4f})")
         out["other_workloads"] = others
-        dw = workloads.DECODE_B256
-        log(f"[bench] decode {dw.name}")
-        out["decode"] = bench_decode(hip, dw)
-        log(f"[bench] decode {out['decode']['ms_per_update']:.4f} ms/update")
-        bw = workloads.MAMBA2_130M
-        log(f"[bench] backward {bw.name}")
-        out["backward"] = bench_backward(hip, bw)
-        log(f"[bench]   {out['backward']}")
-        log(f"[bench] packed sequences {workloads.VARLEN_130M.name}")
-        out["varlen"] = bench_varlen(hip, workloads.VARLEN_130M)
-        log(f"[bench]   {out['varlen']}")
-        log("[bench] stages next to the core (conv1d, gated RMSNorm, conv decode update)")
-        out["next_to_core"] = bench_next_to_core(hip)
-        log(f"[bench]   {out['next_to_core']}")
+        out.update(extras(hip))
+        log("[bench] measured peaks")
+        out["measured_peaks"] = measured_peaks(hip)
+        log(f"[bench]   {out['measured_peaks']}")
     if not args.no_cpu_baseline:
         log("[bench] timing the fp64 oracle on host cores")
         out["cpu_baseline"] = cpu_baseline(w)

@@ -28,6 +28,7 @@ import csv
 import glob
 import os
 import re
+import shlex
 import statistics
 import sys
 from collections import defaultdict
@@ -92,32 +93,46 @@ def counters(dirs, match=None):
     return vals
 
 
-def copy_factor(vals, counter: str, copy_bytes: int):
-    """True bytes per counted byte, from the reference device copy of
-    copy_bytes bytes (bench.py --traffic-probe copies it three times after
-    the forward calls): copy_bytes / (KiB counted per copy dispatch * 1024).
-    The copy kernel also serves the small host-to-device uploads of the
-    inputs, so the reference dispatches are the three largest."""
+# counters that measure traffic, calibrated against the reference copy: the
+# copy reads (R) or writes (W) copy_bytes; FETCH_SIZE / WRITE_SIZE count KiB,
+# the TCC_EA0 counters requests
+CALIBRATED = {"FETCH_SIZE": "R", "WRITE_SIZE": "W", "TCC_EA0_RDREQ_DRAM_sum": "R", "TCC_EA0_WRREQ_DRAM_sum": "W",
+              "TCC_EA0_RDREQ_sum": "R", "TCC_EA0_WRREQ_sum": "W"}
+
+
+def copy_value(vals, counter: str):
+    """The counter's value for one reference copy dispatch (bench.py
+    --traffic-probe copies copy_bytes three times after the forward calls;
+    the copy kernel also serves the small host-to-device uploads of the
+    inputs, so the reference dispatches are the three largest)."""
     for name, cs in vals.items():
         if COPY_KERNEL.search(name) and counter in cs:
             top = sorted(cs[counter], reverse=True)[:3]
-            kib = statistics.median(top) if top else 0.0
-            if kib > 0:
-                return copy_bytes / (kib * 1024.0), kib
-    return None, None
+            v = statistics.median(top) if top else 0.0
+            if v > 0:
+                return v
+    return None
+
+
+def copy_factor(vals, counter: str, copy_bytes: int):
+    """True bytes per counted KiB-byte (FETCH_SIZE, WRITE_SIZE: copy_bytes /
+    (KiB counted per copy * 1024)) and the copy's counted KiB."""
+    kib = copy_value(vals, counter)
+    return (copy_bytes / (kib * 1024.0), kib) if kib else (None, None)
 
 
 def counters_cmd(args) -> str:
     vals = counters(args.dirs)
     lines = [f"# {args.title}", "", "commands (repository root, one MI355X, one rocprofv3 --pmc pass each):"]
     lines += [f"  {c}" for c in args.command] + [""]
-    fac = {}
-    for c in ("FETCH_SIZE", "WRITE_SIZE"):
-        f, kib = copy_factor(vals, c, args.copy_bytes)
-        if f:
-            fac[c] = f
-            lines.append(f"calibration: the {args.copy_bytes}-byte device copy reads {c} {kib:.1f} KiB per "
-                         f"dispatch -> {f:.4f} true bytes per counted byte")
+    fac = {}   # true bytes per counted unit
+    for c in CALIBRATED:
+        v = copy_value(vals, c)
+        if v:
+            fac[c] = args.copy_bytes / v
+            lines.append(f"calibration: the {args.copy_bytes}-byte device copy "
+                         f"({'reads' if CALIBRATED[c] == 'R' else 'writes'} that many bytes) counts {c} {v:.1f} per "
+                         f"dispatch -> {fac[c]:.4f} bytes per unit")
     lines.append("")
     for name in sorted(vals):
         if args.match and not re.search(args.match, name):
@@ -130,7 +145,7 @@ def counters_cmd(args) -> str:
             avg = statistics.mean(v)
             extra = ""
             if c in fac:
-                extra = f"   ({avg * 1024 * fac[c] / 1e6:.1f} MB per dispatch, calibrated)"
+                extra = f"   ({avg * fac[c] / 1e6:.1f} MB per dispatch, calibrated)"
             lines.append(f"    {c:<36} {avg:>16.1f} per dispatch ({len(v)} dispatches){extra}")
     return "\n".join(lines) + "\n"
 
@@ -141,12 +156,17 @@ def traffic_cmd(args) -> str:
     wf, wkib = copy_factor(vw, "WRITE_SIZE", args.copy_bytes)
     if not ff or not wf:
         raise SystemExit("no reference copy kernel in the counter output")
-    pick = lambda vals, c: [v for n, cs in vals.items() if re.search(args.kernel, n) for v in cs.get(c, [])]
-    fv, wv = pick(vf, "FETCH_SIZE"), pick(vw, "WRITE_SIZE")
-    if not fv or not wv:
+    # per call: the sum over the matching kernels (a stage may be two
+    # launches) of each one's average per dispatch
+    def per_call(vals, c):
+        ms = [statistics.mean(cs[c]) for n, cs in vals.items() if re.search(args.kernel, n) and cs.get(c)]
+        return sum(ms), len(ms), sum(len(cs.get(c, [])) for n, cs in vals.items() if re.search(args.kernel, n))
+    fk, nk, nd = per_call(vf, "FETCH_SIZE")
+    wk, _, _ = per_call(vw, "WRITE_SIZE")
+    if nk == 0:
         raise SystemExit(f"kernel {args.kernel} not in the counter output")
     names = sorted({short(n, 100) for n in vf if re.search(args.kernel, n)})
-    fk, wk = statistics.mean(fv), statistics.mean(wv)
+    fv = [0] * nd
     hbm = fk * 1024 * ff + wk * 1024 * wf
     lines = [f"# {args.title}", "", "commands (repository root, one MI355X, one pass per counter):"]
     lines += [f"  {c}" for c in args.command] + [""]
@@ -154,9 +174,10 @@ def traffic_cmd(args) -> str:
               f"calibration: a device copy of {args.copy_bytes} bytes reads FETCH_SIZE {fkib:.1f} KiB and "
               f"WRITE_SIZE {wkib:.1f} KiB per dispatch",
               f"  -> fetch factor {ff:.4f}, write factor {wf:.4f} (bytes per counted byte)",
-              "", f"dispatches: {len(fv)}",
+              "", f"dispatches: {nd} ({nk} kernel(s) per call, summed)",
               f"FETCH_SIZE_KiB_per_dispatch: {fk:.1f}", f"WRITE_SIZE_KiB_per_dispatch: {wk:.1f}",
               f"algorithmic_bytes_per_dispatch: {args.alg_bytes}",
+              f"launch_own_bytes_per_dispatch: {args.impl_bytes}",
               f"hbm_bytes_per_dispatch: {hbm:.0f}",
               f"source_digest: {args.source_digest}"]
     return "\n".join(lines) + "\n"
@@ -177,6 +198,7 @@ def main():
     r.add_argument("--kernel", required=True)
     r.add_argument("--workload", required=True)
     r.add_argument("--alg-bytes", type=int, required=True)
+    r.add_argument("--impl-bytes", type=int, default=0)
     r.add_argument("--source-digest", required=True)
     r.add_argument("--copy-bytes", type=int, default=256 << 20)
     for p in (t, c, r):
@@ -192,6 +214,10 @@ def main():
         text = counters_cmd(args)
     else:
         text = traffic_cmd(args)
+    # the summary's own command, in full (its header lists the rocprofv3 runs)
+    own = "python3 profile_summary.py " + " ".join(shlex.quote(a) for a in sys.argv[1:])
+    head, _, rest = text.partition("\n\n")
+    text = head + "\n\nsummarised by:\n  " + own + "\n\n" + rest
     if args.out:
         with open(args.out, "w") as f:
             f.write(text)

@@ -106,6 +106,8 @@ def lib() -> ctypes.CDLL:
     L.ssd_causal_conv1d_update.restype = i32
     L.ssd_chunk_scan_bwd_workspace.argtypes = [i32] * 7
     L.ssd_chunk_scan_bwd_workspace.restype = sz
+    L.ssd_mfma_bf16_probe.argtypes = [i32, i32, vp, vp]
+    L.ssd_mfma_bf16_probe.restype = i32
     L.ssd_chunk_scan_bwd_fused_walks.argtypes = [i32] * 7
     L.ssd_chunk_scan_bwd_fused_walks.restype = i32
     L.ssd_chunk_scan_bwd.argtypes = [vp] * 16 + [i32] * 7 + [vp, sz, vp]

@@ -74,7 +74,7 @@ __device__ __forceinline__ u32x4 seg_combine(const u32x4& v, const float* hin, f
 // VARLEN: chunk rows from the chunk table tab (packed sequences), else the
 // equal-length layout (tab unused). SEG: the segment correction above.
 template <int N, int P, bool HLDS, bool VARLEN, bool SEG, int W>
-__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(W == 8 ? 4 : 1)))
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(W == 8 && P <= 64 ? 4 : 1)))
 void chunk_scan_mfma_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ CB, const uint16_t* __restrict__ Cm,
     const float* __restrict__ Acs, const float* __restrict__ dtq, const uint16_t* __restrict__ Hb,

@@ -23,7 +23,7 @@ def L():
 
 def declared_symbols():
     out = []
-    for h in ("ssd_api.h", "ssd_epilogue.h", "ssd_backward.h"):
+    for h in ("ssd_api.h", "ssd_epilogue.h", "ssd_backward.h", "ssd_measure.h"):
         text = open(os.path.join(ROOT, "include", h)).read()
         out += re.findall(r"SSD_API\s+[\w\s\*]*?\b(ssd_\w+)\s*\(", text)
     return out
@@ -37,7 +37,8 @@ def test_header_declares_the_entry_points():
                                        "ssd_chunk_scan_fwd_varlen", "ssd_chunk_scan_fwd_varlen_workspace",
                                        "ssd_chunk_scan_bwd", "ssd_chunk_scan_bwd_workspace",
                                        "ssd_chunk_scan_fwd_fused_states", "ssd_chunk_scan_bwd_fused_walks",
-                                       "ssd_chunk_scan_fwd_plan", "ssd_chunk_scan_fwd_noalloc"}
+                                       "ssd_chunk_scan_fwd_plan", "ssd_chunk_scan_fwd_noalloc",
+                                       "ssd_mfma_bf16_probe"}
 
 
 def test_fused_states_query_rejects_what_the_forward_rejects():
