@@ -33,11 +33,11 @@
 // operands), writing bf16 when it holds the whole group, else an fp32 partial
 // per slice that a last kernel adds in a fixed order (as dA, dD over chunks).
 //
-// Three kernels: the s side (dx, dB; NB waves, wave i owns 32-token block i
-// as the tokens s and the tiles of l-blocks j >= i), the l side (dC; wave i
-// owns block i as the tokens l and the tiles of s-blocks j <= i) and a last
-// one per (batch, chunk, head) that turns the per-token dots of both into
-// ddt, dA and dD. The s side works in tiles whose lanes are tokens s
+// Two kernels: one work-group per (batch, chunk, group, slice of heads) with
+// the s side (dx, dB; wave i owns 32-token block i as the tokens s and the
+// tiles of l-blocks j >= i) and the l side (dC; wave NB + i owns block i as
+// the tokens l and the tiles of s-blocks j <= i), and a last one per (batch,
+// chunk, head) that turns the per-token dots of both into ddt, dA and dD. The s side works in tiles whose lanes are tokens s
 // (registers over rows l), so its two contractions over l take the tile as
 // the B operand under the k permutation the A operand reproduces with
 // transposed LDS reads (as chunk_scan does); the l side mirrors it with
@@ -52,6 +52,25 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+// Element offset, in a ROWS-swizzled natural tile with RB chunks per row, of
+// lane `lane`'s 8-byte transposed read u (0, 1) of the 32-column block mt:
+// rows 4 (lane/32) + 8 u + (lane%16)/4 of a 32-row block whose k order is the
+// accumulator row order, columns 32 mt + 16 ((lane/16)%2) + 4 (lane%4) .. +3.
+template <int RB>
+__device__ __forceinline__ int tr_off(int lane, int u, int mt) {
+  const int q16 = lane & 15;
+  return lds_off<RB, true>(4 * (lane >> 5) + 8 * u + (q16 >> 2), 32 * mt + 16 * ((lane >> 4) & 1) + 4 * (q16 & 3));
+}
+
+// v, hidden from the optimizer: values derived from it inside a loop are
+// recomputed there instead of being hoisted out of the loop and held in
+// registers for its whole length (the swizzled LDS addresses of the unrolled
+// reads would otherwise take more registers than the MFMA accumulators).
+__device__ __forceinline__ int opaque(int v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
 // Rows 0 .. NROW-1 of a token-major tensor (row stride `stride` elements,
 // RB 16-byte chunks from `col0`) of the chunk, into registers (rows past the
 // valid tokens as zeros) and then into a swizzled natural LDS tile. All
@@ -60,6 +79,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 template <int RB, int NROW, int kThr>
 struct RowStage {
   static constexpr int PER = (NROW * RB + kThr - 1) / kThr;
+  static constexpr bool kEven = NROW * RB % kThr == 0;   // every thread takes PER chunks
   u32x4 v[PER];
   __device__ __forceinline__ void load(const uint16_t* __restrict__ src, long r0, int nv, size_t stride,
                                        size_t col0, int tid) {
@@ -67,7 +87,7 @@ struct RowStage {
     for (int m = 0; m < PER; ++m) {
       const int e = tid + m * kThr;
       const int r = e / RB, cc = e % RB;
-      if (e < NROW * RB)
+      if (kEven || e < NROW * RB)
         v[m] = keep_or_zero(r < nv, load16(src + (r0 + min(r, nv - 1)) * stride + col0 + 8 * cc));
     }
   }
@@ -76,21 +96,10 @@ struct RowStage {
 #pragma unroll
     for (int m = 0; m < PER; ++m) {
       const int e = tid + m * kThr;
-      if (e < NROW * RB) *reinterpret_cast<u32x4*>(&tile[lds_off<RB, ROWS>(e / RB, 8 * (e % RB))]) = v[m];
+      if (kEven || e < NROW * RB) *reinterpret_cast<u32x4*>(&tile[lds_off<RB, ROWS>(e / RB, 8 * (e % RB))]) = v[m];
     }
   }
 };
-
-// The C B^T tiles of one (batch, chunk, group) (ntile x 1024 fp32, lane L's 16
-// values contiguous) into LDS as [tile][4][64 lanes] f32x4, so that lane L
-// reads its 4 quads at consecutive 16-byte slots (no bank conflicts).
-template <int ntile, int kThr>
-__device__ __forceinline__ void stage_tiles(f32x4* sT, const float* __restrict__ src, int tid) {
-  for (int e = tid; e < ntile * 256; e += kThr) {
-    const int t = e / 256, L = (e / 4) % 64, q = e % 4;
-    sT[(t * 4 + q) * 64 + L] = reinterpret_cast<const f32x4*>(src)[e];
-  }
-}
 
 // 16 bytes (8 consecutive columns from col) of row r of a swizzled natural tile
 // (tiles read by rows use the ROWS swizzle of mfma_util.h: 32 lanes reading
@@ -104,21 +113,32 @@ __device__ __forceinline__ u32x2 lds_row8(const uint16_t* tile, int r, int col) 
   return *reinterpret_cast<const u32x2*>(&tile[lds_off<RB, true>(r, col)]);
 }
 
-// s side: dx, dB (summed over the work-group's heads) and, per head and
+// The s and l sides of one (batch, chunk, group) and a slice of the group's
+// heads, in one work-group of 2 NB waves. Waves 0 .. NB-1 take the s side of
+// 32-token block i = wave: dx, dB (summed over the heads) and, per head and
 // token s, B_s . dB'_s (sds), dt_s B_s . (e_{Q-1,s} G_c x_s) (sdst) and
-// dy_s . x_s (sdd), for the last kernel. Wave i owns tokens s of block i and
-// the tiles of l-blocks j >= i. Every operand comes from LDS: B, C and the
-// C B^T tiles once per work-group, and per head x, dy and G_c, loaded by all
-// threads at once.
+// dy_s . x_s (sdd), over the tiles of l-blocks j >= i. Waves NB .. 2NB-1 take
+// the l side of block i = wave - NB: dC (summed over the heads) and, per head
+// and token l, C_l . dC_l (sdl), over the tiles of s-blocks j <= i. Block i
+// has NB - i tiles on the s side and i + 1 on the l side: waves w and w + NB,
+// which the round-robin placement of a work-group's waves puts on one SIMD,
+// hold NB + 1 tiles together on every SIMD. The chunk's B and C rows are
+// staged once per work-group, each head's x, dy, G_c and bf16(H_c) once per
+// head for both sides (all tiles in the ROWS swizzle except bf16(H_c), which
+// is read transposed only); the fp32 C B^T tiles come from memory one tile
+// ahead, and the hi + lo pair of H_c for the l side's dot straight from its
+// fp32 rows.
 template <int N, int P, int NB>
-__global__ __launch_bounds__(64 * NB) void bwd_s_kernel(
+__global__ __launch_bounds__(128 * NB) void bwd_sl_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ Bm, const uint16_t* __restrict__ Cm,
     const uint16_t* __restrict__ dy, const float* __restrict__ Acs, const float* __restrict__ dtq,
-    const float* __restrict__ CBt, const uint16_t* __restrict__ Gb, const float* __restrict__ D,
-    uint16_t* __restrict__ dx, uint16_t* __restrict__ dBo, float* __restrict__ dBs, float* __restrict__ gsds,
-    float* __restrict__ gsdst, float* __restrict__ gsdd, int T, int H, int G, int nc, int nslice) {
+    const float* __restrict__ CBf, const float* __restrict__ CBt, const float* __restrict__ Hst,
+    const uint16_t* __restrict__ Gb, const float* __restrict__ D, uint16_t* __restrict__ dx,
+    uint16_t* __restrict__ dBo, uint16_t* __restrict__ dCo, float* __restrict__ dBs, float* __restrict__ dCs,
+    float* __restrict__ gsds, float* __restrict__ gsdst, float* __restrict__ gsdd, float* __restrict__ gsdl,
+    int T, int H, int G, int nc, int nslice) {
   constexpr int Q = 32 * NB;
-  constexpr int kThr = 64 * NB;
+  constexpr int kThr = 128 * NB;
   constexpr int RBP = P / 8, RBN = N / 8;   // 16-byte chunks per row
   constexpr int ntile = NB * (NB + 1) / 2;
   __shared__ __attribute__((aligned(16))) uint16_t sB[Q * N];
@@ -126,8 +146,8 @@ __global__ __launch_bounds__(64 * NB) void bwd_s_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t sX[Q * P];
   __shared__ __attribute__((aligned(16))) uint16_t sDY[Q * P];
   __shared__ __attribute__((aligned(16))) uint16_t sG[P * N];     // G_c, rows p
-  __shared__ f32x4 sT[ntile * 4 * 64];                            // C B^T tiles, lanes = s
-  __shared__ float sA2[Q], sdt[Q], sEL[Q], sEl[Q];
+  __shared__ __attribute__((aligned(16))) uint16_t sH[P * N];     // bf16(H_c), rows p
+  __shared__ float sA2[Q], sdt[Q], sEL[Q], sEl[Q], sF[Q], sL[Q];
 
   const int id = xcd_swizzle(blockIdx.x, gridDim.x);
   const int sl = id % nslice;
@@ -139,6 +159,8 @@ __global__ __launch_bounds__(64 * NB) void bwd_s_kernel(
   const int h0 = g * (H / G) + sl * hps;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = wave_id();
+  const bool sside = wave < NB;
+  const int i = sside ? wave : wave - NB;       // this wave's 32-token block
   const int l32 = lane & 31, g2 = lane >> 5;
   const long r0 = long(b) * T + long(c) * Q;        // first token row of the chunk
   const int nv = min(Q, T - c * Q);                 // valid tokens
@@ -147,462 +169,347 @@ __global__ __launch_bounds__(64 * NB) void bwd_s_kernel(
     RowStage<RBN, Q, kThr> rb, rc;
     rb.load(Bm, r0, nv, size_t(G) * N, size_t(g) * N, tid);
     rc.load(Cm, r0, nv, size_t(G) * N, size_t(g) * N, tid);
-    rb.template store<true>(sB, tid);              // read by rows
-    rc.template store<false>(sC, tid);             // read transposed only
+    rb.template store<true>(sB, tid);
+    rc.template store<true>(sC, tid);
   }
-  stage_tiles<ntile, kThr>(sT, CBt + ((size_t(b) * nc + c) * G + g) * ntile * 1024, tid);
+  // the chunk's tiles, [tile][4][64 lanes] float4; this lane's first quad
+  const size_t tbase = ((size_t(b) * nc + c) * G + g) * size_t(ntile) * 1024;
+  const f32x4* tS = reinterpret_cast<const f32x4*>(CBt + tbase) + lane;   // lanes = s
+  const f32x4* tL = reinterpret_cast<const f32x4*>(CBf + tbase) + lane;   // lanes = l
 
-  // lane constants of the permuted transposed reads (k = rows of a 32-row
-  // block, in the order of the accumulator rows), per 32-column block
-  const int q16 = lane & 15;
-  const int mcol = 16 * ((lane >> 4) & 1) + 4 * (q16 & 3);
-  auto toff = [&](auto rb, auto rows, int u, int mt) {
-    constexpr int RB = decltype(rb)::value;
-    return lds_off<RB, decltype(rows)::value>(4 * g2 + 8 * u + (q16 >> 2), 32 * mt + mcol);
-  };
-  using RBPc = std::integral_constant<int, RBP>;
-  using RBNc = std::integral_constant<int, RBN>;
-  using kRows = std::integral_constant<bool, true>;
-  using kPlain = std::integral_constant<bool, false>;
 
-  const int i = wave;
-  const int s = 32 * i + l32;
-  const bool sok = s < nv;
-  const long srow = r0 + min(s, nv - 1);
-  const int jend = min(NB, (nv + 31) / 32);   // l-blocks past the valid tokens add nothing
-
-  // dB of this wave's 32 tokens summed over the work-group's heads:
-  // transposed, rows n, lane = s
+  // dB (s side) or dC (l side) of this wave's 32 tokens summed over the
+  // work-group's heads: transposed, rows n, lane = token
   f32x16 accT[N / 32];
 #pragma unroll
   for (int nt = 0; nt < N / 32; ++nt) accT[nt] = zero16();
 
-  // A head's operands: its decay tables (thread t < Q takes token t), x and
-  // dy rows and G_c. All loads of a head are issued together; with few
-  // registers per thread (kAhead) the next head's loads are issued right after
-  // this head's staging, so they run under this head's compute.
-  RowStage<RBP, Q, kThr> rx, rd;
-  RowStage<RBN, P, kThr> rg;
-  constexpr bool kAhead = 2 * RowStage<RBP, Q, kThr>::PER + RowStage<RBN, P, kThr>::PER <= 12;
-  float ta = 0.f, tb = 0.f, tc = 0.f, td = 0.f;
-  auto fetch = [&](int h) {
+  for (int hk = 0; hk < hps; ++hk) {
+    const int h = h0 + hk;
     const size_t arow = ((size_t(b) * H + h) * nc + c) * Q;
+    const size_t sbase = ((size_t(b) * nc + c) * H + h) * size_t(P) * N;
+    // lane constants, recomputed per head (see opaque)
+    const int tid = opaque(threadIdx.x), lane = tid & 63;
+    const int l32 = lane & 31, g2 = lane >> 5;
+    __syncthreads();   // the previous head's tiles and tables are consumed
+    {
+    // the head's operands: its decay tables (thread t < Q takes token t), x
+    // and dy rows, G_c and H_c, loaded by all threads together
+    constexpr int PH = (P * RBN + kThr - 1) / kThr;
+    constexpr bool kHEven = P * RBN % kThr == 0;
+    RowStage<RBP, Q, kThr> rx, rd;
+    RowStage<RBN, P, kThr> rg;
+    f32x4 hv[PH][2];
+    float ta = 0.f, tbs = 0.f, tbl = 0.f, tc = 0.f, td = 0.f;
     if (tid < Q) {
       ta = Acs[arow + tid];
-      tb = Acs[arow + (tid & ~31)];
+      tbs = Acs[arow + (tid & ~31)];
+      tbl = Acs[arow + (tid | 31)];
       tc = Acs[arow + Q - 1];
       td = dtq[arow + tid];
     }
     rx.load(x, r0, nv, size_t(H) * P, size_t(h) * P, tid);
     rd.load(dy, r0, nv, size_t(H) * P, size_t(h) * P, tid);
-    if constexpr (kAhead)
-      rg.load(Gb + ((size_t(b) * nc + c) * H + h) * size_t(P) * N, 0, P, N, 0, tid);   // G_c rows p
-  };
-  if (hps > 0) fetch(h0);
-
-  for (int hk = 0; hk < hps; ++hk) {
-    const int h = h0 + hk;
-    const size_t arow = ((size_t(b) * H + h) * nc + c) * Q;
-    const size_t sbase = ((size_t(b) * nc + c) * H + h) * size_t(P) * N;
-    __syncthreads();   // the previous head's tiles and tables are consumed
-    if (tid < Q) {
-      const float a2 = ta * kLog2e;
-      sA2[tid] = a2;
-      sdt[tid] = td;
-      sEL[tid] = __builtin_amdgcn_exp2f(a2 - tb * kLog2e);    // <= 1
-      sEl[tid] = __builtin_amdgcn_exp2f(tc * kLog2e - a2);    // <= 1
-    }
-    rx.template store<true>(sX, tid);
-    rd.template store<true>(sDY, tid);             // read by rows and transposed
-    if constexpr (!kAhead) rg.load(Gb + sbase, 0, P, N, 0, tid);
-    rg.template store<true>(sG, tid);              // read by rows and transposed
-    __syncthreads();
-    if (kAhead && hk + 1 < hps) fetch(h + 1);
-
-    const float dts = sdt[s], a2s = sA2[s], els = sEl[s];
-    u32x4 xr[P / 16];
-#pragma unroll
-    for (int kk = 0; kk < P / 16; ++kk) xr[kk] = lds_row16<RBP>(sX, s, 16 * kk + 8 * g2);
-
-    // state terms. dx^T(p, s) = e_{Q-1,s} dt_s sum_n G(n, p) B_s[n]; the same
-    // product dotted with x_s is this head's B_s . (e_{Q-1,s} G_c x_s)
-    f32x16 adx[P / 32];
-#pragma unroll
-    for (int pt = 0; pt < P / 32; ++pt) {
-      adx[pt] = zero16();
-#pragma unroll
-      for (int kk = 0; kk < N / 16; ++kk)
-        adx[pt] = mfma32x32x16(lds_row16<RBN>(sG, 32 * pt + l32, 16 * kk + 8 * g2),
-                               lds_row16<RBN>(sB, s, 16 * kk + 8 * g2), adx[pt]);
-    }
-    float bdst = 0.f;
-#pragma unroll
-    for (int pt = 0; pt < P / 32; ++pt)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const u32x2 xv = lds_row8<RBP>(sX, s, 32 * pt + 8 * q + 4 * g2);
-        bdst += adx[pt][4 * q] * bf16_lo(xv[0]) + adx[pt][4 * q + 1] * bf16_hi(xv[0]) +
-                adx[pt][4 * q + 2] * bf16_lo(xv[1]) + adx[pt][4 * q + 3] * bf16_hi(xv[1]);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) adx[pt][4 * q + r] *= dts * els;
-      }
-    bdst = els * (bdst + __shfl_xor(bdst, 32, 64));
-    // dB^T(n, s) += sum_p G(n, p) (dt_s e_{Q-1,s} x_s[p])   (G rows n: transposed reads)
-    {
-      u32x4 xs[P / 16];
-      const float f = dts * els;
-#pragma unroll
-      for (int kk = 0; kk < P / 16; ++kk)
-#pragma unroll
-        for (int w = 0; w < 4; ++w) xs[kk][w] = pack_bf16x2(bf16_lo(xr[kk][w]) * f, bf16_hi(xr[kk][w]) * f);
-#pragma unroll
-      for (int nt = 0; nt < N / 32; ++nt)
-#pragma unroll
-        for (int kk = 0; kk < P / 16; ++kk) {
-          const int kb = 16 * kk + 8 * g2;
-          accT[nt] = mfma32x32x16(frag_tr<RBN, true>(sG, kb, kb + 4, 32 * nt, lane), xs[kk], accT[nt]);
-        }
-    }
-
-    // intra-chunk terms, one 32 x 32 tile (rows l of block j, lanes s) at a time
-    float bd = 0.f;                              // this head's sum_l W_ls
-    for (int j = i; j < jend; ++j) {
-      const f32x4* tsrc = sT + (j * (j + 1) / 2 + i) * 256 + lane;
-      const f32x4 cb4[4] = {tsrc[0], tsrc[64], tsrc[128], tsrc[192]};   // C_l . B_s, rows l in accumulator order
-      f32x16 accS = zero16();
-#pragma unroll
-      for (int kk = 0; kk < P / 16; ++kk)
-        accS = mfma32x32x16(lds_row16<RBP>(sDY, 32 * j + l32, 16 * kk + 8 * g2), xr[kk], accS);   // Sxy^T
-      const bool diag = j == i;
-      const float lf = diag ? 0.f : __builtin_amdgcn_exp2f(sA2[32 * j] - a2s);
-      uint32_t zw[8], mw[8];
-#pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        const float cb_lo = cb4[m / 2][2 * (m % 2)], cb_hi = cb4[m / 2][2 * (m % 2) + 1];
-        float e2[2];
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int r = 2 * m + u;
-          const int l = 32 * j + 8 * (r / 4) + 4 * g2 + (r % 4);
-          if (diag) {
-            const float ex = __builtin_amdgcn_exp2f(fminf(sA2[l] - a2s, 0.f));
-            e2[u] = l >= s ? ex : 0.f;
-          } else {
-            e2[u] = sEL[l] * lf;
-          }
-        }
-        const float z0 = e2[0] * accS[2 * m], z1 = e2[1] * accS[2 * m + 1];
-        bd += z0 * cb_lo + z1 * cb_hi;                              // column sum of W
-        zw[m] = pack_bf16x2(dts * z0, dts * z1);
-        mw[m] = pack_bf16x2(e2[0] * dts * cb_lo, e2[1] * dts * cb_hi);
-      }
-      const u32x4 zga = u32x4{zw[0], zw[1], zw[2], zw[3]}, zgb = u32x4{zw[4], zw[5], zw[6], zw[7]};
-      const u32x4 mga = u32x4{mw[0], mw[1], mw[2], mw[3]}, mgb = u32x4{mw[4], mw[5], mw[6], mw[7]};
-      // dx^T(p, s) += sum_l dy^T(p, l) M(l, s)
-      const int joP = 32 * j * P;
-#pragma unroll
-      for (int pt = 0; pt < P / 32; ++pt) {
-        const int o0 = toff(RBPc{}, kRows{}, 0, pt) + joP, o1 = toff(RBPc{}, kRows{}, 1, pt) + joP;
-        const u32x2 a0 = lds_read_tr16(sDY, o0), a1 = lds_read_tr16(sDY, o1);
-        const u32x2 b0 = lds_read_tr16(sDY, o0 + 16 * P), b1 = lds_read_tr16(sDY, o1 + 16 * P);
-        adx[pt] = mfma32x32x16(u32x4{a0[0], a0[1], a1[0], a1[1]}, mga, adx[pt]);
-        adx[pt] = mfma32x32x16(u32x4{b0[0], b0[1], b1[0], b1[1]}, mgb, adx[pt]);
-      }
-      // dB^T(n, s) += sum_l C^T(n, l) dt_s Z(l, s)
-      const int joN = 32 * j * N;
-#pragma unroll
-      for (int nt = 0; nt < N / 32; ++nt) {
-        const int o0 = toff(RBNc{}, kPlain{}, 0, nt) + joN, o1 = toff(RBNc{}, kPlain{}, 1, nt) + joN;
-        const u32x2 a0 = lds_read_tr16(sC, o0), a1 = lds_read_tr16(sC, o1);
-        const u32x2 b0 = lds_read_tr16(sC, o0 + 16 * N), b1 = lds_read_tr16(sC, o1 + 16 * N);
-        accT[nt] = mfma32x32x16(u32x4{a0[0], a0[1], a1[0], a1[1]}, zga, accT[nt]);
-        accT[nt] = mfma32x32x16(u32x4{b0[0], b0[1], b1[0], b1[1]}, zgb, accT[nt]);
-      }
-    }
-
-    // dx = ... + D dy (rows p = 32 pt + 8 q + 4 g2 + 0..3 of lane s), stored as bf16
-    const float Dh = D ? D[h] : 0.f;
-#pragma unroll
-    for (int pt = 0; pt < P / 32; ++pt)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int p = 32 * pt + 8 * q + 4 * g2;
-        const u32x2 dv = lds_row8<RBP>(sDY, s, p);
-        const float v0 = adx[pt][4 * q] + Dh * bf16_lo(dv[0]), v1 = adx[pt][4 * q + 1] + Dh * bf16_hi(dv[0]);
-        const float v2 = adx[pt][4 * q + 2] + Dh * bf16_lo(dv[1]), v3 = adx[pt][4 * q + 3] + Dh * bf16_hi(dv[1]);
-        if (sok)
-          *reinterpret_cast<u32x2*>(dx + (srow * H + h) * size_t(P) + p) =
-              u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
-      }
-    bd += __shfl_xor(bd, 32, 64);
-    // dy_s . x_s (for dD)
-    float dd = 0.f;
-#pragma unroll
-    for (int kk = 0; kk < P / 16; ++kk) {
-      const u32x4 dv = lds_row16<RBP>(sDY, s, 16 * kk + 8 * g2);
-#pragma unroll
-      for (int w = 0; w < 4; ++w)
-        dd += bf16_lo(dv[w]) * bf16_lo(xr[kk][w]) + bf16_hi(dv[w]) * bf16_hi(xr[kk][w]);
-    }
-    dd += __shfl_xor(dd, 32, 64);
-    if (g2 == 0) {
-      gsds[arow + s] = sok ? bd + bdst : 0.f;     // B_s . dB'_s of this head
-      gsdst[arow + s] = sok ? dts * bdst : 0.f;
-      gsdd[arow + s] = dd;
-    }
-  }
-
-  // ---- the work-group's sum over its heads: bf16 when it holds all heads
-  //      of the group, else an fp32 partial of its slice
-  if (sok) {
-    const size_t row = size_t(srow) * G + g;
-    const long rows = long(gridDim.x / nslice / G / nc) * T;   // batch rows x tokens
-#pragma unroll
-    for (int nt = 0; nt < N / 32; ++nt)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int n = 32 * nt + 8 * q + 4 * g2;
-        const f32x4 v4 = f32x4{accT[nt][4 * q], accT[nt][4 * q + 1], accT[nt][4 * q + 2], accT[nt][4 * q + 3]};
-        if (nslice == 1)
-          *reinterpret_cast<u32x2*>(dBo + row * N + n) = u32x2{pack_bf16x2(v4[0], v4[1]), pack_bf16x2(v4[2], v4[3])};
-        else
-          *reinterpret_cast<f32x4*>(dBs + (size_t(sl) * rows * G + row) * N + n) = v4;
-      }
-  }
-}
-
-// l side: dC (summed over the work-group's heads) and, per head and token l,
-// C_l . dC_l (sdl) for the last kernel. Wave i owns tokens l of block i and
-// the tiles of s-blocks j <= i. Operands from LDS as on the s side (B, C and
-// the tiles once; x, dy and bf16(H_c) per head; the hi + lo pair of H_c for
-// the dot straight from its fp32 rows).
-template <int N, int P, int NB>
-__global__ __launch_bounds__(64 * NB) void bwd_l_kernel(
-    const uint16_t* __restrict__ x, const uint16_t* __restrict__ Bm, const uint16_t* __restrict__ Cm,
-    const uint16_t* __restrict__ dy, const float* __restrict__ Acs, const float* __restrict__ dtq,
-    const float* __restrict__ CBf, const float* __restrict__ Hst, uint16_t* __restrict__ dCo,
-    float* __restrict__ dCs, float* __restrict__ gsdl, int T, int H, int G, int nc, int nslice) {
-  constexpr int Q = 32 * NB;
-  constexpr int kThr = 64 * NB;
-  constexpr int RBP = P / 8, RBN = N / 8;   // 16-byte chunks per row
-  constexpr int ntile = NB * (NB + 1) / 2;
-  __shared__ __attribute__((aligned(16))) uint16_t sB[Q * N];
-  __shared__ __attribute__((aligned(16))) uint16_t sC[Q * N];
-  __shared__ __attribute__((aligned(16))) uint16_t sX[Q * P];
-  __shared__ __attribute__((aligned(16))) uint16_t sDY[Q * P];
-  __shared__ __attribute__((aligned(16))) uint16_t sH[P * N];     // bf16(H_c), rows p
-  __shared__ f32x4 sT[ntile * 4 * 64];                            // C B^T tiles, lanes = l
-  __shared__ float sA2[Q], sF[Q], sL[Q];
-
-  const int id = xcd_swizzle(blockIdx.x, gridDim.x);
-  const int sl = id % nslice;
-  const int rest = id / nslice;
-  const int g = rest % G;
-  const int bc = rest / G;
-  const int c = bc % nc, b = bc / nc;
-  const int hps = H / G / nslice;               // heads of this work-group
-  const int h0 = g * (H / G) + sl * hps;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = wave_id();
-  const int l32 = lane & 31, g2 = lane >> 5;
-  const long r0 = long(b) * T + long(c) * Q;        // first token row of the chunk
-  const int nv = min(Q, T - c * Q);                 // valid tokens
-
-  {
-    RowStage<RBN, Q, kThr> rb, rc;
-    rb.load(Bm, r0, nv, size_t(G) * N, size_t(g) * N, tid);
-    rc.load(Cm, r0, nv, size_t(G) * N, size_t(g) * N, tid);
-    rb.template store<false>(sB, tid);             // read transposed only
-    rc.template store<true>(sC, tid);              // read by rows
-  }
-  stage_tiles<ntile, kThr>(sT, CBf + ((size_t(b) * nc + c) * G + g) * ntile * 1024, tid);
-
-  const int q16 = lane & 15;
-  const int mcol = 16 * ((lane >> 4) & 1) + 4 * (q16 & 3);
-  auto toff = [&](auto rb, int u, int mt) {
-    constexpr int RB = decltype(rb)::value;
-    return lds_off<RB>(4 * g2 + 8 * u + (q16 >> 2), 32 * mt + mcol);   // sB: plain swizzle
-  };
-  using RBNc = std::integral_constant<int, RBN>;
-
-  const int i = wave;
-  const int l = 32 * i + l32;
-  const bool lok = l < nv;
-  const long lrow = r0 + min(l, nv - 1);
-  const int jlast = 32 * i < nv ? i : -1;       // no tiles when the whole block is past the tokens
-
-  // dC of this wave's 32 tokens summed over the work-group's heads:
-  // transposed, rows n, lane = l
-  f32x16 accT[N / 32];
-#pragma unroll
-  for (int nt = 0; nt < N / 32; ++nt) accT[nt] = zero16();
-
-  // A head's operands (tables, x and dy rows, H_c), loaded together; with
-  // few registers per thread (kAhead) the next head's loads are issued right
-  // after this head's staging, under this head's compute.
-  constexpr int PH = (P * RBN + kThr - 1) / kThr;
-  RowStage<RBP, Q, kThr> rx, rd;
-  f32x4 hv[PH][2];
-  constexpr bool kAhead = 2 * RowStage<RBP, Q, kThr>::PER + 2 * PH <= 16;
-  float ta = 0.f, tb = 0.f, td = 0.f;
-  auto fetch_h = [&](size_t sbase) {
+    rg.load(Gb + sbase, 0, P, N, 0, tid);
 #pragma unroll
     for (int m = 0; m < PH; ++m) {
       const int e = tid + m * kThr;
-      if (e < P * RBN) {
+      if (kHEven || e < P * RBN) {
         const float* hr = Hst + sbase + size_t(e / RBN) * N + 8 * (e % RBN);
         hv[m][0] = *reinterpret_cast<const f32x4*>(hr);
         hv[m][1] = *reinterpret_cast<const f32x4*>(hr + 4);
       }
     }
-  };
-  auto fetch = [&](int h) {
-    const size_t arow = ((size_t(b) * H + h) * nc + c) * Q;
-    if (tid < Q) {
-      ta = Acs[arow + tid];
-      tb = Acs[arow + (tid | 31)];
-      td = dtq[arow + tid];
-    }
-    rx.load(x, r0, nv, size_t(H) * P, size_t(h) * P, tid);
-    rd.load(dy, r0, nv, size_t(H) * P, size_t(h) * P, tid);
-    if constexpr (kAhead) fetch_h(((size_t(b) * nc + c) * H + h) * size_t(P) * N);
-  };
-  if (hps > 0) fetch(h0);
-
-  for (int hk = 0; hk < hps; ++hk) {
-    const int h = h0 + hk;
-    const size_t arow = ((size_t(b) * H + h) * nc + c) * Q;
-    const size_t sbase = ((size_t(b) * nc + c) * H + h) * size_t(P) * N;
-    __syncthreads();   // the previous head's tiles and tables are consumed
     if (tid < Q) {
       const float a2 = ta * kLog2e;
       sA2[tid] = a2;
-      sF[tid] = __builtin_amdgcn_exp2f(tb * kLog2e - a2) * td;   // <= dt
-      sL[tid] = __builtin_amdgcn_logf(td) - a2;                    // -inf where dt = 0
+      sdt[tid] = td;
+      sEL[tid] = __builtin_amdgcn_exp2f(a2 - tbs * kLog2e);         // <= 1
+      sEl[tid] = __builtin_amdgcn_exp2f(tc * kLog2e - a2);          // <= 1
+      sF[tid] = __builtin_amdgcn_exp2f(tbl * kLog2e - a2) * td;     // <= dt
+      sL[tid] = __builtin_amdgcn_logf(td) - a2;                     // -inf where dt = 0
     }
     rx.template store<true>(sX, tid);
     rd.template store<true>(sDY, tid);
-    if constexpr (!kAhead) fetch_h(sbase);
+    rg.template store<true>(sG, tid);
 #pragma unroll
     for (int m = 0; m < PH; ++m) {
       const int e = tid + m * kThr;
-      if (e < P * RBN)
+      if (kHEven || e < P * RBN)
         *reinterpret_cast<u32x4*>(&sH[lds_off<RBN>(e / RBN, 8 * (e % RBN))]) =
             u32x4{pack_bf16x2(hv[m][0][0], hv[m][0][1]), pack_bf16x2(hv[m][0][2], hv[m][0][3]),
                   pack_bf16x2(hv[m][1][0], hv[m][1][1]), pack_bf16x2(hv[m][1][2], hv[m][1][3])};
     }
-    __syncthreads();
-    if (kAhead && hk + 1 < hps) fetch(h + 1);
-
-    const float a2l = sA2[l];
-    const float el = __builtin_amdgcn_exp2f(a2l);
-    u32x4 dyr[P / 16];
-#pragma unroll
-    for (int kk = 0; kk < P / 16; ++kk) dyr[kk] = lds_row16<RBP>(sDY, l, 16 * kk + 8 * g2);
-    // state term of dC: dC^T(n, l) += sum_p H(n, p) (exp(Acs_l) dy_l[p])
-    {
-      u32x4 dys[P / 16];
-#pragma unroll
-      for (int kk = 0; kk < P / 16; ++kk)
-#pragma unroll
-        for (int w = 0; w < 4; ++w) dys[kk][w] = pack_bf16x2(bf16_lo(dyr[kk][w]) * el, bf16_hi(dyr[kk][w]) * el);
-#pragma unroll
-      for (int nt = 0; nt < N / 32; ++nt)
-#pragma unroll
-        for (int kk = 0; kk < P / 16; ++kk) {
-          const int kb = 16 * kk + 8 * g2;
-          accT[nt] = mfma32x32x16(frag_tr<RBN>(sH, kb, kb + 4, 32 * nt, lane), dys[kk], accT[nt]);
-        }
     }
-    // this head's C_l . (state term of dC_l) = exp(Acs_l) dy_l . (H^T C_l),
-    // with H as hi + lo (from its fp32 rows p): y^T(p, l) = sum_n H(n, p) C_l[n]
-    float cd = 0.f;
-    {
-      f32x16 yst[P / 32];
+    __syncthreads();
+
+    if (sside) {
+      // ------------------------------------------------------------ s side
+      const int s = 32 * i + l32;
+      const bool sok = s < nv;
+      const long srow = r0 + min(s, nv - 1);
+      const int jend = min(NB, (nv + 31) / 32);   // l-blocks past the valid tokens add nothing
+
+      const float dts = sdt[s], a2s = sA2[s], els = sEl[s];
+      u32x4 xr[P / 16];
+#pragma unroll
+      for (int kk = 0; kk < P / 16; ++kk) xr[kk] = lds_row16<RBP>(sX, s, 16 * kk + 8 * g2);
+
+      // state terms. dx^T(p, s) = e_{Q-1,s} dt_s sum_n G(n, p) B_s[n]; the same
+      // product dotted with x_s is this head's B_s . (e_{Q-1,s} G_c x_s)
+      f32x16 adx[P / 32];
 #pragma unroll
       for (int pt = 0; pt < P / 32; ++pt) {
-        f32x4 hv[N / 16][2];
+        adx[pt] = zero16();
 #pragma unroll
-        for (int kk = 0; kk < N / 16; ++kk) {
-          const float* hr = Hst + sbase + size_t(32 * pt + l32) * N + 16 * kk + 8 * g2;
-          hv[kk][0] = *reinterpret_cast<const f32x4*>(hr);
-          hv[kk][1] = *reinterpret_cast<const f32x4*>(hr + 4);
-        }
-        yst[pt] = zero16();
-#pragma unroll
-        for (int kk = 0; kk < N / 16; ++kk) {
-          const u32x4 cl = lds_row16<RBN>(sC, l, 16 * kk + 8 * g2);
-          u32x4 hi, lo;
-#pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            const float v0 = hv[kk][w / 2][2 * (w % 2)], v1 = hv[kk][w / 2][2 * (w % 2) + 1];
-            hi[w] = pack_bf16x2(v0, v1);
-            lo[w] = pack_bf16x2(v0 - bf16_lo(hi[w]), v1 - bf16_hi(hi[w]));
-          }
-          yst[pt] = mfma32x32x16(hi, cl, yst[pt]);
-          yst[pt] = mfma32x32x16(lo, cl, yst[pt]);
-        }
+        for (int kk = 0; kk < N / 16; ++kk)
+          adx[pt] = mfma32x32x16(lds_row16<RBN>(sG, 32 * pt + l32, 16 * kk + 8 * g2),
+                                 lds_row16<RBN>(sB, s, 16 * kk + 8 * g2), adx[pt]);
       }
+      float bdst = 0.f;
 #pragma unroll
       for (int pt = 0; pt < P / 32; ++pt)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const u32x2 dv = lds_row8<RBP>(sDY, l, 32 * pt + 8 * q + 4 * g2);
-          cd += yst[pt][4 * q] * bf16_lo(dv[0]) + yst[pt][4 * q + 1] * bf16_hi(dv[0]) +
-                yst[pt][4 * q + 2] * bf16_lo(dv[1]) + yst[pt][4 * q + 3] * bf16_hi(dv[1]);
+          const u32x2 xv = lds_row8<RBP>(sX, s, 32 * pt + 8 * q + 4 * g2);
+          bdst += adx[pt][4 * q] * bf16_lo(xv[0]) + adx[pt][4 * q + 1] * bf16_hi(xv[0]) +
+                  adx[pt][4 * q + 2] * bf16_lo(xv[1]) + adx[pt][4 * q + 3] * bf16_hi(xv[1]);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) adx[pt][4 * q + r] *= dts * els;
         }
-      cd *= el;
-    }
-    // intra-chunk terms, tiles of rows s (block j) and lanes l
-    for (int j = 0; j <= jlast; ++j) {
-      // C B^T in the forward orientation (rows s, lane l)
-      const f32x4* fsrc = sT + (i * (i + 1) / 2 + j) * 256 + lane;
-      const f32x4 cf4[4] = {fsrc[0], fsrc[64], fsrc[128], fsrc[192]};
-      f32x16 accS = zero16();
+      bdst = els * (bdst + __shfl_xor(bdst, 32, 64));
+      // dB^T(n, s) += sum_p G(n, p) (dt_s e_{Q-1,s} x_s[p])   (G rows n: transposed reads)
+      {
+        u32x4 xs[P / 16];
+        const float f = dts * els;
 #pragma unroll
-      for (int kk = 0; kk < P / 16; ++kk)
-        accS = mfma32x32x16(lds_row16<RBP>(sX, 32 * j + l32, 16 * kk + 8 * g2), dyr[kk], accS);   // Sxy
-      const bool diag = j == i;
-      const float lfac = diag ? 0.f : __builtin_amdgcn_exp2f(a2l - sA2[32 * j + 31]);
-      uint32_t zw[8];
+        for (int kk = 0; kk < P / 16; ++kk)
 #pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        const float cf_lo = cf4[m / 2][2 * (m % 2)], cf_hi = cf4[m / 2][2 * (m % 2) + 1];
-        float z2[2];
+          for (int w = 0; w < 4; ++w) xs[kk][w] = pack_bf16x2(bf16_lo(xr[kk][w]) * f, bf16_hi(xr[kk][w]) * f);
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int r = 2 * m + u;
-          const int sr = 32 * j + 8 * (r / 4) + 4 * g2 + (r % 4);
-          float dec;
-          if (diag) {
-            const float pv = __builtin_amdgcn_exp2f(a2l + sL[sr]);   // exp(Acs_l - Acs_s) dt_s
-            dec = sr <= l ? pv : 0.f;
-          } else {
-            dec = lfac * sF[sr];
+        for (int nt = 0; nt < N / 32; ++nt)
+#pragma unroll
+          for (int kk = 0; kk < P / 16; ++kk) {
+            const int kb = 16 * kk + 8 * g2;
+            accT[nt] = mfma32x32x16(frag_tr<RBN, true>(sG, kb, kb + 4, 32 * nt, lane), xs[kk], accT[nt]);
           }
-          z2[u] = dec * accS[r];
-        }
-        cd += z2[0] * cf_lo + z2[1] * cf_hi;                          // row sum of dt W
-        zw[m] = pack_bf16x2(z2[0], z2[1]);
       }
-      const u32x4 zga = u32x4{zw[0], zw[1], zw[2], zw[3]}, zgb = u32x4{zw[4], zw[5], zw[6], zw[7]};
-      const int joN = 32 * j * N;
+
+      // dy_s . x_s (for dD)
+      float dd = 0.f;
 #pragma unroll
-      for (int nt = 0; nt < N / 32; ++nt) {
-        const int o0 = toff(RBNc{}, 0, nt) + joN, o1 = toff(RBNc{}, 1, nt) + joN;
-        const u32x2 a0 = lds_read_tr16(sB, o0), a1 = lds_read_tr16(sB, o1);
-        const u32x2 b0 = lds_read_tr16(sB, o0 + 16 * N), b1 = lds_read_tr16(sB, o1 + 16 * N);
-        accT[nt] = mfma32x32x16(u32x4{a0[0], a0[1], a1[0], a1[1]}, zga, accT[nt]);
-        accT[nt] = mfma32x32x16(u32x4{b0[0], b0[1], b1[0], b1[1]}, zgb, accT[nt]);
+      for (int kk = 0; kk < P / 16; ++kk) {
+        const u32x4 dv = lds_row16<RBP>(sDY, s, 16 * kk + 8 * g2);
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+          dd += bf16_lo(dv[w]) * bf16_lo(xr[kk][w]) + bf16_hi(dv[w]) * bf16_hi(xr[kk][w]);
       }
+      dd += __shfl_xor(dd, 32, 64);
+      // intra-chunk terms, one 32 x 32 tile (rows l of block j, lanes s) at a time
+      float bd = 0.f;                              // this head's sum_l W_ls
+      // one tile; the diagonal one (j == i, masked) apart from the others
+      auto tile = [&](int j, auto diag_c) {
+        constexpr bool diag = decltype(diag_c)::value;
+        const int ln = opaque(lane);                 // per-tile addresses (see opaque)
+        // C_l . B_s, rows l in accumulator order (from L2; used after the Sxy products)
+        const f32x4* tp = tS + (j * (j + 1) / 2 + i) * 256;
+        const f32x4 cb4[4] = {tp[0], tp[64], tp[128], tp[192]};
+        f32x16 accS = zero16();
+#pragma unroll
+        for (int kk = 0; kk < P / 16; ++kk)
+          accS = mfma32x32x16(lds_row16<RBP>(sDY, 32 * j + (ln & 31), 16 * kk + 8 * (ln >> 5)),
+                              lds_row16<RBP>(sX, 32 * i + (ln & 31), 16 * kk + 8 * (ln >> 5)), accS);   // Sxy^T
+        const float lf = diag ? 0.f : __builtin_amdgcn_exp2f(sA2[32 * j] - a2s);
+        uint32_t zw[8], mw[8];
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+          const float cb_lo = cb4[m / 2][2 * (m % 2)], cb_hi = cb4[m / 2][2 * (m % 2) + 1];
+          float e2[2];
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const int r = 2 * m + u;
+            const int l = 32 * j + 8 * (r / 4) + 4 * g2 + (r % 4);
+            if constexpr (diag) {
+              const float ex = __builtin_amdgcn_exp2f(fminf(sA2[l] - a2s, 0.f));
+              e2[u] = l >= s ? ex : 0.f;
+            } else {
+              e2[u] = sEL[l] * lf;
+            }
+          }
+          const float z0 = e2[0] * accS[2 * m], z1 = e2[1] * accS[2 * m + 1];
+          bd += z0 * cb_lo + z1 * cb_hi;                              // column sum of W
+          zw[m] = pack_bf16x2(dts * z0, dts * z1);
+          mw[m] = pack_bf16x2(e2[0] * dts * cb_lo, e2[1] * dts * cb_hi);
+        }
+        const u32x4 zga = u32x4{zw[0], zw[1], zw[2], zw[3]}, zgb = u32x4{zw[4], zw[5], zw[6], zw[7]};
+        const u32x4 mga = u32x4{mw[0], mw[1], mw[2], mw[3]}, mgb = u32x4{mw[4], mw[5], mw[6], mw[7]};
+        // dx^T(p, s) += sum_l dy^T(p, l) M(l, s)
+        const int joP = 32 * j * P;
+#pragma unroll
+        for (int pt = 0; pt < P / 32; ++pt) {
+          const int o0 = tr_off<RBP>(ln, 0, pt) + joP, o1 = tr_off<RBP>(ln, 1, pt) + joP;
+          const u32x2 a0 = lds_read_tr16(sDY, o0), a1 = lds_read_tr16(sDY, o1);
+          const u32x2 b0 = lds_read_tr16(sDY, o0 + 16 * P), b1 = lds_read_tr16(sDY, o1 + 16 * P);
+          adx[pt] = mfma32x32x16(u32x4{a0[0], a0[1], a1[0], a1[1]}, mga, adx[pt]);
+          adx[pt] = mfma32x32x16(u32x4{b0[0], b0[1], b1[0], b1[1]}, mgb, adx[pt]);
+        }
+        // dB^T(n, s) += sum_l C^T(n, l) dt_s Z(l, s)
+        const int joN = 32 * j * N;
+#pragma unroll
+        for (int nt = 0; nt < N / 32; ++nt) {
+          const int o0 = tr_off<RBN>(ln, 0, nt) + joN, o1 = tr_off<RBN>(ln, 1, nt) + joN;
+          const u32x2 a0 = lds_read_tr16(sC, o0), a1 = lds_read_tr16(sC, o1);
+          const u32x2 b0 = lds_read_tr16(sC, o0 + 16 * N), b1 = lds_read_tr16(sC, o1 + 16 * N);
+          accT[nt] = mfma32x32x16(u32x4{a0[0], a0[1], a1[0], a1[1]}, zga, accT[nt]);
+          accT[nt] = mfma32x32x16(u32x4{b0[0], b0[1], b1[0], b1[1]}, zgb, accT[nt]);
+        }
+      };
+      if (i < jend) tile(i, std::true_type{});
+      for (int j = i + 1; j < jend; ++j) tile(j, std::false_type{});
+
+      // dx = ... + D dy (rows p = 32 pt + 8 q + 4 g2 + 0..3 of lane s), stored as bf16
+      const float Dh = D ? D[h] : 0.f;
+#pragma unroll
+      for (int pt = 0; pt < P / 32; ++pt)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int p = 32 * pt + 8 * q + 4 * g2;
+          const u32x2 dv = lds_row8<RBP>(sDY, s, p);
+          const float v0 = adx[pt][4 * q] + Dh * bf16_lo(dv[0]), v1 = adx[pt][4 * q + 1] + Dh * bf16_hi(dv[0]);
+          const float v2 = adx[pt][4 * q + 2] + Dh * bf16_lo(dv[1]), v3 = adx[pt][4 * q + 3] + Dh * bf16_hi(dv[1]);
+          if (sok)
+            *reinterpret_cast<u32x2*>(dx + (srow * H + h) * size_t(P) + p) =
+                u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
+        }
+      bd += __shfl_xor(bd, 32, 64);
+      if (g2 == 0) {
+        gsds[arow + s] = sok ? bd + bdst : 0.f;     // B_s . dB'_s of this head
+        gsdst[arow + s] = sok ? dts * bdst : 0.f;
+        gsdd[arow + s] = dd;
+      }
+    } else {
+      // ------------------------------------------------------------ l side
+      const int l = 32 * i + l32;
+      const bool lok = l < nv;
+      const int jlast = 32 * i < nv ? i : -1;       // no tiles when the whole block is past the tokens
+
+      const float a2l = sA2[l];
+      const float el = __builtin_amdgcn_exp2f(a2l);
+      u32x4 dyr[P / 16];
+#pragma unroll
+      for (int kk = 0; kk < P / 16; ++kk) dyr[kk] = lds_row16<RBP>(sDY, l, 16 * kk + 8 * g2);
+      // state term of dC: dC^T(n, l) += sum_p H(n, p) (exp(Acs_l) dy_l[p])
+      {
+        u32x4 dys[P / 16];
+#pragma unroll
+        for (int kk = 0; kk < P / 16; ++kk)
+#pragma unroll
+          for (int w = 0; w < 4; ++w) dys[kk][w] = pack_bf16x2(bf16_lo(dyr[kk][w]) * el, bf16_hi(dyr[kk][w]) * el);
+#pragma unroll
+        for (int nt = 0; nt < N / 32; ++nt)
+#pragma unroll
+          for (int kk = 0; kk < P / 16; ++kk) {
+            const int kb = 16 * kk + 8 * g2;
+            accT[nt] = mfma32x32x16(frag_tr<RBN>(sH, kb, kb + 4, 32 * nt, lane), dys[kk], accT[nt]);
+          }
+      }
+      // this head's C_l . (state term of dC_l) = exp(Acs_l) dy_l . (H^T C_l),
+      // with H as hi + lo (from its fp32 rows p): y^T(p, l) = sum_n H(n, p) C_l[n]
+      float cd = 0.f;
+      {
+        f32x16 yst[P / 32];
+#pragma unroll
+        for (int pt = 0; pt < P / 32; ++pt) {
+          const float* hrow = Hst + sbase + size_t(32 * pt + l32) * N + 8 * g2;
+          yst[pt] = zero16();
+#pragma unroll 2
+          for (int kk = 0; kk < N / 16; ++kk) {
+            const f32x4 hq0 = *reinterpret_cast<const f32x4*>(hrow + 16 * kk);
+            const f32x4 hq1 = *reinterpret_cast<const f32x4*>(hrow + 16 * kk + 4);
+            const u32x4 cl = lds_row16<RBN>(sC, l, 16 * kk + 8 * g2);
+            u32x4 hi, lo;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+              const f32x4& hq = w < 2 ? hq0 : hq1;
+              const float v0 = hq[2 * (w % 2)], v1 = hq[2 * (w % 2) + 1];
+              hi[w] = pack_bf16x2(v0, v1);
+              lo[w] = pack_bf16x2(v0 - bf16_lo(hi[w]), v1 - bf16_hi(hi[w]));
+            }
+            yst[pt] = mfma32x32x16(hi, cl, yst[pt]);
+            yst[pt] = mfma32x32x16(lo, cl, yst[pt]);
+          }
+        }
+#pragma unroll
+        for (int pt = 0; pt < P / 32; ++pt)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const u32x2 dv = lds_row8<RBP>(sDY, l, 32 * pt + 8 * q + 4 * g2);
+            cd += yst[pt][4 * q] * bf16_lo(dv[0]) + yst[pt][4 * q + 1] * bf16_hi(dv[0]) +
+                  yst[pt][4 * q + 2] * bf16_lo(dv[1]) + yst[pt][4 * q + 3] * bf16_hi(dv[1]);
+          }
+        cd *= el;
+      }
+      // intra-chunk terms, tiles of rows s (block j) and lanes l
+      // one tile; the diagonal one (j == i, masked) apart from the others
+      auto tile = [&](int j, auto diag_c) {
+        constexpr bool diag = decltype(diag_c)::value;
+        const int ln = opaque(lane);                 // per-tile addresses (see opaque)
+        // C B^T in the forward orientation (rows s, lane l)
+        const f32x4* tp = tL + (i * (i + 1) / 2 + j) * 256;
+        const f32x4 cf4[4] = {tp[0], tp[64], tp[128], tp[192]};
+        f32x16 accS = zero16();
+#pragma unroll
+        for (int kk = 0; kk < P / 16; ++kk)
+          accS = mfma32x32x16(lds_row16<RBP>(sX, 32 * j + (ln & 31), 16 * kk + 8 * (ln >> 5)),
+                              lds_row16<RBP>(sDY, 32 * i + (ln & 31), 16 * kk + 8 * (ln >> 5)), accS);   // Sxy
+        const float lfac = diag ? 0.f : __builtin_amdgcn_exp2f(a2l - sA2[32 * j + 31]);
+        uint32_t zw[8];
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+          const float cf_lo = cf4[m / 2][2 * (m % 2)], cf_hi = cf4[m / 2][2 * (m % 2) + 1];
+          float z2[2];
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const int r = 2 * m + u;
+            const int sr = 32 * j + 8 * (r / 4) + 4 * g2 + (r % 4);
+            float dec;
+            if constexpr (diag) {
+              const float pv = __builtin_amdgcn_exp2f(a2l + sL[sr]);   // exp(Acs_l - Acs_s) dt_s
+              dec = sr <= l ? pv : 0.f;
+            } else {
+              dec = lfac * sF[sr];
+            }
+            z2[u] = dec * accS[r];
+          }
+          cd += z2[0] * cf_lo + z2[1] * cf_hi;                          // row sum of dt W
+          zw[m] = pack_bf16x2(z2[0], z2[1]);
+        }
+        const u32x4 zga = u32x4{zw[0], zw[1], zw[2], zw[3]}, zgb = u32x4{zw[4], zw[5], zw[6], zw[7]};
+        const int joN = 32 * j * N;
+#pragma unroll
+        for (int nt = 0; nt < N / 32; ++nt) {
+          const int o0 = tr_off<RBN>(ln, 0, nt) + joN, o1 = tr_off<RBN>(ln, 1, nt) + joN;
+          const u32x2 a0 = lds_read_tr16(sB, o0), a1 = lds_read_tr16(sB, o1);
+          const u32x2 b0 = lds_read_tr16(sB, o0 + 16 * N), b1 = lds_read_tr16(sB, o1 + 16 * N);
+          accT[nt] = mfma32x32x16(u32x4{a0[0], a0[1], a1[0], a1[1]}, zga, accT[nt]);
+          accT[nt] = mfma32x32x16(u32x4{b0[0], b0[1], b1[0], b1[1]}, zgb, accT[nt]);
+        }
+      };
+      for (int j = 0; j < jlast; ++j) tile(j, std::false_type{});
+      if (jlast >= 0) tile(jlast, std::true_type{});
+      cd += __shfl_xor(cd, 32, 64);
+      if (g2 == 0) gsdl[arow + l] = lok ? cd : 0.f;   // C_l . dC_l of this head
     }
-    cd += __shfl_xor(cd, 32, 64);
-    if (g2 == 0) gsdl[arow + l] = lok ? cd : 0.f;   // C_l . dC_l of this head
   }
 
-  if (lok) {
-    const size_t row = size_t(lrow) * G + g;
+  // ---- the work-group's sum over its heads: bf16 when it holds all heads
+  //      of the group, else an fp32 partial of its slice
+  const int t = 32 * i + l32;
+  if (t < nv) {
+    const size_t row = size_t(r0 + t) * G + g;
     const long rows = long(gridDim.x / nslice / G / nc) * T;   // batch rows x tokens
+    uint16_t* out = sside ? dBo : dCo;
+    float* part = sside ? dBs : dCs;
 #pragma unroll
     for (int nt = 0; nt < N / 32; ++nt)
 #pragma unroll
@@ -610,9 +517,9 @@ __global__ __launch_bounds__(64 * NB) void bwd_l_kernel(
         const int n = 32 * nt + 8 * q + 4 * g2;
         const f32x4 v4 = f32x4{accT[nt][4 * q], accT[nt][4 * q + 1], accT[nt][4 * q + 2], accT[nt][4 * q + 3]};
         if (nslice == 1)
-          *reinterpret_cast<u32x2*>(dCo + row * N + n) = u32x2{pack_bf16x2(v4[0], v4[1]), pack_bf16x2(v4[2], v4[3])};
+          *reinterpret_cast<u32x2*>(out + row * N + n) = u32x2{pack_bf16x2(v4[0], v4[1]), pack_bf16x2(v4[2], v4[3])};
         else
-          *reinterpret_cast<f32x4*>(dCs + (size_t(sl) * rows * G + row) * N + n) = v4;
+          *reinterpret_cast<f32x4*>(part + (size_t(sl) * rows * G + row) * N + n) = v4;
       }
   }
 }
@@ -725,15 +632,12 @@ __global__ __launch_bounds__(64) void bwd_reduce_ad(const float* __restrict__ dA
 template <int N, int P, int NB>
 hipError_t launch_npq(const FwdShape& s, const BwdArgs& a, hipStream_t st) {
   const long blocks = long(s.b) * s.nc * s.G * a.nslice;
-  hipLaunchKernelGGL((bwd_s_kernel<N, P, NB>), dim3(unsigned(blocks)), dim3(64 * NB), 0, st,
-                     static_cast<const uint16_t*>(a.x), static_cast<const uint16_t*>(a.B),
-                     static_cast<const uint16_t*>(a.C), static_cast<const uint16_t*>(a.dy), a.Acs, a.dtq, a.CBt,
-                     a.Gb, a.D, static_cast<uint16_t*>(a.dx), static_cast<uint16_t*>(a.dB), a.dBs, a.tsds,
-                     a.tsdst, a.tsdd, s.T, s.H, s.G, s.nc, a.nslice);
-  hipLaunchKernelGGL((bwd_l_kernel<N, P, NB>), dim3(unsigned(blocks)), dim3(64 * NB), 0, st,
+  hipLaunchKernelGGL((bwd_sl_kernel<N, P, NB>), dim3(unsigned(blocks)), dim3(128 * NB), 0, st,
                      static_cast<const uint16_t*>(a.x), static_cast<const uint16_t*>(a.B),
                      static_cast<const uint16_t*>(a.C), static_cast<const uint16_t*>(a.dy), a.Acs, a.dtq, a.CB,
-                     a.Hst, static_cast<uint16_t*>(a.dC), a.dCs, a.tsdl, s.T, s.H, s.G, s.nc, a.nslice);
+                     a.CBt, a.Hst, a.Gb, a.D, static_cast<uint16_t*>(a.dx), static_cast<uint16_t*>(a.dB),
+                     static_cast<uint16_t*>(a.dC), a.dBs, a.dCs, a.tsds, a.tsdst, a.tsdd, a.tsdl, s.T, s.H, s.G,
+                     s.nc, a.nslice);
   hipLaunchKernelGGL((bwd_ddt_kernel<32 * NB>), dim3(unsigned(long(s.b) * s.H * s.nc)), dim3(32 * NB), 0, st,
                      a.Acs, a.dtq, a.tsds, a.tsdst, a.tsdd, a.tsdl, a.ghp, a.A, static_cast<uint16_t*>(a.ddt),
                      a.dAp, a.dDp, s.T, s.H, s.nc, a.nghp);

@@ -56,11 +56,13 @@ constexpr int kMaxQ = 256;
 // MFMA, loaded there with two coalesced 16-byte reads per lane.
 // Layout: CB [b, nc, G, ntile, 64, 16] bf16 with ntile = lpc(lpc+1)/2,
 // lpc = Q/32, tile (s, l) of a chunk at index l(l+1)/2 + s.
-// BOTH (the backward's recomputation): the tiles stay fp32 (16 floats per
-// lane, 4 KB per tile, at the same index), and the same products with the
-// roles of the two operands swapped go to CBt, where lane L holds column
-// s = L%32 and the registers run over rows l. The backward takes sums of
-// these products that largely cancel, so they are not rounded to bf16.
+// BOTH (the backward's recomputation): the tiles stay fp32 (4 KB per tile at
+// the same index, as four 1 KB rows of 64 float4: quad m of lane L at float4
+// 64 m + L, so that a 16-byte load per lane reads one whole row), and the
+// same products with the roles of the two operands swapped go to CBt, where
+// lane L holds column s = L%32 and the registers run over rows l. The
+// backward takes sums of these products that largely cancel, so they are not
+// rounded to bf16.
 template <int N, bool BOTH = false>
 __device__ __forceinline__ void chunk_scores_tile(const uint16_t* __restrict__ Bm,
                                                   const uint16_t* __restrict__ Cm,
@@ -90,11 +92,12 @@ __device__ __forceinline__ void chunk_scores_tile(const uint16_t* __restrict__ B
     cf[ks] = keep_or_zero(tl < cr0.n, load16(cr + 16 * ks));
     bf[ks] = keep_or_zero(ts < cr0.n, load16(br + 16 * ks));
   }
-  const size_t at = (((size_t(b) * nc + c) * G + g) * ntile + ti) * 1024 + size_t(lane) * 16;
+  const size_t tile_at = (((size_t(b) * nc + c) * G + g) * ntile + ti) * 1024;
+  const size_t at = tile_at + size_t(lane) * 16;
   auto store32 = [&](uint16_t* dstbase, const f32x16& acc) {
-    f32x4* dst = reinterpret_cast<f32x4*>(reinterpret_cast<float*>(dstbase) + at);
+    f32x4* dst = reinterpret_cast<f32x4*>(reinterpret_cast<float*>(dstbase) + tile_at) + lane;
 #pragma unroll
-    for (int m = 0; m < 4; ++m) dst[m] = f32x4{acc[4 * m], acc[4 * m + 1], acc[4 * m + 2], acc[4 * m + 3]};
+    for (int m = 0; m < 4; ++m) dst[64 * m] = f32x4{acc[4 * m], acc[4 * m + 1], acc[4 * m + 2], acc[4 * m + 3]};
   };
   auto store = [&](uint16_t* dstbase, const f32x16& acc) {
     u32x4 lo, hi;

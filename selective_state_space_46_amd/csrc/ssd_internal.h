@@ -313,14 +313,15 @@ hipError_t launch_causal_conv1d_update(ssd_dtype type, void* state, const void* 
 // Backward pass (bwd_chunk_mfma.hip, state_passing.hip, chunk_state_mfma.hip).
 // The backward recomputes the forward with its own chunk length, the largest
 // of 128, 64, 32 whose per-chunk tiles fit the 160 KB of LDS of a CU (x, dy,
-// B, C rows of the chunk, one P x N state and the chunk's fp32 C B^T tiles),
-// so one kernel serves each (headdim, dstate); 0: shape not supported. 128 at most: its work-group has 4 waves
-// per 128 tokens, and 1024-thread work-groups would leave 128 registers per
-// lane, too few for the accumulators.
+// B, C rows of the chunk, the P x N state gradient and state in bf16, six
+// per-token tables), so one kernel serves each (headdim, dstate); 0: shape
+// not supported. 128 at most: its work-group has 8 waves per 128 tokens, and
+// 16-wave work-groups would leave 128 registers per lane, too few for the
+// accumulators.
 // ---------------------------------------------------------------------------
 constexpr int kBwdLdsMax = 160 * 1024;
 constexpr long bwd_lds_bytes(int P, int N, int Q) {
-  return 4L * Q * (P + N) + 2L * P * N + 4096L * (Q / 32) * (Q / 32 + 1) / 2 + 16L * Q;
+  return 4L * Q * (P + N) + 4L * P * N + 24L * Q;
 }
 constexpr int bwd_chunk_len(int P, int N) {
   return P * N > 128 * 128                        ? 0     // states beyond 64 KB in bf16: not supported
