@@ -553,6 +553,14 @@ def traffic_probe(w):
     log("[bench] traffic probe done (copy of 268435456 bytes x3)")
 
 
+def backward_probe():
+    """Four backward calls on the 130M-shaped layer (one warm-up and three
+    timed by bench_backward's loop; for rocprofv3 --pmc runs on the backward
+    kernels)."""
+    r = bench_backward(Hip(), workloads.MAMBA2_130M, steps=3, warmup=1)
+    log(f"[bench] backward probe done ({r['ms_per_call']} ms per call)")
+
+
 def cpu_baseline(w, min_seconds=10.0):
     import oracle
     inp = workloads.make_fwd_inputs(w)
@@ -661,6 +669,8 @@ def main():
                          "rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs and their calibration)")
     ap.add_argument("--decode-probe", action="store_true",
                     help="only run eight decode updates and the calibration copies (for rocprofv3 --pmc)")
+    ap.add_argument("--backward-probe", action="store_true",
+                    help="only run a few backward calls on the 130M-shaped layer (for rocprofv3 --pmc)")
     ap.add_argument("--extras-only", action="store_true",
                     help="only the sections beside the headline (decode, backward, packed sequences, "
                          "stages next to the core), one JSON line (for kernel traces of them)")
@@ -680,6 +690,9 @@ def main():
         return
     if args.decode_probe:
         decode_probe()
+        return
+    if args.backward_probe:
+        backward_probe()
         return
     if args.peaks:
         print(json.dumps(measured_peaks(hip)), flush=True)

@@ -664,12 +664,15 @@ hipError_t launch_n(const FwdShape& s, const BwdArgs& a, hipStream_t st) {
 }  // namespace
 
 int bwd_slices(const FwdShape& s) {
-  // heads of a group split over work-groups until the grid has ~2 work-groups
-  // per compute unit (slices divide the group's heads)
+  // heads of a group split over work-groups until the grid has a work-group
+  // per compute unit of a 256-unit device (the per-chunk kernel's LDS allows
+  // one per unit; slices divide the group's heads). Measured on the 130M
+  // layer: 2 slices (256 work-groups) 0.314 ms per backward call, 4 slices
+  // 0.330, 6 slices 0.342, 8 slices 0.354.
   const int hpg = s.H / s.G;
   const long base = long(s.b) * s.nc * s.G;
   for (int d = 1; d <= hpg; ++d)
-    if (hpg % d == 0 && base * d >= 512) return d;
+    if (hpg % d == 0 && base * d >= 256) return d;
   return hpg;
 }
 

@@ -101,6 +101,15 @@ def test_bwd_full_130m_layer():
     _check(inp)
 
 
+@pytest.mark.parametrize("b,T,H,G", [(2, 300, 4, 4), (8, 4096, 2, 1)])
+def test_bwd_whole_group_per_work_group(b, T, H, G):
+    """one work-group holds every head of its group (one head per group, or
+    256 (batch, chunk, group) items, a work-group per compute unit already):
+    dB and dC are written as bf16 by the per-chunk kernel itself, with no fp32
+    partials and no reduction after it"""
+    _check(_inputs(b, T, H, 64, 128, G, seed=7650 + H + G))
+
+
 def _walks(b, T, H, P, N, G):
     import selective_state_space_46_amd as ssd
     return ssd.ssd_chunk_scan_bwd_fused_walks(b, T, H, P, N, G, ssd.SSD_BF16)
