@@ -58,7 +58,16 @@ extern "C" {
 #define SSD_API
 #endif
 
-typedef enum {
+/* In C++ the status and dtype enums are declared over int, so that every int
+ * value is a valid value of them (a caller may pass any int: unknown values
+ * are answered, not undefined). */
+#ifdef __cplusplus
+#define SSD_ENUM(name) enum name : int
+#else
+#define SSD_ENUM(name) enum name
+#endif
+
+typedef SSD_ENUM(ssd_status) {
     SSD_OK = 0,
     SSD_ERR_NULL = 1,      /* a required pointer is NULL                          */
     SSD_ERR_SHAPE = 2,     /* a dimension is < 1, nheads % ngroups != 0, or a
@@ -72,7 +81,8 @@ typedef enum {
     SSD_ERR_VALUE = 9      /* a scalar argument is out of range (eps, activation) */
 } ssd_status;
 
-typedef enum { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype;
+/* Element type of the activations (an unknown value: SSD_ERR_DTYPE). */
+typedef SSD_ENUM(ssd_dtype) { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype;
 
 /* Supported ranges (checked; anything else is SSD_ERR_SHAPE / SSD_ERR_CHUNK):
  *   1 <= headdim <= 256, 1 <= dstate <= 256, chunk_len in {16,32,64,128,256},

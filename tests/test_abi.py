@@ -52,6 +52,25 @@ def test_fused_states_query_rejects_what_the_forward_rejects():
     assert not q(8, 2048, 24, 64, 128, 1, 256, ssd.SSD_F32)
 
 
+@pytest.mark.parametrize("lang", ["c", "c++"])
+def test_headers_compile_as_c_and_cpp(tmp_path, lang):
+    """the public headers are plain C (C11) and also valid C++17, pedantic,
+    with no warning"""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc" if lang == "c" else "g++")
+    if cc is None:
+        pytest.skip(f"no {lang} compiler")
+    src = tmp_path / "h.c"
+    src.write_text("".join(f'#include "{h}"\n' for h in ("ssd_api.h", "ssd_epilogue.h", "ssd_backward.h",
+                                                          "ssd_measure.h")) +
+                   "int main(void) { ssd_dtype d = SSD_BF16; ssd_status s = SSD_OK; return (int)d + (int)s; }\n")
+    std = ["-std=c11"] if lang == "c" else ["-std=c++17", "-x", "c++"]
+    r = subprocess.run([cc] + std + ["-Wall", "-Wextra", "-pedantic", "-Werror", "-I", os.path.join(ROOT, "include"),
+                                      "-c", str(src), "-o", str(tmp_path / "h.o")], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+
+
 def test_library_exports_every_declared_symbol(L):
     for name in declared_symbols():
         assert hasattr(L, name), name
