@@ -154,4 +154,32 @@ __device__ __forceinline__ u32x4 keep_or_zero(bool keep, const u32x4& v) {
   return keep ? v : u32x4{0u, 0u, 0u, 0u};
 }
 
+// ---------------------------------------------------------------------------
+// Direct global -> LDS copies and the waits around them.
+// ---------------------------------------------------------------------------
+
+// vmcnt(n), the other counters left alone (low four bits of n in bits 3..0,
+// high two in bits 15..14)
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Work-group barrier for LDS traffic only (the waves of this launch share
+// nothing else through memory): this wave's LDS operations complete, then
+// the barrier; the memory clobber keeps the compiler from moving memory
+// accesses across it. Unlike __syncthreads it does not make each wave wait
+// for its slice copies still in flight, which the copy protocol waits for
+// by count instead.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// One wave's direct copy of 64 x 16 bytes from global memory into LDS: lane
+// L's 16 bytes land at dst + 16 L (dst wave-uniform; checked on MI355X).
+__device__ __forceinline__ void copy_to_lds16(const uint16_t* src, uint16_t* dst) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(dst), 16, 0, 0);
+}
+
 }  // namespace ssd
