@@ -186,12 +186,20 @@ def decode_work(w: workloads.DecodeWorkload) -> dict:
 # HBM traffic from committed rocprofv3 counter summaries
 # --------------------------------------------------------------------------
 
+def _code_only(text: str) -> str:
+    """C++ source without its comments and whitespace: edits to comments
+    leave a kernel's digest (and its counted traffic) as it was."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return re.sub(r"\s+", "", text)
+
+
 def sources_digest(kernel: str) -> str:
     h = hashlib.sha256()
     for f in KERNEL_SOURCES[kernel] + ["ssd_internal.h"]:
         p = os.path.join(ROOT, "selective_state_space_46_amd", "csrc", f)
         if os.path.exists(p):
-            h.update(open(p, "rb").read())
+            h.update(_code_only(open(p).read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -29,7 +29,9 @@
 // chunk_state launch, chunk_state_mfma.hip) in MFMA-fragment order. The
 // super-chunk is cut into eight 32-row blocks l; with W = 4 wave w owns
 // blocks w and 7-w so that the causal triangle splits evenly, with W = 8 one
-// block each (twice the waves on the same LDS, for latency hiding). The output is produced transposed (y^T: rows p, lane = token
+// block each (twice the waves on the same LDS, for latency hiding): wave w <
+// 4 block w, wave w >= 4 block 11 - w, so the two waves that share a SIMD
+// (w and w + 4) hold blocks k and 7 - k, 9 tiles on every SIMD. The output is produced transposed (y^T: rows p, lane = token
 // l), which makes every per-token factor one multiplier per lane:
 //   1. y^T = H_c^T C_l^T (k = dstate): H_c staged once in LDS as stored (bf16,
 //      fragment order, from the fused walk or state_passing, see hb_off) when
@@ -145,8 +147,12 @@ void chunk_scan_mfma_kernel(
 #pragma unroll
     for (int ks = 0; ks < N / 16; ++ks) cfv[ks] = load16(cr + 16 * ks);
   };
+  // the wave's first block: with W = 8 (one block each) waves w and w + 4
+  // share a SIMD, so wave w >= 4 takes block 11 - w: every SIMD then holds
+  // blocks k and 7 - k, 9 tiles
+  const int blk0 = (W == 8 && wave >= 4) ? 11 - wave : wave;
   u32x4 pre_tdiag[2], pre_tnext[2], pre_cf[N / 16];
-  if ((wave % lpc) * 32 < crows(wave / lpc).n) issue_block_loads(wave, pre_tdiag, pre_tnext, pre_cf);
+  if ((blk0 % lpc) * 32 < crows(blk0 / lpc).n) issue_block_loads(blk0, pre_tdiag, pre_tnext, pre_cf);
 
   // ---- staging 1: Acs, the per-token factor, H_c^T
   for (int i = tid; i < kSC; i += kThreads) {
@@ -229,7 +235,7 @@ void chunk_scan_mfma_kernel(
 
   const float Dh = D ? D[h] : 0.f;
   for (int which = 0; which < NB; ++which) {
-    const int i = which ? 7 - wave : wave;  // 32-row block of the super-chunk
+    const int i = which ? 7 - wave : blk0;  // 32-row block of the super-chunk
     const ChunkRows cr = crows(i / lpc);
     const int rq0 = (i % lpc) * 32;         // first row of the block inside its chunk
     if (rq0 >= cr.n) continue;              // wave-uniform: nothing to produce

@@ -212,3 +212,14 @@ def test_fragment_order_operand_reads(P, N):
                 o = 256 * g2 + 4 * l32 + 256 * ((pb * (N // 32) + ks // 2) * 4 + 2 * (ks % 2))
                 p, n = 32 * pb + l32, 16 * ks + 8 * g2
                 assert o == _hb_off(p, n, N) and o + 128 == _hb_off(p, n + 4, N)
+
+
+def test_traffic_digest_ignores_comments_only():
+    """bench.py keeps a committed traffic summary while the kernel's code is
+    unchanged: comments and whitespace do not enter the digest, code does"""
+    import bench
+    a = "int f(int x) {  // first\n  return x + 1; /* note */ }\n"
+    b = "int f(int x) {\n  // reworded comment\n  return x + 1;\n}\n"
+    c = "int f(int x) { return x + 2; }\n"
+    assert bench._code_only(a) == bench._code_only(b)
+    assert bench._code_only(a) != bench._code_only(c)
