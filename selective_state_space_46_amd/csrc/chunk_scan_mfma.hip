@@ -359,19 +359,34 @@ void chunk_scan_mfma_kernel(
         acc[pb] = mfma32x32x16(u32x4{b0[0], b0[1], b1[0], b1[1]}, gb, acc[pb]);
       }
     };
-    // off-diagonal tiles two at a time, ping-pong buffers (the tile after
-    // next loads while the current one is applied; no register copies)
-    u32x4 tB[2];
-    int jj = 0;
+    if constexpr (W == 8) {
+      // one block per wave (at most 7 off-diagonal tiles): all of them in
+      // flight at once, in the registers the C rows held until here
+      u32x4 tall[7][2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) tall[0][u] = tnext[u];
+#pragma unroll
+      for (int t = 1; t < 7; ++t)
+        if (t < irel) load_tile(t, tall[t]);
+#pragma unroll
+      for (int t = 0; t < 7; ++t)
+        if (t < irel) apply(t, tall[t], false);
+      apply(irel, tdiag, true);
+    } else {
+      // off-diagonal tiles two at a time, ping-pong buffers (the tile after
+      // next loads while the current one is applied; no register copies)
+      u32x4 tB[2];
+      int jj = 0;
 #pragma unroll 1
-    for (; jj + 1 < irel; jj += 2) {
-      load_tile(jj + 1, tB);
-      apply(jj, tnext, false);
-      if (jj + 2 < irel) load_tile(jj + 2, tnext);
-      apply(jj + 1, tB, false);
+      for (; jj + 1 < irel; jj += 2) {
+        load_tile(jj + 1, tB);
+        apply(jj, tnext, false);
+        if (jj + 2 < irel) load_tile(jj + 2, tnext);
+        apply(jj + 1, tB, false);
+      }
+      if (jj < irel) apply(jj, tnext, false);
+      apply(irel, tdiag, true);
     }
-    if (jj < irel) apply(jj, tnext, false);
-    apply(irel, tdiag, true);
 
     // ---- epilogue: + D x (x re-read, from L2), round, store 4 consecutive p (8 bytes) per run
     if (tok_ok) {
