@@ -39,7 +39,12 @@
  *    stream) and never synchronise. All argument checks run on the host
  *    before the first launch: on any error nothing is launched, nothing is
  *    written and a status is returned. A launch failure returns SSD_ERR_HIP;
- *    a device-side fault surfaces at the caller's next synchronisation.
+ *    a device-side fault surfaces at the caller's next synchronisation, or,
+ *    with SSD_DEBUG=1 in the environment (read once per process), at the
+ *    call itself: every entry point that launched work then synchronises its
+ *    stream before returning and answers SSD_ERR_HIP if a kernel failed (a
+ *    debugging aid: it serialises the caller with the GPU and cannot be used
+ *    under stream capture).
  *  - No C++ exception crosses this interface. Results are deterministic
  *    (no atomics): the same inputs give bitwise-identical outputs.
  */

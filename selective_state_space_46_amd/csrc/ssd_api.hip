@@ -1,6 +1,7 @@
 // ssd_api.hip -- the C ABI: host-side argument checks, workspace layout and the
 // launch sequence. Every check runs before the first launch; on any error
 // nothing is launched or written.
+#include <cstdlib>
 #include <stdint.h>
 
 #include <algorithm>
@@ -35,6 +36,24 @@ bool overlaps(const void* a, size_t abytes, const void* b, size_t bbytes) {
 }
 
 size_t esize(ssd_dtype t) { return t == SSD_BF16 ? 2 : 4; }
+
+// SSD_DEBUG=1 in the environment: an entry point that launched work
+// synchronises its stream before it returns, so a kernel that failed on the
+// device is reported as SSD_ERR_HIP by the call that launched it instead of by
+// the caller's next synchronisation (not for use under stream capture, where
+// synchronising is not allowed). Read once per process.
+bool debug_sync() {
+  static const bool on = [] {
+    const char* v = std::getenv("SSD_DEBUG");
+    return v != nullptr && v[0] == '1';
+  }();
+  return on;
+}
+ssd_status launched(hipStream_t st) {
+  if (!debug_sync()) return SSD_OK;
+  const bool ok = hipStreamSynchronize(st) == hipSuccess && hipGetLastError() == hipSuccess;
+  return ok ? SSD_OK : SSD_ERR_HIP;
+}
 
 ssd_status check_dims(int batch, int seqlen, int H, int P, int N, int G) {
   if (batch < 1 || seqlen < 1 || H < 1 || P < 1 || N < 1 || G < 1) return SSD_ERR_SHAPE;
@@ -323,7 +342,7 @@ ssd_status ssd_chunk_scan_fwd_timed(const void* x, const void* dt, const float* 
       sg.seglen = pl.seglen;
       if (launch_chunk_scan_mfma(s, x, CB, C, Acs, dtq, Hb, D, y, nullptr, hs, ev(3), sg) != hipSuccess)
         return SSD_ERR_HIP;
-      return SSD_OK;
+      return launched(hs);
     }
     // chunk states and state passing in one launch: stage 2 launches nothing
     if (launch_chunk_state_chain(s, pl, x, B, C, dt, A, Acs, dtq, Hb, init_state, final_state, CB, nullptr,
@@ -341,7 +360,7 @@ ssd_status ssd_chunk_scan_fwd_timed(const void* x, const void* dt, const float* 
   }
   if (launch_chunk_scan(s, dtype, mfma, x, B, C, Acs, dtq, S, Hb, CB, D, y, hs, ev(3)) != hipSuccess)
     return SSD_ERR_HIP;
-  return SSD_OK;
+  return launched(hs);
 }
 
 ssd_status ssd_chunk_scan_fwd(const void* x, const void* dt, const float* A, const void* B,
@@ -395,7 +414,7 @@ ssd_status ssd_state_update(float* state, const void* x, const void* dt, const f
   if (launch_state_update(dtype, state, x, dt, A, B, C, D, y, batch, nheads, headdim, dstate,
                           ngroups, static_cast<hipStream_t>(stream)) != hipSuccess)
     return SSD_ERR_HIP;
-  return SSD_OK;
+  return launched(static_cast<hipStream_t>(stream));
 }
 
 // ---------------------------------------------------------------------------
@@ -487,7 +506,7 @@ ssd_status ssd_chunk_scan_fwd_varlen(const void* x, const void* dt, const float*
   if (launch_state_passing_varlen(s, S, Hb, Acs, cu_seqlens, nseq, init_states, final_states, hs) != hipSuccess)
     return SSD_ERR_HIP;
   if (launch_chunk_scan_mfma(s, x, CB, C, Acs, dtq, Hb, D, y, tab, hs) != hipSuccess) return SSD_ERR_HIP;
-  return SSD_OK;
+  return launched(hs);
 }
 
 ssd_status ssd_gated_rmsnorm(const void* y, const void* z, const float* weight, void* out, long ntokens,
@@ -507,7 +526,7 @@ ssd_status ssd_gated_rmsnorm(const void* y, const void* z, const float* weight, 
   if (launch_gated_rmsnorm(dtype, y, z, weight, out, ntokens, dim, group, eps,
                            static_cast<hipStream_t>(stream)) != hipSuccess)
     return SSD_ERR_HIP;
-  return SSD_OK;
+  return launched(static_cast<hipStream_t>(stream));
 }
 
 ssd_status ssd_causal_conv1d_fwd(const void* x, const float* weight, const float* bias,
@@ -543,7 +562,7 @@ ssd_status ssd_causal_conv1d_fwd(const void* x, const float* weight, const float
                            seqlen, channels, kernel_width, activation,
                            static_cast<hipStream_t>(stream)) != hipSuccess)
     return SSD_ERR_HIP;
-  return SSD_OK;
+  return launched(static_cast<hipStream_t>(stream));
 }
 
 ssd_status ssd_causal_conv1d_update(void* state, const void* x, const float* weight, const float* bias,
@@ -572,7 +591,7 @@ ssd_status ssd_causal_conv1d_update(void* state, const void* x, const float* wei
   if (launch_causal_conv1d_update(dtype, state, x, weight, bias, out, batch, channels, kernel_width,
                                   activation, static_cast<hipStream_t>(stream)) != hipSuccess)
     return SSD_ERR_HIP;
-  return SSD_OK;
+  return launched(static_cast<hipStream_t>(stream));
 }
 
 size_t ssd_chunk_scan_bwd_workspace(int batch, int seqlen, int nheads, int headdim, int dstate, int ngroups,
@@ -679,7 +698,7 @@ ssd_status ssd_chunk_scan_bwd(const void* x, const void* dt, const float* A, con
   a.tsds = tokd; a.tsdst = tokd + rowf; a.tsdd = tokd + 2 * rowf; a.tsdl = tokd + 3 * rowf;
   if (launch_bwd_chunk(s, a, hs) != hipSuccess) return SSD_ERR_HIP;
   if (launch_bwd_reduce(s, a, dA, dD, hs) != hipSuccess) return SSD_ERR_HIP;
-  return SSD_OK;
+  return launched(hs);
 }
 
 }  // extern "C"
