@@ -188,11 +188,15 @@ __device__ __forceinline__ typename Chunk<T, V>::raw f_to_chunk(const float (&f)
   return r;
 }
 
+// fin (or null): the final state, written by the thread of each column's
+// last run from its window (the last K-1 values of carried state and x).
+// Only passed when no other thread still reads the carried state it may
+// overwrite: fin is not the carried state, or a row is one run.
 template <typename T, int K, int V>
 __global__ __launch_bounds__(kThreads) void conv1d_fwd(const T* __restrict__ x,
                                                        const float* __restrict__ w,
                                                        const float* __restrict__ bias,
-                                                       const T* __restrict__ init, T* __restrict__ out,
+                                                       const T* init, T* __restrict__ out, T* fin,
                                                        int b_, int T_, int C, int nruns, int act) {
   typedef typename Chunk<T, V>::raw raw_t;
   const int nv = C / V;
@@ -264,6 +268,13 @@ __global__ __launch_bounds__(kThreads) void conv1d_fwd(const T* __restrict__ x,
       chunk_to_f<T, V>(ld(xb + size_t(t) * C), win[K - 1]);
       step(t);
     }
+  }
+  // after the last token win[0 .. K-2] holds the last K-1 values of (carried
+  // state, x); bf16 -> fp32 -> bf16 is exact
+  if (fin && run == nruns - 1) {
+#pragma unroll
+    for (int k = 0; k < K - 1; ++k)
+      *reinterpret_cast<raw_t*>(fin + (size_t(b) * (K - 1) + k) * C + c0) = f_to_chunk<T, V>(win[k]);
   }
 }
 
@@ -352,16 +363,20 @@ hipError_t conv_k(const void* x, const float* w, const float* bias, const void* 
   const bool vec = C % 4 == 0;
   const long total = long(b) * nruns * (vec ? C / 4 : C);
   const long blocks = (total + kThreads - 1) / kThreads;
+  // the final state from the main kernel where that cannot race with a read
+  // of the carried state (see conv1d_fwd), else from a launch after it
+  const bool fused = fin && K > 1 && (fin != init || nruns == 1);
+  T* kfin = fused ? static_cast<T*>(fin) : nullptr;
   if (vec)
     hipLaunchKernelGGL((conv1d_fwd<T, K, 4>), dim3(unsigned(blocks)), dim3(kThreads), 0, st,
                        static_cast<const T*>(x), w, bias, static_cast<const T*>(init), static_cast<T*>(out),
-                       b, T_, C, nruns, act);
+                       kfin, b, T_, C, nruns, act);
   else
     hipLaunchKernelGGL((conv1d_fwd<T, K, 1>), dim3(unsigned(blocks)), dim3(kThreads), 0, st,
                        static_cast<const T*>(x), w, bias, static_cast<const T*>(init), static_cast<T*>(out),
-                       b, T_, C, nruns, act);
+                       kfin, b, T_, C, nruns, act);
   if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
-  if (fin && K > 1) {
+  if (fin && K > 1 && !fused) {
     // after the main kernel in stream order: it has finished reading the
     // carried state, which the final state may overwrite
     const long fb = (long(b) * C + kThreads - 1) / kThreads;
