@@ -146,7 +146,11 @@ __global__ __launch_bounds__(128 * NB) void bwd_sl_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t sX[Q * P];
   __shared__ __attribute__((aligned(16))) uint16_t sDY[Q * P];
   __shared__ __attribute__((aligned(16))) uint16_t sG[P * N];     // G_c, rows p
-  __shared__ __attribute__((aligned(16))) uint16_t sH[P * N];     // bf16(H_c), rows p
+  // the state's low part in LDS too where it fits beside the rest (else the
+  // C . dC dot reads H_c's fp32 rows from memory)
+  constexpr bool HLO = bwd_lds_bytes(P, N, Q) + 2L * P * N <= kBwdLdsMax;
+  __shared__ __attribute__((aligned(16))) uint16_t sH[P * N];     // bf16(H_c) = hi, rows p
+  __shared__ __attribute__((aligned(16))) uint16_t sHl[HLO ? P * N : 8];   // bf16(H_c - hi) = lo
   __shared__ float sA2[Q], sdt[Q], sEL[Q], sEl[Q], sF[Q], sL[Q];
 
   const int id = xcd_swizzle(blockIdx.x, gridDim.x);
@@ -235,10 +239,20 @@ __global__ __launch_bounds__(128 * NB) void bwd_sl_kernel(
 #pragma unroll
     for (int m = 0; m < PH; ++m) {
       const int e = tid + m * kThr;
-      if (kHEven || e < P * RBN)
-        *reinterpret_cast<u32x4*>(&sH[lds_off<RBN>(e / RBN, 8 * (e % RBN))]) =
-            u32x4{pack_bf16x2(hv[m][0][0], hv[m][0][1]), pack_bf16x2(hv[m][0][2], hv[m][0][3]),
-                  pack_bf16x2(hv[m][1][0], hv[m][1][1]), pack_bf16x2(hv[m][1][2], hv[m][1][3])};
+      if (kHEven || e < P * RBN) {
+        // H_c as the bf16 pair hi + lo (lo = bf16(H - hi)): hi alone is the
+        // operand of the dC state term, the pair the one of the C . dC dot
+        u32x4 hi, lo;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const float v0 = hv[m][w / 2][2 * (w % 2)], v1 = hv[m][w / 2][2 * (w % 2) + 1];
+          hi[w] = pack_bf16x2(v0, v1);
+          lo[w] = pack_bf16x2(v0 - bf16_lo(hi[w]), v1 - bf16_hi(hi[w]));
+        }
+        const int o = lds_off<RBN, true>(e / RBN, 8 * (e % RBN));
+        *reinterpret_cast<u32x4*>(&sH[o]) = hi;
+        if constexpr (HLO) *reinterpret_cast<u32x4*>(&sHl[o]) = lo;
+      }
     }
     }
     __syncthreads();
@@ -410,11 +424,11 @@ __global__ __launch_bounds__(128 * NB) void bwd_sl_kernel(
 #pragma unroll
           for (int kk = 0; kk < P / 16; ++kk) {
             const int kb = 16 * kk + 8 * g2;
-            accT[nt] = mfma32x32x16(frag_tr<RBN>(sH, kb, kb + 4, 32 * nt, lane), dys[kk], accT[nt]);
+            accT[nt] = mfma32x32x16(frag_tr<RBN, true>(sH, kb, kb + 4, 32 * nt, lane), dys[kk], accT[nt]);
           }
       }
       // this head's C_l . (state term of dC_l) = exp(Acs_l) dy_l . (H^T C_l),
-      // with H as hi + lo (from its fp32 rows p): y^T(p, l) = sum_n H(n, p) C_l[n]
+      // with H as hi + lo (rows p): y^T(p, l) = sum_n H(n, p) C_l[n]
       float cd = 0.f;
       {
         f32x16 yst[P / 32];
@@ -424,16 +438,21 @@ __global__ __launch_bounds__(128 * NB) void bwd_sl_kernel(
           yst[pt] = zero16();
 #pragma unroll 2
           for (int kk = 0; kk < N / 16; ++kk) {
-            const f32x4 hq0 = *reinterpret_cast<const f32x4*>(hrow + 16 * kk);
-            const f32x4 hq1 = *reinterpret_cast<const f32x4*>(hrow + 16 * kk + 4);
             const u32x4 cl = lds_row16<RBN>(sC, l, 16 * kk + 8 * g2);
             u32x4 hi, lo;
+            if constexpr (HLO) {
+              hi = lds_row16<RBN>(sH, 32 * pt + l32, 16 * kk + 8 * g2);
+              lo = lds_row16<RBN>(sHl, 32 * pt + l32, 16 * kk + 8 * g2);
+            } else {
+              const f32x4 hq0 = *reinterpret_cast<const f32x4*>(hrow + 16 * kk);
+              const f32x4 hq1 = *reinterpret_cast<const f32x4*>(hrow + 16 * kk + 4);
 #pragma unroll
-            for (int w = 0; w < 4; ++w) {
-              const f32x4& hq = w < 2 ? hq0 : hq1;
-              const float v0 = hq[2 * (w % 2)], v1 = hq[2 * (w % 2) + 1];
-              hi[w] = pack_bf16x2(v0, v1);
-              lo[w] = pack_bf16x2(v0 - bf16_lo(hi[w]), v1 - bf16_hi(hi[w]));
+              for (int w = 0; w < 4; ++w) {
+                const f32x4& hq = w < 2 ? hq0 : hq1;
+                const float v0 = hq[2 * (w % 2)], v1 = hq[2 * (w % 2) + 1];
+                hi[w] = pack_bf16x2(v0, v1);
+                lo[w] = pack_bf16x2(v0 - bf16_lo(hi[w]), v1 - bf16_hi(hi[w]));
+              }
             }
             yst[pt] = mfma32x32x16(hi, cl, yst[pt]);
             yst[pt] = mfma32x32x16(lo, cl, yst[pt]);

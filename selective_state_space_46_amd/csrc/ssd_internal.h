@@ -314,7 +314,7 @@ hipError_t launch_causal_conv1d_update(ssd_dtype type, void* state, const void* 
 // The backward recomputes the forward with its own chunk length, the largest
 // of 128, 64, 32 whose per-chunk tiles fit the 160 KB of LDS of a CU (x, dy,
 // B, C rows of the chunk, the P x N state gradient and state in bf16, six
-// per-token tables), so one kernel serves each (headdim, dstate); 0: shape
+// per-token tables; the state's bf16 low part as well where it fits too), so one kernel serves each (headdim, dstate); 0: shape
 // not supported. 128 at most: its work-group has 8 waves per 128 tokens, and
 // 16-wave work-groups would leave 128 registers per lane, too few for the
 // accumulators.
