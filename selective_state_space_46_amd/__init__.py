@@ -16,6 +16,7 @@ Entry points (same names as the C ABI):
     ssd_status_string(code) -> str
     ssd_chunk_scan_fwd_varlen(x, dt, A, B, C, D, cu_seqlens, init_states, chunk_len)
         -> (y, final_states)                          (packed variable-length sequences)
+    ssd_chunk_scan_fwd_varlen_plan(...) -> (segment slots, chunks per segment) ((0, 0): per chunk)
 and, from ``include/ssd_backward.h``, the backward pass:
     ssd_chunk_scan_bwd(x, dt, A, B, C, D, init_state, dy, dfinal)
         -> dict(dx, ddt, dA, dB, dC, dD, dinit)
@@ -36,7 +37,7 @@ __all__ = [
     "ssd_chunk_scan_fwd_fused_states", "ssd_chunk_scan_fwd_plan", "ssd_chunk_scan_fwd_noalloc",
     "SSD_NOALLOC_SCRATCH_BYTES",
     "ssd_state_update", "ssd_status_string", "ssd_chunk_scan_fwd_varlen",
-    "ssd_chunk_scan_fwd_varlen_workspace", "ssd_gated_rmsnorm", "ssd_causal_conv1d_fwd",
+    "ssd_chunk_scan_fwd_varlen_workspace", "ssd_chunk_scan_fwd_varlen_plan", "ssd_gated_rmsnorm", "ssd_causal_conv1d_fwd",
     "ssd_causal_conv1d_update", "ssd_chunk_scan_bwd_workspace", "ssd_chunk_scan_bwd",
     "ssd_chunk_scan_bwd_fused_walks",
 ]
@@ -98,6 +99,8 @@ def lib() -> ctypes.CDLL:
     L.ssd_chunk_scan_fwd_varlen_workspace.restype = sz
     L.ssd_chunk_scan_fwd_varlen.argtypes = [vp] * 10 + [i32] * 8 + [vp, sz, vp]
     L.ssd_chunk_scan_fwd_varlen.restype = i32
+    L.ssd_chunk_scan_fwd_varlen_plan.argtypes = [i32] * 8 + [i32, ctypes.POINTER(i32)]
+    L.ssd_chunk_scan_fwd_varlen_plan.restype = i32
     L.ssd_gated_rmsnorm.argtypes = [vp] * 4 + [i64, i32, i32, f32, i32, vp]
     L.ssd_gated_rmsnorm.restype = i32
     L.ssd_causal_conv1d_fwd.argtypes = [vp] * 6 + [i32] * 5 + [i32, vp]
@@ -155,6 +158,17 @@ def ssd_chunk_scan_fwd_plan(batch: int, seqlen: int, nheads: int, headdim: int, 
     sl = ctypes.c_int(0)
     n = int(lib().ssd_chunk_scan_fwd_plan(batch, seqlen, nheads, headdim, dstate, ngroups, chunk_len, dtype,
                                           compute_units, ctypes.byref(sl)))
+    return n, int(sl.value)
+
+
+def ssd_chunk_scan_fwd_varlen_plan(total_tokens: int, nseq: int, nheads: int, headdim: int, dstate: int,
+                                   ngroups: int, chunk_len: int, dtype: int, compute_units: int) -> Tuple[int, int]:
+    """(segment slots, chunks per segment) the packed forward chooses on a
+    device with `compute_units` compute units; (0, 0) = chunk-state launch
+    and a recurrence per sequence over its chunks. Needs no device."""
+    sl = ctypes.c_int(0)
+    n = int(lib().ssd_chunk_scan_fwd_varlen_plan(total_tokens, nseq, nheads, headdim, dstate, ngroups, chunk_len,
+                                                 dtype, compute_units, ctypes.byref(sl)))
     return n, int(sl.value)
 
 

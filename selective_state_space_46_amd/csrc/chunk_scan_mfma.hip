@@ -53,7 +53,9 @@
 // cdec_c <= 0), formed in fp32 where
 // H_c is staged or loaded and rounded to bf16 once. Where exp(cdec_c)
 // underflows to zero (a decayed segment start) the correction is exactly
-// zero and Hin is not read.
+// zero and Hin is not read. Packed sequences (VARLEN with SEG) take each
+// chunk's segment slot, and whether its segment is its sequence's first (no
+// correction), from the chunk table's flags.
 #include "mfma_util.h"
 
 namespace ssd {
@@ -123,6 +125,18 @@ void chunk_scan_mfma_kernel(
     if (rowsv.n <= 0) rowsv = r;
   }
   if (rowsv.n <= 0) return;            // no valid chunk: uniform, before any barrier
+  // SEG: the segment of chunk c (a valid chunk of the super-chunk) and
+  // whether a state from before the segment enters it
+  auto seg_of = [&](int c, int& k, bool& later) {
+    if constexpr (VARLEN) {
+      const int f = tab[c].w;
+      k = clamp_int(f >> 3, 0, nseg - 1);
+      later = (f & 4) == 0;
+    } else {
+      k = c / seglen;
+      later = k > 0;
+    }
+  };
 
   // C B^T tiles of 32-row block i: tile jj (column block jfirst + jj) of the
   // block's row of its chunk's lower triangle, this lane's 32 bytes
@@ -174,10 +188,12 @@ void chunk_scan_mfma_kernel(
     // alpha times the state entering the segment, stored in the same order)
     const uint16_t* hsrc = Hb + ((size_t(b) * nc + c0) * H + h) * size_t(P) * N;
     constexpr int kPieces = P * N / 8;               // 16-byte pieces of one state
-    const int sg = SEG ? c0 / seglen : 0;            // the chunk's segment (uniform)
+    int sg = 0;                                      // the chunk's segment (uniform)
+    bool later = false;
+    if constexpr (SEG) seg_of(c0, sg, later);
     // the weight of the state entering the segment (uniform; where it
     // underflows to zero the correction adds exactly zero and is skipped)
-    const float alpha = SEG && sg > 0 ? exp_fast(cdec[(size_t(b) * H + h) * nc + c0]) : 0.f;
+    const float alpha = SEG && later ? exp_fast(cdec[(size_t(b) * H + h) * nc + c0]) : 0.f;
     const float* hin = SEG ? Hin + ((size_t(b) * nseg + sg) * H + h) * size_t(P) * N : nullptr;
 #pragma unroll
     for (int k = 0; k < (kPieces + kThreads - 1) / kThreads; ++k) {
@@ -272,8 +288,10 @@ void chunk_scan_mfma_kernel(
     const int hlane = 256 * g2 + 4 * l32;   // this lane's part of a fragment-order offset
     // segments, per-fragment path: this block's chunk's segment and the
     // weight of the state entering it (uniform)
-    const int sgb = SEG && !HLDS ? cg / seglen : 0;
-    const float alpha_b = SEG && !HLDS && sgb > 0 ? exp_fast(cdec[(size_t(b) * H + h) * nc + cg]) : 0.f;
+    int sgb = 0;
+    bool later_b = false;
+    if constexpr (SEG && !HLDS) seg_of(cg, sgb, later_b);
+    const float alpha_b = SEG && !HLDS && later_b ? exp_fast(cdec[(size_t(b) * H + h) * nc + cg]) : 0.f;
 #pragma unroll
     for (int pb = 0; pb < P / 32; ++pb) {
       acc[pb] = zero16();
@@ -431,8 +449,19 @@ hipError_t launch_np(const FwdShape& s, const void* x, const uint16_t* CB, const
                           static_cast<uint16_t*>(y), tab, s.T, s.H, s.G, s.Q, s.nc, nsc, sg.Hin, sg.cdec, sg.nseg,
                           sg.seglen);
   };
-  const bool seg = sg.nseg > 1;
-  if (seg && (tab || !sg.Hin || !sg.cdec || sg.seglen < 1)) return hipErrorInvalidValue;
+  const bool seg = sg.nseg > 1 || sg.var;
+  if (seg && (!sg.Hin || !sg.cdec || (sg.var ? !tab || sg.nseg < 1 : tab || sg.seglen < 1)))
+    return hipErrorInvalidValue;
+  // packed sequences through segments: only where the fused walk runs
+  if constexpr (N >= 128) {
+    if (seg && tab) {
+      if (s.Q == kSC) go(chunk_scan_mfma_kernel<N, P, true, true, true, W>, W);
+      else go(chunk_scan_mfma_kernel<N, P, false, true, true, 4>, 4);
+      return hipGetLastError();
+    }
+  } else {
+    if (seg && tab) return hipErrorInvalidValue;
+  }
   // one chunk per super-chunk: its H_c^T is staged in LDS
   if (s.Q == kSC) {
     if (seg) go(chunk_scan_mfma_kernel<N, P, true, false, true, W>, W);

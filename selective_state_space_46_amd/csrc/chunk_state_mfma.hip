@@ -314,6 +314,17 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma_kernel(
 // state_passing then runs the recurrence over the segments, and chunk_scan
 // adds exp(cdec_c) Hin_k where it stages H_c.
 //
+// Packed sequences (stab not null; one row of chunk slots, the chunk table
+// tab giving each slot's rows). The same segmented walks, over the segment
+// table instead of equal cuts: segment slot k (walks (k, 64 columns)) holds
+// up to seglen consecutive chunk slots of one sequence, starts from that
+// sequence's initial state if it is the sequence's first segment and from
+// zero otherwise, and writes the same local states, cdec, segdec and last
+// local state; a slot without chunks leaves at once. The recurrence then
+// runs per sequence over its segments. The C B^T tiles of the slots stay in
+// this launch, behind the walks: the walks of unused segment slots leave
+// their units to them at once.
+//
 // Tokens stream through 64-row slices of B (all of dstate, shared by the two
 // column blocks) and x (the 64 columns), copied straight from global memory
 // into LDS (global_load_lds, 16 bytes per lane) in a swizzled row-major
@@ -380,7 +391,7 @@ void chunk_state_chain_kernel(
     const float* __restrict__ init, float* __restrict__ fin, const uint16_t* __restrict__ Cm,
     uint16_t* __restrict__ CB, uint16_t* __restrict__ CBt, const float* __restrict__ Hst, float* __restrict__ ghp,
     float* __restrict__ cdec, float* __restrict__ segdec, int T, int H, int G, int Q, int nc, int nb, int nseg,
-    int seglen, int nchain, long ntiles) {
+    int seglen, int nchain, long ntiles, const int4* __restrict__ tab, const int4* __restrict__ stab, int nseq) {
   using Cfg = ChainCfg<N, ST>;
   constexpr int S = Cfg::STAGES, RBB = Cfg::RBB, RBX = Cfg::RBX, NCB = Cfg::NCB, NCX = Cfg::NCX;
   constexpr int OPS = Cfg::OPS, TPW = Cfg::TPW;
@@ -390,7 +401,7 @@ void chunk_state_chain_kernel(
   // work-groups past the chains compute C B^T tiles, one per wave
   if (int(blockIdx.x) >= nchain) {
     const long wid = long(int(blockIdx.x) - nchain) * kChainWaves + wave;
-    if (wid < ntiles) chunk_scores_tile<N, F32S>(Bm, Cm, CB, CBt, nullptr, T, G, Q, nc, wid, lane);
+    if (wid < ntiles) chunk_scores_tile<N, F32S>(Bm, Cm, CB, CBt, tab, T, G, Q, nc, wid, lane);
     return;                                     // no barrier on this path
   }
   __shared__ __attribute__((aligned(16))) uint16_t sB[S][kChainSK * N];
@@ -409,9 +420,24 @@ void chunk_state_chain_kernel(
   const int h0 = c0 / P;                        // first head
   const int g = h0 / (H / G);                   // the B group (both heads share it)
   const int l32 = lane & 31, g2 = lane >> 5;
-  const int cbeg = seg * seglen;                // first chunk of the walk
-  const int ncw = min(nc, cbeg + seglen) - cbeg;   // chunks of the walk
+  int cbeg = seg * seglen;                      // first chunk of the walk
+  int ncw = min(nc, cbeg + seglen) - cbeg;      // chunks of the walk
+  int sq = b;                                   // the initial state's row
+  bool from_init = seg == 0;                    // the walk starts from the initial state
+  if (stab) {
+    // packed sequences: segment slot seg of the segment table (its chunk
+    // slots, sequence and whether it is the sequence's first), indices
+    // clamped into the tables whatever the entry
+    const int4 e = stab[seg];
+    cbeg = clamp_int(e.x, 0, nc - 1);
+    ncw = clamp_int(e.y, 0, min(seglen, nc - cbeg));
+    sq = clamp_int(e.z, 0, nseq - 1);
+    from_init = e.w != 0;
+  }
+  if (ncw <= 0) return;                         // an unused segment slot: uniform, before any barrier
   const int nsl = ncw * SPC;                    // slices of the walk
+  // token rows of chunk c: equal-length rows, or the chunk table's slot
+  auto rows = [&](int c) { return stab ? slot_rows(tab, c, T, Q) : chunk_rows(nullptr, b, c, T, Q); };
   // the walk's step k visits slice ks(k) of the row and its chunk wc = k / SPC
   // is chunk rc(wc) of the row (reversed in the reverse pass)
   auto ks = [&](int k) { return REV ? (cbeg + ncw) * SPC - 1 - k : cbeg * SPC + k; };
@@ -441,7 +467,7 @@ void chunk_state_chain_kernel(
     // chunk's loads are whole aligned words.
     const long last_e = long(nb) * T * H - 1;   // the tensor's last element
     auto dt_load = [&](int wc, uint32_t (&v)[NHW][4], uint32_t (&hi)[NHW]) {
-      const ChunkRows cr = chunk_rows(nullptr, b, rc(wc), T, Q);
+      const ChunkRows cr = rows(rc(wc));
       const bool tail = (last_e & 1) == 0 && cr.r0 + cr.n == long(nb) * T && h0 + NHW == H;
       if (tail) {
 #pragma unroll
@@ -474,7 +500,7 @@ void chunk_state_chain_kernel(
     // of this lane's tokens into acs / v for the rows written after the next
     // dt loads
     auto tables = [&](int wc, int q, const uint32_t (&raw)[4], uint32_t hi, float (&acs)[4], float (&v)[4]) -> float {
-      const ChunkRows cr = chunk_rows(nullptr, b, rc(wc), T, Q);
+      const ChunkRows cr = rows(rc(wc));
       float tot = 0.f;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -595,7 +621,7 @@ void chunk_state_chain_kernel(
       // slice into a free slot) into slot s
       auto issue = [&](int k, int s) {
         k = ks(min(k, nsl - 1));
-        const ChunkRows cr = chunk_rows(nullptr, b, k / SPC, T, Q);
+        const ChunkRows cr = rows(k / SPC);
         const int s0 = (k % SPC) * kChainSK;
         const long row0 = cr.r0 + s0;
         const uint16_t* bbase = Bm + (row0 * G + g) * size_t(N);
@@ -659,7 +685,7 @@ void chunk_state_chain_kernel(
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int n = 32 * ntile(u) + 8 * (r / 4) + 4 * g2 + r % 4;
-      acc[u][r] = init && seg == 0 ? init[(bhj * N + n) * P + pj + l32] : 0.f;
+      acc[u][r] = init && from_init ? init[((size_t(sq) * H + hj) * N + n) * P + pj + l32] : 0.f;
     }
   }
   // chunk c's start: H_c out as bf16 ([p][n] rows, four consecutive n of
@@ -765,7 +791,7 @@ void chunk_state_chain_kernel(
       compute(k, d);
     }
   }
-  if (fin && nseg > 1) {
+  if (fin && (nseg > 1 || stab)) {
     // a segment's last local state, [b, nseg, H, P * N], each head's in
     // fragment order (hb_off), fp32
     float* dst = fin + ((size_t(b) * nseg + seg) * H + hj) * hstate;
@@ -846,11 +872,15 @@ template <int N, int P, int SPC, int ST, bool F32S, bool REV>
 hipError_t launch_chain_np(const FwdShape& s, const ChainPlan& pl, const void* x, const void* B, const void* C,
                            const void* dt, const float* A, float* Acs, float* dtq, void* Hs, const float* init,
                            float* fin, uint16_t* CB, uint16_t* CBt, const float* Hst, float* ghp, float* cdec,
-                           float* segdec, hipStream_t st, const StageEv& ev) {
+                           float* segdec, const int4* tab, const int4* stab, int nseq, hipStream_t st,
+                           const StageEv& ev) {
   const int lpc = s.Q / 32;
   const long alltiles = REV ? 0 : long(s.b) * s.nc * s.G * (lpc * (lpc + 1) / 2);
   const long nchain = long(s.b) * s.H * P / kChainCols * pl.nseg;
-  const bool segd = pl.nseg > 1;
+  // packed sequences keep their tiles in the walk launch: the walks of unused
+  // segment slots leave at once and tile work-groups take their places
+  const bool segd = pl.nseg > 1 && !pl.var;
+  const bool segs = segd || pl.var;         // cdec / segdec written
   // segmented: the tiles first, as a launch of their own (the stage's start
   // event on it, the stop event on the walk)
   if (segd && alltiles > 0) {
@@ -867,9 +897,9 @@ hipError_t launch_chain_np(const FwdShape& s, const ChainPlan& pl, const void* x
                         dim3(kChainThreads), 0, st, segd && alltiles > 0 ? nullptr : ev.start, ev.stop, 0,
                         static_cast<const uint16_t*>(x),
                         static_cast<const uint16_t*>(B), static_cast<const uint16_t*>(dt), A, Acs, dtq, Hs, init, fin,
-                        static_cast<const uint16_t*>(C), CB, CBt, Hst, ghp, segd ? cdec : nullptr,
-                        segd ? segdec : nullptr, s.T, s.H, s.G, s.Q, s.nc, s.b, pl.nseg, pl.seglen, int(nchain),
-                        ntiles);
+                        static_cast<const uint16_t*>(C), CB, CBt, Hst, ghp, segs ? cdec : nullptr,
+                        segs ? segdec : nullptr, s.T, s.H, s.G, s.Q, s.nc, s.b, pl.nseg, pl.seglen, int(nchain),
+                        ntiles, pl.var ? tab : nullptr, pl.var ? stab : nullptr, nseq);
   return hipGetLastError();
 }
 
@@ -955,15 +985,25 @@ int device_units() {
 // equal chunk counts (the last may be shorter), as many as one walk per unit
 // allows and at most one per chunk; if that still leaves more than half the
 // units idle, the two-kernel path runs.
+namespace {
+// the shapes the walk serves: dstate 128 or 256, headdim 32 (two heads of one
+// B/C group per work-group), 64 or 128, chunks of whole 64-token slices
+bool chain_shape_ok(const FwdShape& s) {
+  if (!((s.N == 128 || s.N == 256) && (s.P == 32 || s.P == 64 || s.P == 128) && s.Q % kChainSK == 0)) return false;
+  return !(s.P == 32 && (s.H / s.G) % 2 != 0);
+}
+// walks that fit a unit at once: two at dstate 128 with a chunk start at
+// most every other slice (the registers of a chunk start every slice do not
+// fit that occupancy), else one
+long chain_per_unit(const FwdShape& s) { return s.N == 128 && s.Q >= 2 * kChainSK ? 2 : 1; }
+}  // namespace
+
 ChainPlan chunk_state_chain_plan_for(const FwdShape& s, int cus, bool allow_segments) {
   ChainPlan pl;
-  if (!((s.N == 128 || s.N == 256) && (s.P == 32 || s.P == 64 || s.P == 128) && s.Q % kChainSK == 0)) return pl;
-  if (s.P == 32 && (s.H / s.G) % 2 != 0) return pl;
+  if (!chain_shape_ok(s)) return pl;
   if (cus <= 0 || s.nc < 1) return pl;
   const long wgs = long(s.b) * s.H * s.P / kChainCols;
-  // two per unit: dstate 128 with a chunk start at most every other slice
-  // (the registers of a chunk start every slice do not fit that occupancy)
-  const long per_unit = s.N == 128 && s.Q >= 2 * kChainSK ? 2 : 1;
+  const long per_unit = chain_per_unit(s);
   if (wgs > per_unit * cus) return pl;
   if (2 * wgs >= cus) {
     pl.ok = true;
@@ -984,6 +1024,38 @@ ChainPlan chunk_state_chain_plan_for(const FwdShape& s, int cus, bool allow_segm
   return pl;
 }
 
+// Packed sequences: L chunks per segment give floor(T / (Q L)) + nseq
+// segment slots and as many walks per 64 columns. L is the smallest whose
+// walks all fit at once, L = floor(T / (Q (m + 1))) + 1 with m the largest
+// floor(T / (Q L)) that fits, but at most kVarlenMaxSegChunks: where one
+// segment per sequence leaves little room (several long sequences, dstate
+// 256), more and shorter walks than fit at once queue and finish sooner than
+// a few long ones (packed 64K and 128K-token layers, 8 sequences: 16 chunks
+// 0.54 / 1.00 ms against 86 / 171 chunks 0.57 / 1.10 ms). Sequences longer
+// than Q L tokens take several segments; the rest one each. Where not even
+// one walk per sequence fits at once (many short sequences), the per-chunk
+// path runs.
+constexpr long kVarlenMaxSegChunks = 16;
+
+ChainPlan varlen_chain_plan_for(const FwdShape& s, int nseq, int cus) {
+  ChainPlan pl;
+  if (!chain_shape_ok(s) || s.b != 1 || cus <= 0 || nseq < 1 || s.T < 1) return pl;
+  const long cpr = long(s.H) * s.P / kChainCols;
+  const long room = chain_per_unit(s) * cus / cpr - nseq;   // segment slots beyond one per sequence
+  if (room < 0) return pl;
+  const long L = std::min(long(s.T) / (long(s.Q) * (room + 1)) + 1, kVarlenMaxSegChunks);
+  const long QL = L * s.Q;
+  if (QL > 0x7fffffffL) return pl;
+  pl.ok = true;
+  pl.var = true;
+  pl.seglen = int(L);
+  pl.nseg = varlen_seg_slots(s.T, nseq, int(QL));
+  // two per unit where that fits (more walks than units), else one per unit
+  // (more walks than fit at once queue)
+  pl.two = chain_per_unit(s) == 2 && long(pl.nseg) * cpr > cus;
+  return pl;
+}
+
 ChainPlan chunk_state_chain_plan(const FwdShape& s, bool allow_segments) {
   return chunk_state_chain_plan_for(s, device_units(), allow_segments);
 }
@@ -999,10 +1071,16 @@ template <bool F32S, bool REV>
 hipError_t launch_chain(const FwdShape& s, const ChainPlan& pl, const void* x, const void* B, const void* C,
                         const void* dt, const float* A, float* Acs, float* dtq, void* Hs, const float* init,
                         float* fin, uint16_t* CB, uint16_t* CBt, const float* Hst, float* ghp, float* cdec,
-                        float* segdec, hipStream_t st, const StageEv& ev) {
+                        float* segdec, hipStream_t st, const StageEv& ev, const int4* tab = nullptr,
+                        const int4* stab = nullptr, int nseq = 0) {
   // every walk must own at least one chunk and the segments must cover the
-  // row exactly: a walk without slices would clamp its copies to slice -1
-  if (!chain_plan_valid(s, pl) || ((F32S || REV) && pl.nseg != 1)) return hipErrorInvalidValue;
+  // row exactly: a walk without slices would clamp its copies to slice -1.
+  // Packed sequences: the segment table decides, and a walk whose slot holds
+  // no chunks leaves before its first copy.
+  const bool ok = pl.var ? pl.ok && s.b == 1 && pl.nseg >= 1 && pl.seglen >= 1 && tab && stab && nseq >= 1 &&
+                               cdec && segdec && fin && !F32S && !REV
+                         : chain_plan_valid(s, pl) && !((F32S || REV) && pl.nseg != 1);
+  if (!ok) return hipErrorInvalidValue;
   // two work-groups per unit (three slices resident; chunks of two or four
   // slices, which the plan ensures) where one per unit would not hold them all
   auto by_q = [&](auto np) -> hipError_t {
@@ -1015,10 +1093,10 @@ hipError_t launch_chain(const FwdShape& s, const ChainPlan& pl, const void* x, c
         switch (s.Q / kChainSK) {
           case 2:
             return launch_chain_np<NP::n, NP::p, 2, 3, F32S, REV>(s, pl, x, B, C, dt, A, Acs, dtq, Hs, init, fin, CB,
-                                                                  CBt, Hst, ghp, cdec, segdec, st, ev);
+                                                                  CBt, Hst, ghp, cdec, segdec, tab, stab, nseq, st, ev);
           case 4:
             return launch_chain_np<NP::n, NP::p, 4, 3, F32S, REV>(s, pl, x, B, C, dt, A, Acs, dtq, Hs, init, fin, CB,
-                                                                  CBt, Hst, ghp, cdec, segdec, st, ev);
+                                                                  CBt, Hst, ghp, cdec, segdec, tab, stab, nseq, st, ev);
         }
         return hipErrorInvalidValue;
       }
@@ -1026,13 +1104,13 @@ hipError_t launch_chain(const FwdShape& s, const ChainPlan& pl, const void* x, c
     switch (s.Q / kChainSK) {
       case 1:
         return launch_chain_np<NP::n, NP::p, 1, S1, F32S, REV>(s, pl, x, B, C, dt, A, Acs, dtq, Hs, init, fin, CB,
-                                                               CBt, Hst, ghp, cdec, segdec, st, ev);
+                                                               CBt, Hst, ghp, cdec, segdec, tab, stab, nseq, st, ev);
       case 2:
         return launch_chain_np<NP::n, NP::p, 2, S1, F32S, REV>(s, pl, x, B, C, dt, A, Acs, dtq, Hs, init, fin, CB,
-                                                               CBt, Hst, ghp, cdec, segdec, st, ev);
+                                                               CBt, Hst, ghp, cdec, segdec, tab, stab, nseq, st, ev);
       case 4:
         return launch_chain_np<NP::n, NP::p, 4, S1, F32S, REV>(s, pl, x, B, C, dt, A, Acs, dtq, Hs, init, fin, CB,
-                                                               CBt, Hst, ghp, cdec, segdec, st, ev);
+                                                               CBt, Hst, ghp, cdec, segdec, tab, stab, nseq, st, ev);
     }
     return hipErrorInvalidValue;
   };
@@ -1050,8 +1128,19 @@ hipError_t launch_chunk_state_chain(const FwdShape& s, const ChainPlan& pl, cons
                                     const void* C, const void* dt, const float* A, float* Acs, float* dtq,
                                     uint16_t* Hb, const float* init, float* fin, uint16_t* CB, float* cdec,
                                     float* segdec, hipStream_t st, const StageEv& ev) {
+  if (pl.var) return hipErrorInvalidValue;
   return launch_chain<false, false>(s, pl, x, B, C, dt, A, Acs, dtq, Hb, init, fin, CB, nullptr, nullptr, nullptr,
                                     cdec, segdec, st, ev);
+}
+
+hipError_t launch_chunk_state_chain_varlen(const FwdShape& s, const ChainPlan& pl, const void* x, const void* B,
+                                           const void* C, const void* dt, const float* A, float* Acs, float* dtq,
+                                           uint16_t* Hb, const float* init, float* segS, uint16_t* CB, float* cdec,
+                                           float* segdec, const int4* tab, const int4* stab, int nseq,
+                                           hipStream_t st, const StageEv& ev) {
+  if (!pl.var) return hipErrorInvalidValue;
+  return launch_chain<false, false>(s, pl, x, B, C, dt, A, Acs, dtq, Hb, init, segS, CB, nullptr, nullptr, nullptr,
+                                    cdec, segdec, st, ev, tab, stab, nseq);
 }
 
 hipError_t launch_chunk_state_chain_bwd(const FwdShape& s, const void* x, const void* B, const void* C,

@@ -427,7 +427,21 @@ FwdShape varlen_shape(int total, int nseq, int H, int P, int N, int G, int Q) {
   s.nc = varlen_slots(total, nseq, Q);
   return s;
 }
-size_t varlen_table_offset(const WsLayout& w) { return (w.total + 255) / 256 * 256; }
+// Workspace of a packed call: the forward's layout for one row of chunk
+// slots (with the fused walk's segments where the plan has them: segment
+// states, cdec, segdec), then the chunk table and the segment table.
+struct VarlenWs {
+  WsLayout w;
+  size_t tab, stab, total;
+};
+VarlenWs varlen_ws(const FwdShape& s, const ChainPlan& pl) {
+  VarlenWs v;
+  v.w = ws_layout(s, true, pl);
+  v.tab = align_up(v.w.total, 256);
+  v.stab = align_up(v.tab + size_t(s.nc) * sizeof(int4), 256);
+  v.total = pl.ok ? v.stab + size_t(pl.nseg) * sizeof(int4) : v.tab + size_t(s.nc) * sizeof(int4);
+  return v;
+}
 // the per-sequence state passing launches 256 threads per (sequence, head,
 // 16 x 64 state tile)
 bool varlen_grids_fit(const FwdShape& s, int nseq) {
@@ -442,8 +456,20 @@ size_t ssd_chunk_scan_fwd_varlen_workspace(int total_tokens, int nseq, int nhead
   if (check_dims(1, total_tokens, nheads, headdim, dstate, ngroups) != SSD_OK) return 0;
   const FwdShape s = varlen_shape(total_tokens, nseq, nheads, headdim, dstate, ngroups, chunk_len);
   if (!use_mfma_path(s, dtype) || !varlen_grids_fit(s, nseq)) return 0;
-  const WsLayout w = ws_layout(s, true, ChainPlan{});
-  return varlen_table_offset(w) + size_t(s.nc) * sizeof(int4);
+  return varlen_ws(s, varlen_chain_plan_for(s, nseq, device_units())).total;
+}
+
+int ssd_chunk_scan_fwd_varlen_plan(int total_tokens, int nseq, int nheads, int headdim, int dstate, int ngroups,
+                                   int chunk_len, ssd_dtype dtype, int compute_units, int* seglen) {
+  if (seglen) *seglen = 0;
+  if (!dtype_ok(dtype) || !is_chunk_ok(chunk_len) || nseq < 1 || nseq > 65535) return 0;
+  if (check_dims(1, total_tokens, nheads, headdim, dstate, ngroups) != SSD_OK) return 0;
+  const FwdShape s = varlen_shape(total_tokens, nseq, nheads, headdim, dstate, ngroups, chunk_len);
+  if (!use_mfma_path(s, dtype) || !varlen_grids_fit(s, nseq)) return 0;
+  const ChainPlan pl = varlen_chain_plan_for(s, nseq, compute_units);
+  if (!pl.ok) return 0;
+  if (seglen) *seglen = pl.seglen;
+  return pl.nseg;
 }
 
 ssd_status ssd_chunk_scan_fwd_varlen(const void* x, const void* dt, const float* A, const void* B,
@@ -465,9 +491,10 @@ ssd_status ssd_chunk_scan_fwd_varlen(const void* x, const void* dt, const float*
   if (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) return SSD_ERR_ALIGN;
   const FwdShape s = varlen_shape(total_tokens, nseq, nheads, headdim, dstate, ngroups, chunk_len);
   if (!use_mfma_path(s, dtype) || !varlen_grids_fit(s, nseq)) return SSD_ERR_SHAPE;
-  const WsLayout w = ws_layout(s, true, ChainPlan{});
-  const size_t tab_off = varlen_table_offset(w);
-  if (workspace_bytes < tab_off + size_t(s.nc) * sizeof(int4)) return SSD_ERR_WORKSPACE;
+  const ChainPlan pl = varlen_chain_plan_for(s, nseq, device_units());
+  const VarlenWs v = varlen_ws(s, pl);
+  const WsLayout& w = v.w;
+  if (workspace_bytes < v.total) return SSD_ERR_WORKSPACE;
 
   const size_t e = esize(dtype);
   const size_t tok = size_t(total_tokens);
@@ -475,7 +502,7 @@ ssd_status ssd_chunk_scan_fwd_varlen(const void* x, const void* dt, const float*
   const size_t bcb = tok * ngroups * dstate * e, hb = size_t(nheads) * sizeof(float);
   const size_t stb = size_t(nseq) * nheads * dstate * headdim * sizeof(float);
   const size_t cub = size_t(nseq + 1) * sizeof(int);
-  const size_t wsb = tab_off + size_t(s.nc) * sizeof(int4);
+  const size_t wsb = v.total;
   struct In {
     const void* p;
     size_t n;
@@ -497,11 +524,44 @@ ssd_status ssd_chunk_scan_fwd_varlen(const void* x, const void* dt, const float*
   float* S = reinterpret_cast<float*>(ws + w.st);
   uint16_t* Hb = reinterpret_cast<uint16_t*>(ws + w.hb);
   uint16_t* CB = reinterpret_cast<uint16_t*>(ws + w.cb);
-  int4* tab = reinterpret_cast<int4*>(ws + tab_off);
+  int4* tab = reinterpret_cast<int4*>(ws + v.tab);
+  if (pl.ok) {
+    // the fused walk over segments of at most pl.seglen chunks (a
+    // sequence's first from its initial state, the others from zero), the
+    // recurrence over each sequence's segments, and chunk_scan with the
+    // segment correction. The walk reads init_states before the recurrence
+    // writes any final state, and the recurrence reads a sequence's initial
+    // state (only one without tokens) before it writes that sequence's final
+    // state, so final_states may be init_states.
+    int4* stab = reinterpret_cast<int4*>(ws + v.stab);
+    float* cdec = reinterpret_cast<float*>(ws + w.cdec);
+    float* segdec = reinterpret_cast<float*>(ws + w.segdec);
+    if (launch_varlen_table(cu_seqlens, nseq, total_tokens, chunk_len, tab, pl.seglen, stab, hs) != hipSuccess)
+      return SSD_ERR_HIP;
+    if (launch_chunk_state_chain_varlen(s, pl, x, B, C, dt, A, Acs, dtq, Hb, init_states, S, CB, cdec, segdec, tab,
+                                        stab, nseq, hs) != hipSuccess)
+      return SSD_ERR_HIP;
+    FwdShape ss = s;
+    ss.nc = pl.nseg;
+    if (launch_state_passing_varlen_segments(ss, S, segdec, cu_seqlens, nseq, chunk_len * pl.seglen, init_states,
+                                             final_states, hs) != hipSuccess)
+      return SSD_ERR_HIP;
+    SegStates sg;
+    sg.Hin = S;
+    sg.cdec = cdec;
+    sg.nseg = pl.nseg;
+    sg.seglen = pl.seglen;
+    sg.var = true;
+    if (launch_chunk_scan_mfma(s, x, CB, C, Acs, dtq, Hb, D, y, tab, hs, StageEv{}, sg) != hipSuccess)
+      return SSD_ERR_HIP;
+    return launched(hs);
+  }
+  // per chunk: chunk states, the recurrence per sequence, chunk_scan.
   // state_passing reads each sequence's initial state (whole tile, into
   // LDS) before it writes that sequence's final state, so final_states may
   // be init_states.
-  if (launch_varlen_table(cu_seqlens, nseq, total_tokens, chunk_len, tab, hs) != hipSuccess) return SSD_ERR_HIP;
+  if (launch_varlen_table(cu_seqlens, nseq, total_tokens, chunk_len, tab, 0, nullptr, hs) != hipSuccess)
+    return SSD_ERR_HIP;
   if (launch_chunk_state_mfma(s, x, B, C, dt, A, Acs, dtq, S, CB, tab, hs) != hipSuccess) return SSD_ERR_HIP;
   if (launch_state_passing_varlen(s, S, Hb, Acs, cu_seqlens, nseq, init_states, final_states, hs) != hipSuccess)
     return SSD_ERR_HIP;

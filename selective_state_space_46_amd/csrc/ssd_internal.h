@@ -65,7 +65,17 @@ __device__ __forceinline__ float exp_fast(float x) {
 // (a chunk of sequence i starts before sequence i+1 does, and i grows by
 // one), and the last slot is below ceil(T / Q) + nseq. A table gives each
 // slot tab[c] = {first row, valid tokens (0: unused slot), sequence, flags
-// (bit 0: first chunk of its sequence, bit 1: last)}.
+// (bit 0: first chunk of its sequence, bit 1: last, bit 2: in the
+// sequence's first segment, bits 3 and up: its segment slot)}.
+//
+// Segments (the fused walk over packed sequences): each sequence's chunks
+// are cut into runs of at most L, which take segment slots the way chunks
+// take chunk slots, with Q L tokens in place of Q: segment m of sequence i
+// is slot floor(cu[i] / (Q L)) + i + m. A sequence of len tokens has
+// ceil(len / (Q L)) segments, the last ending at slot floor((cu[i] + len) /
+// (Q L)) + i at most, so floor(T / (Q L)) + nseq slots hold them all. The
+// segment table gives stab[m] = {first chunk slot, chunks (0: unused slot),
+// sequence, 1 for a sequence's first segment}.
 // ---------------------------------------------------------------------------
 struct ChunkRows {
   long r0;   // first token row
@@ -80,17 +90,60 @@ __device__ __forceinline__ ChunkRows chunk_rows(const int4* tab, int b, int c, i
   return ChunkRows{long(b) * T + long(c) * Q, min(Q, T - c * Q)};
 }
 
+// A chunk slot's rows for kernels that read at least one row of every chunk
+// they visit: the first row clamped into [0, T) and 1 .. Q valid tokens,
+// whatever the entry (the table's entries already are).
+__device__ __forceinline__ ChunkRows slot_rows(const int4* tab, int c, int T, int Q) {
+  const int4 e = tab[c];
+  const int r0 = min(max(e.x, 0), T - 1);
+  return ChunkRows{long(r0), min(max(min(e.y, T - r0), 1), Q)};
+}
+
+__host__ __device__ __forceinline__ int clamp_int(int v, int lo, int hi) { return v < lo ? lo : v > hi ? hi : v; }
+
 // The token span of sequence i: offsets are clamped into [0, T] and a span
 // never ends before it starts, so any offsets give in-bounds spans.
 // Well-formed offsets (0 = cu[0] <= ... <= cu[nseq] = T) are used as given.
-__device__ __forceinline__ void varlen_span(const int* cu, int i, int T, int& s0, int& len) {
-  s0 = min(max(cu[i], 0), T);
-  const int s1 = max(s0, min(max(cu[i + 1], 0), T));
+__host__ __device__ __forceinline__ void varlen_span(const int* cu, int i, int T, int& s0, int& len) {
+  s0 = clamp_int(cu[i], 0, T);
+  const int s1 = clamp_int(cu[i + 1], s0, T);
   len = s1 - s0;
 }
 
-// first chunk slot of sequence i, which starts at token s0
-__device__ __forceinline__ int varlen_first_slot(int s0, int i, int Q) { return s0 / Q + i; }
+// first chunk slot of sequence i, which starts at token s0 (with Q L for Q:
+// its first segment slot)
+__host__ __device__ __forceinline__ int varlen_first_slot(int s0, int i, int Q) { return s0 / Q + i; }
+
+// chunk slots for T tokens in nseq sequences
+__host__ __device__ __forceinline__ int varlen_slots(int T, int nseq, int Q) { return (T + Q - 1) / Q + nseq; }
+
+// segment slots for T tokens in nseq sequences, QL = Q L tokens per segment
+__host__ __device__ __forceinline__ int varlen_seg_slots(int T, int nseq, int QL) { return T / QL + nseq; }
+
+// The table entries of sequence i (tokens s0 .. s0 + len - 1): its chunk
+// slots, and with L > 0 (stab not null) its segments and each chunk's
+// segment slot in the flags. Entries past nslots / nsegslots are never
+// reached for a span from varlen_span; they are skipped all the same.
+__host__ __device__ inline void varlen_fill(int i, int s0, int len, int Q, int L, int4* tab, int nslots,
+                                            int4* stab, int nsegslots) {
+  const int nch = (len + Q - 1) / Q;
+  const int first = varlen_first_slot(s0, i, Q);
+  const int sfirst = L > 0 ? varlen_first_slot(s0, i, Q * L) : 0;
+  for (int k = 0; k < nch; ++k) {
+    const int c = first + k;
+    if (c >= nslots) break;
+    const int m = L > 0 ? k / L : 0;
+    const int flags = (k == 0 ? 1 : 0) | (k == nch - 1 ? 2 : 0) | (m == 0 ? 4 : 0) | (L > 0 ? (sfirst + m) << 3 : 0);
+    tab[c] = int4{s0 + k * Q, len - k * Q < Q ? len - k * Q : Q, i, flags};
+  }
+  if (L > 0 && stab) {
+    const int nsg = (nch + L - 1) / L;
+    for (int m = 0; m < nsg; ++m) {
+      if (sfirst + m >= nsegslots) break;
+      stab[sfirst + m] = int4{first + m * L, nch - m * L < L ? nch - m * L : L, i, m == 0 ? 1 : 0};
+    }
+  }
+}
 
 // ---------------------------------------------------------------------------
 // Problem shape of one forward call.
@@ -117,6 +170,9 @@ struct ChainPlan {
   bool ok = false;
   int nseg = 1, seglen = 0;
   bool two = false;
+  // packed sequences: nseg segment slots of at most seglen chunks each
+  // (always segmented, whatever nseg)
+  bool var = false;
 };
 // allow_segments = false: whole rows only (the backward's walks). The plan
 // for a device with `cus` compute units, and for the current device.
@@ -124,6 +180,11 @@ ChainPlan chunk_state_chain_plan_for(const FwdShape& s, int cus, bool allow_segm
 ChainPlan chunk_state_chain_plan(const FwdShape& s, bool allow_segments);
 // pl.ok and its segments cover the row's chunks exactly, each at least one
 bool chain_plan_valid(const FwdShape& s, const ChainPlan& pl);
+// Packed sequences (s: batch 1, T packed tokens, nc chunk slots) through the
+// fused walk: segments of the smallest length L that lets one walk per
+// (segment slot, 64 columns) run at once on `cus` units; ok = false where no
+// L does (the per-chunk path runs).
+ChainPlan varlen_chain_plan_for(const FwdShape& s, int nseq, int cus);
 // compute units of the current device (read once per device; 0 without one)
 constexpr int kMaxDevices = 64;
 int device_units();
@@ -172,7 +233,8 @@ inline WsLayout ws_layout(const FwdShape& s, bool mfma, const ChainPlan& pl) {
   const size_t row = size_t(s.b) * s.H * s.nc * s.Q * sizeof(float);
   const size_t nst = size_t(s.b) * s.nc * s.H * s.N * s.P;
   const bool fused = mfma && pl.ok;
-  const size_t nstf = !fused ? nst : pl.nseg > 1 ? size_t(s.b) * pl.nseg * s.H * s.N * s.P : 0;
+  const bool seg = fused && (pl.nseg > 1 || pl.var);
+  const size_t nstf = !fused ? nst : seg ? size_t(s.b) * pl.nseg * s.H * s.N * s.P : 0;
   w.acs = 0;
   w.dtq = align_up(w.acs + row, 256);
   w.st = align_up(w.dtq + row, 256);
@@ -184,7 +246,6 @@ inline WsLayout ws_layout(const FwdShape& s, bool mfma, const ChainPlan& pl) {
   w.cb = align_up(w.hb + nst * sizeof(uint16_t), 256);
   const size_t lpc = size_t(s.Q) / 32, ntile = lpc * (lpc + 1) / 2;
   w.cdec = align_up(w.cb + size_t(s.b) * s.nc * s.G * ntile * 1024 * sizeof(uint16_t), 256);
-  const bool seg = fused && pl.nseg > 1;
   w.segdec = align_up(w.cdec + (seg ? size_t(s.b) * s.H * s.nc * sizeof(float) : 0), 256);
   w.total = align_up(w.segdec + (seg ? size_t(s.b) * s.H * pl.nseg * sizeof(float) : 0), 256);
   return w;
@@ -240,6 +301,18 @@ hipError_t launch_chunk_state_chain(const FwdShape& s, const ChainPlan& pl, cons
                                     const void* C, const void* dt, const float* A, float* Acs, float* dtq,
                                     uint16_t* Hb, const float* init, float* fin, uint16_t* CB, float* cdec,
                                     float* segdec, hipStream_t st, const StageEv& ev = StageEv{});
+// Packed sequences (pl from varlen_chain_plan_for; s: batch 1, nc chunk
+// slots): one walk per (segment slot, 64 columns) over the segment table
+// stab, rows from the chunk table tab; a sequence's first segment starts
+// from its initial state (init [nseq, H, N, P], may be null), the others
+// from zero. Hb the local states per slot, segS each segment's last local
+// state ([pl.nseg, H, P * N] fp32, fragment order), cdec [H, nc] and segdec
+// [H, pl.nseg], the tiles CB per slot.
+hipError_t launch_chunk_state_chain_varlen(const FwdShape& s, const ChainPlan& pl, const void* x, const void* B,
+                                           const void* C, const void* dt, const float* A, float* Acs, float* dtq,
+                                           uint16_t* Hb, const float* init, float* segS, uint16_t* CB, float* cdec,
+                                           float* segdec, const int4* tab, const int4* stab, int nseq,
+                                           hipStream_t st, const StageEv& ev = StageEv{});
 // The same for the backward's recomputation: the states entering each chunk
 // as fp32 in Hst ([b, c, h, p, n], what state_passing leaves over the chunk
 // states) and the C B^T tiles as fp32 in both orientations (CBf, CBt, as
@@ -273,6 +346,14 @@ hipError_t launch_state_passing(const FwdShape& s, float* S, uint16_t* Hb, const
 hipError_t launch_state_passing_varlen(const FwdShape& s, const float* S, uint16_t* Hb, const float* Acs,
                                        const int* cu, int nseq, const float* init, float* final_state,
                                        hipStream_t st, const StageEv& ev = StageEv{});
+// The same over the fused walk's segments (s.nc = segment slots, QL tokens
+// per segment): S holds each segment's last local state (fragment order),
+// overwritten in place by the state entering each segment, which is zero
+// for a sequence's first (its walk started from init); segdec [H, s.nc] the
+// segments' summed decay exponents; final_state as above.
+hipError_t launch_state_passing_varlen_segments(const FwdShape& s, float* S, const float* segdec, const int* cu,
+                                                int nseq, int QL, const float* init, float* final_state,
+                                                hipStream_t st, const StageEv& ev = StageEv{});
 
 // Generic path reads Hst (fp32, [b, nc, H, P, N]); MFMA path reads Hb (bf16)
 // and the C B^T tiles CB.
@@ -282,11 +363,14 @@ hipError_t launch_chunk_scan(const FwdShape& s, ssd_dtype type, bool mfma, const
                              const float* D, void* y, hipStream_t st, const StageEv& ev = StageEv{});
 // Segmented states (ChainPlan::nseg > 1): the state entering chunk c of
 // segment k >= 1 is Hb_c + exp(cdec_c) Hin_k, Hin [b, nseg, H, P * N] fp32,
-// each head's in fragment order (hb_off).
+// each head's in fragment order (hb_off). var: packed sequences (with the
+// chunk table; dstate 128 or 256), each chunk's segment slot from the
+// table's flags, no correction in a sequence's first segment.
 struct SegStates {
   const float* Hin = nullptr;
   const float* cdec = nullptr;
   int nseg = 1, seglen = 0;
+  bool var = false;
 };
 hipError_t launch_chunk_scan_mfma(const FwdShape& s, const void* x, const uint16_t* CB,
                                   const void* C, const float* Acs, const float* dtq,
@@ -295,9 +379,11 @@ hipError_t launch_chunk_scan_mfma(const FwdShape& s, const void* x, const uint16
                                   const SegStates& seg = SegStates{});
 
 // Packed variable-length sequences (varlen.hip): the chunk table has
-// varlen_slots(T, nseq, Q) int4 entries.
-int varlen_slots(int T, int nseq, int Q);
-hipError_t launch_varlen_table(const int* cu, int nseq, int T, int Q, int4* tab, hipStream_t st);
+// varlen_slots(T, nseq, Q) int4 entries; with stab (not null) also the
+// segment table of varlen_seg_slots(T, nseq, Q L) entries, segments of at
+// most L chunks.
+hipError_t launch_varlen_table(const int* cu, int nseq, int T, int Q, int4* tab, int L, int4* stab,
+                               hipStream_t st);
 
 // Element-wise stages next to the core (epilogue.hip).
 hipError_t launch_gated_rmsnorm(ssd_dtype type, const void* y, const void* z, const float* w, void* out,

@@ -52,12 +52,16 @@ __device__ __forceinline__ void store_out(float* S, uint16_t* Hb, size_t idx, si
 // grid: b * H * ceil(P/kTP) * ceil(N/kTN) work-groups; requires N % 4 == 0.
 // VARLEN: b counts sequences instead of batch rows, and the chunks of
 // sequence b are its slots of the one packed row (cu: sequence offsets, T:
-// packed tokens); init / fin are [nseq, H, N, P] like a batch of nseq rows.
+// packed tokens, span tokens per slot); init / fin are [nseq, H, N, P] like a
+// batch of nseq rows. segs (with VARLEN): the slots are the fused walk's
+// segments (span = Q L), whose walks started from the sequence's initial
+// state, so the recurrence starts from zero and init only passes through a
+// sequence without tokens.
 template <bool VARLEN>
 __global__ __launch_bounds__(kThreads) void state_passing_tiled(
     float* __restrict__ S, uint16_t* __restrict__ Hb, const float* __restrict__ Acs,
     const float* __restrict__ init, float* __restrict__ fin, int H, int P, int N, int Q, int nc,
-    const int* __restrict__ cu, int T, int sfrag) {
+    const int* __restrict__ cu, int T, int sfrag, int span, int segs) {
   __shared__ float tile[kTN][kTP + 1];
   const int tpn = (N + kTN - 1) / kTN, tpp = (P + kTP - 1) / kTP;
   int bid = blockIdx.x;
@@ -72,9 +76,20 @@ __global__ __launch_bounds__(kThreads) void state_passing_tiled(
   const bool active = p < P && n < N;
   const size_t sbh = size_t(N) * P;         // elements of one (b, h) state
 
-  // H_0: init transposed through LDS (or zero)
+  // the chunks this work-group walks: rows [crow, crow + ncw) of the chunk
+  // arrays of batch row brow
+  int brow = b, crow = 0, ncw = nc;
+  if constexpr (VARLEN) {
+    int s0, len;
+    varlen_span(cu, b, T, s0, len);
+    brow = 0;
+    crow = varlen_first_slot(s0, b, span);
+    ncw = (len + span - 1) / span;
+  }
+
+  // H_0: init transposed through LDS (or zero); uniform over the work-group
   f32x4 cur = f32x4{0.f, 0.f, 0.f, 0.f};
-  if (init) {
+  if (init && !(VARLEN && segs && ncw > 0)) {
     for (int e = tid; e < kTN * kTP; e += kThreads) {
       const int nn = e / kTP, pp = e % kTP;
       float v = 0.f;
@@ -84,17 +99,6 @@ __global__ __launch_bounds__(kThreads) void state_passing_tiled(
     __syncthreads();
     cur = f32x4{tile[4 * nq][pi], tile[4 * nq + 1][pi], tile[4 * nq + 2][pi], tile[4 * nq + 3][pi]};
     __syncthreads();
-  }
-
-  // the chunks this work-group walks: rows [crow, crow + ncw) of the chunk
-  // arrays of batch row brow
-  int brow = b, crow = 0, ncw = nc;
-  if constexpr (VARLEN) {
-    int s0, len;
-    varlen_span(cu, b, T, s0, len);
-    brow = 0;
-    crow = varlen_first_slot(s0, b, Q);
-    ncw = (len + Q - 1) / Q;
   }
 
   if (active) {
@@ -294,7 +298,20 @@ hipError_t launch_state_passing_varlen(const FwdShape& s, const float* S, uint16
   // S is only read: the passed states go to Hb
   hipExtLaunchKernelGGL(state_passing_tiled<true>, dim3(unsigned(tiles)), dim3(kThreads), 0, st, ev.start,
                         ev.stop, 0, const_cast<float*>(S), Hb, Acs, init, final_state, s.H, s.P, s.N, s.Q,
-                        s.nc, cu, s.T, 0);
+                        s.nc, cu, s.T, 0, s.Q, 0);
+  return hipGetLastError();
+}
+
+hipError_t launch_state_passing_varlen_segments(const FwdShape& s, float* S, const float* segdec, const int* cu,
+                                                int nseq, int QL, const float* init, float* final_state,
+                                                hipStream_t st, const StageEv& ev) {
+  if (s.N % 32 || s.P % 32 || s.b != 1 || QL < 1) return hipErrorInvalidValue;
+  const long tiles = long(nseq) * s.H * ((s.P + kTP - 1) / kTP) * ((s.N + kTN - 1) / kTN);
+  // the decay of segment k is segdec[h, k] (a "chunk" of one entry); the
+  // states entering each segment overwrite S (fragment order)
+  hipExtLaunchKernelGGL(state_passing_tiled<true>, dim3(unsigned(tiles)), dim3(kThreads), 0, st, ev.start,
+                        ev.stop, 0, S, static_cast<uint16_t*>(nullptr), segdec, init, final_state, s.H, s.P, s.N,
+                        1, s.nc, cu, s.T, 1, QL, 1);
   return hipGetLastError();
 }
 
@@ -306,7 +323,7 @@ hipError_t launch_state_passing(const FwdShape& s, float* S, uint16_t* Hb, const
     const long tiles = long(s.b) * s.H * ((s.P + kTP - 1) / kTP) * ((s.N + kTN - 1) / kTN);
     hipExtLaunchKernelGGL(state_passing_tiled<false>, dim3(unsigned(tiles)), dim3(kThreads), 0, st, ev.start,
                           ev.stop, 0, S, Hb, Acs, init, final_state, s.H, s.P, s.N, s.Q, s.nc,
-                          static_cast<const int*>(nullptr), 0, sfrag ? 1 : 0);
+                          static_cast<const int*>(nullptr), 0, sfrag ? 1 : 0, s.Q, 0);
   } else {
     if (Hb) return hipErrorInvalidValue;     // the MFMA path never has N % 4 != 0
     const long total = long(s.b) * s.H * s.N * s.P;

@@ -9,8 +9,10 @@
 // valid tokens (or Q). Chunk k of sequence i takes slot floor(cu[i] / Q) +
 // i + k (ssd_internal.h), so a sequence's slots follow from its own offset
 // alone; the table lists, for the kernels that walk slots, every slot's
-// first token row, valid tokens, sequence and first/last flags. Slots that
-// no chunk takes stay {0, 0, 0, 0}.
+// first token row, valid tokens, sequence and flags. Slots that no chunk
+// takes stay {0, 0, 0, 0}. For the fused walk over packed sequences the same
+// launch writes the segment table (each sequence's chunks in runs of at most
+// L, ssd_internal.h) and each chunk's segment slot in its flags.
 //
 // cu_seqlens lives on the device and is not seen by the host, so the spans
 // are clamped (varlen_span): malformed offsets give unspecified but
@@ -22,35 +24,33 @@ namespace {
 
 constexpr int kTabThreads = 1024;
 
-// one work-group: clear every slot, then each thread writes the chunks of
-// sequences tid, tid + 1024, ...
+// one work-group: clear every slot, then each thread writes the entries of
+// sequences tid, tid + 1024, ... (varlen_fill: slots < nslots and segment
+// slots < nsegslots for any clamped span)
 __global__ __launch_bounds__(kTabThreads) void varlen_table_kernel(const int* __restrict__ cu, int nseq,
                                                                    int T, int Q, int nslots,
-                                                                   int4* __restrict__ tab) {
+                                                                   int4* __restrict__ tab, int L,
+                                                                   int4* __restrict__ stab, int nsegslots) {
   const int tid = threadIdx.x;
   for (int c = tid; c < nslots; c += kTabThreads) tab[c] = int4{0, 0, 0, 0};
+  if (stab)
+    for (int c = tid; c < nsegslots; c += kTabThreads) stab[c] = int4{0, 0, 0, 0};
   __syncthreads();   // the clears are ordered before the entries below
   for (int i = tid; i < nseq; i += kTabThreads) {
     int s0, len;
     varlen_span(cu, i, T, s0, len);
-    const int nch = (len + Q - 1) / Q;
-    const int first = varlen_first_slot(s0, i, Q);
-    for (int k = 0; k < nch; ++k) {
-      const int c = first + k;                // < nslots for any clamped span
-      if (c >= nslots) break;
-      const int flags = (k == 0 ? 1 : 0) | (k == nch - 1 ? 2 : 0);
-      tab[c] = int4{s0 + k * Q, min(Q, len - k * Q), i, flags};
-    }
+    varlen_fill(i, s0, len, Q, stab ? L : 0, tab, nslots, stab, nsegslots);
   }
 }
 
 }  // namespace
 
-int varlen_slots(int T, int nseq, int Q) { return (T + Q - 1) / Q + nseq; }
-
-hipError_t launch_varlen_table(const int* cu, int nseq, int T, int Q, int4* tab, hipStream_t st) {
+hipError_t launch_varlen_table(const int* cu, int nseq, int T, int Q, int4* tab, int L, int4* stab,
+                               hipStream_t st) {
+  if (stab && (L < 1 || long(Q) * L > 0x7fffffffL)) return hipErrorInvalidValue;
+  const int nsegslots = stab ? varlen_seg_slots(T, nseq, Q * L) : 0;
   hipLaunchKernelGGL(varlen_table_kernel, dim3(1), dim3(kTabThreads), 0, st, cu, nseq, T, Q,
-                     varlen_slots(T, nseq, Q), tab);
+                     varlen_slots(T, nseq, Q), tab, L, stab, nsegslots);
   return hipGetLastError();
 }
 

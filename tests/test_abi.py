@@ -38,7 +38,7 @@ def test_header_declares_the_entry_points():
                                        "ssd_chunk_scan_bwd", "ssd_chunk_scan_bwd_workspace",
                                        "ssd_chunk_scan_fwd_fused_states", "ssd_chunk_scan_bwd_fused_walks",
                                        "ssd_chunk_scan_fwd_plan", "ssd_chunk_scan_fwd_noalloc",
-                                       "ssd_mfma_bf16_probe"}
+                                       "ssd_chunk_scan_fwd_varlen_plan", "ssd_mfma_bf16_probe"}
 
 
 def test_fused_states_query_rejects_what_the_forward_rejects():

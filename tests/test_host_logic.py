@@ -11,6 +11,7 @@ on the uniform tail branch the kernel takes for it, and that the half picked
 out of each word is element e itself. A second group checks the cut of a
 row into segments (every chunk in exactly one segment, segments in order)."""
 import itertools
+import os
 
 import numpy as np
 import pytest
@@ -223,3 +224,141 @@ def test_traffic_digest_ignores_comments_only():
     c = "int f(int x) { return x + 2; }\n"
     assert bench._code_only(a) == bench._code_only(b)
     assert bench._code_only(a) != bench._code_only(c)
+
+
+# ---------------------------------------------------------------- packed sequences through the walk
+
+VARLEN_PLAN_SHAPES = [
+    # T, nseq, H, P, N, G, Q: the packed 130M workload, few and many sequences, both dstates, headdim 32/128
+    (16384, 13, 24, 64, 128, 1, 256), (16384, 13, 24, 64, 128, 1, 128), (16384, 13, 24, 64, 128, 1, 64),
+    (1800, 3, 4, 64, 128, 1, 128), (131072, 4, 24, 64, 256, 1, 256), (5000, 40, 24, 64, 128, 1, 256),
+    (4000, 9, 8, 32, 128, 2, 128), (3000, 5, 2, 128, 256, 1, 128), (700, 300, 24, 64, 128, 1, 256),
+    (1, 1, 2, 64, 128, 1, 64), (375, 3, 2, 64, 256, 1, 128),
+]
+
+
+def _varlen_plan(T, nseq, H, P, N, G, Q, cus=256):
+    import selective_state_space_46_amd as ssd
+    return ssd.ssd_chunk_scan_fwd_varlen_plan(T, nseq, H, P, N, G, Q, ssd.SSD_BF16, cus)
+
+
+@pytest.mark.parametrize("shape", VARLEN_PLAN_SHAPES)
+def test_varlen_walk_plan(shape):
+    """The packed plan: floor(T / (Q L)) + nseq segment slots with the
+    smallest L whose walks all fit a 256-unit device at once (two per unit at
+    dstate 128 with chunk_len >= 128), but at most 16 chunks (then more walks
+    than fit at once); none where not even one segment per sequence fits."""
+    T, nseq, H, P, N, G, Q = shape
+    nslot, L = _varlen_plan(*shape)
+    cpr = H * P // 64
+    cap = (512 if N == 128 and Q >= 128 else 256)
+    if nslot == 0:
+        assert L == 0 and nseq * cpr > cap
+        return
+    assert 1 <= L <= 16 and nslot == T // (Q * L) + nseq
+    assert nslot * cpr <= cap or L == 16
+    if 1 < L < 16:
+        assert (T // (Q * (L - 1)) + nseq) * cpr > cap
+    # other unit counts and rejected sizes
+    assert _varlen_plan(*shape, cus=0) == (0, 0)
+    import selective_state_space_46_amd as ssd
+    assert ssd.ssd_chunk_scan_fwd_varlen_plan(T, nseq, H, P, 64, G, Q, ssd.SSD_BF16, 256) == (0, 0)
+    assert ssd.ssd_chunk_scan_fwd_varlen_plan(T, nseq, H, P, N, G, Q, ssd.SSD_F32, 256) == (0, 0)
+    assert ssd.ssd_chunk_scan_fwd_varlen_plan(T, 0, H, P, N, G, Q, ssd.SSD_BF16, 256) == (0, 0)
+
+
+@pytest.fixture(scope="module")
+def varlen_tables(tmp_path_factory):
+    """builds the packed-sequence tables on the host with the library's own
+    varlen_span / varlen_fill (tests/varlen_tables_driver.hip)"""
+    import subprocess
+    from selective_state_space_46_amd import build
+    try:
+        hipcc = build.hipcc()
+    except RuntimeError:
+        pytest.skip("hipcc is not installed")
+    here = os.path.dirname(os.path.abspath(__file__))
+    root = os.path.dirname(here)
+    exe = str(tmp_path_factory.mktemp("vt") / "varlen_tables")
+    r = subprocess.run([hipcc, f"--offload-arch={build.ARCH}", "-O1",
+                        "-I", os.path.join(root, "selective_state_space_46_amd", "csrc"),
+                        "-I", os.path.join(root, "include"), "-o", exe,
+                        os.path.join(here, "varlen_tables_driver.hip")], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-3000:]
+
+    def run(T, Q, L, cu):
+        inp = f"{T} {len(cu) - 1} {Q} {L}\n" + " ".join(str(int(v)) for v in cu) + "\n"
+        out = subprocess.run([exe], input=inp, capture_output=True, text=True, check=True).stdout.split()
+        v = np.array(out, dtype=np.int64)
+        nslots, nseg = int(v[0]), int(v[1])
+        tab = v[2:2 + 4 * nslots].reshape(nslots, 4)
+        stab = v[2 + 4 * nslots:].reshape(nseg, 4)
+        return tab, stab
+    return run
+
+
+def _varlen_cases():
+    rng = np.random.default_rng(7100)
+    cases = []
+    for Q in (64, 128, 256):
+        for L in (1, 2, 3, 8):
+            lens = [300, 0, 17, 256, 1, 129, 64, 511, 33, 3515, 2048, 0]
+            cases.append((Q, L, np.concatenate([[0], np.cumsum(lens)]).tolist(), int(sum(lens))))
+            for _ in range(4):
+                n = int(rng.integers(1, 20))
+                lens = rng.integers(0, 5 * Q, size=n)
+                cases.append((Q, L, np.concatenate([[0], np.cumsum(lens)]).tolist(), max(1, int(lens.sum()))))
+            # malformed: decreasing, negative, past the end
+            cases.append((Q, L, [0, 150, 90, 400, -5, 10**6], 200))
+            cases.append((Q, L, [-40, 7000, 3, 3, 2999], 3000))
+    return cases
+
+
+@pytest.mark.parametrize("case", _varlen_cases())
+def test_varlen_tables(varlen_tables, case):
+    """Every sequence's chunks fill consecutive slots with their rows, valid
+    tokens, sequence, flags and segment slot; its segments of at most L
+    chunks fill consecutive segment slots and cover exactly its chunk slots;
+    no entry is dropped by the table bounds (so none is needed: the slot
+    counts hold every clamped span); everything else stays empty. Offsets are
+    clamped as the device clamps them."""
+    Q, L, cu, T = case
+    tab, stab = varlen_tables(T, Q, L, cu)
+    nseq = len(cu) - 1
+    assert len(tab) == -(-T // Q) + nseq and len(stab) == T // (Q * L) + nseq
+    want_tab = np.zeros_like(tab)
+    want_stab = np.zeros_like(stab)
+    for i in range(nseq):
+        s0 = min(max(cu[i], 0), T)
+        s1 = min(max(cu[i + 1], s0), T)
+        ln = s1 - s0
+        nch = -(-ln // Q)
+        first, sfirst = s0 // Q + i, s0 // (Q * L) + i
+        for k in range(nch):
+            m = k // L
+            flags = (k == 0) | ((k == nch - 1) << 1) | ((m == 0) << 2) | ((sfirst + m) << 3)
+            want_tab[first + k] = (s0 + k * Q, min(Q, ln - k * Q), i, flags)
+        for m in range(-(-nch // L)):
+            want_stab[sfirst + m] = (first + m * L, min(L, nch - m * L), i, int(m == 0))
+    assert np.array_equal(tab, want_tab)
+    assert np.array_equal(stab, want_stab)
+    # the walks' view: each used segment slot's chunk slots are in range and
+    # hold rows inside the tokens. With well-formed offsets they also hold its
+    # sequence and name it as their segment, and together they are the used
+    # chunk slots, each once (malformed offsets may give two sequences one
+    # slot: the later entry wins, results are unspecified, accesses stay in
+    # bounds)
+    well_formed = cu[0] == 0 and cu[-1] == T and all(a <= b for a, b in zip(cu, cu[1:]))
+    seen = np.zeros(len(tab), dtype=int)
+    for m, (c0, cnt, i, fst) in enumerate(stab):
+        if cnt == 0:
+            continue
+        assert 1 <= cnt <= L and 0 <= c0 and c0 + cnt <= len(tab)
+        for c in range(c0, c0 + cnt):
+            r0, n, seq, flags = tab[c]
+            assert 0 <= r0 and 1 <= n <= Q and r0 + n <= T and 0 <= flags >> 3 < len(stab)
+            if well_formed:
+                assert seq == i and flags >> 3 == m and bool(flags & 4) == bool(fst)
+            seen[c] += 1
+    if well_formed:
+        assert np.array_equal(seen, (tab[:, 1] > 0).astype(int))

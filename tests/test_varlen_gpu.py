@@ -5,7 +5,10 @@ against the equal-length forward run on the same sequences.
 Bar: relative L2 <= 1e-2 on y and on the final states (bf16 tensors, fp32
 states). Sequence layouts cover empty sequences, sequences shorter than a
 chunk, exact multiples of the chunk and long ones, several chunk lengths
-(one and several chunks per 256-token work-group in chunk_scan)."""
+(one and several chunks per 256-token work-group in chunk_scan). At dstate
+128 and 256 the call takes the fused walk over segments of each sequence
+(ssd_chunk_scan_fwd_varlen_plan), sequences longer than a segment included;
+at dstate 32 and 64 the per-chunk launches."""
 import numpy as np
 import pytest
 
@@ -27,6 +30,16 @@ def _inputs(total, H, P, N, G, nseq, seed, with_init=True):
     return {k: (v[0] if k in ("x", "dt", "B", "C") else v) for k, v in inp.items()} | {"init": init}
 
 
+def _plan(inp, cu, Q):
+    """(segment slots, chunks per segment) the call takes on this device"""
+    import torch
+    import selective_state_space_46_amd as ssd
+    T, H, P = inp["x"].shape
+    N, G = inp["B"].shape[2], inp["B"].shape[1]
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    return ssd.ssd_chunk_scan_fwd_varlen_plan(T, len(cu) - 1, H, P, N, G, Q, ssd.SSD_BF16, cus)
+
+
 def _gpu(inp, cu, Q, final_in_place=False):
     import torch
     import selective_state_space_46_amd as ssd
@@ -45,10 +58,12 @@ def _check(inp, cu, Q, final_in_place=False):
     y_ref, f_ref = oracle.ssd_fwd_varlen(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"], cu,
                                          inp["init"])
     ey, ef = rel_l2(y, y_ref), rel_l2(f, f_ref)
-    print(f"[varlen Q={Q} nseq={len(cu) - 1}] rel_l2 y={ey:.3e} final={ef:.3e}", flush=True)
+    nseg, L = _plan(inp, cu, Q)
+    print(f"[varlen Q={Q} nseq={len(cu) - 1} segment slots={nseg} L={L}] rel_l2 y={ey:.3e} final={ef:.3e}",
+          flush=True)
     assert np.all(np.isfinite(y)) and np.all(np.isfinite(f))
     assert ey <= TOL and ef <= TOL, (ey, ef)
-    return y, f
+    return y, f, y_ref
 
 
 @pytest.mark.parametrize("Q", [64, 128, 256])
@@ -76,16 +91,21 @@ def test_varlen_shapes(P, N):
     _check(inp, cu, 128)
 
 
-def test_varlen_equals_equal_length_batch():
-    """Sequences of one length packed give bit for bit the batched forward."""
+@pytest.mark.parametrize("N", [64, 128])
+def test_varlen_equals_equal_length_batch(N):
+    """Sequences of one length packed against the batched forward on the same
+    rows: bit for bit where both take the per-chunk launches (dstate 64);
+    where the packed call walks segments (dstate 128) the two round
+    differently, and agree within the bf16 bar, each with the oracle too."""
     import torch
     import selective_state_space_46_amd as ssd
-    nseq, L, H, P, N = 3, 600, 4, 64, 128
+    nseq, L, H, P = 3, 600, 4, 64
     w = workloads.with_shape(workloads.MAMBA2_130M, batch=nseq, seqlen=L, nheads=H, headdim=P, dstate=N,
                              init="normal0.1", seed=6300)
     inp = workloads.make_fwd_inputs(w)
     xb, dtb, Bb, Cb = (dev(inp[k], "bf16") for k in ("x", "dt", "B", "C"))
     A, D, init = dev(inp["A"]), dev(inp["D"]), dev(inp["init"])
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
     for Q in (128, 256):
         yb, fb = ssd.ssd_chunk_scan_fwd(xb, dtb, A, Bb, Cb, D, init, Q)
         cu = torch.arange(0, (nseq + 1) * L, L, dtype=torch.int32, device="cuda")
@@ -93,8 +113,37 @@ def test_varlen_equals_equal_length_batch():
                                                A, Bb.reshape(nseq * L, 1, N), Cb.reshape(nseq * L, 1, N), D, cu,
                                                init, Q)
         torch.cuda.synchronize()
-        assert torch.equal(yv.reshape(nseq, L, H, P), yb), Q
-        assert torch.equal(fv, fb), Q
+        walked = ssd.ssd_chunk_scan_fwd_varlen_plan(nseq * L, nseq, H, P, N, 1, Q, ssd.SSD_BF16, cus)[0] > 0
+        batched_walk = ssd.ssd_chunk_scan_fwd_plan(nseq, L, H, P, N, 1, Q, ssd.SSD_BF16, cus)[0] > 0
+        assert walked == (N == 128), (N, Q)
+        if not walked and not batched_walk:
+            assert torch.equal(yv.reshape(nseq, L, H, P), yb), Q
+            assert torch.equal(fv, fb), Q
+            continue
+        y_ref, f_ref = oracle.ssd_fwd(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"], inp["init"])
+        ev, efv = rel_l2(host(yv).reshape(nseq, L, H, P), y_ref), rel_l2(host(fv), f_ref)
+        eb, efb = rel_l2(host(yb), y_ref), rel_l2(host(fb), f_ref)
+        ex, efx = rel_l2(host(yv).reshape(nseq, L, H, P), host(yb)), rel_l2(host(fv), host(fb))
+        print(f"[varlen vs batch N={N} Q={Q}] packed {ev:.3e}/{efv:.3e} batched {eb:.3e}/{efb:.3e} "
+              f"between {ex:.3e}/{efx:.3e}", flush=True)
+        assert max(ev, efv, eb, efb, ex, efx) <= TOL
+
+
+def test_varlen_long_packed_workload():
+    """The long packed workload that bench.py times (131072 tokens in 8
+    sequences of 4.9K .. 28.9K tokens, dstate 256, per-sequence initial
+    states: several segments per sequence), whole output against the oracle,
+    and per sequence."""
+    vw = workloads.VARLEN_LONG
+    vi = workloads.make_varlen_inputs(vw)
+    cu = vi["cu_seqlens"].tolist()
+    inp = {k: vi[k] for k in ("x", "dt", "A", "B", "C", "D", "init")}
+    nseg, L = _plan(inp, cu, vw.chunk_len)
+    assert nseg > 0 and L * vw.chunk_len < max(np.diff(cu)), (nseg, L)
+    y, _, y_ref = _check(inp, cu, vw.chunk_len)
+    worst = max(rel_l2(y[a:b], y_ref[a:b]) for a, b in zip(cu[:-1], cu[1:]))
+    print(f"[varlen long] worst sequence rel_l2 y={worst:.3e}", flush=True)
+    assert worst <= TOL
 
 
 def test_varlen_130m_packed_workload():
@@ -108,15 +157,33 @@ def test_varlen_130m_packed_workload():
     _check(inp, cu, vw.chunk_len)
 
 
-def test_varlen_malformed_offsets_stay_in_bounds():
+@pytest.mark.parametrize("N", [64, 128])
+def test_varlen_malformed_offsets_stay_in_bounds(N):
     """Offsets that decrease or leave [0, T] are clamped on the device: the
-    call completes and writes finite values (results unspecified)."""
+    call completes and writes finite values (results unspecified). dstate 64:
+    the per-chunk launches; 128: the walks over segments, whose tables the
+    clamped spans fill (two sequences may then share a chunk slot)."""
     import torch
     import selective_state_space_46_amd as ssd
-    inp = _inputs(200, 2, 64, 64, 1, 4, seed=6500)
+    inp = _inputs(200, 2, 64, N, 1, 5, seed=6500)
     x, dt, B, C = (dev(inp[k], "bf16") for k in ("x", "dt", "B", "C"))
     A, D = dev(inp["A"]), dev(inp["D"])
-    cu = torch.tensor([0, 150, 90, 400, -5], dtype=torch.int32, device="cuda")
+    cu = torch.tensor([0, 150, 90, 400, -5, 10**6], dtype=torch.int32, device="cuda")
+    print(f"[varlen malformed N={N}] plan {_plan(inp, cu.tolist(), 64)}", flush=True)
     y, f = ssd.ssd_chunk_scan_fwd_varlen(x, dt, A, B, C, D, cu, None, 64)
     torch.cuda.synchronize()
     assert np.all(np.isfinite(host(f)))
+
+
+@pytest.mark.parametrize("Q,N,with_init", [(256, 128, True), (128, 128, False), (64, 128, True), (256, 256, True)])
+def test_varlen_long_sequences_span_segments(Q, N, with_init):
+    """Sequences longer than a segment (chunks past the first segment take the
+    state entering theirs through the recurrence over segments) next to
+    short and empty ones, with and without initial states, final states in
+    place; 24 heads so that segments stay short."""
+    lens = [4000, 0, 90, 2500, 256, 1, 3100]
+    cu = np.concatenate([[0], np.cumsum(lens)]).tolist()
+    inp = _inputs(cu[-1], 24, 64, N, 1, len(lens), seed=6600 + Q + N, with_init=with_init)
+    nseg, L = _plan(inp, cu, Q)
+    assert nseg > 0 and L * Q < max(lens), (nseg, L)
+    _check(inp, cu, Q, final_in_place=with_init)

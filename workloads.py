@@ -273,6 +273,10 @@ class VarlenWorkload:
 # batched 8 x 2048 layer), sequences of 64 .. 4096 tokens
 VARLEN_130M = VarlenWorkload("varlen_130m_T16384_H24_P64_N128_Q256_len64-4096", 16384, 24, 64, 128, 1, 256,
                              seed=4620)
+# long packed sequences on the 131072-token layer's heads: a few sequences of
+# 8K .. 64K tokens
+VARLEN_LONG = VarlenWorkload("varlen_long_T131072_H24_P64_N256_Q256_len8192-65536", 131072, 24, 64, 256, 1, 256,
+                             min_len=8192, max_len=65536, seed=4621)
 
 
 def draw_seqlens(rng: np.random.Generator, total: int, lo: int, hi: int) -> np.ndarray:
