@@ -295,19 +295,20 @@ SSD_API ssd_status ssd_chunk_scan_fwd_varlen(const void *x, const void *dt, cons
  * needed; the call itself reads the current device's count): 0 = a
  * chunk-state launch over every chunk and a recurrence per sequence over its
  * chunks (also for sizes the call rejects); k >= 1 = the fused walks of
- * ssd_chunk_scan_fwd_fused_states, one per (segment, 64 columns), where each
- * sequence's chunks are cut into segments of at most *seglen consecutive
- * chunks (a sequence of len tokens has ceil(len / (chunk_len * seglen))) and
- * k = floor(total_tokens / (chunk_len * seglen)) + nseq bounds the segments
- * of all sequences together. A sequence's first segment starts from its
- * initial state and the others from zero; a recurrence over each sequence's
- * segments and the chunk outputs add the rest, as for the segmented batch
- * rows. *seglen is the smallest that lets all k * nheads * headdim / 64 walks
- * run at once, but at most 16 (more walks than fit at once then queue), and
- * 0 with the per-chunk path, which runs where not even nseq segments fit at
- * once; seglen may be NULL. Used for dstate
- * 128 or 256 and chunk_len a multiple of 64 (headdim 32 needs an even number
- * of heads per group). The results agree up to rounding either way.
+ * ssd_chunk_scan_fwd_fused_states over the packed row of chunks: each
+ * sequence takes ceil(len / chunk_len) chunk slots (slot
+ * floor(cu[i] / chunk_len) + i onwards, ceil(total_tokens / chunk_len) + nseq
+ * slots in all, some unused), and the slots are cut into k segments of
+ * *seglen consecutive slots (the last may have fewer), one walk per segment
+ * and 64 columns, as many as fill the device in one round. A walk restarts
+ * from a sequence's initial state at its first chunk (the state never
+ * crosses from one sequence into the next) and writes the final state of
+ * every sequence that ends inside it; a short recurrence over the segments
+ * gives the state entering each one and completes the sequences that cross
+ * a segment boundary. seglen may be NULL (*seglen is 0 with the per-chunk
+ * path). Used for dstate 128 or 256 and chunk_len a multiple of 64 (headdim
+ * 32 needs an even number of heads per group). The results agree up to
+ * rounding either way.
  */
 SSD_API int ssd_chunk_scan_fwd_varlen_plan(int total_tokens, int nseq, int nheads, int headdim, int dstate,
                                            int ngroups, int chunk_len, ssd_dtype dtype, int compute_units,

@@ -62,14 +62,6 @@ __device__ __forceinline__ int tr_off(int lane, int u, int mt) {
   return lds_off<RB, true>(4 * (lane >> 5) + 8 * u + (q16 >> 2), 32 * mt + 16 * ((lane >> 4) & 1) + 4 * (q16 & 3));
 }
 
-// v, hidden from the optimizer: values derived from it inside a loop are
-// recomputed there instead of being hoisted out of the loop and held in
-// registers for its whole length (the swizzled LDS addresses of the unrolled
-// reads would otherwise take more registers than the MFMA accumulators).
-__device__ __forceinline__ int opaque(int v) {
-  asm volatile("" : "+v"(v));
-  return v;
-}
 
 // Rows 0 .. NROW-1 of a token-major tensor (row stride `stride` elements,
 // RB 16-byte chunks from `col0`) of the chunk, into registers (rows past the

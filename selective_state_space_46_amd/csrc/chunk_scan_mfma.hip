@@ -53,9 +53,10 @@
 // cdec_c <= 0), formed in fp32 where
 // H_c is staged or loaded and rounded to bf16 once. Where exp(cdec_c)
 // underflows to zero (a decayed segment start) the correction is exactly
-// zero and Hin is not read. Packed sequences (VARLEN with SEG) take each
-// chunk's segment slot, and whether its segment is its sequence's first (no
-// correction), from the chunk table's flags.
+// zero and Hin is not read. Packed sequences (VARLEN with SEG): the row of
+// chunk slots is cut into segments the same way; the walk leaves cdec = -inf
+// on every chunk after a sequence begins inside its segment, so only the
+// chunks of the sequence the segment continues take a correction.
 #include "mfma_util.h"
 
 namespace ssd {
@@ -125,17 +126,11 @@ void chunk_scan_mfma_kernel(
     if (rowsv.n <= 0) rowsv = r;
   }
   if (rowsv.n <= 0) return;            // no valid chunk: uniform, before any barrier
-  // SEG: the segment of chunk c (a valid chunk of the super-chunk) and
-  // whether a state from before the segment enters it
+  // SEG: the segment of chunk c and whether a state from before the segment
+  // can enter it
   auto seg_of = [&](int c, int& k, bool& later) {
-    if constexpr (VARLEN) {
-      const int f = tab[c].w;
-      k = clamp_int(f >> 3, 0, nseg - 1);
-      later = (f & 4) == 0;
-    } else {
-      k = c / seglen;
-      later = k > 0;
-    }
+    k = min(c / seglen, nseg - 1);
+    later = k > 0;
   };
 
   // C B^T tiles of 32-row block i: tile jj (column block jfirst + jj) of the
@@ -450,8 +445,7 @@ hipError_t launch_np(const FwdShape& s, const void* x, const uint16_t* CB, const
                           sg.seglen);
   };
   const bool seg = sg.nseg > 1 || sg.var;
-  if (seg && (!sg.Hin || !sg.cdec || (sg.var ? !tab || sg.nseg < 1 : tab || sg.seglen < 1)))
-    return hipErrorInvalidValue;
+  if (seg && (!sg.Hin || !sg.cdec || sg.seglen < 1 || sg.var != (tab != nullptr))) return hipErrorInvalidValue;
   // packed sequences through segments: only where the fused walk runs
   if constexpr (N >= 128) {
     if (seg && tab) {

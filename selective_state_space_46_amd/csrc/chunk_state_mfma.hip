@@ -314,16 +314,20 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma_kernel(
 // state_passing then runs the recurrence over the segments, and chunk_scan
 // adds exp(cdec_c) Hin_k where it stages H_c.
 //
-// Packed sequences (stab not null; one row of chunk slots, the chunk table
-// tab giving each slot's rows). The same segmented walks, over the segment
-// table instead of equal cuts: segment slot k (walks (k, 64 columns)) holds
-// up to seglen consecutive chunk slots of one sequence, starts from that
-// sequence's initial state if it is the sequence's first segment and from
-// zero otherwise, and writes the same local states, cdec, segdec and last
-// local state; a slot without chunks leaves at once. The recurrence then
-// runs per sequence over its segments. The C B^T tiles of the slots stay in
-// this launch, behind the walks: the walks of unused segment slots leave
-// their units to them at once.
+// Packed sequences (vw.tab not null): one row of chunk slots (the chunk table
+// gives each slot's rows, sequence and whether it begins or ends its
+// sequence) cut into equal segments like a batch row. A walk starts from
+// zero and, at each chunk that begins a sequence, restarts from that
+// sequence's initial state; the state handed from chunk to chunk is reset
+// there (youngju.dev page, "状態初期化とシーケンス境界": no state crosses from
+// one sequence into the next). From the first restart on, cdec is -inf (no
+// chunk after it takes the state entering the segment) and so is segdec (no
+// state passes through the segment). At the end of a sequence's last chunk
+// the running state is its final state if the sequence began inside this
+// walk; if it is the segment's first sequence, continued from before, it is
+// its local end state, left in F with its decay exponent (fdec) and the
+// sequence (fseq) for the recurrence over segments. Unused slots (between
+// sequences) have no rows: zero weights and decay 1 leave the state as it is.
 //
 // Tokens stream through 64-row slices of B (all of dstate, shared by the two
 // column blocks) and x (the 64 columns), copied straight from global memory
@@ -351,6 +355,7 @@ constexpr int kChainWaves = 8;      // 4 compute, 1 table, 3 copy
 constexpr int kChainThreads = 64 * kChainWaves;
 constexpr int kChainSK = 64;        // tokens per slice
 constexpr int kChainCols = 64;      // flattened (head, p) columns per work-group
+constexpr int kVarWalkSlots = 128;  // chunk slots per walk over packed rows (at most)
 
 template <int V>
 struct IntC {
@@ -383,7 +388,7 @@ struct ChainCfg {
 // (fin). Each G_c goes out as bf16 in Hs ([b, c, h, p, n]) with its dot
 // products with H_c (fp32 states entering each chunk, Hst) in per-wave
 // partials: ghp[((b H + h) nc + c) P / 16 + part]. No tiles, Acs or dt rows.
-template <int N, int P, int SPC, int ST, bool F32S, bool REV>
+template <int N, int P, int SPC, int ST, bool F32S, bool REV, bool VAR>
 __global__ __launch_bounds__(kChainThreads) __attribute__((amdgpu_waves_per_eu(N == 128 && ST <= 3 ? 4 : 1)))
 void chunk_state_chain_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ Bm, const uint16_t* __restrict__ dt,
@@ -391,7 +396,7 @@ void chunk_state_chain_kernel(
     const float* __restrict__ init, float* __restrict__ fin, const uint16_t* __restrict__ Cm,
     uint16_t* __restrict__ CB, uint16_t* __restrict__ CBt, const float* __restrict__ Hst, float* __restrict__ ghp,
     float* __restrict__ cdec, float* __restrict__ segdec, int T, int H, int G, int Q, int nc, int nb, int nseg,
-    int seglen, int nchain, long ntiles, const int4* __restrict__ tab, const int4* __restrict__ stab, int nseq) {
+    int seglen, int nchain, long ntiles, VarWalk vw) {
   using Cfg = ChainCfg<N, ST>;
   constexpr int S = Cfg::STAGES, RBB = Cfg::RBB, RBX = Cfg::RBX, NCB = Cfg::NCB, NCX = Cfg::NCX;
   constexpr int OPS = Cfg::OPS, TPW = Cfg::TPW;
@@ -401,7 +406,7 @@ void chunk_state_chain_kernel(
   // work-groups past the chains compute C B^T tiles, one per wave
   if (int(blockIdx.x) >= nchain) {
     const long wid = long(int(blockIdx.x) - nchain) * kChainWaves + wave;
-    if (wid < ntiles) chunk_scores_tile<N, F32S>(Bm, Cm, CB, CBt, tab, T, G, Q, nc, wid, lane);
+    if (wid < ntiles) chunk_scores_tile<N, F32S>(Bm, Cm, CB, CBt, nullptr, T, G, Q, nc, wid, lane);
     return;                                     // no barrier on this path
   }
   __shared__ __attribute__((aligned(16))) uint16_t sB[S][kChainSK * N];
@@ -410,6 +415,12 @@ void chunk_state_chain_kernel(
   // exp(Acs_{Q-1}) of head h0 + q in [q][c & 1]
   __shared__ __attribute__((aligned(16))) float sw[NHW][2][kMaxQ];
   __shared__ float sdecay[NHW][2];
+  // packed rows: the walk's chunk table entries {first row, valid tokens,
+  // sequence, flags}, clamped (first row in [0, T), sequence in [0, nseq)),
+  // read once from global memory: the waves then take rows, flags and
+  // sequences from LDS, so no global load joins the copy waves' counted
+  // copies
+  __shared__ int4 sslot[kVarWalkSlots];
 
   // walk id = ((b nseg + seg) cpr + column block): the walks of one (row,
   // segment) share every B slice and sit next to each other (one XCD's L2)
@@ -420,24 +431,28 @@ void chunk_state_chain_kernel(
   const int h0 = c0 / P;                        // first head
   const int g = h0 / (H / G);                   // the B group (both heads share it)
   const int l32 = lane & 31, g2 = lane >> 5;
-  int cbeg = seg * seglen;                      // first chunk of the walk
-  int ncw = min(nc, cbeg + seglen) - cbeg;      // chunks of the walk
-  int sq = b;                                   // the initial state's row
-  bool from_init = seg == 0;                    // the walk starts from the initial state
-  if (stab) {
-    // packed sequences: segment slot seg of the segment table (its chunk
-    // slots, sequence and whether it is the sequence's first), indices
-    // clamped into the tables whatever the entry
-    const int4 e = stab[seg];
-    cbeg = clamp_int(e.x, 0, nc - 1);
-    ncw = clamp_int(e.y, 0, min(seglen, nc - cbeg));
-    sq = clamp_int(e.z, 0, nseq - 1);
-    from_init = e.w != 0;
-  }
-  if (ncw <= 0) return;                         // an unused segment slot: uniform, before any barrier
+  const int cbeg = seg * seglen;                // first chunk of the walk
+  const int ncw = min(nc, cbeg + seglen) - cbeg;   // chunks of the walk
   const int nsl = ncw * SPC;                    // slices of the walk
-  // token rows of chunk c: equal-length rows, or the chunk table's slot
-  auto rows = [&](int c) { return stab ? slot_rows(tab, c, T, Q) : chunk_rows(nullptr, b, c, T, Q); };
+  constexpr bool var = VAR;                     // packed rows (vw.tab not null)
+  if (var) {
+    // ncw <= seglen <= kVarWalkSlots (the launcher checks)
+    for (int t = tid; t < ncw; t += kChainThreads) {
+      const int4 e = vw.tab[cbeg + t];
+      const int r0 = clamp_int(e.x, 0, T - 1);
+      sslot[t] = int4{r0, clamp_int(min(e.y, T - r0), 0, Q), clamp_int(e.z, 0, vw.nseq - 1), e.w};
+    }
+    __syncthreads();                            // uniform: var is
+  }
+  // token rows of chunk c: equal-length rows, or the chunk table's slot (an
+  // unused slot has none: its loads read one clamped row, its weights are 0)
+  auto rows = [&](int c) {
+    if (var) {
+      const int4 e = sslot[c - cbeg];
+      return ChunkRows{long(e.x), e.y};
+    }
+    return chunk_rows(nullptr, b, c, T, Q);
+  };
   // the walk's step k visits slice ks(k) of the row and its chunk wc = k / SPC
   // is chunk rc(wc) of the row (reversed in the reverse pass)
   auto ks = [&](int k) { return REV ? (cbeg + ncw) * SPC - 1 - k : cbeg * SPC + k; };
@@ -467,7 +482,10 @@ void chunk_state_chain_kernel(
     // chunk's loads are whole aligned words.
     const long last_e = long(nb) * T * H - 1;   // the tensor's last element
     auto dt_load = [&](int wc, uint32_t (&v)[NHW][4], uint32_t (&hi)[NHW]) {
-      const ChunkRows cr = rows(rc(wc));
+      const ChunkRows cr0 = rows(rc(wc));
+      // rows read: r0 .. r0 + nr - 1 (r0 < T and at least one row, also for
+      // an unused slot of a packed row)
+      const ChunkRows cr = ChunkRows{min(cr0.r0, long(nb) * T - 1), max(cr0.n, 1)};
       const bool tail = (last_e & 1) == 0 && cr.r0 + cr.n == long(nb) * T && h0 + NHW == H;
       if (tail) {
 #pragma unroll
@@ -552,6 +570,12 @@ void chunk_state_chain_kernel(
     float run[NHW];
 #pragma unroll
     for (int q = 0; q < NHW; ++q) run[q] = 0.f;
+    // packed rows: a sequence has begun inside this walk (from then on no
+    // chunk takes the state entering the segment: cdec, segdec -inf); the
+    // segment's first sequence is none until its end is seen
+    bool dead = false;
+    const bool lead = var && c0 == 0 && lane == 0;   // writes fseq[seg]
+    if (lead && vw.fseq) vw.fseq[seg] = -1;
     // chunk c's tables, then chunk c + 1's dt, then chunk c's rows (stores
     // after the loads)
     auto chunk = [&](int wc) {
@@ -560,12 +584,25 @@ void chunk_state_chain_kernel(
       for (int q = 0; q < NHW; ++q) lastq[q] = tables(wc, q, dnext[q], dhi[q], tacs[q], tdt[q]);
       if (wc + 1 < ncw) dt_load(wc + 1, dnext, dhi);
       if constexpr (!REV) {
+        int flags = 0, sqc = 0;
+        if (var) {
+          const int4 e = sslot[wc];
+          flags = e.w;
+          sqc = e.z;
+          if (flags & 1) dead = true;           // a sequence begins at this chunk
+        }
 #pragma unroll
         for (int q = 0; q < NHW; ++q) {
           rows_out(rc(wc), q, tacs[q], tdt[q]);
-          if (cdec && pcol(q) == 0 && lane == 0) cdec[(size_t(b) * H + h0 + q) * nc + rc(wc)] = run[q];
+          if (cdec && pcol(q) == 0 && lane == 0)
+            cdec[(size_t(b) * H + h0 + q) * nc + rc(wc)] = dead ? -INFINITY : run[q];
           run[q] += lastq[q];
+          // the segment's first sequence, continued from before, ends here:
+          // its decay exponent from the segment's start through this chunk
+          if (var && (flags & 2) && !dead && pcol(q) == 0 && lane == 0 && vw.fdec)
+            vw.fdec[size_t(h0 + q) * nseg + seg] = run[q];
         }
+        if (var && (flags & 2) && !dead && lead && vw.fseq) vw.fseq[seg] = sqc;
       }
     };
     dt_load(0, dnext, dhi);
@@ -584,7 +621,7 @@ void chunk_state_chain_kernel(
     if (segdec) {
 #pragma unroll
       for (int q = 0; q < NHW; ++q)
-        if (pcol(q) == 0 && lane == 0) segdec[(size_t(b) * H + h0 + q) * nseg + seg] = run[q];
+        if (pcol(q) == 0 && lane == 0) segdec[(size_t(b) * H + h0 + q) * nseg + seg] = dead ? -INFINITY : run[q];
     }
     return;
   }
@@ -621,7 +658,10 @@ void chunk_state_chain_kernel(
       // slice into a free slot) into slot s
       auto issue = [&](int k, int s) {
         k = ks(min(k, nsl - 1));
-        const ChunkRows cr = rows(k / SPC);
+        const ChunkRows cr0 = rows(k / SPC);
+        // at least one row read, inside the tensor (an unused slot of a packed
+        // row reads one clamped row; its weights are zero)
+        const ChunkRows cr = ChunkRows{min(cr0.r0, long(nb) * T - 1), max(cr0.n, 1)};
         const int s0 = (k % SPC) * kChainSK;
         const long row0 = cr.r0 + s0;
         const uint16_t* bbase = Bm + (row0 * G + g) * size_t(N);
@@ -685,7 +725,7 @@ void chunk_state_chain_kernel(
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int n = 32 * ntile(u) + 8 * (r / 4) + 4 * g2 + r % 4;
-      acc[u][r] = init && from_init ? init[((size_t(sq) * H + hj) * N + n) * P + pj + l32] : 0.f;
+      acc[u][r] = init && seg == 0 && !var ? init[(bhj * N + n) * P + pj + l32] : 0.f;
     }
   }
   // chunk c's start: H_c out as bf16 ([p][n] rows, four consecutive n of
@@ -705,8 +745,63 @@ void chunk_state_chain_kernel(
     }
   };
   if constexpr (REV) h_load(rc(0));
+  // packed rows: the running state is a sequence's; at its last chunk's end
+  // it is that sequence's final state (restarted inside this walk: cdead) or
+  // the local end state of the segment's first sequence, continued from
+  // before (F, completed by the recurrence over segments)
+  bool cdead = false;
+  int pflag = 0, pseq = 0;                      // the previous chunk's flags and sequence
+  // lane-dependent addresses recomputed at each use (see opaque): a lane's
+  // elements of an [n][p] state are one lane base plus constant offsets, and
+  // of a fragment-order one too (hb_off: lane part 4 (l32 + 32 g2))
+  auto np_base = [&](size_t row0) {            // row0: (sequence H + head) of an [.., N, P] tensor
+    const int ln = opaque(lane);
+    return row0 * N * P + size_t(4 * (ln >> 5)) * P + pj + (ln & 31);
+  };
+  auto np_off = [&](int u, int r) { return (32 * ntile(u) + 8 * (r / 4) + r % 4) * P; };
+  auto finish = [&](int sqn) {
+    if (cdead) {
+      if (vw.fin) {
+        float* dst = vw.fin + np_base(size_t(sqn) * H + hj);
+#pragma unroll
+        for (int u = 0; u < TPW; ++u)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) dst[np_off(u, r)] = acc[u][r];
+      }
+    } else if (vw.F) {
+      const int ln = opaque(lane);
+      float* dst = vw.F + (size_t(seg) * H + hj) * hstate + hb_off(pj, 0, N) + 4 * ln;
+#pragma unroll
+      for (int u = 0; u < TPW; ++u)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+          *reinterpret_cast<f32x4*>(dst + hb_off(0, 32 * ntile(u) + 8 * jj, N)) =
+              f32x4{acc[u][4 * jj], acc[u][4 * jj + 1], acc[u][4 * jj + 2], acc[u][4 * jj + 3]};
+    }
+  };
   auto chunk_start = [&](int wc) {
     const int c = rc(wc);
+    if (var) {
+      const int4 e = sslot[wc];
+      const int f = e.w, sqc = e.z;
+      if (pflag & 2) finish(pseq);              // the previous chunk ended a sequence
+      if (f & 1) {
+        // a sequence begins: its initial state (or zero)
+        cdead = true;
+        if (init) {
+          const float* src = init + np_base(size_t(sqc) * H + hj);
+#pragma unroll
+          for (int u = 0; u < TPW; ++u)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[u][r] = src[np_off(u, r)];
+        } else {
+#pragma unroll
+          for (int u = 0; u < TPW; ++u) acc[u] = zero16();
+        }
+      }
+      pflag = f;
+      pseq = sqc;
+    }
     if constexpr (REV) {
       // <G_c, H_c>: this wave's part, one partial per wave
       float dot = 0.f;
@@ -791,7 +886,8 @@ void chunk_state_chain_kernel(
       compute(k, d);
     }
   }
-  if (fin && (nseg > 1 || stab)) {
+  if (var && (pflag & 2)) finish(pseq);        // the last chunk ended a sequence
+  if (fin && (nseg > 1 || var)) {
     // a segment's last local state, [b, nseg, H, P * N], each head's in
     // fragment order (hb_off), fp32
     float* dst = fin + ((size_t(b) * nseg + seg) * H + hj) * hstate;
@@ -825,14 +921,14 @@ template <int N>
 __global__ __launch_bounds__(256) void chunk_scores_rows_kernel(const uint16_t* __restrict__ Bm,
                                                                 const uint16_t* __restrict__ Cm,
                                                                 uint16_t* __restrict__ CB, int T, int G, int Q,
-                                                                int nc) {
+                                                                int nc, const int4* __restrict__ tab) {
   const int lpc = Q / 32, ntile = lpc * (lpc + 1) / 2;
   const int wave = wave_id(), lane = threadIdx.x & 63;
   const int l32 = lane & 31, g2 = lane >> 5;
   const int g = int(blockIdx.x) % G;
   const int c = (int(blockIdx.x) / G) % nc;
   const int b = int(blockIdx.x) / G / nc;
-  const ChunkRows cr = chunk_rows(nullptr, b, c, T, Q);
+  const ChunkRows cr = chunk_rows(tab, b, c, T, Q);   // packed rows: the slot's (none for an unused one)
   // rows tl of C, ts of B inside the chunk (clamped into it; zeroed past it)
   auto rows16 = [&](const uint16_t* M, int t, u32x4 (&f)[N / 16]) {
     const uint16_t* r = M + ((cr.r0 + min(t, cr.n - 1)) * G + g) * size_t(N) + 8 * g2;
@@ -868,38 +964,57 @@ __global__ __launch_bounds__(256) void chunk_scores_rows_kernel(const uint16_t* 
   }
 }
 
-template <int N, int P, int SPC, int ST, bool F32S, bool REV>
+// The same tiles, one wave per tile (chunk_scores_tile), for segmented
+// launches with fewer (chunk, group) rows than work-groups fit on the device
+// at once: the row form would leave most units idle.
+template <int N>
+__global__ __launch_bounds__(kChainThreads) void chunk_scores_tiles_kernel(const uint16_t* __restrict__ Bm,
+                                                                         const uint16_t* __restrict__ Cm,
+                                                                         uint16_t* __restrict__ CB,
+                                                                         const int4* __restrict__ tab, int T, int G,
+                                                                         int Q, int nc, long ntiles) {
+  const long wid = long(blockIdx.x) * kChainWaves + wave_id();
+  if (wid < ntiles) chunk_scores_tile<N, false>(Bm, Cm, CB, nullptr, tab, T, G, Q, nc, wid, threadIdx.x & 63);
+}
+
+template <int N, int P, int SPC, int ST, bool F32S, bool REV, bool VAR>
 hipError_t launch_chain_np(const FwdShape& s, const ChainPlan& pl, const void* x, const void* B, const void* C,
                            const void* dt, const float* A, float* Acs, float* dtq, void* Hs, const float* init,
                            float* fin, uint16_t* CB, uint16_t* CBt, const float* Hst, float* ghp, float* cdec,
-                           float* segdec, const int4* tab, const int4* stab, int nseq, hipStream_t st,
-                           const StageEv& ev) {
+                           float* segdec, const VarWalk& vw, hipStream_t st, const StageEv& ev) {
   const int lpc = s.Q / 32;
   const long alltiles = REV ? 0 : long(s.b) * s.nc * s.G * (lpc * (lpc + 1) / 2);
   const long nchain = long(s.b) * s.H * P / kChainCols * pl.nseg;
-  // packed sequences keep their tiles in the walk launch: the walks of unused
-  // segment slots leave at once and tile work-groups take their places
-  const bool segd = pl.nseg > 1 && !pl.var;
-  const bool segs = segd || pl.var;         // cdec / segdec written
+  // segmented (packed rows always): the tiles in a launch of their own, cdec
+  // and segdec written
+  const bool segd = pl.nseg > 1 || pl.var;
   // segmented: the tiles first, as a launch of their own (the stage's start
   // event on it, the stop event on the walk)
   if (segd && alltiles > 0) {
-    // (segments need chunk_len a multiple of 64: an even number of row blocks)
-    hipExtLaunchKernelGGL((chunk_scores_rows_kernel<N>), dim3(unsigned(long(s.b) * s.nc * s.G)),
-                          dim3(64 * (s.Q / 64)), 0, st, ev.start, nullptr, 0, static_cast<const uint16_t*>(B),
-                          static_cast<const uint16_t*>(C), CB, s.T, s.G, s.Q, s.nc);
+    const long rows = long(s.b) * s.nc * s.G;
+    const int4* tab = pl.var ? vw.tab : nullptr;
+    if (rows >= 2L * device_units()) {
+      // (segments need chunk_len a multiple of 64: an even number of row blocks)
+      hipExtLaunchKernelGGL((chunk_scores_rows_kernel<N>), dim3(unsigned(rows)), dim3(64 * (s.Q / 64)), 0, st,
+                            ev.start, nullptr, 0, static_cast<const uint16_t*>(B), static_cast<const uint16_t*>(C),
+                            CB, s.T, s.G, s.Q, s.nc, tab);
+    } else {
+      hipExtLaunchKernelGGL((chunk_scores_tiles_kernel<N>), dim3(unsigned((alltiles + kChainWaves - 1) / kChainWaves)),
+                            dim3(kChainThreads), 0, st, ev.start, nullptr, 0, static_cast<const uint16_t*>(B),
+                            static_cast<const uint16_t*>(C), CB, tab, s.T, s.G, s.Q, s.nc, alltiles);
+    }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   const long ntiles = segd ? 0 : alltiles;
   const long blocks = nchain + (ntiles + kChainWaves - 1) / kChainWaves;
-  hipExtLaunchKernelGGL((chunk_state_chain_kernel<N, P, SPC, ST, F32S, REV>), dim3(unsigned(blocks)),
+  hipExtLaunchKernelGGL((chunk_state_chain_kernel<N, P, SPC, ST, F32S, REV, VAR>), dim3(unsigned(blocks)),
                         dim3(kChainThreads), 0, st, segd && alltiles > 0 ? nullptr : ev.start, ev.stop, 0,
                         static_cast<const uint16_t*>(x),
                         static_cast<const uint16_t*>(B), static_cast<const uint16_t*>(dt), A, Acs, dtq, Hs, init, fin,
-                        static_cast<const uint16_t*>(C), CB, CBt, Hst, ghp, segs ? cdec : nullptr,
-                        segs ? segdec : nullptr, s.T, s.H, s.G, s.Q, s.nc, s.b, pl.nseg, pl.seglen, int(nchain),
-                        ntiles, pl.var ? tab : nullptr, pl.var ? stab : nullptr, nseq);
+                        static_cast<const uint16_t*>(C), CB, CBt, Hst, ghp, segd ? cdec : nullptr,
+                        segd ? segdec : nullptr, s.T, s.H, s.G, s.Q, s.nc, s.b, pl.nseg, pl.seglen, int(nchain),
+                        ntiles, VAR ? vw : VarWalk{});
   return hipGetLastError();
 }
 
@@ -1024,35 +1139,24 @@ ChainPlan chunk_state_chain_plan_for(const FwdShape& s, int cus, bool allow_segm
   return pl;
 }
 
-// Packed sequences: L chunks per segment give floor(T / (Q L)) + nseq
-// segment slots and as many walks per 64 columns. L is the smallest whose
-// walks all fit at once, L = floor(T / (Q (m + 1))) + 1 with m the largest
-// floor(T / (Q L)) that fits, but at most kVarlenMaxSegChunks: where one
-// segment per sequence leaves little room (several long sequences, dstate
-// 256), more and shorter walks than fit at once queue and finish sooner than
-// a few long ones (packed 64K and 128K-token layers, 8 sequences: 16 chunks
-// 0.54 / 1.00 ms against 86 / 171 chunks 0.57 / 1.10 ms). Sequences longer
-// than Q L tokens take several segments; the rest one each. Where not even
-// one walk per sequence fits at once (many short sequences), the per-chunk
-// path runs.
-constexpr long kVarlenMaxSegChunks = 16;
-
+// Packed sequences: the row of chunk slots is cut like a batch row into
+// equal segments, as many as fill the device with walks in one round (two
+// per unit where they fit) and at most one per slot; sequences begin and end
+// anywhere inside a segment. Any number of sequences is served.
 ChainPlan varlen_chain_plan_for(const FwdShape& s, int nseq, int cus) {
   ChainPlan pl;
-  if (!chain_shape_ok(s) || s.b != 1 || cus <= 0 || nseq < 1 || s.T < 1) return pl;
+  if (!chain_shape_ok(s) || s.b != 1 || cus <= 0 || nseq < 1 || s.nc < 1) return pl;
   const long cpr = long(s.H) * s.P / kChainCols;
-  const long room = chain_per_unit(s) * cus / cpr - nseq;   // segment slots beyond one per sequence
-  if (room < 0) return pl;
-  const long L = std::min(long(s.T) / (long(s.Q) * (room + 1)) + 1, kVarlenMaxSegChunks);
-  const long QL = L * s.Q;
-  if (QL > 0x7fffffffL) return pl;
+  const long per_unit = chain_per_unit(s);
+  const long want = std::min<long>(s.nc, per_unit * cus / cpr);
+  if (want < 1) return pl;                 // not even one walk per 64 columns fits at once
+  // at most kVarWalkSlots slots per segment (their table entries sit in LDS):
+  // longer rows take more segments than fit at once
+  pl.seglen = int(std::min<long>((s.nc + want - 1) / want, kVarWalkSlots));
+  pl.nseg = (s.nc + pl.seglen - 1) / pl.seglen;
   pl.ok = true;
   pl.var = true;
-  pl.seglen = int(L);
-  pl.nseg = varlen_seg_slots(s.T, nseq, int(QL));
-  // two per unit where that fits (more walks than units), else one per unit
-  // (more walks than fit at once queue)
-  pl.two = chain_per_unit(s) == 2 && long(pl.nseg) * cpr > cus;
+  pl.two = per_unit == 2 && long(pl.nseg) * cpr > cus;
   return pl;
 }
 
@@ -1071,46 +1175,47 @@ template <bool F32S, bool REV>
 hipError_t launch_chain(const FwdShape& s, const ChainPlan& pl, const void* x, const void* B, const void* C,
                         const void* dt, const float* A, float* Acs, float* dtq, void* Hs, const float* init,
                         float* fin, uint16_t* CB, uint16_t* CBt, const float* Hst, float* ghp, float* cdec,
-                        float* segdec, hipStream_t st, const StageEv& ev, const int4* tab = nullptr,
-                        const int4* stab = nullptr, int nseq = 0) {
+                        float* segdec, hipStream_t st, const StageEv& ev, const VarWalk& vw = VarWalk{}) {
   // every walk must own at least one chunk and the segments must cover the
-  // row exactly: a walk without slices would clamp its copies to slice -1.
-  // Packed sequences: the segment table decides, and a walk whose slot holds
-  // no chunks leaves before its first copy.
-  const bool ok = pl.var ? pl.ok && s.b == 1 && pl.nseg >= 1 && pl.seglen >= 1 && tab && stab && nseq >= 1 &&
-                               cdec && segdec && fin && !F32S && !REV
-                         : chain_plan_valid(s, pl) && !((F32S || REV) && pl.nseg != 1);
+  // row exactly: a walk without slices would clamp its copies to slice -1
+  const bool ok = chain_plan_valid(s, pl) &&
+                  (pl.var ? s.b == 1 && vw.tab && vw.nseq >= 1 && cdec && segdec && fin && !F32S && !REV &&
+                                pl.seglen <= kVarWalkSlots
+                          : !((F32S || REV) && pl.nseg != 1));
   if (!ok) return hipErrorInvalidValue;
-  // two work-groups per unit (three slices resident; chunks of two or four
-  // slices, which the plan ensures) where one per unit would not hold them all
   auto by_q = [&](auto np) -> hipError_t {
     using NP = decltype(np);
     constexpr int S1 = NP::n == 128 ? 5 : 3;
+    // one instantiation per (slices per chunk, slices resident); the walk
+    // over packed rows is an instantiation of its own
+    auto go = [&](auto spc, auto stg) -> hipError_t {
+      constexpr int SPC_ = decltype(spc)::value, ST_ = decltype(stg)::value;
+      if constexpr (!F32S && !REV) {
+        if (pl.var)
+          return launch_chain_np<NP::n, NP::p, SPC_, ST_, false, false, true>(
+              s, pl, x, B, C, dt, A, Acs, dtq, Hs, init, fin, CB, CBt, Hst, ghp, cdec, segdec, vw, st, ev);
+      }
+      return launch_chain_np<NP::n, NP::p, SPC_, ST_, F32S, REV, false>(
+          s, pl, x, B, C, dt, A, Acs, dtq, Hs, init, fin, CB, CBt, Hst, ghp, cdec, segdec, vw, st, ev);
+    };
     if (pl.two && NP::n == 128) {
+      // two work-groups per unit (three slices resident; chunks of two or
+      // four slices, which the plan ensures) where one per unit would not
+      // hold them all
       if constexpr (REV) {
         return hipErrorInvalidValue;            // one per unit only (registers)
       } else {
         switch (s.Q / kChainSK) {
-          case 2:
-            return launch_chain_np<NP::n, NP::p, 2, 3, F32S, REV>(s, pl, x, B, C, dt, A, Acs, dtq, Hs, init, fin, CB,
-                                                                  CBt, Hst, ghp, cdec, segdec, tab, stab, nseq, st, ev);
-          case 4:
-            return launch_chain_np<NP::n, NP::p, 4, 3, F32S, REV>(s, pl, x, B, C, dt, A, Acs, dtq, Hs, init, fin, CB,
-                                                                  CBt, Hst, ghp, cdec, segdec, tab, stab, nseq, st, ev);
+          case 2: return go(IntC<2>{}, IntC<3>{});
+          case 4: return go(IntC<4>{}, IntC<3>{});
         }
         return hipErrorInvalidValue;
       }
     }
     switch (s.Q / kChainSK) {
-      case 1:
-        return launch_chain_np<NP::n, NP::p, 1, S1, F32S, REV>(s, pl, x, B, C, dt, A, Acs, dtq, Hs, init, fin, CB,
-                                                               CBt, Hst, ghp, cdec, segdec, tab, stab, nseq, st, ev);
-      case 2:
-        return launch_chain_np<NP::n, NP::p, 2, S1, F32S, REV>(s, pl, x, B, C, dt, A, Acs, dtq, Hs, init, fin, CB,
-                                                               CBt, Hst, ghp, cdec, segdec, tab, stab, nseq, st, ev);
-      case 4:
-        return launch_chain_np<NP::n, NP::p, 4, S1, F32S, REV>(s, pl, x, B, C, dt, A, Acs, dtq, Hs, init, fin, CB,
-                                                               CBt, Hst, ghp, cdec, segdec, tab, stab, nseq, st, ev);
+      case 1: return go(IntC<1>{}, IntC<S1>{});
+      case 2: return go(IntC<2>{}, IntC<S1>{});
+      case 4: return go(IntC<4>{}, IntC<S1>{});
     }
     return hipErrorInvalidValue;
   };
@@ -1136,11 +1241,10 @@ hipError_t launch_chunk_state_chain(const FwdShape& s, const ChainPlan& pl, cons
 hipError_t launch_chunk_state_chain_varlen(const FwdShape& s, const ChainPlan& pl, const void* x, const void* B,
                                            const void* C, const void* dt, const float* A, float* Acs, float* dtq,
                                            uint16_t* Hb, const float* init, float* segS, uint16_t* CB, float* cdec,
-                                           float* segdec, const int4* tab, const int4* stab, int nseq,
-                                           hipStream_t st, const StageEv& ev) {
+                                           float* segdec, const VarWalk& vw, hipStream_t st, const StageEv& ev) {
   if (!pl.var) return hipErrorInvalidValue;
   return launch_chain<false, false>(s, pl, x, B, C, dt, A, Acs, dtq, Hb, init, segS, CB, nullptr, nullptr, nullptr,
-                                    cdec, segdec, st, ev, tab, stab, nseq);
+                                    cdec, segdec, st, ev, vw);
 }
 
 hipError_t launch_chunk_state_chain_bwd(const FwdShape& s, const void* x, const void* B, const void* C,

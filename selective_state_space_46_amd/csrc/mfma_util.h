@@ -160,6 +160,15 @@ __device__ __forceinline__ u32x4 keep_or_zero(bool keep, const u32x4& v) {
 
 // vmcnt(n), the other counters left alone (low four bits of n in bits 3..0,
 // high two in bits 15..14)
+// v, hidden from the optimizer: values derived from it inside a loop are
+// recomputed there instead of being hoisted out of the loop and held in
+// registers for its whole length (lane-dependent addresses of unrolled
+// accesses would otherwise take more registers than the MFMA accumulators).
+__device__ __forceinline__ int opaque(int v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
 template <int n>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(n >= 0 && n < 64, "vmcnt range");

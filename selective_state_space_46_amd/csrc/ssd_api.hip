@@ -429,17 +429,22 @@ FwdShape varlen_shape(int total, int nseq, int H, int P, int N, int G, int Q) {
 }
 // Workspace of a packed call: the forward's layout for one row of chunk
 // slots (with the fused walk's segments where the plan has them: segment
-// states, cdec, segdec), then the chunk table and the segment table.
+// states, cdec, segdec), then with the walk F [nseg, H, P * N] f32, fdec
+// [H, nseg] f32 and fseq [nseg] int32 (the segments' first sequences that
+// end inside them), then the chunk table.
 struct VarlenWs {
   WsLayout w;
-  size_t tab, stab, total;
+  size_t F, fdec, fseq, tab, total;
 };
 VarlenWs varlen_ws(const FwdShape& s, const ChainPlan& pl) {
   VarlenWs v;
   v.w = ws_layout(s, true, pl);
-  v.tab = align_up(v.w.total, 256);
-  v.stab = align_up(v.tab + size_t(s.nc) * sizeof(int4), 256);
-  v.total = pl.ok ? v.stab + size_t(pl.nseg) * sizeof(int4) : v.tab + size_t(s.nc) * sizeof(int4);
+  const size_t nsg = pl.ok ? size_t(pl.nseg) : 0;
+  v.F = align_up(v.w.total, 256);
+  v.fdec = align_up(v.F + nsg * s.H * s.P * s.N * sizeof(float), 256);
+  v.fseq = align_up(v.fdec + nsg * s.H * sizeof(float), 256);
+  v.tab = align_up(v.fseq + nsg * sizeof(int), 256);
+  v.total = v.tab + size_t(s.nc) * sizeof(int4);
   return v;
 }
 // the per-sequence state passing launches 256 threads per (sequence, head,
@@ -525,26 +530,32 @@ ssd_status ssd_chunk_scan_fwd_varlen(const void* x, const void* dt, const float*
   uint16_t* Hb = reinterpret_cast<uint16_t*>(ws + w.hb);
   uint16_t* CB = reinterpret_cast<uint16_t*>(ws + w.cb);
   int4* tab = reinterpret_cast<int4*>(ws + v.tab);
+  if (launch_varlen_table(cu_seqlens, nseq, total_tokens, chunk_len, tab, hs) != hipSuccess) return SSD_ERR_HIP;
   if (pl.ok) {
-    // the fused walk over segments of at most pl.seglen chunks (a
-    // sequence's first from its initial state, the others from zero), the
-    // recurrence over each sequence's segments, and chunk_scan with the
-    // segment correction. The walk reads init_states before the recurrence
-    // writes any final state, and the recurrence reads a sequence's initial
-    // state (only one without tokens) before it writes that sequence's final
-    // state, so final_states may be init_states.
-    int4* stab = reinterpret_cast<int4*>(ws + v.stab);
+    // the fused walk over equal segments of the slot row, restarting at each
+    // sequence's first chunk; the recurrence over the segments (states
+    // entering them, the final states of sequences that cross a segment
+    // boundary, empty sequences); chunk_scan with the segment correction.
+    // A sequence's initial state is read by the walk that holds its first
+    // chunk before the final state is written (by the same walk, or by the
+    // recurrence after it; an empty sequence's by the recurrence, element by
+    // element), so final_states may be init_states.
     float* cdec = reinterpret_cast<float*>(ws + w.cdec);
     float* segdec = reinterpret_cast<float*>(ws + w.segdec);
-    if (launch_varlen_table(cu_seqlens, nseq, total_tokens, chunk_len, tab, pl.seglen, stab, hs) != hipSuccess)
-      return SSD_ERR_HIP;
-    if (launch_chunk_state_chain_varlen(s, pl, x, B, C, dt, A, Acs, dtq, Hb, init_states, S, CB, cdec, segdec, tab,
-                                        stab, nseq, hs) != hipSuccess)
+    VarWalk vw;
+    vw.tab = tab;
+    vw.nseq = nseq;
+    vw.fin = final_states;
+    vw.F = reinterpret_cast<float*>(ws + v.F);
+    vw.fdec = reinterpret_cast<float*>(ws + v.fdec);
+    vw.fseq = reinterpret_cast<int*>(ws + v.fseq);
+    if (launch_chunk_state_chain_varlen(s, pl, x, B, C, dt, A, Acs, dtq, Hb, init_states, S, CB, cdec, segdec, vw,
+                                        hs) != hipSuccess)
       return SSD_ERR_HIP;
     FwdShape ss = s;
     ss.nc = pl.nseg;
-    if (launch_state_passing_varlen_segments(ss, S, segdec, cu_seqlens, nseq, chunk_len * pl.seglen, init_states,
-                                             final_states, hs) != hipSuccess)
+    if (launch_varlen_segment_recurrence(ss, S, vw.F, segdec, vw.fdec, vw.fseq, cu_seqlens, nseq, init_states,
+                                         final_states, hs) != hipSuccess)
       return SSD_ERR_HIP;
     SegStates sg;
     sg.Hin = S;
@@ -560,8 +571,6 @@ ssd_status ssd_chunk_scan_fwd_varlen(const void* x, const void* dt, const float*
   // state_passing reads each sequence's initial state (whole tile, into
   // LDS) before it writes that sequence's final state, so final_states may
   // be init_states.
-  if (launch_varlen_table(cu_seqlens, nseq, total_tokens, chunk_len, tab, 0, nullptr, hs) != hipSuccess)
-    return SSD_ERR_HIP;
   if (launch_chunk_state_mfma(s, x, B, C, dt, A, Acs, dtq, S, CB, tab, hs) != hipSuccess) return SSD_ERR_HIP;
   if (launch_state_passing_varlen(s, S, Hb, Acs, cu_seqlens, nseq, init_states, final_states, hs) != hipSuccess)
     return SSD_ERR_HIP;

@@ -65,41 +65,25 @@ __device__ __forceinline__ float exp_fast(float x) {
 // (a chunk of sequence i starts before sequence i+1 does, and i grows by
 // one), and the last slot is below ceil(T / Q) + nseq. A table gives each
 // slot tab[c] = {first row, valid tokens (0: unused slot), sequence, flags
-// (bit 0: first chunk of its sequence, bit 1: last, bit 2: in the
-// sequence's first segment, bits 3 and up: its segment slot)}.
-//
-// Segments (the fused walk over packed sequences): each sequence's chunks
-// are cut into runs of at most L, which take segment slots the way chunks
-// take chunk slots, with Q L tokens in place of Q: segment m of sequence i
-// is slot floor(cu[i] / (Q L)) + i + m. A sequence of len tokens has
-// ceil(len / (Q L)) segments, the last ending at slot floor((cu[i] + len) /
-// (Q L)) + i at most, so floor(T / (Q L)) + nseq slots hold them all. The
-// segment table gives stab[m] = {first chunk slot, chunks (0: unused slot),
-// sequence, 1 for a sequence's first segment}.
+// (bit 0: first chunk of its sequence, bit 1: last)}.
 // ---------------------------------------------------------------------------
 struct ChunkRows {
   long r0;   // first token row
   int n;     // valid tokens (0 .. Q)
 };
 
+__host__ __device__ __forceinline__ int clamp_int(int v, int lo, int hi) { return v < lo ? lo : v > hi ? hi : v; }
+
+// rows stay inside [0, T) whatever a table entry holds: the first row in
+// [0, T], at most T - r0 valid tokens (0 or less: no rows)
 __device__ __forceinline__ ChunkRows chunk_rows(const int4* tab, int b, int c, int T, int Q) {
   if (tab) {
     const int4 e = tab[c];
-    return ChunkRows{long(e.x), min(e.y, T - e.x)};   // rows stay inside [0, T) whatever the entry
+    const int r0 = clamp_int(e.x, 0, T);
+    return ChunkRows{long(r0), min(e.y, T - r0)};
   }
   return ChunkRows{long(b) * T + long(c) * Q, min(Q, T - c * Q)};
 }
-
-// A chunk slot's rows for kernels that read at least one row of every chunk
-// they visit: the first row clamped into [0, T) and 1 .. Q valid tokens,
-// whatever the entry (the table's entries already are).
-__device__ __forceinline__ ChunkRows slot_rows(const int4* tab, int c, int T, int Q) {
-  const int4 e = tab[c];
-  const int r0 = min(max(e.x, 0), T - 1);
-  return ChunkRows{long(r0), min(max(min(e.y, T - r0), 1), Q)};
-}
-
-__host__ __device__ __forceinline__ int clamp_int(int v, int lo, int hi) { return v < lo ? lo : v > hi ? hi : v; }
 
 // The token span of sequence i: offsets are clamped into [0, T] and a span
 // never ends before it starts, so any offsets give in-bounds spans.
@@ -110,38 +94,23 @@ __host__ __device__ __forceinline__ void varlen_span(const int* cu, int i, int T
   len = s1 - s0;
 }
 
-// first chunk slot of sequence i, which starts at token s0 (with Q L for Q:
-// its first segment slot)
+// first chunk slot of sequence i, which starts at token s0
 __host__ __device__ __forceinline__ int varlen_first_slot(int s0, int i, int Q) { return s0 / Q + i; }
 
 // chunk slots for T tokens in nseq sequences
 __host__ __device__ __forceinline__ int varlen_slots(int T, int nseq, int Q) { return (T + Q - 1) / Q + nseq; }
 
-// segment slots for T tokens in nseq sequences, QL = Q L tokens per segment
-__host__ __device__ __forceinline__ int varlen_seg_slots(int T, int nseq, int QL) { return T / QL + nseq; }
-
 // The table entries of sequence i (tokens s0 .. s0 + len - 1): its chunk
-// slots, and with L > 0 (stab not null) its segments and each chunk's
-// segment slot in the flags. Entries past nslots / nsegslots are never
-// reached for a span from varlen_span; they are skipped all the same.
-__host__ __device__ inline void varlen_fill(int i, int s0, int len, int Q, int L, int4* tab, int nslots,
-                                            int4* stab, int nsegslots) {
+// slots. Entries past nslots are never reached for a span from varlen_span;
+// they are skipped all the same.
+__host__ __device__ inline void varlen_fill(int i, int s0, int len, int Q, int4* tab, int nslots) {
   const int nch = (len + Q - 1) / Q;
   const int first = varlen_first_slot(s0, i, Q);
-  const int sfirst = L > 0 ? varlen_first_slot(s0, i, Q * L) : 0;
   for (int k = 0; k < nch; ++k) {
     const int c = first + k;
     if (c >= nslots) break;
-    const int m = L > 0 ? k / L : 0;
-    const int flags = (k == 0 ? 1 : 0) | (k == nch - 1 ? 2 : 0) | (m == 0 ? 4 : 0) | (L > 0 ? (sfirst + m) << 3 : 0);
+    const int flags = (k == 0 ? 1 : 0) | (k == nch - 1 ? 2 : 0);
     tab[c] = int4{s0 + k * Q, len - k * Q < Q ? len - k * Q : Q, i, flags};
-  }
-  if (L > 0 && stab) {
-    const int nsg = (nch + L - 1) / L;
-    for (int m = 0; m < nsg; ++m) {
-      if (sfirst + m >= nsegslots) break;
-      stab[sfirst + m] = int4{first + m * L, nch - m * L < L ? nch - m * L : L, i, m == 0 ? 1 : 0};
-    }
   }
 }
 
@@ -170,8 +139,9 @@ struct ChainPlan {
   bool ok = false;
   int nseg = 1, seglen = 0;
   bool two = false;
-  // packed sequences: nseg segment slots of at most seglen chunks each
-  // (always segmented, whatever nseg)
+  // packed sequences: the row of chunk slots cut into nseg segments of
+  // seglen slots, the walks reset at sequence starts (always segmented,
+  // whatever nseg)
   bool var = false;
 };
 // allow_segments = false: whole rows only (the backward's walks). The plan
@@ -181,9 +151,9 @@ ChainPlan chunk_state_chain_plan(const FwdShape& s, bool allow_segments);
 // pl.ok and its segments cover the row's chunks exactly, each at least one
 bool chain_plan_valid(const FwdShape& s, const ChainPlan& pl);
 // Packed sequences (s: batch 1, T packed tokens, nc chunk slots) through the
-// fused walk: segments of the smallest length L that lets one walk per
-// (segment slot, 64 columns) run at once on `cus` units; ok = false where no
-// L does (the per-chunk path runs).
+// fused walk: the slot row cut into equal segments, as many as fill the
+// device with walks (one per segment and 64 columns) in one round; ok =
+// false where the walk does not serve the shape (the per-chunk path runs).
 ChainPlan varlen_chain_plan_for(const FwdShape& s, int nseq, int cus);
 // compute units of the current device (read once per device; 0 without one)
 constexpr int kMaxDevices = 64;
@@ -302,17 +272,32 @@ hipError_t launch_chunk_state_chain(const FwdShape& s, const ChainPlan& pl, cons
                                     uint16_t* Hb, const float* init, float* fin, uint16_t* CB, float* cdec,
                                     float* segdec, hipStream_t st, const StageEv& ev = StageEv{});
 // Packed sequences (pl from varlen_chain_plan_for; s: batch 1, nc chunk
-// slots): one walk per (segment slot, 64 columns) over the segment table
-// stab, rows from the chunk table tab; a sequence's first segment starts
-// from its initial state (init [nseq, H, N, P], may be null), the others
-// from zero. Hb the local states per slot, segS each segment's last local
-// state ([pl.nseg, H, P * N] fp32, fragment order), cdec [H, nc] and segdec
-// [H, pl.nseg], the tiles CB per slot.
+// slots): the slot row cut into pl.nseg equal segments, one walk per
+// (segment, 64 columns), rows and sequence starts / ends from the chunk table.
+// A walk starts from zero and restarts from a sequence's initial state (init
+// [nseq, H, N, P], may be null) at each chunk that begins a sequence; cdec
+// and segdec are -inf from the first restart on, so that only the chunks of
+// the sequence the segment continues take the state entering the segment.
+// A sequence that begins and ends inside one walk gets its final state
+// (fin [nseq, H, N, P], may be null) from that walk; where the segment's
+// first sequence continues from before and ends inside it, the walk leaves
+// its local end state in F ([nseg, H, P * N] fp32, fragment order), its
+// summed decay exponent from the segment's start in fdec [H, nseg] and the
+// sequence in fseq[seg] (else -1), for the recurrence over segments. segS
+// receives each segment's last local state as for segmented batch rows.
+struct VarWalk {
+  const int4* tab = nullptr;
+  int nseq = 0;
+  float* fin = nullptr;
+  float* F = nullptr;
+  float* fdec = nullptr;
+  int* fseq = nullptr;
+};
 hipError_t launch_chunk_state_chain_varlen(const FwdShape& s, const ChainPlan& pl, const void* x, const void* B,
                                            const void* C, const void* dt, const float* A, float* Acs, float* dtq,
                                            uint16_t* Hb, const float* init, float* segS, uint16_t* CB, float* cdec,
-                                           float* segdec, const int4* tab, const int4* stab, int nseq,
-                                           hipStream_t st, const StageEv& ev = StageEv{});
+                                           float* segdec, const VarWalk& vw, hipStream_t st,
+                                           const StageEv& ev = StageEv{});
 // The same for the backward's recomputation: the states entering each chunk
 // as fp32 in Hst ([b, c, h, p, n], what state_passing leaves over the chunk
 // states) and the C B^T tiles as fp32 in both orientations (CBf, CBt, as
@@ -346,14 +331,17 @@ hipError_t launch_state_passing(const FwdShape& s, float* S, uint16_t* Hb, const
 hipError_t launch_state_passing_varlen(const FwdShape& s, const float* S, uint16_t* Hb, const float* Acs,
                                        const int* cu, int nseq, const float* init, float* final_state,
                                        hipStream_t st, const StageEv& ev = StageEv{});
-// The same over the fused walk's segments (s.nc = segment slots, QL tokens
-// per segment): S holds each segment's last local state (fragment order),
-// overwritten in place by the state entering each segment, which is zero
-// for a sequence's first (its walk started from init); segdec [H, s.nc] the
-// segments' summed decay exponents; final_state as above.
-hipError_t launch_state_passing_varlen_segments(const FwdShape& s, float* S, const float* segdec, const int* cu,
-                                                int nseq, int QL, const float* init, float* final_state,
-                                                hipStream_t st, const StageEv& ev = StageEv{});
+// The recurrence over the packed walks' segments (s.nc = nseg segments):
+// carry_0 = 0; for each segment k in order, the state entering it is
+// carry_k (written over S[k], which held its last local state E_k), the
+// final state of fseq[k] (if >= 0) is F_k + exp(fdec_k) carry_k, and
+// carry_{k+1} = exp(segdec_k) carry_k + E_k (segdec_k = -inf where a
+// sequence began inside segment k). A sequence without tokens gets its
+// initial state (or zero) as its final state. final_state may be null.
+hipError_t launch_varlen_segment_recurrence(const FwdShape& s, float* S, const float* F, const float* segdec,
+                                            const float* fdec, const int* fseq, const int* cu, int nseq,
+                                            const float* init, float* final_state, hipStream_t st,
+                                            const StageEv& ev = StageEv{});
 
 // Generic path reads Hst (fp32, [b, nc, H, P, N]); MFMA path reads Hb (bf16)
 // and the C B^T tiles CB.
@@ -363,9 +351,9 @@ hipError_t launch_chunk_scan(const FwdShape& s, ssd_dtype type, bool mfma, const
                              const float* D, void* y, hipStream_t st, const StageEv& ev = StageEv{});
 // Segmented states (ChainPlan::nseg > 1): the state entering chunk c of
 // segment k >= 1 is Hb_c + exp(cdec_c) Hin_k, Hin [b, nseg, H, P * N] fp32,
-// each head's in fragment order (hb_off). var: packed sequences (with the
-// chunk table; dstate 128 or 256), each chunk's segment slot from the
-// table's flags, no correction in a sequence's first segment.
+// each head's in fragment order (hb_off). var: packed sequences (rows from
+// the chunk table; dstate 128 or 256), segments of seglen slots, cdec -inf
+// for the chunks that take no correction.
 struct SegStates {
   const float* Hin = nullptr;
   const float* cdec = nullptr;
@@ -379,11 +367,8 @@ hipError_t launch_chunk_scan_mfma(const FwdShape& s, const void* x, const uint16
                                   const SegStates& seg = SegStates{});
 
 // Packed variable-length sequences (varlen.hip): the chunk table has
-// varlen_slots(T, nseq, Q) int4 entries; with stab (not null) also the
-// segment table of varlen_seg_slots(T, nseq, Q L) entries, segments of at
-// most L chunks.
-hipError_t launch_varlen_table(const int* cu, int nseq, int T, int Q, int4* tab, int L, int4* stab,
-                               hipStream_t st);
+// varlen_slots(T, nseq, Q) int4 entries.
+hipError_t launch_varlen_table(const int* cu, int nseq, int T, int Q, int4* tab, hipStream_t st);
 
 // Element-wise stages next to the core (epilogue.hip).
 hipError_t launch_gated_rmsnorm(ssd_dtype type, const void* y, const void* z, const float* w, void* out,

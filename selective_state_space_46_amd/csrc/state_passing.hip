@@ -52,16 +52,12 @@ __device__ __forceinline__ void store_out(float* S, uint16_t* Hb, size_t idx, si
 // grid: b * H * ceil(P/kTP) * ceil(N/kTN) work-groups; requires N % 4 == 0.
 // VARLEN: b counts sequences instead of batch rows, and the chunks of
 // sequence b are its slots of the one packed row (cu: sequence offsets, T:
-// packed tokens, span tokens per slot); init / fin are [nseq, H, N, P] like a
-// batch of nseq rows. segs (with VARLEN): the slots are the fused walk's
-// segments (span = Q L), whose walks started from the sequence's initial
-// state, so the recurrence starts from zero and init only passes through a
-// sequence without tokens.
+// packed tokens); init / fin are [nseq, H, N, P] like a batch of nseq rows.
 template <bool VARLEN>
 __global__ __launch_bounds__(kThreads) void state_passing_tiled(
     float* __restrict__ S, uint16_t* __restrict__ Hb, const float* __restrict__ Acs,
     const float* __restrict__ init, float* __restrict__ fin, int H, int P, int N, int Q, int nc,
-    const int* __restrict__ cu, int T, int sfrag, int span, int segs) {
+    const int* __restrict__ cu, int T, int sfrag) {
   __shared__ float tile[kTN][kTP + 1];
   const int tpn = (N + kTN - 1) / kTN, tpp = (P + kTP - 1) / kTP;
   int bid = blockIdx.x;
@@ -83,13 +79,13 @@ __global__ __launch_bounds__(kThreads) void state_passing_tiled(
     int s0, len;
     varlen_span(cu, b, T, s0, len);
     brow = 0;
-    crow = varlen_first_slot(s0, b, span);
-    ncw = (len + span - 1) / span;
+    crow = varlen_first_slot(s0, b, Q);
+    ncw = (len + Q - 1) / Q;
   }
 
-  // H_0: init transposed through LDS (or zero); uniform over the work-group
+  // H_0: init transposed through LDS (or zero)
   f32x4 cur = f32x4{0.f, 0.f, 0.f, 0.f};
-  if (init && !(VARLEN && segs && ncw > 0)) {
+  if (init) {
     for (int e = tid; e < kTN * kTP; e += kThreads) {
       const int nn = e / kTP, pp = e % kTP;
       float v = 0.f;
@@ -275,6 +271,88 @@ __global__ __launch_bounds__(kThreads) void state_passing_bwd_tiled(
   }
 }
 
+// Packed sequences through the fused walk: the recurrence over segments
+// (launch_varlen_segment_recurrence). Work-groups 0 .. ntiles-1: one (head,
+// 16 x 64 tile) each, walking the segments in order with S, F and the decay
+// exponents of the segments ahead loaded kDepth segments early (they do not
+// depend on the recurrence); a final state completed at segment k goes out
+// through LDS in the caller's [n][p] layout. Work-groups ntiles + i: an
+// empty sequence i's final state is its initial state (or zero).
+__global__ __launch_bounds__(kThreads) void varlen_segment_recurrence(
+    float* __restrict__ S, const float* __restrict__ F, const float* __restrict__ segdec,
+    const float* __restrict__ fdec, const int* __restrict__ fseq, const int* __restrict__ cu,
+    const float* __restrict__ init, float* __restrict__ fin, int H, int P, int N, int nseg, int nseq, int T,
+    int ntiles) {
+  __shared__ float tile[kTN][kTP + 1];
+  const int tid = threadIdx.x;
+  const size_t sbh = size_t(N) * P;          // elements of one head's state
+  if (int(blockIdx.x) >= ntiles) {
+    const int i = int(blockIdx.x) - ntiles;   // < nseq by the grid
+    int s0, len;
+    varlen_span(cu, i, T, s0, len);
+    if (len > 0 || !fin) return;
+    const size_t base = size_t(i) * H * sbh;
+    for (size_t e = tid; e < size_t(H) * sbh; e += kThreads) fin[base + e] = init ? init[base + e] : 0.f;
+    return;
+  }
+  const int tpn = (N + kTN - 1) / kTN, tpp = (P + kTP - 1) / kTP;
+  int bid = blockIdx.x;
+  const int tn = bid % tpn; bid /= tpn;
+  const int tp = bid % tpp; bid /= tpp;
+  const int h = bid;                         // < H by the grid
+  const int pi = tid / 16, nq = tid % 16;
+  const int p0 = tp * kTP, n0 = tn * kTN;
+  const int p = p0 + pi, n = n0 + 4 * nq;    // P, N multiples of 32: every thread active
+  const size_t cstride = size_t(H) * sbh;    // elements between segment k and k + 1
+  const size_t off0 = size_t(h) * sbh + hb_off(p, n, N);
+  const float* sd = segdec + size_t(h) * nseg;
+  const float* fd = fdec + size_t(h) * nseg;
+  f32x4 rs[kDepth], rf[kDepth];
+  float rsd[kDepth], rfd[kDepth];
+  int rfs[kDepth];
+  auto fetch = [&](int k, int j) {
+    rs[j] = *reinterpret_cast<const f32x4*>(S + off0 + size_t(k) * cstride);
+    rf[j] = *reinterpret_cast<const f32x4*>(F + off0 + size_t(k) * cstride);
+    rsd[j] = sd[k];
+    rfd[j] = fd[k];
+    rfs[j] = fseq[k];
+  };
+#pragma unroll
+  for (int j = 0; j < kDepth; ++j)
+    if (j < nseg) fetch(j, j);
+  f32x4 carry = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int k0 = 0; k0 < nseg; k0 += kDepth) {
+#pragma unroll
+    for (int j = 0; j < kDepth; ++j) {
+      const int k = k0 + j;
+      if (k < nseg) {
+        const f32x4 e = rs[j], fk = rf[j];
+        const float a = expf(rsd[j]), af = expf(rfd[j]);
+        const int fs = rfs[j];                 // uniform
+        if (k + kDepth < nseg) fetch(k + kDepth, j);
+        if (fs >= 0 && fs < nseq && fin) {
+          // sequence fs, continued into segment k, ends there
+          tile[4 * nq][pi] = fk.x + af * carry.x;
+          tile[4 * nq + 1][pi] = fk.y + af * carry.y;
+          tile[4 * nq + 2][pi] = fk.z + af * carry.z;
+          tile[4 * nq + 3][pi] = fk.w + af * carry.w;
+          __syncthreads();
+          for (int q = tid; q < kTN * kTP; q += kThreads) {
+            const int nn = q / kTP, pp = q % kTP;
+            fin[(size_t(fs) * H + h) * sbh + size_t(n0 + nn) * P + p0 + pp] = tile[nn][pp];
+          }
+          __syncthreads();
+        }
+        *reinterpret_cast<f32x4*>(S + off0 + size_t(k) * cstride) = carry;   // the state entering segment k
+        carry.x = a * carry.x + e.x;
+        carry.y = a * carry.y + e.y;
+        carry.z = a * carry.z + e.z;
+        carry.w = a * carry.w + e.w;
+      }
+    }
+  }
+}
+
 }  // namespace
 
 int state_passing_bwd_partials(const FwdShape& s) {
@@ -298,20 +376,19 @@ hipError_t launch_state_passing_varlen(const FwdShape& s, const float* S, uint16
   // S is only read: the passed states go to Hb
   hipExtLaunchKernelGGL(state_passing_tiled<true>, dim3(unsigned(tiles)), dim3(kThreads), 0, st, ev.start,
                         ev.stop, 0, const_cast<float*>(S), Hb, Acs, init, final_state, s.H, s.P, s.N, s.Q,
-                        s.nc, cu, s.T, 0, s.Q, 0);
+                        s.nc, cu, s.T, 0);
   return hipGetLastError();
 }
 
-hipError_t launch_state_passing_varlen_segments(const FwdShape& s, float* S, const float* segdec, const int* cu,
-                                                int nseq, int QL, const float* init, float* final_state,
-                                                hipStream_t st, const StageEv& ev) {
-  if (s.N % 32 || s.P % 32 || s.b != 1 || QL < 1) return hipErrorInvalidValue;
-  const long tiles = long(nseq) * s.H * ((s.P + kTP - 1) / kTP) * ((s.N + kTN - 1) / kTN);
-  // the decay of segment k is segdec[h, k] (a "chunk" of one entry); the
-  // states entering each segment overwrite S (fragment order)
-  hipExtLaunchKernelGGL(state_passing_tiled<true>, dim3(unsigned(tiles)), dim3(kThreads), 0, st, ev.start,
-                        ev.stop, 0, S, static_cast<uint16_t*>(nullptr), segdec, init, final_state, s.H, s.P, s.N,
-                        1, s.nc, cu, s.T, 1, QL, 1);
+hipError_t launch_varlen_segment_recurrence(const FwdShape& s, float* S, const float* F, const float* segdec,
+                                            const float* fdec, const int* fseq, const int* cu, int nseq,
+                                            const float* init, float* final_state, hipStream_t st,
+                                            const StageEv& ev) {
+  if (s.N % 32 || s.P % 32 || s.b != 1 || s.nc < 1 || nseq < 1) return hipErrorInvalidValue;
+  const long tiles = long(s.H) * ((s.P + kTP - 1) / kTP) * ((s.N + kTN - 1) / kTN);
+  hipExtLaunchKernelGGL(varlen_segment_recurrence, dim3(unsigned(tiles + nseq)), dim3(kThreads), 0, st, ev.start,
+                        ev.stop, 0, S, F, segdec, fdec, fseq, cu, init, final_state, s.H, s.P, s.N, s.nc, nseq,
+                        s.T, int(tiles));
   return hipGetLastError();
 }
 
@@ -323,7 +400,7 @@ hipError_t launch_state_passing(const FwdShape& s, float* S, uint16_t* Hb, const
     const long tiles = long(s.b) * s.H * ((s.P + kTP - 1) / kTP) * ((s.N + kTN - 1) / kTN);
     hipExtLaunchKernelGGL(state_passing_tiled<false>, dim3(unsigned(tiles)), dim3(kThreads), 0, st, ev.start,
                           ev.stop, 0, S, Hb, Acs, init, final_state, s.H, s.P, s.N, s.Q, s.nc,
-                          static_cast<const int*>(nullptr), 0, sfrag ? 1 : 0, s.Q, 0);
+                          static_cast<const int*>(nullptr), 0, sfrag ? 1 : 0);
   } else {
     if (Hb) return hipErrorInvalidValue;     // the MFMA path never has N % 4 != 0
     const long total = long(s.b) * s.H * s.N * s.P;

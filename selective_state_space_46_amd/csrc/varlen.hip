@@ -9,10 +9,8 @@
 // valid tokens (or Q). Chunk k of sequence i takes slot floor(cu[i] / Q) +
 // i + k (ssd_internal.h), so a sequence's slots follow from its own offset
 // alone; the table lists, for the kernels that walk slots, every slot's
-// first token row, valid tokens, sequence and flags. Slots that no chunk
-// takes stay {0, 0, 0, 0}. For the fused walk over packed sequences the same
-// launch writes the segment table (each sequence's chunks in runs of at most
-// L, ssd_internal.h) and each chunk's segment slot in its flags.
+// first token row, valid tokens, sequence and first/last flags. Slots that
+// no chunk takes stay {0, 0, 0, 0}.
 //
 // cu_seqlens lives on the device and is not seen by the host, so the spans
 // are clamped (varlen_span): malformed offsets give unspecified but
@@ -25,32 +23,26 @@ namespace {
 constexpr int kTabThreads = 1024;
 
 // one work-group: clear every slot, then each thread writes the entries of
-// sequences tid, tid + 1024, ... (varlen_fill: slots < nslots and segment
-// slots < nsegslots for any clamped span)
+// sequences tid, tid + 1024, ... (varlen_fill: slots < nslots for any clamped
+// span)
 __global__ __launch_bounds__(kTabThreads) void varlen_table_kernel(const int* __restrict__ cu, int nseq,
                                                                    int T, int Q, int nslots,
-                                                                   int4* __restrict__ tab, int L,
-                                                                   int4* __restrict__ stab, int nsegslots) {
+                                                                   int4* __restrict__ tab) {
   const int tid = threadIdx.x;
   for (int c = tid; c < nslots; c += kTabThreads) tab[c] = int4{0, 0, 0, 0};
-  if (stab)
-    for (int c = tid; c < nsegslots; c += kTabThreads) stab[c] = int4{0, 0, 0, 0};
   __syncthreads();   // the clears are ordered before the entries below
   for (int i = tid; i < nseq; i += kTabThreads) {
     int s0, len;
     varlen_span(cu, i, T, s0, len);
-    varlen_fill(i, s0, len, Q, stab ? L : 0, tab, nslots, stab, nsegslots);
+    varlen_fill(i, s0, len, Q, tab, nslots);
   }
 }
 
 }  // namespace
 
-hipError_t launch_varlen_table(const int* cu, int nseq, int T, int Q, int4* tab, int L, int4* stab,
-                               hipStream_t st) {
-  if (stab && (L < 1 || long(Q) * L > 0x7fffffffL)) return hipErrorInvalidValue;
-  const int nsegslots = stab ? varlen_seg_slots(T, nseq, Q * L) : 0;
+hipError_t launch_varlen_table(const int* cu, int nseq, int T, int Q, int4* tab, hipStream_t st) {
   hipLaunchKernelGGL(varlen_table_kernel, dim3(1), dim3(kTabThreads), 0, st, cu, nseq, T, Q,
-                     varlen_slots(T, nseq, Q), tab, L, stab, nsegslots);
+                     varlen_slots(T, nseq, Q), tab);
   return hipGetLastError();
 }
 
