@@ -460,7 +460,7 @@ def bench_varlen(hip, vw, steps=20, warmup=3):
     nseg, seglen = ssd.ssd_chunk_scan_fwd_varlen_plan(vw.total, nseq, vw.nheads, vw.headdim, vw.dstate, vw.ngroups,
                                                       vw.chunk_len, 1 if vw.dtype == "bf16" else 0, cus)
     return {"workload": vw.name, "nseq": nseq, "min_len": int(lens.min()), "max_len": int(lens.max()),
-            "segment_slots": nseg, "chunks_per_segment": seglen,
+            "segments": nseg, "slots_per_segment": seglen,
             "ms_per_call": round(ms, 5), "tokens_per_s": round(vw.total / (ms * 1e-3), 1)}
 
 

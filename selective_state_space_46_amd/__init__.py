@@ -16,7 +16,7 @@ Entry points (same names as the C ABI):
     ssd_status_string(code) -> str
     ssd_chunk_scan_fwd_varlen(x, dt, A, B, C, D, cu_seqlens, init_states, chunk_len)
         -> (y, final_states)                          (packed variable-length sequences)
-    ssd_chunk_scan_fwd_varlen_plan(...) -> (segment slots, chunks per segment) ((0, 0): per chunk)
+    ssd_chunk_scan_fwd_varlen_plan(...) -> (segments, chunk slots per segment) ((0, 0): per chunk)
 and, from ``include/ssd_backward.h``, the backward pass:
     ssd_chunk_scan_bwd(x, dt, A, B, C, D, init_state, dy, dfinal)
         -> dict(dx, ddt, dA, dB, dC, dD, dinit)
@@ -163,9 +163,10 @@ def ssd_chunk_scan_fwd_plan(batch: int, seqlen: int, nheads: int, headdim: int, 
 
 def ssd_chunk_scan_fwd_varlen_plan(total_tokens: int, nseq: int, nheads: int, headdim: int, dstate: int,
                                    ngroups: int, chunk_len: int, dtype: int, compute_units: int) -> Tuple[int, int]:
-    """(segment slots, chunks per segment) the packed forward chooses on a
-    device with `compute_units` compute units; (0, 0) = chunk-state launch
-    and a recurrence per sequence over its chunks. Needs no device."""
+    """(segments, chunk slots per segment) of the packed row that the packed
+    forward's walks take on a device with `compute_units` compute units;
+    (0, 0) = chunk-state launch and a recurrence per sequence over its
+    chunks. Needs no device."""
     sl = ctypes.c_int(0)
     n = int(lib().ssd_chunk_scan_fwd_varlen_plan(total_tokens, nseq, nheads, headdim, dstate, ngroups, chunk_len,
                                                  dtype, compute_units, ctypes.byref(sl)))

@@ -32,7 +32,7 @@ def _inputs(total, H, P, N, G, nseq, seed, with_init=True):
 
 
 def _plan(inp, cu, Q):
-    """(segment slots, chunks per segment) the call takes on this device"""
+    """(segments, chunk slots per segment) the call takes on this device"""
     import torch
     import selective_state_space_46_amd as ssd
     T, H, P = inp["x"].shape
