@@ -351,11 +351,25 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma_kernel(
 // wave's dt loads are a chunk old when used, and the compute waves only
 // store. All waves pass the same barriers, one per slice.
 // ---------------------------------------------------------------------------
-constexpr int kChainWaves = 8;      // 4 compute, 1 table, 3 copy
+constexpr int kChainWaves = 8;      // 4 compute, 1 table, 3 copy (64 columns)
 constexpr int kChainThreads = 64 * kChainWaves;
 constexpr int kChainSK = 64;        // tokens per slice
-constexpr int kChainCols = 64;      // flattened (head, p) columns per work-group
+constexpr int kChainCols = 64;      // flattened (head, p) columns per work-group (see chain_cols)
 constexpr int kVarWalkSlots = 128;  // chunk slots per walk over packed rows (at most)
+
+// Columns per work-group. The forward at dstate 256, headdim 64 and
+// chunk_len 256 (spc = 4 slices per chunk) takes 128: each 32 KB slice of B
+// then serves twice the columns (B moves from L2 into LDS once per 128
+// columns instead of per 64), with eight compute waves (4 column blocks x 2
+// n-tile groups), 12 waves in all and 150 KB of LDS. Elsewhere 64 (the
+// backward's walks; dstate 128, whose slices are half the size; other
+// headdims and shorter chunks, whose per-head and chunk-start work does not
+// fit the 168 registers a wave of 12 has).
+constexpr int chain_cols(int N, int P, int spc, bool bwd) {
+  return N == 256 && P == 64 && spc == 4 && !bwd ? 128 : 64;
+}
+// waves of a work-group: 2 per 32-column block (compute), 1 table, 3 copy
+constexpr int chain_waves(int cols) { return cols / 16 + 4; }
 
 template <int V>
 struct IntC {
@@ -365,10 +379,10 @@ struct IntC {
 // ST slices resident: 5 at dstate 128 (120 KB: one work-group per compute
 // unit), 3 there when two work-groups share a unit (72 KB each), 3 at
 // dstate 256 (120 KB)
-template <int N, int ST>
+template <int N, int ST, int CW>
 struct ChainCfg {
   static constexpr int STAGES = ST;
-  static constexpr int RBB = N / 8, RBX = kChainCols / 8;        // 16-byte chunks per B / x row
+  static constexpr int RBB = N / 8, RBX = CW / 8;                // 16-byte chunks per B / x row
   static constexpr int NCB = kChainSK * RBB / 64, NCX = kChainSK * RBX / 64;   // wave copies per slice
   static constexpr int OPS = (NCB + NCX + 2) / 3;                // copies per copy wave and slice
   static constexpr int TPW = N / 64;                             // n tiles per compute wave
@@ -389,7 +403,8 @@ struct ChainCfg {
 // products with H_c (fp32 states entering each chunk, Hst) in per-wave
 // partials: ghp[((b H + h) nc + c) P / 16 + part]. No tiles, Acs or dt rows.
 template <int N, int P, int SPC, int ST, bool F32S, bool REV, bool VAR>
-__global__ __launch_bounds__(kChainThreads) __attribute__((amdgpu_waves_per_eu(N == 128 && ST <= 3 ? 4 : 1)))
+__global__ __launch_bounds__(64 * chain_waves(chain_cols(N, P, SPC, F32S || REV)))
+__attribute__((amdgpu_waves_per_eu(N == 128 && ST <= 3 ? 4 : 1)))
 void chunk_state_chain_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ Bm, const uint16_t* __restrict__ dt,
     const float* __restrict__ A, float* __restrict__ Acs, float* __restrict__ dtq, void* __restrict__ Hs,
@@ -397,20 +412,24 @@ void chunk_state_chain_kernel(
     uint16_t* __restrict__ CB, uint16_t* __restrict__ CBt, const float* __restrict__ Hst, float* __restrict__ ghp,
     float* __restrict__ cdec, float* __restrict__ segdec, int T, int H, int G, int Q, int nc, int nb, int nseg,
     int seglen, int nchain, long ntiles, VarWalk vw) {
-  using Cfg = ChainCfg<N, ST>;
+  constexpr int CW = chain_cols(N, P, SPC, F32S || REV);   // columns per work-group
+  constexpr int NCOLB = CW / 32;                // 32-column blocks
+  constexpr int NCWV = 2 * NCOLB;               // compute waves; the table wave is wave NCWV
+  constexpr int NW = chain_waves(CW), NTHR = 64 * NW;
+  using Cfg = ChainCfg<N, ST, CW>;
   constexpr int S = Cfg::STAGES, RBB = Cfg::RBB, RBX = Cfg::RBX, NCB = Cfg::NCB, NCX = Cfg::NCX;
   constexpr int OPS = Cfg::OPS, TPW = Cfg::TPW;
-  constexpr int NHW = P == 32 ? 2 : 1;          // heads per work-group
+  constexpr int NHW = P < CW ? CW / P : 1;      // heads per work-group
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = wave_id();  // wave-uniform (scalar register)
   // work-groups past the chains compute C B^T tiles, one per wave
   if (int(blockIdx.x) >= nchain) {
-    const long wid = long(int(blockIdx.x) - nchain) * kChainWaves + wave;
+    const long wid = long(int(blockIdx.x) - nchain) * NW + wave;
     if (wid < ntiles) chunk_scores_tile<N, F32S>(Bm, Cm, CB, CBt, nullptr, T, G, Q, nc, wid, lane);
     return;                                     // no barrier on this path
   }
   __shared__ __attribute__((aligned(16))) uint16_t sB[S][kChainSK * N];
-  __shared__ __attribute__((aligned(16))) uint16_t sX[S][kChainSK * kChainCols];
+  __shared__ __attribute__((aligned(16))) uint16_t sX[S][kChainSK * CW];
   // chunk c's token weights w_s = exp(Acs_{Q-1} - Acs_s) dt_s and decay
   // exp(Acs_{Q-1}) of head h0 + q in [q][c & 1]
   __shared__ __attribute__((aligned(16))) float sw[NHW][2][kMaxQ];
@@ -425,8 +444,8 @@ void chunk_state_chain_kernel(
   // walk id = ((b nseg + seg) cpr + column block): the walks of one (row,
   // segment) share every B slice and sit next to each other (one XCD's L2)
   const int id = xcd_swizzle(int(blockIdx.x), nchain);
-  const int cpr = H * P / kChainCols;           // work-groups per batch row and segment
-  const int c0 = (id % cpr) * kChainCols;       // first flattened column
+  const int cpr = H * P / CW;                   // work-groups per batch row and segment
+  const int c0 = (id % cpr) * CW;               // first flattened column
   const int seg = (id / cpr) % nseg, b = id / cpr / nseg;
   const int h0 = c0 / P;                        // first head
   const int g = h0 / (H / G);                   // the B group (both heads share it)
@@ -437,7 +456,7 @@ void chunk_state_chain_kernel(
   constexpr bool var = VAR;                     // packed rows (vw.tab not null)
   if (var) {
     // ncw <= seglen <= kVarWalkSlots (the launcher checks)
-    for (int t = tid; t < ncw; t += kChainThreads) {
+    for (int t = tid; t < ncw; t += NTHR) {
       const int4 e = vw.tab[cbeg + t];
       const int r0 = clamp_int(e.x, 0, T - 1);
       sslot[t] = int4{r0, clamp_int(min(e.y, T - r0), 0, Q), clamp_int(e.z, 0, vw.nseq - 1), e.w};
@@ -458,10 +477,12 @@ void chunk_state_chain_kernel(
   auto ks = [&](int k) { return REV ? (cbeg + ncw) * SPC - 1 - k : cbeg * SPC + k; };
   auto rc = [&](int wc) { return REV ? cbeg + ncw - 1 - wc : cbeg + wc; };
   const size_t hstate = size_t(P) * N;          // elements of one (b, h) state
-  // column block j (32 columns): head h0 + (NHW == 2 ? j : 0), columns from pcol(j) of that head
-  auto pcol = [&](int j) { return (c0 + 32 * j) % P; };
+  // whether this work-group holds the first columns of each of its heads
+  // (they write the per-head rows: Acs, dt, cdec, segdec); a head wider
+  // than the work-group is split over several
+  const bool hfirst = P < CW || c0 % P == 0;
 
-  if (wave == 4) {
+  if (wave == NCWV) {
     // ---- table wave: each chunk's tables one chunk ahead, from dt loaded one
     // chunk before that. It issues no copies, so its loads (dt) and stores
     // (the Acs / dt rows) are all its memory counter holds: the wait for a
@@ -545,7 +566,7 @@ void chunk_state_chain_kernel(
     // the Acs / dt rows of chunk c, head h0 + q (by the work-group holding
     // the head's first columns)
     auto rows_out = [&](int c, int q, const float (&acs)[4], const float (&v)[4]) {
-      if (pcol(q) != 0) return;
+      if (!hfirst) return;
       const size_t arow = ((size_t(b) * H + h0 + q) * nc + c) * Q;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -594,12 +615,12 @@ void chunk_state_chain_kernel(
 #pragma unroll
         for (int q = 0; q < NHW; ++q) {
           rows_out(rc(wc), q, tacs[q], tdt[q]);
-          if (cdec && pcol(q) == 0 && lane == 0)
+          if (cdec && hfirst && lane == 0)
             cdec[(size_t(b) * H + h0 + q) * nc + rc(wc)] = dead ? -INFINITY : run[q];
           run[q] += lastq[q];
           // the segment's first sequence, continued from before, ends here:
           // its decay exponent from the segment's start through this chunk
-          if (var && (flags & 2) && !dead && pcol(q) == 0 && lane == 0 && vw.fdec)
+          if (var && (flags & 2) && !dead && hfirst && lane == 0 && vw.fdec)
             vw.fdec[size_t(h0 + q) * nseg + seg] = run[q];
         }
         if (var && (flags & 2) && !dead && lead && vw.fseq) vw.fseq[seg] = sqc;
@@ -621,12 +642,12 @@ void chunk_state_chain_kernel(
     if (segdec) {
 #pragma unroll
       for (int q = 0; q < NHW; ++q)
-        if (pcol(q) == 0 && lane == 0) segdec[(size_t(b) * H + h0 + q) * nseg + seg] = dead ? -INFINITY : run[q];
+        if (hfirst && lane == 0) segdec[(size_t(b) * H + h0 + q) * nseg + seg] = dead ? -INFINITY : run[q];
     }
     return;
   }
 
-  if (wave > 4) {
+  if (wave > NCWV) {
     // ---- copy waves: the slice copies into LDS. Copy q of a slice (q < NCB:
     // B, else x) covers 1 KB of its slot; copy wave v takes q = v, v + 3, ...,
     // the last index repeated where the count falls short (the repeat writes
@@ -649,7 +670,7 @@ void chunk_state_chain_kernel(
           cc[i] = 8 * ((lane % RBB) ^ lds_swz<RBB>(row[i]));
           off[i] = unsigned(row[i] * G * N + cc[i]);
         } else {
-          row[i] = (q - NCB) * (512 / kChainCols) + lane / RBX;
+          row[i] = (q - NCB) * (512 / CW) + lane / RBX;
           cc[i] = 8 * ((lane % RBX) ^ lds_swz<RBX>(row[i]));
           off[i] = unsigned(row[i] * H * P + cc[i]);
         }
@@ -703,21 +724,22 @@ void chunk_state_chain_kernel(
       }
       wait_vmcnt<0>();                          // the last (repeated) copies
     };
-    if (wave == 5) copy_loop(IntC<0>{});
-    else if (wave == 6) copy_loop(IntC<1>{});
+    if (wave == NCWV + 1) copy_loop(IntC<0>{});
+    else if (wave == NCWV + 2) copy_loop(IntC<1>{});
     else copy_loop(IntC<2>{});
     return;
   }
 
-  // ---- compute waves (waves 0 .. 3): column block j = wave & 1 of head
-  // hj = h0 + (NHW == 2 ? j : 0), n tiles (wave >> 1) + 2 u. Each owns its
+  // ---- compute waves (waves 0 .. NCWV - 1): 32-column block j = wave %
+  // NCOLB (of head hj), n tiles wave / NCOLB + 2 u. Each owns its
   // tiles over every token, so the running states need no exchange between
   // waves; they issue no loads inside the walk, so their stores (H_c, the
   // final state) cost no waits.
-  const int j = wave & 1, hq = NHW == 2 ? j : 0, hj = h0 + hq;
-  const int pj = pcol(j);
+  const int j = wave % NCOLB;                   // 32-column block
+  const int hj = (c0 + 32 * j) / P, hq = hj - h0;   // its head
+  const int pj = (c0 + 32 * j) % P;             // its first column of that head
   const size_t bhj = size_t(b) * H + hj;
-  auto ntile = [&](int u) { return (wave >> 1) + 2 * u; };
+  auto ntile = [&](int u) { return wave / NCOLB + 2 * u; };
   // running state, tile u: n = 32 ntile(u) + 8 (r / 4) + 4 g2 + r % 4, p = pj + l32 of head hj
   f32x16 acc[TPW];
 #pragma unroll
@@ -813,7 +835,7 @@ void chunk_state_chain_kernel(
           for (int e = 0; e < 4; ++e) dot += acc[u][4 * jj + e] * hnext[4 * u + jj][e];
 #pragma unroll
       for (int off = 32; off >= 1; off >>= 1) dot += __shfl_xor(dot, off, 64);
-      if (lane == 0) ghp[((size_t(b) * H + hj) * nc + c) * (P / 16) + 2 * (pj / 32) + (wave >> 1)] = dot;
+      if (lane == 0) ghp[((size_t(b) * H + hj) * nc + c) * (P / 16) + 2 * (pj / 32) + wave / NCOLB] = dot;
     }
     // fp32 (F32S) and the reverse walk's gradients: [p][n] rows; the forward's
     // bf16 states: fragment order (hb_off), the accumulators as they are
@@ -853,27 +875,33 @@ void chunk_state_chain_kernel(
     const int s0 = (ks(k) % SPC) * kChainSK;
     const float* swc = sw[hq][(k / SPC) & 1];
     constexpr int KS = kChainSK / 16;
-    // every LDS read of the slice first, so that one wait covers them all
-    u32x4 xr[KS], bf[KS][TPW];
-    f32x4 w0[KS], w1[KS];
+    // the LDS reads of KG k steps first, so that one wait covers them all:
+    // the whole slice at 64 columns; two k steps at a time at 128 (12 waves
+    // leave 168 registers a wave)
+    constexpr int KG = CW == 128 ? 2 : KS;
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk) {
-      const int kb = 16 * kk + 8 * g2;
-      xr[kk] = frag_tr<RBX>(sX[s], kb, kb + 4, 32 * j, lane);   // x rows kb .. kb+7 of column 32 j + l32
-      w0[kk] = *reinterpret_cast<const f32x4*>(&swc[s0 + kb]);
-      w1[kk] = *reinterpret_cast<const f32x4*>(&swc[s0 + kb + 4]);
+    for (int kq = 0; kq < KS; kq += KG) {
+      u32x4 xr[KG], bf[KG][TPW];
+      f32x4 w0[KG], w1[KG];
 #pragma unroll
-      for (int u = 0; u < TPW; ++u) bf[kk][u] = frag_tr<RBB>(sB[s], kb, kb + 4, 32 * ntile(u), lane);
-    }
+      for (int kk = 0; kk < KG; ++kk) {
+        const int kb = 16 * (kq + kk) + 8 * g2;
+        xr[kk] = frag_tr<RBX>(sX[s], kb, kb + 4, 32 * j, lane);   // x rows kb .. kb+7 of column 32 j + l32
+        w0[kk] = *reinterpret_cast<const f32x4*>(&swc[s0 + kb]);
+        w1[kk] = *reinterpret_cast<const f32x4*>(&swc[s0 + kb + 4]);
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk) {
-      const f32x4 v0 = w0[kk], v1 = w1[kk];
-      const u32x4 a = u32x4{pack_bf16x2(bf16_lo(xr[kk][0]) * v0[0], bf16_hi(xr[kk][0]) * v0[1]),
-                            pack_bf16x2(bf16_lo(xr[kk][1]) * v0[2], bf16_hi(xr[kk][1]) * v0[3]),
-                            pack_bf16x2(bf16_lo(xr[kk][2]) * v1[0], bf16_hi(xr[kk][2]) * v1[1]),
-                            pack_bf16x2(bf16_lo(xr[kk][3]) * v1[2], bf16_hi(xr[kk][3]) * v1[3])};
+        for (int u = 0; u < TPW; ++u) bf[kk][u] = frag_tr<RBB>(sB[s], kb, kb + 4, 32 * ntile(u), lane);
+      }
 #pragma unroll
-      for (int u = 0; u < TPW; ++u) acc[u] = mfma32x32x16(bf[kk][u], a, acc[u]);
+      for (int kk = 0; kk < KG; ++kk) {
+        const f32x4 v0 = w0[kk], v1 = w1[kk];
+        const u32x4 a = u32x4{pack_bf16x2(bf16_lo(xr[kk][0]) * v0[0], bf16_hi(xr[kk][0]) * v0[1]),
+                              pack_bf16x2(bf16_lo(xr[kk][1]) * v0[2], bf16_hi(xr[kk][1]) * v0[3]),
+                              pack_bf16x2(bf16_lo(xr[kk][2]) * v1[0], bf16_hi(xr[kk][2]) * v1[1]),
+                              pack_bf16x2(bf16_lo(xr[kk][3]) * v1[2], bf16_hi(xr[kk][3]) * v1[3])};
+#pragma unroll
+        for (int u = 0; u < TPW; ++u) acc[u] = mfma32x32x16(bf[kk][u], a, acc[u]);
+      }
     }
   };
 
@@ -982,9 +1010,12 @@ hipError_t launch_chain_np(const FwdShape& s, const ChainPlan& pl, const void* x
                            const void* dt, const float* A, float* Acs, float* dtq, void* Hs, const float* init,
                            float* fin, uint16_t* CB, uint16_t* CBt, const float* Hst, float* ghp, float* cdec,
                            float* segdec, const VarWalk& vw, hipStream_t st, const StageEv& ev) {
+  constexpr int CW = chain_cols(N, P, SPC, F32S || REV), NW = chain_waves(CW);
+  // whole work-groups per row, and the heads of one in one B/C group
+  if ((long(s.H) * P) % CW != 0 || (P < CW && (s.H / s.G) % (CW / P) != 0)) return hipErrorInvalidValue;
   const int lpc = s.Q / 32;
   const long alltiles = REV ? 0 : long(s.b) * s.nc * s.G * (lpc * (lpc + 1) / 2);
-  const long nchain = long(s.b) * s.H * P / kChainCols * pl.nseg;
+  const long nchain = long(s.b) * s.H * P / CW * pl.nseg;
   // segmented (packed rows always): the tiles in a launch of their own, cdec
   // and segdec written
   const bool segd = pl.nseg > 1 || pl.var;
@@ -1007,9 +1038,9 @@ hipError_t launch_chain_np(const FwdShape& s, const ChainPlan& pl, const void* x
     if (e != hipSuccess) return e;
   }
   const long ntiles = segd ? 0 : alltiles;
-  const long blocks = nchain + (ntiles + kChainWaves - 1) / kChainWaves;
+  const long blocks = nchain + (ntiles + NW - 1) / NW;
   hipExtLaunchKernelGGL((chunk_state_chain_kernel<N, P, SPC, ST, F32S, REV, VAR>), dim3(unsigned(blocks)),
-                        dim3(kChainThreads), 0, st, segd && alltiles > 0 ? nullptr : ev.start, ev.stop, 0,
+                        dim3(64 * NW), 0, st, segd && alltiles > 0 ? nullptr : ev.start, ev.stop, 0,
                         static_cast<const uint16_t*>(x),
                         static_cast<const uint16_t*>(B), static_cast<const uint16_t*>(dt), A, Acs, dtq, Hs, init, fin,
                         static_cast<const uint16_t*>(C), CB, CBt, Hst, ghp, segd ? cdec : nullptr,
@@ -1101,11 +1132,12 @@ int device_units() {
 // allows and at most one per chunk; if that still leaves more than half the
 // units idle, the two-kernel path runs.
 namespace {
-// the shapes the walk serves: dstate 128 or 256, headdim 32 (two heads of one
-// B/C group per work-group), 64 or 128, chunks of whole 64-token slices
-bool chain_shape_ok(const FwdShape& s) {
+// the shapes the walk serves: dstate 128 or 256, headdim 32, 64 or 128,
+// chunks of whole 64-token slices, and where a work-group of cw columns
+// holds several heads (cw / P), whole groups of them in one B/C group
+bool chain_shape_ok(const FwdShape& s, int cw) {
   if (!((s.N == 128 || s.N == 256) && (s.P == 32 || s.P == 64 || s.P == 128) && s.Q % kChainSK == 0)) return false;
-  return !(s.P == 32 && (s.H / s.G) % 2 != 0);
+  return !(s.P < cw && (s.H / s.G) % (cw / s.P) != 0);
 }
 // walks that fit a unit at once: two at dstate 128 with a chunk start at
 // most every other slice (the registers of a chunk start every slice do not
@@ -1115,9 +1147,12 @@ long chain_per_unit(const FwdShape& s) { return s.N == 128 && s.Q >= 2 * kChainS
 
 ChainPlan chunk_state_chain_plan_for(const FwdShape& s, int cus, bool allow_segments) {
   ChainPlan pl;
-  if (!chain_shape_ok(s)) return pl;
+  // the forward's walks (segments allowed) at their column width, the
+  // backward's (whole rows) at 64
+  const int cw = chain_cols(s.N, s.P, s.Q / kChainSK, !allow_segments);
+  if (!chain_shape_ok(s, cw)) return pl;
   if (cus <= 0 || s.nc < 1) return pl;
-  const long wgs = long(s.b) * s.H * s.P / kChainCols;
+  const long wgs = long(s.b) * s.H * s.P / cw;
   const long per_unit = chain_per_unit(s);
   if (wgs > per_unit * cus) return pl;
   if (2 * wgs >= cus) {
@@ -1145,8 +1180,9 @@ ChainPlan chunk_state_chain_plan_for(const FwdShape& s, int cus, bool allow_segm
 // anywhere inside a segment. Any number of sequences is served.
 ChainPlan varlen_chain_plan_for(const FwdShape& s, int nseq, int cus) {
   ChainPlan pl;
-  if (!chain_shape_ok(s) || s.b != 1 || cus <= 0 || nseq < 1 || s.nc < 1) return pl;
-  const long cpr = long(s.H) * s.P / kChainCols;
+  const int cw = chain_cols(s.N, s.P, s.Q / kChainSK, false);
+  if (!chain_shape_ok(s, cw) || s.b != 1 || cus <= 0 || nseq < 1 || s.nc < 1) return pl;
+  const long cpr = long(s.H) * s.P / cw;
   const long per_unit = chain_per_unit(s);
   const long want = std::min<long>(s.nc, per_unit * cus / cpr);
   if (want < 1) return pl;                 // not even one walk per 64 columns fits at once

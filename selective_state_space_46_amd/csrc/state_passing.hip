@@ -273,11 +273,12 @@ __global__ __launch_bounds__(kThreads) void state_passing_bwd_tiled(
 
 // Packed sequences through the fused walk: the recurrence over segments
 // (launch_varlen_segment_recurrence). Work-groups 0 .. ntiles-1: one (head,
-// 16 x 64 tile) each, walking the segments in order with S, F and the decay
-// exponents of the segments ahead loaded kDepth segments early (they do not
-// depend on the recurrence); a final state completed at segment k goes out
-// through LDS in the caller's [n][p] layout. Work-groups ntiles + i: an
-// empty sequence i's final state is its initial state (or zero).
+// 16 x 64 tile) each, walking the segments in order with S and the decay
+// exponents of the segments ahead loaded kDepth segments early (they do
+// not depend on the recurrence); a final state completed at segment k (its F
+// read then) goes out through LDS in the caller's [n][p] layout. Work-groups
+// ntiles + i: an empty sequence i's final state is its initial state (or
+// zero).
 __global__ __launch_bounds__(kThreads) void varlen_segment_recurrence(
     float* __restrict__ S, const float* __restrict__ F, const float* __restrict__ segdec,
     const float* __restrict__ fdec, const int* __restrict__ fseq, const int* __restrict__ cu,
@@ -307,12 +308,11 @@ __global__ __launch_bounds__(kThreads) void varlen_segment_recurrence(
   const size_t off0 = size_t(h) * sbh + hb_off(p, n, N);
   const float* sd = segdec + size_t(h) * nseg;
   const float* fd = fdec + size_t(h) * nseg;
-  f32x4 rs[kDepth], rf[kDepth];
+  f32x4 rs[kDepth];
   float rsd[kDepth], rfd[kDepth];
   int rfs[kDepth];
   auto fetch = [&](int k, int j) {
     rs[j] = *reinterpret_cast<const f32x4*>(S + off0 + size_t(k) * cstride);
-    rf[j] = *reinterpret_cast<const f32x4*>(F + off0 + size_t(k) * cstride);
     rsd[j] = sd[k];
     rfd[j] = fd[k];
     rfs[j] = fseq[k];
@@ -326,12 +326,14 @@ __global__ __launch_bounds__(kThreads) void varlen_segment_recurrence(
     for (int j = 0; j < kDepth; ++j) {
       const int k = k0 + j;
       if (k < nseg) {
-        const f32x4 e = rs[j], fk = rf[j];
+        const f32x4 e = rs[j];
         const float a = expf(rsd[j]), af = expf(rfd[j]);
         const int fs = rfs[j];                 // uniform
         if (k + kDepth < nseg) fetch(k + kDepth, j);
         if (fs >= 0 && fs < nseq && fin) {
-          // sequence fs, continued into segment k, ends there
+          // sequence fs, continued into segment k, ends there (its local end
+          // state read only here: few segments have one)
+          const f32x4 fk = *reinterpret_cast<const f32x4*>(F + off0 + size_t(k) * cstride);
           tile[4 * nq][pi] = fk.x + af * carry.x;
           tile[4 * nq + 1][pi] = fk.y + af * carry.y;
           tile[4 * nq + 2][pi] = fk.z + af * carry.z;

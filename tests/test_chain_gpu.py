@@ -1,9 +1,10 @@
 """GPU parity of the fused chunk-state + state-passing launch (the forward
 path for equal-length rows with dstate 128 or 256 and chunk_len a multiple
 of 64 whose work-groups -- one per batch row and 64 columns of the flattened
-(head, headdim) axis -- fill a 256-unit MI355X in one round: 128 .. 256 of
-them, one per unit, or at dstate 128 with chunk_len >= 128 up to 512, two per
-unit) against the fp64 oracle, through the C ABI.
+(head, headdim) axis, 128 at dstate 256 with headdim 64 and chunk_len 256 --
+fill a 256-unit MI355X in one round: 128 .. 256 of them, one per unit, or at
+dstate 128 with chunk_len >= 128 up to 512, two per unit) against the fp64
+oracle, through the C ABI.
 
 Where whole rows give fewer walks than half the units, each row is cut into
 segments walked from zero, a recurrence over the segments gives the state
@@ -35,8 +36,13 @@ def _units():
     return torch.cuda.get_device_properties(0).multi_processor_count
 
 
+def _cols(N, P, q):
+    """columns per walk work-group (the library's rule)"""
+    return 128 if N == 256 and P == 64 and q == 256 else 64
+
+
 def _w(b, T, H, P, N, G, q, seed, init=True, dt_mode="softplus"):
-    wgs = b * H * P // 64
+    wgs = b * H * P // _cols(N, P, q)
     top = 512 if (N == 128 and q >= 128) else 256
     assert 128 <= wgs <= top and (P != 32 or (H // G) % 2 == 0), "shape must take the fused path"
     return workloads.with_shape(workloads.MAMBA2_130M, batch=b, seqlen=T, nheads=H, headdim=P, dstate=N,
@@ -64,9 +70,25 @@ def test_chain_chunk_lengths_ragged(q):
     _check(_w(2, 3 * 256 + 77, 64, 64, 128, 1, q, seed=8000 + q))
 
 
-@pytest.mark.parametrize("P,N,H", [(32, 128, 128), (128, 128, 32), (32, 256, 128), (64, 256, 64), (128, 256, 32)])
+@pytest.mark.parametrize("P,N,H", [(32, 128, 128), (128, 128, 32), (32, 256, 128), (64, 256, 128), (128, 256, 32)])
 def test_chain_shapes(P, N, H):
+    """(64, 256): 128-column work-groups (two heads each), the C B^T tiles
+    in the same launch behind the walks"""
     _check(_w(2, 300, H, P, N, 1, 256, seed=8100 + P + N))
+
+
+def test_chain_128_columns_groups_and_odd_heads():
+    """128-column walks whose two heads share a B/C group (4 groups of 32
+    heads); an odd number of heads per group at the same shape cannot pair
+    its heads and takes the two-kernel path, with the same results"""
+    import selective_state_space_46_amd as ssd
+    _check(_w(2, 555, 128, 64, 256, 4, 256, seed=8150))
+    w = workloads.with_shape(workloads.MAMBA2_130M, batch=2, seqlen=555, nheads=129, headdim=64, dstate=256,
+                             ngroups=3, chunk_len=256, init="normal0.1", seed=8151)
+    assert ssd.ssd_chunk_scan_fwd_fused_states(2, 555, 129, 64, 256, 3, 256, ssd.SSD_BF16) == 0
+    inp = workloads.make_fwd_inputs(w)
+    y, fin = gpu_fwd(inp, "bf16", 256)
+    assert_fwd_close(fwd_errors(inp, y, fin, 256), TOL, "two-kernel path, 43 heads per group")
 
 
 def test_chain_groups_no_init():
@@ -122,10 +144,10 @@ def test_chain_odd_batch_tokens_heads(b, T, H):
 # ---------------------------------------------------------------- segmented rows
 
 def _seg_plan(b, T, H, P, N, q):
-    """the segment count the library documents: whole rows give b H P / 64
+    """the segment count the library documents: whole rows give b H P / cols
     walks; below half the units each row is cut into ceil(nc / seglen)
     segments of seglen = ceil(nc / min(nc, units // walks)) chunks"""
-    cus, wgs, nc = _units(), b * H * P // 64, -(-T // q)
+    cus, wgs, nc = _units(), b * H * P // _cols(N, P, q), -(-T // q)
     want = min(nc, cus // wgs)
     seglen = -(-nc // want)
     nseg = -(-nc // seglen)
@@ -133,7 +155,8 @@ def _seg_plan(b, T, H, P, N, q):
 
 
 def _ws(b, T, H, P, N, G, q, seed, init=True, dt_mode="softplus"):
-    assert 2 * (b * H * P // 64) < _units() and _seg_plan(b, T, H, P, N, q) > 1, "shape must take segments"
+    assert 2 * (b * H * P // _cols(N, P, q)) < _units() and _seg_plan(b, T, H, P, N, q) > 1, \
+        "shape must take segments"
     return workloads.with_shape(workloads.MAMBA2_130M, batch=b, seqlen=T, nheads=H, headdim=P, dstate=N,
                                 ngroups=G, chunk_len=q, init="normal0.1" if init else "zero",
                                 dt_mode=dt_mode, seed=seed)
@@ -173,8 +196,8 @@ def test_segments_init_in_place():
 def test_fused_path_choice_on_the_workloads():
     """The 130M-shaped layer (192 work-groups, one per unit) and the 2.7B-shaped
     one (320, two per unit) take the fused launch over whole rows; the
-    128K-token row (24 walks of whole rows) is cut into segments, ten on a
-    256-unit MI355X."""
+    128K-token row (12 walks of whole rows, 128 columns each) is cut into
+    segments, 21 on a 256-unit MI355X."""
     import selective_state_space_46_amd as ssd
     for w in (workloads.MAMBA2_130M, workloads.MAMBA2_2P7B, workloads.LONG_128K):
         want = 1 if w is not workloads.LONG_128K else _seg_plan(w.batch, w.seqlen, w.nheads, w.headdim,
@@ -183,4 +206,4 @@ def test_fused_path_choice_on_the_workloads():
                                                   w.chunk_len, ssd.SSD_BF16)
         assert got == want, (w.name, got, want)
     if _units() == 256:
-        assert _seg_plan(1, 131072, 24, 64, 256, 256) == 10
+        assert _seg_plan(1, 131072, 24, 64, 256, 256) == 21

@@ -92,6 +92,12 @@ PLAN_SHAPES = [
 ]
 
 
+def _cols(N, P, Q):
+    """columns per walk work-group: 128 for the forward at dstate 256,
+    headdim 64, chunk_len 256, else 64 (restated from the library)"""
+    return 128 if N == 256 and P == 64 and Q == 256 else 64
+
+
 def _plan(b, T, H, P, N, G, Q, cus=256):
     import selective_state_space_46_amd as ssd
     return ssd.ssd_chunk_scan_fwd_plan(b, T, H, P, N, G, Q, ssd.SSD_BF16, cus)
@@ -109,7 +115,7 @@ def test_walk_plan_covers_every_chunk(shape):
         assert seglen == 0
         return
     assert seglen >= 1 and (nseg - 1) * seglen < nc <= nseg * seglen
-    walks = b * H * P // 64 * nseg
+    walks = b * H * P // _cols(N, P, Q) * nseg
     assert 128 <= walks <= (512 if N == 128 and Q >= 128 else 256)
     if nseg > 1:
         assert walks <= 256
@@ -125,10 +131,11 @@ def test_walk_copies_stay_inside_the_tensors(shape):
     nseg, seglen = _plan(*shape)
     if nseg == 0:
         return
-    nc, SPC, cpr = -(-T // Q), Q // 64, H * P // 64
+    cw = _cols(N, P, Q)
+    nc, SPC, cpr = -(-T // Q), Q // 64, H * P // cw
     rows = np.arange(64)
     for wid in range(b * cpr * nseg):
-        c0 = (wid % cpr) * 64
+        c0 = (wid % cpr) * cw
         seg, bb = (wid // cpr) % nseg, wid // cpr // nseg
         h0 = c0 // P
         g = h0 // (H // G)
@@ -143,12 +150,14 @@ def test_walk_copies_stay_inside_the_tensors(shape):
             tok = r0 + s0 + (rows if s0 + 64 <= n else np.minimum(rows, n - 1 - s0))
             assert tok.min() >= bb * T and tok.max() < (bb + 1) * T
             assert ((tok.max() * G + g) * N + N - 1) < b * T * G * N
-            assert tok.max() * H * P + c0 + 63 < b * T * H * P
+            assert tok.max() * H * P + c0 + cw - 1 < b * T * H * P
         # states entering each chunk, and a segment's last local state
-        hmax = ((bb * nc + cbeg + ncw - 1) * H + (h0 + (1 if P == 32 else 0))) * P * N + P * N - 1
+        hlast = (c0 + cw - 1) // P                    # the work-group's last head
+        assert hlast < H and hlast // (H // G) == g   # its heads share the B group
+        hmax = ((bb * nc + cbeg + ncw - 1) * H + hlast) * P * N + P * N - 1
         assert hmax < b * nc * H * P * N
         if nseg > 1:
-            assert ((bb * nseg + seg) * H + h0) * P * N + P * N - 1 < b * nseg * H * P * N
+            assert ((bb * nseg + seg) * H + hlast) * P * N + P * N - 1 < b * nseg * H * P * N
     # chunk_scan: chunk c's segment and the state entering it
     if nseg > 1:
         assert all(c // seglen < nseg for c in range(nc))
@@ -160,7 +169,7 @@ def test_walk_plan_on_other_unit_counts():
     assert _plan(8, 2048, 24, 64, 128, 1, 256, cus=128) == (1, 8)      # 192 walks, two per unit
     assert _plan(8, 2048, 24, 64, 128, 1, 256, cus=512) == (2, 4)      # under half the units: two segments
     assert _plan(1, 300, 8, 64, 128, 1, 256, cus=256) == (0, 0)        # too little work even in segments
-    assert _plan(1, 131072, 24, 64, 256, 1, 256, cus=256) == (10, 52)
+    assert _plan(1, 131072, 24, 64, 256, 1, 256, cus=256) == (21, 25)  # 128-column walks: 12 per row
     assert _plan(1, 131072, 24, 64, 256, 1, 256, cus=0) == (0, 0)
 
 
@@ -251,7 +260,7 @@ def test_varlen_walk_plan(shape):
     and at most 128 slots each; none for shapes the walk does not serve."""
     T, nseq, H, P, N, G, Q = shape
     nseg, L = _varlen_plan(*shape)
-    cpr = H * P // 64
+    cpr = H * P // _cols(N, P, Q)
     cap = (512 if N == 128 and Q >= 128 else 256)
     nslots = -(-T // Q) + nseq
     if nseg == 0:
