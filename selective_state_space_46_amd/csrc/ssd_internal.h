@@ -224,10 +224,13 @@ inline WsLayout ws_layout(const FwdShape& s, bool mfma, const ChainPlan& pl) {
 // XCD-aware block order: the hardware hands consecutive work-groups to the 8
 // XCDs round-robin, so block id k runs on XCD k % 8. Renumbering blocks so that
 // each XCD receives one contiguous range of logical ids keeps logical
-// neighbours (which share B/C rows) inside one XCD's L2.
-__device__ __forceinline__ int xcd_swizzle(int bid, int nblocks) {
-  if (nblocks % 8) return bid;
-  return (bid % 8) * (nblocks / 8) + bid / 8;
+// neighbours (which share B/C rows) inside one XCD's L2. XCD x holds
+// ceil((nblocks - x) / 8) blocks: q + 1 for the first r = nblocks % 8 of them,
+// q = nblocks / 8 for the rest, so its range starts at x q + min(x, r); a
+// bijection of [0, nblocks) for any nblocks.
+__host__ __device__ __forceinline__ int xcd_swizzle(int bid, int nblocks) {
+  const int q = nblocks / 8, r = nblocks % 8, x = bid % 8;
+  return x * q + (x < r ? x : r) + bid / 8;
 }
 
 // Optional start / stop events of one forward launch. The launchers pass them

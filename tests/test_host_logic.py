@@ -277,6 +277,9 @@ def test_varlen_walk_plan(shape):
     assert ssd.ssd_chunk_scan_fwd_varlen_plan(T, 0, H, P, N, G, Q, ssd.SSD_BF16, 256) == (0, 0)
 
 
+run_xcd = [None]   # set by the varlen_tables fixture: the library's xcd_swizzle on the host
+
+
 @pytest.fixture(scope="module")
 def varlen_tables(tmp_path_factory):
     """builds the packed-sequence chunk table on the host with the library's
@@ -295,6 +298,11 @@ def varlen_tables(tmp_path_factory):
                         "-I", os.path.join(root, "include"), "-o", exe,
                         os.path.join(here, "varlen_tables_driver.hip")], capture_output=True, text=True)
     assert r.returncode == 0, r.stderr[-3000:]
+
+    def xcd(n):
+        out = subprocess.run([exe], input=f"xcd {n}\n", capture_output=True, text=True, check=True).stdout.split()
+        return np.array(out, dtype=np.int64)
+    run_xcd[0] = xcd
 
     def run(T, Q, cu):
         inp = f"{T} {len(cu) - 1} {Q}\n" + " ".join(str(int(v)) for v in cu) + "\n"
@@ -356,3 +364,19 @@ def test_varlen_tables(varlen_tables, case):
             assert bool(flags & 1) == (cur == -1) and (cur == -1 or seq == cur)
             cur = -1 if flags & 2 else seq
         assert cur == -1
+
+
+@pytest.mark.parametrize("n", [1, 7, 8, 9, 240, 252, 255, 256, 257, 12288, 12291])
+def test_xcd_swizzle_is_a_bijection_with_contiguous_ranges(varlen_tables, n):
+    """the library's XCD renumbering (ssd_internal.h, run on the host): a
+    bijection of [0, n) for any n, under which the work-groups the hardware
+    gives XCD x (ids x, x + 8, ...) take one contiguous range of logical ids,
+    in order; multiples of 8 keep the former mapping x (n / 8) + id / 8"""
+    ids = run_xcd[0](n)
+    assert sorted(ids.tolist()) == list(range(n))
+    for x in range(min(n, 8)):
+        mine = ids[x::8]
+        assert np.array_equal(mine, np.arange(mine[0], mine[0] + len(mine)))
+    if n % 8 == 0:
+        b = np.arange(n)
+        assert np.array_equal(ids, (b % 8) * (n // 8) + b // 8)

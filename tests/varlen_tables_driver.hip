@@ -1,14 +1,23 @@
-// Host-only driver for tests/test_host_logic.py: builds the packed-sequence
-// chunk table with the library's own varlen_span / varlen_fill
-// (ssd_internal.h), as the table kernel does per sequence, and prints it.
-// stdin: T nseq Q, then nseq + 1 offsets. stdout: nslots, then one line per
-// chunk slot (4 integers).
+// Host-only driver for tests/test_host_logic.py, running the library's own
+// index helpers (ssd_internal.h) on the host:
+//   stdin "T nseq Q" and nseq + 1 offsets: builds the packed-sequence chunk
+//   table with varlen_span / varlen_fill, as the table kernel does per
+//   sequence; stdout: nslots, then one line per chunk slot (4 integers);
+//   stdin "xcd n": the logical id xcd_swizzle gives each of n work-groups,
+//   one per line.
 #include <cstdio>
 #include <vector>
 
 #include "ssd_internal.h"
 
 int main() {
+  char mode[8] = {0};
+  if (std::scanf(" %7[a-z]", mode) == 1) {
+    int n;
+    if (std::scanf("%d", &n) != 1 || n < 1) return 2;
+    for (int b = 0; b < n; ++b) std::printf("%d\n", ssd::xcd_swizzle(b, n));
+    return 0;
+  }
   int T, nseq, Q;
   if (std::scanf("%d %d %d", &T, &nseq, &Q) != 3 || T < 1 || nseq < 1 || Q < 1) return 2;
   std::vector<int> cu(nseq + 1);
