@@ -940,55 +940,66 @@ void chunk_state_chain_kernel(
 // The C B^T tiles alone, for segmented launches: their walks take nearly
 // every compute unit for the whole launch, so tile work-groups placed behind
 // them (as the whole-row launch does) would all run on the few units left.
-// A work-group per (batch, chunk, group) and a wave per pair of 32-row blocks
-// of C (i and lpc - 1 - i: 1 + lpc tiles per wave, balanced): the wave loads
-// its C rows once per block and streams the B row blocks j <= i, the next
-// one loading while the current one feeds the matrix cores. The tiles are
-// the ones chunk_scores_tile computes, at the same places.
+// The tiles are the ones chunk_scores_tile computes, at the same places.
+// The same tiles with the chunk's B rows staged in LDS once (Q x N bf16,
+// 128 KB at Q 256, N 256; each 16-byte piece p of row r at piece p ^ (r % 8),
+// so the 32 rows a wave reads at one piece fall on different banks): a
+// work-group per (batch, chunk, group) of 8 waves, wave w holding the C rows
+// of 32-row block w (w < 4) or 11 - w (w >= 4), so the two waves of a SIMD
+// hold blocks k and 7 - k (lpc + 1 tiles per SIMD at Q 256); each tile reads
+// its B block from LDS. B crosses from memory once per chunk instead of once
+// per tile.
 template <int N>
-__global__ __launch_bounds__(256) void chunk_scores_rows_kernel(const uint16_t* __restrict__ Bm,
-                                                                const uint16_t* __restrict__ Cm,
-                                                                uint16_t* __restrict__ CB, int T, int G, int Q,
-                                                                int nc, const int4* __restrict__ tab) {
+__global__ __launch_bounds__(512) void chunk_scores_lds_kernel(const uint16_t* __restrict__ Bm,
+                                                               const uint16_t* __restrict__ Cm,
+                                                               uint16_t* __restrict__ CB, int T, int G, int Q,
+                                                               int nc, const int4* __restrict__ tab) {
+  constexpr int RP = N / 8;                     // 16-byte pieces per row
+  __shared__ __attribute__((aligned(16))) uint16_t sB[kMaxQ * N];
   const int lpc = Q / 32, ntile = lpc * (lpc + 1) / 2;
-  const int wave = wave_id(), lane = threadIdx.x & 63;
+  const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
   const int l32 = lane & 31, g2 = lane >> 5;
   const int g = int(blockIdx.x) % G;
   const int c = (int(blockIdx.x) / G) % nc;
   const int b = int(blockIdx.x) / G / nc;
-  const ChunkRows cr = chunk_rows(tab, b, c, T, Q);   // packed rows: the slot's (none for an unused one)
-  // rows tl of C, ts of B inside the chunk (clamped into it; zeroed past it)
-  auto rows16 = [&](const uint16_t* M, int t, u32x4 (&f)[N / 16]) {
-    const uint16_t* r = M + ((cr.r0 + min(t, cr.n - 1)) * G + g) * size_t(N) + 8 * g2;
+  const ChunkRows cr = chunk_rows(tab, b, c, T, Q);
+  if (cr.n <= 0) return;                        // an unused slot: uniform, before the barrier
+  // B rows 0 .. Q-1 of the chunk (rows past its tokens as zeros)
+  for (int e = tid; e < Q * RP; e += 512) {
+    const int r = e / RP, p = e % RP;
+    const u32x4 v = load16(Bm + ((cr.r0 + min(r, cr.n - 1)) * G + g) * size_t(N) + 8 * p);
+    *reinterpret_cast<u32x4*>(&sB[r * N + 8 * (p ^ (r & 7))]) = keep_or_zero(r < cr.n, v);
+  }
+  const int i = wave < 4 ? wave : 11 - wave;    // C row block (wave-uniform)
+  const bool mine = i < lpc && 32 * i < cr.n;
+  u32x4 cf[N / 16];
+  if (mine) {
+    const int t = 32 * i + l32;
+    const uint16_t* crow = Cm + ((cr.r0 + min(t, cr.n - 1)) * G + g) * size_t(N) + 8 * g2;
 #pragma unroll
-    for (int ks = 0; ks < N / 16; ++ks) f[ks] = keep_or_zero(t < cr.n, load16(r + 16 * ks));
-  };
+    for (int ks = 0; ks < N / 16; ++ks) cf[ks] = keep_or_zero(t < cr.n, load16(crow + 16 * ks));
+  }
+  __syncthreads();
+  if (!mine) return;
   const size_t base = ((size_t(b) * nc + c) * G + g) * ntile;
-  for (int which = 0; which < 2; ++which) {
-    const int i = which ? lpc - 1 - wave : wave;      // C row block (wave-uniform)
-    if (32 * i >= cr.n) continue;                     // past the valid tokens: never read
-    u32x4 cf[N / 16], bf[N / 16], bn[N / 16];
-    rows16(Cm, 32 * i + l32, cf);
-    rows16(Bm, l32, bf);                              // B row block 0
-    for (int j = 0; j <= i; ++j) {
-      if (j < i) rows16(Bm, 32 * (j + 1) + l32, bn);  // the next B row block
-      f32x16 acc = zero16();
+  for (int j = 0; j <= i; ++j) {
+    const int r = 32 * j + l32;                 // this lane's B row
+    f32x16 acc = zero16();
 #pragma unroll
-      for (int ks = 0; ks < N / 16; ++ks) acc = mfma32x32x16(bf[ks], cf[ks], acc);   // rows s, column l
-      u32x4 lo, hi;
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        lo[m] = pack_bf16x2(acc[2 * m], acc[2 * m + 1]);
-        hi[m] = pack_bf16x2(acc[8 + 2 * m], acc[8 + 2 * m + 1]);
-      }
-      u32x4* dst = reinterpret_cast<u32x4*>(CB + (base + size_t(i) * (i + 1) / 2 + j) * 1024 + size_t(lane) * 16);
-      dst[0] = lo;
-      dst[1] = hi;
-      if (j < i) {
-#pragma unroll
-        for (int ks = 0; ks < N / 16; ++ks) bf[ks] = bn[ks];
-      }
+    for (int ks = 0; ks < N / 16; ++ks) {
+      const int p = 2 * ks + g2;                // pieces n = 16 ks + 8 g2 .. + 7
+      const u32x4 bf = *reinterpret_cast<const u32x4*>(&sB[r * N + 8 * (p ^ (r & 7))]);
+      acc = mfma32x32x16(bf, cf[ks], acc);      // rows s, column l
     }
+    u32x4 lo, hi;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      lo[m] = pack_bf16x2(acc[2 * m], acc[2 * m + 1]);
+      hi[m] = pack_bf16x2(acc[8 + 2 * m], acc[8 + 2 * m + 1]);
+    }
+    u32x4* dst = reinterpret_cast<u32x4*>(CB + (base + size_t(i) * (i + 1) / 2 + j) * 1024 + size_t(lane) * 16);
+    dst[0] = lo;
+    dst[1] = hi;
   }
 }
 
@@ -1025,10 +1036,9 @@ hipError_t launch_chain_np(const FwdShape& s, const ChainPlan& pl, const void* x
     const long rows = long(s.b) * s.nc * s.G;
     const int4* tab = pl.var ? vw.tab : nullptr;
     if (rows >= 2L * device_units()) {
-      // (segments need chunk_len a multiple of 64: an even number of row blocks)
-      hipExtLaunchKernelGGL((chunk_scores_rows_kernel<N>), dim3(unsigned(rows)), dim3(64 * (s.Q / 64)), 0, st,
-                            ev.start, nullptr, 0, static_cast<const uint16_t*>(B), static_cast<const uint16_t*>(C),
-                            CB, s.T, s.G, s.Q, s.nc, tab);
+      hipExtLaunchKernelGGL((chunk_scores_lds_kernel<N>), dim3(unsigned(rows)), dim3(512), 0, st, ev.start, nullptr,
+                            0, static_cast<const uint16_t*>(B), static_cast<const uint16_t*>(C), CB, s.T, s.G, s.Q,
+                            s.nc, tab);
     } else {
       hipExtLaunchKernelGGL((chunk_scores_tiles_kernel<N>), dim3(unsigned((alltiles + kChainWaves - 1) / kChainWaves)),
                             dim3(kChainThreads), 0, st, ev.start, nullptr, 0, static_cast<const uint16_t*>(B),
