@@ -189,3 +189,18 @@ def test_varlen_long_sequences_span_segments(Q, N, with_init):
     nseg, L = _plan(inp, cu, Q)
     assert nseg > 1 and 2 * L * Q < max(lens), (nseg, L)
     _check(inp, cu, Q, final_in_place=with_init)
+
+
+def test_varlen_many_short_sequences():
+    """150 sequences of 0 .. 300 tokens (several restarts inside each walk,
+    sequences of one chunk and less, empty ones) with initial states,
+    dstate 128, chunk_len 128, 24 heads (about 21 segments): the fused walk
+    over segments"""
+    rng = np.random.default_rng(6700)
+    lens = rng.integers(0, 301, size=150)
+    lens[::17] = 0
+    cu = np.concatenate([[0], np.cumsum(lens)]).tolist()
+    inp = _inputs(cu[-1], 24, 64, 128, 1, len(lens), seed=6701)
+    nseg, L = _plan(inp, cu, 128)
+    assert nseg > 1 and len(lens) >= 4 * nseg, (nseg, L)
+    _check(inp, cu, 128, final_in_place=True)
