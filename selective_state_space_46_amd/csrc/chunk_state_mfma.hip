@@ -286,19 +286,20 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma_kernel(
 // the recurrence of state_passing.hip folded into the chunk-state product
 // (youngju.dev "Mamba / selective SSM", "SSDアルゴリズムとチャンク分割": the
 // state handed from chunk to chunk; Qiita "Mamba-2" article, section 4.2,
-// steps 2 and 3). A work-group owns one batch row and 64 consecutive columns
-// of the flattened (head, p) axis -- two 32-column blocks of one head, or two
-// heads of headdim 32 in one B/C group -- and walks that row's chunks in
+// steps 2 and 3). A work-group owns one batch row and CW (64 or 128, see
+// chain_cols) consecutive columns of the flattened (head, p) axis -- 32-column
+// blocks of one head, or of two heads in one B/C group -- and walks that
+// row's chunks in
 // order, its running states held in the fp32 accumulators of the matrix
 // cores: at a chunk's start the accumulators (= H_c) go out as bf16 for
 // chunk_scan, are scaled by the chunk's decay, and the chunk's products then
 // accumulate on top, leaving H_{c+1}. The fp32 chunk states S_c never reach
 // HBM (the two-kernel form writes and re-reads them).
 //
-// Segments (forward only). Where one walk per (batch row, 64 columns) leaves
+// Segments (forward only). Where one walk per (batch row, CW columns) leaves
 // most compute units idle (a few long rows), each row is cut into nseg
 // segments of seglen consecutive chunks (the last may be shorter) and every
-// (row, 64 columns, segment) walks its own segment: segment 0 from the
+// (row, CW columns, segment) walks its own segment: segment 0 from the
 // initial state, the others from zero. The state handed from chunk to chunk
 // is linear in the state a segment starts from, and the summaries compose
 // associatively ((decay_1, S_1) then (decay_2, S_2) gives (decay_1 decay_2,
@@ -329,8 +330,8 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma_kernel(
 // sequence (fseq) for the recurrence over segments. Unused slots (between
 // sequences) have no rows: zero weights and decay 1 leave the state as it is.
 //
-// Tokens stream through 64-row slices of B (all of dstate, shared by the two
-// column blocks) and x (the 64 columns), copied straight from global memory
+// Tokens stream through 64-row slices of B (all of dstate, shared by the
+// column blocks) and x (the CW columns), copied straight from global memory
 // into LDS (global_load_lds, 16 bytes per lane) in a swizzled row-major
 // layout, STAGES slices resident: one read while the others load. The copies
 // use no registers. The MFMA operands are read transposed
@@ -340,8 +341,9 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma_kernel(
 // n, lanes p), so a lane holds four consecutive n of one p: H_c leaves as
 // runs of its [p][n] rows, init and final ([n][p]) as whole rows of p.
 //
-// Waves: four compute waves (wave w: column block w & 1, n tiles w >> 1,
-// (w >> 1) + 2, ...), one table wave and three copy waves. The table wave
+// Waves: two compute waves per 32-column block (CW / 16 in all; wave w:
+// column block w % (CW / 32), n tiles w / (CW / 32), that + 2, ...), one
+// table wave and three copy waves. The table wave
 // builds each chunk's weights and decay one chunk ahead from dt loaded one
 // chunk before that, and writes the Acs / dt rows; the copy waves issue the
 // slice copies and wait for them by count. The vector memory counter counts
@@ -351,10 +353,9 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma_kernel(
 // wave's dt loads are a chunk old when used, and the compute waves only
 // store. All waves pass the same barriers, one per slice.
 // ---------------------------------------------------------------------------
-constexpr int kChainWaves = 8;      // 4 compute, 1 table, 3 copy (64 columns)
+constexpr int kChainWaves = 8;      // waves of a C B^T tile work-group (one tile per wave)
 constexpr int kChainThreads = 64 * kChainWaves;
 constexpr int kChainSK = 64;        // tokens per slice
-constexpr int kChainCols = 64;      // flattened (head, p) columns per work-group (see chain_cols)
 constexpr int kVarWalkSlots = 128;  // chunk slots per walk over packed rows (at most)
 
 // Columns per work-group. The forward at dstate 256, headdim 64 and
@@ -1195,7 +1196,7 @@ ChainPlan varlen_chain_plan_for(const FwdShape& s, int nseq, int cus) {
   const long cpr = long(s.H) * s.P / cw;
   const long per_unit = chain_per_unit(s);
   const long want = std::min<long>(s.nc, per_unit * cus / cpr);
-  if (want < 1) return pl;                 // not even one walk per 64 columns fits at once
+  if (want < 1) return pl;                 // not even one segment per column block fits at once
   // at most kVarWalkSlots slots per segment (their table entries sit in LDS):
   // longer rows take more segments than fit at once
   pl.seglen = int(std::min<long>((s.nc + want - 1) / want, kVarWalkSlots));
