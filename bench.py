@@ -167,8 +167,10 @@ def impl_work(w: workloads.FwdWorkload, nseg: int) -> dict:
         out["chunk_state"] = {"bytes": x + 2 * bc + dtb + 2 * acs + st + cbt}
     if nseg >= 1:
         sst = 4 * b * nseg * H * N * P
+        # with segments the tiles launch also writes C in operand order (bc
+        # bytes), which chunk_scan reads in place of C
         out["chunk_state"] = {"bytes": x + 2 * bc + dtb + 2 * acs + cbt + hst + ini
-                              + (fst if nseg == 1 else sst + 4 * b * H * (nc + nseg))}
+                              + (fst if nseg == 1 else sst + 4 * b * H * (nc + nseg) + bc)}
         out["state_passing"] = {"bytes": 0 if nseg == 1 else 2 * sst + fst + 4 * b * H * nseg}
         if nseg > 1:
             out["chunk_scan"] = {"bytes": out["chunk_scan"]["bytes"] + sst + 4 * b * H * nc}

@@ -35,8 +35,9 @@
 // l), which makes every per-token factor one multiplier per lane:
 //   1. y^T = H_c^T C_l^T (k = dstate): H_c staged once in LDS as stored (bf16,
 //      fragment order, from the fused walk or state_passing, see hb_off) when
-//      the super-chunk is one chunk, C_l rows straight from HBM; then
-//      y^T *= exp(Acs_l).
+//      the super-chunk is one chunk, C_l rows straight from memory (with
+//      segments: from the copy of C the tiles launch leaves in operand order,
+//      1 KB contiguous per load); then y^T *= exp(Acs_l).
 //   2. for each column block s <= l of the chunk: the C B^T tile (lane =
 //      column l, registers = rows s in runs of 4) times the decay, rounded to
 //      bf16, is the B operand of y^T += X^T G^T under a k permutation that the
@@ -45,7 +46,9 @@
 //      ds_read_b64_tr_b16. Tiles are loaded one tile ahead of use, into two
 //      buffers used in turn.
 //   3. + D x (x from the same LDS tile), bf16 rounding, 8-byte stores of 4
-//      consecutive p.
+//      consecutive p; with W = 8 the rounded rows go back through the x tile
+//      (after a barrier: no wave reads x any more) and leave as 16-byte pieces
+//      of whole token rows.
 // SEG (rows cut into segments by the fused chunk-state walk): Hb holds the
 // local states, from zero at each segment's start; the state entering chunk
 // c of segment k >= 1 is Hb_c + exp(cdec_c) Hin_k (Hin fp32 [b, nseg, H,
@@ -85,7 +88,7 @@ void chunk_scan_mfma_kernel(
     const float* __restrict__ Acs, const float* __restrict__ dtq, const uint16_t* __restrict__ Hb,
     const float* __restrict__ D, uint16_t* __restrict__ y, const int4* __restrict__ tab, int T, int H,
     int G, int Q, int nc, int nsc, const float* __restrict__ Hin, const float* __restrict__ cdec, int nseg,
-    int seglen) {
+    int seglen, const uint16_t* __restrict__ Cf) {
   constexpr int kThreads = 64 * W;
   constexpr int NB = 8 / W;   // 32-row blocks per wave
   constexpr int RBX = P / 8;  // 16-byte chunks per X' row
@@ -150,11 +153,20 @@ void chunk_scan_mfma_kernel(
     td[1] = ts[ir * 128 + 1];
     tn[0] = ts[0];
     tn[1] = ts[1];
-    const ChunkRows r = crows(i / lpc);
-    const long row = r.r0 + min((i % lpc) * 32 + l32, r.n - 1);
-    const uint16_t* cr = Cm + (row * G + g) * size_t(N) + 8 * g2;
+    if constexpr (SEG) {
+      // C in operand order from the tiles launch (Cf, zeros past the chunk's
+      // tokens): each load is 1 KB contiguous per wave
+      const uint16_t* cr =
+          Cf + ((((size_t(b) * nc + c0 + i / lpc) * G + g) * lpc + i % lpc) * (N / 16) * 64 + lane) * 8;
 #pragma unroll
-    for (int ks = 0; ks < N / 16; ++ks) cfv[ks] = load16(cr + 16 * ks);
+      for (int ks = 0; ks < N / 16; ++ks) cfv[ks] = load16(cr + 512 * ks);
+    } else {
+      const ChunkRows r = crows(i / lpc);
+      const long row = r.r0 + min((i % lpc) * 32 + l32, r.n - 1);
+      const uint16_t* cr = Cm + (row * G + g) * size_t(N) + 8 * g2;
+#pragma unroll
+      for (int ks = 0; ks < N / 16; ++ks) cfv[ks] = load16(cr + 16 * ks);
+    }
   };
   // the wave's first block: with W = 8 (one block each) waves w and w + 4
   // share a SIMD, so wave w >= 4 takes block 11 - w: every SIMD then holds
@@ -245,6 +257,15 @@ void chunk_scan_mfma_kernel(
   }
 
   const float Dh = D ? D[h] : 0.f;
+  // YLDS (one block per wave): the rounded outputs wait in registers until
+  // every wave has finished its tiles, then go through this wave's own rows of
+  // the x tile (no wave reads x any more) so that each store instruction
+  // writes whole 16-byte pieces of consecutive token rows; stored straight
+  // from the accumulators, each instruction would write 16 bytes in each of
+  // 32 token rows.
+  constexpr bool YLDS = W == 8;
+  u32x2 yv[P / 32][4];
+  int yblk = -1;                   // the block whose outputs yv holds (uniform), -1: none
   for (int which = 0; which < NB; ++which) {
     const int i = which ? 7 - wave : blk0;  // 32-row block of the super-chunk
     const ChunkRows cr = crows(i / lpc);
@@ -401,8 +422,22 @@ void chunk_scan_mfma_kernel(
       apply(irel, tdiag, true);
     }
 
-    // ---- epilogue: + D x (x re-read, from L2), round, store 4 consecutive p (8 bytes) per run
-    if (tok_ok) {
+    // ---- epilogue: + D x (x from the LDS tile), round; store 4 consecutive p
+    // (8 bytes) per run, or keep them for the row-wise store below
+    if constexpr (YLDS) {
+      yblk = i;
+#pragma unroll
+      for (int pb = 0; pb < P / 32; ++pb)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const u32x2 xv = *reinterpret_cast<const u32x2*>(&sX[lds_off<RBX, true>(lcol, 32 * pb + 8 * q + 4 * g2)]);
+          const float xs[4] = {bf16_lo(xv[0]), bf16_hi(xv[0]), bf16_lo(xv[1]), bf16_hi(xv[1])};
+          float o[4];
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) o[rr] = acc[pb][4 * q + rr] + Dh * xs[rr];
+          yv[pb][q] = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+        }
+    } else if (tok_ok) {
       u32x2 xr[P / 32][4];
 #pragma unroll
       for (int pb = 0; pb < P / 32; ++pb)
@@ -425,6 +460,32 @@ void chunk_scan_mfma_kernel(
       }
     }
   }
+  if constexpr (YLDS) {
+    // every wave is done with x (tiles and D x): each overwrites its own
+    // block's 32 rows of the x tile with its outputs, at the addresses its D x
+    // reads came from, and reads them back as 16-byte row pieces (RBX lanes
+    // per row, 64 / RBX rows per instruction) for the stores
+    __syncthreads();
+    if (yblk >= 0) {
+      const int i = yblk;
+      const ChunkRows cr = crows(i / lpc);
+      const int rq0 = (i % lpc) * 32;
+#pragma unroll
+      for (int pb = 0; pb < P / 32; ++pb)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          *reinterpret_cast<u32x2*>(&sX[lds_off<RBX, true>(32 * i + l32, 32 * pb + 8 * q + 4 * g2)]) = yv[pb][q];
+      constexpr int RPI = 64 / RBX;     // rows per store instruction
+      const int cc = lane % RBX;
+#pragma unroll
+      for (int u = 0; u < 32 / RPI; ++u) {
+        const int r = u * RPI + lane / RBX;   // row of the block
+        const u32x4 v = *reinterpret_cast<const u32x4*>(&sX[lds_off<RBX, true>(32 * i + r, 8 * cc)]);
+        if (rq0 + r < cr.n)
+          *reinterpret_cast<u32x4*>(y + ((cr.r0 + rq0 + r) * H + h) * size_t(P) + 8 * cc) = v;
+      }
+    }
+  }
 }
 
 template <int N, int P>
@@ -442,10 +503,11 @@ hipError_t launch_np(const FwdShape& s, const void* x, const uint16_t* CB, const
     hipExtLaunchKernelGGL(kern, dim3(unsigned(blocks)), dim3(64 * w), 0, st, ev.start, ev.stop, 0,
                           static_cast<const uint16_t*>(x), CB, static_cast<const uint16_t*>(C), Acs, dtq, Hb, D,
                           static_cast<uint16_t*>(y), tab, s.T, s.H, s.G, s.Q, s.nc, nsc, sg.Hin, sg.cdec, sg.nseg,
-                          sg.seglen);
+                          sg.seglen, sg.Cf);
   };
   const bool seg = sg.nseg > 1 || sg.var;
-  if (seg && (!sg.Hin || !sg.cdec || sg.seglen < 1 || sg.var != (tab != nullptr))) return hipErrorInvalidValue;
+  if (seg && (!sg.Hin || !sg.cdec || !sg.Cf || sg.seglen < 1 || sg.var != (tab != nullptr)))
+    return hipErrorInvalidValue;
   // packed sequences through segments: only where the fused walk runs
   if constexpr (N >= 128) {
     if (seg && tab) {

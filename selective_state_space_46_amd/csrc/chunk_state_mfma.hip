@@ -63,12 +63,26 @@ constexpr int kMaxQ = 256;
 // lane L holds column s = L%32 and the registers run over rows l. The
 // backward takes sums of these products that largely cancel, so they are not
 // rounded to bf16.
+// The C rows of 32-row block i of chunk (b, c), group g, as this lane holds
+// them for the matrix cores (cf[ks]: row 32 i + L % 32, dstate 16 ks + 8 (L /
+// 32) .. + 7; zeros past the chunk's tokens), stored in that order:
+// CF [b, nc, G, Q / 32, N / 16, 64 lanes, 8] bf16, so that chunk_scan reads
+// each operand as one contiguous 1 KB per wave (from C itself each of its
+// loads reads 32 bytes in each of 32 rows).
+template <int N>
+__device__ __forceinline__ void store_c_frags(uint16_t* __restrict__ CF, const u32x4 (&cf)[N / 16], int b, int c,
+                                              int g, int i, int G, int Q, int nc, int lane) {
+  u32x4* dst = reinterpret_cast<u32x4*>(CF) + (((size_t(b) * nc + c) * G + g) * (Q / 32) + i) * (N / 16) * 64 + lane;
+#pragma unroll
+  for (int ks = 0; ks < N / 16; ++ks) dst[64 * ks] = cf[ks];
+}
+
 template <int N, bool BOTH = false>
 __device__ __forceinline__ void chunk_scores_tile(const uint16_t* __restrict__ Bm,
                                                   const uint16_t* __restrict__ Cm,
                                                   uint16_t* __restrict__ CB, uint16_t* __restrict__ CBt,
                                                   const int4* __restrict__ tab, int T, int G, int Q, int nc,
-                                                  long wid, int lane) {
+                                                  long wid, int lane, uint16_t* __restrict__ CF = nullptr) {
   const int lpc = Q / 32;
   const int ntile = lpc * (lpc + 1) / 2;
   const int l32 = lane & 31, g2 = lane >> 5;
@@ -94,6 +108,7 @@ __device__ __forceinline__ void chunk_scores_tile(const uint16_t* __restrict__ B
   }
   const size_t tile_at = (((size_t(b) * nc + c) * G + g) * ntile + ti) * 1024;
   const size_t at = tile_at + size_t(lane) * 16;
+  if (CF && j == 0) store_c_frags<N>(CF, cf, b, c, g, i, G, Q, nc, lane);
   auto store32 = [&](uint16_t* dstbase, const f32x16& acc) {
     f32x4* dst = reinterpret_cast<f32x4*>(reinterpret_cast<float*>(dstbase) + tile_at) + lane;
 #pragma unroll
@@ -954,7 +969,8 @@ template <int N>
 __global__ __launch_bounds__(512) void chunk_scores_lds_kernel(const uint16_t* __restrict__ Bm,
                                                                const uint16_t* __restrict__ Cm,
                                                                uint16_t* __restrict__ CB, int T, int G, int Q,
-                                                               int nc, const int4* __restrict__ tab) {
+                                                               int nc, const int4* __restrict__ tab,
+                                                               uint16_t* __restrict__ CF) {
   constexpr int RP = N / 8;                     // 16-byte pieces per row
   __shared__ __attribute__((aligned(16))) uint16_t sB[kMaxQ * N];
   const int lpc = Q / 32, ntile = lpc * (lpc + 1) / 2;
@@ -979,6 +995,7 @@ __global__ __launch_bounds__(512) void chunk_scores_lds_kernel(const uint16_t* _
     const uint16_t* crow = Cm + ((cr.r0 + min(t, cr.n - 1)) * G + g) * size_t(N) + 8 * g2;
 #pragma unroll
     for (int ks = 0; ks < N / 16; ++ks) cf[ks] = keep_or_zero(t < cr.n, load16(crow + 16 * ks));
+    store_c_frags<N>(CF, cf, b, c, g, i, G, Q, nc, lane);
   }
   __syncthreads();
   if (!mine) return;
@@ -1012,16 +1029,17 @@ __global__ __launch_bounds__(kChainThreads) void chunk_scores_tiles_kernel(const
                                                                          const uint16_t* __restrict__ Cm,
                                                                          uint16_t* __restrict__ CB,
                                                                          const int4* __restrict__ tab, int T, int G,
-                                                                         int Q, int nc, long ntiles) {
+                                                                         int Q, int nc, long ntiles,
+                                                                         uint16_t* __restrict__ CF) {
   const long wid = long(blockIdx.x) * kChainWaves + wave_id();
-  if (wid < ntiles) chunk_scores_tile<N, false>(Bm, Cm, CB, nullptr, tab, T, G, Q, nc, wid, threadIdx.x & 63);
+  if (wid < ntiles) chunk_scores_tile<N, false>(Bm, Cm, CB, nullptr, tab, T, G, Q, nc, wid, threadIdx.x & 63, CF);
 }
 
 template <int N, int P, int SPC, int ST, bool F32S, bool REV, bool VAR>
 hipError_t launch_chain_np(const FwdShape& s, const ChainPlan& pl, const void* x, const void* B, const void* C,
                            const void* dt, const float* A, float* Acs, float* dtq, void* Hs, const float* init,
-                           float* fin, uint16_t* CB, uint16_t* CBt, const float* Hst, float* ghp, float* cdec,
-                           float* segdec, const VarWalk& vw, hipStream_t st, const StageEv& ev) {
+                           float* fin, uint16_t* CB, uint16_t* CBt, uint16_t* CF, const float* Hst, float* ghp,
+                           float* cdec, float* segdec, const VarWalk& vw, hipStream_t st, const StageEv& ev) {
   constexpr int CW = chain_cols(N, P, SPC, F32S || REV), NW = chain_waves(CW);
   // whole work-groups per row, and the heads of one in one B/C group
   if ((long(s.H) * P) % CW != 0 || (P < CW && (s.H / s.G) % (CW / P) != 0)) return hipErrorInvalidValue;
@@ -1034,16 +1052,17 @@ hipError_t launch_chain_np(const FwdShape& s, const ChainPlan& pl, const void* x
   // segmented: the tiles first, as a launch of their own (the stage's start
   // event on it, the stop event on the walk)
   if (segd && alltiles > 0) {
+    if (!CF) return hipErrorInvalidValue;
     const long rows = long(s.b) * s.nc * s.G;
     const int4* tab = pl.var ? vw.tab : nullptr;
     if (rows >= 2L * device_units()) {
       hipExtLaunchKernelGGL((chunk_scores_lds_kernel<N>), dim3(unsigned(rows)), dim3(512), 0, st, ev.start, nullptr,
                             0, static_cast<const uint16_t*>(B), static_cast<const uint16_t*>(C), CB, s.T, s.G, s.Q,
-                            s.nc, tab);
+                            s.nc, tab, CF);
     } else {
       hipExtLaunchKernelGGL((chunk_scores_tiles_kernel<N>), dim3(unsigned((alltiles + kChainWaves - 1) / kChainWaves)),
                             dim3(kChainThreads), 0, st, ev.start, nullptr, 0, static_cast<const uint16_t*>(B),
-                            static_cast<const uint16_t*>(C), CB, tab, s.T, s.G, s.Q, s.nc, alltiles);
+                            static_cast<const uint16_t*>(C), CB, tab, s.T, s.G, s.Q, s.nc, alltiles, CF);
     }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -1221,8 +1240,8 @@ bool chunk_state_chain_ok(const FwdShape& s) { return chunk_state_chain_plan(s, 
 template <bool F32S, bool REV>
 hipError_t launch_chain(const FwdShape& s, const ChainPlan& pl, const void* x, const void* B, const void* C,
                         const void* dt, const float* A, float* Acs, float* dtq, void* Hs, const float* init,
-                        float* fin, uint16_t* CB, uint16_t* CBt, const float* Hst, float* ghp, float* cdec,
-                        float* segdec, hipStream_t st, const StageEv& ev, const VarWalk& vw = VarWalk{}) {
+                        float* fin, uint16_t* CB, uint16_t* CBt, uint16_t* CF, const float* Hst, float* ghp,
+                        float* cdec, float* segdec, hipStream_t st, const StageEv& ev, const VarWalk& vw = VarWalk{}) {
   // every walk must own at least one chunk and the segments must cover the
   // row exactly: a walk without slices would clamp its copies to slice -1
   const bool ok = chain_plan_valid(s, pl) &&
@@ -1240,10 +1259,10 @@ hipError_t launch_chain(const FwdShape& s, const ChainPlan& pl, const void* x, c
       if constexpr (!F32S && !REV) {
         if (pl.var)
           return launch_chain_np<NP::n, NP::p, SPC_, ST_, false, false, true>(
-              s, pl, x, B, C, dt, A, Acs, dtq, Hs, init, fin, CB, CBt, Hst, ghp, cdec, segdec, vw, st, ev);
+              s, pl, x, B, C, dt, A, Acs, dtq, Hs, init, fin, CB, CBt, CF, Hst, ghp, cdec, segdec, vw, st, ev);
       }
       return launch_chain_np<NP::n, NP::p, SPC_, ST_, F32S, REV, false>(
-          s, pl, x, B, C, dt, A, Acs, dtq, Hs, init, fin, CB, CBt, Hst, ghp, cdec, segdec, vw, st, ev);
+          s, pl, x, B, C, dt, A, Acs, dtq, Hs, init, fin, CB, CBt, CF, Hst, ghp, cdec, segdec, vw, st, ev);
     };
     if (pl.two && NP::n == 128) {
       // two work-groups per unit (three slices resident; chunks of two or
@@ -1278,20 +1297,21 @@ hipError_t launch_chain(const FwdShape& s, const ChainPlan& pl, const void* x, c
 
 hipError_t launch_chunk_state_chain(const FwdShape& s, const ChainPlan& pl, const void* x, const void* B,
                                     const void* C, const void* dt, const float* A, float* Acs, float* dtq,
-                                    uint16_t* Hb, const float* init, float* fin, uint16_t* CB, float* cdec,
-                                    float* segdec, hipStream_t st, const StageEv& ev) {
+                                    uint16_t* Hb, const float* init, float* fin, uint16_t* CB, uint16_t* CF,
+                                    float* cdec, float* segdec, hipStream_t st, const StageEv& ev) {
   if (pl.var) return hipErrorInvalidValue;
-  return launch_chain<false, false>(s, pl, x, B, C, dt, A, Acs, dtq, Hb, init, fin, CB, nullptr, nullptr, nullptr,
-                                    cdec, segdec, st, ev);
+  return launch_chain<false, false>(s, pl, x, B, C, dt, A, Acs, dtq, Hb, init, fin, CB, nullptr, CF, nullptr,
+                                    nullptr, cdec, segdec, st, ev);
 }
 
 hipError_t launch_chunk_state_chain_varlen(const FwdShape& s, const ChainPlan& pl, const void* x, const void* B,
                                            const void* C, const void* dt, const float* A, float* Acs, float* dtq,
-                                           uint16_t* Hb, const float* init, float* segS, uint16_t* CB, float* cdec,
-                                           float* segdec, const VarWalk& vw, hipStream_t st, const StageEv& ev) {
+                                           uint16_t* Hb, const float* init, float* segS, uint16_t* CB,
+                                           uint16_t* CF, float* cdec, float* segdec, const VarWalk& vw,
+                                           hipStream_t st, const StageEv& ev) {
   if (!pl.var) return hipErrorInvalidValue;
-  return launch_chain<false, false>(s, pl, x, B, C, dt, A, Acs, dtq, Hb, init, segS, CB, nullptr, nullptr, nullptr,
-                                    cdec, segdec, st, ev, vw);
+  return launch_chain<false, false>(s, pl, x, B, C, dt, A, Acs, dtq, Hb, init, segS, CB, nullptr, CF, nullptr,
+                                    nullptr, cdec, segdec, st, ev, vw);
 }
 
 hipError_t launch_chunk_state_chain_bwd(const FwdShape& s, const void* x, const void* B, const void* C,
@@ -1299,7 +1319,7 @@ hipError_t launch_chunk_state_chain_bwd(const FwdShape& s, const void* x, const 
                                         const float* init, float* fin, uint16_t* CBf, uint16_t* CBt,
                                         hipStream_t st) {
   return launch_chain<true, false>(s, chunk_state_chain_plan(s, false), x, B, C, dt, A, Acs, dtq, Hst, init, fin,
-                                   CBf, CBt, nullptr, nullptr, nullptr, nullptr, st, StageEv{});
+                                   CBf, CBt, nullptr, nullptr, nullptr, nullptr, nullptr, st, StageEv{});
 }
 
 // The reverse walk holds a run of H_c per lane besides the accumulators, which
@@ -1314,7 +1334,8 @@ hipError_t launch_chunk_grad_chain_bwd(const FwdShape& s, const void* dy, const 
                                        const float* Hst, float* ghp, hipStream_t st) {
   if (!chunk_grad_chain_ok(s)) return hipErrorInvalidValue;
   return launch_chain<false, true>(s, chunk_state_chain_plan(s, false), dy, C, nullptr, dt, A, nullptr, nullptr, Gb,
-                                   dfinal, dinit, nullptr, nullptr, Hst, ghp, nullptr, nullptr, st, StageEv{});
+                                   dfinal, dinit, nullptr, nullptr, nullptr, Hst, ghp, nullptr, nullptr, st,
+                                   StageEv{});
 }
 
 hipError_t launch_chunk_state_mfma_bwd(const FwdShape& s, const void* x, const void* B, const void* C,

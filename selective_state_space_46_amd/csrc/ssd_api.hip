@@ -327,7 +327,8 @@ ssd_status ssd_chunk_scan_fwd_timed(const void* x, const void* dt, const float* 
       // k, with segment k's summed decay exponent as its "chunk" decay (a
       // chunk length of 1 over segdec), from zero (segment 0 started from
       // init_state itself)
-      if (launch_chunk_state_chain(s, pl, x, B, C, dt, A, Acs, dtq, Hb, init_state, S, CB, cdec, segdec, hs,
+      uint16_t* Cf = reinterpret_cast<uint16_t*>(ws + w.cf);
+      if (launch_chunk_state_chain(s, pl, x, B, C, dt, A, Acs, dtq, Hb, init_state, S, CB, Cf, cdec, segdec, hs,
                                    ev(1)) != hipSuccess)
         return SSD_ERR_HIP;
       FwdShape ss = s;
@@ -336,6 +337,7 @@ ssd_status ssd_chunk_scan_fwd_timed(const void* x, const void* dt, const float* 
       if (launch_state_passing(ss, S, nullptr, segdec, nullptr, final_state, hs, ev(2), true) != hipSuccess)
         return SSD_ERR_HIP;
       SegStates sg;
+      sg.Cf = Cf;
       sg.Hin = S;
       sg.cdec = cdec;
       sg.nseg = pl.nseg;
@@ -346,7 +348,7 @@ ssd_status ssd_chunk_scan_fwd_timed(const void* x, const void* dt, const float* 
     }
     // chunk states and state passing in one launch: stage 2 launches nothing
     if (launch_chunk_state_chain(s, pl, x, B, C, dt, A, Acs, dtq, Hb, init_state, final_state, CB, nullptr,
-                                 nullptr, hs, ev(1)) != hipSuccess)
+                                 nullptr, nullptr, hs, ev(1)) != hipSuccess)
       return SSD_ERR_HIP;
     const StageEv e2 = ev(2);
     if (e2.start && hipEventRecord(e2.start, hs) != hipSuccess) return SSD_ERR_HIP;
@@ -549,8 +551,9 @@ ssd_status ssd_chunk_scan_fwd_varlen(const void* x, const void* dt, const float*
     vw.F = reinterpret_cast<float*>(ws + v.F);
     vw.fdec = reinterpret_cast<float*>(ws + v.fdec);
     vw.fseq = reinterpret_cast<int*>(ws + v.fseq);
-    if (launch_chunk_state_chain_varlen(s, pl, x, B, C, dt, A, Acs, dtq, Hb, init_states, S, CB, cdec, segdec, vw,
-                                        hs) != hipSuccess)
+    uint16_t* Cf = reinterpret_cast<uint16_t*>(ws + w.cf);
+    if (launch_chunk_state_chain_varlen(s, pl, x, B, C, dt, A, Acs, dtq, Hb, init_states, S, CB, Cf, cdec, segdec,
+                                        vw, hs) != hipSuccess)
       return SSD_ERR_HIP;
     FwdShape ss = s;
     ss.nc = pl.nseg;
@@ -558,6 +561,7 @@ ssd_status ssd_chunk_scan_fwd_varlen(const void* x, const void* dt, const float*
                                          final_states, hs) != hipSuccess)
       return SSD_ERR_HIP;
     SegStates sg;
+    sg.Cf = Cf;
     sg.Hin = S;
     sg.cdec = cdec;
     sg.nseg = pl.nseg;

@@ -189,11 +189,14 @@ __host__ __device__ __forceinline__ size_t hb_off(int p, int n, int N) {
 //                            segments, the local ones)
 //   cb  [b, nc, G, ntile, 64, 16] bf16 C B^T tiles of each chunk (MFMA path
 //       only; ntile = lpc (lpc + 1) / 2 lower-triangle tiles, lpc = Q / 32)
+//   cf  [b, nc, G, Q / 32, N / 16, 64, 8] bf16 (segments only): C in the
+//       order chunk_scan's matrix-core operands take it (store_c_frags in
+//       chunk_state_mfma.hip), written by the tiles launch
 //   cdec [b, H, nc] f32, segdec [b, H, nseg] f32 (segments only): summed
 //       chunk decay exponents from the segment's start to each chunk, and over
 //       each segment
 struct WsLayout {
-  size_t acs, dtq, st, hb, cb, cdec, segdec, total;
+  size_t acs, dtq, st, hb, cb, cf, cdec, segdec, total;
 };
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -210,12 +213,13 @@ inline WsLayout ws_layout(const FwdShape& s, bool mfma, const ChainPlan& pl) {
   w.st = align_up(w.dtq + row, 256);
   w.hb = align_up(w.st + nstf * sizeof(float), 256);
   if (!mfma) {
-    w.cb = w.cdec = w.segdec = w.total = w.hb;
+    w.cb = w.cf = w.cdec = w.segdec = w.total = w.hb;
     return w;
   }
   w.cb = align_up(w.hb + nst * sizeof(uint16_t), 256);
   const size_t lpc = size_t(s.Q) / 32, ntile = lpc * (lpc + 1) / 2;
-  w.cdec = align_up(w.cb + size_t(s.b) * s.nc * s.G * ntile * 1024 * sizeof(uint16_t), 256);
+  w.cf = align_up(w.cb + size_t(s.b) * s.nc * s.G * ntile * 1024 * sizeof(uint16_t), 256);
+  w.cdec = align_up(w.cf + (seg ? size_t(s.b) * s.nc * s.G * s.Q * s.N * sizeof(uint16_t) : 0), 256);
   w.segdec = align_up(w.cdec + (seg ? size_t(s.b) * s.H * s.nc * sizeof(float) : 0), 256);
   w.total = align_up(w.segdec + (seg ? size_t(s.b) * s.H * pl.nseg * sizeof(float) : 0), 256);
   return w;
@@ -272,8 +276,8 @@ hipError_t launch_chunk_state_mfma(const FwdShape& s, const void* x, const void*
 bool chunk_state_chain_ok(const FwdShape& s);   // whole rows
 hipError_t launch_chunk_state_chain(const FwdShape& s, const ChainPlan& pl, const void* x, const void* B,
                                     const void* C, const void* dt, const float* A, float* Acs, float* dtq,
-                                    uint16_t* Hb, const float* init, float* fin, uint16_t* CB, float* cdec,
-                                    float* segdec, hipStream_t st, const StageEv& ev = StageEv{});
+                                    uint16_t* Hb, const float* init, float* fin, uint16_t* CB, uint16_t* CF,
+                                    float* cdec, float* segdec, hipStream_t st, const StageEv& ev = StageEv{});
 // Packed sequences (pl from varlen_chain_plan_for; s: batch 1, nc chunk
 // slots): the slot row cut into pl.nseg equal segments, one walk per
 // (segment, 64 columns), rows and sequence starts / ends from the chunk table.
@@ -298,9 +302,9 @@ struct VarWalk {
 };
 hipError_t launch_chunk_state_chain_varlen(const FwdShape& s, const ChainPlan& pl, const void* x, const void* B,
                                            const void* C, const void* dt, const float* A, float* Acs, float* dtq,
-                                           uint16_t* Hb, const float* init, float* segS, uint16_t* CB, float* cdec,
-                                           float* segdec, const VarWalk& vw, hipStream_t st,
-                                           const StageEv& ev = StageEv{});
+                                           uint16_t* Hb, const float* init, float* segS, uint16_t* CB,
+                                           uint16_t* CF, float* cdec, float* segdec, const VarWalk& vw,
+                                           hipStream_t st, const StageEv& ev = StageEv{});
 // The same for the backward's recomputation: the states entering each chunk
 // as fp32 in Hst ([b, c, h, p, n], what state_passing leaves over the chunk
 // states) and the C B^T tiles as fp32 in both orientations (CBf, CBt, as
@@ -358,6 +362,7 @@ hipError_t launch_chunk_scan(const FwdShape& s, ssd_dtype type, bool mfma, const
 // the chunk table; dstate 128 or 256), segments of seglen slots, cdec -inf
 // for the chunks that take no correction.
 struct SegStates {
+  const uint16_t* Cf = nullptr;   // C in fragment order (CF, written by the tiles launch)
   const float* Hin = nullptr;
   const float* cdec = nullptr;
   int nseg = 1, seglen = 0;
