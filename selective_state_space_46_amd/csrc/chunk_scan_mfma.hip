@@ -35,9 +35,10 @@
 // l), which makes every per-token factor one multiplier per lane:
 //   1. y^T = H_c^T C_l^T (k = dstate): H_c staged once in LDS as stored (bf16,
 //      fragment order, from the fused walk or state_passing, see hb_off) when
-//      the super-chunk is one chunk, C_l rows straight from memory (with
-//      segments: from the copy of C the tiles launch leaves in operand order,
-//      1 KB contiguous per load); then y^T *= exp(Acs_l).
+//      the super-chunk is one chunk, C_l rows from the copy of C that the
+//      tiles' producer leaves in operand order (1 KB contiguous per load;
+//      from C itself each load would read 32 bytes in each of 32 rows); then
+//      y^T *= exp(Acs_l).
 //   2. for each column block s <= l of the chunk: the C B^T tile (lane =
 //      column l, registers = rows s in runs of 4) times the decay, rounded to
 //      bf16, is the B operand of y^T += X^T G^T under a k permutation that the
@@ -46,9 +47,9 @@
 //      ds_read_b64_tr_b16. Tiles are loaded one tile ahead of use, into two
 //      buffers used in turn.
 //   3. + D x (x from the same LDS tile), bf16 rounding, 8-byte stores of 4
-//      consecutive p; with W = 8 the rounded rows go back through the x tile
-//      (after a barrier: no wave reads x any more) and leave as 16-byte pieces
-//      of whole token rows.
+//      consecutive p; where the super-chunk is one chunk the rounded rows go
+//      back through the x tile (after a barrier: no wave reads x any more) and
+//      leave as 16-byte pieces of whole token rows.
 // SEG (rows cut into segments by the fused chunk-state walk): Hb holds the
 // local states, from zero at each segment's start; the state entering chunk
 // c of segment k >= 1 is Hb_c + exp(cdec_c) Hin_k (Hin fp32 [b, nseg, H,
@@ -84,11 +85,11 @@ __device__ __forceinline__ u32x4 seg_combine(const u32x4& v, const float* hin, f
 template <int N, int P, bool HLDS, bool VARLEN, bool SEG, int W>
 __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(W == 8 && P <= 64 ? 4 : 1)))
 void chunk_scan_mfma_kernel(
-    const uint16_t* __restrict__ x, const uint16_t* __restrict__ CB, const uint16_t* __restrict__ Cm,
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ CB, const uint16_t* __restrict__ Cf,
     const float* __restrict__ Acs, const float* __restrict__ dtq, const uint16_t* __restrict__ Hb,
     const float* __restrict__ D, uint16_t* __restrict__ y, const int4* __restrict__ tab, int T, int H,
     int G, int Q, int nc, int nsc, const float* __restrict__ Hin, const float* __restrict__ cdec, int nseg,
-    int seglen, const uint16_t* __restrict__ Cf) {
+    int seglen) {
   constexpr int kThreads = 64 * W;
   constexpr int NB = 8 / W;   // 32-row blocks per wave
   constexpr int RBX = P / 8;  // 16-byte chunks per X' row
@@ -153,20 +154,11 @@ void chunk_scan_mfma_kernel(
     td[1] = ts[ir * 128 + 1];
     tn[0] = ts[0];
     tn[1] = ts[1];
-    if constexpr (SEG) {
-      // C in operand order from the tiles launch (Cf, zeros past the chunk's
-      // tokens): each load is 1 KB contiguous per wave
-      const uint16_t* cr =
-          Cf + ((((size_t(b) * nc + c0 + i / lpc) * G + g) * lpc + i % lpc) * (N / 16) * 64 + lane) * 8;
+    // C in operand order, written with the tiles (Cf, zeros past the
+    // chunk's tokens): each load is 1 KB contiguous per wave
+    const uint16_t* cr = Cf + ((((size_t(b) * nc + c0 + i / lpc) * G + g) * lpc + i % lpc) * (N / 16) * 64 + lane) * 8;
 #pragma unroll
-      for (int ks = 0; ks < N / 16; ++ks) cfv[ks] = load16(cr + 512 * ks);
-    } else {
-      const ChunkRows r = crows(i / lpc);
-      const long row = r.r0 + min((i % lpc) * 32 + l32, r.n - 1);
-      const uint16_t* cr = Cm + (row * G + g) * size_t(N) + 8 * g2;
-#pragma unroll
-      for (int ks = 0; ks < N / 16; ++ks) cfv[ks] = load16(cr + 16 * ks);
-    }
+    for (int ks = 0; ks < N / 16; ++ks) cfv[ks] = load16(cr + 512 * ks);
   };
   // the wave's first block: with W = 8 (one block each) waves w and w + 4
   // share a SIMD, so wave w >= 4 takes block 11 - w: every SIMD then holds
@@ -257,15 +249,16 @@ void chunk_scan_mfma_kernel(
   }
 
   const float Dh = D ? D[h] : 0.f;
-  // YLDS (one block per wave): the rounded outputs wait in registers until
-  // every wave has finished its tiles, then go through this wave's own rows of
-  // the x tile (no wave reads x any more) so that each store instruction
-  // writes whole 16-byte pieces of consecutive token rows; stored straight
-  // from the accumulators, each instruction would write 16 bytes in each of
-  // 32 token rows.
-  constexpr bool YLDS = W == 8;
-  u32x2 yv[P / 32][4];
-  int yblk = -1;                   // the block whose outputs yv holds (uniform), -1: none
+  // YLDS (one chunk per super-chunk): the rounded outputs of the wave's
+  // blocks wait in registers (yv[1] the last block's, yv[0] the first's when
+  // a wave has two) until every wave has finished its tiles, then go through
+  // this wave's own rows of the x tile (no wave reads x any more) so that
+  // each store instruction writes whole 16-byte pieces of consecutive token
+  // rows; stored straight from the accumulators, each instruction would
+  // write 16 bytes in each of 32 token rows.
+  constexpr bool YLDS = HLDS;
+  u32x2 yv[2][P / 32][4];
+  int yblk[2] = {-1, -1};          // the blocks whose outputs yv holds (uniform), -1: none
   for (int which = 0; which < NB; ++which) {
     const int i = which ? 7 - wave : blk0;  // 32-row block of the super-chunk
     const ChunkRows cr = crows(i / lpc);
@@ -425,7 +418,7 @@ void chunk_scan_mfma_kernel(
     // ---- epilogue: + D x (x from the LDS tile), round; store 4 consecutive p
     // (8 bytes) per run, or keep them for the row-wise store below
     if constexpr (YLDS) {
-      yblk = i;
+      u32x2 cur[P / 32][4];
 #pragma unroll
       for (int pb = 0; pb < P / 32; ++pb)
 #pragma unroll
@@ -435,8 +428,22 @@ void chunk_scan_mfma_kernel(
           float o[4];
 #pragma unroll
           for (int rr = 0; rr < 4; ++rr) o[rr] = acc[pb][4 * q + rr] + Dh * xs[rr];
-          yv[pb][q] = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+          cur[pb][q] = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
         }
+      // slot 0: a first block of two (uniform branch)
+      if (NB == 2 && which == 0) {
+        yblk[0] = i;
+#pragma unroll
+        for (int pb = 0; pb < P / 32; ++pb)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) yv[0][pb][q] = cur[pb][q];
+      } else {
+        yblk[1] = i;
+#pragma unroll
+        for (int pb = 0; pb < P / 32; ++pb)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) yv[1][pb][q] = cur[pb][q];
+      }
     } else if (tok_ok) {
       u32x2 xr[P / 32][4];
 #pragma unroll
@@ -466,15 +473,17 @@ void chunk_scan_mfma_kernel(
     // reads came from, and reads them back as 16-byte row pieces (RBX lanes
     // per row, 64 / RBX rows per instruction) for the stores
     __syncthreads();
-    if (yblk >= 0) {
-      const int i = yblk;
+#pragma unroll
+    for (int sl = 2 - NB; sl < 2; ++sl) {
+      if (yblk[sl] < 0) continue;       // uniform
+      const int i = yblk[sl];
       const ChunkRows cr = crows(i / lpc);
       const int rq0 = (i % lpc) * 32;
 #pragma unroll
       for (int pb = 0; pb < P / 32; ++pb)
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-          *reinterpret_cast<u32x2*>(&sX[lds_off<RBX, true>(32 * i + l32, 32 * pb + 8 * q + 4 * g2)]) = yv[pb][q];
+          *reinterpret_cast<u32x2*>(&sX[lds_off<RBX, true>(32 * i + l32, 32 * pb + 8 * q + 4 * g2)]) = yv[sl][pb][q];
       constexpr int RPI = 64 / RBX;     // rows per store instruction
       const int cc = lane % RBX;
 #pragma unroll
@@ -489,7 +498,7 @@ void chunk_scan_mfma_kernel(
 }
 
 template <int N, int P>
-hipError_t launch_np(const FwdShape& s, const void* x, const uint16_t* CB, const void* C,
+hipError_t launch_np(const FwdShape& s, const void* x, const uint16_t* CB, const uint16_t* Cf,
                      const float* Acs, const float* dtq, const uint16_t* Hb, const float* D, void* y,
                      const int4* tab, hipStream_t st, const StageEv& ev, const SegStates& sg) {
   const int cps = kSC / s.Q;
@@ -501,12 +510,12 @@ hipError_t launch_np(const FwdShape& s, const void* x, const uint16_t* CB, const
   constexpr int W = N == 256 ? 8 : 4;
   auto go = [&](auto kern, int w) {
     hipExtLaunchKernelGGL(kern, dim3(unsigned(blocks)), dim3(64 * w), 0, st, ev.start, ev.stop, 0,
-                          static_cast<const uint16_t*>(x), CB, static_cast<const uint16_t*>(C), Acs, dtq, Hb, D,
+                          static_cast<const uint16_t*>(x), CB, Cf, Acs, dtq, Hb, D,
                           static_cast<uint16_t*>(y), tab, s.T, s.H, s.G, s.Q, s.nc, nsc, sg.Hin, sg.cdec, sg.nseg,
-                          sg.seglen, sg.Cf);
+                          sg.seglen);
   };
   const bool seg = sg.nseg > 1 || sg.var;
-  if (seg && (!sg.Hin || !sg.cdec || !sg.Cf || sg.seglen < 1 || sg.var != (tab != nullptr)))
+  if (!Cf || (seg && (!sg.Hin || !sg.cdec || sg.seglen < 1 || sg.var != (tab != nullptr))))
     return hipErrorInvalidValue;
   // packed sequences through segments: only where the fused walk runs
   if constexpr (N >= 128) {
@@ -532,13 +541,13 @@ hipError_t launch_np(const FwdShape& s, const void* x, const uint16_t* CB, const
 }
 
 template <int N>
-hipError_t launch_n(const FwdShape& s, const void* x, const uint16_t* CB, const void* C,
+hipError_t launch_n(const FwdShape& s, const void* x, const uint16_t* CB, const uint16_t* Cf,
                     const float* Acs, const float* dtq, const uint16_t* Hb, const float* D, void* y,
                     const int4* tab, hipStream_t st, const StageEv& ev, const SegStates& sg) {
   switch (s.P) {
-    case 32: return launch_np<N, 32>(s, x, CB, C, Acs, dtq, Hb, D, y, tab, st, ev, sg);
-    case 64: return launch_np<N, 64>(s, x, CB, C, Acs, dtq, Hb, D, y, tab, st, ev, sg);
-    case 128: return launch_np<N, 128>(s, x, CB, C, Acs, dtq, Hb, D, y, tab, st, ev, sg);
+    case 32: return launch_np<N, 32>(s, x, CB, Cf, Acs, dtq, Hb, D, y, tab, st, ev, sg);
+    case 64: return launch_np<N, 64>(s, x, CB, Cf, Acs, dtq, Hb, D, y, tab, st, ev, sg);
+    case 128: return launch_np<N, 128>(s, x, CB, Cf, Acs, dtq, Hb, D, y, tab, st, ev, sg);
   }
   return hipErrorInvalidValue;
 }
@@ -546,14 +555,14 @@ hipError_t launch_n(const FwdShape& s, const void* x, const uint16_t* CB, const 
 }  // namespace
 
 hipError_t launch_chunk_scan_mfma(const FwdShape& s, const void* x, const uint16_t* CB,
-                                  const void* C, const float* Acs, const float* dtq,
+                                  const uint16_t* Cf, const float* Acs, const float* dtq,
                                   const uint16_t* Hb, const float* D, void* y, const int4* tab,
                                   hipStream_t st, const StageEv& ev, const SegStates& sg) {
   switch (s.N) {
-    case 32: return launch_n<32>(s, x, CB, C, Acs, dtq, Hb, D, y, tab, st, ev, sg);
-    case 64: return launch_n<64>(s, x, CB, C, Acs, dtq, Hb, D, y, tab, st, ev, sg);
-    case 128: return launch_n<128>(s, x, CB, C, Acs, dtq, Hb, D, y, tab, st, ev, sg);
-    case 256: return launch_n<256>(s, x, CB, C, Acs, dtq, Hb, D, y, tab, st, ev, sg);
+    case 32: return launch_n<32>(s, x, CB, Cf, Acs, dtq, Hb, D, y, tab, st, ev, sg);
+    case 64: return launch_n<64>(s, x, CB, Cf, Acs, dtq, Hb, D, y, tab, st, ev, sg);
+    case 128: return launch_n<128>(s, x, CB, Cf, Acs, dtq, Hb, D, y, tab, st, ev, sg);
+    case 256: return launch_n<256>(s, x, CB, Cf, Acs, dtq, Hb, D, y, tab, st, ev, sg);
   }
   return hipErrorInvalidValue;
 }

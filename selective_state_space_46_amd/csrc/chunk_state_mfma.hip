@@ -152,11 +152,14 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ Bm, const uint16_t* __restrict__ dt,
     const float* __restrict__ A, float* __restrict__ Acs, float* __restrict__ dtq, float* __restrict__ S,
     const uint16_t* __restrict__ Cm, uint16_t* __restrict__ CB, uint16_t* __restrict__ CBt,
-    const int4* __restrict__ tab, int T, int H, int G, int Q, int nc, int nscore_wg, long ntiles) {
-  // the first nscore_wg work-groups compute C B^T tiles, one per wave
+    const int4* __restrict__ tab, int T, int H, int G, int Q, int nc, int nscore_wg, long ntiles,
+    uint16_t* __restrict__ CF) {
+  // the first nscore_wg work-groups compute C B^T tiles, one per wave (and
+  // with CF, C in chunk_scan's operand order)
   if (int(blockIdx.x) < nscore_wg) {
     const long wid = long(blockIdx.x) * kWaves + (threadIdx.x >> 6);
-    if (wid < ntiles) chunk_scores_tile<N, MODE == 1>(Bm, Cm, CB, CBt, tab, T, G, Q, nc, wid, threadIdx.x & 63);
+    if (wid < ntiles)
+      chunk_scores_tile<N, MODE == 1>(Bm, Cm, CB, CBt, tab, T, G, Q, nc, wid, threadIdx.x & 63, CF);
     return;                                     // no barrier on this path
   }
   constexpr int RBB = N / 8, RBW = P / 8;            // 16-byte chunks per row
@@ -427,7 +430,7 @@ void chunk_state_chain_kernel(
     const float* __restrict__ init, float* __restrict__ fin, const uint16_t* __restrict__ Cm,
     uint16_t* __restrict__ CB, uint16_t* __restrict__ CBt, const float* __restrict__ Hst, float* __restrict__ ghp,
     float* __restrict__ cdec, float* __restrict__ segdec, int T, int H, int G, int Q, int nc, int nb, int nseg,
-    int seglen, int nchain, long ntiles, VarWalk vw) {
+    int seglen, int nchain, long ntiles, VarWalk vw, uint16_t* __restrict__ CF) {
   constexpr int CW = chain_cols(N, P, SPC, F32S || REV);   // columns per work-group
   constexpr int NCOLB = CW / 32;                // 32-column blocks
   constexpr int NCWV = 2 * NCOLB;               // compute waves; the table wave is wave NCWV
@@ -441,7 +444,7 @@ void chunk_state_chain_kernel(
   // work-groups past the chains compute C B^T tiles, one per wave
   if (int(blockIdx.x) >= nchain) {
     const long wid = long(int(blockIdx.x) - nchain) * NW + wave;
-    if (wid < ntiles) chunk_scores_tile<N, F32S>(Bm, Cm, CB, CBt, nullptr, T, G, Q, nc, wid, lane);
+    if (wid < ntiles) chunk_scores_tile<N, F32S>(Bm, Cm, CB, CBt, nullptr, T, G, Q, nc, wid, lane, CF);
     return;                                     // no barrier on this path
   }
   __shared__ __attribute__((aligned(16))) uint16_t sB[S][kChainSK * N];
@@ -1051,8 +1054,8 @@ hipError_t launch_chain_np(const FwdShape& s, const ChainPlan& pl, const void* x
   const bool segd = pl.nseg > 1 || pl.var;
   // segmented: the tiles first, as a launch of their own (the stage's start
   // event on it, the stop event on the walk)
+  if (alltiles > 0 && !F32S && !CF) return hipErrorInvalidValue;   // the forward's tiles also write C in operand order
   if (segd && alltiles > 0) {
-    if (!CF) return hipErrorInvalidValue;
     const long rows = long(s.b) * s.nc * s.G;
     const int4* tab = pl.var ? vw.tab : nullptr;
     if (rows >= 2L * device_units()) {
@@ -1075,14 +1078,14 @@ hipError_t launch_chain_np(const FwdShape& s, const ChainPlan& pl, const void* x
                         static_cast<const uint16_t*>(B), static_cast<const uint16_t*>(dt), A, Acs, dtq, Hs, init, fin,
                         static_cast<const uint16_t*>(C), CB, CBt, Hst, ghp, segd ? cdec : nullptr,
                         segd ? segdec : nullptr, s.T, s.H, s.G, s.Q, s.nc, s.b, pl.nseg, pl.seglen, int(nchain),
-                        ntiles, VAR ? vw : VarWalk{});
+                        ntiles, VAR ? vw : VarWalk{}, segd ? nullptr : CF);
   return hipGetLastError();
 }
 
 template <int N, int P, int MODE>
 hipError_t launch_np(const FwdShape& s, const void* x, const void* B, const void* C, const void* dt,
-                     const float* A, float* Acs, float* dtq, float* S, uint16_t* CB, uint16_t* CBt, const int4* tab,
-                     hipStream_t st, const StageEv& ev) {
+                     const float* A, float* Acs, float* dtq, float* S, uint16_t* CB, uint16_t* CBt, uint16_t* CF,
+                     const int4* tab, hipStream_t st, const StageEv& ev) {
   const int lpc = s.Q / 32;
   const long ntiles = MODE == 2 ? 0 : long(s.b) * s.nc * s.G * (lpc * (lpc + 1) / 2);
   // score work-groups first (they start with the first wave of work-groups),
@@ -1092,18 +1095,18 @@ hipError_t launch_np(const FwdShape& s, const void* x, const void* B, const void
   hipExtLaunchKernelGGL((chunk_state_mfma_kernel<N, P, MODE>), dim3(unsigned(blocks)), dim3(kThreads), 0, st,
                         ev.start, ev.stop, 0, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(B),
                         static_cast<const uint16_t*>(dt), A, Acs, dtq, S, static_cast<const uint16_t*>(C), CB,
-                        CBt, tab, s.T, s.H, s.G, s.Q, s.nc, int(nscore), ntiles);
+                        CBt, tab, s.T, s.H, s.G, s.Q, s.nc, int(nscore), ntiles, CF);
   return hipGetLastError();
 }
 
 template <int N, int MODE>
 hipError_t launch_n(const FwdShape& s, const void* x, const void* B, const void* C, const void* dt,
-                    const float* A, float* Acs, float* dtq, float* S, uint16_t* CB, uint16_t* CBt, const int4* tab,
-                    hipStream_t st, const StageEv& ev) {
+                    const float* A, float* Acs, float* dtq, float* S, uint16_t* CB, uint16_t* CBt, uint16_t* CF,
+                    const int4* tab, hipStream_t st, const StageEv& ev) {
   switch (s.P) {
-    case 32: return launch_np<N, 32, MODE>(s, x, B, C, dt, A, Acs, dtq, S, CB, CBt, tab, st, ev);
-    case 64: return launch_np<N, 64, MODE>(s, x, B, C, dt, A, Acs, dtq, S, CB, CBt, tab, st, ev);
-    case 128: return launch_np<N, 128, MODE>(s, x, B, C, dt, A, Acs, dtq, S, CB, CBt, tab, st, ev);
+    case 32: return launch_np<N, 32, MODE>(s, x, B, C, dt, A, Acs, dtq, S, CB, CBt, CF, tab, st, ev);
+    case 64: return launch_np<N, 64, MODE>(s, x, B, C, dt, A, Acs, dtq, S, CB, CBt, CF, tab, st, ev);
+    case 128: return launch_np<N, 128, MODE>(s, x, B, C, dt, A, Acs, dtq, S, CB, CBt, CF, tab, st, ev);
   }
   return hipErrorInvalidValue;
 }
@@ -1111,12 +1114,12 @@ hipError_t launch_n(const FwdShape& s, const void* x, const void* B, const void*
 template <int MODE>
 hipError_t launch_mode(const FwdShape& s, const void* x, const void* B, const void* C, const void* dt,
                        const float* A, float* Acs, float* dtq, float* S, uint16_t* CB, uint16_t* CBt,
-                       const int4* tab, hipStream_t st, const StageEv& ev) {
+                       uint16_t* CF, const int4* tab, hipStream_t st, const StageEv& ev) {
   switch (s.N) {
-    case 32: return launch_n<32, MODE>(s, x, B, C, dt, A, Acs, dtq, S, CB, CBt, tab, st, ev);
-    case 64: return launch_n<64, MODE>(s, x, B, C, dt, A, Acs, dtq, S, CB, CBt, tab, st, ev);
-    case 128: return launch_n<128, MODE>(s, x, B, C, dt, A, Acs, dtq, S, CB, CBt, tab, st, ev);
-    case 256: return launch_n<256, MODE>(s, x, B, C, dt, A, Acs, dtq, S, CB, CBt, tab, st, ev);
+    case 32: return launch_n<32, MODE>(s, x, B, C, dt, A, Acs, dtq, S, CB, CBt, CF, tab, st, ev);
+    case 64: return launch_n<64, MODE>(s, x, B, C, dt, A, Acs, dtq, S, CB, CBt, CF, tab, st, ev);
+    case 128: return launch_n<128, MODE>(s, x, B, C, dt, A, Acs, dtq, S, CB, CBt, CF, tab, st, ev);
+    case 256: return launch_n<256, MODE>(s, x, B, C, dt, A, Acs, dtq, S, CB, CBt, CF, tab, st, ev);
   }
   return hipErrorInvalidValue;
 }
@@ -1125,9 +1128,10 @@ hipError_t launch_mode(const FwdShape& s, const void* x, const void* B, const vo
 
 hipError_t launch_chunk_state_mfma(const FwdShape& s, const void* x, const void* B, const void* C,
                                    const void* dt, const float* A, float* Acs, float* dtq,
-                                   float* S, uint16_t* CB, const int4* tab, hipStream_t st,
+                                   float* S, uint16_t* CB, uint16_t* CF, const int4* tab, hipStream_t st,
                                    const StageEv& ev) {
-  return launch_mode<0>(s, x, B, C, dt, A, Acs, dtq, S, CB, nullptr, tab, st, ev);
+  if (!CF) return hipErrorInvalidValue;
+  return launch_mode<0>(s, x, B, C, dt, A, Acs, dtq, S, CB, nullptr, CF, tab, st, ev);
 }
 
 template <int N_, int P_>
@@ -1341,12 +1345,13 @@ hipError_t launch_chunk_grad_chain_bwd(const FwdShape& s, const void* dy, const 
 hipError_t launch_chunk_state_mfma_bwd(const FwdShape& s, const void* x, const void* B, const void* C,
                                        const void* dt, const float* A, float* Acs, float* dtq, float* S,
                                        uint16_t* CB, uint16_t* CBt, hipStream_t st) {
-  return launch_mode<1>(s, x, B, C, dt, A, Acs, dtq, S, CB, CBt, nullptr, st, StageEv{});
+  return launch_mode<1>(s, x, B, C, dt, A, Acs, dtq, S, CB, CBt, nullptr, nullptr, st, StageEv{});
 }
 
 hipError_t launch_chunk_dstates_mfma(const FwdShape& s, const void* dy, const void* C, const void* dt,
                                      const float* A, float* dS, hipStream_t st) {
-  return launch_mode<2>(s, dy, C, nullptr, dt, A, nullptr, nullptr, dS, nullptr, nullptr, nullptr, st, StageEv{});
+  return launch_mode<2>(s, dy, C, nullptr, dt, A, nullptr, nullptr, dS, nullptr, nullptr, nullptr, nullptr, st,
+                        StageEv{});
 }
 
 }  // namespace ssd

@@ -298,6 +298,7 @@ ssd_status ssd_chunk_scan_fwd_timed(const void* x, const void* dt, const float* 
   uint16_t* CB = mfma ? reinterpret_cast<uint16_t*>(ws + w.cb) : nullptr;
   float* cdec = reinterpret_cast<float*>(ws + w.cdec);
   float* segdec = reinterpret_cast<float*>(ws + w.segdec);
+  uint16_t* Cf = mfma ? reinterpret_cast<uint16_t*>(ws + w.cf) : nullptr;
 
   // stage i's events: stage_events[2 i] (start), stage_events[2 i + 1] (stop),
   // recorded by the kernel's own dispatch
@@ -327,7 +328,6 @@ ssd_status ssd_chunk_scan_fwd_timed(const void* x, const void* dt, const float* 
       // k, with segment k's summed decay exponent as its "chunk" decay (a
       // chunk length of 1 over segdec), from zero (segment 0 started from
       // init_state itself)
-      uint16_t* Cf = reinterpret_cast<uint16_t*>(ws + w.cf);
       if (launch_chunk_state_chain(s, pl, x, B, C, dt, A, Acs, dtq, Hb, init_state, S, CB, Cf, cdec, segdec, hs,
                                    ev(1)) != hipSuccess)
         return SSD_ERR_HIP;
@@ -337,30 +337,29 @@ ssd_status ssd_chunk_scan_fwd_timed(const void* x, const void* dt, const float* 
       if (launch_state_passing(ss, S, nullptr, segdec, nullptr, final_state, hs, ev(2), true) != hipSuccess)
         return SSD_ERR_HIP;
       SegStates sg;
-      sg.Cf = Cf;
       sg.Hin = S;
       sg.cdec = cdec;
       sg.nseg = pl.nseg;
       sg.seglen = pl.seglen;
-      if (launch_chunk_scan_mfma(s, x, CB, C, Acs, dtq, Hb, D, y, nullptr, hs, ev(3), sg) != hipSuccess)
+      if (launch_chunk_scan_mfma(s, x, CB, Cf, Acs, dtq, Hb, D, y, nullptr, hs, ev(3), sg) != hipSuccess)
         return SSD_ERR_HIP;
       return launched(hs);
     }
     // chunk states and state passing in one launch: stage 2 launches nothing
-    if (launch_chunk_state_chain(s, pl, x, B, C, dt, A, Acs, dtq, Hb, init_state, final_state, CB, nullptr,
-                                 nullptr, nullptr, hs, ev(1)) != hipSuccess)
+    if (launch_chunk_state_chain(s, pl, x, B, C, dt, A, Acs, dtq, Hb, init_state, final_state, CB, Cf, nullptr,
+                                 nullptr, hs, ev(1)) != hipSuccess)
       return SSD_ERR_HIP;
     const StageEv e2 = ev(2);
     if (e2.start && hipEventRecord(e2.start, hs) != hipSuccess) return SSD_ERR_HIP;
     if (e2.stop && hipEventRecord(e2.stop, hs) != hipSuccess) return SSD_ERR_HIP;
   } else {
-    const hipError_t se = mfma ? launch_chunk_state_mfma(s, x, B, C, dt, A, Acs, dtq, S, CB, nullptr, hs, ev(1))
+    const hipError_t se = mfma ? launch_chunk_state_mfma(s, x, B, C, dt, A, Acs, dtq, S, CB, Cf, nullptr, hs, ev(1))
                                : launch_chunk_state(s, dtype, x, B, Acs, dtq, S, hs, ev(1));
     if (se != hipSuccess) return SSD_ERR_HIP;
     if (launch_state_passing(s, S, Hb, Acs, init_state, final_state, hs, ev(2)) != hipSuccess)
       return SSD_ERR_HIP;
   }
-  if (launch_chunk_scan(s, dtype, mfma, x, B, C, Acs, dtq, S, Hb, CB, D, y, hs, ev(3)) != hipSuccess)
+  if (launch_chunk_scan(s, dtype, mfma, x, B, C, Acs, dtq, S, Hb, CB, Cf, D, y, hs, ev(3)) != hipSuccess)
     return SSD_ERR_HIP;
   return launched(hs);
 }
@@ -531,6 +530,7 @@ ssd_status ssd_chunk_scan_fwd_varlen(const void* x, const void* dt, const float*
   float* S = reinterpret_cast<float*>(ws + w.st);
   uint16_t* Hb = reinterpret_cast<uint16_t*>(ws + w.hb);
   uint16_t* CB = reinterpret_cast<uint16_t*>(ws + w.cb);
+  uint16_t* Cf = reinterpret_cast<uint16_t*>(ws + w.cf);
   int4* tab = reinterpret_cast<int4*>(ws + v.tab);
   if (launch_varlen_table(cu_seqlens, nseq, total_tokens, chunk_len, tab, hs) != hipSuccess) return SSD_ERR_HIP;
   if (pl.ok) {
@@ -551,7 +551,6 @@ ssd_status ssd_chunk_scan_fwd_varlen(const void* x, const void* dt, const float*
     vw.F = reinterpret_cast<float*>(ws + v.F);
     vw.fdec = reinterpret_cast<float*>(ws + v.fdec);
     vw.fseq = reinterpret_cast<int*>(ws + v.fseq);
-    uint16_t* Cf = reinterpret_cast<uint16_t*>(ws + w.cf);
     if (launch_chunk_state_chain_varlen(s, pl, x, B, C, dt, A, Acs, dtq, Hb, init_states, S, CB, Cf, cdec, segdec,
                                         vw, hs) != hipSuccess)
       return SSD_ERR_HIP;
@@ -561,13 +560,12 @@ ssd_status ssd_chunk_scan_fwd_varlen(const void* x, const void* dt, const float*
                                          final_states, hs) != hipSuccess)
       return SSD_ERR_HIP;
     SegStates sg;
-    sg.Cf = Cf;
     sg.Hin = S;
     sg.cdec = cdec;
     sg.nseg = pl.nseg;
     sg.seglen = pl.seglen;
     sg.var = true;
-    if (launch_chunk_scan_mfma(s, x, CB, C, Acs, dtq, Hb, D, y, tab, hs, StageEv{}, sg) != hipSuccess)
+    if (launch_chunk_scan_mfma(s, x, CB, Cf, Acs, dtq, Hb, D, y, tab, hs, StageEv{}, sg) != hipSuccess)
       return SSD_ERR_HIP;
     return launched(hs);
   }
@@ -575,10 +573,10 @@ ssd_status ssd_chunk_scan_fwd_varlen(const void* x, const void* dt, const float*
   // state_passing reads each sequence's initial state (whole tile, into
   // LDS) before it writes that sequence's final state, so final_states may
   // be init_states.
-  if (launch_chunk_state_mfma(s, x, B, C, dt, A, Acs, dtq, S, CB, tab, hs) != hipSuccess) return SSD_ERR_HIP;
+  if (launch_chunk_state_mfma(s, x, B, C, dt, A, Acs, dtq, S, CB, Cf, tab, hs) != hipSuccess) return SSD_ERR_HIP;
   if (launch_state_passing_varlen(s, S, Hb, Acs, cu_seqlens, nseq, init_states, final_states, hs) != hipSuccess)
     return SSD_ERR_HIP;
-  if (launch_chunk_scan_mfma(s, x, CB, C, Acs, dtq, Hb, D, y, tab, hs) != hipSuccess) return SSD_ERR_HIP;
+  if (launch_chunk_scan_mfma(s, x, CB, Cf, Acs, dtq, Hb, D, y, tab, hs) != hipSuccess) return SSD_ERR_HIP;
   return launched(hs);
 }
 

@@ -189,9 +189,9 @@ __host__ __device__ __forceinline__ size_t hb_off(int p, int n, int N) {
 //                            segments, the local ones)
 //   cb  [b, nc, G, ntile, 64, 16] bf16 C B^T tiles of each chunk (MFMA path
 //       only; ntile = lpc (lpc + 1) / 2 lower-triangle tiles, lpc = Q / 32)
-//   cf  [b, nc, G, Q / 32, N / 16, 64, 8] bf16 (segments only): C in the
+//   cf  [b, nc, G, Q / 32, N / 16, 64, 8] bf16 (MFMA path only): C in the
 //       order chunk_scan's matrix-core operands take it (store_c_frags in
-//       chunk_state_mfma.hip), written by the tiles launch
+//       chunk_state_mfma.hip), written with the C B^T tiles
 //   cdec [b, H, nc] f32, segdec [b, H, nseg] f32 (segments only): summed
 //       chunk decay exponents from the segment's start to each chunk, and over
 //       each segment
@@ -219,7 +219,7 @@ inline WsLayout ws_layout(const FwdShape& s, bool mfma, const ChainPlan& pl) {
   w.cb = align_up(w.hb + nst * sizeof(uint16_t), 256);
   const size_t lpc = size_t(s.Q) / 32, ntile = lpc * (lpc + 1) / 2;
   w.cf = align_up(w.cb + size_t(s.b) * s.nc * s.G * ntile * 1024 * sizeof(uint16_t), 256);
-  w.cdec = align_up(w.cf + (seg ? size_t(s.b) * s.nc * s.G * s.Q * s.N * sizeof(uint16_t) : 0), 256);
+  w.cdec = align_up(w.cf + size_t(s.b) * s.nc * s.G * s.Q * s.N * sizeof(uint16_t), 256);
   w.segdec = align_up(w.cdec + (seg ? size_t(s.b) * s.H * s.nc * sizeof(float) : 0), 256);
   w.total = align_up(w.segdec + (seg ? size_t(s.b) * s.H * pl.nseg * sizeof(float) : 0), 256);
   return w;
@@ -258,11 +258,12 @@ hipError_t launch_chunk_state(const FwdShape& s, ssd_dtype type, const void* x, 
                               const float* Acs, const float* dtq, float* S, hipStream_t st, const StageEv& ev = StageEv{});
 // Matrix-core path: S^T [b, nc, H, P, N] f32; the same launch also computes
 // the in-chunk cumulative sums (written to Acs / dtq) and the C B^T tiles
-// (CB [b, nc, G, ntile, 64, 16] bf16) for the kernels after it.
+// (CB [b, nc, G, ntile, 64, 16] bf16) with C in chunk_scan's operand order
+// (CF, the workspace's cf region) for the kernels after it.
 // tab: the chunk table of packed variable-length sequences, or nullptr.
 hipError_t launch_chunk_state_mfma(const FwdShape& s, const void* x, const void* B, const void* C,
                                    const void* dt, const float* A, float* Acs, float* dtq,
-                                   float* S, uint16_t* CB, const int4* tab, hipStream_t st,
+                                   float* S, uint16_t* CB, uint16_t* CF, const int4* tab, hipStream_t st,
                                    const StageEv& ev = StageEv{});
 
 // Chunk states and state passing fused (equal-length rows, bf16 MFMA path):
@@ -350,11 +351,11 @@ hipError_t launch_varlen_segment_recurrence(const FwdShape& s, float* S, const f
                                             const float* init, float* final_state, hipStream_t st,
                                             const StageEv& ev = StageEv{});
 
-// Generic path reads Hst (fp32, [b, nc, H, P, N]); MFMA path reads Hb (bf16)
-// and the C B^T tiles CB.
+// Generic path reads Hst (fp32, [b, nc, H, P, N]) and C; MFMA path reads Hb
+// (bf16), the C B^T tiles CB and C in operand order (Cf).
 hipError_t launch_chunk_scan(const FwdShape& s, ssd_dtype type, bool mfma, const void* x,
                              const void* B, const void* C, const float* Acs, const float* dtq,
-                             const float* Hst, const uint16_t* Hb, const uint16_t* CB,
+                             const float* Hst, const uint16_t* Hb, const uint16_t* CB, const uint16_t* Cf,
                              const float* D, void* y, hipStream_t st, const StageEv& ev = StageEv{});
 // Segmented states (ChainPlan::nseg > 1): the state entering chunk c of
 // segment k >= 1 is Hb_c + exp(cdec_c) Hin_k, Hin [b, nseg, H, P * N] fp32,
@@ -362,14 +363,13 @@ hipError_t launch_chunk_scan(const FwdShape& s, ssd_dtype type, bool mfma, const
 // the chunk table; dstate 128 or 256), segments of seglen slots, cdec -inf
 // for the chunks that take no correction.
 struct SegStates {
-  const uint16_t* Cf = nullptr;   // C in fragment order (CF, written by the tiles launch)
   const float* Hin = nullptr;
   const float* cdec = nullptr;
   int nseg = 1, seglen = 0;
   bool var = false;
 };
 hipError_t launch_chunk_scan_mfma(const FwdShape& s, const void* x, const uint16_t* CB,
-                                  const void* C, const float* Acs, const float* dtq,
+                                  const uint16_t* Cf, const float* Acs, const float* dtq,
                                   const uint16_t* Hb, const float* D, void* y, const int4* tab,
                                   hipStream_t st, const StageEv& ev = StageEv{},
                                   const SegStates& seg = SegStates{});
