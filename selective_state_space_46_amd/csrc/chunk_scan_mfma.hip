@@ -100,6 +100,9 @@ void chunk_scan_mfma_kernel(
   __shared__ __attribute__((aligned(16))) float sF[kSC];  // exp(Acs[block end] - Acs_s) * dt_s
   __shared__ __attribute__((aligned(16))) float sL[kSC];  // log2(dt_s) - Acs_s log2(e)
 
+  // HLDS kernels run only with one chunk per super-chunk: Q as a constant
+  // lets every index below fold
+  if constexpr (HLDS) Q = kSC;
   const int id = xcd_swizzle(blockIdx.x, gridDim.x);
   const int h = id % H;
   const int bs = id / H;
@@ -113,7 +116,10 @@ void chunk_scan_mfma_kernel(
   const int lpc = Q / 32;         // 32-row blocks per chunk
   const int ntile = lpc * (lpc + 1) / 2;
   // token rows of the super-chunk's chunks (ci = 0 .. cps-1); n = 0 past the last chunk
+  // (one chunk per super-chunk: its table entry read once)
+  const ChunkRows row_c0 = chunk_rows(VARLEN ? tab : static_cast<const int4*>(nullptr), b, c0, T, Q);
   auto crows = [&](int ci) {
+    if constexpr (HLDS) return ci == 0 ? row_c0 : ChunkRows{0, 0};
     return c0 + ci < nc ? chunk_rows(VARLEN ? tab : static_cast<const int4*>(nullptr), b, c0 + ci, T, Q)
                         : ChunkRows{0, 0};
   };
@@ -145,13 +151,16 @@ void chunk_scan_mfma_kernel(
         CB + (((size_t(b) * nc + cgi) * G + g) * ntile + size_t(ir) * (ir + 1) / 2) * 1024 +
         size_t(lane) * 16);
   };
-  // a block's first loads: its diagonal tile, its first tile, its C rows
-  // (k = dstate, rows clamped into the tensor; zeroed past the end at use)
+  // a block's first loads: its diagonal tile (W = 4; with W = 8 it comes
+  // with the other tiles, after the C rows are used), its first tile, its C
+  // rows (k = dstate, rows clamped into the tensor; zeroed past the end at use)
   auto issue_block_loads = [&](int i, u32x4 (&td)[2], u32x4 (&tn)[2], u32x4 (&cfv)[N / 16]) {
     const u32x4* ts = tile_src(i);
     const int ir = i - (i / lpc) * lpc;
-    td[0] = ts[ir * 128];
-    td[1] = ts[ir * 128 + 1];
+    if constexpr (W != 8) {
+      td[0] = ts[ir * 128];
+      td[1] = ts[ir * 128 + 1];
+    }
     tn[0] = ts[0];
     tn[1] = ts[1];
     // C in operand order, written with the tiles (Cf, zeros past the
@@ -164,73 +173,105 @@ void chunk_scan_mfma_kernel(
   // share a SIMD, so wave w >= 4 takes block 11 - w: every SIMD then holds
   // blocks k and 7 - k, 9 tiles
   const int blk0 = (W == 8 && wave >= 4) ? 11 - wave : wave;
+
+  // ---- staging: the per-token tables (Acs, the per-token factor), H_c and
+  // x into LDS, and the first block's tiles and C rows into registers. Every
+  // load is issued before the first value is used, tables first and the
+  // register-only loads last: the vector memory counter retires loads in
+  // issue order, so each wait below covers only what is needed there (a
+  // wait for the tables or H would otherwise also wait for the C rows).
+  // tables: one token per thread (kSC <= threads)
+  static_assert(kSC <= kThreads, "one table entry per thread");
+  // (loads unconditional, at an in-bounds index, and masked where used, so
+  // that nothing waits for them before the loads below are issued)
+  const int tq = min(tid, kSC - 1);
+  const bool tvalid = tid < kSC && crows(tq / Q).n > 0;
+  float ta, tl, td;
+  {
+    const size_t row = ((size_t(b) * H + h) * nc + min(c0 + tq / Q, nc - 1)) * Q;
+    const int q = tq % Q;
+    ta = Acs[row + q];
+    tl = Acs[row + (q | 31)];
+    td = dtq[row + q];
+  }
+  // H_c in fragment order (hb_off), copied as it is (with segments, plus
+  // alpha times the state entering the segment, stored in the same order)
+  constexpr int kPieces = HLDS ? P * N / 8 : 1;      // 16-byte pieces of one state
+  constexpr int KP = (kPieces + kThreads - 1) / kThreads;
+  u32x4 hv[KP];
+  float alpha = 0.f;                                 // uniform
+  int sgk = 0;                                       // the chunk's segment (uniform)
+  if constexpr (HLDS) {
+    const uint16_t* hsrc = Hb + ((size_t(b) * nc + c0) * H + h) * size_t(P) * N;
+    bool later = false;
+    if constexpr (SEG) seg_of(c0, sgk, later);
+    // the weight of the state entering the segment (where it underflows to
+    // zero the correction adds exactly zero and is skipped)
+    if (SEG && later) alpha = exp_fast(cdec[(size_t(b) * H + h) * nc + c0]);
+#pragma unroll
+    for (int k = 0; k < KP; ++k) {
+      const int e = min(tid + k * kThreads, kPieces - 1);
+      hv[k] = load16(hsrc + 8 * size_t(e));
+    }
+  }
+  // raw x, token-major, swizzled. Thread tid copies 16-byte chunk tid % RBX
+  // of rows tid / RBX + k kStep; kStep is a multiple of the swizzle period
+  // (16 rows), so every row of the thread has the same swizzle and its LDS
+  // offsets differ by constants.
+  static_assert(kThreads % RBX == 0 && (kThreads / RBX) % 16 == 0, "x staging shape");
+  constexpr int kStep = kThreads / RBX;
+  const int xr0 = tid / RBX, xcc = tid % RBX;
+  u32x4 xv[kSC / kStep];
+  bool xok[kSC / kStep];       // rows past their chunk's tokens: zeros, applied when written
+  if (fast) {
+    const uint16_t* src = x + ((rows0.r0 + xr0) * H + h) * size_t(P) + 8 * xcc;
+    const size_t step = size_t(kStep) * H * P;
+#pragma unroll
+    for (int k = 0; k < kSC / kStep; ++k) {
+      xv[k] = load16(src + k * step);
+      xok[k] = opaque(1) != 0;   // not a constant: the mask stays at the writes below
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < kSC / kStep; ++k) {
+      const int r = xr0 + k * kStep;
+      const ChunkRows cr = crows(r / Q);
+      const int rq = r % Q;
+      // a chunk with no valid rows (past the last chunk, or an unused table
+      // slot) reads a valid row of another chunk instead: any in-bounds row
+      const long row = cr.n > 0 ? cr.r0 + min(rq, cr.n - 1) : rowsv.r0;
+      xv[k] = load16(x + (row * H + h) * size_t(P) + 8 * xcc);
+      xok[k] = rq < cr.n;
+    }
+  }
   u32x4 pre_tdiag[2], pre_tnext[2], pre_cf[N / 16];
   if ((blk0 % lpc) * 32 < crows(blk0 / lpc).n) issue_block_loads(blk0, pre_tdiag, pre_tnext, pre_cf);
 
-  // ---- staging 1: Acs, the per-token factor, H_c^T
-  for (int i = tid; i < kSC; i += kThreads) {
-    const int c = c0 + i / Q;
-    float a = 0.f, f = 0.f, d = 0.f;
-    if (crows(i / Q).n > 0) {
-      const size_t row = ((size_t(b) * H + h) * nc + c) * Q;
-      const int q = i % Q;
-      a = Acs[row + q] * kLog2e;
-      d = dtq[row + q];
-      f = __builtin_amdgcn_exp2f(Acs[row + (q | 31)] * kLog2e - a) * d;  // exponent <= 0
-    }
-    sA[i] = a;
-    sF[i] = f;
-    sL[i] = __builtin_amdgcn_logf(d) - a;    // log2; -inf where dt = 0
+  if (tid < kSC) {
+    const float a = tvalid ? ta * kLog2e : 0.f, d = tvalid ? td : 0.f;
+    sA[tid] = a;
+    sF[tid] = tvalid ? __builtin_amdgcn_exp2f(tl * kLog2e - a) * d : 0.f;  // exponent <= 0
+    sL[tid] = __builtin_amdgcn_logf(d) - a;                               // log2; -inf where dt = 0
   }
   if constexpr (HLDS) {
-    // H_c in fragment order (hb_off), copied as it is (with segments, plus
-    // alpha times the state entering the segment, stored in the same order)
-    const uint16_t* hsrc = Hb + ((size_t(b) * nc + c0) * H + h) * size_t(P) * N;
-    constexpr int kPieces = P * N / 8;               // 16-byte pieces of one state
-    int sg = 0;                                      // the chunk's segment (uniform)
-    bool later = false;
-    if constexpr (SEG) seg_of(c0, sg, later);
-    // the weight of the state entering the segment (uniform; where it
-    // underflows to zero the correction adds exactly zero and is skipped)
-    const float alpha = SEG && later ? exp_fast(cdec[(size_t(b) * H + h) * nc + c0]) : 0.f;
-    const float* hin = SEG ? Hin + ((size_t(b) * nseg + sg) * H + h) * size_t(P) * N : nullptr;
+    if (SEG && alpha != 0.f) {
+      const float* hin = Hin + ((size_t(b) * nseg + sgk) * H + h) * size_t(P) * N;
 #pragma unroll
-    for (int k = 0; k < (kPieces + kThreads - 1) / kThreads; ++k) {
-      const int e = tid + k * kThreads;
-      if (kPieces % kThreads != 0 && e >= kPieces) break;
-      u32x4 v = load16(hsrc + 8 * size_t(e));
-      if (SEG && alpha != 0.f) v = seg_combine(v, hin + 8 * size_t(e), alpha);   // Hin: the same order
-      *reinterpret_cast<u32x4*>(&sH[8 * e]) = v;
-    }
-  }
-  // raw x, token-major, swizzled: issued with the loads above. Thread tid
-  // copies 16-byte chunk tid % RBX of rows tid / RBX + k kStep; kStep is a
-  // multiple of the swizzle period (16 rows), so every row of the thread has
-  // the same swizzle and its LDS offsets differ by constants.
-  static_assert(kThreads % RBX == 0 && (kThreads / RBX) % 16 == 0, "x staging shape");
-  {
-    constexpr int kStep = kThreads / RBX;
-    const int r0 = tid / RBX, cc = tid % RBX;
-    uint16_t* dst = &sX[lds_off<RBX, true>(r0, 8 * cc)];
-    if (fast) {
-      const uint16_t* src = x + ((rows0.r0 + r0) * H + h) * size_t(P) + 8 * cc;
-      const size_t step = size_t(kStep) * H * P;
-#pragma unroll
-      for (int k = 0; k < kSC / kStep; ++k)
-        *reinterpret_cast<u32x4*>(dst + k * kStep * P) = load16(src + k * step);
-    } else {
-#pragma unroll
-      for (int k = 0; k < kSC / kStep; ++k) {
-        const int r = r0 + k * kStep;
-        const ChunkRows cr = crows(r / Q);
-        const int rq = r % Q;
-        // a chunk with no valid rows (past the last chunk, or an unused table
-        // slot) reads a valid row of another chunk instead: any in-bounds row
-        const long row = cr.n > 0 ? cr.r0 + min(rq, cr.n - 1) : rowsv.r0;
-        const u32x4 v = load16(x + (row * H + h) * size_t(P) + 8 * cc);
-        *reinterpret_cast<u32x4*>(dst + k * kStep * P) = keep_or_zero(rq < cr.n, v);
+      for (int k = 0; k < KP; ++k) {
+        const int e = min(tid + k * kThreads, kPieces - 1);
+        hv[k] = seg_combine(hv[k], hin + 8 * size_t(e), alpha);   // Hin: the same order
       }
     }
+#pragma unroll
+    for (int k = 0; k < KP; ++k) {
+      const int e = tid + k * kThreads;
+      if (kPieces % kThreads == 0 || e < kPieces) *reinterpret_cast<u32x4*>(&sH[8 * e]) = hv[k];
+    }
+  }
+  {
+    uint16_t* dst = &sX[lds_off<RBX, true>(xr0, 8 * xcc)];
+#pragma unroll
+    for (int k = 0; k < kSC / kStep; ++k) *reinterpret_cast<u32x4*>(dst + k * kStep * P) = keep_or_zero(xok[k], xv[k]);
   }
   __syncthreads();
 
@@ -280,7 +321,10 @@ void chunk_scan_mfma_kernel(
     u32x4 tdiag[2], tnext[2], cf[N / 16];
     if (which == 0) {
 #pragma unroll
-      for (int m = 0; m < 2; ++m) { tdiag[m] = pre_tdiag[m]; tnext[m] = pre_tnext[m]; }
+      for (int m = 0; m < 2; ++m) {
+        if constexpr (W != 8) tdiag[m] = pre_tdiag[m];
+        tnext[m] = pre_tnext[m];
+      }
 #pragma unroll
       for (int ks = 0; ks < N / 16; ++ks) cf[ks] = pre_cf[ks];
     } else {
@@ -387,18 +431,20 @@ void chunk_scan_mfma_kernel(
       }
     };
     if constexpr (W == 8) {
-      // one block per wave (at most 7 off-diagonal tiles): all of them in
-      // flight at once, in the registers the C rows held until here
-      u32x4 tall[7][2];
+      // one block per wave (at most 7 off-diagonal tiles): all of them and
+      // the diagonal one in flight at once, in the registers the C rows held
+      // until here
+      u32x4 tall[7][2], tdg[2];
 #pragma unroll
       for (int u = 0; u < 2; ++u) tall[0][u] = tnext[u];
 #pragma unroll
       for (int t = 1; t < 7; ++t)
         if (t < irel) load_tile(t, tall[t]);
+      load_tile(irel, tdg);
 #pragma unroll
       for (int t = 0; t < 7; ++t)
         if (t < irel) apply(t, tall[t], false);
-      apply(irel, tdiag, true);
+      apply(irel, tdg, true);
     } else {
       // off-diagonal tiles two at a time, ping-pong buffers (the tile after
       // next loads while the current one is applied; no register copies)
