@@ -984,11 +984,17 @@ __global__ __launch_bounds__(512) void chunk_scores_lds_kernel(const uint16_t* _
   const int b = int(blockIdx.x) / G / nc;
   const ChunkRows cr = chunk_rows(tab, b, c, T, Q);
   if (cr.n <= 0) return;                        // an unused slot: uniform, before the barrier
-  // B rows 0 .. Q-1 of the chunk (rows past its tokens as zeros)
-  for (int e = tid; e < Q * RP; e += 512) {
-    const int r = e / RP, p = e % RP;
-    const u32x4 v = load16(Bm + ((cr.r0 + min(r, cr.n - 1)) * G + g) * size_t(N) + 8 * p);
-    *reinterpret_cast<u32x4*>(&sB[r * N + 8 * (p ^ (r & 7))]) = keep_or_zero(r < cr.n, v);
+  // B rows 0 .. Q-1 of the chunk, copied straight into LDS: the wave's 64
+  // lanes fill 64 consecutive 16-byte slots, slot (r, q) taking piece
+  // q ^ (r % 8) of row r. Rows past the chunk's tokens repeat its last row:
+  // every product they enter meets a zero x or a masked weight in chunk_scan
+  // (their rows s lie past every valid output row l >= s). All copies are in
+  // flight at once; the wait before the barrier covers them.
+  static_assert((kMaxQ * RP) % 512 == 0, "whole waves of copies");
+  for (int e0 = 0; e0 < Q * RP; e0 += 512) {
+    const int e = e0 + tid, r = e / RP, q = e % RP;
+    copy_to_lds16(Bm + ((cr.r0 + min(r, cr.n - 1)) * G + g) * size_t(N) + 8 * (q ^ (r & 7)),
+                  &sB[size_t(e0 + 64 * wave) * 8]);
   }
   const int i = wave < 4 ? wave : 11 - wave;    // C row block (wave-uniform)
   const bool mine = i < lpc && 32 * i < cr.n;
@@ -998,10 +1004,11 @@ __global__ __launch_bounds__(512) void chunk_scores_lds_kernel(const uint16_t* _
     const uint16_t* crow = Cm + ((cr.r0 + min(t, cr.n - 1)) * G + g) * size_t(N) + 8 * g2;
 #pragma unroll
     for (int ks = 0; ks < N / 16; ++ks) cf[ks] = keep_or_zero(t < cr.n, load16(crow + 16 * ks));
-    store_c_frags<N>(CF, cf, b, c, g, i, G, Q, nc, lane);
   }
+  wait_vmcnt<0>();                              // this wave's B copies are in LDS
   __syncthreads();
   if (!mine) return;
+  store_c_frags<N>(CF, cf, b, c, g, i, G, Q, nc, lane);   // (after the barrier: no wait for these stores)
   const size_t base = ((size_t(b) * nc + c) * G + g) * ntile;
   for (int j = 0; j <= i; ++j) {
     const int r = 32 * j + l32;                 // this lane's B row
