@@ -446,18 +446,24 @@ void chunk_scan_mfma_kernel(
         if (t < irel) apply(t, tall[t], false);
       apply(irel, tdg, true);
     } else {
-      // off-diagonal tiles two at a time, ping-pong buffers (the tile after
-      // next loads while the current one is applied; no register copies)
-      u32x4 tB[2];
-      int jj = 0;
+      // off-diagonal tiles through a ring of three buffers: the next two
+      // tiles load while one is applied (no register copies)
+      u32x4 tB[2], tC[2];
+      if (1 < irel) load_tile(1, tB);
+      if (2 < irel) load_tile(2, tC);
 #pragma unroll 1
-      for (; jj + 1 < irel; jj += 2) {
-        load_tile(jj + 1, tB);
+      for (int jj = 0; jj < irel; jj += 3) {
         apply(jj, tnext, false);
-        if (jj + 2 < irel) load_tile(jj + 2, tnext);
-        apply(jj + 1, tB, false);
+        if (jj + 3 < irel) load_tile(jj + 3, tnext);
+        if (jj + 1 < irel) {
+          apply(jj + 1, tB, false);
+          if (jj + 4 < irel) load_tile(jj + 4, tB);
+        }
+        if (jj + 2 < irel) {
+          apply(jj + 2, tC, false);
+          if (jj + 5 < irel) load_tile(jj + 5, tC);
+        }
       }
-      if (jj < irel) apply(jj, tnext, false);
       apply(irel, tdiag, true);
     }
 
