@@ -308,11 +308,15 @@ __global__ __launch_bounds__(kThreads) void varlen_segment_recurrence(
   const size_t off0 = size_t(h) * sbh + hb_off(p, n, N);
   const float* sd = segdec + size_t(h) * nseg;
   const float* fd = fdec + size_t(h) * nseg;
-  f32x4 rs[kDepth];
+  f32x4 rs[kDepth], rf[kDepth];
   float rsd[kDepth], rfd[kDepth];
   int rfs[kDepth];
+  // F (the local end state of a sequence that ends in segment k) is fetched
+  // with S, used only where fseq[k] names such a sequence: a load and its
+  // wait per ending would otherwise sit on the chain
   auto fetch = [&](int k, int j) {
     rs[j] = *reinterpret_cast<const f32x4*>(S + off0 + size_t(k) * cstride);
+    rf[j] = *reinterpret_cast<const f32x4*>(F + off0 + size_t(k) * cstride);
     rsd[j] = sd[k];
     rfd[j] = fd[k];
     rfs[j] = fseq[k];
@@ -326,14 +330,12 @@ __global__ __launch_bounds__(kThreads) void varlen_segment_recurrence(
     for (int j = 0; j < kDepth; ++j) {
       const int k = k0 + j;
       if (k < nseg) {
-        const f32x4 e = rs[j];
+        const f32x4 e = rs[j], fk = rf[j];
         const float a = expf(rsd[j]), af = expf(rfd[j]);
         const int fs = rfs[j];                 // uniform
         if (k + kDepth < nseg) fetch(k + kDepth, j);
         if (fs >= 0 && fs < nseq && fin) {
-          // sequence fs, continued into segment k, ends there (its local end
-          // state read only here: few segments have one)
-          const f32x4 fk = *reinterpret_cast<const f32x4*>(F + off0 + size_t(k) * cstride);
+          // sequence fs, continued into segment k, ends there
           tile[4 * nq][pi] = fk.x + af * carry.x;
           tile[4 * nq + 1][pi] = fk.y + af * carry.y;
           tile[4 * nq + 2][pi] = fk.z + af * carry.z;
