@@ -48,6 +48,13 @@ METRIC = "SSD fwd tokens/s per layer + % of bf16 MFMA / HBM roofline on 1 MI355X
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 PROFILES = os.path.join(ROOT, "profiles")
+# Before a forward workload's warm-up steps the step runs untimed for this
+# long: under a sudden sustained load the GPU's clocks dip and recover over
+# the first ~20 ms (measured on the 128K-token layer: per-call times rise
+# from 0.63 to 0.83 ms within 5 calls and settle back over ~20 more), so 5
+# warm-up steps alone leave the timed window in that transient (0.706 ms per
+# step against 0.630 with 50 or 200 warm-up steps).
+SETTLE_S = 0.15
 KERNEL_SOURCES = {
     "chunk_cumsum": ["chunk_cumsum.hip"],
     "chunk_state": ["chunk_state.hip", "chunk_state_mfma.hip", "mfma_util.h"],
@@ -232,7 +239,7 @@ def to_dev(a, dtype):
     return t.to(torch.bfloat16) if dtype == "bf16" else t
 
 
-def bench_fwd(hip, w, steps, warmup, cold=False):
+def bench_fwd(hip, w, steps, warmup, cold=False, settle=True):
     import torch
     import selective_state_space_46_amd as ssd
 
@@ -253,6 +260,13 @@ def bench_fwd(hip, w, steps, warmup, cold=False):
         ssd.ssd_chunk_scan_fwd_timed(x, dt, A, B, C, D, init, w.chunk_len, y=y, final_state=fin,
                                      workspace=ws, stream=stream, stage_events=ev)
 
+    # untimed: clocks settled (SETTLE_S of back-to-back steps), then the
+    # warm-up steps
+    t_settle = time.perf_counter()
+    while settle and time.perf_counter() - t_settle < SETTLE_S:
+        for _ in range(4):
+            call()
+        torch.cuda.synchronize()
     for _ in range(warmup):
         call()
     torch.cuda.synchronize()
@@ -580,7 +594,7 @@ def traffic_probe(w):
     copy kernel that reads and writes exactly 256 MiB, against which the
     FETCH_SIZE / WRITE_SIZE counters are calibrated."""
     import torch
-    bench_fwd(Hip(), w, 3, 0)
+    bench_fwd(Hip(), w, 3, 0, settle=False)
     src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda").fill_(1)
     dst = torch.empty_like(src)
     torch.cuda.synchronize()
@@ -743,7 +757,7 @@ def main():
     log(f"[bench] {w.name}: warmup {args.warmup}, steps {args.steps}")
     r = bench_fwd(hip, w, args.steps, args.warmup)
     log(f"[bench] {r['ms_per_step']:.4f} ms/step, {r['tokens_per_s']:.4g} tok/s, stages {r['stage_ms']}")
-    cold = bench_fwd(hip, w, max(3, args.steps // 4), 1, cold=True)
+    cold = bench_fwd(hip, w, max(3, args.steps // 4), 1, cold=True, settle=False)
     log(f"[bench] cold (Infinity Cache flushed): {cold['ms_per_step']:.4f} ms/step")
     nseg = plan_of(w)
     kernels, roofline = fwd_report(w, r, nseg)
@@ -768,7 +782,7 @@ def main():
                 continue
             log(f"[bench] {ow.name}")
             rr = bench_fwd(hip, ow, 20, 5)
-            rc = bench_fwd(hip, ow, 5, 1, cold=True)
+            rc = bench_fwd(hip, ow, 5, 1, cold=True, settle=False)
             ok, oroof = fwd_report(ow, rr, plan_of(ow))
             others[ow.name] = {"tokens_per_s": round(rr["tokens_per_s"], 1),
                                "ms_per_step": round(rr["ms_per_step"], 5),
