@@ -106,7 +106,8 @@ typedef SSD_ENUM(ssd_dtype) { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype;
  * each chunk (fp32 [batch, nchunks, nheads, dstate, headdim] on the generic
  * path; on the bf16 matrix-core path bf16, plus the chunk states in fp32 when
  * they are passed by a separate launch, plus the C B^T products of each
- * chunk). It carries nothing from one call to the next. `dtype` is an
+ * chunk and a copy of C in the order the matrix-core kernels read it). It
+ * carries nothing from one call to the next. `dtype` is an
  * argument because the two paths need different amounts. The answer depends
  * on the current HIP device (its compute-unit count chooses the launches,
  * see ssd_chunk_scan_fwd_fused_states): query on the device that runs the

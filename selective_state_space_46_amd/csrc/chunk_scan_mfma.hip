@@ -44,8 +44,8 @@
 //      bf16, is the B operand of y^T += X^T G^T under a k permutation that the
 //      X operand reproduces: x sits in LDS in natural token-major order
 //      (swizzled 16-byte chunks) and is read transposed with
-//      ds_read_b64_tr_b16. Tiles are loaded one tile ahead of use, into two
-//      buffers used in turn.
+//      ds_read_b64_tr_b16. With W = 8 a block's tiles all load at once; with
+//      W = 4 through a ring of three buffers, two tiles ahead of use.
 //   3. + D x (x from the same LDS tile), bf16 rounding, 8-byte stores of 4
 //      consecutive p; where the super-chunk is one chunk the rounded rows go
 //      back through the x tile (after a barrier: no wave reads x any more) and
