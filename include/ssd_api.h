@@ -219,7 +219,7 @@ SSD_API ssd_status ssd_chunk_scan_fwd_timed(const void *x, const void *dt, const
  * allocating routine; its workspace is a scratch array that the library
  * holds in device memory, SSD_NOALLOC_SCRATCH_BYTES (64 MiB) per GPU, for the
  * life of the process (the 130M-shaped layer, batch 8 x 2048 tokens, needs
- * about 33 MiB of it). Sizes whose workspace (ssd_chunk_scan_fwd_workspace)
+ * about 36 MiB of it). Sizes whose workspace (ssd_chunk_scan_fwd_workspace)
  * exceeds that return SSD_ERR_WORKSPACE before any launch; every other
  * argument and error is as for ssd_chunk_scan_fwd, and the results are
  * bit-for-bit the same. The first call on a device looks up that device's
