@@ -100,18 +100,36 @@ __host__ __device__ __forceinline__ int varlen_first_slot(int s0, int i, int Q) 
 // chunk slots for T tokens in nseq sequences
 __host__ __device__ __forceinline__ int varlen_slots(int T, int nseq, int Q) { return (T + Q - 1) / Q + nseq; }
 
-// The table entries of sequence i (tokens s0 .. s0 + len - 1): its chunk
-// slots. Entries past nslots are never reached for a span from varlen_span;
-// they are skipped all the same.
-__host__ __device__ inline void varlen_fill(int i, int s0, int len, int Q, int4* tab, int nslots) {
-  const int nch = (len + Q - 1) / Q;
-  const int first = varlen_first_slot(s0, i, Q);
-  for (int k = 0; k < nch; ++k) {
-    const int c = first + k;
-    if (c >= nslots) break;
-    const int flags = (k == 0 ? 1 : 0) | (k == nch - 1 ? 2 : 0);
-    tab[c] = int4{s0 + k * Q, len - k * Q < Q ? len - k * Q : Q, i, flags};
+// The table entry of chunk slot c, built slot by slot (the table kernel, one
+// thread per slot): the sequence holding c is the last one whose first slot
+// is <= c (first(i) = floor(s0_i / Q) + i grows with i for well-formed
+// offsets, and a sequence's chunks end before the next sequence's first
+// slot), found by bisection over first(); `first` gives first(i) for
+// 0 <= i < nseq. Slot c holds chunk c - first(i) of that sequence when the
+// sequence reaches that far, else nothing. For well-formed offsets every
+// sequence's chunks fill consecutive slots from its first and the slots
+// between sequences stay empty; for any offsets an entry is one chunk of a
+// clamped span or empty, so every row it names lies inside the tokens.
+template <class First>
+__host__ __device__ inline int4 varlen_slot_entry(const int* cu, int nseq, int T, int Q, int c, First first) {
+  int lo = 0, hi = nseq - 1, i = -1;
+  while (lo <= hi) {
+    const int mid = (lo + hi) >> 1;
+    if (first(mid) <= c) {
+      i = mid;
+      lo = mid + 1;
+    } else {
+      hi = mid - 1;
+    }
   }
+  if (i < 0) return int4{0, 0, 0, 0};
+  int s0, len;
+  varlen_span(cu, i, T, s0, len);
+  const int nch = (len + Q - 1) / Q;
+  const int k = c - varlen_first_slot(s0, i, Q);
+  if (k < 0 || k >= nch) return int4{0, 0, 0, 0};
+  const int flags = (k == 0 ? 1 : 0) | (k == nch - 1 ? 2 : 0);
+  return int4{s0 + k * Q, len - k * Q < Q ? len - k * Q : Q, i, flags};
 }
 
 // ---------------------------------------------------------------------------

@@ -20,29 +20,38 @@
 namespace ssd {
 namespace {
 
-constexpr int kTabThreads = 1024;
+constexpr int kTabThreads = 256;
+constexpr int kTabLds = 4096;   // sequences whose first slots are staged in LDS
 
-// one work-group: clear every slot, then each thread writes the entries of
-// sequences tid, tid + 1024, ... (varlen_fill: slots < nslots for any clamped
-// span)
+// one thread per slot, each writing its whole entry (varlen_slot_entry), so
+// no slot needs clearing first and no thread walks a sequence's chunks in
+// turn; up to kTabLds sequences, each work-group stages the sequences' first
+// slots in LDS for the bisection, else it reads the offsets from memory
 __global__ __launch_bounds__(kTabThreads) void varlen_table_kernel(const int* __restrict__ cu, int nseq,
                                                                    int T, int Q, int nslots,
                                                                    int4* __restrict__ tab) {
+  __shared__ int sfirst[kTabLds];
   const int tid = threadIdx.x;
-  for (int c = tid; c < nslots; c += kTabThreads) tab[c] = int4{0, 0, 0, 0};
-  __syncthreads();   // the clears are ordered before the entries below
-  for (int i = tid; i < nseq; i += kTabThreads) {
-    int s0, len;
-    varlen_span(cu, i, T, s0, len);
-    varlen_fill(i, s0, len, Q, tab, nslots);
+  const int c = int(blockIdx.x) * kTabThreads + tid;
+  int4 e;
+  if (nseq <= kTabLds) {
+    for (int i = tid; i < nseq; i += kTabThreads) sfirst[i] = varlen_first_slot(clamp_int(cu[i], 0, T), i, Q);
+    __syncthreads();
+    if (c >= nslots) return;
+    e = varlen_slot_entry(cu, nseq, T, Q, c, [&](int i) { return sfirst[i]; });
+  } else {
+    if (c >= nslots) return;
+    e = varlen_slot_entry(cu, nseq, T, Q, c, [&](int i) { return varlen_first_slot(clamp_int(cu[i], 0, T), i, Q); });
   }
+  tab[c] = e;
 }
 
 }  // namespace
 
 hipError_t launch_varlen_table(const int* cu, int nseq, int T, int Q, int4* tab, hipStream_t st) {
-  hipLaunchKernelGGL(varlen_table_kernel, dim3(1), dim3(kTabThreads), 0, st, cu, nseq, T, Q,
-                     varlen_slots(T, nseq, Q), tab);
+  const int nslots = varlen_slots(T, nseq, Q);
+  hipLaunchKernelGGL(varlen_table_kernel, dim3(unsigned((nslots + kTabThreads - 1) / kTabThreads)),
+                     dim3(kTabThreads), 0, st, cu, nseq, T, Q, nslots, tab);
   return hipGetLastError();
 }
 

@@ -1,8 +1,8 @@
 // Host-only driver for tests/test_host_logic.py, running the library's own
 // index helpers (ssd_internal.h) on the host:
 //   stdin "T nseq Q" and nseq + 1 offsets: builds the packed-sequence chunk
-//   table with varlen_span / varlen_fill, as the table kernel does per
-//   sequence; stdout: nslots, then one line per chunk slot (4 integers);
+//   table with varlen_slot_entry, slot by slot as the table kernel does;
+//   stdout: nslots, then one line per chunk slot (4 integers);
 //   stdin "xcd n": the logical id xcd_swizzle gives each of n work-groups,
 //   one per line.
 #include <cstdio>
@@ -24,12 +24,11 @@ int main() {
   for (int& v : cu)
     if (std::scanf("%d", &v) != 1) return 2;
   const int nslots = ssd::varlen_slots(T, nseq, Q);
-  std::vector<int4> tab(nslots, int4{0, 0, 0, 0});
-  for (int i = 0; i < nseq; ++i) {
-    int s0, len;
-    ssd::varlen_span(cu.data(), i, T, s0, len);
-    ssd::varlen_fill(i, s0, len, Q, tab.data(), nslots);
-  }
+  std::vector<int4> tab(nslots);
+  for (int c = 0; c < nslots; ++c)
+    tab[c] = ssd::varlen_slot_entry(cu.data(), nseq, T, Q, c, [&](int i) {
+      return ssd::varlen_first_slot(ssd::clamp_int(cu[i], 0, T), i, Q);
+    });
   std::printf("%d\n", nslots);
   for (const int4& e : tab) std::printf("%d %d %d %d\n", e.x, e.y, e.z, e.w);
   return 0;
