@@ -204,3 +204,19 @@ def test_varlen_many_short_sequences():
     nseg, L = _plan(inp, cu, 128)
     assert nseg > 1 and len(lens) >= 4 * nseg, (nseg, L)
     _check(inp, cu, 128, final_in_place=True)
+
+
+def test_varlen_more_sequences_than_the_table_stages():
+    """4500 sequences of 0 .. 6 tokens (more than the 4096 whose first slots
+    the chunk-table kernel stages in LDS, so every slot bisects over the
+    offsets in memory), no initial states, headdim 32, chunk_len 64: most
+    chunk slots are a whole sequence, many sequences are empty"""
+    rng = np.random.default_rng(7300)
+    lens = rng.integers(0, 7, size=4500)
+    lens[::13] = 0
+    cu = np.concatenate([[0], np.cumsum(lens)]).tolist()
+    inp = _inputs(cu[-1], 2, 32, 128, 1, len(lens), seed=7301, with_init=False)
+    assert len(lens) > 4096
+    nseg, L = _plan(inp, cu, 64)
+    assert nseg > 1, (nseg, L)
+    _check(inp, cu, 64)
